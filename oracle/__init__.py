@@ -1,0 +1,177 @@
+"""CPU oracle of the H-BitLinear forward (ctypes wrapper around ``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark may use it; the product library never does.  It shares no
+code with the HIP path.  See ``oracle.c`` for the specification of each step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", "-std=c11"]
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.oracle_quantize_weights.argtypes = [P, I64, I64, P, P]
+        L.oracle_weight_scale.argtypes = [ctypes.c_float]
+        L.oracle_weight_scale.restype = ctypes.c_double
+        L.oracle_rmsnorm.argtypes = [P, P, I64, P]
+        L.oracle_fwht.argtypes = [P, I64]
+        L.oracle_hadamard_rotate.argtypes = [P, I64, P]
+        L.oracle_quant_act.argtypes = [P, I64, I, P, P, P]
+        L.oracle_gemm_ternary.argtypes = [P, P, I64, I64, I64, P, I]
+        L.oracle_dequant.argtypes = [P, P, ctypes.c_float, I64, I64, P]
+        L.oracle_forward.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, I, P, P, P, P, P, P, I]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _chk(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def max_threads() -> int:
+    return lib().oracle_max_threads()
+
+
+def quantize_weights(w: np.ndarray):
+    """Ternarise latent weights [N][K] -> (w_t int8 [N][K], alpha fp32)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    wt = np.empty((N, K), dtype=np.int8)
+    alpha = np.zeros(1, dtype=np.float32)
+    _chk(lib().oracle_quantize_weights(_p(w), N, K, _p(wt), _p(alpha)), "quantize_weights")
+    return wt, np.float32(alpha[0])
+
+
+def weight_scale(alpha) -> float:
+    return lib().oracle_weight_scale(float(alpha))
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray | None = None) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    K = x.shape[-1]
+    g = None if g is None else np.ascontiguousarray(g, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.float64)
+    xr, orr = x.reshape(-1, K), out.reshape(-1, K)
+    for m in range(xr.shape[0]):
+        _chk(lib().oracle_rmsnorm(_p(xr[m]), _p(g), K, _p(orr[m])), "rmsnorm")
+    return out
+
+
+def fwht(v: np.ndarray) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform (Sylvester order) of each row."""
+    v = np.array(v, dtype=np.float64, order="C", copy=True)
+    n = v.shape[-1]
+    vr = v.reshape(-1, n)
+    for m in range(vr.shape[0]):
+        _chk(lib().oracle_fwht(_p(vr[m]), n), "fwht")
+    return v
+
+
+def hadamard_rotate(u: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    K = u.shape[-1]
+    out = np.empty(u.shape, dtype=np.float64)
+    ur, orr = u.reshape(-1, K), out.reshape(-1, K)
+    for m in range(ur.shape[0]):
+        _chk(lib().oracle_hadamard_rotate(_p(ur[m]), K, _p(orr[m])), "hadamard_rotate")
+    return out
+
+
+def quant_act(xt: np.ndarray, bits: int):
+    """Per-token quantisation of rows -> (codes int8, d double [M], pre double)."""
+    xt = np.ascontiguousarray(xt, dtype=np.float64)
+    K = xt.shape[-1]
+    xr = xt.reshape(-1, K)
+    q = np.empty(xr.shape, dtype=np.int8)
+    pre = np.empty(xr.shape, dtype=np.float64)
+    d = np.empty(xr.shape[0], dtype=np.float64)
+    for m in range(xr.shape[0]):
+        dm = np.zeros(1, dtype=np.float64)
+        _chk(lib().oracle_quant_act(_p(xr[m]), K, bits, _p(q[m]), _p(dm), _p(pre[m])), "quant_act")
+        d[m] = dm[0]
+    return q.reshape(xt.shape), d, pre.reshape(xt.shape)
+
+
+def gemm_ternary(q: np.ndarray, wt: np.ndarray, nthreads: int = 0) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    wt = np.ascontiguousarray(wt, dtype=np.int8)
+    M, K = q.shape
+    N = wt.shape[0]
+    acc = np.empty((M, N), dtype=np.int32)
+    _chk(lib().oracle_gemm_ternary(_p(q), _p(wt), M, N, K, _p(acc), nthreads), "gemm_ternary")
+    return acc
+
+
+def dequant(acc: np.ndarray, d: np.ndarray, alpha) -> np.ndarray:
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    d = np.ascontiguousarray(d, dtype=np.float64)
+    M, N = acc.shape
+    y = np.empty((M, N), dtype=np.float64)
+    _chk(lib().oracle_dequant(_p(acc), _p(d), float(alpha), M, N, _p(y)), "dequant")
+    return y
+
+
+def forward(x: np.ndarray, wt: np.ndarray, alpha, bits: int, g: np.ndarray | None = None,
+            keep: bool = True, nthreads: int = 0) -> dict:
+    """Whole layer on fp32 activations [M][K] with ternary weights [N][K].
+
+    Returns a dict with ``y`` (double [M][N]) and, if ``keep``, the stages
+    ``xt``, ``q``, ``d``, ``pre``, ``acc``.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    wt = np.ascontiguousarray(wt, dtype=np.int8)
+    M, K = x.shape
+    N = wt.shape[0]
+    g = None if g is None else np.ascontiguousarray(g, dtype=np.float32)
+    y = np.empty((M, N), dtype=np.float64)
+    out = {"y": y}
+    if keep:
+        out.update(xt=np.empty((M, K)), q=np.empty((M, K), dtype=np.int8), d=np.empty(M),
+                   pre=np.empty((M, K)), acc=np.empty((M, N), dtype=np.int32))
+    rc = lib().oracle_forward(_p(x), _p(g), _p(wt), float(alpha), M, K, N, bits,
+                              _p(out.get("xt")), _p(out.get("q")), _p(out.get("d")),
+                              _p(out.get("pre")), _p(out.get("acc")), _p(y), nthreads)
+    _chk(rc, "forward")
+    return out
+
+
+def to_bf16_rne(y: np.ndarray) -> np.ndarray:
+    """Round double outputs to bf16 values (via fp32 round-to-nearest, then
+    bf16 round-half-even), returned as fp32 — the output dtype of bf16 runs."""
+    f = np.ascontiguousarray(y, dtype=np.float32).view(np.uint32)
+    lsb = (f >> 16) & 1
+    r = ((f + np.uint32(0x7FFF) + lsb) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)

@@ -1,0 +1,268 @@
+/*
+ * oracle.c -- plain, slow CPU reference of the BitNet v2 H-BitLinear forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes or
+ * calls this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark load it.  It shares no code, header or constant with the HIP
+ * path.
+ *
+ * Sources (the pages print no formula; every formula image is missing, so the
+ * steps below are the plain reading of the surrounding text):
+ *   [QbitAI]  量子位 article on BitNet v2, section 引入H-BitLinear模块
+ *   [XZY]     新智元 article "微软再放LLM量化大招！原生4bit量化...", sections
+ *             BitNet v2：原生4位激活 and H-BitLinear模块
+ *   [AINEWS]  "微软LLM量化再突破：BitNet v2实现原生4bit..." section
+ *             揭秘核心魔法：H-BitLinear与Hadamard变换
+ *   [DIGEST]  "BitNet v2: Native 4-bit Activations with Hadamard Transformation
+ *             for 1-bit LLMs" (arXiv digest page), abstract and 方法详解
+ *
+ * Precision: every floating-point step is done in double; values are rounded
+ * only where the method itself produces a stored low-precision quantity
+ * (the per-tensor weight scale, the integer codes) -- see each function.
+ * Rounding is round-half-to-even (nearbyint under the default FE_TONEAREST).
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC
+ * OpenMP is used only across tokens (rows), never inside one token.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Constants of the specification (the pages give none; readings listed in the
+ * design notes).  RMSNorm epsilon is added to the mean square; the quantiser
+ * floor is applied to the per-tensor / per-token statistic. */
+static const double EPS_NORM = 1e-6;
+static const double EPS_Q = 1e-5;
+static const double Q8 = 127.0;      /* INT8 absmax: max |x| maps to code 127 */
+/* INT4 absmean multiplier: sqrt(7) (reading; not printed on the pages). */
+#define Q4 (sqrt(7.0))
+
+int oracle_version(void) { return 1; }
+
+static double rne(double v) { return nearbyint(v); }
+
+static double clampd(double v, double lo, double hi) {
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+/* ---------------------------------------------------------------------------
+ * Weights: per-tensor absmean ternarisation to {-1, 0, 1}.
+ * [QbitAI §引入H-BitLinear模块], [XZY §H-BitLinear模块], [AINEWS].
+ *   S      = sum of |w| : each row summed left to right in double, then the
+ *            row sums added in row order in double;
+ *   alpha  = (float)(S / (N*K))       -- the stored per-tensor scale (fp32);
+ *   a      = max(alpha, EPS_Q);
+ *   w_t    = clamp(round(w / a), -1, 1)  (w / a in double).
+ * Returns 0, or -1 on bad arguments.
+ * ------------------------------------------------------------------------- */
+int oracle_quantize_weights(const float *w, int64_t N, int64_t K, int8_t *wt, float *alpha_out)
+{
+    if (!w || !wt || !alpha_out || N <= 0 || K <= 0) return -1;
+    double S = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double row = 0.0;
+        for (int64_t k = 0; k < K; ++k) row += fabs((double)w[n * K + k]);
+        S += row;
+    }
+    float alpha = (float)(S / ((double)N * (double)K));
+    double a = (double)alpha;
+    if (a < EPS_Q) a = (double)(float)EPS_Q;
+    for (int64_t i = 0; i < N * K; ++i)
+        wt[i] = (int8_t)clampd(rne((double)w[i] / a), -1.0, 1.0);
+    *alpha_out = alpha;
+    return 0;
+}
+
+/* The effective weight scale used for both ternarising and dequantising. */
+double oracle_weight_scale(float alpha)
+{
+    double a = (double)alpha;
+    if (a < EPS_Q) a = (double)(float)EPS_Q;
+    return a;
+}
+
+/* ---------------------------------------------------------------------------
+ * RMSNorm (the "LN" inside H-BitLinear; the stack is LLaMA-like with RMS
+ * normalisation and no bias) [XZY §BitNet v2：原生4位激活], [QbitAI].
+ *   r = sqrt(mean_k x_k^2 + EPS_NORM),   u_k = x_k * g_k / r     (g = 1 if NULL)
+ * ------------------------------------------------------------------------- */
+int oracle_rmsnorm(const float *x, const float *g, int64_t K, double *u)
+{
+    if (!x || !u || K <= 0) return -1;
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; ++k) ss += (double)x[k] * (double)x[k];
+    double r = sqrt(ss / (double)K + EPS_NORM);
+    for (int64_t k = 0; k < K; ++k) {
+        double gk = g ? (double)g[k] : 1.0;
+        u[k] = (double)x[k] * gk / r;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Walsh-Hadamard transform by its recursive definition (Sylvester order):
+ *   F(v) = v                         if len(v) == 1
+ *   F(v) = [F(a) + F(b), F(a) - F(b)] with a, b the first and second halves.
+ * This is H_n v with H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]], i.e.
+ * H[i][j] = (-1)^popcount(i & j); entries +-1 and H H^T = n I
+ * [XZY §H-BitLinear模块] (entries +-1, rows mutually orthogonal, computed by the
+ * fast O(n log n) transform).  Unnormalised; in place; n a power of two.
+ * ------------------------------------------------------------------------- */
+static void fwht_rec(double *v, int64_t n)
+{
+    if (n == 1) return;
+    int64_t h = n / 2;
+    fwht_rec(v, h);
+    fwht_rec(v + h, h);
+    for (int64_t i = 0; i < h; ++i) {
+        double a = v[i], b = v[h + i];
+        v[i] = a + b;
+        v[h + i] = a - b;
+    }
+}
+
+static int is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
+
+int oracle_fwht(double *v, int64_t n)
+{
+    if (!v || !is_pow2(n)) return -1;
+    fwht_rec(v, n);
+    return 0;
+}
+
+/* Online Hadamard rotation applied to the activations before quantisation,
+ * scaled to be orthogonal:  xt = H_K u / sqrt(K)
+ * [QbitAI §引入H-BitLinear模块], [AINEWS], [DIGEST abstract]. */
+int oracle_hadamard_rotate(const double *u, int64_t K, double *xt)
+{
+    if (!u || !xt || !is_pow2(K)) return -1;
+    memcpy(xt, u, (size_t)K * sizeof(double));
+    fwht_rec(xt, K);
+    double s = sqrt((double)K);
+    for (int64_t k = 0; k < K; ++k) xt[k] = xt[k] / s;
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Per-token activation quantisation [QbitAI §引入H-BitLinear模块],
+ * [XZY §H-BitLinear模块]: 8-bit uses the per-token absmax, 4-bit the per-token
+ * absmean.
+ *   INT8:  stat = max_k |xt_k|,        Q = 127,     codes in [-128, 127]
+ *   INT4:  stat = mean_k |xt_k|,       Q = sqrt(7), codes in [-8, 7]
+ *   G = max(stat, EPS_Q);  pre_k = xt_k * (Q / G);  q_k = clamp(round(pre_k));
+ *   dequant scale d = G / Q.
+ * pre (optional) receives the pre-rounding values (used by the tests to show
+ * that code differences sit at rounding ties).
+ * ------------------------------------------------------------------------- */
+int oracle_quant_act(const double *xt, int64_t K, int bits, int8_t *q, double *d, double *pre)
+{
+    if (!xt || !q || !d || K <= 0 || (bits != 8 && bits != 4)) return -1;
+    double stat = 0.0, Q, lo, hi;
+    if (bits == 8) {
+        for (int64_t k = 0; k < K; ++k) if (fabs(xt[k]) > stat) stat = fabs(xt[k]);
+        Q = Q8; lo = -128.0; hi = 127.0;
+    } else {
+        for (int64_t k = 0; k < K; ++k) stat += fabs(xt[k]);
+        stat = stat / (double)K;
+        Q = Q4; lo = -8.0; hi = 7.0;
+    }
+    double G = stat > EPS_Q ? stat : EPS_Q;
+    double s = Q / G;
+    for (int64_t k = 0; k < K; ++k) {
+        double v = xt[k] * s;
+        if (pre) pre[k] = v;
+        q[k] = (int8_t)clampd(rne(v), lo, hi);
+    }
+    *d = G / Q;
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Ternary integer matmul: acc[m][n] = sum_k q[m][k] * w_t[n][k]  (exact, int32).
+ * Weights are [N][K] (out x in).  Naive triple loop.
+ * ------------------------------------------------------------------------- */
+int oracle_gemm_ternary(const int8_t *q, const int8_t *wt, int64_t M, int64_t N, int64_t K,
+                        int32_t *acc, int nthreads)
+{
+    if (!q || !wt || !acc || M < 0 || N <= 0 || K <= 0) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t s = 0;
+            for (int64_t k = 0; k < K; ++k) s += (int32_t)q[m * K + k] * (int32_t)wt[n * K + k];
+            acc[m * N + n] = s;
+        }
+    return 0;
+}
+
+/* Dequantisation with the activation and weight scales:
+ *   y[m][n] = acc[m][n] * d[m] * a,  a = max(alpha, EPS_Q). */
+int oracle_dequant(const int32_t *acc, const double *d, float alpha, int64_t M, int64_t N, double *y)
+{
+    if (!acc || !d || !y || M < 0 || N <= 0) return -1;
+    double a = oracle_weight_scale(alpha);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = (double)acc[m * N + n] * d[m] * a;
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Whole forward, token by token: RMSNorm -> Hadamard rotation -> quantise ->
+ * ternary matmul -> dequantise [QbitAI §引入H-BitLinear模块] (the layer is the
+ * quantised matmul of the normalised, rotated activations), [DIGEST 方法详解]
+ * (input -> Hadamard -> quantise -> rest).
+ * x [M][K] fp32; g [K] or NULL; wt [N][K]; outputs (each optional except y):
+ *   xt [M][K] double, q [M][K] int8, d [M] double, pre [M][K] double,
+ *   acc [M][N] int32, y [M][N] double.
+ * ------------------------------------------------------------------------- */
+int oracle_forward(const float *x, const float *g, const int8_t *wt, float alpha,
+                   int64_t M, int64_t K, int64_t N, int bits,
+                   double *xt, int8_t *q, double *d, double *pre, int32_t *acc, double *y,
+                   int nthreads)
+{
+    if (!x || !wt || !y || M < 0 || N <= 0 || !is_pow2(K) || (bits != 8 && bits != 4)) return -1;
+    double a = oracle_weight_scale(alpha);
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+#endif
+    for (int64_t m = 0; m < M; ++m) {
+        double *u = (double *)malloc((size_t)K * sizeof(double));
+        double *t = (double *)malloc((size_t)K * sizeof(double));
+        int8_t *qm = (int8_t *)malloc((size_t)K);
+        if (!u || !t || !qm) { bad = 1; free(u); free(t); free(qm); continue; }
+        double dm;
+        oracle_rmsnorm(x + m * K, g, K, u);
+        oracle_hadamard_rotate(u, K, t);
+        oracle_quant_act(t, K, bits, qm, &dm, pre ? pre + m * K : NULL);
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t s = 0;
+            for (int64_t k = 0; k < K; ++k) s += (int32_t)qm[k] * (int32_t)wt[n * K + k];
+            if (acc) acc[m * N + n] = s;
+            y[m * N + n] = (double)s * dm * a;
+        }
+        if (xt) memcpy(xt + m * K, t, (size_t)K * sizeof(double));
+        if (q) memcpy(q + m * K, qm, (size_t)K);
+        if (d) d[m] = dm;
+        free(u); free(t); free(qm);
+    }
+    return bad ? -2 : 0;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

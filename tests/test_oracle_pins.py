@@ -1,0 +1,317 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test ties one oracle step to something other than the oracle itself:
+hand-worked fixtures under tests/golden/, closed forms, textbook identities of
+the Hadamard matrix, brute force with independent numpy code, and
+invariants.  No expected value here comes from the GPU path.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from conftest import read_golden
+
+
+def popcount_sign(i, j):
+    """(-1)^popcount(i & j): the Sylvester Hadamard entry, closed form."""
+    return -1.0 if bin(i & j).count("1") % 2 else 1.0
+
+
+def dense_sylvester(n):
+    """H_n built by block recursion with numpy (independent of the oracle)."""
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+# ----------------------------------------------------------------- Hadamard
+
+def test_h8_matches_hand_written_golden():
+    g = read_golden("hadamard_8.txt")
+    H8 = np.array([g[f"row{i}"] for i in range(8)])
+    Hor = oracle.fwht(np.eye(8))          # row i = F(e_i) = column i of H (H symmetric)
+    assert np.array_equal(Hor, H8)
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64])
+def test_fwht_equals_dense_sylvester_and_closed_form(n):
+    H_block = dense_sylvester(n)
+    H_closed = np.array([[popcount_sign(i, j) for j in range(n)] for i in range(n)])
+    assert np.array_equal(H_block, H_closed)
+    Hor = oracle.fwht(np.eye(n))
+    assert np.array_equal(Hor, H_closed)
+    rng = np.random.default_rng(n)
+    v = rng.normal(size=(5, n))
+    np.testing.assert_allclose(oracle.fwht(v), v @ H_closed.T, rtol=0, atol=1e-12 * n)
+
+
+@pytest.mark.parametrize("n", [2, 16, 64, 256])
+def test_hadamard_is_orthogonal_with_pm1_entries(n):
+    H = oracle.fwht(np.eye(n))
+    assert set(np.unique(H)) <= {-1.0, 1.0}
+    assert np.array_equal(H, H.T)
+    assert np.array_equal(H @ H.T, n * np.eye(n))
+
+
+@pytest.mark.parametrize("K", [64, 1024, 16384])
+def test_rotation_is_orthonormal_involution(K):
+    rng = np.random.default_rng(K)
+    u = rng.laplace(size=(3, K))
+    t = oracle.hadamard_rotate(u)
+    np.testing.assert_allclose(np.linalg.norm(t, axis=1), np.linalg.norm(u, axis=1), rtol=1e-12)
+    np.testing.assert_allclose(oracle.hadamard_rotate(t), u, rtol=0, atol=1e-12 * np.abs(u).max())
+
+
+@pytest.mark.parametrize("K", [4, 256, 4096])
+def test_rotation_special_cases(K):
+    e0 = np.zeros(K); e0[0] = 1.0
+    np.testing.assert_allclose(oracle.hadamard_rotate(e0), np.full(K, 1 / math.sqrt(K)), rtol=1e-14)
+    np.testing.assert_allclose(oracle.hadamard_rotate(np.ones(K)), math.sqrt(K) * e0, atol=1e-12)
+    # one-hot at j gives the j-th Walsh function
+    j = K // 2 + 1 if K > 2 else 1
+    ej = np.zeros(K); ej[j] = 1.0
+    expect = np.array([popcount_sign(k, j) for k in range(K)]) / math.sqrt(K)
+    np.testing.assert_allclose(oracle.hadamard_rotate(ej), expect, rtol=1e-14)
+
+
+def test_fwht_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        oracle.fwht(np.ones(12))
+
+
+# ----------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_closed_forms():
+    # x = c * ones(K): mean square c^2, so u = c / sqrt(c^2 + eps)
+    for c in (3.0, 1e-2, 1e-4):
+        K = 64
+        u = oracle.rmsnorm(np.full((1, K), c, np.float32))
+        expect = float(np.float32(c)) / math.sqrt(float(np.float32(c)) ** 2 + 1e-6)
+        np.testing.assert_allclose(u, expect, rtol=1e-14)
+    # x = [3, 4]: mean square 12.5
+    u = oracle.rmsnorm(np.array([[3.0, 4.0]], np.float32))
+    r = math.sqrt(12.5 + 1e-6)
+    np.testing.assert_allclose(u[0], [3 / r, 4 / r], rtol=1e-15)
+
+
+def test_rmsnorm_invariants():
+    rng = np.random.default_rng(7)
+    x = rng.normal(size=(4, 512)).astype(np.float32)
+    u = oracle.rmsnorm(x)
+    ms = np.mean(x.astype(np.float64) ** 2, axis=1)
+    # mean(u^2) = ms / (ms + eps)
+    np.testing.assert_allclose(np.mean(u ** 2, axis=1), ms / (ms + 1e-6), rtol=1e-13)
+    # odd and (nearly) scale invariant; gain multiplies channel-wise
+    np.testing.assert_array_equal(oracle.rmsnorm(-x), -u)
+    np.testing.assert_allclose(oracle.rmsnorm(4 * x), u, rtol=2e-6)
+    g = synthetic.make_gain(512, 0)
+    np.testing.assert_allclose(oracle.rmsnorm(x, g), u * g, rtol=1e-14)
+
+
+# ----------------------------------------------------------------- quantisers
+
+def test_int8_absmax_hand_golden():
+    g = read_golden("quant_int8_exact.txt")
+    q, d, pre = oracle.quant_act(np.array([g["xt"]]), 8)
+    np.testing.assert_array_equal(pre[0], g["pre"])
+    np.testing.assert_array_equal(q[0], g["codes"])
+    assert d[0] == g["d"][0]
+
+
+def test_int4_absmean_hand_golden():
+    g = read_golden("quant_int4_hand.txt")
+    for case in "abcd":
+        q, d, _ = oracle.quant_act(np.array([g[f"{case}_xt"]]), 4)
+        np.testing.assert_array_equal(q[0], g[f"{case}_codes"])
+        if f"{case}_d" in g:
+            np.testing.assert_allclose(d[0], g[f"{case}_d"][0], rtol=1e-15)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantiser_ranges_and_reconstruction(bits):
+    rng = np.random.default_rng(bits)
+    xt = rng.laplace(size=(16, 2048))
+    xt[:, :7] *= 30
+    q, d, pre = oracle.quant_act(xt, bits)
+    lo, hi = (-128, 127) if bits == 8 else (-8, 7)
+    assert q.min() >= lo and q.max() <= hi
+    unclipped = (pre >= lo - 0.5) & (pre <= hi + 0.5)
+    err = np.abs(xt - q * d[:, None])
+    assert np.all(err[unclipped] <= (d[:, None] / 2 * (1 + 1e-12) + 1e-300).repeat(xt.shape[1], 1)[unclipped])
+    if bits == 8:
+        # absmax maps the largest |x| of every token onto +-127; -128 unreachable
+        assert np.all(np.abs(q).max(axis=1) == 127)
+        assert q.min() >= -127
+        np.testing.assert_allclose(d, np.abs(xt).max(axis=1) / 127, rtol=1e-15)
+    else:
+        np.testing.assert_allclose(d, np.abs(xt).mean(axis=1) / math.sqrt(7), rtol=1e-14)
+
+
+def test_int4_code_edges_gaussian():
+    """For exactly Gaussian x (sigma 1), beta = sqrt(2/pi) and the multiplier is
+    sqrt 7 / beta, so code 7 <=> x > 6.5 beta / sqrt 7 = 1.96023 (P = 0.024984)
+    and code -8 <=> x <= -7.5 beta / sqrt 7 = -2.26180 (P = 0.011856)."""
+    rng = np.random.default_rng(11)
+    xt = rng.normal(size=(64, 16384))
+    q, d, _ = oracle.quant_act(xt, 4)
+    assert abs(np.mean(q == 7) - 0.024984) < 0.0007
+    assert abs(np.mean(q == -8) - 0.011856) < 0.0005
+
+
+# ----------------------------------------------------------------- ternary weights
+
+def test_ternary_hand_golden():
+    g = read_golden("ternary_hand.txt")
+    wt, alpha = oracle.quantize_weights(np.array(g["a_w"], np.float32).reshape(2, 4))
+    assert alpha == np.float32(g["a_alpha"][0])
+    np.testing.assert_array_equal(wt.ravel(), g["a_codes"])
+    wt, alpha = oracle.quantize_weights(np.array(g["b_w"], np.float32).reshape(1, 4))
+    assert alpha == np.float32(g["b_alpha"][0])
+    np.testing.assert_array_equal(wt.ravel(), g["b_codes"])
+
+
+def test_ternary_statistics_gaussian():
+    rng = np.random.default_rng(3)
+    w = rng.normal(0, 0.02, (256, 1024)).astype(np.float32)
+    wt, alpha = oracle.quantize_weights(w)
+    assert set(np.unique(wt)) <= {-1, 0, 1}
+    # E|w| = sigma sqrt(2/pi)
+    assert abs(alpha / (0.02 * math.sqrt(2 / math.pi)) - 1) < 0.01
+    # P(|z| <= 0.5 sqrt(2/pi)) = 2 Phi(0.39894) - 1 = 0.31006
+    assert abs(np.mean(wt == 0) - 0.31006) < 0.005
+    # threshold form: nonzero iff |w| > a/2, sign kept
+    a = oracle.weight_scale(alpha)
+    np.testing.assert_array_equal(wt != 0, np.abs(w.astype(np.float64)) > a / 2)
+    np.testing.assert_array_equal(wt[wt != 0], np.sign(w[wt != 0]))
+
+
+def test_ternary_constant_and_zero():
+    wt, alpha = oracle.quantize_weights(np.full((4, 8), -0.3, np.float32))
+    assert alpha == np.float32(0.3) or abs(alpha - 0.3) < 1e-7
+    assert np.all(wt == -1)
+    wt, alpha = oracle.quantize_weights(np.zeros((2, 8), np.float32))
+    assert alpha == 0 and np.all(wt == 0)
+    assert oracle.weight_scale(alpha) == float(np.float32(1e-5))
+
+
+# ----------------------------------------------------------------- GEMM / dequant
+
+def test_gemm_brute_force_and_closed_forms():
+    rng = np.random.default_rng(5)
+    q = rng.integers(-128, 128, (7, 96)).astype(np.int8)
+    wt = rng.integers(-1, 2, (5, 96)).astype(np.int8)
+    acc = oracle.gemm_ternary(q, wt)
+    brute = np.array([[sum(int(q[m, k]) * int(wt[n, k]) for k in range(96)) for n in range(5)] for m in range(7)])
+    np.testing.assert_array_equal(acc, brute)
+    # all-ones codes give the weight row sums; extreme magnitudes stay exact in int32
+    K = 32768
+    ones = np.ones((1, K), np.int8)
+    wt2 = np.ones((2, K), np.int8); wt2[1] = -1
+    np.testing.assert_array_equal(oracle.gemm_ternary(ones * -128, wt2), [[-128 * K, 128 * K]])
+
+
+def test_dequant_closed_form():
+    acc = np.array([[3, -5], [0, 127]], np.int32)
+    d = np.array([0.5, 2.0])
+    y = oracle.dequant(acc, d, np.float32(0.25))
+    np.testing.assert_array_equal(y, [[0.375, -0.625], [0.0, 63.5]])
+
+
+# ----------------------------------------------------------------- whole layer
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("K,j,c", [(256, 0, 2.5), (256, 77, 1e-3), (4096, 3001, 40.0)])
+def test_one_hot_layer_closed_form(bits, K, j, c):
+    """x = c e_j: every rotated entry has magnitude v = c / sqrt(c^2 + K eps),
+    so codes are +-127 (INT8) or +-3 (INT4, round(sqrt 7)) with the sign of
+    the Walsh function, and y_n = v a S_n (INT8) or 3 v a S_n / sqrt 7 (INT4),
+    S_n = sum_k W_t[n, k] (-1)^popcount(k & j)."""
+    N = 24
+    rng = np.random.default_rng(K + j)
+    w = rng.normal(0, 0.02, (N, K)).astype(np.float32)
+    wt, alpha = oracle.quantize_weights(w)
+    a = float(alpha)
+    x = np.zeros((1, K), np.float32); x[0, j] = c
+    cf = float(np.float32(c))
+    v = cf / math.sqrt(cf * cf + K * 1e-6)
+    walsh = np.array([popcount_sign(k, j) for k in range(K)])
+    S = wt.astype(np.float64) @ walsh
+    out = oracle.forward(x, wt, alpha, bits)
+    np.testing.assert_allclose(np.abs(out["xt"][0]), v, rtol=1e-12)
+    if bits == 8:
+        np.testing.assert_array_equal(out["q"][0], 127 * walsh)
+        np.testing.assert_allclose(out["y"][0], v * a * S, rtol=1e-12, atol=1e-15)
+    else:
+        np.testing.assert_array_equal(out["q"][0], 3 * walsh)
+        np.testing.assert_allclose(out["y"][0], 3 * v * a * S / math.sqrt(7), rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_brute_force_dense_small(bits):
+    """Tiny inputs against an independent dense-matrix implementation."""
+    rng = np.random.default_rng(21 + bits)
+    M, K, N = 4, 16, 4
+    x = rng.normal(size=(M, K)).astype(np.float32)
+    x[:, 3] *= 20
+    g = synthetic.make_gain(K, 1)
+    wl = rng.normal(0, 0.02, (N, K)).astype(np.float32)
+    wt, alpha = oracle.quantize_weights(wl)
+    out = oracle.forward(x, wt, alpha, bits, g=g)
+    H = dense_sylvester(K) / math.sqrt(K)
+    xd = x.astype(np.float64)
+    u = xd * g / np.sqrt(np.mean(xd ** 2, axis=1, keepdims=True) + 1e-6)
+    xt = u @ H.T
+    if bits == 8:
+        G = np.maximum(np.abs(xt).max(1), 1e-5); Q = 127.0; lo, hi = -128, 127
+    else:
+        G = np.maximum(np.abs(xt).mean(1), 1e-5); Q = math.sqrt(7); lo, hi = -8, 7
+    q = np.clip(np.round(xt * (Q / G)[:, None]), lo, hi)
+    y = (q @ wt.T.astype(np.float64)) * (G / Q)[:, None] * a_of(alpha)
+    np.testing.assert_allclose(out["xt"], xt, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(out["q"], q)
+    np.testing.assert_allclose(out["y"], y, rtol=1e-13, atol=1e-16)
+
+
+def a_of(alpha):
+    return max(float(alpha), float(np.float32(1e-5)))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_layer_invariants(bits):
+    w = synthetic.WORKLOADS["tiny_int8"]
+    x, _, wl = synthetic.make_inputs(w)
+    wt, alpha = oracle.quantize_weights(wl)
+    y = oracle.forward(x, wt, alpha, bits)["y"]
+    # token independence: permuting rows permutes outputs exactly
+    perm = np.random.default_rng(0).permutation(x.shape[0])
+    np.testing.assert_array_equal(oracle.forward(x[perm], wt, alpha, bits)["y"], y[perm])
+    if bits == 8:
+        # symmetric absmax + round-half-even: the layer is exactly odd
+        np.testing.assert_array_equal(oracle.forward(-x, wt, alpha, bits)["y"], -y)
+    # a zero token gives a zero output
+    z = oracle.forward(np.zeros((1, x.shape[1]), np.float32), wt, alpha, bits)
+    assert np.all(z["y"] == 0) and np.all(z["q"] == 0)
+
+
+# ----------------------------------------------------------------- the method's claim
+
+@pytest.mark.parametrize("name", ["wo_1p3b_int4", "wdown_3b_int4", "wdown_7b_int4"])
+def test_hadamard_tames_outlier_channels(name):
+    """The rotation turns sharp, outlier-heavy activations into Gaussian-like
+    ones (QbitAI article, section 引入H-BitLinear模块; 新智元 article, Figures
+    2-3 discussion): per-token max/rms drops and INT4 error falls."""
+    w = synthetic.WORKLOADS[name]
+    x, _, _ = synthetic.make_inputs(w, M=32, with_weights=False)
+    u = oracle.rmsnorm(x)
+    xt = oracle.hadamard_rotate(u)
+    def peak_ratio(v):
+        return np.mean(np.abs(v).max(1) / np.sqrt(np.mean(v ** 2, 1)))
+    assert peak_ratio(xt) / peak_ratio(u) < 0.3
+    def rel_mse(v):
+        q, d, _ = oracle.quant_act(v, 4)
+        return np.mean((v - q * d[:, None]) ** 2) / np.mean(v ** 2)
+    assert rel_mse(xt) / rel_mse(u) < 0.1

@@ -1,0 +1,183 @@
+"""Python binding of libhbl.so, the H-BitLinear (BitNet v2) forward for MI355X.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  The binding
+never falls back to another implementation: a missing library or a non-gfx950
+device raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhbl.so")
+HEADER = os.path.join(_HERE, "..", "include", "hbl.h")
+
+HBL_F32, HBL_BF16 = 0, 1
+OP_QUANTIZE_WEIGHTS, OP_MATMUL, OP_FORWARD_INT4, OP_FORWARD_INT8 = 0, 1, 4, 8
+STATUS = {0: "HBL_OK", 1: "HBL_ERR_NULL", 2: "HBL_ERR_SHAPE", 3: "HBL_ERR_DTYPE", 4: "HBL_ERR_ALIGN",
+          5: "HBL_ERR_WORKSPACE", 6: "HBL_ERR_LAUNCH", 7: "HBL_ERR_DEVICE"}
+
+
+class HBLError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}")
+
+
+_lib = None
+P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "hbl_status_string": ([I], ctypes.c_char_p),
+    "hbl_workspace_bytes": ([I, I64, I64, I64], SZ),
+    "hbl_quantize_weights": ([P, I64, I64, P, P, P, SZ, P], I),
+    "hbl_forward_int8": ([P, I, P, P, P, I64, I64, I64, P, I, P, SZ, P], I),
+    "hbl_forward_int4": ([P, I, P, P, P, I64, I64, I64, P, I, P, SZ, P], I),
+    "hbl_quantize_act": ([P, I, P, I64, I64, I, P, P, P], I),
+    "hbl_matmul_dequant": ([P, I, P, P, P, I64, I64, I64, P, I, P, SZ, P], I),
+    "hbl_rmsnorm_fwht": ([P, I, P, I64, I64, P, P], I),
+    "hbl_gemm_ternary": ([P, I, P, I64, I64, I64, P, P, SZ, P], I),
+    "hbl_unpack_weights": ([P, I64, I64, P, P], I),
+}
+
+
+def declared_symbols() -> list:
+    """Entry points declared in include/hbl.h."""
+    with open(HEADER) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^\s*(?:hbl_status|size_t|const char \*)\s*\*?\s*(hbl_\w+)\s*\(", src, re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhbl.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with hadamard_rotated_ternary_amd/build.py "
+                               "(or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes, fn.restype = args, res
+        _lib = L
+    return _lib
+
+
+def _call(name, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != 0:
+        raise HBLError(name, rc)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return HBL_F32
+    if dt == torch.bfloat16:
+        return HBL_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _dev(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def workspace_bytes(op: int, M: int, K: int, N: int) -> int:
+    return int(lib().hbl_workspace_bytes(op, M, K, N))
+
+
+def _workspace(nbytes, device, workspace=None):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def quantize_weights(w: torch.Tensor):
+    """Latent fp32 weights [N][K] -> (packed uint8 [N][K/4], alpha fp32 [1])."""
+    _dev(w, "w")
+    N, K = w.shape
+    wp = torch.empty((N, K // 4), dtype=torch.uint8, device=w.device)
+    alpha = torch.empty(4, dtype=torch.float32, device=w.device)[:1]
+    ws = _workspace(workspace_bytes(OP_QUANTIZE_WEIGHTS, 0, K, N), w.device)
+    _call("hbl_quantize_weights", _ptr(w), N, K, _ptr(wp), _ptr(alpha), _ptr(ws), ws.numel(), _stream())
+    return wp, alpha
+
+
+def forward(x: torch.Tensor, w_packed: torch.Tensor, w_alpha: torch.Tensor, bits: int,
+            gain: torch.Tensor | None = None, out_dtype=None, workspace=None, out=None) -> torch.Tensor:
+    """Whole H-BitLinear forward: x [M][K] (fp32/bf16) -> y [M][N]."""
+    _dev(x, "x")
+    M, K = x.shape
+    N = w_packed.shape[0]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    y = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
+    op = OP_FORWARD_INT8 if bits == 8 else OP_FORWARD_INT4
+    ws = _workspace(workspace_bytes(op, M, K, N), x.device, workspace)
+    fn = "hbl_forward_int8" if bits == 8 else "hbl_forward_int4"
+    _call(fn, _ptr(x), _dtype_code(x.dtype), _ptr(gain), _ptr(w_packed), _ptr(w_alpha), M, K, N,
+          _ptr(y), _dtype_code(out_dtype), _ptr(ws), ws.numel(), _stream())
+    return y
+
+
+def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None):
+    """Stage 1: x [M][K] -> (codes, per-token scales fp32 [M])."""
+    _dev(x, "x")
+    M, K = x.shape
+    codes = torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
+                        device=x.device)
+    d = torch.empty(M + 4, dtype=torch.float32, device=x.device)[:M]
+    _call("hbl_quantize_act", _ptr(x), _dtype_code(x.dtype), _ptr(gain), M, K, bits, _ptr(codes), _ptr(d),
+          _stream())
+    return codes, d
+
+
+def matmul_dequant(codes, bits, dscale, w_packed, w_alpha, K, out_dtype=torch.bfloat16, workspace=None):
+    """Stage 2: codes -> y [M][N]."""
+    M = codes.shape[0]
+    N = w_packed.shape[0]
+    y = torch.empty((M, N), dtype=out_dtype, device=codes.device)
+    ws = _workspace(workspace_bytes(OP_MATMUL, M, K, N), codes.device, workspace)
+    _call("hbl_matmul_dequant", _ptr(codes), bits, _ptr(dscale), _ptr(w_packed), _ptr(w_alpha), M, K, N,
+          _ptr(y), _dtype_code(out_dtype), _ptr(ws), ws.numel(), _stream())
+    return y
+
+
+def rmsnorm_fwht(x: torch.Tensor, gain: torch.Tensor | None = None) -> torch.Tensor:
+    """Debug view: rotated normalised activations fp32 [M][K]."""
+    _dev(x, "x")
+    M, K = x.shape
+    xt = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    _call("hbl_rmsnorm_fwht", _ptr(x), _dtype_code(x.dtype), _ptr(gain), M, K, _ptr(xt), _stream())
+    return xt
+
+
+def gemm_ternary(codes, bits, w_packed, K, workspace=None) -> torch.Tensor:
+    """Debug view: exact int32 accumulators [M][N]."""
+    M = codes.shape[0]
+    N = w_packed.shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32, device=codes.device)
+    ws = _workspace(workspace_bytes(OP_MATMUL, M, K, N), codes.device, workspace)
+    _call("hbl_gemm_ternary", _ptr(codes), bits, _ptr(w_packed), M, K, N, _ptr(acc), _ptr(ws), ws.numel(),
+          _stream())
+    return acc
+
+
+def unpack_weights(w_packed: torch.Tensor, K: int) -> torch.Tensor:
+    N = w_packed.shape[0]
+    wt = torch.empty((N, K), dtype=torch.int8, device=w_packed.device)
+    _call("hbl_unpack_weights", _ptr(w_packed), N, K, _ptr(wt), _stream())
+    return wt

@@ -1,0 +1,44 @@
+// Shared device helpers for the H-BitLinear kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define HBL_DEV __device__ __forceinline__
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+namespace hbl {
+
+constexpr float kEpsNorm = 1e-6f;   // RMSNorm epsilon, added to the mean square
+constexpr float kEpsQ = 1e-5f;      // floor of the per-token and per-tensor statistics
+constexpr float kQ8 = 127.0f;       // INT8 absmax: max|x| maps to code 127
+constexpr float kQ4 = 2.6457513110645906f;  // INT4 absmean multiplier sqrt(7), rounded to fp32
+// Adding 1.5 * 2^23 rounds a float of magnitude < 2^22 to the nearest integer
+// (ties to even, by the adder) and leaves that integer in the low mantissa bits.
+constexpr float kRoundMagic = 12582912.0f;
+
+HBL_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+HBL_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 with round-half-to-even (finite inputs).
+HBL_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int W>
+HBL_DEV float xor_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+template <int W>
+HBL_DEV float xor_max(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace hbl

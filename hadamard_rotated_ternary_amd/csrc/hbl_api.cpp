@@ -1,0 +1,224 @@
+// C ABI of the H-BitLinear forward: argument validation, workspace layout and
+// kernel dispatch.  Every check runs before any HIP call, so invalid calls
+// return without touching the device.
+#include "../../include/hbl.h"
+
+#include <hip/hip_runtime.h>
+#include <mutex>
+#include <string.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];  // 1 = gfx950, 0 = not supported
+
+hbl_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HBL_ERR_DEVICE;
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t p;
+    g_dev_ok[dev] = hipGetDeviceProperties(&p, dev) == hipSuccess && strncmp(p.gcnArchName, "gfx950", 6) == 0;
+  });
+  return g_dev_ok[dev] ? HBL_OK : HBL_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_exact(int64_t k) {
+  if (k <= 0 || (k & (k - 1)) != 0) return -1;
+  int l = 0;
+  while ((int64_t(1) << l) < k) ++l;
+  return l;
+}
+
+constexpr int64_t kMinK = 256, kMaxK = 16384;
+
+hbl_status check_shape(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || M >= (int64_t(1) << 31)) return HBL_ERR_SHAPE;
+  if (log2_exact(K) < 0 || K < kMinK || K > kMaxK) return HBL_ERR_SHAPE;
+  if (N <= 0 || N % 16 != 0 || N >= (int64_t(1) << 31)) return HBL_ERR_SHAPE;
+  if (M * (K > N ? K : N) >= (int64_t(1) << 40)) return HBL_ERR_SHAPE;
+  return HBL_OK;
+}
+
+bool valid_dtype(hbl_dtype d) { return d == HBL_F32 || d == HBL_BF16; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Forward workspace: [codes][scales][matmul scratch].
+size_t codes_bytes(int bits, int64_t M, int64_t K) { return align256((size_t)M * K * bits / 8); }
+size_t scales_bytes(int64_t M) { return align256((size_t)M * 4); }
+
+hbl_status launched(hipError_t e) { return e == hipSuccess ? HBL_OK : HBL_ERR_LAUNCH; }
+
+hbl_status forward(int bits, const void* x, hbl_dtype x_dtype, const float* gain, const uint8_t* w_packed,
+                   const float* w_alpha, int64_t M, int64_t K, int64_t N, void* y, hbl_dtype y_dtype,
+                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return HBL_ERR_DTYPE;
+  if (hbl_status s = check_shape(M, K, N)) return s;
+  if (M == 0) return HBL_OK;
+  if (!x || !w_packed || !w_alpha || !y || !workspace) return HBL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_packed) || !aligned16(w_alpha) || !aligned16(y) || !aligned16(workspace) ||
+      (gain && !aligned16(gain)))
+    return HBL_ERR_ALIGN;
+  if (ws_bytes < hbl_workspace_bytes(bits == 8 ? HBL_OP_FORWARD_INT8 : HBL_OP_FORWARD_INT4, M, K, N))
+    return HBL_ERR_WORKSPACE;
+  if (hbl_status s = check_device()) return s;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* codes = ws;
+  float* dscale = reinterpret_cast<float*>(ws + codes_bytes(bits, M, K));
+  void* gws = ws + codes_bytes(bits, M, K) + scales_bytes(M);
+  const size_t gws_bytes = hbl::gemm_workspace_bytes(M, K, N);
+
+  hbl::PrepArgs p{};
+  p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.logk = log2_exact(K);
+  p.bits = bits; p.mode = 0; p.codes = codes; p.dscale = dscale; p.xt = nullptr;
+  // The prep kernel also clears the matmul's split-K counters.
+  p.zero_n = hbl::gemm_zero_words(M, K, N);
+  p.zero_ptr = p.zero_n ? hbl::gemm_counters(gws, M, K, N) : nullptr;
+  p.stream = stream;
+  if (hipError_t e = hbl::launch_prep(p)) return launched(e);
+
+  hbl::GemmArgs g{};
+  g.codes = codes; g.bits = bits; g.wpack = w_packed; g.dscale = dscale; g.walpha = w_alpha; g.out = y;
+  g.out_kind = y_dtype == HBL_BF16 ? hbl::OUT_BF16 : hbl::OUT_F32;
+  g.M = (int)M; g.N = (int)N; g.K = (int)K; g.ws = gws; g.ws_bytes = gws_bytes; g.stream = stream;
+  return launched(hbl::launch_gemm(g));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hbl_status_string(hbl_status s) {
+  switch (s) {
+    case HBL_OK: return "ok";
+    case HBL_ERR_NULL: return "null pointer";
+    case HBL_ERR_SHAPE: return "unsupported shape";
+    case HBL_ERR_DTYPE: return "unsupported dtype or bit width";
+    case HBL_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case HBL_ERR_WORKSPACE: return "workspace too small";
+    case HBL_ERR_LAUNCH: return "kernel launch failed";
+    case HBL_ERR_DEVICE: return "no gfx950 device";
+  }
+  return "unknown status";
+}
+
+size_t hbl_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K <= 0 || N <= 0) return 0;
+  switch (op) {
+    case HBL_OP_QUANTIZE_WEIGHTS: return align256((size_t)N * 8);
+    case HBL_OP_MATMUL: return align256(hbl::gemm_workspace_bytes(M, K, N));
+    case HBL_OP_FORWARD_INT8:
+    case HBL_OP_FORWARD_INT4: {
+      const int bits = op == HBL_OP_FORWARD_INT8 ? 8 : 4;
+      return codes_bytes(bits, M, K) + scales_bytes(M) + align256(hbl::gemm_workspace_bytes(M, K, N));
+    }
+    default: return 0;
+  }
+}
+
+hbl_status hbl_quantize_weights(const float* w, int64_t N, int64_t K, uint8_t* w_packed, float* w_alpha,
+                                void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!w || !w_packed || !w_alpha || !workspace) return HBL_ERR_NULL;
+  if (hbl_status s = check_shape(0, K, N)) return s;
+  if (!aligned16(w) || !aligned16(w_packed) || !aligned16(w_alpha) || !aligned16(workspace)) return HBL_ERR_ALIGN;
+  if (ws_bytes < hbl_workspace_bytes(HBL_OP_QUANTIZE_WEIGHTS, 0, K, N)) return HBL_ERR_WORKSPACE;
+  if (hbl_status s = check_device()) return s;
+  hbl::WquantArgs a{w, (int)N, (int)K, w_packed, w_alpha, static_cast<double*>(workspace), stream};
+  return launched(hbl::launch_wquant(a));
+}
+
+hbl_status hbl_forward_int8(const void* x, hbl_dtype x_dtype, const float* gain, const uint8_t* w_packed,
+                            const float* w_alpha, int64_t M, int64_t K, int64_t N, void* y, hbl_dtype y_dtype,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return forward(8, x, x_dtype, gain, w_packed, w_alpha, M, K, N, y, y_dtype, workspace, ws_bytes, stream);
+}
+
+hbl_status hbl_forward_int4(const void* x, hbl_dtype x_dtype, const float* gain, const uint8_t* w_packed,
+                            const float* w_alpha, int64_t M, int64_t K, int64_t N, void* y, hbl_dtype y_dtype,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return forward(4, x, x_dtype, gain, w_packed, w_alpha, M, K, N, y, y_dtype, workspace, ws_bytes, stream);
+}
+
+hbl_status hbl_quantize_act(const void* x, hbl_dtype x_dtype, const float* gain, int64_t M, int64_t K, int bits,
+                            void* codes, float* dscale, hipStream_t stream) {
+  if (!valid_dtype(x_dtype) || (bits != 8 && bits != 4)) return HBL_ERR_DTYPE;
+  if (hbl_status s = check_shape(M, K, 16)) return s;
+  if (M == 0) return HBL_OK;
+  if (!x || !codes || !dscale) return HBL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(dscale) || (gain && !aligned16(gain))) return HBL_ERR_ALIGN;
+  if (hbl_status s = check_device()) return s;
+  hbl::PrepArgs p{};
+  p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.logk = log2_exact(K);
+  p.bits = bits; p.mode = 0; p.codes = static_cast<uint8_t*>(codes); p.dscale = dscale; p.stream = stream;
+  return launched(hbl::launch_prep(p));
+}
+
+hbl_status hbl_rmsnorm_fwht(const void* x, hbl_dtype x_dtype, const float* gain, int64_t M, int64_t K, float* xt,
+                            hipStream_t stream) {
+  if (!valid_dtype(x_dtype)) return HBL_ERR_DTYPE;
+  if (hbl_status s = check_shape(M, K, 16)) return s;
+  if (M == 0) return HBL_OK;
+  if (!x || !xt) return HBL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xt) || (gain && !aligned16(gain))) return HBL_ERR_ALIGN;
+  if (hbl_status s = check_device()) return s;
+  hbl::PrepArgs p{};
+  p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.logk = log2_exact(K);
+  p.bits = 8; p.mode = 1; p.xt = xt; p.stream = stream;
+  return launched(hbl::launch_prep(p));
+}
+
+static hbl_status matmul(const void* codes, int bits, const float* dscale, const uint8_t* w_packed,
+                         const float* w_alpha, int64_t M, int64_t K, int64_t N, void* out, int out_kind,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (bits != 8 && bits != 4) return HBL_ERR_DTYPE;
+  if (hbl_status s = check_shape(M, K, N)) return s;
+  if (M == 0) return HBL_OK;
+  if (!codes || !w_packed || !out) return HBL_ERR_NULL;
+  if (out_kind != hbl::OUT_ACC_I32 && (!dscale || !w_alpha)) return HBL_ERR_NULL;
+  const size_t need = align256(hbl::gemm_workspace_bytes(M, K, N));
+  if (need && !workspace) return HBL_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(w_packed) || !aligned16(out) || (dscale && !aligned16(dscale)) ||
+      (w_alpha && !aligned16(w_alpha)) || (workspace && !aligned16(workspace)))
+    return HBL_ERR_ALIGN;
+  if (ws_bytes < need) return HBL_ERR_WORKSPACE;
+  if (hbl_status s = check_device()) return s;
+  const int zn = hbl::gemm_zero_words(M, K, N);
+  if (zn) {
+    if (hipError_t e = hbl::launch_zero_i32(hbl::gemm_counters(workspace, M, K, N), zn, stream)) return launched(e);
+  }
+  hbl::GemmArgs g{};
+  g.codes = static_cast<const uint8_t*>(codes); g.bits = bits; g.wpack = w_packed; g.dscale = dscale;
+  g.walpha = w_alpha; g.out = out; g.out_kind = out_kind; g.M = (int)M; g.N = (int)N; g.K = (int)K;
+  g.ws = workspace; g.ws_bytes = ws_bytes; g.stream = stream;
+  return launched(hbl::launch_gemm(g));
+}
+
+hbl_status hbl_matmul_dequant(const void* codes, int bits, const float* dscale, const uint8_t* w_packed,
+                              const float* w_alpha, int64_t M, int64_t K, int64_t N, void* y, hbl_dtype y_dtype,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(y_dtype)) return HBL_ERR_DTYPE;
+  return matmul(codes, bits, dscale, w_packed, w_alpha, M, K, N, y,
+                y_dtype == HBL_BF16 ? hbl::OUT_BF16 : hbl::OUT_F32, workspace, ws_bytes, stream);
+}
+
+hbl_status hbl_gemm_ternary(const void* codes, int bits, const uint8_t* w_packed, int64_t M, int64_t K, int64_t N,
+                            int32_t* acc, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return matmul(codes, bits, nullptr, w_packed, nullptr, M, K, N, acc, hbl::OUT_ACC_I32, workspace, ws_bytes,
+                stream);
+}
+
+hbl_status hbl_unpack_weights(const uint8_t* w_packed, int64_t N, int64_t K, int8_t* w_t, hipStream_t stream) {
+  if (!w_packed || !w_t) return HBL_ERR_NULL;
+  if (hbl_status s = check_shape(0, K, N)) return s;
+  if (!aligned16(w_packed) || !aligned16(w_t)) return HBL_ERR_ALIGN;
+  if (hbl_status s = check_device()) return s;
+  return launched(hbl::launch_unpack(w_packed, (int)N, (int)K, w_t, stream));
+}
+
+}  // extern "C"

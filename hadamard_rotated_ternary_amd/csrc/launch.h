@@ -1,0 +1,59 @@
+// Host-side launch descriptors shared by the C ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hbl {
+
+struct PrepArgs {
+  const void* x;
+  bool x_bf16;
+  const float* gain;
+  int M;
+  int logk;
+  int bits;          // 8 or 4
+  int mode;          // 0: codes + scales, 1: rotated activations (fp32)
+  uint8_t* codes;
+  float* dscale;
+  float* xt;
+  int* zero_ptr;     // optional int32 region cleared by the first workgroup
+  int zero_n;
+  hipStream_t stream;
+};
+hipError_t launch_prep(const PrepArgs& a);
+
+enum OutKind { OUT_ACC_I32 = 0, OUT_F32 = 1, OUT_BF16 = 2 };
+
+struct GemmArgs {
+  const uint8_t* codes;   // int8 [M][K] or int4 [M][K/2]
+  int bits;
+  const uint8_t* wpack;   // [N][K/4]
+  const float* dscale;    // [M]   (unused for OUT_ACC_I32)
+  const float* walpha;    // [1]   (unused for OUT_ACC_I32)
+  void* out;
+  int out_kind;
+  int M, N, K;
+  void* ws;               // split-K partials and counters (decode path)
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+hipError_t launch_gemm(const GemmArgs& a);
+// Workspace bytes the matmul needs beyond the codes and scales.
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+// Int32 words the matmul needs zeroed before it runs (decode counters), and where they are.
+int gemm_zero_words(int64_t M, int64_t K, int64_t N);
+int* gemm_counters(void* ws, int64_t M, int64_t K, int64_t N);
+hipError_t launch_zero_i32(int* p, int n, hipStream_t stream);
+
+struct WquantArgs {
+  const float* w;
+  int N, K;
+  uint8_t* wpack;
+  float* walpha;
+  double* rowsum;         // workspace [N]
+  hipStream_t stream;
+};
+hipError_t launch_wquant(const WquantArgs& a);
+hipError_t launch_unpack(const uint8_t* wpack, int N, int K, int8_t* wt, hipStream_t stream);
+
+}  // namespace hbl

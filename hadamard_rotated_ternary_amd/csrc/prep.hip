@@ -1,0 +1,364 @@
+// Fused RMSNorm -> online Walsh-Hadamard rotation -> per-token quantisation.
+//
+// QbitAI article on BitNet v2, section 引入H-BitLinear模块, and 新智元 article
+// "微软再放LLM量化大招", section H-BitLinear模块: the layer normalises the
+// activations, applies an orthogonal +-1 Hadamard transform computed by the
+// fast O(n log n) algorithm, then quantises each token (INT8 absmax or INT4
+// absmean) before the ternary matmul.
+//
+// One token of K = 2^LOGK features is spread over T = 2^(LOGK-LOGE) threads
+// holding E = 2^LOGE values each.  The Walsh-Hadamard transform is a product
+// of independent radix-2 butterflies, one per index bit, that may be applied
+// in any order; each "pass" applies the butterflies of the index bits that a
+// thread currently holds in registers, and an LDS exchange between passes
+// re-deals the index bits so that the not-yet-transformed ones land in
+// registers.  No shuffles are needed: every add/sub is register to register.
+//
+// RMSNorm's 1/r and the 1/sqrt(K) scale are per-token scalars that commute
+// with the transform, so the transform runs on x*g and both scalars are
+// applied once, folded into the quantiser multiplier.
+#include "common.h"
+
+namespace hbl {
+
+// ---------------------------------------------------------------------------
+// Compile-time bit dealing.
+struct PassBits {
+  int reg[8];   // index bit held by register-number bit i
+  int thr[16];  // index bit held by thread-number bit j
+  int fresh;    // register-number bits whose butterflies run in this pass
+};
+
+constexpr int num_passes(int logk, int loge) {
+  return 1 + ((logk - loge) + loge - 1) / loge;
+}
+
+// Pass 0 holds index bits {0,1,2} (8 contiguous features = one 16-byte load)
+// plus the top LOGE-3 bits; later passes take the middle bits upward, LOGE at
+// a time, padding the last one with the lowest already-transformed bits.
+constexpr PassBits pass_bits(int logk, int loge, int p) {
+  PassBits b{};
+  bool inreg[32] = {};
+  bool fresh[32] = {};
+  if (p == 0) {
+    for (int k = 0; k < 3; ++k) inreg[k] = fresh[k] = true;
+    for (int k = logk - (loge - 3); k < logk; ++k) inreg[k] = fresh[k] = true;
+  } else {
+    const int lo = 3 + (p - 1) * loge, hi = logk - (loge - 3);
+    int n = 0;
+    for (int k = lo; k < hi && n < loge; ++k) { inreg[k] = fresh[k] = true; ++n; }
+    for (int k = 0; k < logk && n < loge; ++k)
+      if (!inreg[k]) { inreg[k] = true; ++n; }
+  }
+  int i = 0, j = 0;
+  b.fresh = 0;
+  for (int k = 0; k < logk; ++k) {
+    if (inreg[k]) { if (fresh[k]) b.fresh |= 1 << i; b.reg[i++] = k; }
+    else b.thr[j++] = k;
+  }
+  return b;
+}
+
+template <int LOGK, int LOGE, int P>
+struct Pass {
+  static constexpr PassBits B = pass_bits(LOGK, LOGE, P);
+  static constexpr int LOGT = LOGK - LOGE;
+  // Register part of the feature index of register r (compile-time).
+  static constexpr int reg_idx(int r) {
+    int v = 0;
+    for (int i = 0; i < LOGE; ++i) if ((r >> i) & 1) v |= 1 << B.reg[i];
+    return v;
+  }
+  // Thread part of the feature index of thread tau.
+  static HBL_DEV int thr_idx(int tau) {
+    int v = 0;
+#pragma unroll
+    for (int j = 0; j < LOGT; ++j) v |= ((tau >> j) & 1) << B.thr[j];
+    return v;
+  }
+  static constexpr bool vec4 = B.reg[0] == 0 && B.reg[1] == 1;
+};
+
+// Padded LDS position of feature index i; thread and register parts of i
+// occupy disjoint bits, so pad(thr | reg) == pad(thr) + pad(reg).  The
+// padding makes every exchange of the shipped configurations free of bank
+// conflicts and keeps groups of 4 consecutive features 16-byte aligned.
+template <int P2>
+HBL_DEV constexpr int pad(int i) { return i + 4 * (i >> 5) + 4 * (i >> P2); }
+// Byte buffer used to gather the codes before the coalesced store.
+HBL_DEV constexpr int padb(int i) { return i + 16 * (i >> 10); }
+
+template <int LOGE, int FRESH>
+HBL_DEV void butterflies(float (&v)[1 << LOGE]) {
+#pragma unroll
+  for (int i = 0; i < LOGE; ++i) {
+    if (!((FRESH >> i) & 1)) continue;
+#pragma unroll
+    for (int r = 0; r < (1 << LOGE); ++r) {
+      if (r & (1 << i)) continue;
+      const float a = v[r], b = v[r | (1 << i)];
+      v[r] = a + b;
+      v[r | (1 << i)] = a - b;
+    }
+  }
+}
+
+template <int LOGK, int LOGE, int P2>
+struct PrepCfg {
+  static constexpr int K = 1 << LOGK, E = 1 << LOGE, LOGT = LOGK - LOGE, T = 1 << LOGT;
+  static constexpr int WG = T < 64 ? 64 : T;     // threads per workgroup
+  static constexpr int TPB = WG / T;             // tokens per workgroup
+  static constexpr int NP = num_passes(LOGK, LOGE);
+  static constexpr int REGION = pad<P2>(K - 1) + 1;  // floats per token
+  static_assert(LOGE >= 4 && LOGE <= 7, "4..7 register bits");
+  static_assert(REGION * 4 >= K + 16 * (K >> 10), "byte buffer must fit");
+};
+
+// Token-wide reductions: the T threads of a token are contiguous lanes of one
+// wave (T <= 64) or whole waves of a one-token workgroup (T > 64).
+template <int T, bool MAX>
+HBL_DEV float token_reduce(float v, float* red) {
+  constexpr int W = T < 64 ? T : 64;
+  v = MAX ? xor_max<W>(v) : xor_sum<W>(v);
+  if constexpr (T > 64) {
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    float s = red[0];
+#pragma unroll
+    for (int w = 1; w < T / 64; ++w) s = MAX ? fmaxf(s, red[w]) : s + red[w];
+    v = s;
+  }
+  return v;
+}
+
+// Exchange: registers dealt as pass P -> registers dealt as pass P+1.
+template <int LOGK, int LOGE, int P2, int P>
+HBL_DEV void exchange(float (&v)[1 << LOGE], float* region, int tau) {
+  using A = Pass<LOGK, LOGE, P>;
+  using Bn = Pass<LOGK, LOGE, P + 1>;
+  constexpr int E = 1 << LOGE;
+  const int wbase = pad<P2>(A::thr_idx(tau));
+  if constexpr (A::vec4) {
+#pragma unroll
+    for (int r = 0; r < E; r += 4)
+      *reinterpret_cast<float4*>(region + wbase + pad<P2>(A::reg_idx(r))) =
+          make_float4(v[r], v[r + 1], v[r + 2], v[r + 3]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < E; ++r) region[wbase + pad<P2>(A::reg_idx(r))] = v[r];
+  }
+  __syncthreads();
+  const int rbase = pad<P2>(Bn::thr_idx(tau));
+  if constexpr (Bn::vec4) {
+#pragma unroll
+    for (int r = 0; r < E; r += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(region + rbase + pad<P2>(Bn::reg_idx(r)));
+      v[r] = f.x; v[r + 1] = f.y; v[r + 2] = f.z; v[r + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < E; ++r) v[r] = region[rbase + pad<P2>(Bn::reg_idx(r))];
+  }
+  __syncthreads();
+}
+
+template <int LOGK, int LOGE, int P2, int P>
+HBL_DEV void run_passes(float (&v)[1 << LOGE], float* region, int tau) {
+  using C = PrepCfg<LOGK, LOGE, P2>;
+  butterflies<LOGE, Pass<LOGK, LOGE, P>::B.fresh>(v);
+  if constexpr (P + 1 < C::NP) {
+    exchange<LOGK, LOGE, P2, P>(v, region, tau);
+    run_passes<LOGK, LOGE, P2, P + 1>(v, region, tau);
+  }
+}
+
+// MODE 0: write codes + scales.  MODE 1: write the rotated activations (fp32).
+constexpr int prep_wg(int logk, int loge) { return (1 << (logk - loge)) < 64 ? 64 : (1 << (logk - loge)); }
+
+template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int MODE>
+__global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
+    const void* __restrict__ x, const float* __restrict__ gain, int M,
+    uint8_t* __restrict__ codes, float* __restrict__ dscale, float* __restrict__ xt,
+    int* __restrict__ zero_ptr, int zero_n) {
+  using C = PrepCfg<LOGK, LOGE, P2>;
+  using P0 = Pass<LOGK, LOGE, 0>;
+  using PL = Pass<LOGK, LOGE, C::NP - 1>;
+  constexpr int K = C::K, E = C::E, T = C::T;
+  __shared__ __attribute__((aligned(16))) float lds[C::REGION * C::TPB];
+  __shared__ float red[16];
+
+  if (zero_ptr != nullptr && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < zero_n; i += C::WG) zero_ptr[i] = 0;
+
+  const int tok = threadIdx.x / T;
+  const int tau = threadIdx.x % T;
+  const int m = blockIdx.x * C::TPB + tok;
+  const bool valid = m < M;
+  float* region = lds + tok * C::REGION;
+
+  // ---- load (pass-0 dealing: 8 contiguous features per 16-byte load)
+  float v[E];
+  const int base0 = P0::thr_idx(tau);
+#pragma unroll
+  for (int g = 0; g < E / 8; ++g) {
+    const int idx = base0 + P0::reg_idx(8 * g);
+    if constexpr (XBF16) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (valid) w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (size_t)m * K + idx);
+      v[8 * g + 0] = bf16_lo(w.x); v[8 * g + 1] = bf16_hi(w.x);
+      v[8 * g + 2] = bf16_lo(w.y); v[8 * g + 3] = bf16_hi(w.y);
+      v[8 * g + 4] = bf16_lo(w.z); v[8 * g + 5] = bf16_hi(w.z);
+      v[8 * g + 6] = bf16_lo(w.w); v[8 * g + 7] = bf16_hi(w.w);
+    } else {
+      float4 a = make_float4(0, 0, 0, 0), b = a;
+      if (valid) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)m * K + idx);
+        a = p[0]; b = p[1];
+      }
+      v[8 * g + 0] = a.x; v[8 * g + 1] = a.y; v[8 * g + 2] = a.z; v[8 * g + 3] = a.w;
+      v[8 * g + 4] = b.x; v[8 * g + 5] = b.y; v[8 * g + 6] = b.z; v[8 * g + 7] = b.w;
+    }
+  }
+  // ---- RMSNorm statistic (of x, before the gain)
+  float ss = 0.f;
+#pragma unroll
+  for (int r = 0; r < E; ++r) ss += v[r] * v[r];
+  ss = token_reduce<T, false>(ss, red);
+  if (gain != nullptr) {
+#pragma unroll
+    for (int g = 0; g < E / 8; ++g) {
+      const int idx = base0 + P0::reg_idx(8 * g);
+      const float4* p = reinterpret_cast<const float4*>(gain + idx);
+      const float4 a = p[0], b = p[1];
+      v[8 * g + 0] *= a.x; v[8 * g + 1] *= a.y; v[8 * g + 2] *= a.z; v[8 * g + 3] *= a.w;
+      v[8 * g + 4] *= b.x; v[8 * g + 5] *= b.y; v[8 * g + 6] *= b.z; v[8 * g + 7] *= b.w;
+    }
+  }
+  // c = 1 / (r * sqrt(K)), r = sqrt(mean x^2 + eps)
+  const float rr = sqrtf(ss * (1.0f / K) + kEpsNorm);
+  const float c = 1.0f / (rr * sqrtf((float)K));
+
+  // ---- Walsh-Hadamard transform (unnormalised) of x*g
+  run_passes<LOGK, LOGE, P2, 0>(v, region, tau);
+
+  const int baseL = PL::thr_idx(tau);
+  if constexpr (MODE == 1) {
+    if (valid) {
+#pragma unroll
+      for (int r = 0; r < E; ++r) xt[(size_t)m * K + baseL + PL::reg_idx(r)] = v[r] * c;
+    }
+    return;
+  } else {
+    // ---- per-token statistic of the rotated token xt = v * c
+    float st = 0.f;
+    if constexpr (BITS == 8) {
+#pragma unroll
+      for (int r = 0; r < E; ++r) st = fmaxf(st, fabsf(v[r]));
+      st = token_reduce<T, true>(st, red);
+      st = st * c;
+    } else {
+#pragma unroll
+      for (int r = 0; r < E; ++r) st += fabsf(v[r]);
+      st = token_reduce<T, false>(st, red);
+      st = (st * (1.0f / K)) * c;
+    }
+    const float Q = BITS == 8 ? kQ8 : kQ4;
+    const float G = fmaxf(st, kEpsQ);
+    const float s = Q / G;
+    const float cs = c * s;
+    if (valid && tau == 0) dscale[m] = G / Q;
+
+    // ---- round to codes; gather them through LDS for coalesced stores
+    uint8_t* bytes = reinterpret_cast<uint8_t*>(region);
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      float q = v[r] * cs;
+      if constexpr (BITS == 4) q = fminf(fmaxf(q, -8.0f), 7.0f);
+      const float t = q + kRoundMagic;
+      bytes[padb(baseL + PL::reg_idx(r))] = (uint8_t)__float_as_uint(t);
+    }
+    __syncthreads();
+    if (!valid) return;
+    if constexpr (BITS == 8) {
+      // int8 codes: thread tau stores 16-byte chunks j*T + tau
+      uint8_t* out = codes + (size_t)m * K;
+#pragma unroll
+      for (int j = 0; j < E / 16; ++j) {
+        const int ch = j * T + tau;
+        const int b = padb(16 * ch);
+        const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + b);
+        *reinterpret_cast<uint4*>(out + 16 * ch) = make_uint4(s4[0], s4[1], s4[2], s4[3]);
+      }
+    } else {
+      // int4 codes: 8 consecutive codes per 32-bit word, code k0+4j+i at bits 8i+4j
+      uint8_t* out = codes + (size_t)m * (K / 2);
+      constexpr int OB = E / 2;  // output bytes per thread
+      if constexpr (OB >= 16) {
+#pragma unroll
+        for (int j = 0; j < OB / 16; ++j) {
+          const int ch = j * T + tau;  // 16 output bytes = 32 codes
+          const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(32 * ch));
+          uint32_t w[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = (s4[2 * i] & 0x0F0F0F0Fu) | ((s4[2 * i + 1] & 0x0F0F0F0Fu) << 4);
+          *reinterpret_cast<uint4*>(out + 16 * ch) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      } else {
+        static_assert(OB == 8, "E >= 16");
+        const int ch = tau;  // 8 output bytes = 16 codes
+        const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(16 * ch));
+        uint32_t w0 = (s4[0] & 0x0F0F0F0Fu) | ((s4[1] & 0x0F0F0F0Fu) << 4);
+        uint32_t w1 = (s4[2] & 0x0F0F0F0Fu) | ((s4[3] & 0x0F0F0F0Fu) << 4);
+        *reinterpret_cast<uint2*>(out + 8 * ch) = make_uint2(w0, w1);
+      }
+    }
+  }
+}
+
+}  // namespace hbl
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (called from the C ABI layer).
+#include "launch.h"
+
+namespace hbl {
+
+template <int LOGK, int LOGE, int P2>
+static hipError_t launch_prep_t(const PrepArgs& a) {
+  using C = PrepCfg<LOGK, LOGE, P2>;
+  const int grid = (a.M + C::TPB - 1) / C::TPB;
+  if (grid == 0) return hipSuccess;
+#define HBL_PREP(BITS, BF, MODE)                                                           \
+  hipLaunchKernelGGL((prep_kernel<LOGK, LOGE, P2, BITS, BF, MODE>), dim3(grid), dim3(C::WG), 0, \
+                     a.stream, a.x, a.gain, a.M, a.codes, a.dscale, a.xt, a.zero_ptr, a.zero_n)
+  if (a.mode == 1) {
+    if (a.x_bf16) HBL_PREP(8, true, 1); else HBL_PREP(8, false, 1);
+  } else if (a.bits == 8) {
+    if (a.x_bf16) HBL_PREP(8, true, 0); else HBL_PREP(8, false, 0);
+  } else {
+    if (a.x_bf16) HBL_PREP(4, true, 0); else HBL_PREP(4, false, 0);
+  }
+#undef HBL_PREP
+  return hipGetLastError();
+}
+
+// Dealing per K: one LDS exchange for the prefill shapes (E >= T), more
+// threads per token for small M so a single token is not latency bound.
+hipError_t launch_prep(const PrepArgs& a) {
+  const bool small = a.M <= 64;
+  switch (a.logk) {
+    case 8:  return launch_prep_t<8, 4, 6>(a);
+    case 9:  return launch_prep_t<9, 5, 6>(a);
+    case 10: return launch_prep_t<10, 5, 7>(a);
+    case 11: return launch_prep_t<11, 6, 7>(a);
+    case 12: return small ? launch_prep_t<12, 4, 6>(a) : launch_prep_t<12, 6, 8>(a);
+    case 13: return small ? launch_prep_t<13, 4, 6>(a) : launch_prep_t<13, 7, 8>(a);
+    case 14: return small ? launch_prep_t<14, 4, 6>(a) : launch_prep_t<14, 7, 9>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace hbl

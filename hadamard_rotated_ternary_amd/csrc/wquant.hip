@@ -1,0 +1,102 @@
+// Offline per-tensor absmean ternarisation of latent weights and 2-bit packing.
+//
+// QbitAI article on BitNet v2, section 引入H-BitLinear模块, and 新智元 article
+// "微软再放LLM量化大招", section H-BitLinear模块: weights are mapped to
+// {-1, 0, 1} with a single per-tensor scale, the mean of |W|.
+//
+// The sum of |W| is taken in fp64 in a fixed order (each row left to right,
+// then the row sums in row order) so alpha is reproducible to the last bit.
+// Code(w) = round-half-even(w / a) clamped to [-1, 1] is nonzero exactly when
+// |w| > a / 2 (a tie rounds to 0), and 0.5f * a is exact in fp32, so the
+// kernel decides with one comparison instead of a division.
+#include "common.h"
+#include "launch.h"
+
+namespace hbl {
+
+// Row sums of |w| in fp64, strictly in column order.  A 64-thread workgroup
+// owns 64 rows; tiles of 64x64 are staged through LDS with coalesced loads,
+// then each thread walks its own row.
+__global__ __launch_bounds__(64) void wrowsum_kernel(const float* __restrict__ w, int N, int K,
+                                                    double* __restrict__ rowsum) {
+  __shared__ float tile[64][65];
+  const int t = threadIdx.x;
+  const int n0 = blockIdx.x * 64;
+  double acc = 0.0;
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    for (int r = 0; r < 64; ++r) {
+      const int n = n0 + r;
+      tile[r][t] = (n < N && k0 + t < K) ? w[(size_t)n * K + k0 + t] : 0.0f;
+    }
+    __syncthreads();
+    const int kend = K - k0 < 64 ? K - k0 : 64;
+    for (int c = 0; c < kend; ++c) acc += (double)fabsf(tile[t][c]);
+    __syncthreads();
+  }
+  if (n0 + t < N) rowsum[n0 + t] = acc;
+}
+
+// alpha = fp32(sum_n rowsum[n] / (N K)), summed in row order by one thread.
+__global__ void walpha_kernel(const double* __restrict__ rowsum, int N, int K, float* __restrict__ walpha) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  double s = 0.0;
+  for (int n = 0; n < N; ++n) s += rowsum[n];
+  walpha[0] = (float)(s / ((double)N * (double)K));
+}
+
+// One thread per packed 32-bit word (16 consecutive k of one row).
+__global__ __launch_bounds__(256) void wpack_kernel(const float* __restrict__ w, int N, int K,
+                                                   const float* __restrict__ walpha,
+                                                   uint32_t* __restrict__ wpack) {
+  const size_t words = (size_t)N * (K / 16);
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= words) return;
+  const float a = fmaxf(walpha[0], kEpsQ);
+  const float half = 0.5f * a;
+  const float4* src = reinterpret_cast<const float4*>(w + q * 16);
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float4 f = src[j];
+    const float e[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // element 4j+i of this group of 16: k0 + 4j + i -> bits 8i + 2j
+      const float x = e[i];
+      const uint32_t code = fabsf(x) > half ? (x > 0.f ? 1u : 3u) : 0u;
+      word |= code << (8 * i + 2 * j);
+    }
+  }
+  wpack[q] = word;
+}
+
+__global__ __launch_bounds__(256) void wunpack_kernel(const uint32_t* __restrict__ wpack, int N, int K,
+                                                     int8_t* __restrict__ wt) {
+  const size_t words = (size_t)N * (K / 16);
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= words) return;
+  const uint32_t p = wpack[q];
+  uint32_t out[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    out[j] = __builtin_amdgcn_perm(0u, 0xFF000100u, (p >> (2 * j)) & 0x03030303u);
+  *reinterpret_cast<uint4*>(wt + q * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+hipError_t launch_wquant(const WquantArgs& a) {
+  hipLaunchKernelGGL(wrowsum_kernel, dim3((a.N + 63) / 64), dim3(64), 0, a.stream, a.w, a.N, a.K, a.rowsum);
+  hipLaunchKernelGGL(walpha_kernel, dim3(1), dim3(64), 0, a.stream, a.rowsum, a.N, a.K, a.walpha);
+  const size_t words = (size_t)a.N * (a.K / 16);
+  hipLaunchKernelGGL(wpack_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, a.stream, a.w, a.N,
+                     a.K, a.walpha, reinterpret_cast<uint32_t*>(a.wpack));
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t* wpack, int N, int K, int8_t* wt, hipStream_t stream) {
+  const size_t words = (size_t)N * (K / 16);
+  hipLaunchKernelGGL(wunpack_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint32_t*>(wpack), N, K, wt);
+  return hipGetLastError();
+}
+
+}  // namespace hbl

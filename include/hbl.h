@@ -1,0 +1,174 @@
+/*
+ * hbl.h -- C ABI of the H-BitLinear forward pass (BitNet v2) for AMD MI355X (gfx950).
+ *
+ * The layer (QbitAI article on BitNet v2, section 引入H-BitLinear模块; 新智元
+ * article "微软再放LLM量化大招", sections BitNet v2：原生4位激活 and H-BitLinear模块):
+ *
+ *     y = dequant( Q_act( H_K . RMSNorm(x) / sqrt(K) ) . W_t^T )
+ *
+ *   RMSNorm    r_m = sqrt(mean_k x[m][k]^2 + 1e-6),  u = x * g / r_m   (g = 1 if gain == NULL)
+ *   rotation   online Walsh-Hadamard transform over K, Sylvester order, scaled by 1/sqrt(K)
+ *   INT8       per-token absmax:  G = max(max_k |xt|, 1e-5), q = round(xt * 127 / G), d = G / 127
+ *   INT4       per-token absmean: G = max(mean_k |xt|, 1e-5), q = clamp(round(xt * sqrt7 / G), -8, 7),
+ *              d = G / sqrt7
+ *   weights    per-tensor absmean ternary: alpha = mean |W|, a = max(alpha, 1e-5),
+ *              W_t = clamp(round(W / a), -1, 1)   (done once, offline)
+ *   matmul     acc[m][n] = sum_k q[m][k] * W_t[n][k]   (exact int32)
+ *   dequant    y[m][n] = acc[m][n] * (d[m] * a)
+ * Rounding is round-half-to-even.  The HIP path computes the normalisation,
+ * rotation and scales in fp32.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates or frees memory.  Tensors are dense row-major.
+ *   - Every call is asynchronous on `stream` (NULL = default stream) and does
+ *     no host synchronisation; outputs are valid once the stream reaches them.
+ *   - Arguments are validated before anything is launched.  On any error
+ *     nothing is launched and outputs are untouched.  Launch failures are
+ *     reported as HBL_ERR_LAUNCH.  Nothing aborts or throws across the ABI.
+ *   - M == 0 is valid: after the dtype and shape checks the call returns
+ *     HBL_OK without launching anything (pointers may then be NULL).
+ *   - Shapes: K is a power of two with 256 <= K <= 16384; N % 16 == 0 and
+ *     N > 0; 0 <= M < 2^31; M * max(K, N) < 2^40.
+ *   - Alignment: every pointer must be 16-byte aligned (HBL_ERR_ALIGN).
+ *   - The library keeps no mutable global state other than a per-device
+ *     cache of device properties filled on first use; distinct streams may
+ *     call concurrently with distinct workspaces.
+ *   - Only gfx950 devices are supported (HBL_ERR_DEVICE otherwise).
+ *
+ * Data formats:
+ *   packed ternary weights  uint8 [N][K/4]: for each row, one little-endian
+ *       32-bit word per 16 consecutive k; the code of k0 + 4*j + i (i, j in
+ *       0..3) occupies bits 8*i + 2*j .. 8*i + 2*j + 1 of the word of k0, with
+ *       the 2-bit codes 0b00 = 0, 0b01 = +1, 0b11 = -1 (0b10 never written).
+ *   INT8 activation codes   int8 [M][K], two's complement.
+ *   INT4 activation codes   uint8 [M][K/2]: for each row, one little-endian
+ *       32-bit word per 8 consecutive k; the code of k0 + 4*j + i (i in 0..3,
+ *       j in 0..1) occupies bits 8*i + 4*j .. 8*i + 4*j + 3, as a 4-bit two's
+ *       complement nibble.
+ *   per-token dequant scales d   fp32 [M].
+ *   per-tensor weight scale      fp32 [1] (alpha; the floor 1e-5 is applied on use).
+ */
+#ifndef HBL_H
+#define HBL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HBL_OK = 0,
+    HBL_ERR_NULL = 1,       /* a required pointer is NULL */
+    HBL_ERR_SHAPE = 2,      /* M, K or N outside the supported set */
+    HBL_ERR_DTYPE = 3,      /* unknown dtype or bit width */
+    HBL_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned */
+    HBL_ERR_WORKSPACE = 5,  /* workspace smaller than hbl_workspace_bytes() */
+    HBL_ERR_LAUNCH = 6,     /* the HIP runtime reported an error at launch */
+    HBL_ERR_DEVICE = 7      /* no current device, or it is not gfx950 */
+} hbl_status;
+
+typedef enum { HBL_F32 = 0, HBL_BF16 = 1 } hbl_dtype;
+
+/* Operation selector for hbl_workspace_bytes. */
+enum { HBL_OP_QUANTIZE_WEIGHTS = 0, HBL_OP_MATMUL = 1, HBL_OP_FORWARD_INT4 = 4, HBL_OP_FORWARD_INT8 = 8 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *hbl_status_string(hbl_status s);
+
+/* Bytes of device workspace the operation needs for these sizes (0 for an
+ * invalid op).  Host-only; never touches the device. */
+size_t hbl_workspace_bytes(int op, int64_t M, int64_t K, int64_t N);
+
+/*
+ * Offline per-tensor absmean ternarisation of latent weights
+ * (QbitAI article, section 引入H-BitLinear模块; 新智元 article, section
+ * H-BitLinear模块: weights become {-1, 0, 1} with one absmean scale).
+ *   w         fp32 [N][K] latent weights (device, read only)
+ *   w_packed  uint8 [N][K/4] packed ternary codes (device, written)
+ *   w_alpha   fp32 [1] alpha = mean|W| (device, written).  The sum of |W| is
+ *             taken in fp64, each row in order and then the rows in order,
+ *             so alpha is reproducible to the last bit.
+ *   workspace at least hbl_workspace_bytes(HBL_OP_QUANTIZE_WEIGHTS, 0, K, N) bytes.
+ */
+hbl_status hbl_quantize_weights(const float *w, int64_t N, int64_t K,
+                                uint8_t *w_packed, float *w_alpha,
+                                void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Whole H-BitLinear forward with INT8 (per-token absmax) activations
+ * (QbitAI article, section 引入H-BitLinear模块; 新智元 article, section
+ * H-BitLinear模块).
+ *   x         [M][K] activations, dtype x_dtype (fp32 or bf16)
+ *   gain      fp32 [K] RMSNorm gain, or NULL for 1
+ *   w_packed  uint8 [N][K/4] from hbl_quantize_weights;  w_alpha fp32 [1]
+ *   y         [M][N] output, dtype y_dtype (fp32 or bf16; bf16 rounds to nearest even)
+ *   workspace at least hbl_workspace_bytes(HBL_OP_FORWARD_INT8, M, K, N) bytes;
+ *             holds the activation codes and scales between the two kernels.
+ */
+hbl_status hbl_forward_int8(const void *x, hbl_dtype x_dtype, const float *gain,
+                            const uint8_t *w_packed, const float *w_alpha,
+                            int64_t M, int64_t K, int64_t N,
+                            void *y, hbl_dtype y_dtype,
+                            void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Same with INT4 (per-token absmean) activations; the arguments mean the same. */
+hbl_status hbl_forward_int4(const void *x, hbl_dtype x_dtype, const float *gain,
+                            const uint8_t *w_packed, const float *w_alpha,
+                            int64_t M, int64_t K, int64_t N,
+                            void *y, hbl_dtype y_dtype,
+                            void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- the two stages of the forward, exported for stage-wise checking ---- */
+
+/*
+ * Stage 1: RMSNorm -> Hadamard rotation -> per-token quantisation, one fused
+ * kernel (新智元 article, section H-BitLinear模块: the transform is applied to
+ * the activations before they are quantised).
+ *   bits      8 or 4
+ *   codes     INT8: int8 [M][K];  INT4: uint8 [M][K/2] (formats above)
+ *   dscale    fp32 [M] per-token dequant scales d
+ */
+hbl_status hbl_quantize_act(const void *x, hbl_dtype x_dtype, const float *gain,
+                            int64_t M, int64_t K, int bits,
+                            void *codes, float *dscale, hipStream_t stream);
+
+/*
+ * Stage 2: ternary integer matmul of the codes with dequant epilogue.
+ *   codes, dscale as written by hbl_quantize_act;  y [M][N] of y_dtype.
+ *   workspace at least hbl_workspace_bytes(HBL_OP_MATMUL, M, K, N) bytes (split-K
+ *             scratch of the small-M path; may be NULL when that size is 0).
+ *   When the scratch is used, its counters are cleared by a small kernel
+ *   enqueued first; calls sharing one workspace must be stream-ordered.
+ */
+hbl_status hbl_matmul_dequant(const void *codes, int bits, const float *dscale,
+                              const uint8_t *w_packed, const float *w_alpha,
+                              int64_t M, int64_t K, int64_t N,
+                              void *y, hbl_dtype y_dtype,
+                              void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- debug views used by the parity tests ---- */
+
+/* The rotated, normalised activations xt = H_K RMSNorm(x) / sqrt(K) as fp32
+ * [M][K], computed by the same code as stage 1 stopped before quantisation. */
+hbl_status hbl_rmsnorm_fwht(const void *x, hbl_dtype x_dtype, const float *gain,
+                            int64_t M, int64_t K, float *xt, hipStream_t stream);
+
+/* The exact int32 accumulators acc[m][n] = sum_k q[m][k] W_t[n][k] [M][N],
+ * computed by the same matmul kernels as stage 2 without the dequant epilogue.
+ * Workspace as for hbl_matmul_dequant. */
+hbl_status hbl_gemm_ternary(const void *codes, int bits, const uint8_t *w_packed,
+                            int64_t M, int64_t K, int64_t N, int32_t *acc,
+                            void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Expand packed ternary weights to int8 [N][K] in {-1, 0, 1}. */
+hbl_status hbl_unpack_weights(const uint8_t *w_packed, int64_t N, int64_t K,
+                              int8_t *w_t, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HBL_H */

@@ -1,0 +1,120 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects invalid arguments before touching the device.
+No kernel is launched here."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import hadamard_rotated_ternary_amd as hbl
+from layouts import pack_int4, pack_ternary, unpack_int4, unpack_ternary
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE = 0, 1, 2, 3, 4, 5
+A = ctypes.c_void_p(0x10000)        # aligned dummy address (never dereferenced here)
+A2 = ctypes.c_void_p(0x20000)
+BAD = ctypes.c_void_p(0x10008)      # 8-byte aligned only
+S = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hbl.LIB_PATH):
+        from hadamard_rotated_ternary_amd import build
+        build.build()
+    return hbl.lib()
+
+
+def test_header_entry_points_are_exported(L):
+    declared = hbl.declared_symbols()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", hbl.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(declared) <= exported
+    assert set(hbl.SIGNATURES) == set(declared)
+
+
+def test_status_strings(L):
+    for code in range(8):
+        assert L.hbl_status_string(code)
+    assert L.hbl_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes(L):
+    ws8 = L.hbl_workspace_bytes(8, 8192, 16384, 4096)
+    ws4 = L.hbl_workspace_bytes(4, 8192, 16384, 4096)
+    assert ws8 >= 8192 * 16384 + 8192 * 4 and ws4 >= 8192 * 16384 // 2 + 8192 * 4
+    assert ws4 < ws8
+    assert L.hbl_workspace_bytes(0, 0, 16384, 4096) >= 4096 * 8
+    assert L.hbl_workspace_bytes(1, 1, 16384, 4096) > 0       # split-K scratch of the small-M path
+    assert L.hbl_workspace_bytes(1, 8192, 16384, 4096) == 0
+    assert L.hbl_workspace_bytes(3, 1, 256, 16) == 0
+
+
+def fwd(L, bits=8, x=A, xd=1, gain=None, wp=A, wa=A, M=8, K=256, N=256, y=A2, yd=1, ws=A, wsb=None):
+    if wsb is None:
+        wsb = L.hbl_workspace_bytes(bits, M if M >= 0 else 0, K, N)
+    fn = L.hbl_forward_int8 if bits == 8 else L.hbl_forward_int4
+    return fn(x, xd, gain, wp, wa, M, K, N, y, yd, ws, wsb, S)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_forward_validation(L, bits):
+    assert fwd(L, bits, x=None) == NULL
+    assert fwd(L, bits, wp=None) == NULL
+    assert fwd(L, bits, y=None) == NULL
+    assert fwd(L, bits, ws=None) == NULL
+    assert fwd(L, bits, xd=5) == DTYPE
+    assert fwd(L, bits, yd=-1) == DTYPE
+    for K in (128, 300, 32768, 0):
+        assert fwd(L, bits, K=K, wsb=1 << 40) == SHAPE
+    for N in (0, 8, 250):
+        assert fwd(L, bits, N=N, wsb=1 << 40) == SHAPE
+    assert fwd(L, bits, M=-1, wsb=1 << 40) == SHAPE
+    assert fwd(L, bits, x=BAD) == ALIGN
+    assert fwd(L, bits, gain=BAD) == ALIGN
+    assert fwd(L, bits, wsb=16) == WORKSPACE
+    # empty input: valid, nothing launched
+    assert fwd(L, bits, M=0) == OK
+
+
+def test_stage_validation(L):
+    assert L.hbl_quantize_act(A, 1, None, 4, 256, 6, A, A2, S) == DTYPE
+    assert L.hbl_quantize_act(A, 1, None, 4, 200, 8, A, A2, S) == SHAPE
+    assert L.hbl_quantize_act(None, 1, None, 4, 256, 8, A, A2, S) == NULL
+    assert L.hbl_quantize_act(A, 1, None, 0, 256, 8, A, A2, S) == OK
+    assert L.hbl_rmsnorm_fwht(A, 1, None, 4, 256, BAD, S) == ALIGN
+    assert L.hbl_rmsnorm_fwht(A, 1, None, 0, 256, A, S) == OK
+    assert L.hbl_gemm_ternary(A, 5, A, 4, 256, 256, A, None, 0, S) == DTYPE
+    assert L.hbl_gemm_ternary(A, 8, A, 4, 256, 250, A, None, 0, S) == SHAPE
+    assert L.hbl_gemm_ternary(A, 8, A, 4, 256, 256, A, None, 0, S) == NULL      # small-M needs scratch
+    assert L.hbl_gemm_ternary(A, 8, A, 4, 256, 256, A, A2, 16, S) == WORKSPACE
+    assert L.hbl_matmul_dequant(A, 8, None, A, A, 100, 256, 256, A, 1, None, 0, S) == NULL
+    assert L.hbl_quantize_weights(A, 256, 255, A, A, A, 1 << 20, S) == SHAPE
+    assert L.hbl_quantize_weights(A, 256, 256, A, A, A, 8, S) == WORKSPACE
+    assert L.hbl_unpack_weights(A, 16, 256, None, S) == NULL
+
+
+def test_layout_codecs_hand_examples():
+    # ternary: k0..k15 = +1, -1, 0, 0 | 0 ... ; code of k (=4j+i) at bits 8i+2j
+    wt = np.zeros((1, 16), np.int8)
+    wt[0, 0] = 1    # i=0 j=0 -> bits 0-1 = 01
+    wt[0, 1] = -1   # i=1 j=0 -> bits 8-9 = 11
+    wt[0, 4] = -1   # i=0 j=1 -> bits 2-3 = 11
+    wt[0, 15] = 1   # i=3 j=3 -> bits 30-31 = 01
+    p = pack_ternary(wt)
+    assert p.view(np.uint32)[0, 0] == 0b01 | (0b11 << 8) | (0b11 << 2) | (0b01 << 30)
+    np.testing.assert_array_equal(unpack_ternary(p, 16), wt)
+    # int4: code of k (=4j+i) at bits 8i+4j
+    q = np.array([[1, -1, 7, -8, 2, 0, 0, 3]], np.int8)
+    w = pack_int4(q).view(np.uint32)[0, 0]
+    assert w == (0x1 | (0xF << 8) | (0x7 << 16) | (0x8 << 24) | (0x2 << 4) | (0x3 << 28))
+    np.testing.assert_array_equal(unpack_int4(pack_int4(q), 8), q)
+    rng = np.random.default_rng(0)
+    q = rng.integers(-8, 8, (5, 64)).astype(np.int8)
+    np.testing.assert_array_equal(unpack_int4(pack_int4(q), 64), q)
+    wt = rng.integers(-1, 2, (3, 256)).astype(np.int8)
+    np.testing.assert_array_equal(unpack_ternary(pack_ternary(wt), 256), wt)

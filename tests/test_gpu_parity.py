@@ -1,0 +1,254 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bars:
+  * ternary weights and alpha: bit-exact;
+  * rotated activations: relative L2 <= 1e-5 per token;
+  * activation codes: equal except +-1 at rounding ties of the oracle's
+    pre-rounding value (|pre - tie| < 1e-4), in at most 1e-4 of the codes;
+    per-token scales within 1e-5 relative;
+  * integer matmul: bit-exact int32 on identical codes;
+  * outputs: relative L2 <= 2e-3 against the oracle rounded to the output dtype.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hadamard_rotated_ternary_amd as hbl
+import oracle
+import synthetic
+from layouts import pack_int4, pack_ternary, unpack_int4, unpack_ternary
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a gfx950 device"
+    assert "gfx950" in torch.cuda.get_device_properties(0).gcnArchName
+    hbl.lib()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def x_to_dev(x_f32, x_bits):
+    if x_bits is None:
+        return dev(x_f32)
+    return dev(x_bits.view(np.int16)).view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64); b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def check_codes(q_gpu, q_or, pre_or, max_frac=1e-4, tie_tol=1e-4):
+    q_gpu = q_gpu.astype(np.int32); q_or = q_or.astype(np.int32)
+    diff = q_gpu != q_or
+    n = int(diff.sum())
+    if n:
+        assert np.all(np.abs(q_gpu[diff] - q_or[diff]) == 1), "code differs by more than 1"
+        tie = (q_gpu[diff] + q_or[diff]) / 2.0
+        assert np.all(np.abs(pre_or[diff] - tie) < tie_tol), "code differs away from a rounding tie"
+    assert n <= max(1, max_frac * q_or.size), f"{n} code mismatches of {q_or.size}"
+    return n
+
+
+def gpu_codes_unpacked(codes, bits, K):
+    c = host(codes)
+    return c.astype(np.int8) if bits == 8 else unpack_int4(c, K)
+
+
+# ------------------------------------------------------------------ weights
+
+@pytest.mark.parametrize("N,K", [(16, 256), (272, 2048), (4096, 4096), (3072, 8192), (4096, 16384)])
+def test_weight_ternarisation_bit_exact(N, K):
+    rng = np.random.default_rng(N + K)
+    w = rng.normal(0, 0.02, (N, K)).astype(np.float32)
+    wt, alpha = oracle.quantize_weights(w)
+    wp, a = hbl.quantize_weights(dev(w))
+    assert host(a)[0] == alpha
+    wp_h = host(wp)
+    np.testing.assert_array_equal(unpack_ternary(wp_h, K), wt)
+    np.testing.assert_array_equal(wp_h, pack_ternary(wt))
+    np.testing.assert_array_equal(host(hbl.unpack_weights(wp, K)), wt)
+
+
+def test_weight_ternarisation_ties_and_zero():
+    # alpha = 1 exactly; +-0.5 are ties that must round to 0
+    w = np.tile(np.array([2.0, 0.5, -0.5, 1.0], np.float32), (16, 64))
+    wt, alpha = oracle.quantize_weights(w)
+    wp, a = hbl.quantize_weights(dev(w))
+    assert host(a)[0] == alpha == 1.0
+    np.testing.assert_array_equal(unpack_ternary(host(wp), 256), wt)
+    wz = np.zeros((16, 256), np.float32)
+    wp, a = hbl.quantize_weights(dev(wz))
+    assert host(a)[0] == 0.0 and not host(wp).any()
+
+
+# ------------------------------------------------------------------ rotation and quantisation
+
+KS = [256, 512, 1024, 2048, 4096, 8192, 16384]
+
+
+def make_x(M, K, seed, dist="laplace", bf16=True):
+    w = synthetic.Workload("t", M, K, 16, 4, "bf16" if bf16 else "f32", dist, 0.05 if dist == "laplace" else 1.0,
+                           max(1, K // 200), 100.0, seed)
+    x, xb, _ = synthetic.make_inputs(w, with_weights=False)
+    return x, xb
+
+
+@pytest.mark.parametrize("K", KS)
+@pytest.mark.parametrize("M", [1, 3, 70])
+def test_rotation_matches_oracle(K, M):
+    x, xb = make_x(M, K, K + M)
+    for gain in (None, synthetic.make_gain(K, K)):
+        xt = host(hbl.rmsnorm_fwht(x_to_dev(x, xb), None if gain is None else dev(gain)))
+        ref = oracle.hadamard_rotate(oracle.rmsnorm(x, gain))
+        for m in range(M):
+            assert rel_l2(xt[m], ref[m]) <= 1e-5, (m, rel_l2(xt[m], ref[m]))
+
+
+@pytest.mark.parametrize("K", KS)
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M", [1, 5, 64, 129])
+def test_codes_match_oracle(K, bits, M):
+    x, xb = make_x(M, K, 7 * K + M, dist="normal" if K % 3 else "laplace", bf16=(M != 5))
+    codes, d = hbl.quantize_act(x_to_dev(x, xb), bits)
+    q = gpu_codes_unpacked(codes, bits, K)
+    xt = oracle.hadamard_rotate(oracle.rmsnorm(x))
+    q_or, d_or, pre = oracle.quant_act(xt, bits)
+    check_codes(q, q_or, pre)
+    np.testing.assert_allclose(host(d), d_or, rtol=1e-5)
+
+
+def test_zero_token_and_tiny_token():
+    K = 1024
+    x = np.zeros((3, K), np.float32)
+    x[1, 5] = 1e-30
+    x[2] = 1e-3
+    for bits in (8, 4):
+        codes, d = hbl.quantize_act(dev(x), bits)
+        q = gpu_codes_unpacked(codes, bits, K)
+        q_or, d_or, pre = oracle.quant_act(oracle.hadamard_rotate(oracle.rmsnorm(x)), bits)
+        np.testing.assert_array_equal(q[0], 0)
+        check_codes(q, q_or, pre)
+        np.testing.assert_allclose(host(d), d_or, rtol=1e-5)
+
+
+# ------------------------------------------------------------------ integer matmul
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,K,N", [(1, 256, 16), (7, 512, 272), (16, 2048, 512), (33, 4096, 64),
+                                   (64, 16384, 128), (65, 256, 256), (300, 1024, 272), (512, 2048, 512),
+                                   (257, 16384, 528)])
+def test_matmul_bit_exact(bits, M, K, N):
+    rng = np.random.default_rng(M * 7 + K + N + bits)
+    lo, hi = (-128, 128) if bits == 8 else (-8, 8)
+    q = rng.integers(lo, hi, (M, K)).astype(np.int8)
+    q[0, :] = lo                      # extreme magnitudes
+    wt = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    wt[0, :] = -1
+    acc_or = oracle.gemm_ternary(q, wt)
+    codes = dev(q) if bits == 8 else dev(pack_int4(q))
+    acc = host(hbl.gemm_ternary(codes, bits, dev(pack_ternary(wt)), K))
+    np.testing.assert_array_equal(acc, acc_or)
+
+
+# ------------------------------------------------------------------ whole layer
+
+def run_layer(w: synthetic.Workload, M=None, gain=None, sample=None):
+    x, xb, wl = synthetic.make_inputs(w, M=M)
+    wt, alpha = oracle.quantize_weights(wl)
+    wp, a = hbl.quantize_weights(dev(wl))
+    assert host(a)[0] == alpha
+    xd = x_to_dev(x, xb)
+    gd = None if gain is None else dev(gain)
+    y = hbl.forward(xd, wp, a, w.bits, gain=gd)
+    rows = np.arange(x.shape[0]) if sample is None else sample
+    ref = oracle.forward(x[rows], wt, alpha, w.bits, g=gain)
+    yh = host(y.float())[rows]
+    y_ref = ref["y"] if y.dtype == torch.float32 else oracle.to_bf16_rne(ref["y"])
+    return yh, y_ref, ref, xd, wp, a, rows
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,K,N", [(8, 256, 256), (1, 16384, 4096), (17, 4096, 272), (64, 8192, 512),
+                                   (300, 2048, 272), (513, 16384, 256)])
+def test_layer_small(bits, M, K, N):
+    w = synthetic.Workload("t", M, K, N, bits, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, M + K + N)
+    yh, y_ref, ref, xd, wp, a, rows = run_layer(w)
+    assert rel_l2(yh, y_ref) <= 2e-3, rel_l2(yh, y_ref)
+    # stage view of the same call chain
+    codes, d = hbl.quantize_act(xd, bits)
+    check_codes(gpu_codes_unpacked(codes, bits, K), ref["q"], ref["pre"])
+    np.testing.assert_allclose(host(d), ref["d"], rtol=1e-5)
+
+
+def test_layer_with_gain_fp32_out():
+    w = synthetic.WORKLOADS["tiny_int8"]
+    g = synthetic.make_gain(w.K, 3)
+    yh, y_ref, *_ = run_layer(w, gain=g)
+    assert rel_l2(yh, y_ref) <= 2e-3
+
+
+WORKLOAD_SAMPLES = [("tiny_int8", None), ("wo_1p3b_int4", 48), ("wdown_3b_int4", 24), ("wo_7b_int8", 24),
+                    ("wo_7b_int4", 24), ("wdown_7b_int8", 16), ("wdown_7b_int4", 16), ("decode_7b_m1", None),
+                    ("decode_7b_m16", None), ("decode_7b_m64", None)]
+
+
+@pytest.mark.parametrize("name,count", WORKLOAD_SAMPLES)
+def test_layer_full_workloads(name, count):
+    """Every workload at its full size; the oracle checks a deterministic token
+    sample (evenly spaced rows plus first and last) of the GPU output."""
+    w = synthetic.WORKLOADS[name]
+    sample = None if count is None else synthetic.sample_rows(w.M, count)
+    yh, y_ref, ref, xd, wp, a, rows = run_layer(w, sample=sample)
+    assert rel_l2(yh, y_ref) <= 2e-3, rel_l2(yh, y_ref)
+    # exact integer accumulators on the sampled rows, from the oracle's own codes
+    q = ref["q"]
+    codes = dev(q) if w.bits == 8 else dev(pack_int4(q))
+    acc = host(hbl.gemm_ternary(codes, w.bits, wp, w.K))
+    np.testing.assert_array_equal(acc, ref["acc"])
+
+
+# ------------------------------------------------------------------ invariants of the GPU path
+
+def test_int8_layer_is_exactly_odd_and_deterministic():
+    w = synthetic.WORKLOADS["wo_1p3b_int4"].with_(bits=8, M=512)
+    x, xb, wl = synthetic.make_inputs(w)
+    wp, a = hbl.quantize_weights(dev(wl))
+    xd = x_to_dev(x, xb)
+    y1 = hbl.forward(xd, wp, a, 8)
+    y2 = hbl.forward(xd, wp, a, 8)
+    yn = hbl.forward(-xd, wp, a, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(yn, -y1)
+
+
+def test_token_permutation_equivariance():
+    w = synthetic.WORKLOADS["wo_1p3b_int4"].with_(M=384)
+    x, xb, wl = synthetic.make_inputs(w)
+    wp, a = hbl.quantize_weights(dev(wl))
+    xd = x_to_dev(x, xb)
+    perm = torch.randperm(xd.shape[0], generator=torch.Generator().manual_seed(0)).cuda()
+    y = hbl.forward(xd, wp, a, 4)
+    yp = hbl.forward(xd[perm].contiguous(), wp, a, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y[perm])
+
+
+def test_empty_batch():
+    wp = torch.zeros((256, 64), dtype=torch.uint8, device="cuda")
+    a = torch.ones(4, dtype=torch.float32, device="cuda")[:1]
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    y = hbl.forward(x, wp, a, 8)
+    assert y.shape == (0, 256)

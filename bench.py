@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the H-BitLinear forward (BitNet v2) on one MI355X.
+
+A step is one pass of the whole layer over one batch: the fused RMSNorm +
+Hadamard + quantisation kernel, then the ternary int8-MFMA matmul with its
+dequant epilogue (the two kernels hbl_forward_int{8,4} launches).  Inputs are
+seeded synthetic data already resident in device memory when timing starts.
+Default workload: 7B-shaped FFN down projection, M=8192 tokens, K=16384,
+N=4096, INT4 activations, bf16 in/out.
+
+Prints one JSON line on stdout.  Extra context (INT8 path, decode shapes,
+weight ternarisation) goes into extra keys of the same line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "H-BitLinear tokens/s + effective int TOPS & HBM GB/s vs roofline, 7B Wdown"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_prefill_wdown_7b.json")
+GEMM_SOURCES = [os.path.join(ROOT, "hadamard_rotated_ternary_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(M, K, N, x_bytes=2, y_bytes=2):
+    """What the layer itself must move: activations in, packed weights once, outputs out."""
+    return M * K * x_bytes + N * K // 4 + M * N * y_bytes
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wdown_7b_int4")
+    ap.add_argument("--no-extras", action="store_true", help="skip the INT8 and decode side measurements")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall-clock budget of the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
+              "sharding is a design note, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import hadamard_rotated_ternary_amd as hbl
+    import synthetic
+
+    assert torch.cuda.is_available(), "needs an MI355X"
+    props = torch.cuda.get_device_properties(0)
+    if "gfx950" not in props.gcnArchName:
+        raise SystemExit(f"not a gfx950 device: {props.gcnArchName}")
+    hbl.lib()
+
+    w = synthetic.WORKLOADS[args.workload]
+    M, K, N, bits = w.M, w.K, w.N, w.bits
+    log(f"[bench] workload {w.name}: M={M} K={K} N={N} INT{bits} x={w.x_dtype}")
+    x, xb, wl = synthetic.make_inputs(w)
+    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16) if xb is not None else torch.from_numpy(x).cuda()
+    wd = torch.from_numpy(wl).cuda()
+
+    # ---- offline weight ternarisation (not part of a step; reported for information)
+    wp, a = hbl.quantize_weights(wd)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        hbl.quantize_weights(wd)
+    e1.record()
+    torch.cuda.synchronize()
+    wq_ms = e0.elapsed_time(e1) / 3
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    res = time_layer(torch, hbl, xd, wp, a, M, K, N, bits, args.steps, args.warmup)
+    step_s = res["ms_per_step"] / 1e3
+    gemm_s = res["gemm_ms"] / 1e3
+    ops = 2.0 * M * N * K
+    achieved = ops / gemm_s / 1e12
+    traffic = stored_traffic(args.workload)
+
+    out = {
+        "metric": METRIC,
+        "value": M / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "K": K, "N": N, "activation_bits": bits,
+                   "x_dtype": w.x_dtype, "y_dtype": w.x_dtype, "parallelism": "single-gpu"},
+        "effective_int_tops": ops / step_s / 1e12,
+        "hbm_gbps_algorithmic": algorithmic_bytes(M, K, N) / step_s / 1e9,
+        "roofline": {"kernel": "gemm_prefill_kernel", "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": achieved / PEAK_INT8_TOPS,
+                     "traffic": traffic},
+        "kernels": {
+            "prep_ms": res["prep_ms"], "gemm_ms": res["gemm_ms"],
+            "prep_gbps_impl": (M * K * 2 + M * K * bits / 8 + M * 4) / (res["prep_ms"] / 1e3) / 1e9,
+            "gemm_tops": achieved,
+            "forward_entry_ms": res["forward_ms"],
+        },
+        "weight_ternarise_ms": wq_ms,
+    }
+    if not args.no_extras:
+        out["extras"] = extras(torch, hbl, synthetic, args)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(x, wl, bits, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup):
+    """Time `steps` forwards; events between the two kernels give per-kernel times."""
+    codes = torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
+    d = torch.empty(M + 4, dtype=torch.float32, device="cuda")[:M]
+    y = torch.empty((M, N), dtype=xd.dtype, device="cuda")
+    ws = torch.empty(max(hbl.workspace_bytes(hbl.OP_MATMUL, M, K, N), 16), dtype=torch.uint8, device="cuda")
+    wsf = torch.empty(max(hbl.workspace_bytes(hbl.OP_FORWARD_INT8 if bits == 8 else hbl.OP_FORWARD_INT4, M, K, N), 16),
+                      dtype=torch.uint8, device="cuda")
+
+    def step(evs=None):
+        if evs: evs[0].record()
+        hbl.quantize_act(xd, bits, out=(codes, d))
+        if evs: evs[1].record()
+        hbl.matmul_dequant(codes, bits, d, wp, a, K, workspace=ws, out=y)
+        if evs: evs[2].record()
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prep = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # the public single-call entry point, same kernels
+    for _ in range(max(2, warmup // 2)):
+        hbl.forward(xd, wp, a, bits, workspace=wsf, out=y)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    f0.record()
+    for _ in range(steps):
+        hbl.forward(xd, wp, a, bits, workspace=wsf, out=y)
+    f1.record()
+    torch.cuda.synchronize()
+    return {"ms_per_step": (t1 - t0) * 1e3 / steps, "prep_ms": prep, "gemm_ms": gemm,
+            "forward_ms": f0.elapsed_time(f1) / steps}
+
+
+def stored_traffic(workload):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if
+    they were taken on the current matmul source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != gemm_source_sha() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def extras(torch, hbl, synthetic, args):
+    out = {}
+    # INT8 activations on the same 7B Wdown shape
+    w8 = synthetic.WORKLOADS["wdown_7b_int8"]
+    x, xb, wl = synthetic.make_inputs(w8)
+    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    wp, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
+    r = time_layer(torch, hbl, xd, wp, a, w8.M, w8.K, w8.N, 8, max(10, args.steps // 2), 5)
+    ops = 2.0 * w8.M * w8.N * w8.K
+    out["wdown_7b_int8"] = {"tokens_per_s": w8.M / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
+                            "prep_ms": r["prep_ms"], "gemm_ms": r["gemm_ms"],
+                            "gemm_tops": ops / (r["gemm_ms"] / 1e3) / 1e12,
+                            "gemm_mfma_frac": ops / (r["gemm_ms"] / 1e3) / 1e12 / PEAK_INT8_TOPS}
+    del xd, wp
+    # decode shapes: weights rotated over enough copies to defeat the 256 MB Infinity Cache
+    base = synthetic.WORKLOADS["decode_7b_m64"]
+    x, xb, wl = synthetic.make_inputs(base)
+    wp0, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
+    R = 40
+    wps = [wp0.clone() for _ in range(R)]
+    xfull = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    for M in (1, 16, 64):
+        xd = xfull[:M].contiguous()
+        codes, d = hbl.quantize_act(xd, 4)
+        ws = torch.empty(max(hbl.workspace_bytes(hbl.OP_MATMUL, M, base.K, base.N), 16), dtype=torch.uint8, device="cuda")
+        wsf = torch.empty(hbl.workspace_bytes(hbl.OP_FORWARD_INT4, M, base.K, base.N), dtype=torch.uint8, device="cuda")
+        y = torch.empty((M, base.N), dtype=torch.bfloat16, device="cuda")
+        iters = 200
+        for i in range(20):
+            hbl.matmul_dequant(codes, 4, d, wps[i % R], a, base.K, workspace=ws, out=y)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i in range(iters):
+            evs[i][0].record()
+            hbl.matmul_dequant(codes, 4, d, wps[i % R], a, base.K, workspace=ws, out=y)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        g_us = 1e3 * float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for i in range(iters):
+            hbl.forward(xd, wps[i % R], a, 4, workspace=wsf, out=y)
+        f1.record()
+        torch.cuda.synchronize()
+        fwd_us = 1e3 * f0.elapsed_time(f1) / iters
+        gbytes = base.N * base.K / 4 + M * base.K / 2 + M * base.N * 2 + M * 4
+        out[f"decode_7b_m{M}"] = {"gemm_us_event": g_us, "gemm_gbps": gbytes / (g_us / 1e6) / 1e9,
+                                  "gemm_hbm_frac": gbytes / (g_us / 1e6) / 1e9 / PEAK_HBM_GBS,
+                                  "forward_us": fwd_us, "tokens_per_s": M / (fwd_us / 1e6)}
+    return out
+
+
+def cpu_baseline(x, wl, bits, budget_s):
+    """The oracle as it stands, on the host cores, on the first tokens of the
+    same workload (sample sized to about `budget_s` seconds)."""
+    import oracle
+    wt, alpha = oracle.quantize_weights(wl)
+    threads = oracle.max_threads()
+    n0 = max(1, threads)
+    t0 = time.perf_counter()
+    oracle.forward(x[:n0], wt, alpha, bits, keep=False)
+    dt = time.perf_counter() - t0
+    n = int(min(x.shape[0], max(n0, n0 * budget_s / max(dt, 1e-6))))
+    n = max(n0, (n // n0) * n0)
+    t0 = time.perf_counter()
+    oracle.forward(x[:n], wt, alpha, bits, keep=False)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {x.shape[0]} tokens of the same workload (INT{bits}), {dt:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

@@ -133,23 +133,27 @@ def forward(x: torch.Tensor, w_packed: torch.Tensor, w_alpha: torch.Tensor, bits
     return y
 
 
-def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None):
+def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, out=None):
     """Stage 1: x [M][K] -> (codes, per-token scales fp32 [M])."""
     _dev(x, "x")
     M, K = x.shape
-    codes = torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
-                        device=x.device)
-    d = torch.empty(M + 4, dtype=torch.float32, device=x.device)[:M]
+    if out is not None:
+        codes, d = out
+    else:
+        codes = torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
+                            device=x.device)
+        d = torch.empty(M + 4, dtype=torch.float32, device=x.device)[:M]
     _call("hbl_quantize_act", _ptr(x), _dtype_code(x.dtype), _ptr(gain), M, K, bits, _ptr(codes), _ptr(d),
           _stream())
     return codes, d
 
 
-def matmul_dequant(codes, bits, dscale, w_packed, w_alpha, K, out_dtype=torch.bfloat16, workspace=None):
+def matmul_dequant(codes, bits, dscale, w_packed, w_alpha, K, out_dtype=torch.bfloat16, workspace=None, out=None):
     """Stage 2: codes -> y [M][N]."""
     M = codes.shape[0]
     N = w_packed.shape[0]
-    y = torch.empty((M, N), dtype=out_dtype, device=codes.device)
+    y = torch.empty((M, N), dtype=out_dtype, device=codes.device) if out is None else out
+    out_dtype = y.dtype
     ws = _workspace(workspace_bytes(OP_MATMUL, M, K, N), codes.device, workspace)
     _call("hbl_matmul_dequant", _ptr(codes), bits, _ptr(dscale), _ptr(w_packed), _ptr(w_alpha), M, K, N,
           _ptr(y), _dtype_code(out_dtype), _ptr(ws), ws.numel(), _stream())

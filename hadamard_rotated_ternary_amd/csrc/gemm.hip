@@ -32,30 +32,30 @@
 
 namespace hbl {
 
-// 16 ternary codes (2-bit, k0+4j+i at bits 8i+2j) -> 16 int8 in k order.
-HBL_DEV v4i expand_ternary(uint32_t p) {
-  v4i o;
-  o[0] = (int)__builtin_amdgcn_perm(0u, 0xFF000100u, p & 0x03030303u);
-  o[1] = (int)__builtin_amdgcn_perm(0u, 0xFF000100u, (p >> 2) & 0x03030303u);
-  o[2] = (int)__builtin_amdgcn_perm(0u, 0xFF000100u, (p >> 4) & 0x03030303u);
-  o[3] = (int)__builtin_amdgcn_perm(0u, 0xFF000100u, (p >> 6) & 0x03030303u);
-  return o;
+// Operand expansion without lookups.
+//
+// A packed weight word holds the 2-bit two's complement codes of 16
+// consecutive k, the code of k0+4j+i in bits 8i+2j (field j of byte i).
+// Shifting field j to the top of its byte and masking gives, byte by byte,
+// exactly 64*w as a signed int8 (0x40 = +64, 0xC0 = -64).  MFMA step j of a
+// 64-k group takes field j of four packed words, so its operand covers codes
+// 16d + 4j + i (d = word, i = byte): 1-2 VALU ops per operand dword.
+HBL_DEV uint32_t wfield(uint32_t p, int j) {
+  return (j == 3 ? p : (p << (6 - 2 * j))) & 0xC0C0C0C0u;
 }
-
-// Four 4-bit two's complement codes in the low nibbles of the bytes of x
-// (already XORed with 0x08 per byte) -> four int8.
-HBL_DEV int sext_nibbles(uint32_t e) { return (int)((e + 0x78787878u) ^ 0x80808080u); }
-
-// 16 INT4 codes (two words; k0+4j+i at bits 8i+4j of each) -> 16 int8 in k order.
-HBL_DEV v4i expand_int4(uint32_t w0, uint32_t w1) {
-  const uint32_t a = w0 ^ 0x88888888u, b = w1 ^ 0x88888888u;
-  v4i o;
-  o[0] = sext_nibbles(a & 0x0F0F0F0Fu);
-  o[1] = sext_nibbles((a >> 4) & 0x0F0F0F0Fu);
-  o[2] = sext_nibbles(b & 0x0F0F0F0Fu);
-  o[3] = sext_nibbles((b >> 4) & 0x0F0F0F0Fu);
-  return o;
+// INT4 activation words hold codes 8 at a time, the code of k0+4j+i in bits
+// 8i+4j.  Moving a nibble to the top of its byte gives 16*q as a signed int8.
+// For the same code set 16d + 4j + i, step j takes the low (j even) or high
+// (j odd) nibbles of word 2d + j/2.
+HBL_DEV uint32_t a4field(uint32_t w, int j) {
+  return ((j & 1) ? w : (w << 4)) & 0xF0F0F0F0u;
 }
+// The accumulators therefore hold 64 * acc (INT8 path) or 1024 * acc (INT4),
+// exact multiples whose magnitude stays below 2^27 for K <= 16384 (|q| <= 128
+// after scaling, |w| = 64): an arithmetic shift recovers acc exactly.
+template <int BITS>
+HBL_DEV int unscale(int v) { return BITS == 8 ? (v >> 6) : (v >> 10); }
+HBL_DEV uint32_t u4get(const uint4& u, int j) { return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w; }
 
 template <int OUT>
 HBL_DEV void store_out(void* Y, size_t off, int acc, float t) {
@@ -164,39 +164,48 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     if (kt + 1 < KT) gload(kt + 1);
     const uint8_t* sa = smem + buf * C::STAGE;
     const uint8_t* sb = sa + C::A_STAGE;
+    // weight fragments: 4 packed words = k-chunks 4g..4g+3 of channel n
     uint4 bq[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int n = wn * 128 + cb * 32 + l32;
       bq[cb] = *reinterpret_cast<const uint4*>(sb + n * 32 + 16 * (g ^ swz_b(n)));
     }
-    uint4 aq[4][2];
-    if constexpr (BITS == 4) {
+    // activation fragments: k-chunks 4g..4g+3 of row m (64 codes)
+    uint4 aq[4][4];
 #pragma unroll
-      for (int rbk = 0; rbk < 4; ++rbk) {
-        const int row = wm * 128 + rbk * 32 + l32;
+    for (int rbk = 0; rbk < 4; ++rbk) {
+      const int row = wm * 128 + rbk * 32 + l32;
+      if constexpr (BITS == 8) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          aq[rbk][d] = *reinterpret_cast<const uint4*>(sa + row * 128 + 16 * ((4 * g + d) ^ swz_a<8>(row)));
+      } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           aq[rbk][h] = *reinterpret_cast<const uint4*>(sa + row * 64 + 16 * ((2 * g + h) ^ swz_a<4>(row)));
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int j = 0; j < 4; ++j) {
       v4i bf[4];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const uint32_t p = ks == 0 ? bq[cb].x : ks == 1 ? bq[cb].y : ks == 2 ? bq[cb].z : bq[cb].w;
-        bf[cb] = expand_ternary(p);
-      }
+      for (int cb = 0; cb < 4; ++cb)
+        bf[cb] = v4i{(int)wfield(bq[cb].x, j), (int)wfield(bq[cb].y, j), (int)wfield(bq[cb].z, j),
+                     (int)wfield(bq[cb].w, j)};
 #pragma unroll
       for (int rbk = 0; rbk < 4; ++rbk) {
         v4i af;
         if constexpr (BITS == 8) {
-          const int row = wm * 128 + rbk * 32 + l32;
-          af = *reinterpret_cast<const v4i*>(sa + row * 128 + 16 * ((4 * g + ks) ^ swz_a<8>(row)));
+          // dword j of chunks 4g..4g+3: codes 16d + 4j .. +3
+          af = v4i{(int)u4get(aq[rbk][0], j), (int)u4get(aq[rbk][1], j), (int)u4get(aq[rbk][2], j),
+                   (int)u4get(aq[rbk][3], j)};
         } else {
-          const uint4 u = aq[rbk][ks >> 1];
-          af = (ks & 1) ? expand_int4(u.z, u.w) : expand_int4(u.x, u.y);
+          // chunk d = words 2d, 2d+1 of the 32 bytes; step j uses word 2d + j/2
+          const uint32_t w[8] = {aq[rbk][0].x, aq[rbk][0].y, aq[rbk][0].z, aq[rbk][0].w,
+                                 aq[rbk][1].x, aq[rbk][1].y, aq[rbk][1].z, aq[rbk][1].w};
+          af = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
+                   (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
         }
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
@@ -220,148 +229,145 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const int n = n0 + wn * 128 + cb * 32 + l32;
-        if (n < N) store_out<OUT>(Y, (size_t)m * N + n, acc[rbk][cb][r], t);
+        if (n < N) store_out<OUT>(Y, (size_t)m * N + n, unscale<BITS>(acc[rbk][cb][r]), t);
       }
     }
   }
 }
 
 // ===========================================================================
-// Decode (M <= 64)
-constexpr int DWAVES = 4;          // waves per workgroup
-constexpr int DCH = 16 * DWAVES;   // output channels per workgroup
-constexpr int DKB = 256;           // k per load block (16 bytes of packed weights per lane)
+// Decode (M <= 64): weight streaming.
+//
+// A workgroup of 4 waves owns 16*CPW output channels and one of S equal K
+// ranges.  The range is cut into 256-k blocks dealt round-robin to the waves;
+// each wave issues all its packed-weight loads (16 bytes per lane per block)
+// up front, so every weight byte is read from HBM once with the whole stream
+// in flight, and reads the (small, L2-resident) activation codes per block.
+// v_mfma_i32_16x16x64_i8 runs with channels on the MFMA's M side and up to 16
+// tokens on its N side.  The waves' int32 partials meet in LDS through integer
+// atomics (exact, order free).  With S > 1 a second small kernel sums the S
+// partials in order and dequantises; integer sums are exact, so the result is
+// the same for every S.
+constexpr int DKB = 256;
 
-// Split of K into KS slabs so that about 512 workgroups stream the weights,
-// while the slab's activation codes still fit in 64 KiB of LDS.
-static int decode_splits(int M, int K, int N, int bits) {
-  const int nblk = (N + DCH - 1) / DCH;
-  int ks = 1;
-  while (nblk * ks < 512 && K / (2 * ks) >= DKB) ks *= 2;
-  while ((long long)M * (K / ks) * bits / 8 + (long long)M * 16 > 65536 && K / (2 * ks) >= DKB) ks *= 2;
-  return ks;
+struct DecodePlan { int cpw, S, mb; };
+static DecodePlan decode_plan(int M, int K) {
+  DecodePlan p = M <= 4 ? DecodePlan{1, 1, 1} : M <= 16 ? DecodePlan{2, 2, 1} : DecodePlan{4, 4, 4};
+  while (p.S > 1 && K / p.S < DKB) p.S /= 2;
+  return p;
 }
+// Weight blocks a wave may hold in registers (MAXB * CPW uint4 <= 16).
+constexpr int decode_maxb(int cpw) { return 16 / cpw; }
 
-template <int BITS>
-struct DCfg {
-  static constexpr int PADB = BITS == 8 ? 16 : 8;  // LDS row padding (bytes) against bank conflicts
-};
-
-template <int BITS, int MB, int OUT>
+template <int BITS, int MB, int CPW, int OUT>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
-    const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int KS,
-    int32_t* __restrict__ partial, int* __restrict__ counters) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t sact[];
-  __shared__ int s_last;
+    const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int S,
+    int32_t* __restrict__ partial) {
+  constexpr int MAXB = decode_maxb(CPW);
+  constexpr int CH = 16 * CPW;
+  __shared__ int red[CH * MB * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nblk = blockIdx.x, ks = blockIdx.y;
-  const int Kslab = K / KS, kbeg = ks * Kslab;
-  const int nkb = Kslab / DKB;
-  const int row_bytes = Kslab * BITS / 8;
-  const int srow = row_bytes + DCfg<BITS>::PADB;
+  const int c = lane & 15, g = lane >> 4;
+  const int ch0 = blockIdx.x * CH, s = blockIdx.y;
+  const int Kr = K / S, kbeg = s * Kr;
+  const int nblk = Kr / DKB;                       // 256-k blocks in this range
+  const int nb = nblk > wave ? (nblk - wave + 3) / 4 : 0;   // blocks of this wave: wave, wave+4, ...
   const size_t arow = (size_t)K * BITS / 8;
 
-  // ---- stage this slab's activation codes (M rows) in LDS, 16 bytes per thread per step
-  {
-    const int units = row_bytes / 16;
-    for (int q = tid; q < M * units; q += 256) {
-      const int t = q / units, u = q % units;
-      const uint4 v = *reinterpret_cast<const uint4*>(A + (size_t)t * arow + (size_t)kbeg * BITS / 8 + 16 * u);
-      uint32_t* d = reinterpret_cast<uint32_t*>(sact + t * srow + 16 * u);
-      if constexpr (DCfg<BITS>::PADB == 16) {
-        *reinterpret_cast<uint4*>(d) = v;
-      } else {
-        *reinterpret_cast<uint2*>(d) = make_uint2(v.x, v.y);
-        *reinterpret_cast<uint2*>(d + 2) = make_uint2(v.z, v.w);
-      }
+  for (int i = tid; i < CH * MB * 16; i += 256) red[i] = 0;
+
+  // ---- all weight loads of this wave: block b = wave + 4i, channel ch0 + 16cp + c, k [64g, 64g+64)
+  uint4 wq[MAXB][CPW];
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+#pragma unroll
+    for (int cp = 0; cp < CPW; ++cp) {
+      const int n = ch0 + 16 * cp + c;
+      const int kb = kbeg + (wave + 4 * i) * DKB;
+      wq[i][cp] = (i < nb && n < N) ? *reinterpret_cast<const uint4*>(W + (size_t)n * (K / 4) + kb / 4 + 16 * g)
+                                    : make_uint4(0, 0, 0, 0);
     }
   }
+  v4i acc[CPW][MB];
+#pragma unroll
+  for (int cp = 0; cp < CPW; ++cp)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[cp][mb] = v4i{};
 
-  // ---- weights: lane (channel c = lane%16, group g = lane/16) takes k in
-  // [kb*256 + 64g, +64) of every 256-k block: one 16-byte load per block.
-  const int c = lane & 15, g = lane >> 4;
-  // N is a multiple of 16, so a wave's 16 channels are all valid or all past N.
-  const bool wave_ok = nblk * DCH + wave * 16 < N;
-  const int n = wave_ok ? nblk * DCH + wave * 16 + c : 0;
-  const uint8_t* wp = W + (size_t)n * (K / 4) + kbeg / 4 + 16 * g;
-  v4i acc[MB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) acc[i] = v4i{};
-  __syncthreads();
-
-  constexpr int UNR = 8;  // weight loads kept in flight per lane
-  for (int kb0 = 0; kb0 < nkb; kb0 += UNR) {
-    uint4 wq[UNR];
+  for (int i = 0; i < MAXB; ++i) {
+    if (i >= nb) continue;   // wave-uniform; keeps the loop fully unrolled (wq stays in registers)
+    const int kb = kbeg + (wave + 4 * i) * DKB + 64 * g;   // this lane's 64 codes
+    uint4 aq[MB][4];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u)
-      wq[u] = (wave_ok && kb0 + u < nkb) ? *reinterpret_cast<const uint4*>(wp + (size_t)(kb0 + u) * (DKB / 4))
-                                         : make_uint4(0, 0, 0, 0);
+    for (int mb = 0; mb < MB; ++mb) {
+      const int t = 16 * mb + c;
+      const uint8_t* ap = A + (size_t)t * arow + (size_t)kb * BITS / 8;
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      if (kb0 + u >= nkb) break;
-      const int kb = kb0 + u;
+      for (int d = 0; d < BITS / 2; ++d)
+        aq[mb][d] = t < M ? reinterpret_cast<const uint4*>(ap)[d] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t p = j == 0 ? wq[u].x : j == 1 ? wq[u].y : j == 2 ? wq[u].z : wq[u].w;
-        const v4i a = expand_ternary(p);
-        const int kk = kb * DKB + 64 * g + 16 * j;  // k offset inside the slab
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int cp = 0; cp < CPW; ++cp) {
+        const uint4 p = wq[i][cp];
+        const v4i wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int t = mb * 16 + c;
-          v4i b = v4i{};
-          if (t < M) {
-            if constexpr (BITS == 8) {
-              b = *reinterpret_cast<const v4i*>(sact + t * srow + kk);
-            } else {
-              const uint2 w2 = *reinterpret_cast<const uint2*>(sact + t * srow + kk / 2);
-              b = expand_int4(w2.x, w2.y);
-            }
+          v4i aop;
+          if constexpr (BITS == 8) {
+            aop = v4i{(int)u4get(aq[mb][0], j), (int)u4get(aq[mb][1], j), (int)u4get(aq[mb][2], j),
+                      (int)u4get(aq[mb][3], j)};
+          } else {
+            const uint32_t w[8] = {aq[mb][0].x, aq[mb][0].y, aq[mb][0].z, aq[mb][0].w,
+                                   aq[mb][1].x, aq[mb][1].y, aq[mb][1].z, aq[mb][1].w};
+            aop = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
+                      (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
           }
-          acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[mb], 0, 0, 0);
+          acc[cp][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc[cp][mb], 0, 0, 0);
         }
       }
     }
   }
+  __syncthreads();
+  // 16x16 accumulator layout: lane l / register r hold channel 4*(l/16)+r, token l%16
+#pragma unroll
+  for (int cp = 0; cp < CPW; ++cp)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        atomicAdd(&red[(16 * mb + c) * CH + 16 * cp + 4 * g + r], acc[cp][mb][r]);
+  __syncthreads();
 
-  // ---- 16x16 accumulator layout: lane l / register r hold channel 4*(l/16)+r, token l%16
   const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
-  const int ch0 = nblk * DCH + wave * 16 + 4 * g;
-  if (KS == 1) {
-    if (!wave_ok) return;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int t = mb * 16 + c;
-      if (t >= M) continue;
+  for (int e = tid; e < M * CH && e < MB * 16 * CH; e += 256) {
+    const int t = e / CH, n = ch0 + e % CH;
+    if (n >= N) continue;
+    const int v = red[e];
+    if (S == 1) {
       const float tt = OUT == OUT_ACC_I32 ? 0.f : dscale[t] * aw;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) store_out<OUT>(Y, (size_t)t * N + ch0 + r, acc[mb][r], tt);
+      store_out<OUT>(Y, (size_t)t * N + n, unscale<BITS>(v), tt);
+    } else {
+      partial[((size_t)s * M + t) * N + n] = v;
     }
-    return;
   }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int t = mb * 16 + c;
-    if (t >= M || !wave_ok) continue;
-    *reinterpret_cast<int4*>(partial + ((size_t)ks * M + t) * N + ch0) =
-        make_int4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
-  }
-  // Last workgroup of this channel block sums the slabs in slab order.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&counters[nblk], 1) == KS - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int e = tid; e < M * DCH; e += 256) {
-    const int t = e / DCH, ch = nblk * DCH + e % DCH;
-    if (ch >= N) continue;
-    int s = 0;
-    for (int k2 = 0; k2 < KS; ++k2) s += __builtin_nontemporal_load(partial + ((size_t)k2 * M + t) * N + ch);
-    const float tt = OUT == OUT_ACC_I32 ? 0.f : dscale[t] * aw;
-    store_out<OUT>(Y, (size_t)t * N + ch, s, tt);
-  }
-  if (tid == 0) counters[nblk] = 0;
+}
+
+// Sum of the S partials in slab order, then unscale and dequantise.
+template <int BITS, int OUT>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(const int32_t* __restrict__ partial, int S, int M, int N,
+                                                           const float* __restrict__ dscale,
+                                                           const float* __restrict__ walpha, void* __restrict__ Y) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= M * N) return;
+  int v = 0;
+  for (int s = 0; s < S; ++s) v += partial[(size_t)s * M * N + e];
+  const int t = e / N;
+  const float tt = OUT == OUT_ACC_I32 ? 0.f : dscale[t] * fmaxf(walpha[0], kEpsQ);
+  store_out<OUT>(Y, (size_t)e, unscale<BITS>(v), tt);
 }
 
 // ===========================================================================
@@ -369,53 +375,28 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
 
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   if (M > 64 || M <= 0) return 0;
-  // worst case over the two activation widths
-  const int ks = decode_splits((int)M, (int)K, (int)N, 8) > decode_splits((int)M, (int)K, (int)N, 4)
-                     ? decode_splits((int)M, (int)K, (int)N, 8) : decode_splits((int)M, (int)K, (int)N, 4);
-  const size_t part = (size_t)ks * M * N * 4;
-  const size_t cnt = (size_t)((N + DCH - 1) / DCH + 64) * 4;
-  return ((part + 255) & ~(size_t)255) + ((cnt + 255) & ~(size_t)255);
+  const DecodePlan p = decode_plan((int)M, (int)K);
+  return p.S > 1 ? (((size_t)p.S * M * N * 4 + 255) & ~(size_t)255) : 0;
 }
 
-int gemm_zero_words(int64_t M, int64_t K, int64_t N) {
-  (void)K;
-  return (M > 0 && M <= 64) ? (int)((N + DCH - 1) / DCH) : 0;
-}
-
-// Counters live after the partials in the workspace.
-static int* decode_counters(void* ws, int64_t M, int64_t K, int64_t N) {
-  const size_t part = gemm_workspace_bytes(M, K, N) - (((size_t)((N + DCH - 1) / DCH + 64) * 4 + 255) & ~(size_t)255);
-  return reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + part);
-}
-int* gemm_counters(void* ws, int64_t M, int64_t K, int64_t N) { return decode_counters(ws, M, K, N); }
-
-__global__ void zero_i32_kernel(int* __restrict__ p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-hipError_t launch_zero_i32(int* p, int n, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p, n);
-  return hipGetLastError();
+template <int BITS, int MB, int CPW, int OUT>
+static void launch_decode_p(const GemmArgs& a, int S) {
+  constexpr int CH = 16 * CPW;
+  dim3 grid((a.N + CH - 1) / CH, S);
+  int32_t* part = static_cast<int32_t*>(a.ws);
+  hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, OUT>), grid, dim3(256), 0, a.stream, a.codes, a.wpack,
+                     a.dscale, a.walpha, a.out, a.M, a.N, a.K, S, part);
+  if (S > 1)
+    hipLaunchKernelGGL((decode_reduce_kernel<BITS, OUT>), dim3((a.M * a.N + 255) / 256), dim3(256), 0, a.stream,
+                       part, S, a.M, a.N, a.dscale, a.walpha, a.out);
 }
 
 template <int BITS, int OUT>
 static void launch_decode_t(const GemmArgs& a) {
-  const int KS = decode_splits(a.M, a.K, a.N, BITS);
-  const int MB = (a.M + 15) / 16;
-  const size_t lds = (size_t)a.M * ((size_t)(a.K / KS) * BITS / 8 + DCfg<BITS>::PADB);
-  dim3 grid((a.N + DCH - 1) / DCH, KS);
-  int32_t* part = static_cast<int32_t*>(a.ws);
-  int* cnt = decode_counters(a.ws, a.M, a.K, a.N);
-#define HBL_DEC(MBV)                                                                                      \
-  hipLaunchKernelGGL((gemm_decode_kernel<BITS, MBV, OUT>), grid, dim3(256), lds, a.stream, a.codes, a.wpack, \
-                     a.dscale, a.walpha, a.out, a.M, a.N, a.K, KS, part, cnt)
-  switch (MB) {
-    case 1: HBL_DEC(1); break;
-    case 2: HBL_DEC(2); break;
-    case 3: HBL_DEC(3); break;
-    default: HBL_DEC(4); break;
-  }
-#undef HBL_DEC
+  const DecodePlan p = decode_plan(a.M, a.K);
+  if (p.cpw == 1) launch_decode_p<BITS, 1, 1, OUT>(a, p.S);
+  else if (p.cpw == 2) launch_decode_p<BITS, 1, 2, OUT>(a, p.S);
+  else launch_decode_p<BITS, 4, 4, OUT>(a, p.S);
 }
 
 template <int BITS, int OUT>

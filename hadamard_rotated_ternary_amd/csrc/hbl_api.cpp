@@ -77,9 +77,6 @@ hbl_status forward(int bits, const void* x, hbl_dtype x_dtype, const float* gain
   hbl::PrepArgs p{};
   p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.logk = log2_exact(K);
   p.bits = bits; p.mode = 0; p.codes = codes; p.dscale = dscale; p.xt = nullptr;
-  // The prep kernel also clears the matmul's split-K counters.
-  p.zero_n = hbl::gemm_zero_words(M, K, N);
-  p.zero_ptr = p.zero_n ? hbl::gemm_counters(gws, M, K, N) : nullptr;
   p.stream = stream;
   if (hipError_t e = hbl::launch_prep(p)) return launched(e);
 
@@ -188,10 +185,6 @@ static hbl_status matmul(const void* codes, int bits, const float* dscale, const
     return HBL_ERR_ALIGN;
   if (ws_bytes < need) return HBL_ERR_WORKSPACE;
   if (hbl_status s = check_device()) return s;
-  const int zn = hbl::gemm_zero_words(M, K, N);
-  if (zn) {
-    if (hipError_t e = hbl::launch_zero_i32(hbl::gemm_counters(workspace, M, K, N), zn, stream)) return launched(e);
-  }
   hbl::GemmArgs g{};
   g.codes = static_cast<const uint8_t*>(codes); g.bits = bits; g.wpack = w_packed; g.dscale = dscale;
   g.walpha = w_alpha; g.out = out; g.out_kind = out_kind; g.M = (int)M; g.N = (int)N; g.K = (int)K;

@@ -16,8 +16,6 @@ struct PrepArgs {
   uint8_t* codes;
   float* dscale;
   float* xt;
-  int* zero_ptr;     // optional int32 region cleared by the first workgroup
-  int zero_n;
   hipStream_t stream;
 };
 hipError_t launch_prep(const PrepArgs& a);
@@ -33,17 +31,13 @@ struct GemmArgs {
   void* out;
   int out_kind;
   int M, N, K;
-  void* ws;               // split-K partials and counters (decode path)
+  void* ws;               // split-K partials (decode path)
   size_t ws_bytes;
   hipStream_t stream;
 };
 hipError_t launch_gemm(const GemmArgs& a);
 // Workspace bytes the matmul needs beyond the codes and scales.
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
-// Int32 words the matmul needs zeroed before it runs (decode counters), and where they are.
-int gemm_zero_words(int64_t M, int64_t K, int64_t N);
-int* gemm_counters(void* ws, int64_t M, int64_t K, int64_t N);
-hipError_t launch_zero_i32(int* p, int n, hipStream_t stream);
 
 struct WquantArgs {
   const float* w;

@@ -180,17 +180,13 @@ constexpr int prep_wg(int logk, int loge) { return (1 << (logk - loge)) < 64 ? 6
 template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int MODE>
 __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
     const void* __restrict__ x, const float* __restrict__ gain, int M,
-    uint8_t* __restrict__ codes, float* __restrict__ dscale, float* __restrict__ xt,
-    int* __restrict__ zero_ptr, int zero_n) {
+    uint8_t* __restrict__ codes, float* __restrict__ dscale, float* __restrict__ xt) {
   using C = PrepCfg<LOGK, LOGE, P2>;
   using P0 = Pass<LOGK, LOGE, 0>;
   using PL = Pass<LOGK, LOGE, C::NP - 1>;
   constexpr int K = C::K, E = C::E, T = C::T;
   __shared__ __attribute__((aligned(16))) float lds[C::REGION * C::TPB];
   __shared__ float red[16];
-
-  if (zero_ptr != nullptr && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < zero_n; i += C::WG) zero_ptr[i] = 0;
 
   const int tok = threadIdx.x / T;
   const int tau = threadIdx.x % T;
@@ -333,7 +329,7 @@ static hipError_t launch_prep_t(const PrepArgs& a) {
   if (grid == 0) return hipSuccess;
 #define HBL_PREP(BITS, BF, MODE)                                                           \
   hipLaunchKernelGGL((prep_kernel<LOGK, LOGE, P2, BITS, BF, MODE>), dim3(grid), dim3(C::WG), 0, \
-                     a.stream, a.x, a.gain, a.M, a.codes, a.dscale, a.xt, a.zero_ptr, a.zero_n)
+                     a.stream, a.x, a.gain, a.M, a.codes, a.dscale, a.xt)
   if (a.mode == 1) {
     if (a.x_bf16) HBL_PREP(8, true, 1); else HBL_PREP(8, false, 1);
   } else if (a.bits == 8) {

@@ -141,8 +141,7 @@ hbl_status hbl_quantize_act(const void *x, hbl_dtype x_dtype, const float *gain,
  *   codes, dscale as written by hbl_quantize_act;  y [M][N] of y_dtype.
  *   workspace at least hbl_workspace_bytes(HBL_OP_MATMUL, M, K, N) bytes (split-K
  *             scratch of the small-M path; may be NULL when that size is 0).
- *   When the scratch is used, its counters are cleared by a small kernel
- *   enqueued first; calls sharing one workspace must be stream-ordered.
+ *   Calls sharing one workspace must be stream-ordered.
  */
 hbl_status hbl_matmul_dequant(const void *codes, int bits, const float *dscale,
                               const uint8_t *w_packed, const float *w_alpha,

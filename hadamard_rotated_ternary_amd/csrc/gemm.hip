@@ -57,6 +57,25 @@ template <int BITS>
 HBL_DEV int unscale(int v) { return BITS == 8 ? (v >> 6) : (v >> 10); }
 HBL_DEV uint32_t u4get(const uint4& u, int j) { return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w; }
 
+// Copy 16 bytes per lane from global memory straight into LDS: the wave's
+// 64 lanes fill 1 KiB at lds_base (wave-uniform), lane L at +16L.  Issued from
+// inline asm so the compiler does not track it (it cannot tell which LDS
+// buffer such a copy targets and would otherwise wait for every copy before
+// any LDS read); the caller orders it with wait_vmcnt() and s_barrier.  The
+// instruction has no destination registers and reads its address operands at
+// issue.
+HBL_DEV void lds_copy16(const void* gsrc, void* lds_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(l), "v"(gsrc) : "memory", "m0");
+}
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt[3:0] and [15:14], expcnt and lgkmcnt at max).
+template <int N>
+HBL_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int OUT>
 HBL_DEV void store_out(void* Y, size_t off, int acc, float t) {
   if constexpr (OUT == OUT_ACC_I32) {
@@ -98,7 +117,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int tiles_m, int tiles_n) {
   using C = PCfg<BITS>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * C::STAGE];
 
   // Tile order: consecutive workgroups go to different XCDs, so give each XCD
   // a contiguous run of logical tiles, and walk them in groups of 4 tile-rows
@@ -119,34 +138,33 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
   const size_t arow = BITS == 8 ? (size_t)K : (size_t)K / 2;
   const size_t wrow = (size_t)K / 4;
 
-  uint4 ra[C::A_LOADS], rb[C::B_LOADS];
-  auto gload = [&](int kt) {
+  // Global -> LDS directly (global_load_lds_dwordx4: no staging registers),
+  // three LDS stages in a ring so every stage is requested two stages before
+  // it is consumed.  One wave instruction fills 1 KiB of LDS, lane L writing
+  // bytes 16L..16L+15; each lane therefore fetches the global 16-byte unit
+  // that the swizzled layout places at its LDS position.  Rows past M and
+  // channels past N are clamped to the last valid one (never stored), so the
+  // loads are unconditional.
+  const uint8_t* a_src[C::A_LOADS];
+  const uint8_t* b_src[C::B_LOADS];
 #pragma unroll
-    for (int j = 0; j < C::A_LOADS; ++j) {
-      const int q = j * 256 + tid, row = q / C::AUNITS, u = q % C::AUNITS, m = m0 + row;
-      ra[j] = m < M ? *reinterpret_cast<const uint4*>(A + (size_t)m * arow + (size_t)kt * C::ABYTES + 16 * u)
-                    : make_uint4(0, 0, 0, 0);
-    }
+  for (int j = 0; j < C::A_LOADS; ++j) {
+    const int P = (j * 4 + wave) * 64 + lane, row = P / C::AUNITS, u = (P % C::AUNITS) ^ swz_a<BITS>(row);
+    a_src[j] = A + (size_t)min(m0 + row, M - 1) * arow + 16 * u;
+  }
 #pragma unroll
-    for (int j = 0; j < C::B_LOADS; ++j) {
-      const int q = j * 256 + tid, row = q >> 1, u = q & 1, n = n0 + row;
-      rb[j] = n < N ? *reinterpret_cast<const uint4*>(W + (size_t)n * wrow + (size_t)kt * (PBK / 4) + 16 * u)
-                    : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* sa = smem + buf * C::STAGE;
-    uint8_t* sb = sa + C::A_STAGE;
+  for (int j = 0; j < C::B_LOADS; ++j) {
+    const int P = (j * 4 + wave) * 64 + lane, row = P >> 1, u = (P & 1) ^ swz_b(row);
+    b_src[j] = W + (size_t)min(n0 + row, N - 1) * wrow + 16 * u;
+  }
+  auto dma = [&](int kt, int buf) {
+    uint8_t* base = smem + buf * C::STAGE;
 #pragma unroll
-    for (int j = 0; j < C::A_LOADS; ++j) {
-      const int q = j * 256 + tid, row = q / C::AUNITS, u = q % C::AUNITS;
-      *reinterpret_cast<uint4*>(sa + row * C::ABYTES + 16 * (u ^ swz_a<BITS>(row))) = ra[j];
-    }
+    for (int j = 0; j < C::A_LOADS; ++j)
+      lds_copy16(a_src[j] + (size_t)kt * C::ABYTES, base + (j * 4 + wave) * 1024);
 #pragma unroll
-    for (int j = 0; j < C::B_LOADS; ++j) {
-      const int q = j * 256 + tid, row = q >> 1, u = q & 1;
-      *reinterpret_cast<uint4*>(sb + row * 32 + 16 * (u ^ swz_b(row))) = rb[j];
-    }
+    for (int j = 0; j < C::B_LOADS; ++j)
+      lds_copy16(b_src[j] + (size_t)kt * (PBK / 4), base + C::A_STAGE + (j * 4 + wave) * 1024);
   };
 
   v16i acc[4][4];
@@ -155,13 +173,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
 
-  const int KT = K / PBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+  auto compute = [&](int buf) {
     const uint8_t* sa = smem + buf * C::STAGE;
     const uint8_t* sb = sa + C::A_STAGE;
     // weight fragments: 4 packed words = k-chunks 4g..4g+3 of channel n
@@ -212,8 +224,27 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
           acc[rbk][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf[cb], acc[rbk][cb], 0, 0, 0);
       }
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  // Stage kt lives in LDS buffer kt % 3.  Before consuming stage kt a wave
+  // waits for its own copies of that stage (only the next stage's may still
+  // be in flight), then the barrier makes every wave's copies visible and
+  // guarantees that all waves are done with stage kt-1, whose buffer is then
+  // refilled with stage kt+2.
+  constexpr int NL = C::A_LOADS + C::B_LOADS;   // copy instructions per wave per stage
+  const int KT = K / PBK;
+  auto phase = [&](int kt, int buf) {
+    if (kt + 1 < KT) wait_vmcnt<NL>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < KT) dma(kt + 2, buf == 0 ? 2 : buf - 1);
+    compute(buf);
+  };
+  dma(0, 0);
+  if (KT > 1) dma(1, 1);
+  for (int kt = 0; kt < KT; kt += 3) {
+    phase(kt, 0);
+    if (kt + 1 < KT) phase(kt + 1, 1);
+    if (kt + 2 < KT) phase(kt + 2, 2);
   }
 
   // ---- epilogue: 32x32 accumulator layout, lane l / register r hold
@@ -238,11 +269,13 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 // ===========================================================================
 // Decode (M <= 64): weight streaming.
 //
-// A workgroup of 4 waves owns 16*CPW output channels and one of S equal K
-// ranges.  The range is cut into 256-k blocks dealt round-robin to the waves;
-// each wave issues all its packed-weight loads (16 bytes per lane per block)
-// up front, so every weight byte is read from HBM once with the whole stream
-// in flight, and reads the (small, L2-resident) activation codes per block.
+// A workgroup of NW waves owns 16*CPW output channels and one of S equal K
+// ranges.  The range is cut into 256-k blocks dealt round-robin to the waves.
+// Each wave issues every load it will need up front -- per block, its packed
+// weights (16 bytes per lane per 16 channels) and then that block's
+// activation codes -- so the whole weight stream is in flight at once and,
+// because loads retire in issue order, block i can start as soon as its own
+// two loads have landed.  Every weight byte is read from HBM once.
 // v_mfma_i32_16x16x64_i8 runs with channels on the MFMA's M side and up to 16
 // tokens on its N side.  The waves' int32 partials meet in LDS through integer
 // atomics (exact, order free).  With S > 1 a second small kernel sums the S
@@ -250,83 +283,90 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 // the same for every S.
 constexpr int DKB = 256;
 
-struct DecodePlan { int cpw, S, mb; };
+struct DecodePlan { int cpw, S, mb, nw; };
 static DecodePlan decode_plan(int M, int K) {
-  DecodePlan p = M <= 4 ? DecodePlan{1, 1, 1} : M <= 16 ? DecodePlan{2, 2, 1} : DecodePlan{4, 4, 4};
+#ifdef HBL_DECODE_PLAN
+  DecodePlan p = HBL_DECODE_PLAN(M);
+#else
+  DecodePlan p = M <= 16 ? DecodePlan{1, 1, 1, 8} : DecodePlan{4, 4, 4, 4};
+#endif
   while (p.S > 1 && K / p.S < DKB) p.S /= 2;
   return p;
 }
-// Weight blocks a wave may hold in registers (MAXB * CPW uint4 <= 16).
-constexpr int decode_maxb(int cpw) { return 16 / cpw; }
 
-template <int BITS, int MB, int CPW, int OUT>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(
+template <int BITS, int MB, int CPW, int NW, int OUT>
+__global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int S,
     int32_t* __restrict__ partial) {
-  constexpr int MAXB = decode_maxb(CPW);
+  // Blocks held per wave per round: their loads need MAXB * (CPW + MB*BITS/2)
+  // uint4 registers, kept near 48 (192 VGPRs).
+  constexpr int MAXB = (48 / (CPW + MB * BITS / 2)) >= 8 ? 8 : (48 / (CPW + MB * BITS / 2)) >= 4 ? 4 : 2;
   constexpr int CH = 16 * CPW;
   __shared__ int red[CH * MB * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int ch0 = blockIdx.x * CH, s = blockIdx.y;
   const int Kr = K / S, kbeg = s * Kr;
-  const int nblk = Kr / DKB;                       // 256-k blocks in this range
-  const int nb = nblk > wave ? (nblk - wave + 3) / 4 : 0;   // blocks of this wave: wave, wave+4, ...
+  const int nblk = Kr / DKB;                                   // 256-k blocks in this range
   const size_t arow = (size_t)K * BITS / 8;
 
-  for (int i = tid; i < CH * MB * 16; i += 256) red[i] = 0;
+  for (int i = tid; i < CH * MB * 16; i += 64 * NW) red[i] = 0;
 
-  // ---- all weight loads of this wave: block b = wave + 4i, channel ch0 + 16cp + c, k [64g, 64g+64)
-  uint4 wq[MAXB][CPW];
-#pragma unroll
-  for (int i = 0; i < MAXB; ++i) {
-#pragma unroll
-    for (int cp = 0; cp < CPW; ++cp) {
-      const int n = ch0 + 16 * cp + c;
-      const int kb = kbeg + (wave + 4 * i) * DKB;
-      wq[i][cp] = (i < nb && n < N) ? *reinterpret_cast<const uint4*>(W + (size_t)n * (K / 4) + kb / 4 + 16 * g)
-                                    : make_uint4(0, 0, 0, 0);
-    }
-  }
   v4i acc[CPW][MB];
 #pragma unroll
   for (int cp = 0; cp < CPW; ++cp)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[cp][mb] = v4i{};
 
+  // Blocks b = wave + NW*i, taken MAXB at a time.
+  for (int b0 = wave; b0 < nblk; b0 += NW * MAXB) {
+    uint4 wq[MAXB][CPW];
+    uint4 aq[MAXB][MB][BITS / 2];
+    // Loads are unconditional (out-of-range indices are clamped to valid
+    // addresses and the values discarded), so the compiler can release block i
+    // with a partial vmcnt wait instead of waiting for every load.
 #pragma unroll
-  for (int i = 0; i < MAXB; ++i) {
-    if (i >= nb) continue;   // wave-uniform; keeps the loop fully unrolled (wq stays in registers)
-    const int kb = kbeg + (wave + 4 * i) * DKB + 64 * g;   // this lane's 64 codes
-    uint4 aq[MB][4];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int t = 16 * mb + c;
-      const uint8_t* ap = A + (size_t)t * arow + (size_t)kb * BITS / 8;
-#pragma unroll
-      for (int d = 0; d < BITS / 2; ++d)
-        aq[mb][d] = t < M ? reinterpret_cast<const uint4*>(ap)[d] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int i = 0; i < MAXB; ++i) {
+      const int b = min(b0 + NW * i, nblk - 1);
+      const int kb = kbeg + b * DKB + 64 * g;                 // this lane's 64 codes of block b
 #pragma unroll
       for (int cp = 0; cp < CPW; ++cp) {
-        const uint4 p = wq[i][cp];
-        const v4i wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
+        const int n = min(ch0 + 16 * cp + c, N - 1);
+        wq[i][cp] = *reinterpret_cast<const uint4*>(W + (size_t)n * (K / 4) + kb / 4);
+      }
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          v4i aop;
-          if constexpr (BITS == 8) {
-            aop = v4i{(int)u4get(aq[mb][0], j), (int)u4get(aq[mb][1], j), (int)u4get(aq[mb][2], j),
-                      (int)u4get(aq[mb][3], j)};
-          } else {
-            const uint32_t w[8] = {aq[mb][0].x, aq[mb][0].y, aq[mb][0].z, aq[mb][0].w,
-                                   aq[mb][1].x, aq[mb][1].y, aq[mb][1].z, aq[mb][1].w};
-            aop = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
-                      (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
+      for (int mb = 0; mb < MB; ++mb) {
+        const int t = min(16 * mb + c, M - 1);
+        const uint4* ap = reinterpret_cast<const uint4*>(A + (size_t)t * arow + (size_t)kb * BITS / 8);
+#pragma unroll
+        for (int d = 0; d < BITS / 2; ++d) aq[i][mb][d] = ap[d];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXB; ++i) {
+      if (b0 + NW * i >= nblk) continue;   // wave-uniform; keeps the loop unrolled (registers, no scratch)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int cp = 0; cp < CPW; ++cp) {
+          const uint4 p = wq[i][cp];
+          const v4i wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            v4i aop;
+            if constexpr (BITS == 8) {
+              aop = v4i{(int)u4get(aq[i][mb][0], j), (int)u4get(aq[i][mb][1], j), (int)u4get(aq[i][mb][2], j),
+                        (int)u4get(aq[i][mb][3], j)};
+            } else {
+              const uint4 q0 = aq[i][mb][0], q1 = aq[i][mb][1];
+              const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+              aop = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
+                        (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
+            }
+            if (16 * mb + c >= M) aop = v4i{};   // padding tokens
+            acc[cp][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc[cp][mb], 0, 0, 0);
           }
-          acc[cp][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc[cp][mb], 0, 0, 0);
         }
       }
     }
@@ -339,11 +379,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        atomicAdd(&red[(16 * mb + c) * CH + 16 * cp + 4 * g + r], acc[cp][mb][r]);
+        if (16 * mb + c < M) atomicAdd(&red[(16 * mb + c) * CH + 16 * cp + 4 * g + r], acc[cp][mb][r]);
   __syncthreads();
 
   const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
-  for (int e = tid; e < M * CH && e < MB * 16 * CH; e += 256) {
+  for (int e = tid; e < M * CH; e += 64 * NW) {
     const int t = e / CH, n = ch0 + e % CH;
     if (n >= N) continue;
     const int v = red[e];
@@ -379,13 +419,13 @@ size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   return p.S > 1 ? (((size_t)p.S * M * N * 4 + 255) & ~(size_t)255) : 0;
 }
 
-template <int BITS, int MB, int CPW, int OUT>
+template <int BITS, int MB, int CPW, int NW, int OUT>
 static void launch_decode_p(const GemmArgs& a, int S) {
   constexpr int CH = 16 * CPW;
   dim3 grid((a.N + CH - 1) / CH, S);
   int32_t* part = static_cast<int32_t*>(a.ws);
-  hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, OUT>), grid, dim3(256), 0, a.stream, a.codes, a.wpack,
-                     a.dscale, a.walpha, a.out, a.M, a.N, a.K, S, part);
+  hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, NW, OUT>), grid, dim3(64 * NW), 0, a.stream, a.codes,
+                     a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K, S, part);
   if (S > 1)
     hipLaunchKernelGGL((decode_reduce_kernel<BITS, OUT>), dim3((a.M * a.N + 255) / 256), dim3(256), 0, a.stream,
                        part, S, a.M, a.N, a.dscale, a.walpha, a.out);
@@ -394,9 +434,11 @@ static void launch_decode_p(const GemmArgs& a, int S) {
 template <int BITS, int OUT>
 static void launch_decode_t(const GemmArgs& a) {
   const DecodePlan p = decode_plan(a.M, a.K);
-  if (p.cpw == 1) launch_decode_p<BITS, 1, 1, OUT>(a, p.S);
-  else if (p.cpw == 2) launch_decode_p<BITS, 1, 2, OUT>(a, p.S);
-  else launch_decode_p<BITS, 4, 4, OUT>(a, p.S);
+#ifdef HBL_DECODE_VARIANTS
+  HBL_DECODE_VARIANTS
+#endif
+  if (p.mb == 1) launch_decode_p<BITS, 1, 1, 8, OUT>(a, p.S);
+  else launch_decode_p<BITS, 4, 4, 4, OUT>(a, p.S);
 }
 
 template <int BITS, int OUT>

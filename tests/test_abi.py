@@ -49,7 +49,7 @@ def test_workspace_sizes(L):
     assert ws8 >= 8192 * 16384 + 8192 * 4 and ws4 >= 8192 * 16384 // 2 + 8192 * 4
     assert ws4 < ws8
     assert L.hbl_workspace_bytes(0, 0, 16384, 4096) >= 4096 * 8
-    assert L.hbl_workspace_bytes(1, 16, 16384, 4096) > 0      # split-K scratch of the small-M path
+    assert L.hbl_workspace_bytes(1, 64, 16384, 4096) > 0      # split-K scratch of the small-M path
     assert L.hbl_workspace_bytes(1, 1, 16384, 4096) == 0      # one token: no split
     assert L.hbl_workspace_bytes(1, 8192, 16384, 4096) == 0
     assert L.hbl_workspace_bytes(3, 1, 256, 16) == 0
@@ -91,8 +91,8 @@ def test_stage_validation(L):
     assert L.hbl_rmsnorm_fwht(A, 1, None, 0, 256, A, S) == OK
     assert L.hbl_gemm_ternary(A, 5, A, 4, 256, 256, A, None, 0, S) == DTYPE
     assert L.hbl_gemm_ternary(A, 8, A, 4, 256, 250, A, None, 0, S) == SHAPE
-    assert L.hbl_gemm_ternary(A, 8, A, 16, 1024, 256, A, None, 0, S) == NULL     # split small-M needs scratch
-    assert L.hbl_gemm_ternary(A, 8, A, 16, 1024, 256, A, A2, 16, S) == WORKSPACE
+    assert L.hbl_gemm_ternary(A, 8, A, 64, 1024, 256, A, None, 0, S) == NULL     # split small-M needs scratch
+    assert L.hbl_gemm_ternary(A, 8, A, 64, 1024, 256, A, A2, 16, S) == WORKSPACE
     assert L.hbl_matmul_dequant(A, 8, None, A, A, 100, 256, 256, A, 1, None, 0, S) == NULL
     assert L.hbl_quantize_weights(A, 256, 255, A, A, A, 1 << 20, S) == SHAPE
     assert L.hbl_quantize_weights(A, 256, 256, A, A, A, 8, S) == WORKSPACE

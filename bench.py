@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "H-BitLinear tokens/s + effective int TOPS & HBM GB/s vs roofline, 7B Wdown"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_prefill_wdown_7b.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wdown_7b_int4_hbm_traffic.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "hadamard_rotated_ternary_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
 
 
@@ -189,16 +189,18 @@ def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup):
 
 
 def stored_traffic(workload):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if
-    they were taken on the current matmul source; otherwise None."""
+    """HBM bytes per matmul launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), if they were taken on
+    the current matmul source and this workload; otherwise None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
         return None
-    if t.get("source_sha") != gemm_source_sha() or t.get("workload") != workload:
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha") != gemm_source_sha() or kv.get("workload") != workload:
         return None
-    return t.get("bytes_per_launch")
+    return int(kv["bytes_per_launch"])
 
 
 def extras(torch, hbl, synthetic, args):

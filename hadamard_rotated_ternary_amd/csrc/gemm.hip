@@ -312,6 +312,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
   const size_t arow = (size_t)K * BITS / 8;
 
   for (int i = tid; i < CH * MB * 16; i += 64 * NW) red[i] = 0;
+  // epilogue scales fetched up front (their latency is not paid at the end)
+  const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
+  float ds_pre[(MB * 16 * CH + 64 * NW - 1) / (64 * NW)];
+#pragma unroll
+  for (int q = 0; q < (MB * 16 * CH + 64 * NW - 1) / (64 * NW); ++q)
+    ds_pre[q] = OUT == OUT_ACC_I32 ? 0.f : dscale[min((q * 64 * NW + tid) / CH, M - 1)];
 
   v4i acc[CPW][MB];
 #pragma unroll
@@ -382,17 +388,105 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
         if (16 * mb + c < M) atomicAdd(&red[(16 * mb + c) * CH + 16 * cp + 4 * g + r], acc[cp][mb][r]);
   __syncthreads();
 
-  const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
-  for (int e = tid; e < M * CH; e += 64 * NW) {
+#pragma unroll
+  for (int q = 0; q < (MB * 16 * CH + 64 * NW - 1) / (64 * NW); ++q) {
+    const int e = q * 64 * NW + tid;
+    if (e >= M * CH) continue;
     const int t = e / CH, n = ch0 + e % CH;
     if (n >= N) continue;
     const int v = red[e];
-    if (S == 1) {
-      const float tt = OUT == OUT_ACC_I32 ? 0.f : dscale[t] * aw;
-      store_out<OUT>(Y, (size_t)t * N + n, unscale<BITS>(v), tt);
+    if (S == 1) store_out<OUT>(Y, (size_t)t * N + n, unscale<BITS>(v), ds_pre[q] * aw);
+    else partial[((size_t)s * M + t) * N + n] = v;
+  }
+}
+
+// Few tokens (M <= 4): one workgroup of NW waves per 16 channels and the whole
+// K.  The tokens' activation codes are staged once per workgroup in LDS,
+// already in MFMA operand form (int8; INT4 codes as 16*q), so each MFMA step
+// only expands its packed weights.  The staging load is issued before the
+// weight stream so waiting for it is a partial wait.  Lanes of padding tokens
+// read a zeroed 64-byte LDS row.
+template <int BITS, int NW, int UPT, int OUT>
+__global__ __launch_bounds__(64 * NW) void gemm_decode_few_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
+    const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t slab[];   // [M][K] int8 operands, then 64 zero bytes
+  __shared__ int red[16 * 16];
+  constexpr int MAXB = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int ch0 = blockIdx.x * 16;
+  const int nblk = K / DKB;
+  const size_t arow = (size_t)K * BITS / 8;
+
+  // ---- epilogue scales, fetched first so their latency is not paid at the end
+  const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
+  const float ds_mine = OUT == OUT_ACC_I32 ? 0.f : dscale[min(tid / 16, M - 1)];
+  // ---- activation staging load (issued first): UPT 16-byte units per thread,
+  // UPT * 64 * NW >= M * K * BITS / 128 (chosen by the launcher).
+  const int units = M * (int)(arow / 16);
+  uint4 st[UPT];
+#pragma unroll
+  for (int q = 0; q < UPT; ++q) st[q] = reinterpret_cast<const uint4*>(A)[min(q * 64 * NW + tid, units - 1)];
+  // ---- weight stream: blocks b = wave + NW*i (NW*MAXB*256 >= K for K <= 16384)
+  uint4 wq[MAXB];
+  const int n = min(ch0 + c, N - 1);
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    const int b = min(wave + NW * i, nblk - 1);
+    wq[i] = *reinterpret_cast<const uint4*>(W + (size_t)n * (K / 4) + (size_t)b * (DKB / 4) + 16 * g);
+  }
+  // ---- operand form of the staged codes, token rows of K bytes
+  const int opr = K;
+  const int upr = (int)(arow / 16);                        // packed units per token row
+#pragma unroll
+  for (int q = 0; q < UPT; ++q) {
+    const int u = q * 64 * NW + tid;
+    if (u >= units) continue;
+    const int t = u / upr, ub = u % upr;
+    if constexpr (BITS == 8) {
+      *reinterpret_cast<uint4*>(slab + t * opr + 16 * ub) = st[q];
     } else {
-      partial[((size_t)s * M + t) * N + n] = v;
+      // 32 INT4 codes -> 32 operand bytes 16*q in k order
+      const uint32_t w[4] = {st[q].x, st[q].y, st[q].z, st[q].w};
+      uint4 o0, o1;
+      o0.x = (w[0] << 4) & 0xF0F0F0F0u; o0.y = w[0] & 0xF0F0F0F0u;
+      o0.z = (w[1] << 4) & 0xF0F0F0F0u; o0.w = w[1] & 0xF0F0F0F0u;
+      o1.x = (w[2] << 4) & 0xF0F0F0F0u; o1.y = w[2] & 0xF0F0F0F0u;
+      o1.z = (w[3] << 4) & 0xF0F0F0F0u; o1.w = w[3] & 0xF0F0F0F0u;
+      *reinterpret_cast<uint4*>(slab + t * opr + 32 * ub) = o0;
+      *reinterpret_cast<uint4*>(slab + t * opr + 32 * ub + 16) = o1;
     }
+  }
+  if (tid < 4) reinterpret_cast<uint4*>(slab + M * opr)[tid] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < 256; i += 64 * NW) red[i] = 0;
+  __syncthreads();
+
+  v4i acc = v4i{};
+  const uint8_t* arow_lds = c < M ? slab + c * opr + 64 * g : slab + M * opr;
+  const int astep = c < M ? 1 : 0;                         // padding lanes keep reading the zero row
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    const int b = wave + NW * i;
+    if (b >= nblk) continue;                               // wave-uniform
+    const uint4* ap = reinterpret_cast<const uint4*>(arow_lds + astep * b * DKB);
+    const uint4 a0 = ap[0], a1 = ap[1], a2 = ap[2], a3 = ap[3];
+    const uint4 p = wq[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4i wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
+      const v4i aop = v4i{(int)u4get(a0, j), (int)u4get(a1, j), (int)u4get(a2, j), (int)u4get(a3, j)};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc, 0, 0, 0);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (c < M) atomicAdd(&red[c * 16 + 4 * g + r], acc[r]);
+  __syncthreads();
+  if (tid < M * 16) {   // M <= 4: one pass covers every (token, channel)
+    const int t = tid / 16, nn = ch0 + tid % 16;
+    if (nn < N) store_out<OUT>(Y, (size_t)t * N + nn, unscale<BITS>(red[tid]), ds_mine * aw);
   }
 }
 
@@ -431,8 +525,31 @@ static void launch_decode_p(const GemmArgs& a, int S) {
                        part, S, a.M, a.N, a.dscale, a.walpha, a.out);
 }
 
+template <int BITS, int UPT, int OUT>
+static void launch_decode_few_u(const GemmArgs& a) {
+  const size_t lds = (size_t)a.M * a.K + 64;
+  static bool attr = false;   // same value from every thread; set before the first launch
+  if (!attr) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode_few_kernel<BITS, 8, UPT, OUT>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    attr = true;
+  }
+  hipLaunchKernelGGL((gemm_decode_few_kernel<BITS, 8, UPT, OUT>), dim3((a.N + 15) / 16), dim3(512), lds,
+                     a.stream, a.codes, a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K);
+}
+
+template <int BITS, int OUT>
+static void launch_decode_few(const GemmArgs& a) {
+  const long units = (long)a.M * a.K * BITS / 128;        // 16-byte units of packed codes
+  if (units <= 512) launch_decode_few_u<BITS, 1, OUT>(a);
+  else if (units <= 1024) launch_decode_few_u<BITS, 2, OUT>(a);
+  else if (units <= 2048) launch_decode_few_u<BITS, 4, OUT>(a);
+  else launch_decode_few_u<BITS, 8, OUT>(a);
+}
+
 template <int BITS, int OUT>
 static void launch_decode_t(const GemmArgs& a) {
+  if (a.M <= 4) { launch_decode_few<BITS, OUT>(a); return; }
   const DecodePlan p = decode_plan(a.M, a.K);
 #ifdef HBL_DECODE_VARIANTS
   HBL_DECODE_VARIANTS

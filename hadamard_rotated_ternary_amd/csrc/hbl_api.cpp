@@ -13,15 +13,18 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
-int g_dev_ok[kMaxDevices];  // 1 = gfx950, 0 = not supported
+int g_dev_ok[kMaxDevices];   // 1 = gfx950, 0 = not supported
+int g_dev_cus[kMaxDevices];  // compute units
 
-hbl_status check_device() {
+hbl_status check_device(int* cus = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HBL_ERR_DEVICE;
   std::call_once(g_dev_once[dev], [dev] {
     hipDeviceProp_t p;
     g_dev_ok[dev] = hipGetDeviceProperties(&p, dev) == hipSuccess && strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    g_dev_cus[dev] = g_dev_ok[dev] ? p.multiProcessorCount : 0;
   });
+  if (cus) *cus = g_dev_cus[dev];
   return g_dev_ok[dev] ? HBL_OK : HBL_ERR_DEVICE;
 }
 
@@ -66,7 +69,8 @@ hbl_status forward(int bits, const void* x, hbl_dtype x_dtype, const float* gain
     return HBL_ERR_ALIGN;
   if (ws_bytes < hbl_workspace_bytes(bits == 8 ? HBL_OP_FORWARD_INT8 : HBL_OP_FORWARD_INT4, M, K, N))
     return HBL_ERR_WORKSPACE;
-  if (hbl_status s = check_device()) return s;
+  int cus = 0;
+  if (hbl_status s = check_device(&cus)) return s;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* codes = ws;
@@ -75,7 +79,7 @@ hbl_status forward(int bits, const void* x, hbl_dtype x_dtype, const float* gain
   const size_t gws_bytes = hbl::gemm_workspace_bytes(M, K, N);
 
   hbl::PrepArgs p{};
-  p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.logk = log2_exact(K);
+  p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
   p.bits = bits; p.mode = 0; p.codes = codes; p.dscale = dscale; p.xt = nullptr;
   p.stream = stream;
   if (hipError_t e = hbl::launch_prep(p)) return launched(e);
@@ -149,9 +153,10 @@ hbl_status hbl_quantize_act(const void* x, hbl_dtype x_dtype, const float* gain,
   if (M == 0) return HBL_OK;
   if (!x || !codes || !dscale) return HBL_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(dscale) || (gain && !aligned16(gain))) return HBL_ERR_ALIGN;
-  if (hbl_status s = check_device()) return s;
+  int cus = 0;
+  if (hbl_status s = check_device(&cus)) return s;
   hbl::PrepArgs p{};
-  p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.logk = log2_exact(K);
+  p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
   p.bits = bits; p.mode = 0; p.codes = static_cast<uint8_t*>(codes); p.dscale = dscale; p.stream = stream;
   return launched(hbl::launch_prep(p));
 }
@@ -163,9 +168,10 @@ hbl_status hbl_rmsnorm_fwht(const void* x, hbl_dtype x_dtype, const float* gain,
   if (M == 0) return HBL_OK;
   if (!x || !xt) return HBL_ERR_NULL;
   if (!aligned16(x) || !aligned16(xt) || (gain && !aligned16(gain))) return HBL_ERR_ALIGN;
-  if (hbl_status s = check_device()) return s;
+  int cus = 0;
+  if (hbl_status s = check_device(&cus)) return s;
   hbl::PrepArgs p{};
-  p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.logk = log2_exact(K);
+  p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
   p.bits = 8; p.mode = 1; p.xt = xt; p.stream = stream;
   return launched(hbl::launch_prep(p));
 }

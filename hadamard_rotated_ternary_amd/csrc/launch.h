@@ -10,6 +10,7 @@ struct PrepArgs {
   bool x_bf16;
   const float* gain;
   int M;
+  int cus;           // compute units of the device (persistent grid size)
   int logk;
   int bits;          // 8 or 4
   int mode;          // 0: codes + scales, 1: rotated activations (fp32)

@@ -174,9 +174,19 @@ HBL_DEV void run_passes(float (&v)[1 << LOGE], float* region, int tau) {
   }
 }
 
+// Raw activations of one thread for one token: E values, 16-byte units.
+template <int E, bool XBF16>
+struct RawX {
+  static constexpr int U = XBF16 ? E / 8 : E / 4;
+  uint4 u[U];
+};
+
 // MODE 0: write codes + scales.  MODE 1: write the rotated activations (fp32).
 constexpr int prep_wg(int logk, int loge) { return (1 << (logk - loge)) < 64 ? 64 : (1 << (logk - loge)); }
 
+// Persistent: a workgroup walks tokens blockIdx.x*TPB + tok, then + gridDim.x*TPB,
+// ...; the next token's activations are requested right after the current
+// ones have been unpacked, so their HBM latency hides behind the transform.
 template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int MODE>
 __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
     const void* __restrict__ x, const float* __restrict__ gain, int M,
@@ -190,127 +200,154 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
 
   const int tok = threadIdx.x / T;
   const int tau = threadIdx.x % T;
-  const int m = blockIdx.x * C::TPB + tok;
-  const bool valid = m < M;
   float* region = lds + tok * C::REGION;
-
-  // ---- load (pass-0 dealing: 8 contiguous features per 16-byte load)
-  float v[E];
+  const int stride = gridDim.x * C::TPB;
+  const int first = blockIdx.x * C::TPB;
+  const int iters = first < M ? (M - first + stride - 1) / stride : 0;   // uniform over the workgroup
   const int base0 = P0::thr_idx(tau);
-#pragma unroll
-  for (int g = 0; g < E / 8; ++g) {
-    const int idx = base0 + P0::reg_idx(8 * g);
-    if constexpr (XBF16) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (valid) w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (size_t)m * K + idx);
-      v[8 * g + 0] = bf16_lo(w.x); v[8 * g + 1] = bf16_hi(w.x);
-      v[8 * g + 2] = bf16_lo(w.y); v[8 * g + 3] = bf16_hi(w.y);
-      v[8 * g + 4] = bf16_lo(w.z); v[8 * g + 5] = bf16_hi(w.z);
-      v[8 * g + 6] = bf16_lo(w.w); v[8 * g + 7] = bf16_hi(w.w);
-    } else {
-      float4 a = make_float4(0, 0, 0, 0), b = a;
-      if (valid) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)m * K + idx);
-        a = p[0]; b = p[1];
-      }
-      v[8 * g + 0] = a.x; v[8 * g + 1] = a.y; v[8 * g + 2] = a.z; v[8 * g + 3] = a.w;
-      v[8 * g + 4] = b.x; v[8 * g + 5] = b.y; v[8 * g + 6] = b.z; v[8 * g + 7] = b.w;
-    }
-  }
-  // ---- RMSNorm statistic (of x, before the gain)
-  float ss = 0.f;
-#pragma unroll
-  for (int r = 0; r < E; ++r) ss += v[r] * v[r];
-  ss = token_reduce<T, false>(ss, red);
-  if (gain != nullptr) {
-#pragma unroll
-    for (int g = 0; g < E / 8; ++g) {
-      const int idx = base0 + P0::reg_idx(8 * g);
-      const float4* p = reinterpret_cast<const float4*>(gain + idx);
-      const float4 a = p[0], b = p[1];
-      v[8 * g + 0] *= a.x; v[8 * g + 1] *= a.y; v[8 * g + 2] *= a.z; v[8 * g + 3] *= a.w;
-      v[8 * g + 4] *= b.x; v[8 * g + 5] *= b.y; v[8 * g + 6] *= b.z; v[8 * g + 7] *= b.w;
-    }
-  }
-  // c = 1 / (r * sqrt(K)), r = sqrt(mean x^2 + eps)
-  const float rr = sqrtf(ss * (1.0f / K) + kEpsNorm);
-  const float c = 1.0f / (rr * sqrtf((float)K));
-
-  // ---- Walsh-Hadamard transform (unnormalised) of x*g
-  run_passes<LOGK, LOGE, P2, 0>(v, region, tau);
-
   const int baseL = PL::thr_idx(tau);
-  if constexpr (MODE == 1) {
-    if (valid) {
-#pragma unroll
-      for (int r = 0; r < E; ++r) xt[(size_t)m * K + baseL + PL::reg_idx(r)] = v[r] * c;
-    }
-    return;
-  } else {
-    // ---- per-token statistic of the rotated token xt = v * c
-    float st = 0.f;
-    if constexpr (BITS == 8) {
-#pragma unroll
-      for (int r = 0; r < E; ++r) st = fmaxf(st, fabsf(v[r]));
-      st = token_reduce<T, true>(st, red);
-      st = st * c;
-    } else {
-#pragma unroll
-      for (int r = 0; r < E; ++r) st += fabsf(v[r]);
-      st = token_reduce<T, false>(st, red);
-      st = (st * (1.0f / K)) * c;
-    }
-    const float Q = BITS == 8 ? kQ8 : kQ4;
-    const float G = fmaxf(st, kEpsQ);
-    const float s = Q / G;
-    const float cs = c * s;
-    if (valid && tau == 0) dscale[m] = G / Q;
 
-    // ---- round to codes; gather them through LDS for coalesced stores
-    uint8_t* bytes = reinterpret_cast<uint8_t*>(region);
+  // pass-0 dealing: 8 contiguous features per 16-byte (bf16) or 2x16-byte (fp32) load
+  RawX<E, XBF16> raw;
+  auto load = [&](int m) {
+    const bool ok = m < M;
+    const int mm = ok ? m : M - 1;
 #pragma unroll
-    for (int r = 0; r < E; ++r) {
-      float q = v[r] * cs;
-      if constexpr (BITS == 4) q = fminf(fmaxf(q, -8.0f), 7.0f);
-      const float t = q + kRoundMagic;
-      bytes[padb(baseL + PL::reg_idx(r))] = (uint8_t)__float_as_uint(t);
+    for (int gi = 0; gi < E / 8; ++gi) {
+      const int idx = base0 + P0::reg_idx(8 * gi);
+      if constexpr (XBF16) {
+        raw.u[gi] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (size_t)mm * K + idx);
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + (size_t)mm * K + idx);
+        raw.u[2 * gi] = p[0];
+        raw.u[2 * gi + 1] = p[1];
+      }
     }
-    __syncthreads();
-    if (!valid) return;
-    if constexpr (BITS == 8) {
-      // int8 codes: thread tau stores 16-byte chunks j*T + tau
-      uint8_t* out = codes + (size_t)m * K;
+  };
+  if (iters > 0) load(first + tok);
+
+  for (int it = 0; it < iters; ++it) {
+    const int m = first + tok + it * stride;
+    const bool valid = m < M;
+    float v[E];
 #pragma unroll
-      for (int j = 0; j < E / 16; ++j) {
-        const int ch = j * T + tau;
-        const int b = padb(16 * ch);
-        const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + b);
-        *reinterpret_cast<uint4*>(out + 16 * ch) = make_uint4(s4[0], s4[1], s4[2], s4[3]);
+    for (int gi = 0; gi < E / 8; ++gi) {
+      if constexpr (XBF16) {
+        const uint4 w = raw.u[gi];
+        v[8 * gi + 0] = bf16_lo(w.x); v[8 * gi + 1] = bf16_hi(w.x);
+        v[8 * gi + 2] = bf16_lo(w.y); v[8 * gi + 3] = bf16_hi(w.y);
+        v[8 * gi + 4] = bf16_lo(w.z); v[8 * gi + 5] = bf16_hi(w.z);
+        v[8 * gi + 6] = bf16_lo(w.w); v[8 * gi + 7] = bf16_hi(w.w);
+      } else {
+        const uint4 a = raw.u[2 * gi], b = raw.u[2 * gi + 1];
+        v[8 * gi + 0] = __uint_as_float(a.x); v[8 * gi + 1] = __uint_as_float(a.y);
+        v[8 * gi + 2] = __uint_as_float(a.z); v[8 * gi + 3] = __uint_as_float(a.w);
+        v[8 * gi + 4] = __uint_as_float(b.x); v[8 * gi + 5] = __uint_as_float(b.y);
+        v[8 * gi + 6] = __uint_as_float(b.z); v[8 * gi + 7] = __uint_as_float(b.w);
+      }
+    }
+    if (it + 1 < iters) load(m + stride);
+    if (!valid) {
+#pragma unroll
+      for (int r = 0; r < E; ++r) v[r] = 0.f;
+    }
+
+    // ---- RMSNorm statistic (of x, before the gain)
+    float ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < E; ++r) ss = __builtin_fmaf(v[r], v[r], ss);
+    ss = token_reduce<T, false>(ss, red);
+    if (gain != nullptr) {
+#pragma unroll
+      for (int gi = 0; gi < E / 8; ++gi) {
+        const int idx = base0 + P0::reg_idx(8 * gi);
+        const float4* p = reinterpret_cast<const float4*>(gain + idx);
+        const float4 a = p[0], b = p[1];
+        v[8 * gi + 0] *= a.x; v[8 * gi + 1] *= a.y; v[8 * gi + 2] *= a.z; v[8 * gi + 3] *= a.w;
+        v[8 * gi + 4] *= b.x; v[8 * gi + 5] *= b.y; v[8 * gi + 6] *= b.z; v[8 * gi + 7] *= b.w;
+      }
+    }
+    // c = 1 / (r * sqrt(K)), r = sqrt(mean x^2 + eps)
+    const float rr = sqrtf(ss * (1.0f / K) + kEpsNorm);
+    const float c = 1.0f / (rr * sqrtf((float)K));
+
+    // ---- Walsh-Hadamard transform (unnormalised) of x*g
+    run_passes<LOGK, LOGE, P2, 0>(v, region, tau);
+
+    if constexpr (MODE == 1) {
+      if (valid) {
+#pragma unroll
+        for (int r = 0; r < E; ++r) xt[(size_t)m * K + baseL + PL::reg_idx(r)] = v[r] * c;
       }
     } else {
-      // int4 codes: 8 consecutive codes per 32-bit word, code k0+4j+i at bits 8i+4j
-      uint8_t* out = codes + (size_t)m * (K / 2);
-      constexpr int OB = E / 2;  // output bytes per thread
-      if constexpr (OB >= 16) {
+      // ---- per-token statistic of the rotated token xt = v * c
+      float st = 0.f;
+      if constexpr (BITS == 8) {
 #pragma unroll
-        for (int j = 0; j < OB / 16; ++j) {
-          const int ch = j * T + tau;  // 16 output bytes = 32 codes
-          const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(32 * ch));
-          uint32_t w[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            w[i] = (s4[2 * i] & 0x0F0F0F0Fu) | ((s4[2 * i + 1] & 0x0F0F0F0Fu) << 4);
-          *reinterpret_cast<uint4*>(out + 16 * ch) = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+        for (int r = 0; r < E; ++r) st = fmaxf(st, fabsf(v[r]));
+        st = token_reduce<T, true>(st, red);
+        st = st * c;
       } else {
-        static_assert(OB == 8, "E >= 16");
-        const int ch = tau;  // 8 output bytes = 16 codes
-        const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(16 * ch));
-        uint32_t w0 = (s4[0] & 0x0F0F0F0Fu) | ((s4[1] & 0x0F0F0F0Fu) << 4);
-        uint32_t w1 = (s4[2] & 0x0F0F0F0Fu) | ((s4[3] & 0x0F0F0F0Fu) << 4);
-        *reinterpret_cast<uint2*>(out + 8 * ch) = make_uint2(w0, w1);
+#pragma unroll
+        for (int r = 0; r < E; ++r) st += fabsf(v[r]);
+        st = token_reduce<T, false>(st, red);
+        st = (st * (1.0f / K)) * c;
+      }
+      const float Q = BITS == 8 ? kQ8 : kQ4;
+      const float G = fmaxf(st, kEpsQ);
+      const float s = Q / G;
+      const float cs = c * s;
+      if (valid && tau == 0) dscale[m] = G / Q;
+
+      // ---- round to codes: fma(v, cs, 1.5*2^23) rounds v*cs to the nearest
+      // integer (ties to even) and leaves it in the low mantissa bits; INT4
+      // clamps in that representation.  Codes are gathered through LDS for
+      // coalesced stores.
+      uint8_t* bytes = reinterpret_cast<uint8_t*>(region);
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        float t = __builtin_fmaf(v[r], cs, kRoundMagic);
+        if constexpr (BITS == 4) t = fminf(fmaxf(t, kRoundMagic - 8.0f), kRoundMagic + 7.0f);
+        bytes[padb(baseL + PL::reg_idx(r))] = (uint8_t)__float_as_uint(t);
+      }
+      __syncthreads();
+      if (valid) {
+        if constexpr (BITS == 8) {
+          // int8 codes: thread tau stores 16-byte chunks j*T + tau
+          uint8_t* out = codes + (size_t)m * K;
+#pragma unroll
+          for (int j = 0; j < E / 16; ++j) {
+            const int ch = j * T + tau;
+            const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(16 * ch));
+            *reinterpret_cast<uint4*>(out + 16 * ch) = make_uint4(s4[0], s4[1], s4[2], s4[3]);
+          }
+        } else {
+          // int4 codes: 8 consecutive codes per 32-bit word, code k0+4j+i at bits 8i+4j
+          uint8_t* out = codes + (size_t)m * (K / 2);
+          constexpr int OB = E / 2;  // output bytes per thread
+          if constexpr (OB >= 16) {
+#pragma unroll
+            for (int j = 0; j < OB / 16; ++j) {
+              const int ch = j * T + tau;  // 16 output bytes = 32 codes
+              const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(32 * ch));
+              uint32_t w[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                w[i] = (s4[2 * i] & 0x0F0F0F0Fu) | ((s4[2 * i + 1] & 0x0F0F0F0Fu) << 4);
+              *reinterpret_cast<uint4*>(out + 16 * ch) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+          } else {
+            static_assert(OB == 8, "E >= 16");
+            const int ch = tau;  // 8 output bytes = 16 codes
+            const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(16 * ch));
+            uint32_t w0 = (s4[0] & 0x0F0F0F0Fu) | ((s4[1] & 0x0F0F0F0Fu) << 4);
+            uint32_t w1 = (s4[2] & 0x0F0F0F0Fu) | ((s4[3] & 0x0F0F0F0Fu) << 4);
+            *reinterpret_cast<uint2*>(out + 8 * ch) = make_uint2(w0, w1);
+          }
+        }
       }
     }
+    __syncthreads();   // the region is rewritten by the next token
   }
 }
 
@@ -325,7 +362,11 @@ namespace hbl {
 template <int LOGK, int LOGE, int P2>
 static hipError_t launch_prep_t(const PrepArgs& a) {
   using C = PrepCfg<LOGK, LOGE, P2>;
-  const int grid = (a.M + C::TPB - 1) / C::TPB;
+  // persistent grid: enough workgroups to fill every CU at the occupancy the
+  // LDS footprint allows (two workgroups per CU for the prefill dealings)
+  const int per_cu = (160 * 1024) / (int)(sizeof(float) * C::REGION * C::TPB + 64) >= 2 ? 2 : 1;
+  const int want = (a.M + C::TPB - 1) / C::TPB;
+  const int grid = want < a.cus * per_cu ? want : a.cus * per_cu;
   if (grid == 0) return hipSuccess;
 #define HBL_PREP(BITS, BF, MODE)                                                           \
   hipLaunchKernelGGL((prep_kernel<LOGK, LOGE, P2, BITS, BF, MODE>), dim3(grid), dim3(C::WG), 0, \

@@ -146,7 +146,8 @@ def test_zero_token_and_tiny_token():
 # ------------------------------------------------------------------ integer matmul
 
 @pytest.mark.parametrize("bits", [8, 4])
-@pytest.mark.parametrize("M,K,N", [(1, 256, 16), (7, 512, 272), (16, 2048, 512), (33, 4096, 64),
+@pytest.mark.parametrize("M,K,N", [(1, 256, 16), (2, 1024, 48), (4, 16384, 272), (3, 8192, 4096),
+                                   (7, 512, 272), (16, 2048, 512), (33, 4096, 64),
                                    (64, 16384, 128), (65, 256, 256), (300, 1024, 272), (512, 2048, 512),
                                    (257, 16384, 528)])
 def test_matmul_bit_exact(bits, M, K, N):

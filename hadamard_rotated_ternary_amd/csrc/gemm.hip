@@ -89,35 +89,44 @@ HBL_DEV void store_out(void* Y, size_t off, int acc, float t) {
 
 // ===========================================================================
 // Prefill
-constexpr int PBM = 256, PBN = 256, PBK = 128;
+constexpr int PBM = 256, PBN = 256;
 
-template <int BITS>
+// Stage geometry: BK codes of K per stage (128 or 256).
+template <int BITS, int BK>
 struct PCfg {
-  static constexpr int ABYTES = BITS == 8 ? PBK : PBK / 2;  // A bytes per row per stage
-  static constexpr int AUNITS = ABYTES / 16;
+  static constexpr int ABYTES = BK * BITS / 8;        // A bytes per row per stage
+  static constexpr int AUNITS = ABYTES / 16;          // 16-byte units per A row
+  static constexpr int BBYTES = BK / 4;               // packed weight bytes per row per stage
+  static constexpr int BUNITS = BBYTES / 16;
   static constexpr int A_STAGE = PBM * ABYTES;
-  static constexpr int B_STAGE = PBN * (PBK / 4);
+  static constexpr int B_STAGE = PBN * BBYTES;
   static constexpr int STAGE = A_STAGE + B_STAGE;
-  static constexpr int A_LOADS = A_STAGE / 16 / 256;
-  static constexpr int B_LOADS = B_STAGE / 16 / 256;
+  static constexpr int A_COPIES = A_STAGE / 16;        // 16-byte copies per stage
+  static constexpr int B_COPIES = B_STAGE / 16;
+  static constexpr int HALVES = BK / 128;             // 128-k sub-steps per stage
+  static_assert(AUNITS == 4 || AUNITS == 8, "row of 4 or 8 units");
+  static_assert(BUNITS == 2 || BUNITS == 4, "row of 2 or 4 units");
 };
 
-// XOR swizzles of the 16-byte units of an LDS row, chosen so the MFMA
-// fragment reads (8 or 16 lanes per LDS cycle, rows r..r+7 / r+15 of one
-// unit column) and the staging writes hit distinct banks.
-template <int BITS>
-HBL_DEV int swz_a(int row) {
-  if constexpr (BITS == 8) return (row ^ (row >> 3)) & 7;
-  else return ((row >> 1) ^ (row >> 3)) & 3;
+// XOR swizzles of the 16-byte units of an LDS row (U units per row), chosen
+// so that the MFMA fragment reads (8 or 16 lanes per LDS cycle: rows r..r+7 or
+// r..r+15 of one unit column) and the copies hit distinct banks.
+template <int U>
+HBL_DEV int swz(int row) {
+  if constexpr (U == 8) return (row ^ (row >> 3)) & 7;
+  else if constexpr (U == 4) return ((row >> 1) ^ (row >> 3)) & 3;
+  else return ((row >> 2) ^ (row >> 3)) & 1;
 }
-HBL_DEV int swz_b(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
 
-template <int BITS, int OUT>
-__global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
+// NWV waves: 2 along M (128 rows each) and NWV/2 along N (256/(NWV/2) columns).
+template <int BITS, int BK, int NWV, int OUT>
+__global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int tiles_m, int tiles_n) {
-  using C = PCfg<BITS>;
+  using C = PCfg<BITS, BK>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[3 * C::STAGE];
+  constexpr int A_LOADS = C::A_COPIES / (64 * NWV), B_LOADS = C::B_COPIES / (64 * NWV);
+  static_assert(A_LOADS * 64 * NWV == C::A_COPIES && B_LOADS * 64 * NWV == C::B_COPIES, "copies per thread");
 
   // Tile order: consecutive workgroups go to different XCDs, so give each XCD
   // a contiguous run of logical tiles, and walk them in groups of 4 tile-rows
@@ -132,8 +141,11 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
   const int m0 = (first_m + in_g % gm) * PBM;
   const int n0 = (in_g / gm) * PBN;
 
+  constexpr int NT = 64 * NWV;                 // threads
+  constexpr int WNW = NWV / 2;                 // waves along N
+  constexpr int CB = 256 / (WNW * 32);         // 32-column blocks per wave (4 or 2)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int l32 = lane & 31, g = lane >> 5;
   const size_t arow = BITS == 8 ? (size_t)K : (size_t)K / 2;
   const size_t wrow = (size_t)K / 4;
@@ -145,83 +157,88 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
   // that the swizzled layout places at its LDS position.  Rows past M and
   // channels past N are clamped to the last valid one (never stored), so the
   // loads are unconditional.
-  const uint8_t* a_src[C::A_LOADS];
-  const uint8_t* b_src[C::B_LOADS];
+  const uint8_t* a_src[A_LOADS];
+  const uint8_t* b_src[B_LOADS];
 #pragma unroll
-  for (int j = 0; j < C::A_LOADS; ++j) {
-    const int P = (j * 4 + wave) * 64 + lane, row = P / C::AUNITS, u = (P % C::AUNITS) ^ swz_a<BITS>(row);
+  for (int j = 0; j < A_LOADS; ++j) {
+    const int P = (j * NWV + wave) * 64 + lane, row = P / C::AUNITS, u = (P % C::AUNITS) ^ swz<C::AUNITS>(row);
     a_src[j] = A + (size_t)min(m0 + row, M - 1) * arow + 16 * u;
   }
 #pragma unroll
-  for (int j = 0; j < C::B_LOADS; ++j) {
-    const int P = (j * 4 + wave) * 64 + lane, row = P >> 1, u = (P & 1) ^ swz_b(row);
+  for (int j = 0; j < B_LOADS; ++j) {
+    const int P = (j * NWV + wave) * 64 + lane, row = P / C::BUNITS, u = (P % C::BUNITS) ^ swz<C::BUNITS>(row);
     b_src[j] = W + (size_t)min(n0 + row, N - 1) * wrow + 16 * u;
   }
   auto dma = [&](int kt, int buf) {
     uint8_t* base = smem + buf * C::STAGE;
 #pragma unroll
-    for (int j = 0; j < C::A_LOADS; ++j)
-      lds_copy16(a_src[j] + (size_t)kt * C::ABYTES, base + (j * 4 + wave) * 1024);
+    for (int j = 0; j < A_LOADS; ++j)
+      lds_copy16(a_src[j] + (size_t)kt * C::ABYTES, base + (j * NWV + wave) * 1024);
 #pragma unroll
-    for (int j = 0; j < C::B_LOADS; ++j)
-      lds_copy16(b_src[j] + (size_t)kt * (PBK / 4), base + C::A_STAGE + (j * 4 + wave) * 1024);
+    for (int j = 0; j < B_LOADS; ++j)
+      lds_copy16(b_src[j] + (size_t)kt * C::BBYTES, base + C::A_STAGE + (j * NWV + wave) * 1024);
   };
 
-  v16i acc[4][4];
+  v16i acc[4][CB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+    for (int j = 0; j < CB; ++j) acc[i][j] = v16i{};
 
   auto compute = [&](int buf) {
     const uint8_t* sa = smem + buf * C::STAGE;
     const uint8_t* sb = sa + C::A_STAGE;
-    // weight fragments: 4 packed words = k-chunks 4g..4g+3 of channel n
-    uint4 bq[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int n = wn * 128 + cb * 32 + l32;
-      bq[cb] = *reinterpret_cast<const uint4*>(sb + n * 32 + 16 * (g ^ swz_b(n)));
-    }
-    // activation fragments: k-chunks 4g..4g+3 of row m (64 codes)
-    uint4 aq[4][4];
+    for (int hh = 0; hh < C::HALVES; ++hh) {
+      // weight fragments: 4 packed words = k-chunks 4g..4g+3 (of this 128-k half) of channel n
+      uint4 bq[CB];
 #pragma unroll
-    for (int rbk = 0; rbk < 4; ++rbk) {
-      const int row = wm * 128 + rbk * 32 + l32;
-      if constexpr (BITS == 8) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          aq[rbk][d] = *reinterpret_cast<const uint4*>(sa + row * 128 + 16 * ((4 * g + d) ^ swz_a<8>(row)));
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          aq[rbk][h] = *reinterpret_cast<const uint4*>(sa + row * 64 + 16 * ((2 * g + h) ^ swz_a<4>(row)));
+      for (int cb = 0; cb < CB; ++cb) {
+        const int n = wn * (32 * CB) + cb * 32 + l32;
+        bq[cb] = *reinterpret_cast<const uint4*>(sb + n * C::BBYTES + 16 * ((2 * hh + g) ^ swz<C::BUNITS>(n)));
       }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v4i bf[4];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-        bf[cb] = v4i{(int)wfield(bq[cb].x, j), (int)wfield(bq[cb].y, j), (int)wfield(bq[cb].z, j),
-                     (int)wfield(bq[cb].w, j)};
+      // activation fragments: k-chunks 4g..4g+3 of row m (64 codes)
+      uint4 aq[4][4];
 #pragma unroll
       for (int rbk = 0; rbk < 4; ++rbk) {
-        v4i af;
+        const int row = wm * 128 + rbk * 32 + l32;
         if constexpr (BITS == 8) {
-          // dword j of chunks 4g..4g+3: codes 16d + 4j .. +3
-          af = v4i{(int)u4get(aq[rbk][0], j), (int)u4get(aq[rbk][1], j), (int)u4get(aq[rbk][2], j),
-                   (int)u4get(aq[rbk][3], j)};
-        } else {
-          // chunk d = words 2d, 2d+1 of the 32 bytes; step j uses word 2d + j/2
-          const uint32_t w[8] = {aq[rbk][0].x, aq[rbk][0].y, aq[rbk][0].z, aq[rbk][0].w,
-                                 aq[rbk][1].x, aq[rbk][1].y, aq[rbk][1].z, aq[rbk][1].w};
-          af = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
-                   (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
-        }
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          acc[rbk][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf[cb], acc[rbk][cb], 0, 0, 0);
+          for (int d = 0; d < 4; ++d)
+            aq[rbk][d] = *reinterpret_cast<const uint4*>(
+                sa + row * C::ABYTES + 16 * ((8 * hh + 4 * g + d) ^ swz<C::AUNITS>(row)));
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            aq[rbk][h] = *reinterpret_cast<const uint4*>(
+                sa + row * C::ABYTES + 16 * ((4 * hh + 2 * g + h) ^ swz<C::AUNITS>(row)));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v4i bf[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          bf[cb] = v4i{(int)wfield(bq[cb].x, j), (int)wfield(bq[cb].y, j), (int)wfield(bq[cb].z, j),
+                       (int)wfield(bq[cb].w, j)};
+#pragma unroll
+        for (int rbk = 0; rbk < 4; ++rbk) {
+          v4i af;
+          if constexpr (BITS == 8) {
+            // dword j of chunks 4g..4g+3: codes 16d + 4j .. +3
+            af = v4i{(int)u4get(aq[rbk][0], j), (int)u4get(aq[rbk][1], j), (int)u4get(aq[rbk][2], j),
+                     (int)u4get(aq[rbk][3], j)};
+          } else {
+            // chunk d = words 2d, 2d+1 of the 32 bytes; step j uses word 2d + j/2
+            const uint32_t w[8] = {aq[rbk][0].x, aq[rbk][0].y, aq[rbk][0].z, aq[rbk][0].w,
+                                   aq[rbk][1].x, aq[rbk][1].y, aq[rbk][1].z, aq[rbk][1].w};
+            af = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
+                     (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
+          }
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[rbk][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf[cb], acc[rbk][cb], 0, 0, 0);
+        }
       }
     }
   };
@@ -231,8 +248,8 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
   // be in flight), then the barrier makes every wave's copies visible and
   // guarantees that all waves are done with stage kt-1, whose buffer is then
   // refilled with stage kt+2.
-  constexpr int NL = C::A_LOADS + C::B_LOADS;   // copy instructions per wave per stage
-  const int KT = K / PBK;
+  constexpr int NL = A_LOADS + B_LOADS;   // copy instructions per wave per stage
+  const int KT = K / BK;
   auto phase = [&](int kt, int buf) {
     if (kt + 1 < KT) wait_vmcnt<NL>(); else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
@@ -258,8 +275,8 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
       if (m >= M) continue;
       const float t = OUT == OUT_ACC_I32 ? 0.f : dscale[m] * aw;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int n = n0 + wn * 128 + cb * 32 + l32;
+      for (int cb = 0; cb < CB; ++cb) {
+        const int n = n0 + wn * (32 * CB) + cb * 32 + l32;
         if (n < N) store_out<OUT>(Y, (size_t)m * N + n, unscale<BITS>(acc[rbk][cb][r]), t);
       }
     }
@@ -558,11 +575,20 @@ static void launch_decode_t(const GemmArgs& a) {
   else launch_decode_p<BITS, 4, 4, 4, OUT>(a, p.S);
 }
 
+// INT4 stages hold 256 k (3 x 48 KiB of LDS), INT8 stages 128 k (3 x 40 KiB).
+// INT4 runs 8 waves (2 per SIMD: one wave's operand expansion overlaps the
+// other's MFMAs); INT8 keeps 4 (its wider activation fragments would spill).
+template <int BITS>
+constexpr int prefill_waves() { return BITS == 4 ? 8 : 4; }
+template <int BITS>
+constexpr int prefill_bk() { return BITS == 4 ? 256 : 128; }
+
 template <int BITS, int OUT>
 static void launch_prefill_t(const GemmArgs& a) {
   const int tm = (a.M + PBM - 1) / PBM, tn = (a.N + PBN - 1) / PBN;
-  hipLaunchKernelGGL((gemm_prefill_kernel<BITS, OUT>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,
-                     a.dscale, a.walpha, a.out, a.M, a.N, a.K, tm, tn);
+  hipLaunchKernelGGL((gemm_prefill_kernel<BITS, prefill_bk<BITS>(), prefill_waves<BITS>(), OUT>), dim3(tm * tn),
+                     dim3(64 * prefill_waves<BITS>()), 0, a.stream, a.codes, a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K,
+                     tm, tn);
 }
 
 template <int BITS, int OUT>

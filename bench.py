@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "H-BitLinear tokens/s + effective int TOPS & HBM GB/s vs roofline, 7B Wdown"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+PEAK_FP6_TFLOPS = 10100.0    # MI355X dense fp6 / fp4 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wdown_7b_int4_hbm_traffic.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "hadamard_rotated_ternary_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
@@ -111,6 +112,8 @@ def main():
     ops = 2.0 * M * N * K
     achieved = ops / gemm_s / 1e12
     traffic = stored_traffic(args.workload)
+    fp6 = bits == 4 and M > 64
+    kernel, peak = ("gemm_fp6_kernel", PEAK_FP6_TFLOPS) if fp6 else ("gemm_prefill_kernel", PEAK_INT8_TOPS)
 
     out = {
         "metric": METRIC,
@@ -123,18 +126,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": "fp6xfp4" if fp6 else "i8",
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "K": K, "N": N, "activation_bits": bits,
                    "x_dtype": w.x_dtype, "y_dtype": w.x_dtype, "parallelism": "single-gpu"},
         "effective_int_tops": ops / step_s / 1e12,
         "hbm_gbps_algorithmic": algorithmic_bytes(M, K, N) / step_s / 1e9,
-        "roofline": {"kernel": "gemm_prefill_kernel", "bound": "mfma", "achieved": achieved,
-                     "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": achieved / PEAK_INT8_TOPS,
+        "roofline": {"kernel": kernel, "bound": "mfma", "achieved": achieved,
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic},
         "kernels": {
             "prep_ms": res["prep_ms"], "gemm_ms": res["gemm_ms"],
-            "prep_gbps_impl": (M * K * 2 + M * K * bits / 8 + M * 4) / (res["prep_ms"] / 1e3) / 1e9,
+            "prep_gbps_impl": (M * K * 2 + M * hbl.codes_row_bytes(6 if fp6 else bits, K) + M * 4)
+                              / (res["prep_ms"] / 1e3) / 1e9,
             "gemm_tops": achieved,
             "forward_entry_ms": res["forward_ms"],
         },
@@ -148,8 +152,12 @@ def main():
 
 
 def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup):
-    """Time `steps` forwards; events between the two kernels give per-kernel times."""
-    codes = torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
+    """Time `steps` forwards; events between the two kernels give per-kernel times.
+    The two stage calls launch the same kernels as the single-call forward (the
+    INT4 forward of more than 64 tokens keeps its codes in the fp6 operand
+    layout, format 6)."""
+    sb = 6 if bits == 4 and M > 64 else bits
+    codes = torch.empty((M, hbl.codes_row_bytes(sb, K)), dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
     d = torch.empty(M + 4, dtype=torch.float32, device="cuda")[:M]
     y = torch.empty((M, N), dtype=xd.dtype, device="cuda")
     ws = torch.empty(max(hbl.workspace_bytes(hbl.OP_MATMUL, M, K, N), 16), dtype=torch.uint8, device="cuda")
@@ -158,9 +166,9 @@ def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup):
 
     def step(evs=None):
         if evs: evs[0].record()
-        hbl.quantize_act(xd, bits, out=(codes, d))
+        hbl.quantize_act(xd, sb, out=(codes, d))
         if evs: evs[1].record()
-        hbl.matmul_dequant(codes, bits, d, wp, a, K, workspace=ws, out=y)
+        hbl.matmul_dequant(codes, sb, d, wp, a, K, workspace=ws, out=y)
         if evs: evs[2].record()
 
     for _ in range(warmup):

@@ -133,6 +133,14 @@ def forward(x: torch.Tensor, w_packed: torch.Tensor, w_alpha: torch.Tensor, bits
     return y
 
 
+BITS_INT4, BITS_INT4_FP6, BITS_INT8 = 4, 6, 8
+
+
+def codes_row_bytes(bits: int, K: int) -> int:
+    """Bytes per token of the activation codes in format `bits` (8, 4 or 6)."""
+    return {8: K, 4: K // 2, 6: K // 4 * 3}[bits]
+
+
 def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, out=None):
     """Stage 1: x [M][K] -> (codes, per-token scales fp32 [M])."""
     _dev(x, "x")
@@ -140,7 +148,7 @@ def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, o
     if out is not None:
         codes, d = out
     else:
-        codes = torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
+        codes = torch.empty((M, codes_row_bytes(bits, K)), dtype=torch.int8 if bits == 8 else torch.uint8,
                             device=x.device)
         d = torch.empty(M + 4, dtype=torch.float32, device=x.device)[:M]
     _call("hbl_quantize_act", _ptr(x), _dtype_code(x.dtype), _ptr(gain), M, K, bits, _ptr(codes), _ptr(d),

@@ -284,6 +284,177 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
 }
 
 // ===========================================================================
+// INT4 prefill on the fp6 x fp4 matrix instruction
+// (v_mfma_scale_f32_32x32x64_f8f6f4, A in e2m3, B in e2m1, unit scales).
+//
+// gfx950 runs this instruction at twice the int8 rate.  Every INT4 code q is
+// an e2m3 value once halved (q/2 in [-4, 3.5]); a ternary weight w doubled
+// is an e2m1 value (2w in {-2, 0, 2}).  Each product is the integer q*w and
+// every partial sum is an integer below 2^24 in magnitude, so the fp32
+// accumulator holds the exact integer dot product whatever the order of
+// accumulation.
+//
+// A comes from prep mode 2: per token one 24-byte group per 32 k, six-bit
+// fields in the operand order.  B stays the packed 2-bit format: masking
+// bits 2-3 and 6-7 of every byte of a packed word (after a left shift by 2
+// for fields 0 and 2) leaves, nibble by nibble, the e2m1 code of 2w
+// (code 01 -> 0100 = +2, 11 -> 1100 = -2).  Word w0 (k0..k0+15) gives operand
+// dwords 0 and 1, word w1 (k0+16..k0+31) dwords 2 and 3; the fp6 field order
+// matches that nibble order.
+//
+// 256x256 tile per workgroup of 4 waves (2x2, 128x128 each), 128 k per LDS
+// stage (A 96 bytes per row, B 32 bytes per column), 4 stages in a ring with
+// copies issued 3 stages ahead.  Lane group g of the 64-k instruction takes
+// 32-k group 2g+s of the stage in step s, so every lane reads 48 contiguous
+// A bytes and 16 contiguous B bytes per stage.
+constexpr int F6_BK = 128, F6_NBUF = 4;
+constexpr int F6_AROW = F6_BK / 4 * 3;             // 96 bytes of fp6 codes per row per stage
+constexpr int F6_BROW = F6_BK / 4;                 // 32 bytes of packed weights per column
+constexpr int F6_A_STAGE = PBM * F6_AROW;          // 24 KiB
+constexpr int F6_B_STAGE = PBN * F6_BROW;          // 8 KiB
+constexpr int F6_STAGE = F6_A_STAGE + F6_B_STAGE;  // 32 KiB
+
+// LDS rows of A hold 6 units of 16 bytes; rows with bit 2 set are rotated by
+// one unit, so 8 consecutive rows reading the same unit hit 8 distinct 4-bank
+// groups.  B columns hold 2 units, swapped on the same row bit.
+HBL_DEV int f6_arot(int row) { return (row >> 2) & 1; }
+
+template <int OUT>
+__global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
+    const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[F6_NBUF * F6_STAGE];
+  constexpr int A_LOADS = F6_A_STAGE / 16 / 256, B_LOADS = F6_B_STAGE / 16 / 256;   // 6 and 2
+  constexpr int NL = A_LOADS + B_LOADS;
+
+  const int bid = blockIdx.x, total = tiles_m * tiles_n;
+  const int logical = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
+  constexpr int GM = 4;
+  const int per_group = GM * tiles_n;
+  const int first_m = (logical / per_group) * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int in_g = logical % per_group;
+  const int m0 = (first_m + in_g % gm) * PBM;
+  const int n0 = (in_g / gm) * PBN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, g = lane >> 5;
+  const size_t arow = (size_t)K / 4 * 3;
+  const size_t wrow = (size_t)K / 4;
+
+  // copy P of a stage fills LDS bytes 16P..16P+15 (wave instruction = 1 KiB)
+  const uint8_t* a_src[A_LOADS];
+  const uint8_t* b_src[B_LOADS];
+#pragma unroll
+  for (int j = 0; j < A_LOADS; ++j) {
+    const int P = (j * 4 + wave) * 64 + lane, row = P / 6, pu = P % 6;
+    int u = pu - f6_arot(row);
+    if (u < 0) u += 6;
+    a_src[j] = A + (size_t)min(m0 + row, M - 1) * arow + 16 * u;
+  }
+#pragma unroll
+  for (int j = 0; j < B_LOADS; ++j) {
+    const int P = (j * 4 + wave) * 64 + lane, row = P >> 1, u = (P & 1) ^ f6_arot(row);
+    b_src[j] = W + (size_t)min(n0 + row, N - 1) * wrow + 16 * u;
+  }
+  auto dma = [&](int kt) __attribute__((always_inline)) {
+    uint8_t* base = smem + (kt & (F6_NBUF - 1)) * F6_STAGE;
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j)
+      lds_copy16(a_src[j] + (size_t)kt * F6_AROW, base + (j * 4 + wave) * 1024);
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j)
+      lds_copy16(b_src[j] + (size_t)kt * F6_BROW, base + F6_A_STAGE + (j * 4 + wave) * 1024);
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+  auto compute = [&](int kt) __attribute__((always_inline)) {
+    const uint8_t* sa = smem + (kt & (F6_NBUF - 1)) * F6_STAGE;
+    const uint8_t* sb = sa + F6_A_STAGE;
+    v4i bq[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int n = wn * 128 + cb * 32 + l32;
+      bq[cb] = *reinterpret_cast<const v4i*>(sb + n * F6_BROW + 16 * (g ^ f6_arot(n)));
+    }
+    v4i aq[4][3];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int row = wm * 128 + rb * 32 + l32;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        int pu = 3 * g + t + f6_arot(row);
+        if (pu >= 6) pu -= 6;
+        aq[rb][t] = *reinterpret_cast<const v4i*>(sa + row * F6_AROW + 16 * pu);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      v8i bf[4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const uint32_t w0 = (uint32_t)bq[cb][2 * st], w1 = (uint32_t)bq[cb][2 * st + 1];
+        bf[cb] = v8i{(int)((w0 << 2) & 0xCCCCCCCCu), (int)(w0 & 0xCCCCCCCCu), (int)((w1 << 2) & 0xCCCCCCCCu),
+                     (int)(w1 & 0xCCCCCCCCu), 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        // dwords 6st .. 6st+5 of the lane's 12 A dwords
+        int a[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) a[i] = aq[rb][(6 * st + i) >> 2][(6 * st + i) & 3];
+        const v8i af = v8i{a[0], a[1], a[2], a[3], a[4], a[5], 0, 0};
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[cb], acc[rb][cb], 2, 4, 0, 127, 0, 127);
+      }
+    }
+  };
+
+  // Stage kt lives in buffer kt % 4.  Before stage kt: wait for this wave's
+  // copies of kt (up to two later stages may still be in flight), then the
+  // barrier (every wave's copies of kt have landed and every wave is done
+  // with stage kt-1), then refill stage kt-1's buffer with stage kt+3.
+  const int KT = K / F6_BK;
+  for (int j = 0; j < F6_NBUF - 1; ++j)
+    if (j < KT) dma(j);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int later = min(KT - 1 - kt, F6_NBUF - 2);
+    if (later >= 2) wait_vmcnt<2 * NL>();
+    else if (later == 1) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+    if (kt + F6_NBUF - 1 < KT) dma(kt + F6_NBUF - 1);
+    compute(kt);
+  }
+
+  // epilogue: 32x32 accumulator layout, lane l / register r hold
+  // row 8*(r/4) + 4*(l/32) + r%4, column l%32.  The accumulators are exact
+  // integers below 2^24.
+  const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 128 + rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (m >= M) continue;
+      const float t = OUT == OUT_ACC_I32 ? 0.f : dscale[m] * aw;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int n = n0 + wn * 128 + cb * 32 + l32;
+        if (n < N) store_out<OUT>(Y, (size_t)m * N + n, (int)acc[rb][cb][r], t);
+      }
+    }
+  }
+}
+
+// ===========================================================================
 // Decode (M <= 64): weight streaming.
 //
 // A workgroup of NW waves owns 16*CPW output channels and one of S equal K
@@ -595,6 +766,21 @@ template <int BITS, int OUT>
 static void launch_t(const GemmArgs& a) {
   if (a.M <= 64) launch_decode_t<BITS, OUT>(a);
   else launch_prefill_t<BITS, OUT>(a);
+}
+
+hipError_t launch_gemm_fp6(const GemmArgs& a) {
+  if (a.M == 0) return hipSuccess;
+  const int tm = (a.M + PBM - 1) / PBM, tn = (a.N + PBN - 1) / PBN;
+#define HBL_F6(OUT)                                                                                       \
+  hipLaunchKernelGGL((gemm_fp6_kernel<OUT>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack, a.dscale, \
+                     a.walpha, a.out, a.M, a.N, a.K, tm, tn)
+  switch (a.out_kind) {
+    case OUT_ACC_I32: HBL_F6(OUT_ACC_I32); break;
+    case OUT_F32: HBL_F6(OUT_F32); break;
+    default: HBL_F6(OUT_BF16); break;
+  }
+#undef HBL_F6
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& a) {

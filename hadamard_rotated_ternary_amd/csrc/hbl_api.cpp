@@ -51,8 +51,13 @@ bool valid_dtype(hbl_dtype d) { return d == HBL_F32 || d == HBL_BF16; }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Forward workspace: [codes][scales][matmul scratch].
-size_t codes_bytes(int bits, int64_t M, int64_t K) { return align256((size_t)M * K * bits / 8); }
+// Forward workspace: [codes][scales][matmul scratch].  The INT4 prefill
+// (M > kFp6MinM) keeps its codes in the six-bit operand layout of the fp6 x
+// fp4 matrix instruction.
+bool fp6_path(int bits, int64_t M) { return bits == 4 && M > hbl::kFp6MinM; }
+size_t codes_bytes(int bits, int64_t M, int64_t K) {
+  return align256((size_t)M * K * (fp6_path(bits, M) ? 6 : bits) / 8);
+}
 size_t scales_bytes(int64_t M) { return align256((size_t)M * 4); }
 
 hbl_status launched(hipError_t e) { return e == hipSuccess ? HBL_OK : HBL_ERR_LAUNCH; }
@@ -80,7 +85,7 @@ hbl_status forward(int bits, const void* x, hbl_dtype x_dtype, const float* gain
 
   hbl::PrepArgs p{};
   p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
-  p.bits = bits; p.mode = 0; p.codes = codes; p.dscale = dscale; p.xt = nullptr;
+  p.bits = bits; p.mode = fp6_path(bits, M) ? 2 : 0; p.codes = codes; p.dscale = dscale; p.xt = nullptr;
   p.stream = stream;
   if (hipError_t e = hbl::launch_prep(p)) return launched(e);
 
@@ -88,7 +93,7 @@ hbl_status forward(int bits, const void* x, hbl_dtype x_dtype, const float* gain
   g.codes = codes; g.bits = bits; g.wpack = w_packed; g.dscale = dscale; g.walpha = w_alpha; g.out = y;
   g.out_kind = y_dtype == HBL_BF16 ? hbl::OUT_BF16 : hbl::OUT_F32;
   g.M = (int)M; g.N = (int)N; g.K = (int)K; g.ws = gws; g.ws_bytes = gws_bytes; g.stream = stream;
-  return launched(hbl::launch_gemm(g));
+  return launched(fp6_path(bits, M) ? hbl::launch_gemm_fp6(g) : hbl::launch_gemm(g));
 }
 
 }  // namespace
@@ -148,7 +153,7 @@ hbl_status hbl_forward_int4(const void* x, hbl_dtype x_dtype, const float* gain,
 
 hbl_status hbl_quantize_act(const void* x, hbl_dtype x_dtype, const float* gain, int64_t M, int64_t K, int bits,
                             void* codes, float* dscale, hipStream_t stream) {
-  if (!valid_dtype(x_dtype) || (bits != 8 && bits != 4)) return HBL_ERR_DTYPE;
+  if (!valid_dtype(x_dtype) || (bits != 8 && bits != 4 && bits != HBL_BITS_INT4_FP6)) return HBL_ERR_DTYPE;
   if (hbl_status s = check_shape(M, K, 16)) return s;
   if (M == 0) return HBL_OK;
   if (!x || !codes || !dscale) return HBL_ERR_NULL;
@@ -157,7 +162,8 @@ hbl_status hbl_quantize_act(const void* x, hbl_dtype x_dtype, const float* gain,
   if (hbl_status s = check_device(&cus)) return s;
   hbl::PrepArgs p{};
   p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
-  p.bits = bits; p.mode = 0; p.codes = static_cast<uint8_t*>(codes); p.dscale = dscale; p.stream = stream;
+  p.bits = bits == 8 ? 8 : 4; p.mode = bits == HBL_BITS_INT4_FP6 ? 2 : 0;
+  p.codes = static_cast<uint8_t*>(codes); p.dscale = dscale; p.stream = stream;
   return launched(hbl::launch_prep(p));
 }
 
@@ -179,12 +185,13 @@ hbl_status hbl_rmsnorm_fwht(const void* x, hbl_dtype x_dtype, const float* gain,
 static hbl_status matmul(const void* codes, int bits, const float* dscale, const uint8_t* w_packed,
                          const float* w_alpha, int64_t M, int64_t K, int64_t N, void* out, int out_kind,
                          void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (bits != 8 && bits != 4) return HBL_ERR_DTYPE;
+  if (bits != 8 && bits != 4 && bits != HBL_BITS_INT4_FP6) return HBL_ERR_DTYPE;
   if (hbl_status s = check_shape(M, K, N)) return s;
   if (M == 0) return HBL_OK;
   if (!codes || !w_packed || !out) return HBL_ERR_NULL;
   if (out_kind != hbl::OUT_ACC_I32 && (!dscale || !w_alpha)) return HBL_ERR_NULL;
-  const size_t need = align256(hbl::gemm_workspace_bytes(M, K, N));
+  const bool fp6 = bits == HBL_BITS_INT4_FP6;
+  const size_t need = fp6 ? 0 : align256(hbl::gemm_workspace_bytes(M, K, N));
   if (need && !workspace) return HBL_ERR_NULL;
   if (!aligned16(codes) || !aligned16(w_packed) || !aligned16(out) || (dscale && !aligned16(dscale)) ||
       (w_alpha && !aligned16(w_alpha)) || (workspace && !aligned16(workspace)))
@@ -195,7 +202,7 @@ static hbl_status matmul(const void* codes, int bits, const float* dscale, const
   g.codes = static_cast<const uint8_t*>(codes); g.bits = bits; g.wpack = w_packed; g.dscale = dscale;
   g.walpha = w_alpha; g.out = out; g.out_kind = out_kind; g.M = (int)M; g.N = (int)N; g.K = (int)K;
   g.ws = workspace; g.ws_bytes = ws_bytes; g.stream = stream;
-  return launched(hbl::launch_gemm(g));
+  return launched(fp6 ? hbl::launch_gemm_fp6(g) : hbl::launch_gemm(g));
 }
 
 hbl_status hbl_matmul_dequant(const void* codes, int bits, const float* dscale, const uint8_t* w_packed,

@@ -13,7 +13,8 @@ struct PrepArgs {
   int cus;           // compute units of the device (persistent grid size)
   int logk;
   int bits;          // 8 or 4
-  int mode;          // 0: codes + scales, 1: rotated activations (fp32)
+  int mode;          // 0: codes + scales, 1: rotated activations (fp32),
+                     // 2: INT4 codes in the fp6 operand layout + scales
   uint8_t* codes;
   float* dscale;
   float* xt;
@@ -37,6 +38,10 @@ struct GemmArgs {
   hipStream_t stream;
 };
 hipError_t launch_gemm(const GemmArgs& a);
+// INT4 prefill on the fp6 x fp4 matrix instruction: codes in the fp6 operand
+// layout that prep mode 2 writes, [M][K*3/4].  Used for M > kFp6MinM.
+constexpr int kFp6MinM = 64;
+hipError_t launch_gemm_fp6(const GemmArgs& a);
 // Workspace bytes the matmul needs beyond the codes and scales.
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 

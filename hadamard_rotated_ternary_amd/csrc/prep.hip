@@ -182,6 +182,15 @@ struct RawX {
 };
 
 // MODE 0: write codes + scales.  MODE 1: write the rotated activations (fp32).
+// MODE 2 (INT4 only): write the codes as the fp6 (e2m3) operand of the
+// fp6 x fp4 matrix instruction, plus the scales.  Layout per token: one
+// 24-byte group per 32 consecutive k (k0 = 32c), holding q/2 for the 32 codes
+// as six-bit fields, field p at bits 6p, where field p = h + 2b + 8d0 + 16d1
+// carries k = k0 + b + 4d0 + 8h + 16d1 (b < 4).  That is the order in which
+// the matmul unpacks a pair of packed ternary words into fp4 operands.
+HBL_DEV constexpr int fp6_pos(int k) {
+  return (k & ~31) | ((k >> 3) & 1) | ((k & 3) << 1) | (((k >> 2) & 1) << 3) | (k & 16);
+}
 constexpr int prep_wg(int logk, int loge) { return (1 << (logk - loge)) < 64 ? 64 : (1 << (logk - loge)); }
 
 // Persistent: a workgroup walks tokens blockIdx.x*TPB + tok, then + gridDim.x*TPB,
@@ -294,6 +303,9 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
         st = (st * (1.0f / K)) * c;
       }
       const float Q = BITS == 8 ? kQ8 : kQ4;
+      // MODE 2 keeps q + 8 (0..15) in the low byte; the extra 8 is even, so
+      // the ties of the rounding fall the same way.
+      constexpr float RM = MODE == 2 ? kRoundMagic + 8.0f : kRoundMagic;
       const float G = fmaxf(st, kEpsQ);
       const float s = Q / G;
       const float cs = c * s;
@@ -304,15 +316,50 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
       // clamps in that representation.  Codes are gathered through LDS for
       // coalesced stores.
       uint8_t* bytes = reinterpret_cast<uint8_t*>(region);
+      // MODE 2 stores code k at LDS byte fp6_pos(k): the bit permutation acts
+      // on the low five index bits, which split between thread and register
+      // bits, so the address is a per-thread base plus a constant.
+      const int wb = MODE == 2 ? padb(fp6_pos(baseL)) : padb(baseL);
 #pragma unroll
       for (int r = 0; r < E; ++r) {
-        float t = __builtin_fmaf(v[r], cs, kRoundMagic);
-        if constexpr (BITS == 4) t = fminf(fmaxf(t, kRoundMagic - 8.0f), kRoundMagic + 7.0f);
-        bytes[padb(baseL + PL::reg_idx(r))] = (uint8_t)__float_as_uint(t);
+        float t = __builtin_fmaf(v[r], cs, RM);
+        if constexpr (BITS == 4) t = fminf(fmaxf(t, RM - 8.0f), RM + 7.0f);
+        const int ri = PL::reg_idx(r);
+        bytes[wb + (MODE == 2 ? padb(fp6_pos(ri)) : padb(ri))] = (uint8_t)__float_as_uint(t);
       }
       __syncthreads();
       if (valid) {
-        if constexpr (BITS == 8) {
+        if constexpr (MODE == 2) {
+          // 64 codes (two 32-k groups) per step -> 48 bytes.  Byte pairs
+          // become f16 pairs 1024 + n (byte permute next to the constant
+          // 0x64), then q/2 = 0.5 * (1024 + n) - 516 exactly, then one packed
+          // conversion turns 32 halves into 32 fp6 fields (exact: every q/2
+          // in [-4, 3.5] is an e2m3 value).
+          uint8_t* out = codes + (size_t)m * (K / 4 * 3);
+          for (int cp = tau; cp < K / 64; cp += T) {
+            uint32_t o[12];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(64 * cp + 32 * c));
+              h32 hv;
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const uint32_t pr = __builtin_amdgcn_perm(0x64646464u, s4[e >> 1], (e & 1) ? 0x04030402u : 0x04010400u);
+                const h2 x = __builtin_elementwise_fma(__builtin_bit_cast(h2, pr), h2{(_Float16)0.5f, (_Float16)0.5f},
+                                                       h2{(_Float16)-516.0f, (_Float16)-516.0f});
+                hv[2 * e] = x[0];
+                hv[2 * e + 1] = x[1];
+              }
+              const u6 f = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(hv, 1.0f);
+#pragma unroll
+              for (int i = 0; i < 6; ++i) o[6 * c + i] = f[i];
+            }
+            uint4* dst = reinterpret_cast<uint4*>(out + 48 * cp);
+            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+            dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
+          }
+        } else if constexpr (BITS == 8) {
           // int8 codes: thread tau stores 16-byte chunks j*T + tau
           uint8_t* out = codes + (size_t)m * K;
 #pragma unroll
@@ -373,6 +420,8 @@ static hipError_t launch_prep_t(const PrepArgs& a) {
                      a.stream, a.x, a.gain, a.M, a.codes, a.dscale, a.xt)
   if (a.mode == 1) {
     if (a.x_bf16) HBL_PREP(8, true, 1); else HBL_PREP(8, false, 1);
+  } else if (a.mode == 2) {
+    if (a.x_bf16) HBL_PREP(4, true, 2); else HBL_PREP(4, false, 2);
   } else if (a.bits == 8) {
     if (a.x_bf16) HBL_PREP(8, true, 0); else HBL_PREP(8, false, 0);
   } else {

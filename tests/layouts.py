@@ -48,3 +48,48 @@ def unpack_int4(p: np.ndarray, K: int) -> np.ndarray:
     shifts = (8 * np.arange(4)[None, :] + 4 * np.arange(2)[:, None]).astype(np.uint32)
     nib = ((words >> shifts) & 0xF).astype(np.int32)
     return np.where(nib >= 8, nib - 16, nib).astype(np.int8).reshape(M, K)
+
+
+def e2m3_value(code: int) -> float:
+    """Value of a six-bit OCP fp6 e2m3 code: sign bit 5, exponent bits 4..3
+    (bias 1), mantissa bits 2..0; exponent 0 is subnormal (m/8)."""
+    s, e, m = (code >> 5) & 1, (code >> 3) & 3, code & 7
+    v = m / 8.0 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 1)
+    return -v if s else v
+
+
+def _fp6_field_k() -> np.ndarray:
+    """k offset (within a 32-k group) carried by field p: p = h + 2b + 8d0 + 16d1
+    holds k = b + 4d0 + 8h + 16d1."""
+    k = np.empty(32, np.int64)
+    for p in range(32):
+        h, b, d0, d1 = p & 1, (p >> 1) & 3, (p >> 3) & 1, (p >> 4) & 1
+        k[p] = b + 4 * d0 + 8 * h + 16 * d1
+    return k
+
+
+def pack_int4_fp6(q: np.ndarray) -> np.ndarray:
+    """int8 [M][K] in [-8,7] -> uint8 [M][K*3/4]: per 32 k a 24-byte LE group,
+    field p (bits 6p..6p+5) = e2m3 code of q/2 for the k of _fp6_field_k()[p]."""
+    q = np.asarray(q, dtype=np.int8)
+    M, K = q.shape
+    enc = {}
+    for c in range(64):
+        enc.setdefault(e2m3_value(c), c)          # +0 before -0
+    table = np.array([enc[v / 2.0] for v in range(-8, 8)], np.uint8)
+    fields = table[q.reshape(M, K // 32, 32)[:, :, _fp6_field_k()].astype(np.int32) + 8]   # [M, G, p]
+    bits = ((fields[..., None] >> np.arange(6, dtype=np.uint8)) & 1).reshape(M, K // 32, 192)
+    return np.packbits(bits, axis=-1, bitorder="little").reshape(M, K // 32 * 24)
+
+
+def unpack_int4_fp6(p: np.ndarray, K: int) -> np.ndarray:
+    p = np.ascontiguousarray(p, dtype=np.uint8)
+    M = p.shape[0]
+    bits = np.unpackbits(p.reshape(M, K // 32, 24), axis=-1, bitorder="little").reshape(M, K // 32, 32, 6)
+    codes = (bits.astype(np.int32) << np.arange(6)).sum(-1)
+    vals = np.vectorize(e2m3_value)(np.arange(64))[codes] * 2.0
+    if np.any(vals != np.round(vals)) or np.any(vals < -8) or np.any(vals > 7):
+        raise ValueError("fp6 field is not an INT4 code / 2")
+    q = np.empty((M, K // 32, 32), np.int8)
+    q[:, :, _fp6_field_k()] = vals.astype(np.int8)
+    return q.reshape(M, K)

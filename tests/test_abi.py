@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import hadamard_rotated_ternary_amd as hbl
-from layouts import pack_int4, pack_ternary, unpack_int4, unpack_ternary
+from layouts import pack_int4, pack_int4_fp6, pack_ternary, unpack_int4, unpack_int4_fp6, unpack_ternary
 
 OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE = 0, 1, 2, 3, 4, 5
 A = ctypes.c_void_p(0x10000)        # aligned dummy address (never dereferenced here)
@@ -83,7 +83,9 @@ def test_forward_validation(L, bits):
 
 
 def test_stage_validation(L):
-    assert L.hbl_quantize_act(A, 1, None, 4, 256, 6, A, A2, S) == DTYPE
+    assert L.hbl_quantize_act(A, 1, None, 4, 256, 5, A, A2, S) == DTYPE
+    assert L.hbl_quantize_act(A, 1, None, 0, 256, 6, A, A2, S) == OK           # fp6 operand layout
+    assert L.hbl_quantize_act(A, 1, None, 4, 256, 6, BAD, A2, S) == ALIGN
     assert L.hbl_quantize_act(A, 1, None, 4, 200, 8, A, A2, S) == SHAPE
     assert L.hbl_quantize_act(None, 1, None, 4, 256, 8, A, A2, S) == NULL
     assert L.hbl_quantize_act(A, 1, None, 0, 256, 8, A, A2, S) == OK
@@ -93,6 +95,7 @@ def test_stage_validation(L):
     assert L.hbl_gemm_ternary(A, 8, A, 4, 256, 250, A, None, 0, S) == SHAPE
     assert L.hbl_gemm_ternary(A, 8, A, 64, 1024, 256, A, None, 0, S) == NULL     # split small-M needs scratch
     assert L.hbl_gemm_ternary(A, 8, A, 64, 1024, 256, A, A2, 16, S) == WORKSPACE
+    assert L.hbl_gemm_ternary(A, 6, A, 64, 1024, 256, BAD, None, 0, S) == ALIGN   # fp6 path: no scratch
     assert L.hbl_matmul_dequant(A, 8, None, A, A, 100, 256, 256, A, 1, None, 0, S) == NULL
     assert L.hbl_quantize_weights(A, 256, 255, A, A, A, 1 << 20, S) == SHAPE
     assert L.hbl_quantize_weights(A, 256, 256, A, A, A, 8, S) == WORKSPACE
@@ -119,3 +122,16 @@ def test_layout_codecs_hand_examples():
     np.testing.assert_array_equal(unpack_int4(pack_int4(q), 64), q)
     wt = rng.integers(-1, 2, (3, 256)).astype(np.int8)
     np.testing.assert_array_equal(unpack_ternary(pack_ternary(wt), 256), wt)
+    # fp6 operand layout: field p = h + 2b + 8d0 + 16d1 carries k = b + 4d0 + 8h + 16d1,
+    # as the e2m3 code of q/2 (q=7 -> 3.5 = 1.75*2 -> 0b010110; q=-8 -> -4 -> 0b111000;
+    # q=1 -> 0.5, subnormal 4/8 -> 0b000100; q=-3 -> -1.5 -> 0b101100)
+    q = np.zeros((1, 32), np.int8)
+    q[0, 8] = 7      # h=1 -> p=1, bits 6..11
+    q[0, 31] = -8    # b=3 d0=1 h=1 d1=1 -> p=31, bits 186..191
+    q[0, 1] = 1      # b=1 -> p=2, bits 12..17
+    q[0, 20] = -3    # d0=1 d1=1 -> p=24, bits 144..149
+    g = int.from_bytes(pack_int4_fp6(q)[0].tobytes(), "little")
+    assert g == (0b010110 << 6) | (0b111000 << 186) | (0b000100 << 12) | (0b101100 << 144)
+    np.testing.assert_array_equal(unpack_int4_fp6(pack_int4_fp6(q), 32), q)
+    q = rng.integers(-8, 8, (4, 256)).astype(np.int8)
+    np.testing.assert_array_equal(unpack_int4_fp6(pack_int4_fp6(q), 256), q)

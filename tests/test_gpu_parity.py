@@ -16,7 +16,7 @@ import torch
 import hadamard_rotated_ternary_amd as hbl
 import oracle
 import synthetic
-from layouts import pack_int4, pack_ternary, unpack_int4, unpack_ternary
+from layouts import pack_int4, pack_int4_fp6, pack_ternary, unpack_int4, unpack_int4_fp6, unpack_ternary
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,14 @@ def check_codes(q_gpu, q_or, pre_or, max_frac=1e-4, tie_tol=1e-4):
 
 def gpu_codes_unpacked(codes, bits, K):
     c = host(codes)
+    if bits == 6:
+        return unpack_int4_fp6(c, K)
     return c.astype(np.int8) if bits == 8 else unpack_int4(c, K)
+
+
+def pack_codes(q, bits):
+    """Oracle codes int8 [M][K] -> the device format `bits` (8, 4 or 6)."""
+    return {8: lambda: q, 4: lambda: pack_int4(q), 6: lambda: pack_int4_fp6(q)}[bits]()
 
 
 # ------------------------------------------------------------------ weights
@@ -117,14 +124,14 @@ def test_rotation_matches_oracle(K, M):
 
 
 @pytest.mark.parametrize("K", KS)
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 6])
 @pytest.mark.parametrize("M", [1, 5, 64, 129])
 def test_codes_match_oracle(K, bits, M):
     x, xb = make_x(M, K, 7 * K + M, dist="normal" if K % 3 else "laplace", bf16=(M != 5))
     codes, d = hbl.quantize_act(x_to_dev(x, xb), bits)
     q = gpu_codes_unpacked(codes, bits, K)
     xt = oracle.hadamard_rotate(oracle.rmsnorm(x))
-    q_or, d_or, pre = oracle.quant_act(xt, bits)
+    q_or, d_or, pre = oracle.quant_act(xt, 8 if bits == 8 else 4)
     check_codes(q, q_or, pre)
     np.testing.assert_allclose(host(d), d_or, rtol=1e-5)
 
@@ -145,7 +152,7 @@ def test_zero_token_and_tiny_token():
 
 # ------------------------------------------------------------------ integer matmul
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 6])
 @pytest.mark.parametrize("M,K,N", [(1, 256, 16), (2, 1024, 48), (4, 16384, 272), (3, 8192, 4096),
                                    (7, 512, 272), (16, 2048, 512), (33, 4096, 64),
                                    (64, 16384, 128), (65, 256, 256), (300, 1024, 272), (512, 2048, 512),
@@ -158,8 +165,7 @@ def test_matmul_bit_exact(bits, M, K, N):
     wt = rng.integers(-1, 2, (N, K)).astype(np.int8)
     wt[0, :] = -1
     acc_or = oracle.gemm_ternary(q, wt)
-    codes = dev(q) if bits == 8 else dev(pack_int4(q))
-    acc = host(hbl.gemm_ternary(codes, bits, dev(pack_ternary(wt)), K))
+    acc = host(hbl.gemm_ternary(dev(pack_codes(q, bits)), bits, dev(pack_ternary(wt)), K))
     np.testing.assert_array_equal(acc, acc_or)
 
 
@@ -215,12 +221,33 @@ def test_layer_full_workloads(name, count):
     assert rel_l2(yh, y_ref) <= 2e-3, rel_l2(yh, y_ref)
     # exact integer accumulators on the sampled rows, from the oracle's own codes
     q = ref["q"]
-    codes = dev(q) if w.bits == 8 else dev(pack_int4(q))
-    acc = host(hbl.gemm_ternary(codes, w.bits, wp, w.K))
-    np.testing.assert_array_equal(acc, ref["acc"])
+    for bits in ((8,) if w.bits == 8 else (4, 6)):
+        acc = host(hbl.gemm_ternary(dev(pack_codes(q, bits)), bits, wp, w.K))
+        np.testing.assert_array_equal(acc, ref["acc"])
 
 
 # ------------------------------------------------------------------ invariants of the GPU path
+
+@pytest.mark.parametrize("M,K,N", [(65, 256, 16), (257, 1024, 272), (300, 2048, 512), (513, 16384, 256),
+                                   (1000, 4096, 4096), (8192, 16384, 4096)])
+def test_int4_prefill_fp6_path_equals_int8_instruction_path(M, K, N):
+    """The fused INT4 forward for more than 64 tokens runs its matmul on the
+    fp6 x fp4 instruction; the stage calls run the same codes through the
+    int8 instruction (bit-exact against the oracle above).  Same codes, exact
+    integer accumulators and the same dequantisation: equal bit for bit."""
+    w = synthetic.Workload("t", M, K, N, 4, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, M + 3 * K + N)
+    x, xb, wl = synthetic.make_inputs(w)
+    wp, a = hbl.quantize_weights(dev(wl))
+    xd = x_to_dev(x, xb)
+    y = hbl.forward(xd, wp, a, 4)
+    codes, d = hbl.quantize_act(xd, 4)
+    y2 = hbl.matmul_dequant(codes, 4, d, wp, a, K)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    # saturated codes at both ends of the INT4 range occur in these inputs
+    q = unpack_int4(host(codes), K)
+    assert (q == -8).any() and (q == 7).any()
+
 
 def test_int8_layer_is_exactly_odd_and_deterministic():
     w = synthetic.WORKLOADS["wo_1p3b_int4"].with_(bits=8, M=512)

@@ -358,14 +358,13 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
     const int P = (j * 4 + wave) * 64 + lane, row = P >> 1, u = (P & 1) ^ f6_arot(row);
     b_src[j] = W + (size_t)min(n0 + row, N - 1) * wrow + 16 * u;
   }
-  auto dma = [&](int kt) __attribute__((always_inline)) {
-    uint8_t* base = smem + (kt & (F6_NBUF - 1)) * F6_STAGE;
-#pragma unroll
-    for (int j = 0; j < A_LOADS; ++j)
+  // copy j (A copies 0..5, B copies 6..7) of stage kt into LDS buffer buf
+  auto dma1 = [&](int j, int kt, int buf) __attribute__((always_inline)) {
+    uint8_t* base = smem + buf * F6_STAGE;
+    if (j < A_LOADS)
       lds_copy16(a_src[j] + (size_t)kt * F6_AROW, base + (j * 4 + wave) * 1024);
-#pragma unroll
-    for (int j = 0; j < B_LOADS; ++j)
-      lds_copy16(b_src[j] + (size_t)kt * F6_BROW, base + F6_A_STAGE + (j * 4 + wave) * 1024);
+    else
+      lds_copy16(b_src[j - A_LOADS] + (size_t)kt * F6_BROW, base + F6_A_STAGE + ((j - A_LOADS) * 4 + wave) * 1024);
   };
 
   v16f acc[4][4];
@@ -374,65 +373,107 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  auto compute = [&](int kt) __attribute__((always_inline)) {
-    const uint8_t* sa = smem + (kt & (F6_NBUF - 1)) * F6_STAGE;
-    const uint8_t* sb = sa + F6_A_STAGE;
-    v4i bq[4];
+  // Register fragments of one stage: per lane 48 A bytes (32-k groups 2g and
+  // 2g+1 of four 32-row blocks) and 16 packed B bytes (the same groups of
+  // four 32-column blocks).  Read r of a stage: r < 4 the B block r, else A
+  // block (r-4)/3, unit (r-4)%3.
+  struct Frag {
+    v4i a[4][3];
+    v4i b[4];
+  };
+  auto read1 = [&](Frag& f, int r, int buf) __attribute__((always_inline)) {
+    const uint8_t* sa = smem + buf * F6_STAGE;
+    if (r < 4) {
+      const int n = wn * 128 + r * 32 + l32;
+      f.b[r] = *reinterpret_cast<const v4i*>(sa + F6_A_STAGE + n * F6_BROW + 16 * (g ^ f6_arot(n)));
+    } else {
+      const int rb = (r - 4) / 3, t = (r - 4) % 3;
+      const int row = wm * 128 + rb * 32 + l32;
+      int pu = 3 * g + t + f6_arot(row);
+      if (pu >= 6) pu -= 6;
+      f.a[rb][t] = *reinterpret_cast<const v4i*>(sa + row * F6_AROW + 16 * pu);
+    }
+  };
+  auto bexp = [&](const Frag& f, int st, v8i* bf) __attribute__((always_inline)) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const int n = wn * 128 + cb * 32 + l32;
-      bq[cb] = *reinterpret_cast<const v4i*>(sb + n * F6_BROW + 16 * (g ^ f6_arot(n)));
+      const uint32_t w0 = (uint32_t)f.b[cb][2 * st], w1 = (uint32_t)f.b[cb][2 * st + 1];
+      bf[cb] = v8i{(int)((w0 << 2) & 0xCCCCCCCCu), (int)(w0 & 0xCCCCCCCCu), (int)((w1 << 2) & 0xCCCCCCCCu),
+                   (int)(w1 & 0xCCCCCCCCu), 0, 0, 0, 0};
     }
-    v4i aq[4][3];
+  };
+  auto aop = [&](const Frag& f, int st, int rb) __attribute__((always_inline)) {
+    // dwords 6st .. 6st+5 of the lane's 12 A dwords
+    int a[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) a[i] = f.a[rb][(6 * st + i) >> 2][(6 * st + i) & 3];
+    return v8i{a[0], a[1], a[2], a[3], a[4], a[5], 0, 0};
+  };
+  auto mfma = [&](const v8i& af, const v8i& bf, v16f& c) __attribute__((always_inline)) {
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, c, 2, 4, 0, 127, 0, 127);
+  };
+
+  // Software pipeline, one wave per SIMD.  Stage kt lives in buffer kt % 4
+  // and its fragments are in registers (cur) when it starts.  First MFMA
+  // step of cur; then wait for this wave's copies of stage kt+1 and barrier
+  // (every wave's copies of kt+1 have landed, every wave's reads of stage kt
+  // are complete); then the second MFMA step, with one LDS read of stage
+  // kt+1's fragments (nxt) after every MFMA and one copy of stage kt+4 into
+  // stage kt's buffer after every other MFMA, so the memory instructions
+  // issue in the shadow of the matrix instructions instead of in bursts.
+  // Past the last stage the copies repeat stage KT-1 and the reads fetch an
+  // unused buffer (both harmless), which keeps the loop free of branches and
+  // the copy count per stage constant.
+  const int KT = K / F6_BK;                 // even: K >= 256
+  auto stage = [&](int kt, const Frag& cur, Frag& nxt) __attribute__((always_inline)) {
+    // sched_barrier(0) keeps the instruction groups in this order: the
+    // operands of row block rb are assembled right before its MFMAs (each
+    // waits only for its own LDS reads), and all of step 0 issues before the
+    // barrier so the matrix pipe has work while the wave waits.
+    __builtin_amdgcn_sched_barrier(0);
+    v8i bf[4];
+    bexp(cur, 0, bf);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      const int row = wm * 128 + rb * 32 + l32;
+      const v8i af = aop(cur, 0, rb);
 #pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        int pu = 3 * g + t + f6_arot(row);
-        if (pu >= 6) pu -= 6;
-        aq[rb][t] = *reinterpret_cast<const v4i*>(sa + row * F6_AROW + 16 * pu);
-      }
+      for (int cb = 0; cb < 4; ++cb) mfma(af, bf[cb], acc[rb][cb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    wait_vmcnt<2 * NL>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+    const int nbuf = (kt + 1) & (F6_NBUF - 1), dbuf = kt & (F6_NBUF - 1);
+    const int dkt = min(kt + F6_NBUF, KT - 1);
+    bexp(cur, 1, bf);
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      v8i bf[4];
+    for (int rb = 0; rb < 4; ++rb) {
+      const v8i af = aop(cur, 1, rb);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const uint32_t w0 = (uint32_t)bq[cb][2 * st], w1 = (uint32_t)bq[cb][2 * st + 1];
-        bf[cb] = v8i{(int)((w0 << 2) & 0xCCCCCCCCu), (int)(w0 & 0xCCCCCCCCu), (int)((w1 << 2) & 0xCCCCCCCCu),
-                     (int)(w1 & 0xCCCCCCCCu), 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        // dwords 6st .. 6st+5 of the lane's 12 A dwords
-        int a[6];
-#pragma unroll
-        for (int i = 0; i < 6; ++i) a[i] = aq[rb][(6 * st + i) >> 2][(6 * st + i) & 3];
-        const v8i af = v8i{a[0], a[1], a[2], a[3], a[4], a[5], 0, 0};
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[cb], acc[rb][cb], 2, 4, 0, 127, 0, 127);
+        const int i = rb * 4 + cb;
+        mfma(af, bf[cb], acc[rb][cb]);
+        read1(nxt, i, nbuf);
+        if (i & 1) dma1(i >> 1, dkt, dbuf);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  // Stage kt lives in buffer kt % 4.  Before stage kt: wait for this wave's
-  // copies of kt (up to two later stages may still be in flight), then the
-  // barrier (every wave's copies of kt have landed and every wave is done
-  // with stage kt-1), then refill stage kt-1's buffer with stage kt+3.
-  const int KT = K / F6_BK;
-  for (int j = 0; j < F6_NBUF - 1; ++j)
-    if (j < KT) dma(j);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int later = min(KT - 1 - kt, F6_NBUF - 2);
-    if (later >= 2) wait_vmcnt<2 * NL>();
-    else if (later == 1) wait_vmcnt<NL>();
-    else wait_vmcnt<0>();
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-    if (kt + F6_NBUF - 1 < KT) dma(kt + F6_NBUF - 1);
-    compute(kt);
+  Frag f0, f1;
+#pragma unroll
+  for (int j = 0; j < F6_NBUF; ++j)
+#pragma unroll
+    for (int c = 0; c < NL; ++c) dma1(c, min(j, KT - 1), j);
+  wait_vmcnt<3 * NL>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) read1(f0, r, 0);
+  for (int kt = 0; kt < KT; kt += 2) {
+    stage(kt, f0, f1);
+    stage(kt + 1, f1, f0);
   }
+  // no copy may still be writing LDS when the workgroup exits
+  wait_vmcnt<0>();
 
   // epilogue: 32x32 accumulator layout, lane l / register r hold
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.  The accumulators are exact

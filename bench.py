@@ -157,7 +157,7 @@ def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup):
     INT4 forward of more than 64 tokens keeps its codes in the fp6 operand
     layout, format 6)."""
     sb = 6 if bits == 4 and M > 64 else bits
-    codes = torch.empty((M, hbl.codes_row_bytes(sb, K)), dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
+    codes = torch.empty(hbl.codes_shape(sb, M, K), dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
     d = torch.empty(M + 4, dtype=torch.float32, device="cuda")[:M]
     y = torch.empty((M, N), dtype=xd.dtype, device="cuda")
     ws = torch.empty(max(hbl.workspace_bytes(hbl.OP_MATMUL, M, K, N), 16), dtype=torch.uint8, device="cuda")

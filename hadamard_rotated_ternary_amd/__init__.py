@@ -141,6 +141,15 @@ def codes_row_bytes(bits: int, K: int) -> int:
     return {8: K, 4: K // 2, 6: K // 4 * 3}[bits]
 
 
+def codes_shape(bits: int, M: int, K: int) -> tuple:
+    """Tensor shape of the codes: [M][K] (8), [M][K/2] (4), [K/128][M][96] (6)."""
+    return (K // 128, M, 96) if bits == 6 else (M, codes_row_bytes(bits, K))
+
+
+def _codes_m(codes, bits: int) -> int:
+    return codes.shape[1] if bits == 6 else codes.shape[0]
+
+
 def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, out=None):
     """Stage 1: x [M][K] -> (codes, per-token scales fp32 [M])."""
     _dev(x, "x")
@@ -148,7 +157,7 @@ def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, o
     if out is not None:
         codes, d = out
     else:
-        codes = torch.empty((M, codes_row_bytes(bits, K)), dtype=torch.int8 if bits == 8 else torch.uint8,
+        codes = torch.empty(codes_shape(bits, M, K), dtype=torch.int8 if bits == 8 else torch.uint8,
                             device=x.device)
         d = torch.empty(M + 4, dtype=torch.float32, device=x.device)[:M]
     _call("hbl_quantize_act", _ptr(x), _dtype_code(x.dtype), _ptr(gain), M, K, bits, _ptr(codes), _ptr(d),
@@ -158,7 +167,7 @@ def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, o
 
 def matmul_dequant(codes, bits, dscale, w_packed, w_alpha, K, out_dtype=torch.bfloat16, workspace=None, out=None):
     """Stage 2: codes -> y [M][N]."""
-    M = codes.shape[0]
+    M = _codes_m(codes, bits)
     N = w_packed.shape[0]
     y = torch.empty((M, N), dtype=out_dtype, device=codes.device) if out is None else out
     out_dtype = y.dtype
@@ -179,7 +188,7 @@ def rmsnorm_fwht(x: torch.Tensor, gain: torch.Tensor | None = None) -> torch.Ten
 
 def gemm_ternary(codes, bits, w_packed, K, workspace=None) -> torch.Tensor:
     """Debug view: exact int32 accumulators [M][N]."""
-    M = codes.shape[0]
+    M = _codes_m(codes, bits)
     N = w_packed.shape[0]
     acc = torch.empty((M, N), dtype=torch.int32, device=codes.device)
     ws = _workspace(workspace_bytes(OP_MATMUL, M, K, N), codes.device, workspace)

@@ -8,6 +8,7 @@
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v12i __attribute__((ext_vector_type(12)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned u6 __attribute__((ext_vector_type(6)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
 // accumulation.
 //
 // A comes from prep mode 2: per token one 24-byte group per 32 k, six-bit
-// fields in the operand order.  B stays the packed 2-bit format: masking
+// fields in the operand order, blocked by 128 k ([K/128][M][96 bytes]).  B stays the packed 2-bit format: masking
 // bits 2-3 and 6-7 of every byte of a packed word (after a left shift by 2
 // for fields 0 and 2) leaves, nibble by nibble, the e2m1 code of 2w
 // (code 01 -> 0100 = +2, 11 -> 1100 = -2).  Word w0 (k0..k0+15) gives operand
@@ -319,7 +319,16 @@ constexpr int F6_STAGE = F6_A_STAGE + F6_B_STAGE;  // 32 KiB
 // groups.  B columns hold 2 units, swapped on the same row bit.
 HBL_DEV int f6_arot(int row) { return (row >> 2) & 1; }
 
-template <int OUT>
+// Copy 16 bytes per lane from global memory (scalar base + 32-bit per-lane
+// offset) straight into LDS at lds_base + 16 * lane (wave-uniform base).
+HBL_DEV void lds_copy16s(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds_base), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+// US: stages per loop trip (4; 2 when K = 256), so that LDS buffer numbers are
+// compile-time constants.
+template <int OUT, int US>
 __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int tiles_m, int tiles_n) {
@@ -338,33 +347,40 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   const int n0 = (in_g / gm) * PBN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, g = lane >> 5;
-  const size_t arow = (size_t)K / 4 * 3;
-  const size_t wrow = (size_t)K / 4;
+  // A is blocked by 128 k: stage kt of the tile is the contiguous run of
+  // 256 x 96 bytes at (kt * M + m0) * 96.
+  const size_t a_stage = (size_t)M * F6_AROW;
+  const uint32_t wrow = (uint32_t)K / 4;
+  const uint8_t* a_tile = A + (size_t)m0 * F6_AROW;
+  const uint8_t* b_tile = W + (size_t)n0 * wrow;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
-  // copy P of a stage fills LDS bytes 16P..16P+15 (wave instruction = 1 KiB)
-  const uint8_t* a_src[A_LOADS];
-  const uint8_t* b_src[B_LOADS];
+  // copy P of a stage fills LDS bytes 16P..16P+15 (wave instruction = 1 KiB);
+  // per-lane source offsets inside the tile (rows past M / channels past N
+  // repeat the last one and are never stored) fit 32 bits: < 256 rows.
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
   for (int j = 0; j < A_LOADS; ++j) {
     const int P = (j * 4 + wave) * 64 + lane, row = P / 6, pu = P % 6;
     int u = pu - f6_arot(row);
     if (u < 0) u += 6;
-    a_src[j] = A + (size_t)min(m0 + row, M - 1) * arow + 16 * u;
+    a_off[j] = (uint32_t)(min(m0 + row, M - 1) - m0) * F6_AROW + 16 * u;
   }
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
     const int P = (j * 4 + wave) * 64 + lane, row = P >> 1, u = (P & 1) ^ f6_arot(row);
-    b_src[j] = W + (size_t)min(n0 + row, N - 1) * wrow + 16 * u;
+    b_off[j] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + 16 * u;
   }
   // copy j (A copies 0..5, B copies 6..7) of stage kt into LDS buffer buf
   auto dma1 = [&](int j, int kt, int buf) __attribute__((always_inline)) {
-    uint8_t* base = smem + buf * F6_STAGE;
     if (j < A_LOADS)
-      lds_copy16(a_src[j] + (size_t)kt * F6_AROW, base + (j * 4 + wave) * 1024);
+      lds_copy16s(a_tile + (size_t)kt * a_stage, a_off[j], lds0 + buf * F6_STAGE + (j * 4 + wave_s) * 1024);
     else
-      lds_copy16(b_src[j - A_LOADS] + (size_t)kt * F6_BROW, base + F6_A_STAGE + ((j - A_LOADS) * 4 + wave) * 1024);
+      lds_copy16s(b_tile + (size_t)kt * F6_BROW, b_off[j - A_LOADS],
+                  lds0 + buf * F6_STAGE + F6_A_STAGE + ((j - A_LOADS) * 4 + wave_s) * 1024);
   };
 
   v16f acc[4][4];
@@ -374,11 +390,13 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
   // Register fragments of one stage: per lane 48 A bytes (32-k groups 2g and
-  // 2g+1 of four 32-row blocks) and 16 packed B bytes (the same groups of
-  // four 32-column blocks).  Read r of a stage: r < 4 the B block r, else A
-  // block (r-4)/3, unit (r-4)%3.
+  // 2g+1 of four 32-row blocks), kept as one 12-dword vector per block so the
+  // two 6-dword MFMA operands (8-dword vectors, the last two unused) are
+  // sub-ranges of it, and 16 packed B bytes
+  // (the same groups of four 32-column blocks).  Read r of a stage: r < 4 the
+  // B block r, else A block (r-4)/3, unit (r-4)%3.
   struct Frag {
-    v4i a[4][3];
+    v16i a[4];
     v4i b[4];
   };
   auto read1 = [&](Frag& f, int r, int buf) __attribute__((always_inline)) {
@@ -391,23 +409,27 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
       const int row = wm * 128 + rb * 32 + l32;
       int pu = 3 * g + t + f6_arot(row);
       if (pu >= 6) pu -= 6;
-      f.a[rb][t] = *reinterpret_cast<const v4i*>(sa + row * F6_AROW + 16 * pu);
+      const v4i x = *reinterpret_cast<const v4i*>(sa + row * F6_AROW + 16 * pu);
+      const v16i xe = __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1);
+      if (t == 0)
+        f.a[rb] = __builtin_shufflevector(f.a[rb], xe, 16, 17, 18, 19, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      else if (t == 1)
+        f.a[rb] = __builtin_shufflevector(f.a[rb], xe, 0, 1, 2, 3, 16, 17, 18, 19, 8, 9, 10, 11, 12, 13, 14, 15);
+      else
+        f.a[rb] = __builtin_shufflevector(f.a[rb], xe, 0, 1, 2, 3, 4, 5, 6, 7, 16, 17, 18, 19, 12, 13, 14, 15);
     }
   };
-  auto bexp = [&](const Frag& f, int st, v8i* bf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const uint32_t w0 = (uint32_t)f.b[cb][2 * st], w1 = (uint32_t)f.b[cb][2 * st + 1];
-      bf[cb] = v8i{(int)((w0 << 2) & 0xCCCCCCCCu), (int)(w0 & 0xCCCCCCCCu), (int)((w1 << 2) & 0xCCCCCCCCu),
-                   (int)(w1 & 0xCCCCCCCCu), 0, 0, 0, 0};
-    }
+  // fp4 operand of MFMA step st for 32-column block cb: 2w per nibble
+  auto bexp1 = [&](const Frag& f, int st, int cb) __attribute__((always_inline)) {
+    const uint32_t w0 = (uint32_t)f.b[cb][2 * st], w1 = (uint32_t)f.b[cb][2 * st + 1];
+    return v8i{(int)((w0 << 2) & 0xCCCCCCCCu), (int)(w0 & 0xCCCCCCCCu), (int)((w1 << 2) & 0xCCCCCCCCu),
+               (int)(w1 & 0xCCCCCCCCu), 0, 0, 0, 0};
   };
+  // dwords 6st .. 6st+5 of the block's 12 A dwords (the instruction reads six
+  // registers for fp6; the last two lanes of the vector are not used)
   auto aop = [&](const Frag& f, int st, int rb) __attribute__((always_inline)) {
-    // dwords 6st .. 6st+5 of the lane's 12 A dwords
-    int a[6];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) a[i] = f.a[rb][(6 * st + i) >> 2][(6 * st + i) & 3];
-    return v8i{a[0], a[1], a[2], a[3], a[4], a[5], 0, 0};
+    return st == 0 ? __builtin_shufflevector(f.a[rb], f.a[rb], 0, 1, 2, 3, 4, 5, 6, 7)
+                   : __builtin_shufflevector(f.a[rb], f.a[rb], 6, 7, 8, 9, 10, 11, 12, 13);
   };
   auto mfma = [&](const v8i& af, const v8i& bf, v16f& c) __attribute__((always_inline)) {
     c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, c, 2, 4, 0, 127, 0, 127);
@@ -424,36 +446,38 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   // Past the last stage the copies repeat stage KT-1 and the reads fetch an
   // unused buffer (both harmless), which keeps the loop free of branches and
   // the copy count per stage constant.
-  const int KT = K / F6_BK;                 // even: K >= 256
-  auto stage = [&](int kt, const Frag& cur, Frag& nxt) __attribute__((always_inline)) {
-    // sched_barrier(0) keeps the instruction groups in this order: the
-    // operands of row block rb are assembled right before its MFMAs (each
-    // waits only for its own LDS reads), and all of step 0 issues before the
-    // barrier so the matrix pipe has work while the wave waits.
+  // The operand expansion is pipelined too: during step 0 the B operands of
+  // step 1 (bf1) are expanded, during step 1 those of the next stage's step 0
+  // (bf0, from nxt, a few MFMAs after their LDS reads were issued).  All the
+  // VALU work then issues between MFMAs.  sched_barrier(0) fixes the order
+  // of these groups.
+  const int KT = K / F6_BK;                 // a multiple of US
+  auto stage = [&](int kt, int buf, const Frag& cur, Frag& nxt, v8i* bf0, v8i* bf1) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    v8i bf[4];
-    bexp(cur, 0, bf);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const v8i af = aop(cur, 0, rb);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) mfma(af, bf[cb], acc[rb][cb]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int cb = 0; cb < 4; ++cb) {
+        mfma(af, bf0[cb], acc[rb][cb]);
+        if (cb == 1) bf1[rb] = bexp1(cur, 1, rb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     wait_vmcnt<2 * NL>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-    const int nbuf = (kt + 1) & (F6_NBUF - 1), dbuf = kt & (F6_NBUF - 1);
+    const int nbuf = (buf + 1) & (F6_NBUF - 1);
     const int dkt = min(kt + F6_NBUF, KT - 1);
-    bexp(cur, 1, bf);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const v8i af = aop(cur, 1, rb);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const int i = rb * 4 + cb;
-        mfma(af, bf[cb], acc[rb][cb]);
+        mfma(af, bf1[cb], acc[rb][cb]);
         read1(nxt, i, nbuf);
-        if (i & 1) dma1(i >> 1, dkt, dbuf);
+        if (i & 1) dma1(i >> 1, dkt, buf);
+        if (i >= 8 && !(i & 1)) bf0[(i - 8) >> 1] = bexp1(nxt, 0, (i - 8) >> 1);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -468,9 +492,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 #pragma unroll
   for (int r = 0; r < 16; ++r) read1(f0, r, 0);
-  for (int kt = 0; kt < KT; kt += 2) {
-    stage(kt, f0, f1);
-    stage(kt + 1, f1, f0);
+  v8i bf0[4], bf1[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) bf0[cb] = bexp1(f0, 0, cb);
+  for (int kt = 0; kt < KT; kt += US) {
+#pragma unroll
+    for (int u = 0; u < US; u += 2) {
+      stage(kt + u, u, f0, f1, bf0, bf1);
+      stage(kt + u + 1, u + 1, f1, f0, bf0, bf1);
+    }
   }
   // no copy may still be writing LDS when the workgroup exits
   wait_vmcnt<0>();
@@ -812,9 +842,13 @@ static void launch_t(const GemmArgs& a) {
 hipError_t launch_gemm_fp6(const GemmArgs& a) {
   if (a.M == 0) return hipSuccess;
   const int tm = (a.M + PBM - 1) / PBM, tn = (a.N + PBN - 1) / PBN;
-#define HBL_F6(OUT)                                                                                       \
-  hipLaunchKernelGGL((gemm_fp6_kernel<OUT>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack, a.dscale, \
-                     a.walpha, a.out, a.M, a.N, a.K, tm, tn)
+#define HBL_F6(OUT)                                                                                          \
+  if (a.K == 256)                                                                                                \
+    hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 2>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,         \
+                       a.dscale, a.walpha, a.out, a.M, a.N, a.K, tm, tn);                                          \
+  else                                                                                                           \
+    hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 4>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,         \
+                       a.dscale, a.walpha, a.out, a.M, a.N, a.K, tm, tn)
   switch (a.out_kind) {
     case OUT_ACC_I32: HBL_F6(OUT_ACC_I32); break;
     case OUT_F32: HBL_F6(OUT_F32); break;

@@ -183,11 +183,13 @@ struct RawX {
 
 // MODE 0: write codes + scales.  MODE 1: write the rotated activations (fp32).
 // MODE 2 (INT4 only): write the codes as the fp6 (e2m3) operand of the
-// fp6 x fp4 matrix instruction, plus the scales.  Layout per token: one
-// 24-byte group per 32 consecutive k (k0 = 32c), holding q/2 for the 32 codes
-// as six-bit fields, field p at bits 6p, where field p = h + 2b + 8d0 + 16d1
-// carries k = k0 + b + 4d0 + 8h + 16d1 (b < 4).  That is the order in which
-// the matmul unpacks a pair of packed ternary words into fp4 operands.
+// fp6 x fp4 matrix instruction, plus the scales.  One 24-byte group per token
+// and 32 consecutive k (k0 = 32c) holds q/2 for the 32 codes as six-bit
+// fields, field p at bits 6p, where field p = h + 2b + 8d0 + 16d1 carries
+// k = k0 + b + 4d0 + 8h + 16d1 (b < 4): the order in which the matmul unpacks
+// a pair of packed ternary words into fp4 operands.  The groups are blocked
+// by 128 k: block kb = c / 4 is a [M][96-byte] array at byte kb * M * 96, so
+// the matmul's 128-k stage of 256 tokens is one contiguous 24 KiB run.
 HBL_DEV constexpr int fp6_pos(int k) {
   return (k & ~31) | ((k >> 3) & 1) | ((k & 3) << 1) | (((k >> 2) & 1) << 3) | (k & 16);
 }
@@ -335,7 +337,8 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
           // 0x64), then q/2 = 0.5 * (1024 + n) - 516 exactly, then one packed
           // conversion turns 32 halves into 32 fp6 fields (exact: every q/2
           // in [-4, 3.5] is an e2m3 value).
-          uint8_t* out = codes + (size_t)m * (K / 4 * 3);
+          uint8_t* out = codes + (size_t)m * 96;
+          const size_t kb_stride = (size_t)M * 96;
           for (int cp = tau; cp < K / 64; cp += T) {
             uint32_t o[12];
 #pragma unroll
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
 #pragma unroll
               for (int i = 0; i < 6; ++i) o[6 * c + i] = f[i];
             }
-            uint4* dst = reinterpret_cast<uint4*>(out + 48 * cp);
+            uint4* dst = reinterpret_cast<uint4*>(out + (size_t)(cp >> 1) * kb_stride + 48 * (cp & 1));
             dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
             dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
             dst[2] = make_uint4(o[8], o[9], o[10], o[11]);

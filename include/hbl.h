@@ -46,16 +46,18 @@
  *       32-bit word per 8 consecutive k; the code of k0 + 4*j + i (i in 0..3,
  *       j in 0..1) occupies bits 8*i + 4*j .. 8*i + 4*j + 3, as a 4-bit two's
  *       complement nibble.
- *   INT4 codes, fp6 operand layout (bits = HBL_BITS_INT4_FP6)   uint8 [M][K*3/4]:
- *       the same codes q in [-8, 7], each stored as the OCP fp6 e2m3 encoding
- *       of q/2 (sign bit 5, exponent bits 4..3 with bias 1, mantissa bits
- *       2..0; every q/2 is exact).  For each row, one 24-byte little-endian
- *       group per 32 consecutive k (k0 = 32*c, group at byte 24*c); field p
- *       (p in 0..31) occupies bits 6*p .. 6*p + 5 of the group and holds the
+ *   INT4 codes, fp6 operand layout (bits = HBL_BITS_INT4_FP6)   uint8 [K/128][M][96]
+ *       (M*K*3/4 bytes): the same codes q in [-8, 7], each stored as the OCP
+ *       fp6 e2m3 encoding of q/2 (sign bit 5, exponent bits 4..3 with bias 1,
+ *       mantissa bits 2..0; every q/2 is exact).  Token m's codes of the k
+ *       block [128*kb, 128*kb + 128) are the 96 bytes at (kb*M + m)*96: four
+ *       24-byte little-endian groups, group j for k0 = 128*kb + 32*j; field p
+ *       (p in 0..31) occupies bits 6*p .. 6*p + 5 of its group and holds the
  *       code of k0 + b + 4*d0 + 8*h + 16*d1, where p = h + 2*b + 8*d0 + 16*d1
  *       (b in 0..3; h, d0, d1 in 0..1).  This is the operand layout of the
- *       gfx950 fp6 x fp4 matrix instruction for the weights' packed order;
- *       the INT4 forward uses it internally for M > 64.
+ *       gfx950 fp6 x fp4 matrix instruction for the weights' packed order,
+ *       blocked so that 128 k of consecutive tokens are contiguous; the INT4
+ *       forward uses it internally for M > 64.
  *   per-token dequant scales d   fp32 [M].
  *   per-tensor weight scale      fp32 [1] (alpha; the floor 1e-5 is applied on use).
  */
@@ -142,7 +144,7 @@ hbl_status hbl_forward_int4(const void *x, hbl_dtype x_dtype, const float *gain,
  * kernel (新智元 article, section H-BitLinear模块: the transform is applied to
  * the activations before they are quantised).
  *   bits      8, 4 or HBL_BITS_INT4_FP6 (6: INT4 codes in the fp6 operand layout)
- *   codes     INT8: int8 [M][K];  INT4: uint8 [M][K/2];  6: uint8 [M][K*3/4]
+ *   codes     INT8: int8 [M][K];  INT4: uint8 [M][K/2];  6: uint8 [K/128][M][96]
  *             (formats above)
  *   dscale    fp32 [M] per-token dequant scales d
  */

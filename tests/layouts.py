@@ -69,8 +69,10 @@ def _fp6_field_k() -> np.ndarray:
 
 
 def pack_int4_fp6(q: np.ndarray) -> np.ndarray:
-    """int8 [M][K] in [-8,7] -> uint8 [M][K*3/4]: per 32 k a 24-byte LE group,
-    field p (bits 6p..6p+5) = e2m3 code of q/2 for the k of _fp6_field_k()[p]."""
+    """int8 [M][K] in [-8,7] -> uint8 [K/128][M][96]: per token and 32 k a
+    24-byte LE group, field p (bits 6p..6p+5) = e2m3 code of q/2 for the k of
+    _fp6_field_k()[p]; the four groups of a 128-k block are token m's 96 bytes
+    of block kb."""
     q = np.asarray(q, dtype=np.int8)
     M, K = q.shape
     enc = {}
@@ -79,13 +81,15 @@ def pack_int4_fp6(q: np.ndarray) -> np.ndarray:
     table = np.array([enc[v / 2.0] for v in range(-8, 8)], np.uint8)
     fields = table[q.reshape(M, K // 32, 32)[:, :, _fp6_field_k()].astype(np.int32) + 8]   # [M, G, p]
     bits = ((fields[..., None] >> np.arange(6, dtype=np.uint8)) & 1).reshape(M, K // 32, 192)
-    return np.packbits(bits, axis=-1, bitorder="little").reshape(M, K // 32 * 24)
+    rows = np.packbits(bits, axis=-1, bitorder="little").reshape(M, K // 128, 96)
+    return np.ascontiguousarray(rows.transpose(1, 0, 2))
 
 
 def unpack_int4_fp6(p: np.ndarray, K: int) -> np.ndarray:
-    p = np.ascontiguousarray(p, dtype=np.uint8)
-    M = p.shape[0]
-    bits = np.unpackbits(p.reshape(M, K // 32, 24), axis=-1, bitorder="little").reshape(M, K // 32, 32, 6)
+    p = np.asarray(p, dtype=np.uint8).reshape(K // 128, -1, 96)
+    M = p.shape[1]
+    rows = np.ascontiguousarray(p.transpose(1, 0, 2)).reshape(M, K // 32, 24)
+    bits = np.unpackbits(rows, axis=-1, bitorder="little").reshape(M, K // 32, 32, 6)
     codes = (bits.astype(np.int32) << np.arange(6)).sum(-1)
     vals = np.vectorize(e2m3_value)(np.arange(64))[codes] * 2.0
     if np.any(vals != np.round(vals)) or np.any(vals < -8) or np.any(vals > 7):

@@ -125,13 +125,17 @@ def test_layout_codecs_hand_examples():
     # fp6 operand layout: field p = h + 2b + 8d0 + 16d1 carries k = b + 4d0 + 8h + 16d1,
     # as the e2m3 code of q/2 (q=7 -> 3.5 = 1.75*2 -> 0b010110; q=-8 -> -4 -> 0b111000;
     # q=1 -> 0.5, subnormal 4/8 -> 0b000100; q=-3 -> -1.5 -> 0b101100)
-    q = np.zeros((1, 32), np.int8)
+    q = np.zeros((1, 128), np.int8)
     q[0, 8] = 7      # h=1 -> p=1, bits 6..11
     q[0, 31] = -8    # b=3 d0=1 h=1 d1=1 -> p=31, bits 186..191
     q[0, 1] = 1      # b=1 -> p=2, bits 12..17
     q[0, 20] = -3    # d0=1 d1=1 -> p=24, bits 144..149
-    g = int.from_bytes(pack_int4_fp6(q)[0].tobytes(), "little")
+    g = int.from_bytes(pack_int4_fp6(q)[0, 0, :24].tobytes(), "little")
     assert g == (0b010110 << 6) | (0b111000 << 186) | (0b000100 << 12) | (0b101100 << 144)
-    np.testing.assert_array_equal(unpack_int4_fp6(pack_int4_fp6(q), 32), q)
-    q = rng.integers(-8, 8, (4, 256)).astype(np.int8)
-    np.testing.assert_array_equal(unpack_int4_fp6(pack_int4_fp6(q), 256), q)
+    np.testing.assert_array_equal(unpack_int4_fp6(pack_int4_fp6(q), 128), q)
+    # blocked by 128 k: token m's bytes of block kb at (kb * M + m) * 96
+    q = rng.integers(-8, 8, (5, 256)).astype(np.int8)
+    p = pack_int4_fp6(q)
+    assert p.shape == (2, 5, 96)
+    np.testing.assert_array_equal(p[1, 3], pack_int4_fp6(q[3:4, 128:])[0, 0])
+    np.testing.assert_array_equal(unpack_int4_fp6(p, 256), q)

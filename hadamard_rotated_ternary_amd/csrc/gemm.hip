@@ -295,29 +295,38 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
 // accumulation.
 //
 // A comes from prep mode 2: per token one 24-byte group per 32 k, six-bit
-// fields in the operand order, blocked by 128 k ([K/128][M][96 bytes]).  B stays the packed 2-bit format: masking
+// fields in the operand order, blocked by 128 k ([K/128][M][96 bytes]).
+// B stays the packed 2-bit format: masking
 // bits 2-3 and 6-7 of every byte of a packed word (after a left shift by 2
 // for fields 0 and 2) leaves, nibble by nibble, the e2m1 code of 2w
 // (code 01 -> 0100 = +2, 11 -> 1100 = -2).  Word w0 (k0..k0+15) gives operand
 // dwords 0 and 1, word w1 (k0+16..k0+31) dwords 2 and 3; the fp6 field order
 // matches that nibble order.
 //
-// 256x256 tile per workgroup of 4 waves (2x2, 128x128 each), 128 k per LDS
-// stage (A 96 bytes per row, B 32 bytes per column), 4 stages in a ring with
-// copies issued 3 stages ahead.  Lane group g of the 64-k instruction takes
-// 32-k group 2g+s of the stage in step s, so every lane reads 48 contiguous
-// A bytes and 16 contiguous B bytes per stage.
+// 256x256 tile per workgroup of 4 waves (2x2, 128x128 each), 128 k per
+// stage.  A: 96 bytes per row per stage, 4 stage buffers in a ring, copies
+// issued 3-4 stages ahead.  B: fetched for two stages at once (64 bytes per
+// column, so each column costs one cache-line request per two stages), 2
+// pair slots.  Lane group g of the 64-k instruction takes 32-k group 2g+s
+// of the stage in step s, so every lane reads 48 contiguous A bytes and 16
+// contiguous B bytes per stage.  The global memory requests are what bounds
+// this kernel, so both operands are fetched as whole, contiguous runs.
 constexpr int F6_BK = 128, F6_NBUF = 4;
 constexpr int F6_AROW = F6_BK / 4 * 3;             // 96 bytes of fp6 codes per row per stage
-constexpr int F6_BROW = F6_BK / 4;                 // 32 bytes of packed weights per column
 constexpr int F6_A_STAGE = PBM * F6_AROW;          // 24 KiB
-constexpr int F6_B_STAGE = PBN * F6_BROW;          // 8 KiB
-constexpr int F6_STAGE = F6_A_STAGE + F6_B_STAGE;  // 32 KiB
+constexpr int F6_BPROW = 2 * F6_BK / 4;            // 64 bytes of packed weights per column per stage pair
+constexpr int F6_B_PAIR = PBN * F6_BPROW;          // 16 KiB
+constexpr int F6_B_BASE = F6_NBUF * F6_A_STAGE;    // B slots after the A ring
+constexpr int F6_LDS = F6_B_BASE + 2 * F6_B_PAIR;  // 128 KiB
 
-// LDS rows of A hold 6 units of 16 bytes; rows with bit 2 set are rotated by
-// one unit, so 8 consecutive rows reading the same unit hit 8 distinct 4-bank
-// groups.  B columns hold 2 units, swapped on the same row bit.
-HBL_DEV int f6_arot(int row) { return (row >> 2) & 1; }
+// gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16 consecutive
+// lanes per cycle, so 16 consecutive rows reading the same logical unit must
+// hit 16 distinct 16-byte bank groups.  A rows hold 6 units of 16 bytes
+// (96 bytes: 6*row mod 16 repeats after 8 rows); rows with bit 3 set are
+// rotated by one unit.  B columns hold 4 units (stage parity, lane group) of
+// 64-byte rows (repeating after 4 columns), xor-swizzled by column bits 2-3.
+HBL_DEV int f6_arot(int row) { return (row >> 3) & 1; }
+HBL_DEV int f6_bswz(int col) { return (col >> 2) & 3; }
 
 // Copy 16 bytes per lane from global memory (scalar base + 32-bit per-lane
 // offset) straight into LDS at lds_base + 16 * lane (wave-uniform base).
@@ -332,9 +341,8 @@ template <int OUT, int US>
 __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[F6_NBUF * F6_STAGE];
-  constexpr int A_LOADS = F6_A_STAGE / 16 / 256, B_LOADS = F6_B_STAGE / 16 / 256;   // 6 and 2
-  constexpr int NL = A_LOADS + B_LOADS;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[F6_LDS];
+  constexpr int A_LOADS = F6_A_STAGE / 16 / 256, B_LOADS = F6_B_PAIR / 16 / 256;   // 6 and 4
 
   const int bid = blockIdx.x, total = tiles_m * tiles_n;
   const int logical = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
@@ -371,16 +379,16 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   }
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
-    const int P = (j * 4 + wave) * 64 + lane, row = P >> 1, u = (P & 1) ^ f6_arot(row);
-    b_off[j] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + 16 * u;
+    const int P = (j * 4 + wave) * 64 + lane, col = P >> 2, u = (P & 3) ^ f6_bswz(col);
+    b_off[j] = (uint32_t)(min(n0 + col, N - 1) - n0) * wrow + 16 * u;
   }
-  // copy j (A copies 0..5, B copies 6..7) of stage kt into LDS buffer buf
-  auto dma1 = [&](int j, int kt, int buf) __attribute__((always_inline)) {
-    if (j < A_LOADS)
-      lds_copy16s(a_tile + (size_t)kt * a_stage, a_off[j], lds0 + buf * F6_STAGE + (j * 4 + wave_s) * 1024);
-    else
-      lds_copy16s(b_tile + (size_t)kt * F6_BROW, b_off[j - A_LOADS],
-                  lds0 + buf * F6_STAGE + F6_A_STAGE + ((j - A_LOADS) * 4 + wave_s) * 1024);
+  // A copy j (0..5) of stage kt into A buffer buf; B copy j (0..3) of stage
+  // pair p into B slot sl
+  auto dmaA = [&](int j, int kt, int buf) __attribute__((always_inline)) {
+    lds_copy16s(a_tile + (size_t)kt * a_stage, a_off[j], lds0 + buf * F6_A_STAGE + (j * 4 + wave_s) * 1024);
+  };
+  auto dmaB = [&](int j, int p, int sl) __attribute__((always_inline)) {
+    lds_copy16s(b_tile + (size_t)p * F6_BPROW, b_off[j], lds0 + F6_B_BASE + sl * F6_B_PAIR + (j * 4 + wave_s) * 1024);
   };
 
   v16f acc[4][4];
@@ -399,11 +407,13 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
     v16i a[4];
     v4i b[4];
   };
-  auto read1 = [&](Frag& f, int r, int buf) __attribute__((always_inline)) {
-    const uint8_t* sa = smem + buf * F6_STAGE;
+  // read r of stage kt (A buffer kt % 4, B slot (kt / 2) % 2, half kt % 2)
+  auto read1 = [&](Frag& f, int r, int kt) __attribute__((always_inline)) {
+    const uint8_t* sa = smem + (kt & (F6_NBUF - 1)) * F6_A_STAGE;
     if (r < 4) {
       const int n = wn * 128 + r * 32 + l32;
-      f.b[r] = *reinterpret_cast<const v4i*>(sa + F6_A_STAGE + n * F6_BROW + 16 * (g ^ f6_arot(n)));
+      const uint8_t* sb = smem + F6_B_BASE + ((kt >> 1) & 1) * F6_B_PAIR;
+      f.b[r] = *reinterpret_cast<const v4i*>(sb + n * F6_BPROW + 16 * ((2 * (kt & 1) + g) ^ f6_bswz(n)));
     } else {
       const int rb = (r - 4) / 3, t = (r - 4) % 3;
       const int row = wm * 128 + rb * 32 + l32;
@@ -451,8 +461,16 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   // (bf0, from nxt, a few MFMAs after their LDS reads were issued).  All the
   // VALU work then issues between MFMAs.  sched_barrier(0) fixes the order
   // of these groups.
+  // Copy issue order (each A stage 6 instructions per wave, each B pair 4):
+  // prologue A0 B0 A1 A2 B1 A3; at the boundary of stage kt, B pair
+  // (kt+3)/2 if kt is odd, then A stage kt+4.  Before reading stage kt+1
+  // this wave waits until A kt+1 and B pair (kt+1)/2 have landed, which
+  // leaves 16 instructions (A, B, A) in flight after an even stage and 12
+  // (A, A) after an odd one.  Past the end, copies repeat the last stage or
+  // pair into the buffer just freed, which keeps the counts constant.
   const int KT = K / F6_BK;                 // a multiple of US
-  auto stage = [&](int kt, int buf, const Frag& cur, Frag& nxt, v8i* bf0, v8i* bf1) __attribute__((always_inline)) {
+  const int KP = KT / 2;
+  auto stage = [&](int kt, int u, const Frag& cur, Frag& nxt, v8i* bf0, v8i* bf1) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -464,10 +482,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    wait_vmcnt<2 * NL>();
+    if (u & 1) wait_vmcnt<2 * A_LOADS>(); else wait_vmcnt<2 * A_LOADS + B_LOADS>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-    const int nbuf = (buf + 1) & (F6_NBUF - 1);
-    const int dkt = min(kt + F6_NBUF, KT - 1);
+    const int akt = min(kt + F6_NBUF, KT - 1);
+    const int bp = min((kt + 3) >> 1, KP - 1);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const v8i af = aop(cur, 1, rb);
@@ -475,8 +493,14 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
       for (int cb = 0; cb < 4; ++cb) {
         const int i = rb * 4 + cb;
         mfma(af, bf1[cb], acc[rb][cb]);
-        read1(nxt, i, nbuf);
-        if (i & 1) dma1(i >> 1, dkt, buf);
+        read1(nxt, i, u + 1);
+        if (u & 1) {
+          // odd stage: B pair into the slot this pair of stages used, then A
+          if (i < B_LOADS) dmaB(i, bp, ((u + 3) >> 1) & 1);
+          else if (i < B_LOADS + A_LOADS) dmaA(i - B_LOADS, akt, u & (F6_NBUF - 1));
+        } else {
+          if (i & 1) dmaA(i >> 1, akt, u & (F6_NBUF - 1));
+        }
         if (i >= 8 && !(i & 1)) bf0[(i - 8) >> 1] = bexp1(nxt, 0, (i - 8) >> 1);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -484,11 +508,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   };
 
   Frag f0, f1;
+  // prologue: A0 B0 A1 A2 B1 A3
+  auto dmaA_all = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 0; j < F6_NBUF; ++j)
+    for (int j = 0; j < A_LOADS; ++j) dmaA(j, min(kt, KT - 1), kt);
+  };
+  auto dmaB_all = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < NL; ++c) dma1(c, min(j, KT - 1), j);
-  wait_vmcnt<3 * NL>();
+    for (int j = 0; j < B_LOADS; ++j) dmaB(j, min(p, KP - 1), p);
+  };
+  dmaA_all(0); dmaB_all(0); dmaA_all(1); dmaA_all(2); dmaB_all(1); dmaA_all(3);
+  wait_vmcnt<3 * A_LOADS + B_LOADS>();     // A0 and B0 have landed
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 #pragma unroll
   for (int r = 0; r < 16; ++r) read1(f0, r, 0);

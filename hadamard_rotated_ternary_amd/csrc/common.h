@@ -12,6 +12,7 @@ typedef int v12i __attribute__((ext_vector_type(12)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned u6 __attribute__((ext_vector_type(6)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h32 __attribute__((ext_vector_type(32)));
 
 namespace hbl {

@@ -114,23 +114,53 @@ struct PrepCfg {
   static_assert(REGION * 4 >= K + 16 * (K >> 10), "byte buffer must fit");
 };
 
-// Token-wide reductions: the T threads of a token are contiguous lanes of one
-// wave (T <= 64) or whole waves of a one-token workgroup (T > 64).
-template <int T, bool MAX>
-HBL_DEV float token_reduce(float v, float* red) {
+// Reduction over W consecutive lanes (W a power of two up to 64), result in
+// every lane of the group.  Within a row of 16 lanes it uses DPP moves (swap
+// neighbours, swap pairs, mirror 8, mirror 16: after each step every lane
+// holds the reduction of its 2, 4, 8, 16 lanes); across rows, lane reads.
+template <int CTRL>
+HBL_DEV float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <bool MAX>
+HBL_DEV float rop(float a, float b) { return MAX ? fmaxf(a, b) : a + b; }
+template <int W, bool MAX>
+HBL_DEV float lane_reduce(float v) {
+  if constexpr (W >= 2) v = rop<MAX>(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v = rop<MAX>(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) v = rop<MAX>(v, dpp<0x141>(v));   // row_half_mirror
+  if constexpr (W >= 16) v = rop<MAX>(v, dpp<0x140>(v));  // row_mirror
+  if constexpr (W == 32) v = rop<MAX>(v, __shfl_xor(v, 16, 64));
+  if constexpr (W == 64) {
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    v = rop<MAX>(rop<MAX>(r0, r1), rop<MAX>(r2, r3));
+  }
+  return v;
+}
+
+// Token-wide reductions of two statistics at once (a: sum; b: sum or max):
+// the T threads of a token are contiguous lanes of one wave (T <= 64) or
+// whole waves of a one-token workgroup (T > 64).
+template <int T, bool MAXB>
+HBL_DEV void token_reduce2(float& a, float& b, float* red) {
   constexpr int W = T < 64 ? T : 64;
-  v = MAX ? xor_max<W>(v) : xor_sum<W>(v);
+  a = lane_reduce<W, false>(a);
+  b = lane_reduce<W, MAXB>(b);
   if constexpr (T > 64) {
     const int wave = threadIdx.x >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    constexpr int NW = T / 64;   // waves of the token; red holds 2 * NW floats
+    static_assert(2 * NW <= 32, "reduction scratch");
+    if ((threadIdx.x & 63) == 0) { red[wave] = a; red[NW + wave] = b; }
     __syncthreads();
-    float s = red[0];
+    float sa = red[0], sb = red[NW];
 #pragma unroll
-    for (int w = 1; w < T / 64; ++w) s = MAX ? fmaxf(s, red[w]) : s + red[w];
-    v = s;
+    for (int w = 1; w < NW; ++w) { sa += red[w]; sb = rop<MAXB>(sb, red[NW + w]); }
+    a = sa; b = sb;
   }
-  return v;
 }
 
 // Exchange: registers dealt as pass P -> registers dealt as pass P+1.
@@ -207,7 +237,7 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
   using PL = Pass<LOGK, LOGE, C::NP - 1>;
   constexpr int K = C::K, E = C::E, T = C::T;
   __shared__ __attribute__((aligned(16))) float lds[C::REGION * C::TPB];
-  __shared__ float red[16];
+  __shared__ float red[32];
 
   const int tok = threadIdx.x / T;
   const int tau = threadIdx.x % T;
@@ -241,10 +271,19 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
     const int m = first + tok + it * stride;
     const bool valid = m < M;
     float v[E];
+    // ---- RMSNorm statistic (of x, before the gain); bf16 pairs go through
+    // the packed dot product.  It is reduced over the token together with
+    // the quantisation statistic after the transform, which does not need it
+    // (1/r is applied after, as a scalar).
+    float ss = 0.f;
 #pragma unroll
     for (int gi = 0; gi < E / 8; ++gi) {
       if constexpr (XBF16) {
         const uint4 w = raw.u[gi];
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w.x), __builtin_bit_cast(bf2, w.x), ss, false);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w.y), __builtin_bit_cast(bf2, w.y), ss, false);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w.z), __builtin_bit_cast(bf2, w.z), ss, false);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w.w), __builtin_bit_cast(bf2, w.w), ss, false);
         v[8 * gi + 0] = bf16_lo(w.x); v[8 * gi + 1] = bf16_hi(w.x);
         v[8 * gi + 2] = bf16_lo(w.y); v[8 * gi + 3] = bf16_hi(w.y);
         v[8 * gi + 4] = bf16_lo(w.z); v[8 * gi + 5] = bf16_hi(w.z);
@@ -263,11 +302,10 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
       for (int r = 0; r < E; ++r) v[r] = 0.f;
     }
 
-    // ---- RMSNorm statistic (of x, before the gain)
-    float ss = 0.f;
+    if constexpr (!XBF16) {
 #pragma unroll
-    for (int r = 0; r < E; ++r) ss = __builtin_fmaf(v[r], v[r], ss);
-    ss = token_reduce<T, false>(ss, red);
+      for (int r = 0; r < E; ++r) ss = __builtin_fmaf(v[r], v[r], ss);
+    }
     if (gain != nullptr) {
 #pragma unroll
       for (int gi = 0; gi < E / 8; ++gi) {
@@ -278,14 +316,15 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
         v[8 * gi + 4] *= b.x; v[8 * gi + 5] *= b.y; v[8 * gi + 6] *= b.z; v[8 * gi + 7] *= b.w;
       }
     }
-    // c = 1 / (r * sqrt(K)), r = sqrt(mean x^2 + eps)
-    const float rr = sqrtf(ss * (1.0f / K) + kEpsNorm);
-    const float c = 1.0f / (rr * sqrtf((float)K));
-
     // ---- Walsh-Hadamard transform (unnormalised) of x*g
     run_passes<LOGK, LOGE, P2, 0>(v, region, tau);
 
+    // c = 1 / (r * sqrt(K)), r = sqrt(mean x^2 + eps)
+    auto scale_c = [&](float sst) { return 1.0f / (sqrtf(sst * (1.0f / K) + kEpsNorm) * sqrtf((float)K)); };
     if constexpr (MODE == 1) {
+      float unused = 0.f;
+      token_reduce2<T, false>(ss, unused, red);
+      const float c = scale_c(ss);
       if (valid) {
 #pragma unroll
         for (int r = 0; r < E; ++r) xt[(size_t)m * K + baseL + PL::reg_idx(r)] = v[r] * c;
@@ -296,14 +335,13 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
       if constexpr (BITS == 8) {
 #pragma unroll
         for (int r = 0; r < E; ++r) st = fmaxf(st, fabsf(v[r]));
-        st = token_reduce<T, true>(st, red);
-        st = st * c;
       } else {
 #pragma unroll
         for (int r = 0; r < E; ++r) st += fabsf(v[r]);
-        st = token_reduce<T, false>(st, red);
-        st = (st * (1.0f / K)) * c;
       }
+      token_reduce2<T, BITS == 8>(ss, st, red);
+      const float c = scale_c(ss);
+      st = BITS == 8 ? st * c : (st * (1.0f / K)) * c;
       const float Q = BITS == 8 ? kQ8 : kQ4;
       // MODE 2 keeps q + 8 (0..15) in the low byte; the extra 8 is even, so
       // the ties of the rounding fall the same way.

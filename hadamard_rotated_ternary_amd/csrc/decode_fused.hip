@@ -1,0 +1,232 @@
+// Single-launch forward for a few tokens (decode): RMSNorm -> Hadamard
+// rotation -> per-token quantisation -> ternary matmul -> dequant in one
+// kernel.
+//
+// QbitAI article on BitNet v2, section 引入H-BitLinear模块: the layer is
+// normalisation, the online Hadamard transform, activation quantisation, the
+// ternary matmul and dequantisation; 新智元 article "微软再放LLM量化大招",
+// section H-BitLinear模块, for the transform applied to the activations ahead
+// of the quantiser.  With one to four tokens the matmul streams the packed
+// weights once (16 MiB at the 7B down-projection shape) and the activation
+// side is tiny; run as two kernels, the quantiser's latency chain adds a
+// second launch and ~5 us in front of the weight stream.
+//
+// Here every workgroup owns 16 output channels (N/16 workgroups, one per CU
+// at N = 4096).  It first requests its whole slice of the weight stream
+// (16 bytes per lane per 256-k block, straight into registers), then computes
+// the quantised activations of all M tokens itself -- the same transform as
+// the prep kernel, T = 512 threads per token -- while the weights are in
+// flight, and keeps them in LDS in int8 operand form.  Redundant across
+// workgroups (each reads the M tokens from L2), but it hides under the
+// weight stream.  The matmul part is the few-token decode kernel's:
+// v_mfma_i32_16x16x64_i8 with channels on the instruction's M side and the
+// tokens on its N side, integer partials of the 8 waves combined with LDS
+// atomics, then the dequant epilogue.
+#include "fwht.h"
+#include "mma.h"
+
+namespace hbl {
+
+constexpr int FD_NW = 8, FD_MAXM = 4, FD_DKB = 256;
+
+template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int OUT>
+__global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
+    const void* __restrict__ x, const float* __restrict__ gain, const uint8_t* __restrict__ W,
+    const float* __restrict__ walpha, void* __restrict__ Y, int M, int N) {
+  using C = PrepCfg<LOGK, LOGE, P2>;
+  static_assert(C::T == 64 * FD_NW, "one token per pass of the whole workgroup");
+  using P0 = Pass<LOGK, LOGE, 0>;
+  using PL = Pass<LOGK, LOGE, C::NP - 1>;
+  constexpr int K = C::K, E = C::E;
+  constexpr int NBLK = K / FD_DKB;
+  constexpr int MAXB = NBLK / FD_NW;
+  static_assert(MAXB * FD_NW == NBLK, "256-k blocks dealt evenly over the waves");
+  constexpr int REGION_BYTES = (C::REGION * 4 + 15) & ~15;
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  float* region = reinterpret_cast<float*>(dyn);               // transform exchange
+  uint8_t* slab = dyn + REGION_BYTES;                          // [M][K] operand bytes, then a zero row
+  __shared__ float red[32];
+  __shared__ int part[16 * 16];
+  __shared__ float dtok[FD_MAXM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int ch0 = blockIdx.x * 16;
+
+  // ---- the tokens (bf16) and the gain are requested before the weights:
+  // loads complete in issue order, so anything requested after the weight
+  // stream could only be used once the whole stream had arrived
+  const int base0 = P0::thr_idx(tid);
+  const int baseL = PL::thr_idx(tid);
+  uint4 xr[XBF16 ? FD_MAXM : 1][E / 8];
+  if constexpr (XBF16) {
+#pragma unroll
+    for (int t = 0; t < FD_MAXM; ++t) {
+      const int tt = min(t, M - 1);
+#pragma unroll
+      for (int gi = 0; gi < E / 8; ++gi)
+        xr[t][gi] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (size_t)tt * K + base0 +
+                                                    P0::reg_idx(8 * gi));
+    }
+  }
+  float gv[E];
+  if (gain != nullptr) {
+#pragma unroll
+    for (int gi = 0; gi < E / 8; ++gi) {
+      const float4* p = reinterpret_cast<const float4*>(gain + base0 + P0::reg_idx(8 * gi));
+      const float4 a = p[0], b = p[1];
+      gv[8 * gi + 0] = a.x; gv[8 * gi + 1] = a.y; gv[8 * gi + 2] = a.z; gv[8 * gi + 3] = a.w;
+      gv[8 * gi + 4] = b.x; gv[8 * gi + 5] = b.y; gv[8 * gi + 6] = b.z; gv[8 * gi + 7] = b.w;
+    }
+  }
+
+  // ---- weight stream: block b = wave + FD_NW * i, 16 bytes per lane
+  uint4 wq[MAXB];
+  const int n = min(ch0 + c, N - 1);
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    const int b = wave + FD_NW * i;
+    wq[i] = *reinterpret_cast<const uint4*>(W + (size_t)n * (K / 4) + (size_t)b * (FD_DKB / 4) + 16 * g);
+  }
+
+  // ---- quantised activations of the M tokens, into LDS
+  const float Q = BITS == 8 ? kQ8 : kQ4;
+#pragma unroll
+  for (int t = 0; t < FD_MAXM; ++t) {
+    if (t >= M) break;                                     // uniform
+    float v[E];
+    float ss = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < E / 8; ++gi) {
+      const int idx = base0 + P0::reg_idx(8 * gi);
+      if constexpr (XBF16) {
+        const uint4 w = xr[t][gi];
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w.x), __builtin_bit_cast(bf2, w.x), ss, false);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w.y), __builtin_bit_cast(bf2, w.y), ss, false);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w.z), __builtin_bit_cast(bf2, w.z), ss, false);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w.w), __builtin_bit_cast(bf2, w.w), ss, false);
+        v[8 * gi + 0] = bf16_lo(w.x); v[8 * gi + 1] = bf16_hi(w.x);
+        v[8 * gi + 2] = bf16_lo(w.y); v[8 * gi + 3] = bf16_hi(w.y);
+        v[8 * gi + 4] = bf16_lo(w.z); v[8 * gi + 5] = bf16_hi(w.z);
+        v[8 * gi + 6] = bf16_lo(w.w); v[8 * gi + 7] = bf16_hi(w.w);
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + (size_t)t * K + idx);
+        const uint4 a = p[0], b = p[1];
+        v[8 * gi + 0] = __uint_as_float(a.x); v[8 * gi + 1] = __uint_as_float(a.y);
+        v[8 * gi + 2] = __uint_as_float(a.z); v[8 * gi + 3] = __uint_as_float(a.w);
+        v[8 * gi + 4] = __uint_as_float(b.x); v[8 * gi + 5] = __uint_as_float(b.y);
+        v[8 * gi + 6] = __uint_as_float(b.z); v[8 * gi + 7] = __uint_as_float(b.w);
+#pragma unroll
+        for (int r = 8 * gi; r < 8 * gi + 8; ++r) ss = __builtin_fmaf(v[r], v[r], ss);
+      }
+    }
+    if (gain != nullptr) {
+#pragma unroll
+      for (int r = 0; r < E; ++r) v[r] *= gv[r];
+    }
+    run_passes<LOGK, LOGE, P2, 0>(v, region, tid);
+    float st = 0.f;
+    if constexpr (BITS == 8) {
+#pragma unroll
+      for (int r = 0; r < E; ++r) st = fmaxf(st, fabsf(v[r]));
+    } else {
+#pragma unroll
+      for (int r = 0; r < E; ++r) st += fabsf(v[r]);
+    }
+    token_reduce2<C::T, BITS == 8>(ss, st, red);
+    // c = 1 / (r * sqrt(K)), r = sqrt(mean x^2 + eps); statistic of xt = v * c
+    const float cc = 1.0f / (sqrtf(ss * (1.0f / K) + kEpsNorm) * sqrtf((float)K));
+    st = BITS == 8 ? st * cc : (st * (1.0f / K)) * cc;
+    const float G = fmaxf(st, kEpsQ);
+    const float cs = cc * (Q / G);
+    if (tid == 0) dtok[t] = G / Q;
+    // round to nearest even in the adder (fma with 1.5 * 2^23), clamp INT4,
+    // keep the low byte; operand bytes are q (INT8) or 16 q (INT4)
+    uint8_t* row = slab + t * K;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      float q = __builtin_fmaf(v[r], cs, kRoundMagic);
+      if constexpr (BITS == 4) q = fminf(fmaxf(q, kRoundMagic - 8.0f), kRoundMagic + 7.0f);
+      const uint32_t b = __float_as_uint(q);
+      row[baseL + PL::reg_idx(r)] = (uint8_t)(BITS == 8 ? b : (b << 4));
+    }
+  }
+  if (tid < 4) reinterpret_cast<uint4*>(slab + M * K)[tid] = make_uint4(0, 0, 0, 0);
+  if (tid < 256) part[tid] = 0;
+  __syncthreads();
+
+  // ---- matmul: 16 channels x up to 4 tokens, k blocks dealt over the waves
+  v4i acc = v4i{};
+  const uint8_t* arow = c < M ? slab + c * K + 64 * g : slab + M * K;
+  const int astep = c < M ? 1 : 0;                         // padding lanes keep reading the zero row
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    const int b = wave + FD_NW * i;
+    const uint4* ap = reinterpret_cast<const uint4*>(arow + astep * b * FD_DKB);
+    const uint4 a0 = ap[0], a1 = ap[1], a2 = ap[2], a3 = ap[3];
+    const uint4 p = wq[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4i wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
+      const v4i aop = v4i{(int)u4get(a0, j), (int)u4get(a1, j), (int)u4get(a2, j), (int)u4get(a3, j)};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc, 0, 0, 0);
+    }
+  }
+  // 16x16 accumulator layout: lane l, register r -> channel 4*(l/16) + r, token l%16
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (c < M) atomicAdd(&part[c * 16 + 4 * g + r], acc[r]);
+  __syncthreads();
+  if (tid < M * 16) {
+    const int t = tid / 16, nn = ch0 + tid % 16;
+    if (nn < N) store_out<OUT>(Y, (size_t)t * N + nn, unscale<BITS>(part[tid]), dtok[t] * fmaxf(walpha[0], kEpsQ));
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int OUT>
+static hipError_t launch_fd_t(const FusedDecodeArgs& a) {
+  using C = PrepCfg<LOGK, LOGE, P2>;
+  const size_t lds = (size_t)((C::REGION * 4 + 15) & ~15) + (size_t)a.M * C::K + 64;
+  auto kern = &decode_fused_kernel<LOGK, LOGE, P2, BITS, XBF16, OUT>;
+  // more than 64 KiB of dynamic LDS needs the per-function limit raised,
+  // once per device and instantiation
+  static bool attr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr[dev]) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       146 * 1024);
+    if (e != hipSuccess) return e;
+    attr[dev] = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((a.N + 15) / 16), dim3(64 * FD_NW), lds, a.stream, a.x, a.gain, a.wpack, a.walpha,
+                     a.out, a.M, a.N);
+  return hipGetLastError();
+}
+
+template <int LOGK, int LOGE, int P2>
+static hipError_t launch_fd_k(const FusedDecodeArgs& a) {
+#define HBL_FD(BITS, BF, OUT) return launch_fd_t<LOGK, LOGE, P2, BITS, BF, OUT>(a)
+  if (a.bits == 8) {
+    if (a.x_bf16) { if (a.out_kind == OUT_BF16) HBL_FD(8, true, OUT_BF16); HBL_FD(8, true, OUT_F32); }
+    if (a.out_kind == OUT_BF16) HBL_FD(8, false, OUT_BF16);
+    HBL_FD(8, false, OUT_F32);
+  }
+  if (a.x_bf16) { if (a.out_kind == OUT_BF16) HBL_FD(4, true, OUT_BF16); HBL_FD(4, true, OUT_F32); }
+  if (a.out_kind == OUT_BF16) HBL_FD(4, false, OUT_BF16);
+  HBL_FD(4, false, OUT_F32);
+#undef HBL_FD
+}
+
+bool decode_fused_supported(int M, int logk) { return M >= 1 && M <= FD_MAXM && (logk == 13 || logk == 14); }
+
+hipError_t launch_decode_fused(const FusedDecodeArgs& a) {
+  if (!decode_fused_supported(a.M, a.logk)) return hipErrorInvalidValue;
+  // T = 512 threads per token: E = K / 512 values per thread
+  if (a.logk == 14) return launch_fd_k<14, 5, 8>(a);
+  return launch_fd_k<13, 4, 6>(a);
+}
+
+}  // namespace hbl

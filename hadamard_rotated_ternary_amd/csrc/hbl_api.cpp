@@ -77,6 +77,13 @@ hbl_status forward(int bits, const void* x, hbl_dtype x_dtype, const float* gain
   int cus = 0;
   if (hbl_status s = check_device(&cus)) return s;
 
+  if (hbl::decode_fused_supported((int)M, log2_exact(K))) {
+    hbl::FusedDecodeArgs f{};
+    f.x = x; f.x_bf16 = x_dtype == HBL_BF16; f.gain = gain; f.wpack = w_packed; f.walpha = w_alpha; f.out = y;
+    f.out_kind = y_dtype == HBL_BF16 ? hbl::OUT_BF16 : hbl::OUT_F32;
+    f.M = (int)M; f.N = (int)N; f.logk = log2_exact(K); f.bits = bits; f.stream = stream;
+    return launched(hbl::launch_decode_fused(f));
+  }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* codes = ws;
   float* dscale = reinterpret_cast<float*>(ws + codes_bytes(bits, M, K));

@@ -45,6 +45,22 @@ hipError_t launch_gemm_fp6(const GemmArgs& a);
 // Workspace bytes the matmul needs beyond the codes and scales.
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
+// Single-launch forward for 1..4 tokens with K = 8192 or 16384 (decode):
+// transform, quantiser and matmul in one kernel.
+struct FusedDecodeArgs {
+  const void* x;
+  bool x_bf16;
+  const float* gain;
+  const uint8_t* wpack;
+  const float* walpha;
+  void* out;
+  int out_kind;           // OUT_F32 or OUT_BF16
+  int M, N, logk, bits;
+  hipStream_t stream;
+};
+bool decode_fused_supported(int M, int logk);
+hipError_t launch_decode_fused(const FusedDecodeArgs& a);
+
 struct WquantArgs {
   const float* w;
   int N, K;

@@ -1,0 +1,65 @@
+// Device helpers shared by the matmul kernels: packed-operand expansion for
+// the int8 matrix instructions, exact unscaling, global-to-LDS copies with
+// explicit waits, and the dequantising store.
+#pragma once
+#include "common.h"
+#include "launch.h"
+
+namespace hbl {
+
+// Operand expansion without lookups.
+//
+// A packed weight word holds the 2-bit two's complement codes of 16
+// consecutive k, the code of k0+4j+i in bits 8i+2j (field j of byte i).
+// Shifting field j to the top of its byte and masking gives, byte by byte,
+// exactly 64*w as a signed int8 (0x40 = +64, 0xC0 = -64).  MFMA step j of a
+// 64-k group takes field j of four packed words, so its operand covers codes
+// 16d + 4j + i (d = word, i = byte): 1-2 VALU ops per operand dword.
+HBL_DEV uint32_t wfield(uint32_t p, int j) {
+  return (j == 3 ? p : (p << (6 - 2 * j))) & 0xC0C0C0C0u;
+}
+// INT4 activation words hold codes 8 at a time, the code of k0+4j+i in bits
+// 8i+4j.  Moving a nibble to the top of its byte gives 16*q as a signed int8.
+// For the same code set 16d + 4j + i, step j takes the low (j even) or high
+// (j odd) nibbles of word 2d + j/2.
+HBL_DEV uint32_t a4field(uint32_t w, int j) {
+  return ((j & 1) ? w : (w << 4)) & 0xF0F0F0F0u;
+}
+// The accumulators therefore hold 64 * acc (INT8 path) or 1024 * acc (INT4),
+// exact multiples whose magnitude stays below 2^27 for K <= 16384 (|q| <= 128
+// after scaling, |w| = 64): an arithmetic shift recovers acc exactly.
+template <int BITS>
+HBL_DEV int unscale(int v) { return BITS == 8 ? (v >> 6) : (v >> 10); }
+HBL_DEV uint32_t u4get(const uint4& u, int j) { return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w; }
+
+// Copy 16 bytes per lane from global memory straight into LDS: the wave's
+// 64 lanes fill 1 KiB at lds_base (wave-uniform), lane L at +16L.  Issued from
+// inline asm so the compiler does not track it (it cannot tell which LDS
+// buffer such a copy targets and would otherwise wait for every copy before
+// any LDS read); the caller orders it with wait_vmcnt() and s_barrier.  The
+// instruction has no destination registers and reads its address operands at
+// issue.
+HBL_DEV void lds_copy16(const void* gsrc, void* lds_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(l), "v"(gsrc) : "memory", "m0");
+}
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt[3:0] and [15:14], expcnt and lgkmcnt at max).
+template <int N>
+HBL_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int OUT>
+HBL_DEV void store_out(void* Y, size_t off, int acc, float t) {
+  if constexpr (OUT == OUT_ACC_I32) {
+    static_cast<int32_t*>(Y)[off] = acc;
+  } else if constexpr (OUT == OUT_F32) {
+    static_cast<float*>(Y)[off] = (float)acc * t;
+  } else {
+    static_cast<uint16_t*>(Y)[off] = f32_to_bf16((float)acc * t);
+  }
+}
+
+}  // namespace hbl

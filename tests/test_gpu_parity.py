@@ -228,6 +228,25 @@ def test_layer_full_workloads(name, count):
 
 # ------------------------------------------------------------------ invariants of the GPU path
 
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,K,N,xdt,gain", [(1, 16384, 4096, "bf16", False), (2, 16384, 272, "bf16", True),
+                                            (3, 8192, 4096, "f32", False), (4, 16384, 16, "f32", True),
+                                            (4, 8192, 528, "bf16", False), (1, 8192, 48, "bf16", True)])
+def test_single_launch_decode(bits, M, K, N, xdt, gain):
+    """1..4 tokens at K = 8192 / 16384 run as one kernel (transform, quantiser
+    and matmul together).  Against the oracle at the layer bar, and against the
+    two-kernel stage path on the same inputs (the transform's summation order
+    differs, so codes may differ at rounding ties only)."""
+    w = synthetic.Workload("t", M, K, N, bits, xdt, "laplace", 0.05, max(1, K // 200), 100.0, 5 * M + K + N)
+    g = synthetic.make_gain(K, M) if gain else None
+    yh, y_ref, ref, xd, wp, a, rows = run_layer(w, gain=g)
+    assert rel_l2(yh, y_ref) <= 2e-3, rel_l2(yh, y_ref)
+    gd = None if g is None else dev(g)
+    codes, d = hbl.quantize_act(xd, bits, gain=gd)
+    y2 = host(hbl.matmul_dequant(codes, bits, d, wp, a, K, out_dtype=xd.dtype).float())
+    assert rel_l2(yh, y2) <= 1e-3, rel_l2(yh, y2)
+
+
 @pytest.mark.parametrize("M,K,N", [(65, 256, 16), (257, 1024, 272), (300, 2048, 512), (513, 16384, 256),
                                    (1000, 4096, 4096), (8192, 16384, 4096)])
 def test_int4_prefill_fp6_path_equals_int8_instruction_path(M, K, N):

@@ -536,7 +536,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
   // uint4 registers, kept near 48 (192 VGPRs).
   constexpr int MAXB = (48 / (CPW + MB * BITS / 2)) >= 8 ? 8 : (48 / (CPW + MB * BITS / 2)) >= 4 ? 4 : 2;
   constexpr int CH = 16 * CPW;
-  __shared__ int red[CH * MB * 16];
+  // Partial sums per (token, channel), rows of RL ints.  Inside each block of
+  // 16 channels column 4r + q holds channel 4q + r, and RL = 4 (mod 64): the
+  // 64 lanes of one accumulate (token c, channel 4g + r) then hit 64 distinct
+  // banks (4c + g), where plain rows of CH ints would put 16 lanes on one.
+  constexpr int RL = CH + 4;
+  __shared__ int red[MB * 16 * RL];
+  auto red_col = [](int nl) { return (nl & ~15) | ((nl & 3) << 2) | ((nl >> 2) & 3); };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int ch0 = blockIdx.x * CH, s = blockIdx.y;
@@ -544,7 +550,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
   const int nblk = Kr / DKB;                                   // 256-k blocks in this range
   const size_t arow = (size_t)K * BITS / 8;
 
-  for (int i = tid; i < CH * MB * 16; i += 64 * NW) red[i] = 0;
+  for (int i = tid; i < MB * 16 * RL; i += 64 * NW) red[i] = 0;
   // epilogue scales fetched up front (their latency is not paid at the end)
   const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
   float ds_pre[(MB * 16 * CH + 64 * NW - 1) / (64 * NW)];
@@ -603,7 +609,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
               aop = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
                         (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
             }
-            if (16 * mb + c >= M) aop = v4i{};   // padding tokens
+            // padding tokens (16*mb + c >= M) read token M-1's codes; their
+            // sums are never stored
             acc[cp][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc[cp][mb], 0, 0, 0);
           }
         }
@@ -618,7 +625,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (16 * mb + c < M) atomicAdd(&red[(16 * mb + c) * CH + 16 * cp + 4 * g + r], acc[cp][mb][r]);
+        if (16 * mb + c < M) atomicAdd(&red[(16 * mb + c) * RL + 16 * cp + 4 * r + g], acc[cp][mb][r]);
   __syncthreads();
 
 #pragma unroll
@@ -627,7 +634,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
     if (e >= M * CH) continue;
     const int t = e / CH, n = ch0 + e % CH;
     if (n >= N) continue;
-    const int v = red[e];
+    const int v = red[t * RL + red_col(e % CH)];
     if (S == 1) store_out<OUT>(Y, (size_t)t * N + n, unscale<BITS>(v), ds_pre[q] * aw);
     else partial[((size_t)s * M + t) * N + n] = v;
   }

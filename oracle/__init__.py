@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_gemm_ternary.argtypes = [P, P, I64, I64, I64, P, I]
         L.oracle_dequant.argtypes = [P, P, ctypes.c_float, I64, I64, P]
         L.oracle_forward.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, I, P, P, P, P, P, P, I]
+        L.oracle_forward_ex.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, I, I, P, P, P, P, P, P, I]
+        L.oracle_quantize_weights_rotated.argtypes = [P, I64, I64, P, P, P]
         _lib = L
     return _lib
 
@@ -145,11 +147,12 @@ def dequant(acc: np.ndarray, d: np.ndarray, alpha) -> np.ndarray:
 
 
 def forward(x: np.ndarray, wt: np.ndarray, alpha, bits: int, g: np.ndarray | None = None,
-            keep: bool = True, nthreads: int = 0) -> dict:
-    """Whole layer on fp32 activations [M][K] with ternary weights [N][K].
+            keep: bool = True, nthreads: int = 0, rotate: bool = True) -> dict:
+    """Whole layer on fp32 activations [M][K] with ternary weights [N][K]:
+    H-BitLinear (rotate=True) or BitLinear without the rotation (rotate=False).
 
     Returns a dict with ``y`` (double [M][N]) and, if ``keep``, the stages
-    ``xt``, ``q``, ``d``, ``pre``, ``acc``.
+    ``xt`` (the quantiser's input), ``q``, ``d``, ``pre``, ``acc``.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     wt = np.ascontiguousarray(wt, dtype=np.int8)
@@ -161,11 +164,24 @@ def forward(x: np.ndarray, wt: np.ndarray, alpha, bits: int, g: np.ndarray | Non
     if keep:
         out.update(xt=np.empty((M, K)), q=np.empty((M, K), dtype=np.int8), d=np.empty(M),
                    pre=np.empty((M, K)), acc=np.empty((M, N), dtype=np.int32))
-    rc = lib().oracle_forward(_p(x), _p(g), _p(wt), float(alpha), M, K, N, bits,
-                              _p(out.get("xt")), _p(out.get("q")), _p(out.get("d")),
-                              _p(out.get("pre")), _p(out.get("acc")), _p(y), nthreads)
+    rc = lib().oracle_forward_ex(_p(x), _p(g), _p(wt), float(alpha), M, K, N, bits, int(bool(rotate)),
+                                 _p(out.get("xt")), _p(out.get("q")), _p(out.get("d")),
+                                 _p(out.get("pre")), _p(out.get("acc")), _p(y), nthreads)
     _chk(rc, "forward")
     return out
+
+
+def quantize_weights_rotated(w: np.ndarray):
+    """Weight + activation rotation variant: rows rotated by H_K / sqrt(K),
+    then ternarised.  Returns (w_t int8 [N][K], alpha fp32, rotated rows double)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    wt = np.empty((N, K), dtype=np.int8)
+    alpha = np.zeros(1, dtype=np.float32)
+    wr = np.empty((N, K), dtype=np.float64)
+    _chk(lib().oracle_quantize_weights_rotated(_p(w), N, K, _p(wt), _p(alpha), _p(wr)),
+         "quantize_weights_rotated")
+    return wt, np.float32(alpha[0]), wr
 
 
 def to_bf16_rne(y: np.ndarray) -> np.ndarray:

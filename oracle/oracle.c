@@ -15,6 +15,11 @@
  *             揭秘核心魔法：H-BitLinear与Hadamard变换
  *   [DIGEST]  "BitNet v2: Native 4-bit Activations with Hadamard Transformation
  *             for 1-bit LLMs" (arXiv digest page), abstract and 方法详解
+ *   Variants beside H-BitLinear (same quantisers and matmul):
+ *     BitLinear without the rotation, for the layers whose inputs are already
+ *       close to Gaussian (attention/FFN input projections) [XZY §H-BitLinear模块];
+ *     weights rotated offline as well (weight + activation rotation, the
+ *       ablation of [XZY §实验效果], table 5).
  *
  * Precision: every floating-point step is done in double; values are rounded
  * only where the method itself produces a stored low-precision quantity
@@ -223,10 +228,10 @@ int oracle_dequant(const int32_t *acc, const double *d, float alpha, int64_t M, 
  *   xt [M][K] double, q [M][K] int8, d [M] double, pre [M][K] double,
  *   acc [M][N] int32, y [M][N] double.
  * ------------------------------------------------------------------------- */
-int oracle_forward(const float *x, const float *g, const int8_t *wt, float alpha,
-                   int64_t M, int64_t K, int64_t N, int bits,
-                   double *xt, int8_t *q, double *d, double *pre, int32_t *acc, double *y,
-                   int nthreads)
+int oracle_forward_ex(const float *x, const float *g, const int8_t *wt, float alpha,
+                      int64_t M, int64_t K, int64_t N, int bits, int rotate,
+                      double *xt, int8_t *q, double *d, double *pre, int32_t *acc, double *y,
+                      int nthreads)
 {
     if (!x || !wt || !y || M < 0 || N <= 0 || !is_pow2(K) || (bits != 8 && bits != 4)) return -1;
     double a = oracle_weight_scale(alpha);
@@ -242,7 +247,8 @@ int oracle_forward(const float *x, const float *g, const int8_t *wt, float alpha
         if (!u || !t || !qm) { bad = 1; free(u); free(t); free(qm); continue; }
         double dm;
         oracle_rmsnorm(x + m * K, g, K, u);
-        oracle_hadamard_rotate(u, K, t);
+        if (rotate) oracle_hadamard_rotate(u, K, t);
+        else memcpy(t, u, (size_t)K * sizeof(double));
         oracle_quant_act(t, K, bits, qm, &dm, pre ? pre + m * K : NULL);
         for (int64_t n = 0; n < N; ++n) {
             int32_t s = 0;
@@ -256,6 +262,55 @@ int oracle_forward(const float *x, const float *g, const int8_t *wt, float alpha
         free(u); free(t); free(qm);
     }
     return bad ? -2 : 0;
+}
+
+/* H-BitLinear forward (with the rotation). */
+int oracle_forward(const float *x, const float *g, const int8_t *wt, float alpha,
+                   int64_t M, int64_t K, int64_t N, int bits,
+                   double *xt, int8_t *q, double *d, double *pre, int32_t *acc, double *y,
+                   int nthreads)
+{
+    return oracle_forward_ex(x, g, wt, alpha, M, K, N, bits, 1, xt, q, d, pre, acc, y, nthreads);
+}
+
+/* ---------------------------------------------------------------------------
+ * Weight + activation rotation [XZY §实验效果] (table 5 compares rotating the
+ * activations only with rotating weights and activations).  Reading: each
+ * weight row (one output channel over the K inputs) goes through the same
+ * orthonormal transform as the activations, so that
+ *   (H u / sqrt(K)) . (H w / sqrt(K)) = u . w
+ * in exact arithmetic (H symmetric, H H = K I); the rotated rows are then
+ * ternarised as usual:
+ *   wr[n] = H_K w[n] / sqrt(K)   (double),
+ *   S = sum |wr| (rows in order, then the row sums in order, double),
+ *   alpha = (float)(S / (N K)),  a = max(alpha, EPS_Q),
+ *   w_t = clamp(round(wr / a), -1, 1).
+ * wr (optional) receives the rotated rows.
+ * ------------------------------------------------------------------------- */
+int oracle_quantize_weights_rotated(const float *w, int64_t N, int64_t K, int8_t *wt, float *alpha_out,
+                                    double *wr_out)
+{
+    if (!w || !wt || !alpha_out || N <= 0 || !is_pow2(K)) return -1;
+    double *wr = (double *)malloc((size_t)N * K * sizeof(double));
+    double *row = (double *)malloc((size_t)K * sizeof(double));
+    if (!wr || !row) { free(wr); free(row); return -2; }
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) row[k] = (double)w[n * K + k];
+        oracle_hadamard_rotate(row, K, wr + n * K);
+    }
+    double S = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double rs = 0.0;
+        for (int64_t k = 0; k < K; ++k) rs += fabs(wr[n * K + k]);
+        S += rs;
+    }
+    float alpha = (float)(S / ((double)N * (double)K));
+    double a = oracle_weight_scale(alpha);
+    for (int64_t i = 0; i < N * K; ++i) wt[i] = (int8_t)clampd(rne(wr[i] / a), -1.0, 1.0);
+    *alpha_out = alpha;
+    if (wr_out) memcpy(wr_out, wr, (size_t)N * K * sizeof(double));
+    free(wr); free(row);
+    return 0;
 }
 
 int oracle_max_threads(void)

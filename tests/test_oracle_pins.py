@@ -315,3 +315,91 @@ def test_hadamard_tames_outlier_channels(name):
         q, d, _ = oracle.quant_act(v, 4)
         return np.mean((v - q * d[:, None]) ** 2) / np.mean(v ** 2)
     assert rel_mse(xt) / rel_mse(u) < 0.1
+
+
+# ----------------------------------------------------------------- BitLinear without the rotation
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("c", [0.7, 3e-3])
+def test_unrotated_constant_token_closed_form(bits, c):
+    """x = c (every feature): RMSNorm gives u_k = v = c / sqrt(c^2 + eps) for all
+    k, so without the rotation every code is 127 (INT8) or round(sqrt 7) = 3
+    (INT4) and y_n = v a R_n (INT8) or 3 v a R_n / sqrt 7 (INT4), R_n the row
+    sum of W_t."""
+    K, N = 512, 20
+    rng = np.random.default_rng(5)
+    wt, alpha = oracle.quantize_weights(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    x = np.full((1, K), c, np.float32)
+    cf = float(np.float32(c))
+    v = cf / math.sqrt(cf * cf + 1e-6)
+    R = wt.astype(np.float64).sum(1)
+    out = oracle.forward(x, wt, alpha, bits, rotate=False)
+    np.testing.assert_allclose(out["xt"][0], v, rtol=1e-14)
+    if bits == 8:
+        np.testing.assert_array_equal(out["q"][0], 127)
+        np.testing.assert_allclose(out["y"][0], v * a_of(alpha) * R, rtol=1e-12, atol=1e-15)
+    else:
+        np.testing.assert_array_equal(out["q"][0], 3)
+        np.testing.assert_allclose(out["y"][0], 3 * v * a_of(alpha) * R / math.sqrt(7), rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_unrotated_brute_force_dense_small(bits):
+    """Tiny inputs against an independent implementation of the layer with the
+    rotation left out (quantiser input = RMSNorm output)."""
+    rng = np.random.default_rng(41 + bits)
+    M, K, N = 5, 32, 6
+    x = rng.normal(size=(M, K)).astype(np.float32)
+    g = synthetic.make_gain(K, 2)
+    wt, alpha = oracle.quantize_weights(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    out = oracle.forward(x, wt, alpha, bits, g=g, rotate=False)
+    xd = x.astype(np.float64)
+    u = xd * g / np.sqrt(np.mean(xd ** 2, axis=1, keepdims=True) + 1e-6)
+    if bits == 8:
+        G = np.maximum(np.abs(u).max(1), 1e-5); Q = 127.0; lo, hi = -128, 127
+    else:
+        G = np.maximum(np.abs(u).mean(1), 1e-5); Q = math.sqrt(7); lo, hi = -8, 7
+    q = np.clip(np.round(u * (Q / G)[:, None]), lo, hi)
+    y = (q @ wt.T.astype(np.float64)) * (G / Q)[:, None] * a_of(alpha)
+    np.testing.assert_allclose(out["xt"], u, rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(out["q"], q)
+    np.testing.assert_allclose(out["y"], y, rtol=1e-13, atol=1e-16)
+
+
+# ----------------------------------------------------------------- weights rotated as well
+
+def test_rotated_weights_definition_and_cancellation():
+    """Rows rotated by H / sqrt(K) (dense Sylvester matrix, independent of the
+    fast transform), then ternarised as usual; and the rotation cancels in the
+    layer's inner product: (H u / sqrt K) . (H w / sqrt K) = u . w."""
+    rng = np.random.default_rng(9)
+    N, K = 6, 64
+    w = rng.normal(0, 0.02, (N, K)).astype(np.float32)
+    wt, alpha, wr = oracle.quantize_weights_rotated(w)
+    H = dense_sylvester(K) / math.sqrt(K)
+    np.testing.assert_allclose(wr, w.astype(np.float64) @ H.T, rtol=0, atol=1e-15)
+    S = sum(np.abs(wr[n]).sum() for n in range(N))
+    assert alpha == np.float32(S / (N * K))
+    a = a_of(alpha)
+    np.testing.assert_array_equal(wt, np.clip(np.round(wr / a), -1, 1))
+    u = rng.normal(size=(3, K))
+    np.testing.assert_allclose((u @ H.T) @ wr.T, u @ w.T.astype(np.float64), rtol=1e-12, atol=1e-14)
+
+
+def test_rotated_weights_one_hot_and_involution():
+    """A one-hot row e_j rotates to the Walsh function (-1)^popcount(k&j)/sqrt K
+    (all magnitudes equal, so every code is +-1 with alpha = 1/sqrt K), and
+    rotating the rotated rows again gives back the original rows."""
+    K = 256
+    for j in (0, 5, 200):
+        w = np.zeros((1, K), np.float32); w[0, j] = 1.0
+        wt, alpha, wr = oracle.quantize_weights_rotated(w)
+        walsh = np.array([popcount_sign(k, j) for k in range(K)])
+        np.testing.assert_allclose(wr[0], walsh / math.sqrt(K), rtol=1e-14)
+        assert alpha == np.float32(1 / math.sqrt(K))
+        np.testing.assert_array_equal(wt[0], walsh)
+    rng = np.random.default_rng(3)
+    w = rng.normal(size=(4, K)).astype(np.float32)
+    _, _, wr = oracle.quantize_weights_rotated(w)
+    back = np.stack([oracle.hadamard_rotate(r) for r in wr])
+    np.testing.assert_allclose(back, w, rtol=0, atol=1e-12)

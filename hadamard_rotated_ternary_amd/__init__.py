@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libhbl.so")
 HEADER = os.path.join(_HERE, "..", "include", "hbl.h")
 
 HBL_F32, HBL_BF16 = 0, 1
-OP_QUANTIZE_WEIGHTS, OP_MATMUL, OP_FORWARD_INT4, OP_FORWARD_INT8 = 0, 1, 4, 8
+OP_QUANTIZE_WEIGHTS, OP_MATMUL, OP_QUANTIZE_WEIGHTS_ROTATED, OP_FORWARD_INT4, OP_FORWARD_INT8 = 0, 1, 2, 4, 8
 STATUS = {0: "HBL_OK", 1: "HBL_ERR_NULL", 2: "HBL_ERR_SHAPE", 3: "HBL_ERR_DTYPE", 4: "HBL_ERR_ALIGN",
           5: "HBL_ERR_WORKSPACE", 6: "HBL_ERR_LAUNCH", 7: "HBL_ERR_DEVICE"}
 
@@ -42,6 +42,9 @@ SIGNATURES = {
     "hbl_rmsnorm_fwht": ([P, I, P, I64, I64, P, P], I),
     "hbl_gemm_ternary": ([P, I, P, I64, I64, I64, P, P, SZ, P], I),
     "hbl_unpack_weights": ([P, I64, I64, P, P], I),
+    "hbl_bitlinear_forward": ([P, I, P, P, P, I64, I64, I64, I, P, I, P, SZ, P], I),
+    "hbl_quantize_act_unrotated": ([P, I, P, I64, I64, I, P, P, P], I),
+    "hbl_quantize_weights_rotated": ([P, I64, I64, P, P, P, SZ, P], I),
 }
 
 
@@ -106,20 +109,26 @@ def _workspace(nbytes, device, workspace=None):
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
-def quantize_weights(w: torch.Tensor):
-    """Latent fp32 weights [N][K] -> (packed uint8 [N][K/4], alpha fp32 [1])."""
+def quantize_weights(w: torch.Tensor, rotate: bool = False):
+    """Latent fp32 weights [N][K] -> (packed uint8 [N][K/4], alpha fp32 [1]).
+    rotate=True ternarises the rows rotated like the activations
+    (weight + activation rotation variant)."""
     _dev(w, "w")
     N, K = w.shape
     wp = torch.empty((N, K // 4), dtype=torch.uint8, device=w.device)
     alpha = torch.empty(4, dtype=torch.float32, device=w.device)[:1]
-    ws = _workspace(workspace_bytes(OP_QUANTIZE_WEIGHTS, 0, K, N), w.device)
-    _call("hbl_quantize_weights", _ptr(w), N, K, _ptr(wp), _ptr(alpha), _ptr(ws), ws.numel(), _stream())
+    op = OP_QUANTIZE_WEIGHTS_ROTATED if rotate else OP_QUANTIZE_WEIGHTS
+    ws = _workspace(workspace_bytes(op, 0, K, N), w.device)
+    fn = "hbl_quantize_weights_rotated" if rotate else "hbl_quantize_weights"
+    _call(fn, _ptr(w), N, K, _ptr(wp), _ptr(alpha), _ptr(ws), ws.numel(), _stream())
     return wp, alpha
 
 
 def forward(x: torch.Tensor, w_packed: torch.Tensor, w_alpha: torch.Tensor, bits: int,
-            gain: torch.Tensor | None = None, out_dtype=None, workspace=None, out=None) -> torch.Tensor:
-    """Whole H-BitLinear forward: x [M][K] (fp32/bf16) -> y [M][N]."""
+            gain: torch.Tensor | None = None, out_dtype=None, workspace=None, out=None,
+            rotate: bool = True) -> torch.Tensor:
+    """Whole H-BitLinear forward: x [M][K] (fp32/bf16) -> y [M][N].
+    rotate=False runs BitLinear without the Hadamard transform."""
     _dev(x, "x")
     M, K = x.shape
     N = w_packed.shape[0]
@@ -127,9 +136,13 @@ def forward(x: torch.Tensor, w_packed: torch.Tensor, w_alpha: torch.Tensor, bits
     y = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
     op = OP_FORWARD_INT8 if bits == 8 else OP_FORWARD_INT4
     ws = _workspace(workspace_bytes(op, M, K, N), x.device, workspace)
-    fn = "hbl_forward_int8" if bits == 8 else "hbl_forward_int4"
-    _call(fn, _ptr(x), _dtype_code(x.dtype), _ptr(gain), _ptr(w_packed), _ptr(w_alpha), M, K, N,
-          _ptr(y), _dtype_code(out_dtype), _ptr(ws), ws.numel(), _stream())
+    if rotate:
+        fn = "hbl_forward_int8" if bits == 8 else "hbl_forward_int4"
+        _call(fn, _ptr(x), _dtype_code(x.dtype), _ptr(gain), _ptr(w_packed), _ptr(w_alpha), M, K, N,
+              _ptr(y), _dtype_code(out_dtype), _ptr(ws), ws.numel(), _stream())
+    else:
+        _call("hbl_bitlinear_forward", _ptr(x), _dtype_code(x.dtype), _ptr(gain), _ptr(w_packed), _ptr(w_alpha),
+              M, K, N, bits, _ptr(y), _dtype_code(out_dtype), _ptr(ws), ws.numel(), _stream())
     return y
 
 
@@ -150,8 +163,9 @@ def _codes_m(codes, bits: int) -> int:
     return codes.shape[1] if bits == 6 else codes.shape[0]
 
 
-def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, out=None):
-    """Stage 1: x [M][K] -> (codes, per-token scales fp32 [M])."""
+def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, out=None, rotate: bool = True):
+    """Stage 1: x [M][K] -> (codes, per-token scales fp32 [M]); rotate=False
+    leaves the Hadamard transform out."""
     _dev(x, "x")
     M, K = x.shape
     if out is not None:
@@ -160,8 +174,8 @@ def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, o
         codes = torch.empty(codes_shape(bits, M, K), dtype=torch.int8 if bits == 8 else torch.uint8,
                             device=x.device)
         d = torch.empty(M + 4, dtype=torch.float32, device=x.device)[:M]
-    _call("hbl_quantize_act", _ptr(x), _dtype_code(x.dtype), _ptr(gain), M, K, bits, _ptr(codes), _ptr(d),
-          _stream())
+    _call("hbl_quantize_act" if rotate else "hbl_quantize_act_unrotated", _ptr(x), _dtype_code(x.dtype), _ptr(gain),
+          M, K, bits, _ptr(codes), _ptr(d), _stream())
     return codes, d
 
 

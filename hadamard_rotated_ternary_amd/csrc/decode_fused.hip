@@ -29,14 +29,15 @@ namespace hbl {
 
 constexpr int FD_NW = 8, FD_MAXM = 4, FD_DKB = 256;
 
-template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int OUT>
+// ROT = false: BitLinear without the transform (quantiser input x / r).
+template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int OUT, bool ROT>
 __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
     const void* __restrict__ x, const float* __restrict__ gain, const uint8_t* __restrict__ W,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N) {
   using C = PrepCfg<LOGK, LOGE, P2>;
   static_assert(C::T == 64 * FD_NW, "one token per pass of the whole workgroup");
   using P0 = Pass<LOGK, LOGE, 0>;
-  using PL = Pass<LOGK, LOGE, C::NP - 1>;
+  using PL = Pass<LOGK, LOGE, ROT ? C::NP - 1 : 0>;
   constexpr int K = C::K, E = C::E;
   constexpr int NBLK = K / FD_DKB;
   constexpr int MAXB = NBLK / FD_NW;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
 #pragma unroll
       for (int r = 0; r < E; ++r) v[r] *= gv[r];
     }
-    run_passes<LOGK, LOGE, P2, 0>(v, region, tid);
+    if constexpr (ROT) run_passes<LOGK, LOGE, P2, 0>(v, region, tid);
     float st = 0.f;
     if constexpr (BITS == 8) {
 #pragma unroll
@@ -135,8 +136,10 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
       for (int r = 0; r < E; ++r) st += fabsf(v[r]);
     }
     token_reduce2<C::T, BITS == 8>(ss, st, red);
-    // c = 1 / (r * sqrt(K)), r = sqrt(mean x^2 + eps); statistic of xt = v * c
-    const float cc = 1.0f / (sqrtf(ss * (1.0f / K) + kEpsNorm) * sqrtf((float)K));
+    // c = 1 / (r * sqrt(K)) (1 / r without the transform), r = sqrt(mean x^2 + eps);
+    // statistic of xt = v * c
+    const float rr = sqrtf(ss * (1.0f / K) + kEpsNorm);
+    const float cc = ROT ? 1.0f / (rr * sqrtf((float)K)) : 1.0f / rr;
     st = BITS == 8 ? st * cc : (st * (1.0f / K)) * cc;
     const float G = fmaxf(st, kEpsQ);
     const float cs = cc * (Q / G);
@@ -185,11 +188,11 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
 }
 
 // ---------------------------------------------------------------------------
-template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int OUT>
+template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int OUT, bool ROT>
 static hipError_t launch_fd_t(const FusedDecodeArgs& a) {
   using C = PrepCfg<LOGK, LOGE, P2>;
   const size_t lds = (size_t)((C::REGION * 4 + 15) & ~15) + (size_t)a.M * C::K + 64;
-  auto kern = &decode_fused_kernel<LOGK, LOGE, P2, BITS, XBF16, OUT>;
+  auto kern = &decode_fused_kernel<LOGK, LOGE, P2, BITS, XBF16, OUT, ROT>;
   // more than 64 KiB of dynamic LDS needs the per-function limit raised,
   // once per device and instantiation
   static bool attr[64] = {};
@@ -206,9 +209,9 @@ static hipError_t launch_fd_t(const FusedDecodeArgs& a) {
   return hipGetLastError();
 }
 
-template <int LOGK, int LOGE, int P2>
+template <int LOGK, int LOGE, int P2, bool ROT>
 static hipError_t launch_fd_k(const FusedDecodeArgs& a) {
-#define HBL_FD(BITS, BF, OUT) return launch_fd_t<LOGK, LOGE, P2, BITS, BF, OUT>(a)
+#define HBL_FD(BITS, BF, OUT) return launch_fd_t<LOGK, LOGE, P2, BITS, BF, OUT, ROT>(a)
   if (a.bits == 8) {
     if (a.x_bf16) { if (a.out_kind == OUT_BF16) HBL_FD(8, true, OUT_BF16); HBL_FD(8, true, OUT_F32); }
     if (a.out_kind == OUT_BF16) HBL_FD(8, false, OUT_BF16);
@@ -225,8 +228,8 @@ bool decode_fused_supported(int M, int logk) { return M >= 1 && M <= FD_MAXM && 
 hipError_t launch_decode_fused(const FusedDecodeArgs& a) {
   if (!decode_fused_supported(a.M, a.logk)) return hipErrorInvalidValue;
   // T = 512 threads per token: E = K / 512 values per thread
-  if (a.logk == 14) return launch_fd_k<14, 5, 8>(a);
-  return launch_fd_k<13, 4, 6>(a);
+  if (a.logk == 14) return a.rotate ? launch_fd_k<14, 5, 8, true>(a) : launch_fd_k<14, 5, 8, false>(a);
+  return a.rotate ? launch_fd_k<13, 4, 6, true>(a) : launch_fd_k<13, 4, 6, false>(a);
 }
 
 }  // namespace hbl

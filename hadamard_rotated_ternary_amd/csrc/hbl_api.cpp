@@ -62,10 +62,11 @@ size_t scales_bytes(int64_t M) { return align256((size_t)M * 4); }
 
 hbl_status launched(hipError_t e) { return e == hipSuccess ? HBL_OK : HBL_ERR_LAUNCH; }
 
-hbl_status forward(int bits, const void* x, hbl_dtype x_dtype, const float* gain, const uint8_t* w_packed,
-                   const float* w_alpha, int64_t M, int64_t K, int64_t N, void* y, hbl_dtype y_dtype,
-                   void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return HBL_ERR_DTYPE;
+// H-BitLinear forward (rotate) or BitLinear without the transform.
+hbl_status forward(int bits, bool rotate, const void* x, hbl_dtype x_dtype, const float* gain,
+                   const uint8_t* w_packed, const float* w_alpha, int64_t M, int64_t K, int64_t N, void* y,
+                   hbl_dtype y_dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype) || (bits != 8 && bits != 4)) return HBL_ERR_DTYPE;
   if (hbl_status s = check_shape(M, K, N)) return s;
   if (M == 0) return HBL_OK;
   if (!x || !w_packed || !w_alpha || !y || !workspace) return HBL_ERR_NULL;
@@ -81,7 +82,7 @@ hbl_status forward(int bits, const void* x, hbl_dtype x_dtype, const float* gain
     hbl::FusedDecodeArgs f{};
     f.x = x; f.x_bf16 = x_dtype == HBL_BF16; f.gain = gain; f.wpack = w_packed; f.walpha = w_alpha; f.out = y;
     f.out_kind = y_dtype == HBL_BF16 ? hbl::OUT_BF16 : hbl::OUT_F32;
-    f.M = (int)M; f.N = (int)N; f.logk = log2_exact(K); f.bits = bits; f.stream = stream;
+    f.M = (int)M; f.N = (int)N; f.logk = log2_exact(K); f.bits = bits; f.rotate = rotate; f.stream = stream;
     return launched(hbl::launch_decode_fused(f));
   }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -92,8 +93,8 @@ hbl_status forward(int bits, const void* x, hbl_dtype x_dtype, const float* gain
 
   hbl::PrepArgs p{};
   p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
-  p.bits = bits; p.mode = fp6_path(bits, M) ? 2 : 0; p.codes = codes; p.dscale = dscale; p.xt = nullptr;
-  p.stream = stream;
+  p.bits = bits; p.mode = fp6_path(bits, M) ? 2 : 0; p.rotate = rotate; p.codes = codes; p.dscale = dscale;
+  p.xt = nullptr; p.stream = stream;
   if (hipError_t e = hbl::launch_prep(p)) return launched(e);
 
   hbl::GemmArgs g{};
@@ -125,6 +126,7 @@ size_t hbl_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
   if (M < 0 || K <= 0 || N <= 0) return 0;
   switch (op) {
     case HBL_OP_QUANTIZE_WEIGHTS: return align256((size_t)N * 8);
+    case HBL_OP_QUANTIZE_WEIGHTS_ROTATED: return align256((size_t)N * 8) + align256((size_t)N * K * 4);
     case HBL_OP_MATMUL: return align256(hbl::gemm_workspace_bytes(M, K, N));
     case HBL_OP_FORWARD_INT8:
     case HBL_OP_FORWARD_INT4: {
@@ -146,20 +148,38 @@ hbl_status hbl_quantize_weights(const float* w, int64_t N, int64_t K, uint8_t* w
   return launched(hbl::launch_wquant(a));
 }
 
+hbl_status hbl_quantize_weights_rotated(const float* w, int64_t N, int64_t K, uint8_t* w_packed, float* w_alpha,
+                                        void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!w || !w_packed || !w_alpha || !workspace) return HBL_ERR_NULL;
+  if (hbl_status s = check_shape(0, K, N)) return s;
+  if (!aligned16(w) || !aligned16(w_packed) || !aligned16(w_alpha) || !aligned16(workspace)) return HBL_ERR_ALIGN;
+  if (ws_bytes < hbl_workspace_bytes(HBL_OP_QUANTIZE_WEIGHTS_ROTATED, 0, K, N)) return HBL_ERR_WORKSPACE;
+  int cus = 0;
+  if (hbl_status s = check_device(&cus)) return s;
+  // workspace: [row sums, fp64][rotated rows, fp32 [N][K]]
+  float* wr = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256((size_t)N * 8));
+  hbl::PrepArgs p{};
+  p.x = w; p.x_bf16 = false; p.gain = nullptr; p.M = (int)N; p.cus = cus; p.logk = log2_exact(K);
+  p.bits = 8; p.mode = 3; p.rotate = true; p.xt = wr; p.stream = stream;
+  if (hipError_t e = hbl::launch_prep(p)) return launched(e);
+  hbl::WquantArgs a{wr, (int)N, (int)K, w_packed, w_alpha, static_cast<double*>(workspace), stream};
+  return launched(hbl::launch_wquant(a));
+}
+
 hbl_status hbl_forward_int8(const void* x, hbl_dtype x_dtype, const float* gain, const uint8_t* w_packed,
                             const float* w_alpha, int64_t M, int64_t K, int64_t N, void* y, hbl_dtype y_dtype,
                             void* workspace, size_t ws_bytes, hipStream_t stream) {
-  return forward(8, x, x_dtype, gain, w_packed, w_alpha, M, K, N, y, y_dtype, workspace, ws_bytes, stream);
+  return forward(8, true, x, x_dtype, gain, w_packed, w_alpha, M, K, N, y, y_dtype, workspace, ws_bytes, stream);
 }
 
 hbl_status hbl_forward_int4(const void* x, hbl_dtype x_dtype, const float* gain, const uint8_t* w_packed,
                             const float* w_alpha, int64_t M, int64_t K, int64_t N, void* y, hbl_dtype y_dtype,
                             void* workspace, size_t ws_bytes, hipStream_t stream) {
-  return forward(4, x, x_dtype, gain, w_packed, w_alpha, M, K, N, y, y_dtype, workspace, ws_bytes, stream);
+  return forward(4, true, x, x_dtype, gain, w_packed, w_alpha, M, K, N, y, y_dtype, workspace, ws_bytes, stream);
 }
 
-hbl_status hbl_quantize_act(const void* x, hbl_dtype x_dtype, const float* gain, int64_t M, int64_t K, int bits,
-                            void* codes, float* dscale, hipStream_t stream) {
+static hbl_status quantize_act(bool rotate, const void* x, hbl_dtype x_dtype, const float* gain, int64_t M,
+                               int64_t K, int bits, void* codes, float* dscale, hipStream_t stream) {
   if (!valid_dtype(x_dtype) || (bits != 8 && bits != 4 && bits != HBL_BITS_INT4_FP6)) return HBL_ERR_DTYPE;
   if (hbl_status s = check_shape(M, K, 16)) return s;
   if (M == 0) return HBL_OK;
@@ -169,9 +189,25 @@ hbl_status hbl_quantize_act(const void* x, hbl_dtype x_dtype, const float* gain,
   if (hbl_status s = check_device(&cus)) return s;
   hbl::PrepArgs p{};
   p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
-  p.bits = bits == 8 ? 8 : 4; p.mode = bits == HBL_BITS_INT4_FP6 ? 2 : 0;
+  p.bits = bits == 8 ? 8 : 4; p.mode = bits == HBL_BITS_INT4_FP6 ? 2 : 0; p.rotate = rotate;
   p.codes = static_cast<uint8_t*>(codes); p.dscale = dscale; p.stream = stream;
   return launched(hbl::launch_prep(p));
+}
+
+hbl_status hbl_quantize_act(const void* x, hbl_dtype x_dtype, const float* gain, int64_t M, int64_t K, int bits,
+                            void* codes, float* dscale, hipStream_t stream) {
+  return quantize_act(true, x, x_dtype, gain, M, K, bits, codes, dscale, stream);
+}
+
+hbl_status hbl_quantize_act_unrotated(const void* x, hbl_dtype x_dtype, const float* gain, int64_t M, int64_t K,
+                                      int bits, void* codes, float* dscale, hipStream_t stream) {
+  return quantize_act(false, x, x_dtype, gain, M, K, bits, codes, dscale, stream);
+}
+
+hbl_status hbl_bitlinear_forward(const void* x, hbl_dtype x_dtype, const float* gain, const uint8_t* w_packed,
+                                 const float* w_alpha, int64_t M, int64_t K, int64_t N, int bits, void* y,
+                                 hbl_dtype y_dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return forward(bits, false, x, x_dtype, gain, w_packed, w_alpha, M, K, N, y, y_dtype, workspace, ws_bytes, stream);
 }
 
 hbl_status hbl_rmsnorm_fwht(const void* x, hbl_dtype x_dtype, const float* gain, int64_t M, int64_t K, float* xt,
@@ -185,7 +221,7 @@ hbl_status hbl_rmsnorm_fwht(const void* x, hbl_dtype x_dtype, const float* gain,
   if (hbl_status s = check_device(&cus)) return s;
   hbl::PrepArgs p{};
   p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
-  p.bits = 8; p.mode = 1; p.xt = xt; p.stream = stream;
+  p.bits = 8; p.mode = 1; p.rotate = true; p.xt = xt; p.stream = stream;
   return launched(hbl::launch_prep(p));
 }
 

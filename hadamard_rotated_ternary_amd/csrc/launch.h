@@ -14,7 +14,9 @@ struct PrepArgs {
   int logk;
   int bits;          // 8 or 4
   int mode;          // 0: codes + scales, 1: rotated activations (fp32),
-                     // 2: INT4 codes in the fp6 operand layout + scales
+                     // 2: INT4 codes in the fp6 operand layout + scales,
+                     // 3: rows rotated without normalisation (fp32, x fp32)
+  bool rotate;       // modes 0 and 2: false leaves the transform out
   uint8_t* codes;
   float* dscale;
   float* xt;
@@ -56,6 +58,7 @@ struct FusedDecodeArgs {
   void* out;
   int out_kind;           // OUT_F32 or OUT_BF16
   int M, N, logk, bits;
+  bool rotate;            // false: BitLinear without the transform
   hipStream_t stream;
 };
 bool decode_fused_supported(int M, int logk);

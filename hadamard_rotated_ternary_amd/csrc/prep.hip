@@ -17,6 +17,12 @@
 namespace hbl {
 
 // MODE 0: write codes + scales.  MODE 1: write the rotated activations (fp32).
+// MODE 3: rotate rows without normalising (the weight rotation of the
+// weight + activation variant, 新智元 article, section 实验效果, table 5):
+// xt = H_K x / sqrt(K), fp32.
+// ROT = false leaves the transform out (BitLinear for the layers whose inputs
+// are already close to Gaussian, 新智元 article, section H-BitLinear模块): the
+// quantiser then sees RMSNorm(x) = x / r in the load's own dealing.
 // MODE 2 (INT4 only): write the codes as the fp6 (e2m3) operand of the
 // fp6 x fp4 matrix instruction, plus the scales.  One 24-byte group per token
 // and 32 consecutive k (k0 = 32c) holds q/2 for the 32 codes as six-bit
@@ -33,13 +39,14 @@ constexpr int prep_wg(int logk, int loge) { return (1 << (logk - loge)) < 64 ? 6
 // Persistent: a workgroup walks tokens blockIdx.x*TPB + tok, then + gridDim.x*TPB,
 // ...; the next token's activations are requested right after the current
 // ones have been unpacked, so their HBM latency hides behind the transform.
-template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int MODE>
+template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int MODE, bool ROT>
 __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
     const void* __restrict__ x, const float* __restrict__ gain, int M,
     uint8_t* __restrict__ codes, float* __restrict__ dscale, float* __restrict__ xt) {
   using C = PrepCfg<LOGK, LOGE, P2>;
+  static_assert(ROT || (MODE == 0 || MODE == 2), "only the quantising modes run without the transform");
   using P0 = Pass<LOGK, LOGE, 0>;
-  using PL = Pass<LOGK, LOGE, C::NP - 1>;
+  using PL = Pass<LOGK, LOGE, ROT ? C::NP - 1 : 0>;
   constexpr int K = C::K, E = C::E, T = C::T;
   __shared__ __attribute__((aligned(16))) float lds[C::REGION * C::TPB];
   __shared__ float red[32];
@@ -122,14 +129,22 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
       }
     }
     // ---- Walsh-Hadamard transform (unnormalised) of x*g
-    run_passes<LOGK, LOGE, P2, 0>(v, region, tau);
+    if constexpr (ROT) run_passes<LOGK, LOGE, P2, 0>(v, region, tau);
 
-    // c = 1 / (r * sqrt(K)), r = sqrt(mean x^2 + eps)
-    auto scale_c = [&](float sst) { return 1.0f / (sqrtf(sst * (1.0f / K) + kEpsNorm) * sqrtf((float)K)); };
-    if constexpr (MODE == 1) {
-      float unused = 0.f;
-      token_reduce2<T, false>(ss, unused, red);
-      const float c = scale_c(ss);
+    // c = 1 / (r * sqrt(K)) (1 / r without the transform), r = sqrt(mean x^2 + eps)
+    auto scale_c = [&](float sst) {
+      const float r = sqrtf(sst * (1.0f / K) + kEpsNorm);
+      return ROT ? 1.0f / (r * sqrtf((float)K)) : 1.0f / r;
+    };
+    if constexpr (MODE == 1 || MODE == 3) {
+      float c;
+      if constexpr (MODE == 3) {
+        c = 1.0f / sqrtf((float)K);
+      } else {
+        float unused = 0.f;
+        token_reduce2<T, false>(ss, unused, red);
+        c = scale_c(ss);
+      }
       if (valid) {
 #pragma unroll
         for (int r = 0; r < E; ++r) xt[(size_t)m * K + baseL + PL::reg_idx(r)] = v[r] * c;
@@ -261,18 +276,23 @@ static hipError_t launch_prep_t(const PrepArgs& a) {
   const int want = (a.M + C::TPB - 1) / C::TPB;
   const int grid = want < a.cus * per_cu ? want : a.cus * per_cu;
   if (grid == 0) return hipSuccess;
-#define HBL_PREP(BITS, BF, MODE)                                                           \
-  hipLaunchKernelGGL((prep_kernel<LOGK, LOGE, P2, BITS, BF, MODE>), dim3(grid), dim3(C::WG), 0, \
+#define HBL_PREP(BITS, BF, MODE, ROT)                                                           \
+  hipLaunchKernelGGL((prep_kernel<LOGK, LOGE, P2, BITS, BF, MODE, ROT>), dim3(grid), dim3(C::WG), 0, \
                      a.stream, a.x, a.gain, a.M, a.codes, a.dscale, a.xt)
+#define HBL_PREP_R(BITS, BF, MODE) \
+  if (a.rotate) HBL_PREP(BITS, BF, MODE, true); else HBL_PREP(BITS, BF, MODE, false)
   if (a.mode == 1) {
-    if (a.x_bf16) HBL_PREP(8, true, 1); else HBL_PREP(8, false, 1);
+    if (a.x_bf16) HBL_PREP(8, true, 1, true); else HBL_PREP(8, false, 1, true);
+  } else if (a.mode == 3) {
+    HBL_PREP(8, false, 3, true);
   } else if (a.mode == 2) {
-    if (a.x_bf16) HBL_PREP(4, true, 2); else HBL_PREP(4, false, 2);
+    if (a.x_bf16) { HBL_PREP_R(4, true, 2); } else { HBL_PREP_R(4, false, 2); }
   } else if (a.bits == 8) {
-    if (a.x_bf16) HBL_PREP(8, true, 0); else HBL_PREP(8, false, 0);
+    if (a.x_bf16) { HBL_PREP_R(8, true, 0); } else { HBL_PREP_R(8, false, 0); }
   } else {
-    if (a.x_bf16) HBL_PREP(4, true, 0); else HBL_PREP(4, false, 0);
+    if (a.x_bf16) { HBL_PREP_R(4, true, 0); } else { HBL_PREP_R(4, false, 0); }
   }
+#undef HBL_PREP_R
 #undef HBL_PREP
   return hipGetLastError();
 }

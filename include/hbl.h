@@ -89,7 +89,8 @@ typedef enum { HBL_F32 = 0, HBL_BF16 = 1 } hbl_dtype;
 enum { HBL_BITS_INT4 = 4, HBL_BITS_INT4_FP6 = 6, HBL_BITS_INT8 = 8 };
 
 /* Operation selector for hbl_workspace_bytes. */
-enum { HBL_OP_QUANTIZE_WEIGHTS = 0, HBL_OP_MATMUL = 1, HBL_OP_FORWARD_INT4 = 4, HBL_OP_FORWARD_INT8 = 8 };
+enum { HBL_OP_QUANTIZE_WEIGHTS = 0, HBL_OP_MATMUL = 1, HBL_OP_QUANTIZE_WEIGHTS_ROTATED = 2,
+       HBL_OP_FORWARD_INT4 = 4, HBL_OP_FORWARD_INT8 = 8 };
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *hbl_status_string(hbl_status s);
@@ -136,6 +137,48 @@ hbl_status hbl_forward_int4(const void *x, hbl_dtype x_dtype, const float *gain,
                             int64_t M, int64_t K, int64_t N,
                             void *y, hbl_dtype y_dtype,
                             void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- variants beside H-BitLinear ---- */
+
+/*
+ * BitLinear forward without the Hadamard rotation, for the layers whose
+ * inputs are already close to Gaussian (attention and FFN input projections;
+ * 新智元 article "微软再放LLM量化大招", section H-BitLinear模块):
+ *     y = dequant( Q_act( RMSNorm(x) ) . W_t^T )
+ * with the same quantisers, weights, formats and conventions as the H-BitLinear
+ * forward.  bits is 8 or 4; the workspace is sized with HBL_OP_FORWARD_INT8 or
+ * HBL_OP_FORWARD_INT4.  K must still be a power of two in [256, 16384].
+ */
+hbl_status hbl_bitlinear_forward(const void *x, hbl_dtype x_dtype, const float *gain,
+                                 const uint8_t *w_packed, const float *w_alpha,
+                                 int64_t M, int64_t K, int64_t N, int bits,
+                                 void *y, hbl_dtype y_dtype,
+                                 void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Stage 1 of that forward: RMSNorm -> per-token quantisation, no rotation.
+ * Arguments and formats as hbl_quantize_act (bits 8, 4 or 6). */
+hbl_status hbl_quantize_act_unrotated(const void *x, hbl_dtype x_dtype, const float *gain,
+                                      int64_t M, int64_t K, int bits,
+                                      void *codes, float *dscale, hipStream_t stream);
+
+/*
+ * Offline ternarisation of weights rotated like the activations (the weight +
+ * activation rotation of 新智元 article, section 实验效果, table 5): each row
+ * w[n] (one output channel over the K inputs) becomes H_K w[n] / sqrt(K), the
+ * same orthonormal Sylvester transform the activations get, so the layer's
+ * inner products are unchanged before quantisation; the rotated rows are then
+ * ternarised exactly as hbl_quantize_weights does (alpha = mean |rotated W|).
+ * Use the result with hbl_forward_int8 / hbl_forward_int4.
+ *   w         fp32 [N][K] latent weights (device, read only)
+ *   w_packed, w_alpha  as hbl_quantize_weights
+ *   workspace at least hbl_workspace_bytes(HBL_OP_QUANTIZE_WEIGHTS_ROTATED, 0, K, N)
+ *             bytes (holds the rotated rows, fp32, and the row sums).
+ * The rotation runs in fp32, so codes can differ from an exact rotation where
+ * |rotated w| / alpha lies within rounding of 0.5.
+ */
+hbl_status hbl_quantize_weights_rotated(const float *w, int64_t N, int64_t K,
+                                        uint8_t *w_packed, float *w_alpha,
+                                        void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ---- the two stages of the forward, exported for stage-wise checking ---- */
 

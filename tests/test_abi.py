@@ -100,6 +100,18 @@ def test_stage_validation(L):
     assert L.hbl_quantize_weights(A, 256, 255, A, A, A, 1 << 20, S) == SHAPE
     assert L.hbl_quantize_weights(A, 256, 256, A, A, A, 8, S) == WORKSPACE
     assert L.hbl_unpack_weights(A, 16, 256, None, S) == NULL
+    # variants: BitLinear without the rotation, weights rotated offline
+    assert L.hbl_bitlinear_forward(A, 1, None, A, A, 8, 256, 256, 5, A2, 1, A, 1 << 40, S) == DTYPE
+    assert L.hbl_bitlinear_forward(A, 1, None, A, A, 8, 255, 256, 8, A2, 1, A, 1 << 40, S) == SHAPE
+    assert L.hbl_bitlinear_forward(None, 1, None, A, A, 8, 256, 256, 4, A2, 1, A, 1 << 40, S) == NULL
+    assert L.hbl_bitlinear_forward(A, 1, None, A, A, 0, 256, 256, 4, None, 1, None, 0, S) == OK
+    assert L.hbl_quantize_act_unrotated(A, 1, None, 0, 256, 6, A, A2, S) == OK
+    assert L.hbl_quantize_act_unrotated(A, 1, None, 4, 256, 7, A, A2, S) == DTYPE
+    need = L.hbl_workspace_bytes(2, 0, 1024, 64)
+    assert need >= 64 * 1024 * 4 + 64 * 8
+    assert L.hbl_quantize_weights_rotated(A, 64, 1024, A, A, A, need - 1, S) == WORKSPACE
+    assert L.hbl_quantize_weights_rotated(A, 64, 1000, A, A, A, need, S) == SHAPE
+    assert L.hbl_quantize_weights_rotated(BAD, 64, 1024, A, A, A, need, S) == ALIGN
 
 
 def test_layout_codecs_hand_examples():

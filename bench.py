@@ -97,6 +97,15 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     wq_ms = e0.elapsed_time(e1) / 3
+    # the weight + activation rotation variant: rows rotated, then ternarised
+    hbl.quantize_weights(wd, rotate=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        hbl.quantize_weights(wd, rotate=True)
+    e1.record()
+    torch.cuda.synchronize()
+    wq_rot_ms = e0.elapsed_time(e1) / 3
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -143,6 +152,7 @@ def main():
             "forward_entry_ms": res["forward_ms"],
         },
         "weight_ternarise_ms": wq_ms,
+        "weight_rotate_ternarise_ms": wq_rot_ms,
     }
     if not args.no_extras:
         out["extras"] = extras(torch, hbl, synthetic, args)
@@ -151,7 +161,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup):
+def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup, rotate=True):
     """Time `steps` forwards; events between the two kernels give per-kernel times.
     The two stage calls launch the same kernels as the single-call forward (the
     INT4 forward of more than 64 tokens keeps its codes in the fp6 operand
@@ -166,7 +176,7 @@ def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup):
 
     def step(evs=None):
         if evs: evs[0].record()
-        hbl.quantize_act(xd, sb, out=(codes, d))
+        hbl.quantize_act(xd, sb, out=(codes, d), rotate=rotate)
         if evs: evs[1].record()
         hbl.matmul_dequant(codes, sb, d, wp, a, K, workspace=ws, out=y)
         if evs: evs[2].record()
@@ -184,12 +194,12 @@ def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup):
     gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     # the public single-call entry point, same kernels
     for _ in range(max(2, warmup // 2)):
-        hbl.forward(xd, wp, a, bits, workspace=wsf, out=y)
+        hbl.forward(xd, wp, a, bits, workspace=wsf, out=y, rotate=rotate)
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     f0.record()
     for _ in range(steps):
-        hbl.forward(xd, wp, a, bits, workspace=wsf, out=y)
+        hbl.forward(xd, wp, a, bits, workspace=wsf, out=y, rotate=rotate)
     f1.record()
     torch.cuda.synchronize()
     return {"ms_per_step": (t1 - t0) * 1e3 / steps, "prep_ms": prep, "gemm_ms": gemm,
@@ -224,6 +234,18 @@ def extras(torch, hbl, synthetic, args):
                             "prep_ms": r["prep_ms"], "gemm_ms": r["gemm_ms"],
                             "gemm_tops": ops / (r["gemm_ms"] / 1e3) / 1e12,
                             "gemm_mfma_frac": ops / (r["gemm_ms"] / 1e3) / 1e12 / PEAK_INT8_TOPS}
+    del xd, wp
+    # BitLinear without the rotation on a 7B-scale FFN input projection
+    wu = synthetic.WORKLOADS["up_7b_bitlinear_int4"]
+    x, xb, wl = synthetic.make_inputs(wu)
+    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    wp, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
+    r = time_layer(torch, hbl, xd, wp, a, wu.M, wu.K, wu.N, 4, max(10, args.steps // 2), 5, rotate=False)
+    ops = 2.0 * wu.M * wu.N * wu.K
+    out[wu.name] = {"tokens_per_s": wu.M / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
+                    "prep_ms": r["prep_ms"], "gemm_ms": r["gemm_ms"], "M": wu.M, "K": wu.K, "N": wu.N,
+                    "gemm_tflops": ops / (r["gemm_ms"] / 1e3) / 1e12,
+                    "gemm_frac_fp6": ops / (r["gemm_ms"] / 1e3) / 1e12 / PEAK_FP6_TFLOPS}
     del xd, wp
     # decode shapes: weights rotated over enough copies to defeat the 256 MB
     # Infinity Cache; calls replayed from a captured graph so the timing is

@@ -211,6 +211,14 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
   // ---- epilogue: 32x32 accumulator layout, lane l / register r hold
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
+  if constexpr (OUT == OUT_BF16) {
+    static_assert(NWV * 64 * (CB * 64 + 32) <= 3 * C::STAGE, "staging fits the ring");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");   // every wave is done with the ring
+    store_bf16_staged<CB>(smem + wave * (64 * (CB * 64 + 32)), static_cast<uint16_t*>(Y), dscale, aw, M, N,
+                          m0 + wm * 128, n0 + wn * (32 * CB), lane,
+                          [&](int rb, int cb, int r) { return (float)unscale<BITS>(acc[rb][cb][r]); });
+    return;
+  }
 #pragma unroll
   for (int rbk = 0; rbk < 4; ++rbk) {
 #pragma unroll
@@ -484,40 +492,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   // integers below 2^24.
   const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
   if constexpr (OUT == OUT_BF16) {
-    // bf16 output through LDS: each wave rounds its 128x128 block into its
-    // own LDS rows (64 at a time, rows of 288 bytes so the two rows a store
-    // instruction touches fall on different banks), then writes 16 bytes per
-    // lane, whole 256-byte row segments, instead of 2-byte scattered stores.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");   // every wave is done with the ring
-    constexpr int ER = 288;                                   // bytes per staged row
-    uint8_t* stage = smem + wave * (64 * ER);
-    const int mrow0 = m0 + wm * 128, ncol0 = n0 + wn * 128;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int rh = 0; rh < 2; ++rh) {
-        const int rb = 2 * hf + rh;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = rh * 32 + 8 * (r >> 2) + 4 * g + (r & 3);      // row within the half
-          const float t = dscale[min(mrow0 + 64 * hf + rl, M - 1)] * aw;
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            *reinterpret_cast<uint16_t*>(stage + rl * ER + (cb * 32 + l32) * 2) =
-                f32_to_bf16(acc[rb][cb][r] * t);
-        }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rl = 4 * i + (lane >> 4), c16 = lane & 15;         // 4 rows x 16 lanes of 16 bytes
-        const int m = mrow0 + 64 * hf + rl, n = ncol0 + 8 * c16;
-        const uint4 v = *reinterpret_cast<const uint4*>(stage + rl * ER + 16 * c16);
-        if (m < M && n < N)                                          // N % 16 == 0: 8-column chunks are whole
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Y) + (size_t)m * N + n) = v;
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // reads done before the next half overwrites
-    }
+    store_bf16_staged<4>(smem + wave * (64 * (4 * 64 + 32)), static_cast<uint16_t*>(Y), dscale, aw, M, N,
+                         m0 + wm * 128, n0 + wn * 128, lane,
+                         [&](int rb, int cb, int r) { return acc[rb][cb][r]; });
   } else {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {

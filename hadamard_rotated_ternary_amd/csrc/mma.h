@@ -62,4 +62,46 @@ HBL_DEV void store_out(void* Y, size_t off, int acc, float t) {
   }
 }
 
+// bf16 output of a wave's 128 x (32*CB) accumulator block through LDS: the
+// block is rounded into the wave's own LDS rows, 64 rows at a time, then
+// written with 16-byte stores as whole row segments (instead of 2-byte
+// stores scattered over 64 rows).  getv(rb, cb, r) returns the unscaled
+// accumulator of 32x32 block (rb, cb), register r; lane l / register r hold
+// row 8*(r/4) + 4*(l/32) + r%4, column l%32.  Staged rows are CB*64 + 32
+// bytes, so the two rows one store instruction touches start 32 banks apart.
+// The caller makes sure no other wave still uses the stage area.  N % 16 == 0,
+// so 8-column chunks are either whole or outside.
+template <int CB, typename GetV>
+HBL_DEV void store_bf16_staged(uint8_t* stage, uint16_t* Y, const float* __restrict__ dscale, float aw, int M,
+                               int N, int mrow0, int ncol0, int lane, GetV getv) {
+  constexpr int ER = CB * 64 + 32;             // staged row bytes
+  constexpr int LPR = CB * 4;                  // lanes per row on the way out (16 bytes each)
+  constexpr int RPI = 64 / LPR;                // rows per store instruction
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh) {
+      const int rb = 2 * hf + rh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = rh * 32 + 8 * (r >> 2) + 4 * g + (r & 3);     // row within the half
+        const float t = dscale[min(mrow0 + 64 * hf + rl, M - 1)] * aw;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          *reinterpret_cast<uint16_t*>(stage + rl * ER + (cb * 32 + l32) * 2) = f32_to_bf16(getv(rb, cb, r) * t);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+#pragma unroll
+    for (int i = 0; i < 64 / RPI; ++i) {
+      const int rl = RPI * i + lane / LPR, c16 = lane % LPR;
+      const int m = mrow0 + 64 * hf + rl, n = ncol0 + 8 * c16;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + rl * ER + 16 * c16);
+      if (m < M && n < N) *reinterpret_cast<uint4*>(Y + (size_t)m * N + n) = v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");       // reads done before the next half overwrites
+  }
+}
+
 }  // namespace hbl

@@ -53,6 +53,9 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_7b_m1": Workload("decode_7b_m1", 1, 16384, 4096, 4, "bf16", "laplace", 0.05, 82, 100.0, 4),
     "decode_7b_m16": Workload("decode_7b_m16", 16, 16384, 4096, 4, "bf16", "laplace", 0.05, 82, 100.0, 4),
     "decode_7b_m64": Workload("decode_7b_m64", 64, 16384, 4096, 4, "bf16", "laplace", 0.05, 82, 100.0, 4),
+    # input projection of a 7B-scale FFN (up/gate, N = 11008): Gaussian-like
+    # inputs without outlier channels, BitLinear without the rotation
+    "up_7b_bitlinear_int4": Workload("up_7b_bitlinear_int4", 8192, 4096, 11008, 4, "bf16", "normal", 1.0, 0, 1.0, 5),
 }
 
 

@@ -50,6 +50,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_forward.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, I, P, P, P, P, P, P, I]
         L.oracle_forward_ex.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, I, I, P, P, P, P, P, P, I]
         L.oracle_quantize_weights_rotated.argtypes = [P, I64, I64, P, P, P]
+        L.oracle_quant_heads.argtypes = [P, I64, I64, I, P, P, P]
+        L.oracle_dequant_heads.argtypes = [P, P, I64, I64, I, P]
+        L.oracle_attention_decode.argtypes = [P, I, P, P, P, P, I, P, I64, I64, I64, I64, I64, P]
         _lib = L
     return _lib
 
@@ -182,6 +185,49 @@ def quantize_weights_rotated(w: np.ndarray):
     _chk(lib().oracle_quantize_weights_rotated(_p(w), N, K, _p(wt), _p(alpha), _p(wr)),
          "quantize_weights_rotated")
     return wt, np.float32(alpha[0]), wr
+
+
+def quant_heads(x: np.ndarray, bits: int):
+    """Per-head absmax quantisation of post-RoPE attention states to unsigned
+    b-bit codes.  x [R][d] (one row per token and head) -> (codes uint8 [R][d],
+    scale double [R], pre double [R][d])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, d = x.shape
+    codes = np.empty((R, d), dtype=np.uint8)
+    scale = np.empty(R)
+    pre = np.empty((R, d))
+    _chk(lib().oracle_quant_heads(_p(x), R, d, bits, _p(codes), _p(scale), _p(pre)), "quant_heads")
+    return codes, scale, pre
+
+
+def dequant_heads(codes: np.ndarray, scale: np.ndarray, bits: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.float64)
+    R, d = codes.shape
+    y = np.empty((R, d))
+    _chk(lib().oracle_dequant_heads(_p(codes), _p(scale), R, d, bits, _p(y)), "dequant_heads")
+    return y
+
+
+def attention_decode(q, qbits, kc, ks, vc, vs, kvbits, lens):
+    """One decode step of attention over a quantised KV cache.
+
+    q [B][Hq][d] (post-RoPE, quantised inside with ``qbits``); kc, vc
+    [B][Hkv][Tmax][d] unpacked codes; ks, vs [B][Hkv][Tmax] fp32 scales;
+    lens [B] context lengths.  Returns out [B][Hq][d] double."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    kc = np.ascontiguousarray(kc, dtype=np.uint8)
+    vc = np.ascontiguousarray(vc, dtype=np.uint8)
+    ks = np.ascontiguousarray(ks, dtype=np.float32)
+    vs = np.ascontiguousarray(vs, dtype=np.float32)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    B, Hq, d = q.shape
+    _, Hkv, Tmax, d2 = kc.shape
+    assert d2 == d and vc.shape == kc.shape and ks.shape == (B, Hkv, Tmax) and vs.shape == ks.shape
+    out = np.empty((B, Hq, d))
+    _chk(lib().oracle_attention_decode(_p(q), qbits, _p(kc), _p(ks), _p(vc), _p(vs), kvbits, _p(lens),
+                                       B, Hq, Hkv, d, Tmax, _p(out)), "attention_decode")
+    return out
 
 
 def to_bf16_rne(y: np.ndarray) -> np.ndarray:

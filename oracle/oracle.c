@@ -20,6 +20,9 @@
  *       close to Gaussian (attention/FFN input projections) [XZY §H-BitLinear模块];
  *     weights rotated offline as well (weight + activation rotation, the
  *       ablation of [XZY §实验效果], table 5).
+ *   Low-bit attention states [XZY §实验效果], [QbitAI]: post-RoPE Q/K/V heads
+ *     quantised per head by absmax to unsigned integers (3-bit KV cache), and
+ *     one decode step of attention over that cache.
  *
  * Precision: every floating-point step is done in double; values are rounded
  * only where the method itself produces a stored low-precision quantity
@@ -311,6 +314,109 @@ int oracle_quantize_weights_rotated(const float *w, int64_t N, int64_t K, int8_t
     if (wr_out) memcpy(wr_out, wr, (size_t)N * K * sizeof(double));
     free(wr); free(row);
     return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Low-bit attention states [XZY §实验效果] (the QKV states are quantised after
+ * RoPE; every head is mapped straight to unsigned integers by an absmax
+ * function, with no calibration data; tables 2 and 3 vary the bit width, and
+ * a 3-bit KV cache matches the full-precision one).  Reading: per head (one
+ * token, one head: a row of d values), with b bits,
+ *   Qb = 2^(b-1) - 1,  Z = 2^(b-1),
+ *   G  = max(max_e |v_e|, EPS_Q),   s = G / Qb,
+ *   u_e = clamp(round(v_e * Qb / G) + Z, 0, 2^b - 1)   (round half to even),
+ *   v^_e = (u_e - Z) * s.
+ * RoPE itself is applied upstream (the input rows are post-RoPE).
+ * x [R][d] fp32 (R = tokens * heads); codes [R][d] one code per byte;
+ * scale [R] double; pre [R][d] optional (v * Qb / G before rounding).
+ * ------------------------------------------------------------------------- */
+int oracle_quant_heads(const float *x, int64_t R, int64_t d, int bits, uint8_t *codes, double *scale,
+                       double *pre)
+{
+    if (!x || !codes || !scale || R < 0 || d <= 0 || bits < 2 || bits > 8) return -1;
+    const double Qb = (double)((1 << (bits - 1)) - 1), Z = (double)(1 << (bits - 1));
+    const double hi = (double)((1 << bits) - 1);
+    for (int64_t r = 0; r < R; ++r) {
+        const float *v = x + r * d;
+        double G = 0.0;
+        for (int64_t e = 0; e < d; ++e) if (fabs((double)v[e]) > G) G = fabs((double)v[e]);
+        if (G < EPS_Q) G = EPS_Q;
+        for (int64_t e = 0; e < d; ++e) {
+            double p = (double)v[e] * Qb / G;
+            if (pre) pre[r * d + e] = p;
+            codes[r * d + e] = (uint8_t)clampd(rne(p) + Z, 0.0, hi);
+        }
+        scale[r] = G / Qb;
+    }
+    return 0;
+}
+
+/* v^ = (u - Z) * s for every code of every head. */
+int oracle_dequant_heads(const uint8_t *codes, const double *scale, int64_t R, int64_t d, int bits, double *y)
+{
+    if (!codes || !scale || !y || R < 0 || d <= 0 || bits < 2 || bits > 8) return -1;
+    const double Z = (double)(1 << (bits - 1));
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t e = 0; e < d; ++e) y[r * d + e] = ((double)codes[r * d + e] - Z) * scale[r];
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * One decode step of attention over a quantised KV cache.  The method only
+ * fixes the states' quantisation; attention itself is the standard scaled
+ * dot product with softmax:
+ *   q^   = dequant(quant(q, qbits))                     (per head, as above)
+ *   k^_t = (uk_t - Z) * sk_t,   v^_t = (uv_t - Z) * sv_t  (Z = 2^(kvbits-1))
+ *   l_t  = (q^ . k^_t) / sqrt(d),   p_t = exp(l_t - max l) / sum exp(...)
+ *   out  = sum_t p_t v^_t,   t = 0 .. len_b - 1;  len_b = 0 gives out = 0.
+ * Grouped heads: query head h reads KV head h / (Hq / Hkv).
+ * q [B][Hq][d] fp32 (post-RoPE); kc, vc [B][Hkv][Tmax][d] one code per byte;
+ * ks, vs [B][Hkv][Tmax] fp32 (the stored per-row scales); lens [B];
+ * out [B][Hq][d] double.
+ * ------------------------------------------------------------------------- */
+int oracle_attention_decode(const float *q, int qbits, const uint8_t *kc, const float *ks, const uint8_t *vc,
+                            const float *vs, int kvbits, const int32_t *lens, int64_t B, int64_t Hq,
+                            int64_t Hkv, int64_t d, int64_t Tmax, double *out)
+{
+    if (!q || !kc || !ks || !vc || !vs || !lens || !out || B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 ||
+        Tmax < 0 || Hq % Hkv || kvbits < 2 || kvbits > 8 || qbits < 2 || qbits > 8)
+        return -1;
+    for (int64_t b = 0; b < B; ++b)
+        if (lens[b] < 0 || lens[b] > Tmax) return -2;
+    const double Zkv = (double)(1 << (kvbits - 1));
+    const int64_t group = Hq / Hkv;
+    int rc = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : rc)
+    for (int64_t bh = 0; bh < B * Hq; ++bh) {
+        const int64_t b = bh / Hq, h = bh % Hq, hk = h / group;
+        const int64_t len = lens[b];
+        double *o = out + bh * d;
+        uint8_t *uq = malloc((size_t)d);
+        double *qh = malloc(sizeof(double) * (size_t)d);
+        double *lg = malloc(sizeof(double) * (size_t)(len > 0 ? len : 1));
+        double sq = 0.0;
+        if (!uq || !qh || !lg || oracle_quant_heads(q + bh * d, 1, d, qbits, uq, &sq, NULL) != 0) {
+            rc |= 1;
+        } else {
+            oracle_dequant_heads(uq, &sq, 1, d, qbits, qh);
+            const uint8_t *K = kc + (b * Hkv + hk) * Tmax * d, *V = vc + (b * Hkv + hk) * Tmax * d;
+            const float *KS = ks + (b * Hkv + hk) * Tmax, *VS = vs + (b * Hkv + hk) * Tmax;
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < len; ++t) {
+                double dot = 0.0;
+                for (int64_t e = 0; e < d; ++e) dot += qh[e] * (((double)K[t * d + e] - Zkv) * (double)KS[t]);
+                lg[t] = dot / sqrt((double)d);
+                if (lg[t] > mx) mx = lg[t];
+            }
+            double den = 0.0;
+            for (int64_t t = 0; t < len; ++t) { lg[t] = exp(lg[t] - mx); den += lg[t]; }
+            for (int64_t e = 0; e < d; ++e) o[e] = 0.0;
+            for (int64_t t = 0; t < len; ++t)
+                for (int64_t e = 0; e < d; ++e) o[e] += lg[t] / den * (((double)V[t * d + e] - Zkv) * (double)VS[t]);
+        }
+        free(uq); free(qh); free(lg);
+    }
+    return rc ? -3 : 0;
 }
 
 int oracle_max_threads(void)

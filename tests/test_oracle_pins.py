@@ -403,3 +403,186 @@ def test_rotated_weights_one_hot_and_involution():
     _, _, wr = oracle.quantize_weights_rotated(w)
     back = np.stack([oracle.hadamard_rotate(r) for r in wr])
     np.testing.assert_allclose(back, w, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------ low-bit attention states
+# Per-head absmax quantisation of post-RoPE Q/K/V to unsigned b-bit codes and
+# one decode step of attention over such a cache (新智元 article, section
+# 实验效果; 量子位 article on the 3-bit KV cache).
+
+def test_heads_3bit_hand_golden():
+    g = read_golden("heads_3bit_hand.txt")
+    x = np.array([g["x"]], dtype=np.float32)
+    codes, scale, _ = oracle.quant_heads(x, 3)
+    assert codes[0].tolist() == [int(c) for c in g["codes"]]
+    assert scale[0] == g["scale"][0]
+
+
+def _nearest_code_fraction(v, G, bits):
+    """Brute force with exact rationals: the unsigned code whose level
+    (u - Z) * G / Qb is nearest to v, ties to the even signed value."""
+    from fractions import Fraction
+    Qb, Z = 2 ** (bits - 1) - 1, 2 ** (bits - 1)
+    best = None
+    for u in range(2 ** bits):
+        dist = abs(Fraction(v) - Fraction(u - Z) * Fraction(G) / Qb)
+        key = (dist, (u - Z) % 2)
+        if best is None or key < best[0]:
+            best = (key, u)
+    return best[1]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_heads_brute_force_rationals(bits):
+    rng = np.random.default_rng(100 + bits)
+    # bf16-valued inputs with exact ties planted: multiples of G / (2 Qb)
+    Qb = 2 ** (bits - 1) - 1
+    x = rng.normal(size=(6, 16)).astype(np.float32)
+    x = (x.view(np.uint32) & 0xFFFF0000).view(np.float32)
+    x[0, :] = np.arange(-8, 8, dtype=np.float32) * 0.25     # ties for small Qb
+    x[1, 0] = 4.0
+    x[1, 1:] = (np.arange(15) - 7) * (4.0 / (2 * Qb))
+    codes, scale, _ = oracle.quant_heads(x, bits)
+    for r in range(x.shape[0]):
+        G = float(np.max(np.abs(x[r].astype(np.float64))))
+        assert scale[r] == G / Qb
+        for e in range(x.shape[1]):
+            assert codes[r, e] == _nearest_code_fraction(float(x[r, e]), G, bits), (r, e)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_heads_closed_forms_and_invariants(bits):
+    Qb, Z = 2 ** (bits - 1) - 1, 2 ** (bits - 1)
+    # constant-magnitude row +-c: codes Z +- Qb, scale c / Qb
+    c = 0.375
+    x = np.array([[c, -c, c, c, -c, -c, c, -c]], dtype=np.float32)
+    codes, scale, _ = oracle.quant_heads(x, bits)
+    assert codes[0].tolist() == [Z + Qb if v > 0 else Z - Qb for v in x[0]]
+    assert scale[0] == c / Qb
+    # zero row: the floor on the statistic keeps the scale finite, all codes Z
+    codes, scale, _ = oracle.quant_heads(np.zeros((1, 8), np.float32), bits)
+    assert codes[0].tolist() == [Z] * 8 and scale[0] == 1e-5 / Qb
+    # random rows: codes within [Z - Qb, Z + Qb] (code 0 unused for b>=2),
+    # the absmax element at an end, reconstruction error at most half a step
+    rng = np.random.default_rng(bits)
+    x = rng.standard_t(3, size=(40, 64)).astype(np.float32)
+    codes, scale, _ = oracle.quant_heads(x, bits)
+    assert codes.min() >= Z - Qb and codes.max() <= Z + Qb
+    am = np.argmax(np.abs(x), axis=1)
+    ends = codes[np.arange(40), am].astype(int) - Z
+    assert np.array_equal(np.abs(ends), np.full(40, Qb))
+    y = oracle.dequant_heads(codes, scale, bits)
+    assert np.all(np.abs(y - x) <= scale[:, None] / 2 * (1 + 1e-12))
+    # values on the grid come back exactly
+    grid = ((codes.astype(np.float64) - Z) * scale[:, None]).astype(np.float32)
+    c2, s2, _ = oracle.quant_heads(grid, bits)
+    assert np.array_equal(c2, codes)
+
+
+def _cache(rng, B, Hkv, T, d, bits):
+    Qb, Z = 2 ** (bits - 1) - 1, 2 ** (bits - 1)
+    kc = rng.integers(Z - Qb, Z + Qb + 1, size=(B, Hkv, T, d)).astype(np.uint8)
+    vc = rng.integers(Z - Qb, Z + Qb + 1, size=(B, Hkv, T, d)).astype(np.uint8)
+    ks = rng.uniform(0.05, 0.5, size=(B, Hkv, T)).astype(np.float32)
+    vs = rng.uniform(0.05, 0.5, size=(B, Hkv, T)).astype(np.float32)
+    return kc, ks, vc, vs
+
+
+def test_attention_single_token_and_uniform_keys():
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, T, d, bits = 2, 4, 2, 5, 16, 3
+    Z = 4
+    kc, ks, vc, vs = _cache(rng, B, Hkv, T, d, bits)
+    q = rng.normal(size=(B, Hq, d)).astype(np.float32)
+    vh = (vc.astype(np.float64) - Z) * vs[..., None]
+    # one cached token: the output is that token's value row
+    out = oracle.attention_decode(q, 8, kc, ks, vc, vs, bits, np.array([1, 1]))
+    for b in range(B):
+        for h in range(Hq):
+            np.testing.assert_allclose(out[b, h], vh[b, h // 2, 0], rtol=0, atol=1e-15)
+    # identical keys: uniform weights, the output is the mean of the values
+    kc2 = np.repeat(kc[:, :, :1], T, axis=2)
+    ks2 = np.repeat(ks[:, :, :1], T, axis=2)
+    out = oracle.attention_decode(q, 8, kc2, ks2, vc, vs, bits, np.array([T, 3]))
+    for h in range(Hq):
+        np.testing.assert_allclose(out[0, h], vh[0, h // 2].mean(axis=0), rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(out[1, h], vh[1, h // 2, :3].mean(axis=0), rtol=1e-13, atol=1e-15)
+    # empty context: zeros
+    out = oracle.attention_decode(q, 8, kc, ks, vc, vs, bits, np.array([0, 2]))
+    assert np.all(out[0] == 0.0)
+
+
+def test_attention_two_token_closed_form():
+    # d = 4, q = (G, 0, 0, 0): on the grid for any qbits, so q^ = q.
+    # Keys: k^_0 = (2 sk0, ...), k^_1 = (-1 sk1, ...); the logits are
+    # G * 2 sk0 / 2 and -G * sk1 / 2 (sqrt(4) = 2), so p_0 = sigmoid(l0 - l1).
+    G, sk0, sk1 = 1.5, 0.25, 0.5
+    Z = 4
+    q = np.array([[[G, 0, 0, 0]]], dtype=np.float32)
+    kc = np.array([[[[Z + 2, Z + 3, Z - 1, Z], [Z - 1, Z + 1, Z, Z - 3]]]], dtype=np.uint8)
+    ks = np.array([[[sk0, sk1]]], dtype=np.float32)
+    vc = np.array([[[[Z + 1, Z - 2, Z + 3, Z], [Z - 3, Z, Z + 1, Z + 2]]]], dtype=np.uint8)
+    vs = np.array([[[0.125, 0.75]]], dtype=np.float32)
+    out = oracle.attention_decode(q, 4, kc, ks, vc, vs, 3, np.array([2]))
+    l0, l1 = G * 2 * sk0 / 2, -G * 1 * sk1 / 2
+    p0 = 1.0 / (1.0 + math.exp(l1 - l0))
+    v0 = np.array([1, -2, 3, 0]) * 0.125
+    v1 = np.array([-3, 0, 1, 2]) * 0.75
+    np.testing.assert_allclose(out[0, 0], p0 * v0 + (1 - p0) * v1, rtol=1e-14, atol=1e-15)
+
+
+def test_attention_invariants():
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, T, d, bits = 2, 6, 2, 9, 32, 3
+    kc, ks, vc, vs = _cache(rng, B, Hkv, T, d, bits)
+    q = rng.normal(size=(B, Hq, d)).astype(np.float32)
+    q[:, 1] = q[:, 0]                     # same group, same query
+    lens = np.array([9, 6])
+    out = oracle.attention_decode(q, 8, kc, ks, vc, vs, bits, lens)
+    assert np.array_equal(out[:, 0], out[:, 1])
+    # permuting the cached tokens does not change the output
+    perm = rng.permutation(T)
+    out_p = oracle.attention_decode(q, 8, kc[:, :, perm], ks[:, :, perm], vc[:, :, perm], vs[:, :, perm],
+                                    bits, np.array([9, 9]))
+    np.testing.assert_allclose(out_p[0], out[0], rtol=1e-12, atol=1e-14)
+    # tokens past the length are ignored
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[1, :, 6:] = 7
+    vc2[1, :, 6:] = 1
+    out2 = oracle.attention_decode(q, 8, kc2, ks, vc2, vs, bits, lens)
+    assert np.array_equal(out2, out)
+    # a convex combination of the values
+    vh = (vc.astype(np.float64) - 4) * vs[..., None]
+    for b in range(B):
+        for h in range(Hq):
+            seg = vh[b, h // 3, :lens[b]]
+            assert np.all(out[b, h] <= seg.max(axis=0) + 1e-12)
+            assert np.all(out[b, h] >= seg.min(axis=0) - 1e-12)
+    # a dominant key (large logit gap) selects its value row
+    kc3 = np.full_like(kc, 4)
+    ks3 = np.ones_like(ks)
+    qd = np.zeros_like(q)
+    qd[:, :, 0] = 1.0
+    kc3[:, :, 2, 0] = 7                    # k^_2 = (3, 0, ...): logit 3 * 1 / sqrt(32)
+    ks3[:, :, 2] = 200.0                   # gap 600 / sqrt(32) ~ 106: exp(-106) ~ 1e-46
+    out3 = oracle.attention_decode(qd, 8, kc3, ks3, vc, vs, bits, np.array([9, 9]))
+    for b in range(B):
+        for h in range(Hq):
+            np.testing.assert_allclose(out3[b, h], vh[b, h // 3, 2], rtol=1e-12, atol=1e-15)
+
+
+def test_attention_quantises_the_query():
+    # a query off the grid gives the same output as its dequantised grid image
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, T, d, bits = 1, 2, 1, 7, 16, 3
+    kc, ks, vc, vs = _cache(rng, B, Hkv, T, d, bits)
+    q = rng.normal(size=(B, Hq, d)).astype(np.float32)
+    for qbits in (3, 4, 8):
+        c, s, _ = oracle.quant_heads(q.reshape(-1, d), qbits)
+        qg = oracle.dequant_heads(c, s, qbits).astype(np.float32).reshape(q.shape)
+        a = oracle.attention_decode(q, qbits, kc, ks, vc, vs, bits, np.array([T]))
+        g = oracle.attention_decode(qg, qbits, kc, ks, vc, vs, bits, np.array([T]))
+        np.testing.assert_allclose(a, g, rtol=1e-12, atol=1e-14)
+        if qbits == 3:
+            full = oracle.attention_decode(q, 8, kc, ks, vc, vs, bits, np.array([T]))
+            assert not np.allclose(a, full, rtol=1e-6)

@@ -323,7 +323,8 @@ int oracle_quantize_weights_rotated(const float *w, int64_t N, int64_t K, int8_t
  * a 3-bit KV cache matches the full-precision one).  Reading: per head (one
  * token, one head: a row of d values), with b bits,
  *   Qb = 2^(b-1) - 1,  Z = 2^(b-1),
- *   G  = max(max_e |v_e|, EPS_Q),   s = G / Qb,
+ *   G  = max(max_e |v_e|, eps),     s = G / Qb,   eps = 1e-5 rounded to fp32
+ *        (the per-head statistic and its stored scale are fp32 numbers),
  *   u_e = clamp(round(v_e * Qb / G) + Z, 0, 2^b - 1)   (round half to even),
  *   v^_e = (u_e - Z) * s.
  * RoPE itself is applied upstream (the input rows are post-RoPE).
@@ -340,7 +341,7 @@ int oracle_quant_heads(const float *x, int64_t R, int64_t d, int bits, uint8_t *
         const float *v = x + r * d;
         double G = 0.0;
         for (int64_t e = 0; e < d; ++e) if (fabs((double)v[e]) > G) G = fabs((double)v[e]);
-        if (G < EPS_Q) G = EPS_Q;
+        if (G < (double)(float)EPS_Q) G = (double)(float)EPS_Q;
         for (int64_t e = 0; e < d; ++e) {
             double p = (double)v[e] * Qb / G;
             if (pre) pre[r * d + e] = p;

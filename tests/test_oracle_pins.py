@@ -442,9 +442,12 @@ def test_heads_brute_force_rationals(bits):
     x[0, :] = np.arange(-8, 8, dtype=np.float32) * 0.25     # ties for small Qb
     x[1, 0] = 4.0
     x[1, 1:] = (np.arange(15) - 7) * (4.0 / (2 * Qb))
+    x[2] = (x[2] * 1e-6).astype(np.float32)                  # below the floor
+    x[2] = (x[2].view(np.uint32) & 0xFFFF0000).view(np.float32)
     codes, scale, _ = oracle.quant_heads(x, bits)
+    floor = float(np.float32(1e-5))
     for r in range(x.shape[0]):
-        G = float(np.max(np.abs(x[r].astype(np.float64))))
+        G = max(float(np.max(np.abs(x[r].astype(np.float64)))), floor)
         assert scale[r] == G / Qb
         for e in range(x.shape[1]):
             assert codes[r, e] == _nearest_code_fraction(float(x[r, e]), G, bits), (r, e)
@@ -461,7 +464,7 @@ def test_heads_closed_forms_and_invariants(bits):
     assert scale[0] == c / Qb
     # zero row: the floor on the statistic keeps the scale finite, all codes Z
     codes, scale, _ = oracle.quant_heads(np.zeros((1, 8), np.float32), bits)
-    assert codes[0].tolist() == [Z] * 8 and scale[0] == 1e-5 / Qb
+    assert codes[0].tolist() == [Z] * 8 and scale[0] == float(np.float32(1e-5)) / Qb
     # random rows: codes within [Z - Qb, Z + Qb] (code 0 unused for b>=2),
     # the absmax element at an end, reconstruction error at most half a step
     rng = np.random.default_rng(bits)

@@ -15,7 +15,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhbl.so")
-HEADER = os.path.join(_HERE, "..", "include", "hbl.h")
+HEADERS = [os.path.join(_HERE, "..", "include", h) for h in ("hbl.h", "hbl_attn.h")]
 
 HBL_F32, HBL_BF16 = 0, 1
 OP_QUANTIZE_WEIGHTS, OP_MATMUL, OP_QUANTIZE_WEIGHTS_ROTATED, OP_FORWARD_INT4, OP_FORWARD_INT8 = 0, 1, 2, 4, 8
@@ -45,13 +45,20 @@ SIGNATURES = {
     "hbl_bitlinear_forward": ([P, I, P, P, P, I64, I64, I64, I, P, I, P, SZ, P], I),
     "hbl_quantize_act_unrotated": ([P, I, P, I64, I64, I, P, P, P], I),
     "hbl_quantize_weights_rotated": ([P, I64, I64, P, P, P, SZ, P], I),
+    "hbl_quantize_heads": ([P, I64, I64, I, P, P, P], I),
+    "hbl_dequantize_heads": ([P, P, I64, I64, I, P, I, P], I),
+    "hbl_kv_cache_append": ([P, P, I64, I64, I64, I64, I, P, I64, P, P, P, P, P], I),
+    "hbl_attention_workspace_bytes": ([I64, I64, I64, I64], SZ),
+    "hbl_attention_decode": ([P, I, P, P, P, P, I, P, I64, I64, I64, I64, I64, P, I, P, SZ, P], I),
 }
 
 
 def declared_symbols() -> list:
-    """Entry points declared in include/hbl.h."""
-    with open(HEADER) as f:
-        src = f.read()
+    """Entry points declared in include/hbl.h and include/hbl_attn.h."""
+    src = ""
+    for h in HEADERS:
+        with open(h) as f:
+            src += f.read()
     return sorted(set(re.findall(r"^\s*(?:hbl_status|size_t|const char \*)\s*\*?\s*(hbl_\w+)\s*\(", src, re.M)))
 
 
@@ -216,3 +223,82 @@ def unpack_weights(w_packed: torch.Tensor, K: int) -> torch.Tensor:
     wt = torch.empty((N, K), dtype=torch.int8, device=w_packed.device)
     _call("hbl_unpack_weights", _ptr(w_packed), N, K, _ptr(wt), _stream())
     return wt
+
+
+# ------------------------------------------------------- low-bit attention states
+
+def heads_row_bytes(bits: int, d: int) -> int:
+    """Bytes of one packed row of d codes of `bits` bits."""
+    return d * bits // 8
+
+
+def quantize_heads(x: torch.Tensor, bits: int):
+    """Per-head absmax codes: x bf16 [..., d] -> (codes uint8 [R][d*bits/8], scale fp32 [R])."""
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    d = x.shape[-1]
+    R = x.numel() // d
+    codes = torch.empty((R, heads_row_bytes(bits, d)), dtype=torch.uint8, device=x.device)
+    scale = torch.empty(R, dtype=torch.float32, device=x.device)
+    _call("hbl_quantize_heads", _ptr(x), R, d, bits, _ptr(codes), _ptr(scale), _stream())
+    return codes, scale
+
+
+def dequantize_heads(codes: torch.Tensor, scale: torch.Tensor, bits: int, d: int, out_dtype=torch.float32):
+    _dev(codes, "codes")
+    _dev(scale, "scale")
+    R = scale.numel()
+    y = torch.empty((R, d), dtype=out_dtype, device=codes.device)
+    _call("hbl_dequantize_heads", _ptr(codes), _ptr(scale), R, d, bits, _ptr(y), _dtype_code(out_dtype),
+          _stream())
+    return y
+
+
+class KVCache:
+    """Quantised KV cache: codes uint8 [B][Hkv][Tmax][d*bits/8], scales fp32 [B][Hkv][Tmax]."""
+
+    def __init__(self, B: int, Hkv: int, Tmax: int, d: int, bits: int, device="cuda"):
+        self.B, self.Hkv, self.Tmax, self.d, self.bits = B, Hkv, Tmax, d, bits
+        rb = heads_row_bytes(bits, d)
+        self.k_codes = torch.zeros((B, Hkv, Tmax, rb), dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros((B, Hkv, Tmax, rb), dtype=torch.uint8, device=device)
+        self.k_scale = torch.zeros((B, Hkv, Tmax), dtype=torch.float32, device=device)
+        self.v_scale = torch.zeros((B, Hkv, Tmax), dtype=torch.float32, device=device)
+
+    def append(self, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor | None = None):
+        """k, v bf16 [B][Tn][Hkv][d]; pos device int32 [B] (None: position 0)."""
+        _dev(k, "k")
+        _dev(v, "v")
+        if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16 or k.shape != v.shape:
+            raise TypeError("k and v must be bfloat16 tensors of one shape")
+        B, Tn, Hkv, d = k.shape
+        if pos is not None:
+            _dev(pos, "pos")
+            if pos.dtype != torch.int32:
+                raise TypeError("pos must be int32")
+        _call("hbl_kv_cache_append", _ptr(k), _ptr(v), B, Tn, Hkv, d, self.bits, _ptr(pos), self.Tmax,
+              _ptr(self.k_codes), _ptr(self.k_scale), _ptr(self.v_codes), _ptr(self.v_scale), _stream())
+
+
+def attention_workspace_bytes(B: int, Hq: int, d: int, Tmax: int) -> int:
+    return int(lib().hbl_attention_workspace_bytes(B, Hq, d, Tmax))
+
+
+def attention_decode(q: torch.Tensor, q_bits: int, k_codes, k_scale, v_codes, v_scale, kv_bits: int,
+                     lens: torch.Tensor, out_dtype=torch.float32, workspace=None, out=None) -> torch.Tensor:
+    """One decode step over a quantised cache: q bf16 [B][Hq][d] -> out [B][Hq][d]."""
+    for t, n in ((q, "q"), (k_codes, "k_codes"), (k_scale, "k_scale"), (v_codes, "v_codes"),
+                 (v_scale, "v_scale"), (lens, "lens")):
+        _dev(t, n)
+    if q.dtype != torch.bfloat16 or lens.dtype != torch.int32:
+        raise TypeError("q must be bfloat16 and lens int32")
+    B, Hq, d = q.shape
+    Hkv, Tmax = k_scale.shape[1], k_scale.shape[2]
+    ws = _workspace(attention_workspace_bytes(B, Hq, d, Tmax), q.device, workspace)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
+    _call("hbl_attention_decode", _ptr(q), q_bits, _ptr(k_codes), _ptr(k_scale), _ptr(v_codes), _ptr(v_scale),
+          kv_bits, _ptr(lens), B, Hq, Hkv, d, Tmax, _ptr(out), _dtype_code(out.dtype), _ptr(ws),
+          ws.numel() * ws.element_size(), _stream())
+    return out

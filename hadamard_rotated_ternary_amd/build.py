@@ -8,8 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhbl.so")
-SOURCES = ["hbl_api.cpp", "prep.hip", "wquant.hip", "gemm.hip", "decode_fused.hip"]
-HEADERS = ["common.h", "launch.h"]
+SOURCES = ["hbl_api.cpp", "prep.hip", "wquant.hip", "gemm.hip", "decode_fused.hip", "attn.hip"]
+HEADERS = ["common.h", "launch.h", "mma.h", "fwht.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -30,7 +30,7 @@ def stale() -> bool:
         return True
     t = os.path.getmtime(LIB)
     deps = sources() + [os.path.join(CSRC, h) for h in HEADERS] + [
-        os.path.join(HERE, "..", "include", "hbl.h")]
+        os.path.join(HERE, "..", "include", "hbl.h"), os.path.join(HERE, "..", "include", "hbl_attn.h")]
     return any(os.path.getmtime(p) > t for p in deps)
 
 

@@ -2,6 +2,7 @@
 // kernel dispatch.  Every check runs before any HIP call, so invalid calls
 // return without touching the device.
 #include "../../include/hbl.h"
+#include "../../include/hbl_attn.h"
 
 #include <hip/hip_runtime.h>
 #include <mutex>
@@ -268,6 +269,95 @@ hbl_status hbl_unpack_weights(const uint8_t* w_packed, int64_t N, int64_t K, int
   if (!aligned16(w_packed) || !aligned16(w_t)) return HBL_ERR_ALIGN;
   if (hbl_status s = check_device()) return s;
   return launched(hbl::launch_unpack(w_packed, (int)N, (int)K, w_t, stream));
+}
+
+
+// ---------------------------------------------------------------------------
+// Low-bit attention states.
+
+static bool heads_d_ok(int64_t d) { return d == 64 || d == 128 || d == 256; }
+static constexpr int64_t kCount = int64_t(1) << 31;
+
+static size_t attn_part_bytes(int64_t B, int64_t Hq, int64_t d, int64_t Tmax) {
+  const int ct = hbl::attn_chunk_tokens((int)d);
+  const int64_t nchunk = (Tmax + ct - 1) / ct;
+  return align256((size_t)B * Hq * nchunk * hbl::attn_part_stride((int)d) * sizeof(float));
+}
+
+hbl_status hbl_quantize_heads(const void* x, int64_t R, int64_t d, int bits, uint8_t* codes, float* scale,
+                              hipStream_t stream) {
+  if (!hbl::heads_bits_supported(bits)) return HBL_ERR_DTYPE;
+  if (!heads_d_ok(d) || R < 0 || R >= kCount || R * d >= (int64_t(1) << 40)) return HBL_ERR_SHAPE;
+  if (R == 0) return HBL_OK;
+  if (!x || !codes || !scale) return HBL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scale)) return HBL_ERR_ALIGN;
+  if (hbl_status s = check_device()) return s;
+  hbl::QuantHeadsArgs a{};
+  a.x0 = x; a.codes0 = codes; a.scale0 = scale; a.B = 1; a.H = 1; a.Tn = R; a.Tmax = R; a.pos = nullptr;
+  a.d = (int)d; a.bits = bits; a.stream = stream;
+  return launched(hbl::launch_quant_heads(a));
+}
+
+hbl_status hbl_dequantize_heads(const uint8_t* codes, const float* scale, int64_t R, int64_t d, int bits, void* y,
+                                hbl_dtype y_dtype, hipStream_t stream) {
+  if (!hbl::heads_bits_supported(bits) || !valid_dtype(y_dtype)) return HBL_ERR_DTYPE;
+  if (!heads_d_ok(d) || R < 0 || R >= kCount || R * d >= (int64_t(1) << 40)) return HBL_ERR_SHAPE;
+  if (R == 0) return HBL_OK;
+  if (!codes || !scale || !y) return HBL_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(scale) || !aligned16(y)) return HBL_ERR_ALIGN;
+  if (hbl_status s = check_device()) return s;
+  return launched(hbl::launch_dequant_heads(codes, scale, R, (int)d, bits, y, y_dtype == HBL_BF16, stream));
+}
+
+hbl_status hbl_kv_cache_append(const void* k, const void* v, int64_t B, int64_t Tn, int64_t Hkv, int64_t d,
+                               int bits, const int32_t* pos, int64_t Tmax, uint8_t* k_codes, float* k_scale,
+                               uint8_t* v_codes, float* v_scale, hipStream_t stream) {
+  if (!hbl::heads_bits_supported(bits)) return HBL_ERR_DTYPE;
+  if (!heads_d_ok(d) || B < 0 || B >= kCount || Tn < 0 || Tn >= kCount || Hkv <= 0 || Hkv >= kCount ||
+      Tmax <= 0 || Tmax >= kCount || B * Hkv * Tn >= kCount || B * Hkv * Tmax > (int64_t(1) << 34))
+    return HBL_ERR_SHAPE;
+  if (B == 0 || Tn == 0) return HBL_OK;
+  if (!k || !v || !k_codes || !k_scale || !v_codes || !v_scale) return HBL_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_codes) || !aligned16(k_scale) || !aligned16(v_codes) ||
+      !aligned16(v_scale) || (pos && !aligned16(pos)))
+    return HBL_ERR_ALIGN;
+  if (hbl_status s = check_device()) return s;
+  hbl::QuantHeadsArgs a{};
+  a.x0 = k; a.x1 = v; a.codes0 = k_codes; a.codes1 = v_codes; a.scale0 = k_scale; a.scale1 = v_scale;
+  a.B = B; a.H = Hkv; a.Tn = Tn; a.Tmax = Tmax; a.pos = pos; a.d = (int)d; a.bits = bits; a.stream = stream;
+  return launched(hbl::launch_quant_heads(a));
+}
+
+size_t hbl_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t d, int64_t Tmax) {
+  if (!heads_d_ok(d) || B <= 0 || Hq <= 0 || Tmax <= 0) return 0;
+  return attn_part_bytes(B, Hq, d, Tmax);
+}
+
+hbl_status hbl_attention_decode(const void* q, int q_bits, const uint8_t* k_codes, const float* k_scale,
+                                const uint8_t* v_codes, const float* v_scale, int kv_bits, const int32_t* lens,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t Tmax, void* out,
+                                hbl_dtype out_dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!hbl::heads_bits_supported(kv_bits) || q_bits < 2 || q_bits > 8 || !valid_dtype(out_dtype))
+    return HBL_ERR_DTYPE;
+  if (!heads_d_ok(d) || B < 0 || B >= kCount || Hkv <= 0 || Hq <= 0 || Hq >= kCount || Hq % Hkv != 0 ||
+      Tmax <= 0 || Tmax >= kCount || B * Hkv * Tmax > (int64_t(1) << 34))
+    return HBL_ERR_SHAPE;
+  const int ct = hbl::attn_chunk_tokens((int)d);
+  const int64_t nchunk = (Tmax + ct - 1) / ct;
+  if (B * Hq * nchunk >= kCount - 8 * Hq) return HBL_ERR_SHAPE;
+  if (B == 0) return HBL_OK;
+  if (!q || !k_codes || !k_scale || !v_codes || !v_scale || !lens || !out || !workspace) return HBL_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(k_scale) || !aligned16(v_codes) || !aligned16(v_scale) ||
+      !aligned16(lens) || !aligned16(out) || !aligned16(workspace))
+    return HBL_ERR_ALIGN;
+  if (ws_bytes < attn_part_bytes(B, Hq, d, Tmax)) return HBL_ERR_WORKSPACE;
+  if (hbl_status s = check_device()) return s;
+  hbl::AttnArgs a{};
+  a.q = q; a.qbits = q_bits; a.kc = k_codes; a.ks = k_scale; a.vc = v_codes; a.vs = v_scale; a.kvbits = kv_bits;
+  a.lens = lens; a.B = (int)B; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.d = (int)d; a.Tmax = Tmax;
+  a.nchunk = (int)nchunk; a.part = static_cast<float*>(workspace); a.out = out;
+  a.out_bf16 = out_dtype == HBL_BF16; a.stream = stream;
+  return launched(hbl::launch_attention_decode(a));
 }
 
 }  // extern "C"

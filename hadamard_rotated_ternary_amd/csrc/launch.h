@@ -75,4 +75,43 @@ struct WquantArgs {
 hipError_t launch_wquant(const WquantArgs& a);
 hipError_t launch_unpack(const uint8_t* wpack, int N, int K, int8_t* wt, hipStream_t stream);
 
+// Low-bit attention states: per-head absmax codes of post-RoPE Q/K/V.
+struct QuantHeadsArgs {
+  const void* x0;         // bf16 [B][Tn][H][d]
+  const void* x1;         // optional second tensor of the same shape (V beside K)
+  uint8_t* codes0;        // packed rows [B][H][Tmax][d*bits/8]
+  uint8_t* codes1;
+  float* scale0;          // [B][H][Tmax]
+  float* scale1;
+  int64_t B, H, Tn, Tmax;
+  const int32_t* pos;     // device [B] first cache position per sequence, or NULL (0)
+  int d, bits;
+  hipStream_t stream;
+};
+hipError_t launch_quant_heads(const QuantHeadsArgs& a);
+hipError_t launch_dequant_heads(const uint8_t* codes, const float* scale, int64_t R, int d, int bits, void* y,
+                                bool y_bf16, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;          // bf16 [B][Hq][d]
+  int qbits;
+  const uint8_t* kc;      // packed [B][Hkv][Tmax][d*kvbits/8]
+  const float* ks;        // [B][Hkv][Tmax]
+  const uint8_t* vc;
+  const float* vs;
+  int kvbits;
+  const int32_t* lens;    // device [B]
+  int B, Hq, Hkv, d;
+  int64_t Tmax;
+  int nchunk;             // ceil(Tmax / attn_chunk_tokens(d))
+  float* part;            // [B][Hq][nchunk][attn_part_stride(d)]
+  void* out;              // [B][Hq][d]
+  bool out_bf16;
+  hipStream_t stream;
+};
+bool heads_bits_supported(int bits);
+int attn_chunk_tokens(int d);
+int attn_part_stride(int d);
+hipError_t launch_attention_decode(const AttnArgs& a);
+
 }  // namespace hbl

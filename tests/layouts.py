@@ -97,3 +97,56 @@ def unpack_int4_fp6(p: np.ndarray, K: int) -> np.ndarray:
     q = np.empty((M, K // 32, 32), np.int8)
     q[:, :, _fp6_field_k()] = vals.astype(np.int8)
     return q.reshape(M, K)
+
+
+# ------------------------------------------------------------- head codes
+# Packed rows of per-head codes, written from the layout description in
+# include/hbl_attn.h: 32-code groups of `bits` little-endian words; code
+# c = 4q + i of a group sits in byte i of a word.
+
+def _head_places(bits):
+    """For each code c of a group: list of (word, shift, value_shift, nbits)."""
+    places = []
+    for c in range(32):
+        q, i = divmod(c, 4)
+        if bits == 8:
+            places.append([(q, 8 * i, 0, 8)])
+        elif bits == 4:
+            places.append([(q // 2, 8 * i + 4 * (q % 2), 0, 4)])
+        elif bits == 2:
+            places.append([(q // 4, 8 * i + 2 * (q % 4), 0, 2)])
+        elif bits == 3:
+            if q < 6:
+                places.append([(q // 2, 8 * i + 3 * (q % 2), 0, 3)])
+            elif q == 6:
+                places.append([(0, 8 * i + 6, 0, 2), (2, 8 * i + 6, 2, 1)])
+            else:
+                places.append([(1, 8 * i + 6, 0, 2), (2, 8 * i + 7, 2, 1)])
+        else:
+            raise ValueError(bits)
+    return places
+
+
+def pack_heads(u, bits):
+    """Codes uint8 [R][d] (each < 2^bits) -> packed uint8 [R][d*bits/8]."""
+    u = np.asarray(u, dtype=np.uint32)
+    R, d = u.shape
+    assert d % 32 == 0 and np.all(u < (1 << bits))
+    g = u.reshape(R, d // 32, 32)
+    words = np.zeros((R, d // 32, bits), dtype=np.uint32)
+    for c, pl in enumerate(_head_places(bits)):
+        for (wd, sh, vs, nb) in pl:
+            words[:, :, wd] |= ((g[:, :, c] >> vs) & ((1 << nb) - 1)) << sh
+    return words.reshape(R, -1).astype("<u4").view(np.uint8).reshape(R, d * bits // 8)
+
+
+def unpack_heads(packed, bits, d):
+    """Inverse of pack_heads."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    R = packed.shape[0]
+    words = packed.reshape(R, -1).view("<u4").reshape(R, d // 32, bits).astype(np.uint32)
+    u = np.zeros((R, d // 32, 32), dtype=np.uint32)
+    for c, pl in enumerate(_head_places(bits)):
+        for (wd, sh, vs, nb) in pl:
+            u[:, :, c] |= ((words[:, :, wd] >> sh) & ((1 << nb) - 1)) << vs
+    return u.reshape(R, d).astype(np.uint8)

@@ -151,3 +151,46 @@ def test_layout_codecs_hand_examples():
     assert p.shape == (2, 5, 96)
     np.testing.assert_array_equal(p[1, 3], pack_int4_fp6(q[3:4, 128:])[0, 0])
     np.testing.assert_array_equal(unpack_int4_fp6(p, 256), q)
+
+
+def test_head_code_layout_hand_examples():
+    from layouts import pack_heads, unpack_heads
+    # 3-bit group, worked by hand from the layout description
+    u = np.zeros((1, 32), np.uint8)
+    u[0, 0] = 3        # quad 0, byte 0: word 0 bits 0..2
+    u[0, 13] = 7       # quad 3 (word 1, upper field), byte 1: word 1 bits 11..13
+    u[0, 25] = 5       # quad 6, byte 1: 0b01 -> word 0 bits 14..15, bit 2 -> word 2 bit 14
+    u[0, 30] = 6       # quad 7, byte 2: 0b10 -> word 1 bits 22..23, bit 2 -> word 2 bit 23
+    w = pack_heads(u, 3).view("<u4")[0]
+    assert w.tolist() == [3 | (1 << 14), (7 << 11) | (1 << 23), (1 << 14) | (1 << 23)]
+    # 2-bit: code 4q + i at word q//4, bits 8i + 2(q%4); 4-bit: word q//2, bits 8i + 4(q%2)
+    u2 = np.zeros((1, 32), np.uint8); u2[0, 4 * 5 + 3] = 2        # q=5, i=3 -> word 1 bit 24+2
+    assert pack_heads(u2, 2).view("<u4")[0].tolist() == [0, 2 << 26]
+    u4 = np.zeros((1, 32), np.uint8); u4[0, 4 * 3 + 1] = 9        # q=3, i=1 -> word 1 bit 8+4
+    assert pack_heads(u4, 4).view("<u4")[0].tolist() == [0, 9 << 12, 0, 0]
+    rng = np.random.default_rng(0)
+    for bits in (2, 3, 4, 8):
+        for d in (64, 128, 256):
+            uu = rng.integers(0, 1 << bits, size=(5, d)).astype(np.uint8)
+            p = pack_heads(uu, bits)
+            assert p.shape == (5, d * bits // 8)
+            assert np.array_equal(unpack_heads(p, bits, d), uu)
+
+
+def test_attention_entry_points_validate_without_device():
+    import ctypes
+    L = hbl.lib()
+    # unsupported widths and head sizes are rejected before any device call
+    assert L.hbl_quantize_heads(None, 4, 128, 5, None, None, None) == 3
+    assert L.hbl_quantize_heads(None, 4, 96, 3, None, None, None) == 2
+    assert L.hbl_quantize_heads(None, 0, 128, 3, None, None, None) == 0
+    assert L.hbl_kv_cache_append(None, None, 1, 1, 2, 128, 3, None, 0, None, None, None, None, None) == 2
+    assert L.hbl_attention_decode(None, 9, None, None, None, None, 3, None, 1, 4, 2, 128, 16, None, 0, None, 0,
+                                  None) == 3
+    assert L.hbl_attention_decode(None, 8, None, None, None, None, 3, None, 1, 3, 2, 128, 16, None, 0, None, 0,
+                                  None) == 2
+    assert L.hbl_attention_decode(None, 8, None, None, None, None, 3, None, 1, 4, 2, 128, 16, None, 0, None, 0,
+                                  None) == 1
+    # partial records: B * Hq * ceil(Tmax / 512 tokens) of (d + 4) floats, rounded up to 256 bytes
+    assert L.hbl_attention_workspace_bytes(2, 8, 128, 1000) == -(-(2 * 8 * 2 * 132 * 4) // 256) * 256
+    assert L.hbl_attention_workspace_bytes(1, 1, 64, 1) == 512   # 68 floats -> 272 bytes

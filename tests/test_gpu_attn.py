@@ -1,0 +1,207 @@
+"""GPU parity of the low-bit attention states (through the C ABI) against the oracle.
+
+Bars:
+  * head codes: bit-exact (the HIP path decides every code exactly);
+  * head scales: bit-exact against the oracle's scale rounded to fp32
+    (G / Qb is correctly rounded on both sides);
+  * dequantised values: bit-exact in fp32 (one rounding of an exact product)
+    and in bf16 (the same fp32 value rounded to nearest even);
+  * decode attention: |out - ref| <= ATTN_TOL * max|v^| per (sequence, head),
+    with the oracle fed the same cache (codes and fp32 scales) and the same
+    bf16 query.  ATTN_TOL: the kernel's key dot products are exact integers;
+    scores carry a few fp32 roundings (relative 2^-22 each, scores below 40 in
+    magnitude here), so each softmax weight is within ~1e-5 relative; the
+    output is a convex combination, so its error is at most twice that times
+    max|v^|, plus fp32 summation over at most a few thousand terms.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hadamard_rotated_ternary_amd as hbl
+import oracle
+from layouts import pack_heads, unpack_heads
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 3e-5
+BITS = (2, 3, 4, 8)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a gfx950 device"
+    assert "gfx950" in torch.cuda.get_device_properties(0).gcnArchName
+    hbl.lib()
+
+
+def bf16_bits(x):
+    """fp32 array -> (bf16 bit patterns uint16, the bf16 values as fp32), round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return r, (r.astype(np.uint32) << 16).view(np.float32)
+
+
+def to_dev_bf16(bits16):
+    return torch.from_numpy(np.ascontiguousarray(bits16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def head_rows(rng, R, d):
+    """bf16 rows with the structure of post-RoPE states: gaussian, a few
+    outlier channels, plus special rows (zero, below the floor, exact ties)."""
+    x = rng.normal(size=(R, d)).astype(np.float32)
+    x[:, rng.integers(0, d, size=3)] *= 8.0
+    x[0] = 0.0
+    x[1] = x[1] * 1e-7
+    x[2] = np.arange(d, dtype=np.float32) - d / 2          # many exact ties for small widths
+    x[3] = np.where(np.arange(d) % 2, 1.0, -1.0)
+    return bf16_bits(x)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_quantize_heads_bit_exact(bits, d):
+    rng = np.random.default_rng(bits * 1000 + d)
+    R = 1031                                                 # ragged against every rows-per-workgroup
+    xb, xf = head_rows(rng, R, d)
+    codes, scale = hbl.quantize_heads(to_dev_bf16(xb), bits)
+    c_or, s_or, _ = oracle.quant_heads(xf, bits)
+    got = unpack_heads(host(codes), bits, d)
+    assert np.array_equal(got, c_or)
+    assert np.array_equal(host(scale), s_or.astype(np.float32))
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("d", [64, 256])
+def test_dequantize_heads_bit_exact(bits, d):
+    rng = np.random.default_rng(7 + bits)
+    R = 300
+    _, xf = head_rows(rng, R, d)
+    c_or, s_or, _ = oracle.quant_heads(xf, bits)
+    s32 = s_or.astype(np.float32)
+    ref = oracle.dequant_heads(c_or, s32.astype(np.float64), bits)     # exact products in double
+    packed = torch.from_numpy(pack_heads(c_or, bits)).cuda()
+    sc = torch.from_numpy(s32).cuda()
+    y32 = host(hbl.dequantize_heads(packed, sc, bits, d, torch.float32))
+    assert np.array_equal(y32, ref.astype(np.float32))
+    yb = hbl.dequantize_heads(packed, sc, bits, d, torch.bfloat16)
+    yb = host(yb.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(yb, bf16_bits(ref.astype(np.float32))[0])
+
+
+def test_kv_cache_append_positions():
+    rng = np.random.default_rng(3)
+    B, Tn, Hkv, d, Tmax, bits = 3, 5, 4, 128, 16, 3
+    kb, kf = bf16_bits(rng.normal(size=(B, Tn, Hkv, d)))
+    vb, vf = bf16_bits(rng.standard_t(4, size=(B, Tn, Hkv, d)))
+    pos = np.array([0, 7, 13], np.int32)                     # the last runs past Tmax: 2 rows skipped
+    cache = hbl.KVCache(B, Hkv, Tmax, d, bits)
+    for t in (cache.k_codes, cache.v_codes):
+        t.fill_(0xAB)
+    cache.k_scale.fill_(-1.0)
+    cache.v_scale.fill_(-1.0)
+    cache.append(to_dev_bf16(kb), to_dev_bf16(vb), torch.from_numpy(pos).cuda())
+    for codes_t, scale_t, xf in ((cache.k_codes, cache.k_scale, kf), (cache.v_codes, cache.v_scale, vf)):
+        codes = host(codes_t)
+        scale = host(scale_t)
+        for b in range(B):
+            for h in range(Hkv):
+                for t in range(Tmax):
+                    src = t - pos[b]
+                    if 0 <= src < Tn:
+                        c_or, s_or, _ = oracle.quant_heads(xf[b, src, h][None], bits)
+                        assert np.array_equal(unpack_heads(codes[b, h, t][None], bits, d), c_or)
+                        assert scale[b, h, t] == np.float32(s_or[0])
+                    else:
+                        assert np.all(codes[b, h, t] == 0xAB) and scale[b, h, t] == -1.0
+
+
+def make_cache(rng, B, Hkv, Tmax, d, bits):
+    """Oracle-quantised cache from bf16 keys/values: (unpacked codes, fp32
+    scales, packed device codes, device scales) for K and V."""
+    out = []
+    for dist in ("normal", "t"):
+        x = rng.normal(size=(B * Hkv * Tmax, d)) if dist == "normal" else rng.standard_t(4, size=(B * Hkv * Tmax, d))
+        x[:, rng.integers(0, d, size=2)] *= 6.0
+        _, xf = bf16_bits(x)
+        c, s, _ = oracle.quant_heads(xf, bits)
+        s32 = s.astype(np.float32)
+        out.append((c.reshape(B, Hkv, Tmax, d), s32.reshape(B, Hkv, Tmax),
+                    torch.from_numpy(pack_heads(c, bits).reshape(B, Hkv, Tmax, -1)).cuda(),
+                    torch.from_numpy(s32.reshape(B, Hkv, Tmax)).cuda()))
+    return out
+
+
+def check_attention(got, ref, vc, vs, bits, Hq, Hkv, lens, tol=ATTN_TOL):
+    Z = 1 << (bits - 1)
+    g = Hq // Hkv
+    for b in range(got.shape[0]):
+        for h in range(Hq):
+            L = min(max(int(lens[b]), 0), vc.shape[2])
+            if L == 0:
+                assert np.all(got[b, h] == 0.0)
+                continue
+            vh = (vc[b, h // g, :L].astype(np.float64) - Z) * vs[b, h // g, :L, None]
+            bound = tol * np.max(np.abs(vh))
+            err = np.max(np.abs(got[b, h] - ref[b, h]))
+            assert err <= bound, (b, h, err, bound)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_attention_decode_matches_oracle(bits, d):
+    rng = np.random.default_rng(bits * 7 + d)
+    B, Hq, Hkv = 4, 4, 2
+    Tmax = {64: 2100, 128: 1100, 256: 600}[d]                # several chunks and a ragged tail
+    (kc, ks, kcd, ksd), (vc, vs, vcd, vsd) = make_cache(rng, B, Hkv, Tmax, d, bits)
+    qb, qf = bf16_bits(rng.normal(size=(B, Hq, d)) * 2.0)
+    lens = np.array([Tmax, 1, Tmax // 2 + 5, 0], np.int32)
+    for qbits in (8, 4, 3):
+        ref = oracle.attention_decode(qf, qbits, kc, ks, vc, vs, bits, lens)
+        got = host(hbl.attention_decode(to_dev_bf16(qb), qbits, kcd, ksd, vcd, vsd, bits,
+                                        torch.from_numpy(lens).cuda()))
+        check_attention(got, ref, vc, vs, bits, Hq, Hkv, lens)
+
+
+def test_attention_decode_bf16_out_and_length_clamps():
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, d, Tmax, bits = 3, 2, 2, 128, 700, 3
+    (kc, ks, kcd, ksd), (vc, vs, vcd, vsd) = make_cache(rng, B, Hkv, Tmax, d, bits)
+    qb, qf = bf16_bits(rng.normal(size=(B, Hq, d)))
+    lens = np.array([10 ** 6, -5, 513], np.int32)            # clamped to Tmax and 0
+    ref = oracle.attention_decode(qf, 8, kc, ks, vc, vs, bits, np.clip(lens, 0, Tmax))
+    out = hbl.attention_decode(to_dev_bf16(qb), 8, kcd, ksd, vcd, vsd, bits, torch.from_numpy(lens).cuda(),
+                               out_dtype=torch.bfloat16)
+    got = host(out.float())
+    check_attention(got, ref, vc, vs, bits, Hq, Hkv, np.clip(lens, 0, Tmax), tol=ATTN_TOL + 2.0 ** -8)
+
+
+def test_attention_decode_full_size_sampled():
+    """The 7B-like decode workload (16 sequences, 32 heads, 4096 cached tokens,
+    head size 128, 3-bit cache) in the benchmark's launch configuration;
+    sampled heads against the oracle."""
+    rng = np.random.default_rng(99)
+    B, H, d, T, bits = 16, 32, 128, 4096, 3
+    rb = d * bits // 8
+    # random valid 3-bit codes and scales (the oracle takes the same cache)
+    Z = 4
+    codes_k = rng.integers(Z - 3, Z + 4, size=(B, H, T, d)).astype(np.uint8)
+    codes_v = rng.integers(Z - 3, Z + 4, size=(B, H, T, d)).astype(np.uint8)
+    ks = rng.uniform(0.02, 0.3, size=(B, H, T)).astype(np.float32)
+    vs = rng.uniform(0.02, 0.3, size=(B, H, T)).astype(np.float32)
+    kcd = torch.from_numpy(pack_heads(codes_k.reshape(-1, d), bits).reshape(B, H, T, rb)).cuda()
+    vcd = torch.from_numpy(pack_heads(codes_v.reshape(-1, d), bits).reshape(B, H, T, rb)).cuda()
+    qb, qf = bf16_bits(rng.normal(size=(B, H, d)) * 3.0)
+    lens = np.full(B, T, np.int32)
+    got = host(hbl.attention_decode(to_dev_bf16(qb), 8, kcd, torch.from_numpy(ks).cuda(), vcd,
+                                    torch.from_numpy(vs).cuda(), bits, torch.from_numpy(lens).cuda()))
+    for (b, h) in [(0, 0), (5, 17), (15, 31), (9, 3)]:
+        ref = oracle.attention_decode(qf[b:b + 1, h:h + 1], 8, codes_k[b:b + 1, h:h + 1], ks[b:b + 1, h:h + 1],
+                                      codes_v[b:b + 1, h:h + 1], vs[b:b + 1, h:h + 1], bits, lens[b:b + 1])
+        check_attention(got[b:b + 1, h:h + 1], ref, codes_v[b:b + 1, h:h + 1], vs[b:b + 1, h:h + 1], bits, 1, 1,
+                        lens[b:b + 1])

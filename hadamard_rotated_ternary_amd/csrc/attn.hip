@@ -113,6 +113,33 @@ HBL_DEV void load_words(const uint32_t* p, uint32_t (&w)[N]) {
   }
 }
 
+// Buffer descriptor word 3 for raw dword loads on gfx9-class devices (data
+// format 32 bits; a zero format would make every access out of range).
+constexpr int kBufferFlags = 0x00020000;
+
+typedef unsigned u3v __attribute__((ext_vector_type(3)));
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// N dwords at byte offset off of a raw buffer (zeros past its size).
+template <int N>
+HBL_DEV void buffer_words(__amdgpu_buffer_rsrc_t rs, int off, uint32_t (&w)[N]) {
+  if constexpr (N == 2) {
+    const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (N == 3) {
+    const u3v v = __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, 0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z;
+  } else {
+    static_assert(N % 4 == 0, "2, 3 or a multiple of 4 dwords");
+#pragma unroll
+    for (int j = 0; j < N; j += 4) {
+      const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4 * j, 0, 0);
+      w[j] = v.x; w[j + 1] = v.y; w[j + 2] = v.z; w[j + 3] = v.w;
+    }
+  }
+}
+
 template <int N>
 HBL_DEV void store_words(uint32_t* p, const uint32_t (&w)[N]) {
   if constexpr (N % 4 == 0) {
@@ -221,20 +248,24 @@ __global__ __launch_bounds__(256) void dequant_heads_kernel(const uint8_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// Decode attention, first stage: one workgroup per (sequence, query head,
-// chunk of CT cached tokens).  A lane holds one 32-code group (KB dwords) of
-// one token row: LPR = D/32 lanes cover a row, a wave covers RPI = 64/LPR
-// rows per step and each of the four waves takes NI = 8 steps.
-//   pass 1: score of every token: integer dot of the query codes with the
-//           key codes (v_dot4 on the quads), times sq * sk / sqrt(D);
-//   max over the chunk (LDS);
-//   pass 2: weights w = exp(s - max); sum of w * sv * u per channel and of
-//           w * sv, from which the (u - Z) form follows;
-//   the 4 * RPI partial rows are summed through LDS.
-// Output per workgroup: D unnormalised sums, the chunk max and the weight sum.
+// Decode attention.  One workgroup (4 waves) per (sequence, query head, chunk
+// of CT cached tokens); when the heads alone give enough workgroups, CT covers
+// the whole cache and the workgroup writes the output itself, otherwise a
+// second kernel merges the chunks.
+// A lane holds one 32-code group (KB dwords) of one token row: LPR = D/32
+// lanes cover a row and a wave covers RPI = 64/LPR rows per step; a block is
+// NI = 8 steps (BT = 8 * RPI tokens) and the waves take the chunk's blocks in
+// turn, each block's loads issued while the previous block is computed.
+// Per block:
+//   scores: integer dot of the query codes with the key codes (v_dot4 on the
+//           quads), times sq * sk / sqrt(D);
+//   online softmax: the wave's running max, rescaling its sums when it grows;
+//   values: sum of w * sv * u per channel and of w * sv (the (u - Z) form
+//           follows at the end), codes read as fp8 bytes (exact, see above).
+// The four waves' sums are rescaled to one max and added through LDS.
 template <int D>
 struct AttnCfg {
-  static constexpr int LPR = D / 32, RPI = 64 / LPR, NI = 8, CT = 4 * NI * RPI;
+  static constexpr int LPR = D / 32, RPI = 64 / LPR, NI = 8, BT = NI * RPI, WB = 4 * BT;
   static constexpr int STRIDE = D + 8;           // LDS row stride (floats)
   static constexpr int PROWS = 4 * RPI;          // partial rows per workgroup
   static constexpr int SUBS = 1024 / D;          // reduction lanes per 4 channels
@@ -243,56 +274,80 @@ struct AttnCfg {
 // padded to a 16-byte multiple.
 template <int D> constexpr int kPartStride = D + 4;
 
+template <int KB, int NI>
+struct AttnBlock {
+  uint32_t k[NI][KB], v[NI][KB];
+  float ks[NI], vs[NI];
+};
+
 template <int D, int KB>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   using C = AttnCfg<D>;
-  constexpr int LPR = C::LPR, RPI = C::RPI, NI = C::NI;
+  constexpr int LPR = C::LPR, RPI = C::RPI, NI = C::NI, BT = C::BT;
   __shared__ float part[C::PROWS * C::STRIDE];
   __shared__ float red[16];
   __shared__ __align__(16) int8_t qbytes[D];
 
   // Work item, in an XCD-aware order: the query heads that share one KV head
   // and chunk get workgroup ids 8 apart, so they run on the same XCD.
-  const int g = a.Hq / a.Hkv;
-  const int64_t L = blockIdx.x;
-  const int64_t unit = (L / 8 / g) * 8 + (L % 8);
-  const int j = (int)((L / 8) % g);
-  if (unit >= (int64_t)a.B * a.Hkv * a.nchunk) return;
-  const int chunk = (int)(unit % a.nchunk);
-  const int64_t bh = unit / a.nchunk;
-  const int hk = (int)(bh % a.Hkv), b = (int)(bh / a.Hkv);
-  const int hq = hk * g + j;
+  // (32-bit arithmetic: the host bounds every count below 2^31.)
+  const uint32_t g = (uint32_t)(a.Hq / a.Hkv);
+  const uint32_t L = blockIdx.x;
+  const uint32_t unit = (L / 8u / g) * 8u + (L % 8u);
+  const uint32_t j = (L / 8u) % g;
+  if (unit >= (uint32_t)a.B * (uint32_t)a.Hkv * (uint32_t)a.nchunk) return;
+  const uint32_t chunk = unit % (uint32_t)a.nchunk;
+  const uint32_t bh = unit / (uint32_t)a.nchunk;
+  const int hk = (int)(bh % (uint32_t)a.Hkv), b = (int)(bh / (uint32_t)a.Hkv);
+  const int hq = hk * (int)g + (int)j;
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.Tmax ? (int)a.Tmax : len);
-  const int t0 = chunk * C::CT;
-  if (t0 >= len) return;
-
+  const int t0 = (int)chunk * a.ct;
+  const bool single = a.nchunk == 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (t0 >= len) {
+    // Empty context (only possible for chunk 0 of a zero length): zeros.
+    if (single && chunk == 0) {
+      const int64_t ob = ((int64_t)b * a.Hq + hq) * D;
+      for (int e = threadIdx.x; e < D; e += 256) {
+        if (a.out_bf16) static_cast<uint16_t*>(a.out)[ob + e] = 0;
+        else static_cast<float*>(a.out)[ob + e] = 0.0f;
+      }
+    }
+    return;
+  }
+  const int lim = len < t0 + a.ct ? len : t0 + a.ct;   // tokens [t0, lim) of this chunk
   const int c = lane % LPR, r = lane / LPR;
 
   constexpr int RDW = D / 32 * KB;                    // dwords per cache row
+  // Buffer views of this head's cache rows 0 .. len-1: loads past the length
+  // read zeros (their scores are masked), so no address is clamped.
   const int64_t head_row = ((int64_t)b * a.Hkv + hk) * a.Tmax;
-  const uint32_t* kw = reinterpret_cast<const uint32_t*>(a.kc);
-  const uint32_t* vw = reinterpret_cast<const uint32_t*>(a.vc);
-  const int tw0 = t0 + wave * (NI * RPI) + r;
+  const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + head_row * RDW * 4), (short)0, len * RDW * 4,
+                                                     kBufferFlags);
+  const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + head_row * RDW * 4), (short)0, len * RDW * 4,
+                                                     kBufferFlags);
+  const auto kss = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + head_row), (short)0, len * 4, kBufferFlags);
+  const auto vss = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + head_row), (short)0, len * 4, kBufferFlags);
 
-  // Issue every cache load of both passes first.
-  uint32_t kx[NI][KB], vx[NI][KB];
-  float ksc[NI], vsc[NI];
+  auto load_block = [&](AttnBlock<KB, NI>& blk, int tb) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int t = tw0 + i * RPI;
-    const int64_t row = head_row + (t < len ? t : len - 1);
-    load_words<KB>(kw + row * RDW + c * KB, kx[i]);
-    ksc[i] = a.ks[row];
-  }
+    for (int i = 0; i < NI; ++i) {
+      const int t = tb + i * RPI + r;
+      buffer_words<KB>(krs, (t * RDW + c * KB) * 4, blk.k[i]);
+      blk.ks[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kss, t * 4, 0, 0));
+    }
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int t = tw0 + i * RPI;
-    const int64_t row = head_row + (t < len ? t : len - 1);
-    load_words<KB>(vw + row * RDW + c * KB, vx[i]);
-    vsc[i] = a.vs[row];
-  }
+    for (int i = 0; i < NI; ++i) {
+      const int t = tb + i * RPI + r;
+      buffer_words<KB>(vrs, (t * RDW + c * KB) * 4, blk.v[i]);
+      blk.vs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vss, t * 4, 0, 0));
+    }
+  };
+  // Blocks of this wave: t0 + (wave + 4 * n) * BT while below lim.
+  const int tb0 = t0 + wave * BT;
+  AttnBlock<KB, NI> A, Bk;
+  if (tb0 < lim) load_block(A, tb0);
 
   // Query, quantised with the whole head's absmax by wave 0 (D/64 channels
   // per lane) into signed bytes in LDS; every lane then reads the quads of
@@ -332,74 +387,95 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   constexpr float kInvSqrtD = D == 64 ? 0.125f : (D == 128 ? 0.08838834764831845f : 0.0625f);
   const float coef = sq * kInvSqrtD;
   constexpr int ZK = KB == 8 ? 0 : (1 << (KB - 1));   // 8-bit key codes are flipped to signed bytes
-
-  // Pass 1: scores.
-  float s[NI];
-  float smax = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    uint32_t kq[8];
-    unpack_quads<KB>(kx[i], kq);
-    int acc = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      acc = __builtin_amdgcn_sdot4((int)(KB == 8 ? kq[k] ^ 0x80808080u : kq[k]), qd[k], acc, false);
-    float f = lane_reduce<LPR, false>((float)acc) - (float)ZK * qsum;   // integers below 2^24: exact
-    const int t = tw0 + i * RPI;
-    s[i] = t < len ? f * (coef * ksc[i]) : -INFINITY;
-    smax = fmaxf(smax, s[i]);
-  }
-  smax = lane_reduce<64, true>(smax);
-  if (lane == 0) red[wave] = smax;
-  __syncthreads();
-  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
-  // Pass 2: acc_e = sum_t w_t sv_t u_{t,e} and sw = sum_t w_t sv_t.  Codes
-  // below 16 are read as OCP e4m3 bytes, which gives u * unit exactly.
   const float fp8_unit = __builtin_amdgcn_cvt_pk_f32_fp8(1, false)[0];
   const float vmul = KB == 8 ? 1.0f : 1.0f / fp8_unit;
+
   float acc[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
-  float lsum = 0.0f, swv = 0.0f;
+  float m = -INFINITY, lsum = 0.0f, swv = 0.0f;
+
+  auto process = [&](const AttnBlock<KB, NI>& blk, int tb) __attribute__((always_inline)) {
+    float s[NI];
+    float bmax = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const float w = __builtin_amdgcn_exp2f((s[i] - m) * kLog2e);   // 0 for masked tokens
-    lsum += w;
-    const float wsv = w * vsc[i];
-    swv += wsv;
-    const float wv = wsv * vmul;
-    uint32_t vq[8];
-    unpack_quads<KB>(vx[i], vq);
+    for (int i = 0; i < NI; ++i) {
+      uint32_t kq[8];
+      unpack_quads<KB>(blk.k[i], kq);
+      int dot = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if constexpr (KB == 8) {
-        acc[4 * k + 0] = __builtin_fmaf(wv, (float)((vq[k] >> 0) & 0xFFu), acc[4 * k + 0]);
-        acc[4 * k + 1] = __builtin_fmaf(wv, (float)((vq[k] >> 8) & 0xFFu), acc[4 * k + 1]);
-        acc[4 * k + 2] = __builtin_fmaf(wv, (float)((vq[k] >> 16) & 0xFFu), acc[4 * k + 2]);
-        acc[4 * k + 3] = __builtin_fmaf(wv, (float)((vq[k] >> 24) & 0xFFu), acc[4 * k + 3]);
-      } else {
-        const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vq[k], false);
-        const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vq[k], true);
-        acc[4 * k + 0] = __builtin_fmaf(wv, lo.x, acc[4 * k + 0]);
-        acc[4 * k + 1] = __builtin_fmaf(wv, lo.y, acc[4 * k + 1]);
-        acc[4 * k + 2] = __builtin_fmaf(wv, hi.x, acc[4 * k + 2]);
-        acc[4 * k + 3] = __builtin_fmaf(wv, hi.y, acc[4 * k + 3]);
+      for (int k = 0; k < 8; ++k)
+        dot = __builtin_amdgcn_sdot4((int)(KB == 8 ? kq[k] ^ 0x80808080u : kq[k]), qd[k], dot, false);
+      const float f = lane_reduce<LPR, false>((float)dot) - (float)ZK * qsum;   // integers below 2^24: exact
+      s[i] = tb + i * RPI + r < lim ? f * (coef * blk.ks[i]) : -INFINITY;
+      bmax = fmaxf(bmax, s[i]);
+    }
+    bmax = lane_reduce<64, true>(bmax);
+    if (bmax > m) {                                   // wave-uniform
+      const float sc = __builtin_amdgcn_exp2f((m - bmax) * kLog2e);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) acc[e] *= sc;
+      lsum *= sc;
+      swv *= sc;
+      m = bmax;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float w = __builtin_amdgcn_exp2f((s[i] - m) * kLog2e);   // 0 for masked tokens
+      lsum += w;
+      const float wsv = w * blk.vs[i];
+      swv += wsv;
+      const float wv = wsv * vmul;
+      uint32_t vq[8];
+      unpack_quads<KB>(blk.v[i], vq);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if constexpr (KB == 8) {
+          acc[4 * k + 0] = __builtin_fmaf(wv, (float)((vq[k] >> 0) & 0xFFu), acc[4 * k + 0]);
+          acc[4 * k + 1] = __builtin_fmaf(wv, (float)((vq[k] >> 8) & 0xFFu), acc[4 * k + 1]);
+          acc[4 * k + 2] = __builtin_fmaf(wv, (float)((vq[k] >> 16) & 0xFFu), acc[4 * k + 2]);
+          acc[4 * k + 3] = __builtin_fmaf(wv, (float)((vq[k] >> 24) & 0xFFu), acc[4 * k + 3]);
+        } else {
+          const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vq[k], false);
+          const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vq[k], true);
+          acc[4 * k + 0] = __builtin_fmaf(wv, lo.x, acc[4 * k + 0]);
+          acc[4 * k + 1] = __builtin_fmaf(wv, lo.y, acc[4 * k + 1]);
+          acc[4 * k + 2] = __builtin_fmaf(wv, hi.x, acc[4 * k + 2]);
+          acc[4 * k + 3] = __builtin_fmaf(wv, hi.y, acc[4 * k + 3]);
+        }
       }
     }
+  };
+
+  // Ping-pong over the wave's blocks (wave-uniform control flow).
+  for (int tb = tb0; tb < lim; tb += 8 * BT) {
+    const int tn = tb + 4 * BT;
+    if (tn < lim) load_block(Bk, tn);
+    process(A, tb);
+    if (tn >= lim) break;
+    if (tn + 4 * BT < lim) load_block(A, tn + 4 * BT);
+    process(Bk, tn);
   }
 
-  // Sum the partial rows (lane (r, c) of wave w is row w * RPI + r) and the
-  // two per-token sums (counted once per token: lanes with c == 0).
+  // Rescale the four waves to the workgroup max (a wave without blocks has
+  // m = -inf and zero sums) and add their partial rows through LDS.
+  const float lw = lane_reduce<64, false>(c == 0 ? lsum : 0.0f);
+  const float sw = lane_reduce<64, false>(c == 0 ? swv : 0.0f);
+  if (lane == 0) { red[wave] = m; red[4 + wave] = lw; red[8 + wave] = sw; }
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   {
+    const float sc = __builtin_amdgcn_exp2f((m - M) * kLog2e);
     float* pr = part + (wave * RPI + r) * C::STRIDE + c * 32;
 #pragma unroll
     for (int e = 0; e < 32; e += 4)
-      *reinterpret_cast<float4*>(pr + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+      *reinterpret_cast<float4*>(pr + e) = make_float4(acc[e] * sc, acc[e + 1] * sc, acc[e + 2] * sc, acc[e + 3] * sc);
   }
-  const float l = lane_reduce<64, false>(c == 0 ? lsum : 0.0f);
-  const float sw = lane_reduce<64, false>(c == 0 ? swv : 0.0f);
-  if (lane == 0) { red[4 + wave] = l; red[8 + wave] = sw; }
+  float fw[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) fw[w] = __builtin_amdgcn_exp2f((red[w] - M) * kLog2e);
+  const float Lsum = fw[0] * red[4] + fw[1] * red[5] + fw[2] * red[6] + fw[3] * red[7];
+  const float SW = fw[0] * red[8] + fw[1] * red[9] + fw[2] * red[10] + fw[3] * red[11];
   __syncthreads();
   constexpr int SUBS = C::SUBS, RPS = C::PROWS / SUBS;   // rows per reduction lane
   const int sub = threadIdx.x % SUBS, grp = threadIdx.x / SUBS;
@@ -413,44 +489,93 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   sum.y = lane_reduce<SUBS, false>(sum.y);
   sum.z = lane_reduce<SUBS, false>(sum.z);
   sum.w = lane_reduce<SUBS, false>(sum.w);
-  const float zsw = (float)(1 << (KB - 1)) * (red[8] + red[9] + red[10] + red[11]);
+  const float zsw = (float)(1 << (KB - 1)) * SW;
+  const float4 o = make_float4(sum.x - zsw, sum.y - zsw, sum.z - zsw, sum.w - zsw);
+  if (single) {
+    if (sub == 0) {
+      const float inv = 1.0f / Lsum;
+      const int64_t ob = ((int64_t)b * a.Hq + hq) * D + grp * 4;
+      if (a.out_bf16) {
+        uint2 pk;
+        pk.x = f32_to_bf16(o.x * inv) | ((uint32_t)f32_to_bf16(o.y * inv) << 16);
+        pk.y = f32_to_bf16(o.z * inv) | ((uint32_t)f32_to_bf16(o.w * inv) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ob) = pk;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ob) =
+            make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+      }
+    }
+    return;
+  }
   float* out = a.part + (((int64_t)b * a.Hq + hq) * a.nchunk + chunk) * kPartStride<D>;
-  if (sub == 0)
-    *reinterpret_cast<float4*>(out + grp * 4) = make_float4(sum.x - zsw, sum.y - zsw, sum.z - zsw, sum.w - zsw);
+  if (sub == 0) *reinterpret_cast<float4*>(out + grp * 4) = o;
   if (threadIdx.x == 0) {
-    out[D] = m;
-    out[D + 1] = red[4] + red[5] + red[6] + red[7];
+    out[D] = M;
+    out[D + 1] = Lsum;
   }
 }
 
-// Second stage: merge the chunks of one (sequence, query head).
+// Second stage (several chunks per head): merge the chunks of one
+// (sequence, query head); one wave.  Latency-bound, so every load is issued
+// before any result is needed: the partial sums of up to 16 chunks per round
+// (chunks past the length are read too, from the workspace, and discarded by
+// select), and each lane's chunk max and weight sum.
 template <int D, bool OBF16>
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+  constexpr int PS = kPartStride<D>, PER = D / 64, NB = 16;
   const int64_t bh = blockIdx.x;
   const int b = (int)(bh / a.Hq);
+  const int lane = threadIdx.x;
+  const int nch = a.nchunk;
+  const float* p = a.part + bh * nch * PS;
+  float pv[NB][PER];
+#pragma unroll
+  for (int kk = 0; kk < NB; ++kk)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) pv[kk][i] = kk < nch ? p[kk * PS + lane + 64 * i] : 0.0f;
+  const bool own = lane < nch;                      // first round of lane-parallel statistics
+  const float m0 = own ? p[lane * PS + D] : -INFINITY;
+  const float l0 = own ? p[lane * PS + D + 1] : 0.0f;
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.Tmax ? (int)a.Tmax : len);
-  const int n = (len + AttnCfg<D>::CT - 1) / AttnCfg<D>::CT;
-  constexpr int PS = kPartStride<D>;
-  const float* p = a.part + bh * a.nchunk * PS;
-  float M = -INFINITY;
-  for (int k = 0; k < n; ++k) M = fmaxf(M, p[k * PS + D]);
+  const int n = (len + a.ct - 1) / a.ct;
+
+  float M = lane < n ? m0 : -INFINITY;
+  for (int k = lane + 64; k < n; k += 64) M = fmaxf(M, p[k * PS + D]);
+  M = lane_reduce<64, true>(M);
   float Lsum = 0.0f;
-  constexpr int PER = D / 64;
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.0f;
-  for (int k = 0; k < n; ++k) {
-    const float f = __builtin_amdgcn_exp2f((p[k * PS + D] - M) * kLog2e);
-    Lsum = __builtin_fmaf(f, p[k * PS + D + 1], Lsum);
+  for (int k0 = 0; k0 < n; k0 += NB) {
+    if (k0 > 0) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] = __builtin_fmaf(f, p[k * PS + threadIdx.x + 64 * i], o[i]);
+      for (int kk = 0; kk < NB; ++kk)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) pv[kk][i] = k0 + kk < n ? p[(k0 + kk) * PS + lane + 64 * i] : 0.0f;
+    }
+    // factors exp(m_k - M) of chunks k0 .. k0+NB-1, held by lanes 0 .. NB-1
+    const int kl = k0 + (lane % NB);
+    float f = 0.0f, lk = 0.0f;
+    if (kl < n) {
+      const float mk = kl == lane ? m0 : p[kl * PS + D];
+      lk = kl == lane ? l0 : p[kl * PS + D + 1];
+      f = __builtin_amdgcn_exp2f((mk - M) * kLog2e);
+    }
+    if (lane < NB) Lsum = __builtin_fmaf(f, lk, Lsum);
+#pragma unroll
+    for (int kk = 0; kk < NB; ++kk) {
+      const float fk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), kk));
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] = k0 + kk < n ? __builtin_fmaf(fk, pv[kk][i], o[i]) : o[i];
+    }
   }
+  Lsum = lane_reduce<64, false>(Lsum);
   const float inv = n > 0 ? 1.0f / Lsum : 0.0f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const float v = o[i] * inv;
-    const int64_t idx = bh * D + threadIdx.x + 64 * i;
+    const int64_t idx = bh * D + lane + 64 * i;
     if constexpr (OBF16) static_cast<uint16_t*>(a.out)[idx] = f32_to_bf16(v);
     else static_cast<float*>(a.out)[idx] = v;
   }
@@ -469,6 +594,7 @@ hipError_t launch_attn_d(const AttnArgs& a) {
     default: return hipErrorInvalidValue;
   }
   if (hipError_t e = hipGetLastError()) return e;
+  if (a.nchunk == 1) return hipSuccess;
   const dim3 grid((unsigned)((int64_t)a.B * a.Hq));
   if (a.out_bf16) attn_combine_kernel<D, true><<<grid, dim3(64), 0, a.stream>>>(a);
   else attn_combine_kernel<D, false><<<grid, dim3(64), 0, a.stream>>>(a);
@@ -493,8 +619,20 @@ bool heads_bits_supported(int bits) { return bits == 2 || bits == 3 || bits == 4
 
 int attn_part_stride(int d) { return d + 4; }
 
-int attn_chunk_tokens(int d) {
-  return d == 64 ? AttnCfg<64>::CT : d == 128 ? AttnCfg<128>::CT : d == 256 ? AttnCfg<256>::CT : 0;
+void attn_plan(int64_t B, int64_t Hq, int d, int64_t Tmax, int* ct, int* nchunk) {
+  const int64_t wb = attn_block_tokens(d);
+  const int64_t max_chunks = (Tmax + wb - 1) / wb;
+  const int64_t heads = B * Hq;
+  int64_t want = heads >= 512 ? 1 : (512 + heads - 1) / heads;
+  if (want > max_chunks) want = max_chunks;
+  const int64_t per = (Tmax + want - 1) / want;
+  const int64_t c = (per + wb - 1) / wb * wb;
+  *ct = (int)c;
+  *nchunk = (int)((Tmax + c - 1) / c);
+}
+
+int attn_block_tokens(int d) {
+  return d == 64 ? AttnCfg<64>::WB : d == 128 ? AttnCfg<128>::WB : d == 256 ? AttnCfg<256>::WB : 0;
 }
 
 hipError_t launch_quant_heads(const QuantHeadsArgs& a) {

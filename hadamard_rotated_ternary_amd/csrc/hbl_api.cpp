@@ -279,8 +279,9 @@ static bool heads_d_ok(int64_t d) { return d == 64 || d == 128 || d == 256; }
 static constexpr int64_t kCount = int64_t(1) << 31;
 
 static size_t attn_part_bytes(int64_t B, int64_t Hq, int64_t d, int64_t Tmax) {
-  const int ct = hbl::attn_chunk_tokens((int)d);
-  const int64_t nchunk = (Tmax + ct - 1) / ct;
+  int ct = 0, nchunk = 0;
+  hbl::attn_plan(B, Hq, (int)d, Tmax, &ct, &nchunk);
+  if (nchunk == 1) return 0;                 // one workgroup per head writes the output itself
   return align256((size_t)B * Hq * nchunk * hbl::attn_part_stride((int)d) * sizeof(float));
 }
 
@@ -342,20 +343,23 @@ hbl_status hbl_attention_decode(const void* q, int q_bits, const uint8_t* k_code
   if (!heads_d_ok(d) || B < 0 || B >= kCount || Hkv <= 0 || Hq <= 0 || Hq >= kCount || Hq % Hkv != 0 ||
       Tmax <= 0 || Tmax >= kCount || B * Hkv * Tmax > (int64_t(1) << 34))
     return HBL_ERR_SHAPE;
-  const int ct = hbl::attn_chunk_tokens((int)d);
-  const int64_t nchunk = (Tmax + ct - 1) / ct;
-  if (B * Hq * nchunk >= kCount - 8 * Hq) return HBL_ERR_SHAPE;
   if (B == 0) return HBL_OK;
-  if (!q || !k_codes || !k_scale || !v_codes || !v_scale || !lens || !out || !workspace) return HBL_ERR_NULL;
+  int ct = 0, nchunk = 0;
+  hbl::attn_plan(B, Hq, (int)d, Tmax, &ct, &nchunk);
+  if (B * Hq * nchunk >= kCount - 8 * Hq) return HBL_ERR_SHAPE;
+  if (Tmax * (d * kv_bits / 8) >= kCount) return HBL_ERR_SHAPE;   // one head's codes addressed in 32 bits
+  const size_t need = attn_part_bytes(B, Hq, d, Tmax);
+  if (!q || !k_codes || !k_scale || !v_codes || !v_scale || !lens || !out || (need && !workspace))
+    return HBL_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_codes) || !aligned16(k_scale) || !aligned16(v_codes) || !aligned16(v_scale) ||
-      !aligned16(lens) || !aligned16(out) || !aligned16(workspace))
+      !aligned16(lens) || !aligned16(out) || (workspace && !aligned16(workspace)))
     return HBL_ERR_ALIGN;
-  if (ws_bytes < attn_part_bytes(B, Hq, d, Tmax)) return HBL_ERR_WORKSPACE;
+  if (ws_bytes < need) return HBL_ERR_WORKSPACE;
   if (hbl_status s = check_device()) return s;
   hbl::AttnArgs a{};
   a.q = q; a.qbits = q_bits; a.kc = k_codes; a.ks = k_scale; a.vc = v_codes; a.vs = v_scale; a.kvbits = kv_bits;
   a.lens = lens; a.B = (int)B; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.d = (int)d; a.Tmax = Tmax;
-  a.nchunk = (int)nchunk; a.part = static_cast<float*>(workspace); a.out = out;
+  a.ct = ct; a.nchunk = nchunk; a.part = static_cast<float*>(workspace); a.out = out;
   a.out_bf16 = out_dtype == HBL_BF16; a.stream = stream;
   return launched(hbl::launch_attention_decode(a));
 }

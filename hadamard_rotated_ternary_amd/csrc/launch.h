@@ -103,14 +103,18 @@ struct AttnArgs {
   const int32_t* lens;    // device [B]
   int B, Hq, Hkv, d;
   int64_t Tmax;
-  int nchunk;             // ceil(Tmax / attn_chunk_tokens(d))
+  int ct, nchunk;         // tokens per chunk and chunks per head (attn_plan)
   float* part;            // [B][Hq][nchunk][attn_part_stride(d)]
   void* out;              // [B][Hq][d]
   bool out_bf16;
   hipStream_t stream;
 };
 bool heads_bits_supported(int bits);
-int attn_chunk_tokens(int d);
+// Chunking of the cached tokens: one chunk per head when the heads give at
+// least 512 workgroups (two per compute unit of a 256-CU part), otherwise
+// enough chunks to reach that, in whole blocks of attn_block_tokens(d).
+int attn_block_tokens(int d);
+void attn_plan(int64_t B, int64_t Hq, int d, int64_t Tmax, int* ct, int* nchunk);
 int attn_part_stride(int d);
 hipError_t launch_attention_decode(const AttnArgs& a);
 

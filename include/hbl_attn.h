@@ -42,7 +42,8 @@
  * (nothing is launched on error); gfx950 only.
  * Supported: d in {64, 128, 256}; cache widths b in {2, 3, 4, 8}; query widths
  * q_bits in 2..8; counts (R, B, Tn, Hq, Hkv, Tmax) below 2^31, at most 2^34
- * cache rows (B * Hkv * Tmax) and 2^31 partial records (B * Hq * chunks).
+ * cache rows (B * Hkv * Tmax), below 2^31 bytes of codes per head
+ * (Tmax * d * b / 8) and 2^31 partial records (B * Hq * chunks).
  * Lengths and positions live in device memory, so the host cannot check them:
  * the kernels clamp lengths to [0, Tmax] and skip cache rows whose position
  * falls outside [0, Tmax).  Non-finite inputs give unspecified (but in-bounds)

@@ -193,4 +193,4 @@ def test_attention_entry_points_validate_without_device():
                                   None) == 1
     # partial records: B * Hq * ceil(Tmax / 512 tokens) of (d + 4) floats, rounded up to 256 bytes
     assert L.hbl_attention_workspace_bytes(2, 8, 128, 1000) == -(-(2 * 8 * 2 * 132 * 4) // 256) * 256
-    assert L.hbl_attention_workspace_bytes(1, 1, 64, 1) == 512   # 68 floats -> 272 bytes
+    assert L.hbl_attention_workspace_bytes(1, 1, 64, 1) == 0     # one chunk: the output is written directly

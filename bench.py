@@ -299,7 +299,50 @@ def extras(torch, hbl, synthetic, args):
                                   "gemm_hbm_frac": gbytes / (res["gemm"] / 1e6) / 1e9 / PEAK_HBM_GBS,
                                   "forward_us": res["forward"], "tokens_per_s": M / (res["forward"] / 1e6),
                                   "timing": f"graph replay of {R} back-to-back calls over {R} weight copies"}
+    out["decode_attn_7b_kv3"] = attention_extra(torch, hbl, synthetic, args)
     return out
+
+
+def attention_extra(torch, hbl, synthetic, args):
+    """Low-bit attention states: prefill of a 3-bit KV cache and one decode
+    step of attention over it (7B-shaped heads)."""
+    w = synthetic.ATTN_WORKLOADS["decode_attn_7b_kv3"]
+    q, k, v = synthetic.make_heads(w)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    del k, v
+    cache = hbl.KVCache(w.B, w.Hkv, w.T, w.d, w.kv_bits)
+    lens = torch.full((w.B,), w.T, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(hbl.attention_workspace_bytes(w.B, w.Hq, w.d, w.T), 16), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n
+
+    t_app = timed(lambda: cache.append(kd, vd), 10)
+    t_dec = timed(lambda: hbl.attention_decode(qd, w.q_bits, cache.k_codes, cache.k_scale, cache.v_codes,
+                                               cache.v_scale, w.kv_bits, lens, workspace=ws, out=out), 50)
+    rows = w.B * w.Hkv * w.T
+    row_bytes = w.d * w.kv_bits // 8 + 4
+    cache_bytes = 2 * rows * row_bytes
+    dec_bytes = cache_bytes + w.B * w.Hq * w.d * 4
+    app_bytes = 2 * rows * w.d * 2 + cache_bytes
+    return {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "T": w.T, "kv_bits": w.kv_bits, "q_bits": w.q_bits,
+            "decode_us": t_dec, "decode_gbps": dec_bytes / (t_dec / 1e6) / 1e9,
+            "decode_hbm_frac": dec_bytes / (t_dec / 1e6) / 1e9 / PEAK_HBM_GBS,
+            "bf16_cache_hbm_floor_us": (2 * rows * (w.d * 2)) / (PEAK_HBM_GBS * 1e9) * 1e6,
+            "append_prefill_us": t_app, "append_gbps": app_bytes / (t_app / 1e6) / 1e9,
+            "timing": "events around back-to-back calls; cache and lengths resident in HBM"}
 
 
 def cpu_baseline(x, wl, bits, budget_s):

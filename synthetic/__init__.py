@@ -121,3 +121,48 @@ def sample_rows(M: int, count: int) -> np.ndarray:
         return np.arange(M)
     rows = np.unique(np.concatenate([np.linspace(0, M - 1, count - 2).astype(np.int64), [0, M - 1]]))
     return rows
+
+
+# ------------------------------------------------------- attention states
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """One decode step of attention over a quantised KV cache."""
+    name: str
+    B: int            # sequences
+    Hq: int           # query heads
+    Hkv: int          # key/value heads
+    d: int            # head size
+    T: int            # cached tokens per sequence
+    kv_bits: int
+    q_bits: int
+    n_out: int        # outlier channels of the keys (same channels for every token)
+    factor: float
+    seed: int
+
+
+# A 7B-shaped model (32 heads of 128) decoding 16 sequences against 4096
+# cached tokens with the 3-bit KV cache, and a small case for tests.
+ATTN_WORKLOADS: Dict[str, AttnWorkload] = {
+    "decode_attn_7b_kv3": AttnWorkload("decode_attn_7b_kv3", 16, 32, 32, 128, 4096, 3, 8, 4, 8.0, 11),
+    "decode_attn_small": AttnWorkload("decode_attn_small", 4, 4, 2, 128, 1100, 3, 8, 4, 8.0, 12),
+}
+
+
+def make_heads(w: AttnWorkload, with_cache: bool = True):
+    """Draw post-RoPE states: q [B][Hq][d] and, if requested, the new keys and
+    values k, v [B][T][Hkv][d] of a prefill, all as bf16 codes (uint16).
+
+    Queries and values are N(0, 1); keys are N(0, 1) with a few channels
+    scaled by ``factor`` (key states carry channel outliers).  Draw order is
+    fixed: outlier channels, q, k, v.
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    idx = outlier_channels(rng, w.d, w.n_out)
+    q = f32_to_bf16_bits(rng.standard_normal((w.B, w.Hq, w.d), dtype=np.float32))
+    if not with_cache:
+        return q, None, None
+    k = rng.standard_normal((w.B, w.T, w.Hkv, w.d), dtype=np.float32)
+    k[..., idx] *= np.float32(w.factor)
+    k = f32_to_bf16_bits(k)
+    v = f32_to_bf16_bits(rng.standard_normal((w.B, w.T, w.Hkv, w.d), dtype=np.float32))
+    return q, k, v

@@ -221,6 +221,31 @@ def stored_traffic(workload):
     return int(kv["bytes_per_launch"])
 
 
+ATTN_PROFILE = os.path.join(ROOT, "profiles", "decode_attn_7b_kv3_rocprof.txt")
+
+
+def attn_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("attn.hip", "common.h", "fwht.h"):
+        with open(os.path.join(ROOT, "hadamard_rotated_ternary_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_attn_traffic():
+    """HBM bytes per decode-attention launch from the committed counter runs,
+    if they were taken on the current attention source; otherwise None."""
+    try:
+        with open(ATTN_PROFILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha") != attn_source_sha():
+        return None
+    return int(kv["attn_bytes_per_launch"])
+
+
 def extras(torch, hbl, synthetic, args):
     out = {}
     # INT8 activations on the same 7B Wdown shape
@@ -340,6 +365,7 @@ def attention_extra(torch, hbl, synthetic, args):
     return {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "T": w.T, "kv_bits": w.kv_bits, "q_bits": w.q_bits,
             "decode_us": t_dec, "decode_gbps": dec_bytes / (t_dec / 1e6) / 1e9,
             "decode_hbm_frac": dec_bytes / (t_dec / 1e6) / 1e9 / PEAK_HBM_GBS,
+            "decode_traffic_bytes": stored_attn_traffic(),
             "bf16_cache_hbm_floor_us": (2 * rows * (w.d * 2)) / (PEAK_HBM_GBS * 1e9) * 1e6,
             "append_prefill_us": t_app, "append_gbps": app_bytes / (t_app / 1e6) / 1e9,
             "timing": "events around back-to-back calls; cache and lengths resident in HBM"}

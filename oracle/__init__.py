@@ -53,6 +53,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_quant_heads.argtypes = [P, I64, I64, I, P, P, P]
         L.oracle_dequant_heads.argtypes = [P, P, I64, I64, I, P]
         L.oracle_attention_decode.argtypes = [P, I, P, P, P, P, I, P, I64, I64, I64, I64, I64, P]
+        L.oracle_backward.argtypes = [P, P, P, P, P, ctypes.c_float, P, I64, I64, I64, I, P, P, P, P]
         _lib = L
     return _lib
 
@@ -207,6 +208,27 @@ def dequant_heads(codes: np.ndarray, scale: np.ndarray, bits: int) -> np.ndarray
     y = np.empty((R, d))
     _chk(lib().oracle_dequant_heads(_p(codes), _p(scale), R, d, bits, _p(y)), "dequant_heads")
     return y
+
+
+def backward(x, gain, q, d, wt, alpha, dy, rotate=True, want_dxh=False):
+    """Straight-through backward of the layer.  x [M][K] fp32 (the forward
+    input), gain [K] or None, q int8 [M][K] and d [M] (the forward's codes and
+    scales), wt int8 [N][K], alpha fp32, dy [M][N].  Returns (dx, dw, dg, dxh)
+    as float64 arrays (dg None without a gain, dxh None unless requested)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    d = np.ascontiguousarray(d, dtype=np.float64)
+    wt = np.ascontiguousarray(wt, dtype=np.int8)
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    g = None if gain is None else np.ascontiguousarray(gain, dtype=np.float32)
+    M, K = x.shape
+    N = wt.shape[0]
+    dx = np.empty((M, K)); dw = np.empty((N, K))
+    dg = np.empty(K) if g is not None else None
+    dxh = np.empty((M, K)) if want_dxh else None
+    _chk(lib().oracle_backward(_p(x), _p(g), _p(q), _p(d), _p(wt), float(alpha), _p(dy), M, K, N, int(rotate),
+                               _p(dxh), _p(dx), _p(dw), _p(dg)), "backward")
+    return dx, dw, dg, dxh
 
 
 def attention_decode(q, qbits, kc, ks, vc, vs, kvbits, lens):

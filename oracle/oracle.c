@@ -20,6 +20,9 @@
  *       close to Gaussian (attention/FFN input projections) [XZY §H-BitLinear模块];
  *     weights rotated offline as well (weight + activation rotation, the
  *       ablation of [XZY §实验效果], table 5).
+ *   Backward pass [QbitAI §引入H-BitLinear模块] (training paragraph): the
+ *     quantisers are bypassed (straight-through estimator) and the gradient
+ *     goes through the transposed Hadamard transform, which is the transform.
  *   Low-bit attention states [XZY §实验效果], [QbitAI]: post-RoPE Q/K/V heads
  *     quantised per head by absmax to unsigned integers (3-bit KV cache), and
  *     one decode step of attention over that cache.
@@ -418,6 +421,79 @@ int oracle_attention_decode(const float *q, int qbits, const uint8_t *kc, const 
         free(uq); free(qh); free(lg);
     }
     return rc ? -3 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward pass of the layer with the straight-through estimator
+ * [QbitAI §引入H-BitLinear模块] (training: the non-differentiable quantiser
+ * functions are bypassed; the gradient is transformed with the orthogonal
+ * Hadamard matrix).  The forward is y = xh . Wh^T with the quantised operands
+ * xh = q * d (per token) and Wh = W_t * a; the estimator treats both
+ * quantisers as the identity, so
+ *   dxh[m][k] = a * sum_n dy[m][n] W_t[n][k]          (gradient at xt)
+ *   du        = H_K dxh / sqrt(K)  (H symmetric and orthonormal after the
+ *               scaling, so its transpose is itself); du = dxh unrotated
+ *   RMSNorm, u = x g / r, r = sqrt(mean x^2 + EPS_NORM):
+ *   dx[m][j]  = g_j du_j / r - x_j / (K r^3) * sum_i du_i g_i x_i
+ *   dg[k]     = sum_m du[m][k] x[m][k] / r_m           (tokens in order)
+ *   dW[n][k]  = sum_m dy[m][n] q[m][k] d[m]            (latent weights)
+ * q, d are the forward's codes and scales; x, g its input and gain.
+ * Outputs (double): dxh [M][K] (optional), dx [M][K], dw [N][K], dg [K]
+ * (optional; needs g).
+ * ------------------------------------------------------------------------- */
+int oracle_backward(const float *x, const float *g, const int8_t *q, const double *d, const int8_t *wt,
+                    float alpha, const float *dy, int64_t M, int64_t K, int64_t N, int rotate,
+                    double *dxh, double *dx, double *dw, double *dg)
+{
+    if (!x || !q || !d || !wt || !dy || !dx || !dw || M < 0 || N <= 0 || !is_pow2(K) || (dg && !g)) return -1;
+    const double a = oracle_weight_scale(alpha);
+    double *du_all = dg ? (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1) * (size_t)K) : NULL;
+    double *rr = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+    if ((dg && !du_all) || !rr) { free(du_all); free(rr); return -2; }
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        double *t = (double *)malloc(sizeof(double) * (size_t)K);
+        double *du = (double *)malloc(sizeof(double) * (size_t)K);
+        if (!t || !du) { bad = 1; free(t); free(du); continue; }
+        for (int64_t k = 0; k < K; ++k) t[k] = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double gy = (double)dy[m * N + n];
+            if (gy == 0.0) continue;
+            for (int64_t k = 0; k < K; ++k) t[k] += gy * (double)wt[n * K + k];
+        }
+        for (int64_t k = 0; k < K; ++k) t[k] *= a;
+        if (dxh) memcpy(dxh + m * K, t, sizeof(double) * (size_t)K);
+        if (rotate) oracle_hadamard_rotate(t, K, du);
+        else memcpy(du, t, sizeof(double) * (size_t)K);
+        const float *xm = x + m * K;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) ss += (double)xm[k] * (double)xm[k];
+        const double r = sqrt(ss / (double)K + EPS_NORM);
+        double sdot = 0.0;
+        for (int64_t k = 0; k < K; ++k) sdot += du[k] * (g ? (double)g[k] : 1.0) * (double)xm[k];
+        for (int64_t k = 0; k < K; ++k)
+            dx[m * K + k] = (g ? (double)g[k] : 1.0) * du[k] / r - (double)xm[k] * sdot / ((double)K * r * r * r);
+        rr[m] = r;
+        if (du_all) memcpy(du_all + m * K, du, sizeof(double) * (size_t)K);
+        free(t); free(du);
+    }
+    if (!bad && dg) {
+        for (int64_t k = 0; k < K; ++k) dg[k] = 0.0;
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t k = 0; k < K; ++k) dg[k] += du_all[m * K + k] * (double)x[m * K + k] / rr[m];
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) dw[n * K + k] = 0.0;
+        for (int64_t m = 0; m < M; ++m) {
+            const double gy = (double)dy[m * N + n] * d[m];
+            if (gy == 0.0) continue;
+            for (int64_t k = 0; k < K; ++k) dw[n * K + k] += gy * (double)q[m * K + k];
+        }
+    }
+    free(du_all); free(rr);
+    return bad ? -2 : 0;
 }
 
 int oracle_max_threads(void)

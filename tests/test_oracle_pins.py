@@ -589,3 +589,111 @@ def test_attention_quantises_the_query():
         if qbits == 3:
             full = oracle.attention_decode(q, 8, kc, ks, vc, vs, bits, np.array([T]))
             assert not np.allclose(a, full, rtol=1e-6)
+
+
+# ------------------------------------------------------------------ backward
+# Straight-through backward (量子位 article, section 引入H-BitLinear模块,
+# training paragraph): quantisers bypassed, gradient through the transposed
+# (= the same) orthonormal Hadamard transform.  Pinned by finite differences
+# of the quantiser-free surrogate built from the pinned forward steps.
+
+def _surrogate_loss(x, g, wt, a, dy, rotate):
+    """<dy, xt(x) . (W_t a)^T> with xt = H RMSNorm(x) / sqrt(K) (or RMSNorm(x))."""
+    u = oracle.rmsnorm(x, g)
+    xt = oracle.hadamard_rotate(u) if rotate else u
+    y = xt @ (wt.astype(np.float64) * a).T
+    return float(np.sum(y * dy.astype(np.float64)))
+
+
+def _bwd_case(seed, M=3, K=16, N=5, with_gain=True):
+    rng = np.random.default_rng(seed)
+    x = (rng.integers(-64, 65, size=(M, K)) / 16.0).astype(np.float32)   # multiples of 1/16: x +- 2^-10 exact
+    g = (rng.integers(8, 25, size=K) / 16.0).astype(np.float32) if with_gain else None
+    w = rng.normal(0, 0.02, size=(N, K)).astype(np.float32)
+    wt, alpha = oracle.quantize_weights(w)
+    dy = rng.normal(size=(M, N)).astype(np.float32)
+    return x, g, wt, alpha, dy
+
+
+@pytest.mark.parametrize("rotate", [True, False])
+@pytest.mark.parametrize("with_gain", [True, False])
+def test_backward_input_matches_finite_differences(rotate, with_gain):
+    x, g, wt, alpha, dy = _bwd_case(1 + rotate + 2 * with_gain, with_gain=with_gain)
+    a = oracle.weight_scale(alpha)
+    fw = oracle.forward(x, wt, alpha, 8, g=g, rotate=rotate)
+    dx, dw, dg, _ = oracle.backward(x, g, fw["q"], fw["d"], wt, alpha, dy, rotate=rotate)
+    h = np.float32(2.0 ** -10)
+    M, K = x.shape
+    for m in range(M):
+        for j in range(K):
+            xp, xm = x.copy(), x.copy()
+            xp[m, j] += h
+            xm[m, j] -= h
+            fd = (_surrogate_loss(xp, g, wt, a, dy, rotate) - _surrogate_loss(xm, g, wt, a, dy, rotate)) / (
+                float(xp[m, j]) - float(xm[m, j]))
+            assert abs(fd - dx[m, j]) <= 1e-5 * (1.0 + abs(dx[m, j])), (m, j, fd, dx[m, j])
+    if with_gain:
+        for k in range(K):
+            gp, gm = g.copy(), g.copy()
+            gp[k] += h
+            gm[k] -= h
+            fd = (_surrogate_loss(x, gp, wt, a, dy, rotate) - _surrogate_loss(x, gm, wt, a, dy, rotate)) / (
+                float(gp[k]) - float(gm[k]))
+            assert abs(fd - dg[k]) <= 1e-5 * (1.0 + abs(dg[k])), (k, fd, dg[k])
+    else:
+        assert dg is None
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_backward_one_hot_closed_forms(bits):
+    x, g, wt, alpha, _ = _bwd_case(7, M=4, K=32, N=6)
+    a = oracle.weight_scale(alpha)
+    fw = oracle.forward(x, wt, alpha, bits, g=g)
+    m0, n0 = 2, 3
+    dy = np.zeros((4, 6), np.float32)
+    dy[m0, n0] = 1.0
+    dx, dw, dg, dxh = oracle.backward(x, g, fw["q"], fw["d"], wt, alpha, dy, want_dxh=True)
+    # weight gradient: row n0 is the quantised activations of token m0, the rest zero
+    ref = np.zeros_like(dw)
+    ref[n0] = fw["q"][m0].astype(np.float64) * fw["d"][m0]
+    assert np.array_equal(dw, ref)
+    # gradient at the quantiser input: a * W_t[n0] in row m0 only
+    ref = np.zeros_like(dxh)
+    ref[m0] = a * wt[n0].astype(np.float64)
+    assert np.array_equal(dxh, ref)
+    # other tokens get no input gradient
+    assert np.all(dx[[0, 1, 3]] == 0.0)
+    # linearity in dy
+    rng = np.random.default_rng(3)
+    d1 = rng.normal(size=(4, 6)).astype(np.float32)
+    d2 = rng.normal(size=(4, 6)).astype(np.float32)
+    r1 = oracle.backward(x, g, fw["q"], fw["d"], wt, alpha, d1)
+    r2 = oracle.backward(x, g, fw["q"], fw["d"], wt, alpha, d2)
+    r12 = oracle.backward(x, g, fw["q"], fw["d"], wt, alpha, (d1.astype(np.float64) + d2).astype(np.float32))
+    s12 = (d1.astype(np.float64) + d2).astype(np.float32).astype(np.float64)
+    if np.array_equal(s12, d1.astype(np.float64) + d2.astype(np.float64)):
+        for i in range(3):
+            np.testing.assert_allclose(r12[i], r1[i] + r2[i], rtol=1e-12, atol=1e-12)
+
+
+def test_backward_rmsnorm_and_rotation_invariants():
+    # Without a gain: sum_j x_j dx_j = (eps / r^2) <du, u> per token (RMSNorm is
+    # scale invariant up to eps), and the rotation preserves the norm of the
+    # gradient it carries: |du| = |dxh|.
+    rng = np.random.default_rng(9)
+    M, K, N = 5, 64, 7
+    x = rng.normal(size=(M, K)).astype(np.float32) * 0.01        # small rows: eps matters
+    w = rng.normal(0, 0.02, size=(N, K)).astype(np.float32)
+    wt, alpha = oracle.quantize_weights(w)
+    dy = rng.normal(size=(M, N)).astype(np.float32)
+    fw = oracle.forward(x, wt, alpha, 4)
+    dx, dw, dg, dxh = oracle.backward(x, None, fw["q"], fw["d"], wt, alpha, dy, want_dxh=True)
+    u = oracle.rmsnorm(x)
+    du = oracle.hadamard_rotate(dxh)
+    for m in range(M):
+        ms = np.mean(x[m].astype(np.float64) ** 2)
+        r2 = ms + 1e-6
+        lhs = float(np.dot(x[m].astype(np.float64), dx[m]))
+        rhs = 1e-6 / r2 * float(np.dot(du[m], u[m]))
+        assert abs(lhs - rhs) <= 1e-9 * (1 + abs(rhs)) + 1e-12 * np.abs(dx[m]).sum(), (m, lhs, rhs)
+        np.testing.assert_allclose(np.linalg.norm(du[m]), np.linalg.norm(dxh[m]), rtol=1e-12)

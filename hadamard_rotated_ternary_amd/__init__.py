@@ -19,6 +19,7 @@ HEADERS = [os.path.join(_HERE, "..", "include", h) for h in ("hbl.h", "hbl_attn.
 
 HBL_F32, HBL_BF16 = 0, 1
 OP_QUANTIZE_WEIGHTS, OP_MATMUL, OP_QUANTIZE_WEIGHTS_ROTATED, OP_FORWARD_INT4, OP_FORWARD_INT8 = 0, 1, 2, 4, 8
+OP_BACKWARD = 16
 STATUS = {0: "HBL_OK", 1: "HBL_ERR_NULL", 2: "HBL_ERR_SHAPE", 3: "HBL_ERR_DTYPE", 4: "HBL_ERR_ALIGN",
           5: "HBL_ERR_WORKSPACE", 6: "HBL_ERR_LAUNCH", 7: "HBL_ERR_DEVICE"}
 
@@ -45,6 +46,8 @@ SIGNATURES = {
     "hbl_bitlinear_forward": ([P, I, P, P, P, I64, I64, I64, I, P, I, P, SZ, P], I),
     "hbl_quantize_act_unrotated": ([P, I, P, I64, I64, I, P, P, P], I),
     "hbl_quantize_weights_rotated": ([P, I64, I64, P, P, P, SZ, P], I),
+    "hbl_backward_weights": ([P, I64, I64, P, P], I),
+    "hbl_backward": ([P, I, P, P, I, P, P, P, P, I64, I64, I64, I, P, I, P, P, P, SZ, P], I),
     "hbl_quantize_heads": ([P, I64, I64, I, P, P, P], I),
     "hbl_dequantize_heads": ([P, P, I64, I64, I, P, I, P], I),
     "hbl_kv_cache_append": ([P, P, I64, I64, I64, I64, I, P, I64, P, P, P, P, P], I),
@@ -223,6 +226,38 @@ def unpack_weights(w_packed: torch.Tensor, K: int) -> torch.Tensor:
     wt = torch.empty((N, K), dtype=torch.int8, device=w_packed.device)
     _call("hbl_unpack_weights", _ptr(w_packed), N, K, _ptr(wt), _stream())
     return wt
+
+
+# ----------------------------------------------------------------- backward
+
+def backward_weights(w_packed: torch.Tensor, K: int) -> torch.Tensor:
+    """Packed ternary weights [N][K/4] -> W_t^T as bf16 [K][N] (once per update)."""
+    _dev(w_packed, "w_packed")
+    N = w_packed.shape[0]
+    wbt = torch.empty((K, N), dtype=torch.bfloat16, device=w_packed.device)
+    _call("hbl_backward_weights", _ptr(w_packed), N, K, _ptr(wbt), _stream())
+    return wbt
+
+
+def backward(x, gain, codes, bits, d, w_bf16_t, w_alpha, dy, rotate=True, dx_dtype=None, want_dgain=None,
+             workspace=None):
+    """Straight-through backward: returns (dx [M][K], dw fp32 [N][K], dgain fp32 [K] or None)."""
+    for t, n in ((x, "x"), (codes, "codes"), (d, "d"), (w_bf16_t, "w_bf16_t"), (w_alpha, "w_alpha"), (dy, "dy")):
+        _dev(t, n)
+    if dy.dtype != torch.bfloat16:
+        raise TypeError("dy must be bfloat16")
+    M, K = x.shape
+    N = dy.shape[1]
+    dx_dtype = x.dtype if dx_dtype is None else dx_dtype
+    dx = torch.empty((M, K), dtype=dx_dtype, device=x.device)
+    dw = torch.empty((N, K), dtype=torch.float32, device=x.device)
+    want = gain is not None if want_dgain is None else want_dgain
+    dg = torch.empty(K, dtype=torch.float32, device=x.device) if want else None
+    ws = _workspace(workspace_bytes(OP_BACKWARD, M, K, N), x.device, workspace)
+    _call("hbl_backward", _ptr(x), _dtype_code(x.dtype), _ptr(gain), _ptr(codes), bits, _ptr(d), _ptr(w_bf16_t),
+          _ptr(w_alpha), _ptr(dy), M, K, N, int(bool(rotate)), _ptr(dx), _dtype_code(dx_dtype), _ptr(dw), _ptr(dg),
+          _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    return dx, dw, dg
 
 
 # ------------------------------------------------------- low-bit attention states

@@ -1,0 +1,440 @@
+// Backward pass of H-BitLinear with the straight-through estimator.
+//
+// QbitAI article on BitNet v2, section 引入H-BitLinear模块 (training): the
+// quantisers' non-differentiable functions are bypassed and the gradient is
+// transformed with the Hadamard matrix, whose orthogonality makes the
+// transposed transform the transform itself.  With the forward
+// y = xh . Wh^T (xh = q * d per token, Wh = W_t * a):
+//   dxh = dy . Wh                      (bf16 MFMA on exact ternary values)
+//   du  = H_K dxh / sqrt(K)             (the forward's FWHT machinery)
+//   dx  = RMSNorm backward of du        (fused with the transform)
+//   dg  = sum over tokens of du * x / r
+//   dW  = dy^T . xh                     (bf16 MFMA over the tokens)
+// Both products run as one bf16 "NT" kernel (both operands stored with the
+// contraction index contiguous): the weights once per update as W_t^T in
+// bf16, and dy and xh transposed token-last for the weight gradient.
+#include "fwht.h"
+#include "launch.h"
+#include "mma.h"
+
+namespace hbl {
+namespace {
+
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// Ternary weights -> W_t^T as bf16 [K][N] (values -1, 0, +1; the scale a is
+// applied in the product's epilogue).  One thread per 8 consecutive n of one
+// k: the packed code of (n, k) is field (k % 16) / 4 of byte k % 4 of word
+// k / 16 of row n.
+__global__ __launch_bounds__(256) void wbt_kernel(const uint8_t* __restrict__ wpack, int N, int K,
+                                                  uint16_t* __restrict__ wbt) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int ng = N / 8;
+  if (t >= (int64_t)K * ng) return;
+  const int k = (int)(t / ng), n0 = (int)(t % ng) * 8;
+  const int byte = (k >> 4) * 4 + (k & 3), sh = 2 * ((k & 15) >> 2);
+  uint32_t o[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t h = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t c = (wpack[(size_t)(n0 + 2 * p + e) * (K / 4) + byte] >> sh) & 3u;
+      const uint32_t bf = (c & 1u) ? (0x3F80u | ((c & 2u) << 14)) : 0u;   // 01 -> +1, 11 -> -1, 00 -> 0
+      h |= bf << (16 * e);
+    }
+    o[p] = h;
+  }
+  *reinterpret_cast<uint4*>(wbt + (size_t)k * N + n0) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Token-last copies for the weight gradient, through 64 x 64 LDS tiles:
+//   dyT[n][m] = dy[m][n]               (bf16)
+//   xhT[k][m] = bf16(q[m][k] * d[m])    (codes INT8 [M][K] or INT4 [M][K/2])
+// m runs to Mp (a multiple of 64); columns past M are zero.
+template <int KIND>   // 0: dy (bf16), 8: INT8 codes, 4: INT4 codes
+__global__ __launch_bounds__(256) void tr_kernel(const void* __restrict__ src, const float* __restrict__ dscale,
+                                                 int M, int C, int Mp, uint16_t* __restrict__ dst) {
+  __shared__ uint16_t tile[64][66];
+  const int c0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  // read: rows m0 + ty + 4i, column c0 + tx
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = m0 + ty + 4 * i, c = c0 + tx;
+    uint16_t v = 0;
+    if (m < M && c < C) {
+      if constexpr (KIND == 0) {
+        v = static_cast<const uint16_t*>(src)[(size_t)m * C + c];
+      } else {
+        int q;
+        if constexpr (KIND == 8) {
+          q = static_cast<const int8_t*>(src)[(size_t)m * C + c];
+        } else {
+          // INT4: one LE word per 8 k; code of k0 + 4j + i at bits 8i + 4j
+          const uint8_t byte = static_cast<const uint8_t*>(src)[(size_t)m * (C / 2) + (c >> 3) * 4 + (c & 3)];
+          q = ((int)(((byte >> (4 * ((c & 7) >> 2))) & 15u) << 28)) >> 28;
+        }
+        v = f32_to_bf16((float)q * dscale[m]);
+      }
+    }
+    tile[ty + 4 * i][tx] = v;
+  }
+  __syncthreads();
+  // write: rows c0 + ty + 4i of dst, columns m0 + tx
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = c0 + ty + 4 * i, m = m0 + tx;
+    if (c < C && m < Mp) dst[(size_t)c * Mp + m] = tile[tx][ty + 4 * i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 NT product: out[i][j] = s * sum_c A[i][c] B[j][c], fp32 out.
+// 256 x 256 tile per 4-wave workgroup (2 x 2 waves of 128 x 128, each 4 x 4
+// v_mfma_f32_32x32x16_bf16 tiles), 32 c per stage in a three-deep LDS ring
+// filled by global_load_lds_dwordx4 (each stage requested two ahead).  Rows
+// of 64 bytes, 16-byte units XOR-swizzled so the fragment reads (16 lanes:
+// rows r..r+15 of one unit column) and the copies hit distinct banks.
+constexpr int GT = 256, GBK = 32, GROW = GBK * 2, GUNITS = GROW / 16;
+constexpr int G_A_STAGE = GT * GROW, G_STAGE = 2 * G_A_STAGE;
+HBL_DEV int gswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+__global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A,
+                                                              const uint16_t* __restrict__ B,
+                                                              const float* __restrict__ sptr, float* __restrict__ out,
+                                                              int I, int J, int Cn, int tiles_i, int tiles_j) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * G_STAGE];
+  const int bid = blockIdx.x, total = tiles_i * tiles_j;
+  // XCD-aware order (8 consecutive ids go to 8 XCDs): contiguous runs of
+  // logical tiles per XCD, walked 4 tile-rows at a time.
+  const int logical = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
+  constexpr int GM = 4;
+  const int per_group = GM * tiles_j;
+  const int first_i = (logical / per_group) * GM;
+  const int gm = min(tiles_i - first_i, GM);
+  const int in_g = logical % per_group;
+  const int i0 = (first_i + in_g % gm) * GT;
+  const int j0 = (in_g / gm) * GT;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // Per stage: A 16 KiB + B 16 KiB = 32 copies of 1 KiB; 4 A + 4 B per wave.
+  const uint16_t* a_src[4];
+  const uint16_t* b_src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int P = (j * 4 + wave) * 64 + lane, row = P / GUNITS, u = (P % GUNITS) ^ gswz(row);
+    a_src[j] = A + (size_t)min(i0 + row, I - 1) * Cn + 8 * u;
+    b_src[j] = B + (size_t)min(j0 + row, J - 1) * Cn + 8 * u;
+  }
+  auto dma = [&](int kt, int buf) {
+    uint8_t* base = smem + buf * G_STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_copy16(a_src[j] + (size_t)kt * GBK, base + (j * 4 + wave) * 1024);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_copy16(b_src[j] + (size_t)kt * GBK, base + G_A_STAGE + (j * 4 + wave) * 1024);
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+  auto compute = [&](int buf) {
+    const uint8_t* sa = smem + buf * G_STAGE;
+    const uint8_t* sb = sa + G_A_STAGE;
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+      bf8v af[4], bfr[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int row = wi * 128 + rb * 32 + l32;
+        af[rb] = *reinterpret_cast<const bf8v*>(sa + row * GROW + 16 * ((2 * ks + g) ^ gswz(row)));
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int row = wj * 128 + cb * 32 + l32;
+        bfr[cb] = *reinterpret_cast<const bf8v*>(sb + row * GROW + 16 * ((2 * ks + g) ^ gswz(row)));
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bfr[cb], acc[rb][cb], 0, 0, 0);
+    }
+  };
+
+  // Stage kt lives in LDS buffer kt % 3 (as in the int8 prefill product).
+  constexpr int NL = 8;
+  const int KT = Cn / GBK;
+  auto phase = [&](int kt, int buf) {
+    if (kt + 1 < KT) wait_vmcnt<NL>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < KT) dma(kt + 2, buf == 0 ? 2 : buf - 1);
+    compute(buf);
+  };
+  dma(0, 0);
+  if (KT > 1) dma(1, 1);
+  for (int kt = 0; kt < KT; kt += 3) {
+    phase(kt, 0);
+    if (kt + 1 < KT) phase(kt + 1, 1);
+    if (kt + 2 < KT) phase(kt + 2, 2);
+  }
+
+  // Epilogue: lane l / register r of a 32 x 32 block hold row
+  // 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  const float s = sptr ? fmaxf(sptr[0], kEpsQ) : 1.0f;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i0 + wi * 128 + rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int col = j0 + wj * 128 + cb * 32 + l32;
+        if (row < I && col < J) out[(size_t)row * J + col] = acc[rb][cb][r] * s;
+      }
+}
+
+// ---------------------------------------------------------------------------
+// Fused transform + RMSNorm backward, one token per T threads (persistent
+// over tokens like the forward's prep): dxh (fp32, pass-0 dealing: 8
+// contiguous features per group) -> FWHT -> back to the pass-0 dealing ->
+// du = (.) / sqrt(K); with x and g in the same dealing:
+//   r = sqrt(mean x^2 + eps), S = sum du g x,
+//   dx = g du / r - x S / (K r^3),   dg partial += du x / r.
+// Without the rotation du = dxh.  dg partials: one row of K per (workgroup,
+// token slot), summed by dg_reduce_kernel in a fixed order.
+template <int LOGK, int LOGE, int P2, int PA, int PB>
+HBL_DEV void exchange_to(float (&v)[1 << LOGE], float* region, int tau) {
+  using A = Pass<LOGK, LOGE, PA>;
+  using Bn = Pass<LOGK, LOGE, PB>;
+  constexpr int E = 1 << LOGE;
+  const int wbase = pad<P2>(A::thr_idx(tau));
+#pragma unroll
+  for (int r = 0; r < E; ++r) region[wbase + pad<P2>(A::reg_idx(r))] = v[r];
+  __syncthreads();
+  const int rbase = pad<P2>(Bn::thr_idx(tau));
+#pragma unroll
+  for (int r = 0; r < E; ++r) v[r] = region[rbase + pad<P2>(Bn::reg_idx(r))];
+  __syncthreads();
+}
+
+constexpr int bwd_wg(int logk, int loge) { return (1 << (logk - loge)) < 64 ? 64 : (1 << (logk - loge)); }
+
+template <int LOGK, int LOGE, int P2, bool XBF16, bool DXBF16, bool ROT>
+__global__ __launch_bounds__(bwd_wg(LOGK, LOGE)) void bwd_prep_kernel(
+    const float* __restrict__ dxh, const void* __restrict__ x, const float* __restrict__ gain, int M,
+    void* __restrict__ dx, float* __restrict__ dgpart) {
+  using C = PrepCfg<LOGK, LOGE, P2>;
+  using P0 = Pass<LOGK, LOGE, 0>;
+  constexpr int K = C::K, E = C::E, T = C::T;
+  __shared__ __attribute__((aligned(16))) float lds[C::REGION * C::TPB];
+  __shared__ float red[32];
+  const int tok = threadIdx.x / T, tau = threadIdx.x % T;
+  float* region = lds + tok * C::REGION;
+  const int stride = gridDim.x * C::TPB;
+  const int first = blockIdx.x * C::TPB;
+  const int iters = first < M ? (M - first + stride - 1) / stride : 0;   // uniform over the workgroup
+  const int base0 = P0::thr_idx(tau);
+
+  // gain in the pass-0 dealing, read from L1/L2 where needed
+  auto gain8 = [&](int gi, float (&gg)[8]) {
+    if (gain) {
+      const float4* p = reinterpret_cast<const float4*>(gain + base0 + P0::reg_idx(8 * gi));
+      const float4 a = p[0], b = p[1];
+      gg[0] = a.x; gg[1] = a.y; gg[2] = a.z; gg[3] = a.w; gg[4] = b.x; gg[5] = b.y; gg[6] = b.z; gg[7] = b.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gg[e] = 1.0f;
+    }
+  };
+  float dg[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) dg[r] = 0.0f;
+
+  for (int it = 0; it < iters; ++it) {
+    const int m = first + tok + it * stride;
+    const bool valid = m < M;
+    const int mm = valid ? m : M - 1;
+    float v[E];
+#pragma unroll
+    for (int gi = 0; gi < E / 8; ++gi) {
+      const int idx = base0 + P0::reg_idx(8 * gi);
+      const float4* p = reinterpret_cast<const float4*>(dxh + (size_t)mm * K + idx);
+      const float4 a = p[0], b = p[1];
+      v[8 * gi + 0] = a.x; v[8 * gi + 1] = a.y; v[8 * gi + 2] = a.z; v[8 * gi + 3] = a.w;
+      v[8 * gi + 4] = b.x; v[8 * gi + 5] = b.y; v[8 * gi + 6] = b.z; v[8 * gi + 7] = b.w;
+    }
+    if constexpr (ROT) {
+      run_passes<LOGK, LOGE, P2, 0>(v, region, tau);
+      if constexpr (C::NP > 1) exchange_to<LOGK, LOGE, P2, C::NP - 1, 0>(v, region, tau);
+      const float rs = 1.0f / sqrtf((float)K);
+#pragma unroll
+      for (int r = 0; r < E; ++r) v[r] *= rs;
+    }
+    // x of this token in the same dealing (bf16 kept packed: E/2 registers)
+    RawX<E, XBF16> raw;
+#pragma unroll
+    for (int gi = 0; gi < E / 8; ++gi) {
+      const int idx = base0 + P0::reg_idx(8 * gi);
+      if constexpr (XBF16) {
+        raw.u[gi] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (size_t)mm * K + idx);
+      } else {
+        const uint4* q = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + (size_t)mm * K + idx);
+        raw.u[2 * gi] = q[0];
+        raw.u[2 * gi + 1] = q[1];
+      }
+    }
+    auto x8 = [&](int gi, float (&xx)[8]) {
+      if constexpr (XBF16) {
+        const uint4 w = raw.u[gi];
+        xx[0] = bf16_lo(w.x); xx[1] = bf16_hi(w.x); xx[2] = bf16_lo(w.y); xx[3] = bf16_hi(w.y);
+        xx[4] = bf16_lo(w.z); xx[5] = bf16_hi(w.z); xx[6] = bf16_lo(w.w); xx[7] = bf16_hi(w.w);
+      } else {
+        const uint4 a = raw.u[2 * gi], b = raw.u[2 * gi + 1];
+        xx[0] = __uint_as_float(a.x); xx[1] = __uint_as_float(a.y); xx[2] = __uint_as_float(a.z);
+        xx[3] = __uint_as_float(a.w); xx[4] = __uint_as_float(b.x); xx[5] = __uint_as_float(b.y);
+        xx[6] = __uint_as_float(b.z); xx[7] = __uint_as_float(b.w);
+      }
+    };
+    float ss = 0.0f, sd = 0.0f;
+#pragma unroll
+    for (int gi = 0; gi < E / 8; ++gi) {
+      float xx[8], gg[8];
+      x8(gi, xx);
+      gain8(gi, gg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ss = __builtin_fmaf(xx[e], xx[e], ss);
+        sd = __builtin_fmaf(v[8 * gi + e] * gg[e], xx[e], sd);
+      }
+    }
+    token_reduce2<T, false>(ss, sd, red);
+    const float rr = sqrtf(ss * (1.0f / K) + kEpsNorm);
+    const float ir = 1.0f / rr;
+    const float cx = sd * ir * ir * ir * (1.0f / K);
+#pragma unroll
+    for (int gi = 0; gi < E / 8; ++gi) {
+      float xx[8], gg[8], o[8];
+      x8(gi, xx);
+      gain8(gi, gg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[e] = gg[e] * v[8 * gi + e] * ir - xx[e] * cx;
+        if (valid) dg[8 * gi + e] = __builtin_fmaf(v[8 * gi + e] * xx[e], ir, dg[8 * gi + e]);
+      }
+      if (valid) {
+        const int idx = base0 + P0::reg_idx(8 * gi);
+        if constexpr (DXBF16) {
+          uint4 w;
+          w.x = f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+          w.y = f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+          w.z = f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+          w.w = f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dx) + (size_t)m * K + idx) = w;
+        } else {
+          float4* q = reinterpret_cast<float4*>(static_cast<float*>(dx) + (size_t)m * K + idx);
+          q[0] = make_float4(o[0], o[1], o[2], o[3]);
+          q[1] = make_float4(o[4], o[5], o[6], o[7]);
+        }
+      }
+    }
+  }
+  if (dgpart) {
+    float* row = dgpart + ((size_t)blockIdx.x * C::TPB + tok) * K;
+#pragma unroll
+    for (int gi = 0; gi < E / 8; ++gi) {
+      const int idx = base0 + P0::reg_idx(8 * gi);
+      float4* q = reinterpret_cast<float4*>(row + idx);
+      q[0] = make_float4(dg[8 * gi + 0], dg[8 * gi + 1], dg[8 * gi + 2], dg[8 * gi + 3]);
+      q[1] = make_float4(dg[8 * gi + 4], dg[8 * gi + 5], dg[8 * gi + 6], dg[8 * gi + 7]);
+    }
+  }
+}
+
+// dg[k] = sum of the partial rows, in row order.
+__global__ __launch_bounds__(256) void dg_reduce_kernel(const float* __restrict__ part, int rows, int K,
+                                                        float* __restrict__ dg) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  float s = 0.0f;
+  for (int i = 0; i < rows; ++i) s += part[(size_t)i * K + k];
+  dg[k] = s;
+}
+
+// Transform configurations: one token of K features over T threads x E registers.
+template <bool XBF16, bool DXBF16, bool ROT>
+hipError_t launch_bwd_prep_t(const BwdArgs& a, int grid, float* dgpart) {
+#define HBL_BP(LK, LE, P2)                                                                                   \
+  case LK:                                                                                                   \
+    hipLaunchKernelGGL((bwd_prep_kernel<LK, LE, P2, XBF16, DXBF16, ROT>), dim3(grid),                       \
+                       dim3(PrepCfg<LK, LE, P2>::WG), 0, a.stream, a.dxh, a.x, a.gain, a.M, a.dx, dgpart); \
+    break;
+  switch (a.logk) {
+    HBL_BP(8, 4, 6) HBL_BP(9, 5, 6) HBL_BP(10, 5, 7) HBL_BP(11, 6, 7) HBL_BP(12, 6, 8) HBL_BP(13, 6, 8)
+    HBL_BP(14, 6, 9)
+    default: return hipErrorInvalidValue;
+  }
+#undef HBL_BP
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int bwd_prep_tpb(int logk) {
+  switch (logk) {
+    case 8: return PrepCfg<8, 4, 6>::TPB;
+    case 9: return PrepCfg<9, 5, 6>::TPB;
+    case 10: return PrepCfg<10, 5, 7>::TPB;
+    case 11: return PrepCfg<11, 6, 7>::TPB;
+    case 12: return PrepCfg<12, 6, 8>::TPB;
+    case 13: return PrepCfg<13, 6, 8>::TPB;
+    case 14: return PrepCfg<14, 6, 9>::TPB;
+    default: return 0;
+  }
+}
+
+hipError_t launch_wbt(const uint8_t* wpack, int N, int K, uint16_t* wbt, hipStream_t stream) {
+  const int64_t threads = (int64_t)K * (N / 8);
+  hipLaunchKernelGGL(wbt_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, wpack, N, K, wbt);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_tokens(int kind, const void* src, const float* dscale, int M, int C, int Mp,
+                                   uint16_t* dst, hipStream_t stream) {
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(Mp / 64));
+  if (kind == 0) hipLaunchKernelGGL(tr_kernel<0>, grid, dim3(256), 0, stream, src, dscale, M, C, Mp, dst);
+  else if (kind == 8) hipLaunchKernelGGL(tr_kernel<8>, grid, dim3(256), 0, stream, src, dscale, M, C, Mp, dst);
+  else hipLaunchKernelGGL(tr_kernel<4>, grid, dim3(256), 0, stream, src, dscale, M, C, Mp, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_nt(const uint16_t* A, const uint16_t* B, const float* scale, float* out, int I, int J,
+                               int Cn, hipStream_t stream) {
+  const int ti = (I + GT - 1) / GT, tj = (J + GT - 1) / GT;
+  hipLaunchKernelGGL(gemm_bf16_nt_kernel, dim3(ti * tj), dim3(256), 0, stream, A, B, scale, out, I, J, Cn, ti, tj);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const BwdArgs& a, int grid, float* dgpart) {
+#define HBL_BPX(XB, DB, R) \
+  if (a.x_bf16 == XB && a.dx_bf16 == DB && a.rotate == R) return launch_bwd_prep_t<XB, DB, R>(a, grid, dgpart);
+  HBL_BPX(true, true, true) HBL_BPX(true, false, true) HBL_BPX(false, true, true) HBL_BPX(false, false, true)
+  HBL_BPX(true, true, false) HBL_BPX(true, false, false) HBL_BPX(false, true, false) HBL_BPX(false, false, false)
+#undef HBL_BPX
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dg_reduce(const float* part, int rows, int K, float* dg, hipStream_t stream) {
+  hipLaunchKernelGGL(dg_reduce_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream, part, rows, K, dg);
+  return hipGetLastError();
+}
+
+}  // namespace hbl

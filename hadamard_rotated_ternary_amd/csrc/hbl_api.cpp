@@ -63,6 +63,29 @@ size_t scales_bytes(int64_t M) { return align256((size_t)M * 4); }
 
 hbl_status launched(hipError_t e) { return e == hipSuccess ? HBL_OK : HBL_ERR_LAUNCH; }
 
+// Backward workspace: [dxh fp32 M*K][dy^T bf16 N*Mp][xh^T bf16 K*Mp][gain partials fp32 rows*K],
+// Mp = M rounded up to 64 (zero columns).  The transform kernel runs on a
+// fixed grid of up to 512 workgroups (two per CU of a 256-CU part).
+struct BwdLayout {
+  int64_t Mp;
+  int grid, rows;
+  size_t dxh, dyt, xht, dgp, total;
+};
+BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N) {
+  BwdLayout L{};
+  L.Mp = (M + 63) / 64 * 64;
+  const int tpb = hbl::bwd_prep_tpb(log2_exact(K));
+  const int64_t need = tpb > 0 ? (M + tpb - 1) / tpb : 0;
+  L.grid = (int)(need < 512 ? need : 512);
+  L.rows = L.grid * tpb;
+  L.dxh = align256((size_t)M * K * 4);
+  L.dyt = align256((size_t)N * L.Mp * 2);
+  L.xht = align256((size_t)K * L.Mp * 2);
+  L.dgp = align256((size_t)L.rows * K * 4);
+  L.total = L.dxh + L.dyt + L.xht + L.dgp;
+  return L;
+}
+
 // H-BitLinear forward (rotate) or BitLinear without the transform.
 hbl_status forward(int bits, bool rotate, const void* x, hbl_dtype x_dtype, const float* gain,
                    const uint8_t* w_packed, const float* w_alpha, int64_t M, int64_t K, int64_t N, void* y,
@@ -129,6 +152,7 @@ size_t hbl_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
     case HBL_OP_QUANTIZE_WEIGHTS: return align256((size_t)N * 8);
     case HBL_OP_QUANTIZE_WEIGHTS_ROTATED: return align256((size_t)N * 8) + align256((size_t)N * K * 4);
     case HBL_OP_MATMUL: return align256(hbl::gemm_workspace_bytes(M, K, N));
+    case HBL_OP_BACKWARD: return M > 0 && log2_exact(K) > 0 ? bwd_layout(M, K, N).total : 0;
     case HBL_OP_FORWARD_INT8:
     case HBL_OP_FORWARD_INT4: {
       const int bits = op == HBL_OP_FORWARD_INT8 ? 8 : 4;
@@ -362,6 +386,59 @@ hbl_status hbl_attention_decode(const void* q, int q_bits, const uint8_t* k_code
   a.ct = ct; a.nchunk = nchunk; a.part = static_cast<float*>(workspace); a.out = out;
   a.out_bf16 = out_dtype == HBL_BF16; a.stream = stream;
   return launched(hbl::launch_attention_decode(a));
+}
+
+
+// ---------------------------------------------------------------------------
+// Backward pass.
+
+hbl_status hbl_backward_weights(const uint8_t* w_packed, int64_t N, int64_t K, void* w_bf16_t, hipStream_t stream) {
+  if (hbl_status st = check_shape(0, K, N)) return st;
+  if (N % 32 != 0) return HBL_ERR_SHAPE;
+  if (!w_packed || !w_bf16_t) return HBL_ERR_NULL;
+  if (!aligned16(w_packed) || !aligned16(w_bf16_t)) return HBL_ERR_ALIGN;
+  if (hbl_status st = check_device()) return st;
+  return launched(hbl::launch_wbt(w_packed, (int)N, (int)K, static_cast<uint16_t*>(w_bf16_t), stream));
+}
+
+hbl_status hbl_backward(const void* x, hbl_dtype x_dtype, const float* gain, const void* codes, int bits,
+                        const float* d, const void* w_bf16_t, const float* w_alpha, const void* dy, int64_t M,
+                        int64_t K, int64_t N, int rotate, void* dx, hbl_dtype dx_dtype, float* dw, float* dgain,
+                        void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(x_dtype) || !valid_dtype(dx_dtype) || (bits != 8 && bits != 4)) return HBL_ERR_DTYPE;
+  if (hbl_status st = check_shape(M, K, N)) return st;
+  if (M < 1 || N % 32 != 0) return HBL_ERR_SHAPE;
+  if (!x || !codes || !d || !w_bf16_t || !w_alpha || !dy || !dx || !dw || !workspace || (dgain && !gain))
+    return HBL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(d) || !aligned16(w_bf16_t) || !aligned16(w_alpha) ||
+      !aligned16(dy) || !aligned16(dx) || !aligned16(dw) || !aligned16(workspace) || (gain && !aligned16(gain)) ||
+      (dgain && !aligned16(dgain)))
+    return HBL_ERR_ALIGN;
+  const BwdLayout L = bwd_layout(M, K, N);
+  if (ws_bytes < L.total) return HBL_ERR_WORKSPACE;
+  if (hbl_status st = check_device()) return st;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* dxh = reinterpret_cast<float*>(ws);
+  uint16_t* dyt = reinterpret_cast<uint16_t*>(ws + L.dxh);
+  uint16_t* xht = reinterpret_cast<uint16_t*>(ws + L.dxh + L.dyt);
+  float* dgp = reinterpret_cast<float*>(ws + L.dxh + L.dyt + L.xht);
+  // input gradient: dxh = dy . (W_t^T)^T * a, then transform + RMSNorm backward
+  if (hipError_t e = hbl::launch_gemm_bf16_nt(static_cast<const uint16_t*>(dy),
+                                              static_cast<const uint16_t*>(w_bf16_t), w_alpha, dxh, (int)M, (int)K,
+                                              (int)N, stream))
+    return launched(e);
+  hbl::BwdArgs b{};
+  b.dxh = dxh; b.x = x; b.x_bf16 = x_dtype == HBL_BF16; b.gain = gain; b.M = (int)M; b.logk = log2_exact(K);
+  b.dx = dx; b.dx_bf16 = dx_dtype == HBL_BF16; b.rotate = rotate != 0; b.stream = stream;
+  if (hipError_t e = hbl::launch_bwd_prep(b, L.grid, dgain ? dgp : nullptr)) return launched(e);
+  if (dgain)
+    if (hipError_t e = hbl::launch_dg_reduce(dgp, L.rows, (int)K, dgain, stream)) return launched(e);
+  // weight gradient: dw = dy^T . xh over the tokens (token-last copies)
+  if (hipError_t e = hbl::launch_transpose_tokens(0, dy, nullptr, (int)M, (int)N, (int)L.Mp, dyt, stream))
+    return launched(e);
+  if (hipError_t e = hbl::launch_transpose_tokens(bits, codes, d, (int)M, (int)K, (int)L.Mp, xht, stream))
+    return launched(e);
+  return launched(hbl::launch_gemm_bf16_nt(dyt, xht, nullptr, dw, (int)N, (int)K, (int)L.Mp, stream));
 }
 
 }  // extern "C"

@@ -115,7 +115,28 @@ bool heads_bits_supported(int bits);
 // enough chunks to reach that, in whole blocks of attn_block_tokens(d).
 int attn_block_tokens(int d);
 void attn_plan(int64_t B, int64_t Hq, int d, int64_t Tmax, int* ct, int* nchunk);
-int attn_part_stride(int d);
 hipError_t launch_attention_decode(const AttnArgs& a);
+
+// Backward pass (straight-through estimator).
+struct BwdArgs {
+  const float* dxh;       // [M][K] fp32: gradient at the quantiser input
+  const void* x;          // [M][K] the forward's input
+  bool x_bf16;
+  const float* gain;      // [K] or NULL
+  int M, logk;
+  void* dx;               // [M][K]
+  bool dx_bf16;
+  bool rotate;
+  hipStream_t stream;
+};
+int bwd_prep_tpb(int logk);
+hipError_t launch_wbt(const uint8_t* wpack, int N, int K, uint16_t* wbt, hipStream_t stream);
+hipError_t launch_transpose_tokens(int kind, const void* src, const float* dscale, int M, int C, int Mp,
+                                   uint16_t* dst, hipStream_t stream);
+hipError_t launch_gemm_bf16_nt(const uint16_t* A, const uint16_t* B, const float* scale, float* out, int I, int J,
+                               int Cn, hipStream_t stream);
+hipError_t launch_bwd_prep(const BwdArgs& a, int grid, float* dgpart);
+hipError_t launch_dg_reduce(const float* part, int rows, int K, float* dg, hipStream_t stream);
+int attn_part_stride(int d);
 
 }  // namespace hbl

@@ -90,7 +90,7 @@ enum { HBL_BITS_INT4 = 4, HBL_BITS_INT4_FP6 = 6, HBL_BITS_INT8 = 8 };
 
 /* Operation selector for hbl_workspace_bytes. */
 enum { HBL_OP_QUANTIZE_WEIGHTS = 0, HBL_OP_MATMUL = 1, HBL_OP_QUANTIZE_WEIGHTS_ROTATED = 2,
-       HBL_OP_FORWARD_INT4 = 4, HBL_OP_FORWARD_INT8 = 8 };
+       HBL_OP_FORWARD_INT4 = 4, HBL_OP_FORWARD_INT8 = 8, HBL_OP_BACKWARD = 16 };
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *hbl_status_string(hbl_status s);
@@ -227,6 +227,40 @@ hbl_status hbl_gemm_ternary(const void *codes, int bits, const uint8_t *w_packed
 /* Expand packed ternary weights to int8 [N][K] in {-1, 0, 1}. */
 hbl_status hbl_unpack_weights(const uint8_t *w_packed, int64_t N, int64_t K,
                               int8_t *w_t, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward pass (QbitAI article on BitNet v2, section 引入H-BitLinear模块,
+ * training paragraph): the straight-through estimator bypasses both
+ * quantisers, and the gradient goes through the transposed Hadamard
+ * transform, i.e. the transform itself (H symmetric, orthonormal after the
+ * 1/sqrt(K) scale).  With the forward y = xh . Wh^T, xh = q * d (the forward's
+ * codes and per-token scales), Wh = W_t * a:
+ *     dxh = dy . Wh;   du = H_K dxh / sqrt(K)  (du = dxh when rotate == 0);
+ *     dx  = g du / r - x (sum_i du_i g_i x_i) / (K r^3),  r = sqrt(mean x^2 + 1e-6);
+ *     dgain[k] = sum_m du[m][k] x[m][k] / r_m;     dw = dy^T . xh   (fp32 [N][K]).
+ * The HIP path multiplies bf16 operands on the bf16 matrix instruction with
+ * fp32 accumulation: dy and the ternary weights are exact in bf16, xh = q * d
+ * is rounded to bf16 (relative 2^-9) for the weight gradient.
+ */
+
+/* The weights of the input-gradient product: W_t^T as bf16 [K][N] (values
+ * -1, 0, +1; the scale alpha is applied inside hbl_backward).  Computed once
+ * per weight update from the packed ternary weights.  N % 32 == 0. */
+hbl_status hbl_backward_weights(const uint8_t *w_packed, int64_t N, int64_t K, void *w_bf16_t,
+                                hipStream_t stream);
+
+/* Backward of the layer.  x [M][K] (x_dtype) and gain [K] (or NULL) are the
+ * forward's input; codes/d the forward's activation codes (bits 8: int8
+ * [M][K]; bits 4: the INT4 format above) and per-token scales; w_bf16_t from
+ * hbl_backward_weights and w_alpha as in the forward; dy bf16 [M][N].
+ * Outputs dx [M][K] (dx_dtype), dw fp32 [N][K], dgain fp32 [K] (only with a
+ * gain; NULL to skip).  rotate = 1 for H-BitLinear, 0 for BitLinear.
+ * M >= 1, N % 32 == 0; workspace at least
+ * hbl_workspace_bytes(HBL_OP_BACKWARD, M, K, N) bytes. */
+hbl_status hbl_backward(const void *x, hbl_dtype x_dtype, const float *gain, const void *codes, int bits,
+                        const float *d, const void *w_bf16_t, const float *w_alpha, const void *dy,
+                        int64_t M, int64_t K, int64_t N, int rotate, void *dx, hbl_dtype dx_dtype,
+                        float *dw, float *dgain, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -53,41 +53,63 @@ __global__ __launch_bounds__(256) void wbt_kernel(const uint8_t* __restrict__ wp
 // Token-last copies for the weight gradient, through 64 x 64 LDS tiles:
 //   dyT[n][m] = dy[m][n]               (bf16)
 //   xhT[k][m] = bf16(q[m][k] * d[m])    (codes INT8 [M][K] or INT4 [M][K/2])
-// m runs to Mp (a multiple of 64); columns past M are zero.
+// m runs to Mp (a multiple of 64); columns past M are zero.  Loads read 16
+// bytes per lane along a source row; stores write 16 bytes (8 tokens) per
+// lane along a destination row.  C % 8 == 0 (C is N or K here).
 template <int KIND>   // 0: dy (bf16), 8: INT8 codes, 4: INT4 codes
 __global__ __launch_bounds__(256) void tr_kernel(const void* __restrict__ src, const float* __restrict__ dscale,
                                                  int M, int C, int Mp, uint16_t* __restrict__ dst) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ uint16_t tile[64][72];   // [m][c], rows padded to 144 bytes
   const int c0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  // read: rows m0 + ty + 4i, column c0 + tx
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int m = m0 + ty + 4 * i, c = c0 + tx;
-    uint16_t v = 0;
+  // load: 8 columns (16 bytes of bf16 / 8 bytes of int8 / 4 bytes of int4) per item
+  for (int it = threadIdx.x; it < 64 * 8; it += 256) {
+    const int mr = it >> 3, cg = (it & 7) * 8;
+    const int m = m0 + mr, c = c0 + cg;
+    uint16_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (m < M && c < C) {
       if constexpr (KIND == 0) {
-        v = static_cast<const uint16_t*>(src)[(size_t)m * C + c];
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (size_t)m * C + c);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[2 * e] = (uint16_t)w[e]; v[2 * e + 1] = (uint16_t)(w[e] >> 16); }
       } else {
-        int q;
+        const float dm = dscale[m];
+        int q[8];
         if constexpr (KIND == 8) {
-          q = static_cast<const int8_t*>(src)[(size_t)m * C + c];
+          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(src) + (size_t)m * C + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            q[e] = (int)(int8_t)(u.x >> (8 * e));
+            q[4 + e] = (int)(int8_t)(u.y >> (8 * e));
+          }
         } else {
           // INT4: one LE word per 8 k; code of k0 + 4j + i at bits 8i + 4j
-          const uint8_t byte = static_cast<const uint8_t*>(src)[(size_t)m * (C / 2) + (c >> 3) * 4 + (c & 3)];
-          q = ((int)(((byte >> (4 * ((c & 7) >> 2))) & 15u) << 28)) >> 28;
+          const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(src) +
+                                                                (size_t)m * (C / 2) + c / 2);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[e] = ((int)(((u >> (8 * (e & 3) + 4 * (e >> 2))) & 15u) << 28)) >> 28;
         }
-        v = f32_to_bf16((float)q * dscale[m]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16((float)q[e] * dm);
       }
     }
-    tile[ty + 4 * i][tx] = v;
+    uint4 pk;
+    pk.x = v[0] | ((uint32_t)v[1] << 16); pk.y = v[2] | ((uint32_t)v[3] << 16);
+    pk.z = v[4] | ((uint32_t)v[5] << 16); pk.w = v[6] | ((uint32_t)v[7] << 16);
+    *reinterpret_cast<uint4*>(&tile[mr][cg]) = pk;
   }
   __syncthreads();
-  // write: rows c0 + ty + 4i of dst, columns m0 + tx
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = c0 + ty + 4 * i, m = m0 + tx;
-    if (c < C && m < Mp) dst[(size_t)c * Mp + m] = tile[tx][ty + 4 * i];
+  // store: destination row c0 + cr, tokens m0 + mg .. +7
+  for (int it = threadIdx.x; it < 64 * 8; it += 256) {
+    const int cr = it >> 3, mg = (it & 7) * 8;
+    const int c = c0 + cr;
+    if (c >= C) continue;
+    uint4 pk;
+    pk.x = tile[mg + 0][cr] | ((uint32_t)tile[mg + 1][cr] << 16);
+    pk.y = tile[mg + 2][cr] | ((uint32_t)tile[mg + 3][cr] << 16);
+    pk.z = tile[mg + 4][cr] | ((uint32_t)tile[mg + 5][cr] << 16);
+    pk.w = tile[mg + 6][cr] | ((uint32_t)tile[mg + 7][cr] << 16);
+    *reinterpret_cast<uint4*>(dst + (size_t)c * Mp + m0 + mg) = pk;
   }
 }
 
@@ -359,14 +381,29 @@ __global__ __launch_bounds__(bwd_wg(LOGK, LOGE)) void bwd_prep_kernel(
   }
 }
 
-// dg[k] = sum of the partial rows, in row order.
+// dg[k] = sum of the partial rows in a fixed order: a workgroup owns 64
+// columns; its 4 waves sum interleaved row sets (8 independent loads in
+// flight per lane) and the 4 partial sums are added in wave order.
 __global__ __launch_bounds__(256) void dg_reduce_kernel(const float* __restrict__ part, int rows, int K,
                                                         float* __restrict__ dg) {
-  const int k = blockIdx.x * 256 + threadIdx.x;
-  if (k >= K) return;
+  __shared__ float ps[4][64];
+  const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int k = blockIdx.x * 64 + c;
   float s = 0.0f;
-  for (int i = 0; i < rows; ++i) s += part[(size_t)i * K + k];
-  dg[k] = s;
+  if (k < K) {
+    int i = w;
+    for (; i + 28 < rows; i += 32) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(i + 4 * u) * K + k];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; i < rows; i += 4) s += part[(size_t)i * K + k];
+  }
+  ps[w][c] = s;
+  __syncthreads();
+  if (w == 0 && k < K) dg[k] = ((ps[0][c] + ps[1][c]) + ps[2][c]) + ps[3][c];
 }
 
 // Transform configurations: one token of K features over T threads x E registers.
@@ -433,7 +470,7 @@ hipError_t launch_bwd_prep(const BwdArgs& a, int grid, float* dgpart) {
 }
 
 hipError_t launch_dg_reduce(const float* part, int rows, int K, float* dg, hipStream_t stream) {
-  hipLaunchKernelGGL(dg_reduce_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream, part, rows, K, dg);
+  hipLaunchKernelGGL(dg_reduce_kernel, dim3((unsigned)((K + 63) / 64)), dim3(256), 0, stream, part, rows, K, dg);
   return hipGetLastError();
 }
 

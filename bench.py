@@ -325,7 +325,41 @@ def extras(torch, hbl, synthetic, args):
                                   "forward_us": res["forward"], "tokens_per_s": M / (res["forward"] / 1e6),
                                   "timing": f"graph replay of {R} back-to-back calls over {R} weight copies"}
     out["decode_attn_7b_kv3"] = attention_extra(torch, hbl, synthetic, args)
+    out["backward_wdown_7b_int4"] = backward_extra(torch, hbl, synthetic, args)
     return out
+
+
+def backward_extra(torch, hbl, synthetic, args):
+    """Straight-through backward of the same 7B-shaped Wdown layer (INT4):
+    input gradient (bf16 product, transform, RMSNorm backward), gain gradient
+    and latent-weight gradient, from the forward's codes."""
+    w = synthetic.WORKLOADS["wdown_7b_int4"]
+    x, xb, wl = synthetic.make_inputs(w)
+    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    wp, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
+    wbt = hbl.backward_weights(wp, w.K)
+    codes, d = hbl.quantize_act(xd, 4)
+    rng = np.random.Generator(np.random.PCG64(w.seed + 77))
+    dyb = synthetic.f32_to_bf16_bits(rng.normal(0.0, 1.0, (w.M, w.N)).astype(np.float32))
+    dy = torch.from_numpy(dyb.view(np.int16)).cuda().view(torch.bfloat16)
+    g = torch.from_numpy(synthetic.make_gain(w.K, w.seed)).cuda()
+    ws = torch.empty(hbl.workspace_bytes(hbl.OP_BACKWARD, w.M, w.K, w.N), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        hbl.backward(xd, g, codes, 4, d, wbt, a, dy, workspace=ws)
+    torch.cuda.synchronize()
+    n = max(5, args.steps // 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        hbl.backward(xd, g, codes, 4, d, wbt, a, dy, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 2 * 2.0 * w.M * w.N * w.K            # two products of 2MNK each
+    return {"M": w.M, "K": w.K, "N": w.N, "ms_per_step": ms, "tokens_per_s": w.M / (ms / 1e3),
+            "matmul_tflops_if_all_time": flops / (ms / 1e3) / 1e12,
+            "timing": "events around back-to-back hbl_backward calls (both products, transform, norm, gain and "
+                      "weight gradients); per-kernel split in the rocprofv3 trace"}
 
 
 def attention_extra(torch, hbl, synthetic, args):

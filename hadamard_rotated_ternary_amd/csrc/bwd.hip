@@ -168,41 +168,64 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(const uint16_t* __
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  auto compute = [&](int buf) {
+  // Fragments of one 16-wide k-step: 4 A row blocks and 4 B column blocks.
+  struct GFrag {
+    bf8v a[4], b[4];
+  };
+  auto read_frag = [&](GFrag& f, int buf, int ks) __attribute__((always_inline)) {
     const uint8_t* sa = smem + buf * G_STAGE;
     const uint8_t* sb = sa + G_A_STAGE;
 #pragma unroll
-    for (int ks = 0; ks < GBK / 16; ++ks) {
-      bf8v af[4], bfr[4];
+    for (int rb = 0; rb < 4; ++rb) {
+      const int row = wi * 128 + rb * 32 + l32;
+      f.a[rb] = *reinterpret_cast<const bf8v*>(sa + row * GROW + 16 * ((2 * ks + g) ^ gswz(row)));
+    }
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int row = wi * 128 + rb * 32 + l32;
-        af[rb] = *reinterpret_cast<const bf8v*>(sa + row * GROW + 16 * ((2 * ks + g) ^ gswz(row)));
-      }
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int row = wj * 128 + cb * 32 + l32;
-        bfr[cb] = *reinterpret_cast<const bf8v*>(sb + row * GROW + 16 * ((2 * ks + g) ^ gswz(row)));
-      }
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bfr[cb], acc[rb][cb], 0, 0, 0);
+    for (int cb = 0; cb < 4; ++cb) {
+      const int row = wj * 128 + cb * 32 + l32;
+      f.b[cb] = *reinterpret_cast<const bf8v*>(sb + row * GROW + 16 * ((2 * ks + g) ^ gswz(row)));
     }
   };
-
-  // Stage kt lives in LDS buffer kt % 3 (as in the int8 prefill product).
-  constexpr int NL = 8;
-  const int KT = Cn / GBK;
-  auto phase = [&](int kt, int buf) {
-    if (kt + 1 < KT) wait_vmcnt<NL>(); else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kt + 2 < KT) dma(kt + 2, buf == 0 ? 2 : buf - 1);
-    compute(buf);
+  auto mfmas = [&](const GFrag& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
   };
+
+  // Stage kt lives in LDS buffer kt % 3.  Within stage kt the fragments of
+  // k-step 1 are read while the k-step 0 MFMAs run; then this wave waits for
+  // its copies of stage kt+1 (stage kt+2's may still be in flight) and the
+  // barrier makes every wave's copies visible and guarantees that every wave
+  // has read all of stage kt (its reads completed before the barrier), so
+  // stage kt+3 is requested into that buffer; the fragments of stage kt+1's
+  // k-step 0 are read while the k-step 1 MFMAs run.  Copies are thus issued
+  // two stages ahead of their use.
+  constexpr int NL = 8;   // copy instructions per wave per stage
+  const int KT = Cn / GBK;
+  GFrag f0, f1;
   dma(0, 0);
   if (KT > 1) dma(1, 1);
+  if (KT > 2) dma(2, 2);
+  if (KT > 2) wait_vmcnt<2 * NL>(); else if (KT > 1) wait_vmcnt<NL>(); else wait_vmcnt<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+  read_frag(f0, 0, 0);
+  auto phase = [&](int kt, int buf) __attribute__((always_inline)) {
+    read_frag(f1, buf, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < KT) {
+      if (kt + 2 < KT) wait_vmcnt<NL>(); else wait_vmcnt<0>();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+      if (kt + 3 < KT) dma(kt + 3, buf);
+      read_frag(f0, buf == 2 ? 0 : buf + 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   for (int kt = 0; kt < KT; kt += 3) {
     phase(kt, 0);
     if (kt + 1 < KT) phase(kt + 1, 1);

@@ -205,3 +205,45 @@ def test_attention_decode_full_size_sampled():
                                       codes_v[b:b + 1, h:h + 1], vs[b:b + 1, h:h + 1], bits, lens[b:b + 1])
         check_attention(got[b:b + 1, h:h + 1], ref, codes_v[b:b + 1, h:h + 1], vs[b:b + 1, h:h + 1], bits, 1, 1,
                         lens[b:b + 1])
+
+
+@pytest.mark.parametrize("d,Tmax,B,Hq,Hkv", [(64, 1, 1, 1, 1), (128, 5, 2, 2, 1), (256, 3, 1, 4, 4),
+                                             (128, 3000, 1, 2, 2)])
+def test_attention_decode_edge_shapes(d, Tmax, B, Hq, Hkv):
+    # one-token and few-token caches (one workgroup per head, short context),
+    # a single head split over many chunks (merge kernel), grouped heads
+    rng = np.random.default_rng(d + Tmax)
+    bits = 3
+    (kc, ks, kcd, ksd), (vc, vs, vcd, vsd) = make_cache(rng, B, Hkv, Tmax, d, bits)
+    qb, qf = bf16_bits(rng.normal(size=(B, Hq, d)))
+    lens = np.full(B, Tmax, np.int32)
+    lens[-1] = max(Tmax - 1, 0)
+    ref = oracle.attention_decode(qf, 8, kc, ks, vc, vs, bits, lens)
+    got = host(hbl.attention_decode(to_dev_bf16(qb), 8, kcd, ksd, vcd, vsd, bits, torch.from_numpy(lens).cuda()))
+    check_attention(got, ref, vc, vs, bits, Hq, Hkv, lens)
+
+
+def test_attention_decode_single_workgroup_per_head_short_context():
+    # 512 heads (no split, the kernel writes the output itself) with ragged
+    # lengths shorter than one block, including zero
+    rng = np.random.default_rng(77)
+    B, Hq, Hkv, d, Tmax, bits = 16, 32, 32, 128, 40, 4
+    (kc, ks, kcd, ksd), (vc, vs, vcd, vsd) = make_cache(rng, B, Hkv, Tmax, d, bits)
+    qb, qf = bf16_bits(rng.normal(size=(B, Hq, d)))
+    lens = rng.integers(0, Tmax + 1, size=B).astype(np.int32)
+    lens[0] = 0
+    lens[1] = Tmax
+    ref = oracle.attention_decode(qf, 8, kc, ks, vc, vs, bits, lens)
+    got = host(hbl.attention_decode(to_dev_bf16(qb), 8, kcd, ksd, vcd, vsd, bits, torch.from_numpy(lens).cuda()))
+    check_attention(got, ref, vc, vs, bits, Hq, Hkv, lens)
+
+
+def test_quantize_heads_empty_and_single_row():
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    codes, scale = hbl.quantize_heads(x, 3)
+    assert codes.shape == (0, 48) and scale.shape == (0,)
+    xb, xf = bf16_bits(np.linspace(-2, 2, 64, dtype=np.float32)[None])
+    codes, scale = hbl.quantize_heads(to_dev_bf16(xb), 2)
+    c_or, s_or, _ = oracle.quant_heads(xf, 2)
+    assert np.array_equal(unpack_heads(host(codes), 2, 64), c_or)
+    assert host(scale)[0] == np.float32(s_or[0])

@@ -166,3 +166,14 @@ def test_backward_full_size_sampled(bits):
     bound = (2.0 ** -8 + s["M"] * 2.0 ** -23) * (np.abs(s["dyf"]).astype(np.float64).T @ np.abs(xh)) + 1e-30
     assert np.all(np.abs(dw[:, k0:k0 + 64] - rdw) <= bound)
     assert np.all(np.isfinite(dg))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_backward_single_token(bits):
+    w = synthetic.WORKLOADS["wo_1p3b_int4"]
+    s = setup(w, bits, M=1, dy_seed=5)
+    _, dx, dw, dg = run_gpu(s, bits)
+    rdx, rdw, rdg, _ = oracle_bwd(s, True)
+    check_dx(dx, rdx)
+    check_dw(dw, s)
+    assert rel_l2(dg, rdg) <= 2e-5

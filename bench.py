@@ -67,8 +67,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
-              "sharding is a design note, not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU sharding.", file=sys.stderr)
         sys.exit(2)
     import torch
     import hadamard_rotated_ternary_amd as hbl

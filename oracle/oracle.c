@@ -63,22 +63,43 @@ static double clampd(double v, double lo, double hi) {
 /* ---------------------------------------------------------------------------
  * Weights: per-tensor absmean ternarisation to {-1, 0, 1}.
  * [QbitAI §引入H-BitLinear模块], [XZY §H-BitLinear模块], [AINEWS].
- *   S      = sum of |w| : each row summed left to right in double, then the
- *            row sums added in row order in double;
+ *   S      = sum of |w| in double, in a fixed order: each row in blocks of
+ *            64 consecutive columns (the last one may be shorter), each block
+ *            summed left to right, the block sums added left to right, then
+ *            the row sums added in row order;
  *   alpha  = (float)(S / (N*K))       -- the stored per-tensor scale (fp32);
  *   a      = max(alpha, EPS_Q);
  *   w_t    = clamp(round(w / a), -1, 1)  (w / a in double).
  * Returns 0, or -1 on bad arguments.
  * ------------------------------------------------------------------------- */
+/* Sum of |v| over one row in the order above. */
+static double row_abs_sum_f(const float *v, int64_t K)
+{
+    double row = 0.0;
+    for (int64_t b0 = 0; b0 < K; b0 += 64) {
+        double blk = 0.0;
+        for (int64_t k = b0; k < K && k < b0 + 64; ++k) blk += fabs((double)v[k]);
+        row += blk;
+    }
+    return row;
+}
+
+static double row_abs_sum_d(const double *v, int64_t K)
+{
+    double row = 0.0;
+    for (int64_t b0 = 0; b0 < K; b0 += 64) {
+        double blk = 0.0;
+        for (int64_t k = b0; k < K && k < b0 + 64; ++k) blk += fabs(v[k]);
+        row += blk;
+    }
+    return row;
+}
+
 int oracle_quantize_weights(const float *w, int64_t N, int64_t K, int8_t *wt, float *alpha_out)
 {
     if (!w || !wt || !alpha_out || N <= 0 || K <= 0) return -1;
     double S = 0.0;
-    for (int64_t n = 0; n < N; ++n) {
-        double row = 0.0;
-        for (int64_t k = 0; k < K; ++k) row += fabs((double)w[n * K + k]);
-        S += row;
-    }
+    for (int64_t n = 0; n < N; ++n) S += row_abs_sum_f(w + n * K, K);
     float alpha = (float)(S / ((double)N * (double)K));
     double a = (double)alpha;
     if (a < EPS_Q) a = (double)(float)EPS_Q;
@@ -305,11 +326,7 @@ int oracle_quantize_weights_rotated(const float *w, int64_t N, int64_t K, int8_t
         oracle_hadamard_rotate(row, K, wr + n * K);
     }
     double S = 0.0;
-    for (int64_t n = 0; n < N; ++n) {
-        double rs = 0.0;
-        for (int64_t k = 0; k < K; ++k) rs += fabs(wr[n * K + k]);
-        S += rs;
-    }
+    for (int64_t n = 0; n < N; ++n) S += row_abs_sum_d(wr + n * K, K);
     float alpha = (float)(S / ((double)N * (double)K));
     double a = oracle_weight_scale(alpha);
     for (int64_t i = 0; i < N * K; ++i) wt[i] = (int8_t)clampd(rne(wr[i] / a), -1.0, 1.0);

@@ -14,26 +14,38 @@
 
 namespace hbl {
 
-// Row sums of |w| in fp64, strictly in column order.  A 64-thread workgroup
-// owns 64 rows; tiles of 64x64 are staged through LDS with coalesced loads,
-// then each thread walks its own row.
-__global__ __launch_bounds__(64) void wrowsum_kernel(const float* __restrict__ w, int N, int K,
-                                                    double* __restrict__ rowsum) {
-  __shared__ float tile[64][65];
-  const int t = threadIdx.x;
-  const int n0 = blockIdx.x * 64;
-  double acc = 0.0;
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    for (int r = 0; r < 64; ++r) {
-      const int n = n0 + r;
-      tile[r][t] = (n < N && k0 + t < K) ? w[(size_t)n * K + k0 + t] : 0.0f;
-    }
-    __syncthreads();
-    const int kend = K - k0 < 64 ? K - k0 : 64;
-    for (int c = 0; c < kend; ++c) acc += (double)fabsf(tile[t][c]);
-    __syncthreads();
+// Row sums of |w| in fp64 in a fixed order: 64-column blocks, each summed
+// left to right, block sums added left to right.  One 256-thread workgroup
+// per row (K <= 16384, so at most 256 blocks): the row is staged through LDS
+// with coalesced 16-byte loads (blocks padded to 65 floats so the per-block
+// walks hit distinct banks), thread b sums block b, thread 0 adds the block
+// sums in order.
+__global__ __launch_bounds__(256) void wrowsum_kernel(const float* __restrict__ w, int N, int K,
+                                                     double* __restrict__ rowsum) {
+  __shared__ float row[256 * 65];
+  __shared__ double bsum[256];
+  const int n = blockIdx.x, t = threadIdx.x;
+  const float4* src = reinterpret_cast<const float4*>(w + (size_t)n * K);
+  for (int i = t; i < K / 4; i += 256) {
+    const float4 v = src[i];
+    const int e = 4 * i, b = e >> 6, o = e & 63;
+    float* d = row + b * 65 + o;
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
   }
-  if (n0 + t < N) rowsum[n0 + t] = acc;
+  __syncthreads();
+  const int nb = (K + 63) / 64;
+  if (t < nb) {
+    const int len = K - 64 * t < 64 ? K - 64 * t : 64;
+    double acc = 0.0;
+    for (int o = 0; o < len; ++o) acc += (double)fabsf(row[t * 65 + o]);
+    bsum[t] = acc;
+  }
+  __syncthreads();
+  if (t == 0) {
+    double acc = 0.0;
+    for (int b = 0; b < nb; ++b) acc += bsum[b];
+    rowsum[n] = acc;
+  }
 }
 
 // alpha = fp32(sum_n rowsum[n] / (N K)), summed in row order by one thread.
@@ -84,7 +96,7 @@ __global__ __launch_bounds__(256) void wunpack_kernel(const uint32_t* __restrict
 }
 
 hipError_t launch_wquant(const WquantArgs& a) {
-  hipLaunchKernelGGL(wrowsum_kernel, dim3((a.N + 63) / 64), dim3(64), 0, a.stream, a.w, a.N, a.K, a.rowsum);
+  hipLaunchKernelGGL(wrowsum_kernel, dim3(a.N), dim3(256), 0, a.stream, a.w, a.N, a.K, a.rowsum);
   hipLaunchKernelGGL(walpha_kernel, dim3(1), dim3(64), 0, a.stream, a.rowsum, a.N, a.K, a.walpha);
   const size_t words = (size_t)a.N * (a.K / 16);
   hipLaunchKernelGGL(wpack_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, a.stream, a.w, a.N,

@@ -48,12 +48,22 @@ __global__ __launch_bounds__(256) void wrowsum_kernel(const float* __restrict__ 
   }
 }
 
-// alpha = fp32(sum_n rowsum[n] / (N K)), summed in row order by one thread.
-__global__ void walpha_kernel(const double* __restrict__ rowsum, int N, int K, float* __restrict__ walpha) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// alpha = fp32(sum_n rowsum[n] / (N K)), summed in row order by one thread;
+// the row sums are staged through LDS 2048 at a time (coalesced loads) so the
+// ordered sum does not wait on one global load per row.
+__global__ __launch_bounds__(256) void walpha_kernel(const double* __restrict__ rowsum, int N, int K,
+                                                    float* __restrict__ walpha) {
+  __shared__ double chunk[2048];
   double s = 0.0;
-  for (int n = 0; n < N; ++n) s += rowsum[n];
-  walpha[0] = (float)(s / ((double)N * (double)K));
+  for (int n0 = 0; n0 < N; n0 += 2048) {
+    const int cnt = N - n0 < 2048 ? N - n0 : 2048;
+    for (int i = threadIdx.x; i < cnt; i += 256) chunk[i] = rowsum[n0 + i];
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int i = 0; i < cnt; ++i) s += chunk[i];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) walpha[0] = (float)(s / ((double)N * (double)K));
 }
 
 // One thread per packed 32-bit word (16 consecutive k of one row).
@@ -97,7 +107,7 @@ __global__ __launch_bounds__(256) void wunpack_kernel(const uint32_t* __restrict
 
 hipError_t launch_wquant(const WquantArgs& a) {
   hipLaunchKernelGGL(wrowsum_kernel, dim3(a.N), dim3(256), 0, a.stream, a.w, a.N, a.K, a.rowsum);
-  hipLaunchKernelGGL(walpha_kernel, dim3(1), dim3(64), 0, a.stream, a.rowsum, a.N, a.K, a.walpha);
+  hipLaunchKernelGGL(walpha_kernel, dim3(1), dim3(256), 0, a.stream, a.rowsum, a.N, a.K, a.walpha);
   const size_t words = (size_t)a.N * (a.K / 16);
   hipLaunchKernelGGL(wpack_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, a.stream, a.w, a.N,
                      a.K, a.walpha, reinterpret_cast<uint32_t*>(a.wpack));

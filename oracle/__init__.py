@@ -54,6 +54,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_dequant_heads.argtypes = [P, P, I64, I64, I, P]
         L.oracle_attention_decode.argtypes = [P, I, P, P, P, P, I, P, I64, I64, I64, I64, I64, P]
         L.oracle_backward.argtypes = [P, P, P, P, P, ctypes.c_float, P, I64, I64, I64, I, P, P, P, P]
+        L.oracle_attention_prefill.argtypes = [P, I, P, P, P, P, I, P, I64, I64, I64, I64, I64, I64, P]
         _lib = L
     return _lib
 
@@ -249,6 +250,24 @@ def attention_decode(q, qbits, kc, ks, vc, vs, kvbits, lens):
     out = np.empty((B, Hq, d))
     _chk(lib().oracle_attention_decode(_p(q), qbits, _p(kc), _p(ks), _p(vc), _p(vs), kvbits, _p(lens),
                                        B, Hq, Hkv, d, Tmax, _p(out)), "attention_decode")
+    return out
+
+
+def attention_prefill(q, qbits, kc, ks, vc, vs, kvbits, start):
+    """Causal attention of Tn new tokens per sequence over the quantised cache.
+    q [B][Tn][Hq][d]; cache as for attention_decode; start [B] (position of
+    each sequence's first new token).  Returns out [B][Tn][Hq][d] double."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    kc = np.ascontiguousarray(kc, dtype=np.uint8)
+    vc = np.ascontiguousarray(vc, dtype=np.uint8)
+    ks = np.ascontiguousarray(ks, dtype=np.float32)
+    vs = np.ascontiguousarray(vs, dtype=np.float32)
+    start = np.ascontiguousarray(start, dtype=np.int32)
+    B, Tn, Hq, d = q.shape
+    _, Hkv, Tmax, _ = kc.shape
+    out = np.empty((B, Tn, Hq, d))
+    _chk(lib().oracle_attention_prefill(_p(q), qbits, _p(kc), _p(ks), _p(vc), _p(vs), kvbits, _p(start),
+                                        B, Tn, Hq, Hkv, d, Tmax, _p(out)), "attention_prefill")
     return out
 
 

@@ -513,6 +513,37 @@ int oracle_backward(const float *x, const float *g, const int8_t *q, const doubl
     return bad ? -2 : 0;
 }
 
+/* ---------------------------------------------------------------------------
+ * Prefill (causal) attention over the quantised cache: Tn new tokens per
+ * sequence, token i of sequence b at position start_b + i, its query
+ * quantised per head like the decode step's; it attends to the cached tokens
+ * 0 .. start_b + i (the new tokens have been appended to the cache first).
+ * q [B][Tn][Hq][d] fp32; cache and scales as for the decode step; start [B];
+ * out [B][Tn][Hq][d] double.  Each query row is one decode step with length
+ * start_b + i + 1.
+ * ------------------------------------------------------------------------- */
+int oracle_attention_prefill(const float *q, int qbits, const uint8_t *kc, const float *ks, const uint8_t *vc,
+                             const float *vs, int kvbits, const int32_t *start, int64_t B, int64_t Tn,
+                             int64_t Hq, int64_t Hkv, int64_t d, int64_t Tmax, double *out)
+{
+    if (!q || !start || !out || B < 0 || Tn < 0) return -1;
+    for (int64_t b = 0; b < B; ++b)
+        if (start[b] < 0 || start[b] + Tn > Tmax) return -2;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t i = 0; i < Tn; ++i) {
+            /* one decode step of this sequence alone: the cache rows of
+             * sequence b, length start + i + 1 */
+            const int32_t len = (int32_t)(start[b] + i + 1);
+            const int64_t hrow = b * Hkv * Tmax;
+            int rc = oracle_attention_decode(q + ((b * Tn + i) * Hq) * d, qbits, kc + hrow * d, ks + hrow,
+                                             vc + hrow * d, vs + hrow, kvbits, &len, 1, Hq, Hkv, d, Tmax,
+                                             out + ((b * Tn + i) * Hq) * d);
+            if (rc) return rc;
+        }
+    }
+    return 0;
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -697,3 +697,54 @@ def test_backward_rmsnorm_and_rotation_invariants():
         rhs = 1e-6 / r2 * float(np.dot(du[m], u[m]))
         assert abs(lhs - rhs) <= 1e-9 * (1 + abs(rhs)) + 1e-12 * np.abs(dx[m]).sum(), (m, lhs, rhs)
         np.testing.assert_allclose(np.linalg.norm(du[m]), np.linalg.norm(dxh[m]), rtol=1e-12)
+
+
+def test_attention_prefill_causal_closed_forms():
+    # Prefill from position 0: query i sees keys 0..i only.
+    rng = np.random.default_rng(21)
+    B, Tn, Hq, Hkv, d, Tmax, bits = 2, 6, 2, 1, 16, 9, 3
+    kc, ks, vc, vs = _cache(rng, B, Hkv, Tmax, d, bits)
+    q = rng.normal(size=(B, Tn, Hq, d)).astype(np.float32)
+    start = np.array([0, 3])
+    out = oracle.attention_prefill(q, 8, kc, ks, vc, vs, bits, start)
+    vh = (vc.astype(np.float64) - 4) * vs[..., None]
+    # the first query of sequence 0 sees one key: its value row
+    for h in range(Hq):
+        np.testing.assert_allclose(out[0, 0, h], vh[0, 0, 0], rtol=0, atol=1e-15)
+    # identical keys: query i of sequence b gets the mean of values 0..start+i
+    kc2 = np.repeat(kc[:, :, :1], Tmax, axis=2)
+    ks2 = np.repeat(ks[:, :, :1], Tmax, axis=2)
+    out2 = oracle.attention_prefill(q, 8, kc2, ks2, vc, vs, bits, start)
+    for b in range(B):
+        for i in range(Tn):
+            for h in range(Hq):
+                np.testing.assert_allclose(out2[b, i, h], vh[b, 0, :start[b] + i + 1].mean(axis=0),
+                                           rtol=1e-13, atol=1e-15)
+    # causality: cache rows after a query's position do not change its output
+    kc3, vc3 = kc.copy(), vc.copy()
+    kc3[1, :, 6:] = 7
+    vc3[1, :, 6:] = 1
+    out3 = oracle.attention_prefill(q, 8, kc3, ks, vc3, vs, bits, start)
+    assert np.array_equal(out3[0], out[0])
+    assert np.array_equal(out3[1, :3], out[1, :3])          # positions 3, 4, 5 see rows 0..5 only
+    assert not np.allclose(out3[1, 3:], out[1, 3:])
+
+
+def test_attention_prefill_two_token_closed_form():
+    # query 1 (position 1) over keys 0 and 1: p_0 = sigmoid(l0 - l1), as in the decode case
+    G, sk0, sk1 = 1.5, 0.25, 0.5
+    Z = 4
+    q = np.zeros((1, 2, 1, 4), np.float32)
+    q[0, 1, 0, 0] = G
+    q[0, 0, 0, 1] = 1.0
+    kc = np.array([[[[Z + 2, Z + 3, Z - 1, Z], [Z - 1, Z + 1, Z, Z - 3]]]], dtype=np.uint8)
+    ks = np.array([[[sk0, sk1]]], dtype=np.float32)
+    vc = np.array([[[[Z + 1, Z - 2, Z + 3, Z], [Z - 3, Z, Z + 1, Z + 2]]]], dtype=np.uint8)
+    vs = np.array([[[0.125, 0.75]]], dtype=np.float32)
+    out = oracle.attention_prefill(q, 4, kc, ks, vc, vs, 3, np.array([0]))
+    l0, l1 = G * 2 * sk0 / 2, -G * 1 * sk1 / 2
+    p0 = 1.0 / (1.0 + math.exp(l1 - l0))
+    v0 = np.array([1, -2, 3, 0]) * 0.125
+    v1 = np.array([-3, 0, 1, 2]) * 0.75
+    np.testing.assert_allclose(out[0, 1, 0], p0 * v0 + (1 - p0) * v1, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(out[0, 0, 0], v0, rtol=0, atol=1e-15)   # position 0: key 0 only

@@ -53,6 +53,7 @@ SIGNATURES = {
     "hbl_kv_cache_append": ([P, P, I64, I64, I64, I64, I, P, I64, P, P, P, P, P], I),
     "hbl_attention_workspace_bytes": ([I64, I64, I64, I64], SZ),
     "hbl_attention_decode": ([P, I, P, P, P, P, I, P, I64, I64, I64, I64, I64, P, I, P, SZ, P], I),
+    "hbl_attention_prefill": ([P, I, P, P, P, P, I, P, I64, I64, I64, I64, I64, I64, P, I, P], I),
 }
 
 
@@ -336,4 +337,21 @@ def attention_decode(q: torch.Tensor, q_bits: int, k_codes, k_scale, v_codes, v_
     _call("hbl_attention_decode", _ptr(q), q_bits, _ptr(k_codes), _ptr(k_scale), _ptr(v_codes), _ptr(v_scale),
           kv_bits, _ptr(lens), B, Hq, Hkv, d, Tmax, _ptr(out), _dtype_code(out.dtype), _ptr(ws),
           ws.numel() * ws.element_size(), _stream())
+    return out
+
+
+def attention_prefill(q: torch.Tensor, q_bits: int, k_codes, k_scale, v_codes, v_scale, kv_bits: int,
+                      start: torch.Tensor, out_dtype=torch.float32, out=None) -> torch.Tensor:
+    """Causal prefill over a quantised cache: q bf16 [B][Tn][Hq][d] -> out [B][Tn][Hq][d]."""
+    for t, n in ((q, "q"), (k_codes, "k_codes"), (k_scale, "k_scale"), (v_codes, "v_codes"),
+                 (v_scale, "v_scale"), (start, "start")):
+        _dev(t, n)
+    if q.dtype != torch.bfloat16 or start.dtype != torch.int32:
+        raise TypeError("q must be bfloat16 and start int32")
+    B, Tn, Hq, d = q.shape
+    Hkv, Tmax = k_scale.shape[1], k_scale.shape[2]
+    if out is None:
+        out = torch.empty((B, Tn, Hq, d), dtype=out_dtype, device=q.device)
+    _call("hbl_attention_prefill", _ptr(q), q_bits, _ptr(k_codes), _ptr(k_scale), _ptr(v_codes), _ptr(v_scale),
+          kv_bits, _ptr(start), B, Tn, Hq, Hkv, d, Tmax, _ptr(out), _dtype_code(out.dtype), _stream())
     return out

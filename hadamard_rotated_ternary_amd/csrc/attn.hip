@@ -36,6 +36,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 
 // round_half_even(a / G) for a = v * qb exact, given an estimate p of a / G
 // that is within 1/2 of it.
@@ -581,6 +582,257 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill (causal) attention over the quantised cache, on the matrix cores.
+// One workgroup (4 waves) per (sequence, query head, block of 64 new
+// tokens); each wave owns 16 queries.  Key blocks of 64 cached tokens:
+//   the block's key codes go to LDS as signed bytes (u - Z) and its value
+//   codes as bf16 u (exact small integers), transposed to [channel][token]
+//   because the second product contracts over tokens;
+//   scores: v_mfma_i32_16x16x64_i8 of the query codes with the key codes
+//   (exact), times sq * sk / sqrt(D), causal mask, online softmax in fp32;
+//   values: P' = P * sv rounded to bf16, v_mfma_f32_16x16x32_bf16 with u,
+//   and the (u - Z) form from the sum of P'.
+// 16x16 accumulator layout: lane l / register r hold row 4*(l/16) + r,
+// column l%16; A operands: row l%16, k block l/16; B operands: column l%16,
+// k block l/16.
+constexpr int PF_QB = 64, PF_TB = 64;
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct PfCfg {
+  static constexpr int KROW = D + 16;          // key tile row (bytes)
+  static constexpr int VROW = PF_TB + 8;       // value tile row (bf16 per channel)
+  static constexpr int PROW = PF_TB + 8;       // P row (bf16 per query)
+  static constexpr int QROW = D + 16;          // query codes row (bytes)
+  static constexpr int GPR = D / 32;           // 32-code groups per row
+};
+
+template <int D, int KB>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
+  using C = PfCfg<D>;
+  __shared__ __align__(16) int8_t kt[PF_TB * C::KROW];
+  __shared__ __align__(16) uint16_t vt[D * C::VROW];
+  __shared__ __align__(16) uint16_t pt[4 * 16 * C::PROW];
+  __shared__ __align__(16) int8_t qt[PF_QB * C::QROW];
+  __shared__ float ksc[PF_TB], vsc[PF_TB], qsc[PF_QB];
+
+  const int nqb = (a.Tn + PF_QB - 1) / PF_QB;
+  // heavy (late) query blocks first
+  const int64_t L = blockIdx.x;
+  const int qblk = nqb - 1 - (int)(L % nqb);
+  const int64_t bh = L / nqb;
+  const int hq = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const int hk = hq / (a.Hq / a.Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  int start = a.start[b];
+  start = start < 0 ? 0 : start;
+  const int q0 = qblk * PF_QB;
+  const int qend = a.Tn < q0 + PF_QB ? a.Tn : q0 + PF_QB;    // new tokens q0 .. qend-1
+  int len = start + qend;                                     // keys needed by the last query
+  len = len > a.Tmax ? (int)a.Tmax : len;
+
+  // ---- queries: per-head absmax codes of the block's 64 tokens (4 threads per row)
+  {
+    const int row = tid >> 2, qq = tid & 3;
+    const int i = q0 + row;
+    float v[D / 4];
+    if (i < a.Tn) {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.Tn + i) * a.Hq + hq) * D + qq * (D / 4);
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u) {
+        const uint4 w = reinterpret_cast<const uint4*>(qp)[u];
+        v[8 * u + 0] = bf16_lo(w.x); v[8 * u + 1] = bf16_hi(w.x); v[8 * u + 2] = bf16_lo(w.y);
+        v[8 * u + 3] = bf16_hi(w.y); v[8 * u + 4] = bf16_lo(w.z); v[8 * u + 5] = bf16_hi(w.z);
+        v[8 * u + 6] = bf16_lo(w.w); v[8 * u + 7] = bf16_hi(w.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < D / 4; ++e) v[e] = 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) m = fmaxf(m, fabsf(v[e]));
+    m = lane_reduce<4, true>(m);
+    const float G = fmaxf(m, kEpsQ);
+    const float qb = (float)((1 << (a.qbits - 1)) - 1);
+    const float rq = qb / G;
+#pragma unroll
+    for (int e = 0; e < D / 4; e += 4) {
+      uint32_t pk = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pk |= ((uint32_t)round_ratio(v[e + k] * qb, G, v[e + k] * rq) & 0xFFu) << (8 * k);
+      *reinterpret_cast<uint32_t*>(qt + row * C::QROW + qq * (D / 4) + e) = pk;
+    }
+    if (qq == 0) qsc[row] = G / qb;
+  }
+  __syncthreads();
+  // query A operands of this wave's 16 rows: k-step s covers channels 64s .. 64s+63
+  v4i qa[D / 64];
+#pragma unroll
+  for (int s2 = 0; s2 < D / 64; ++s2)
+    qa[s2] = *reinterpret_cast<const v4i*>(qt + (wave * 16 + l16) * C::QROW + 64 * s2 + 16 * g4);
+  float sqr[4];
+  int qpos[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = wave * 16 + 4 * g4 + r;
+    sqr[r] = qsc[row];
+    qpos[r] = start + q0 + row;                 // this query's position (keys 0 .. qpos)
+  }
+  constexpr float kInvSqrtD = D == 64 ? 0.125f : (D == 128 ? 0.08838834764831845f : 0.0625f);
+
+  constexpr int RDW = D / 32 * KB;
+  const int64_t head_row = ((int64_t)b * a.Hkv + hk) * a.Tmax;
+  const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + head_row * RDW * 4), (short)0, len * RDW * 4,
+                                                     kBufferFlags);
+  const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + head_row * RDW * 4), (short)0, len * RDW * 4,
+                                                     kBufferFlags);
+  const auto kss = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + head_row), (short)0, len * 4, kBufferFlags);
+  const auto vss = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + head_row), (short)0, len * 4, kBufferFlags);
+  constexpr int ZK = KB == 8 ? 128 : (1 << (KB - 1));
+
+  v4f o[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) o[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  float mrow[4], lrow[4], sprow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.0f; sprow[r] = 0.0f; }
+
+  const int nkb = (len + PF_TB - 1) / PF_TB;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int t0 = kb * PF_TB;
+    // ---- stage the key and value tiles (one 32-code group per thread and pass)
+    for (int it = tid; it < PF_TB * C::GPR; it += 256) {
+      const int row = it / C::GPR, grp = it % C::GPR;
+      const int t = t0 + row;
+      uint32_t w[KB], qd[8];
+      buffer_words<KB>(krs, (t * RDW + grp * KB) * 4, w);
+      unpack_quads<KB>(w, qd);
+      uint32_t sb[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        sb[k] = KB == 8 ? (qd[k] ^ 0x80808080u) : (((qd[k] | 0x80808080u) - (uint32_t)ZK * 0x01010101u) ^ 0x80808080u);
+      int8_t* kd = kt + row * C::KROW + grp * 32;
+      *reinterpret_cast<uint4*>(kd) = make_uint4(sb[0], sb[1], sb[2], sb[3]);
+      *reinterpret_cast<uint4*>(kd + 16) = make_uint4(sb[4], sb[5], sb[6], sb[7]);
+      buffer_words<KB>(vrs, (t * RDW + grp * KB) * 4, w);
+      unpack_quads<KB>(w, qd);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float f = (float)((qd[k] >> (8 * i)) & 0xFFu);           // exact in bf16 (< 256)
+          vt[(grp * 32 + 4 * k + i) * C::VROW + row] = (uint16_t)(__float_as_uint(f) >> 16);
+        }
+      if (grp == 0) {
+        ksc[row] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kss, t * 4, 0, 0));
+        vsc[row] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vss, t * 4, 0, 0));
+      }
+    }
+    __syncthreads();
+    // ---- scores of this wave's 16 queries against the 64 keys
+    float sc[4][4];        // [key tile][register]
+    float bm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int s2 = 0; s2 < D / 64; ++s2) {
+        const v4i kb4 = *reinterpret_cast<const v4i*>(kt + (nt * 16 + l16) * C::KROW + 64 * s2 + 16 * g4);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[s2], kb4, acc, 0, 0, 0);
+      }
+      const int tcol = nt * 16 + l16;
+      const float kscale = ksc[tcol] * kInvSqrtD;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = (float)acc[r] * (sqr[r] * kscale);
+        sc[nt][r] = t0 + tcol <= qpos[r] && t0 + tcol < len ? v : -INFINITY;
+        bm[r] = fmaxf(bm[r], sc[nt][r]);
+      }
+    }
+    // row max over the 16 lanes that share the rows
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bm[r] = lane_reduce<16, true>(bm[r]);
+    float fac[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mn = fmaxf(mrow[r], bm[r]);
+      fac[r] = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((mrow[r] - mn) * kLog2e);
+      mrow[r] = mn;
+      lrow[r] *= fac[r];
+      sprow[r] *= fac[r];
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[c][r] *= fac[r];
+    // P' = exp(s - m) * sv as bf16 into this wave's P tile (rows = queries)
+    uint16_t* pw = pt + wave * 16 * C::PROW;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f}, sp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int tcol = nt * 16 + l16;
+      const float vscale = vsc[tcol];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = sc[nt][r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((sc[nt][r] - mrow[r]) * kLog2e);
+        ls[r] += pr;
+        const uint16_t pb = f32_to_bf16(pr * vscale);
+        sp[r] += __uint_as_float((uint32_t)pb << 16);
+        pw[(4 * g4 + r) * C::PROW + tcol] = pb;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      lrow[r] += lane_reduce<16, false>(ls[r]);
+      sprow[r] += lane_reduce<16, false>(sp[r]);
+    }
+    __syncthreads();   // P tiles written (and every wave past the score reads of kt)
+    // ---- O += P' . u over the 64 keys
+#pragma unroll
+    for (int s2 = 0; s2 < PF_TB / 32; ++s2) {
+      const bf8v pa = *reinterpret_cast<const bf8v*>(pw + l16 * C::PROW + 32 * s2 + 8 * g4);
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const bf8v vb = *reinterpret_cast<const bf8v*>(vt + (c * 16 + l16) * C::VROW + 32 * s2 + 8 * g4);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[c], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // tiles free for the next block
+  }
+  // ---- out = (O - Z * sum P') / sum P
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = wave * 16 + 4 * g4 + r, i = q0 + row;
+    if (i >= a.Tn) continue;
+    const float inv = lrow[r] > 0.0f ? 1.0f / lrow[r] : 0.0f;
+    const float zs = (float)ZK * sprow[r];
+    const int64_t ob = (((int64_t)b * a.Tn + i) * a.Hq + hq) * D;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const float v = (o[c][r] - zs) * inv;
+      if (a.out_bf16) static_cast<uint16_t*>(a.out)[ob + c * 16 + l16] = f32_to_bf16(v);
+      else static_cast<float*>(a.out)[ob + c * 16 + l16] = v;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_prefill_d(const PrefillArgs& a) {
+  const int nqb = (a.Tn + PF_QB - 1) / PF_QB;
+  const dim3 grid((unsigned)((int64_t)a.B * a.Hq * nqb));
+  switch (a.kvbits) {
+    case 2: attn_prefill_kernel<D, 2><<<grid, dim3(256), 0, a.stream>>>(a); break;
+    case 3: attn_prefill_kernel<D, 3><<<grid, dim3(256), 0, a.stream>>>(a); break;
+    case 4: attn_prefill_kernel<D, 4><<<grid, dim3(256), 0, a.stream>>>(a); break;
+    case 8: attn_prefill_kernel<D, 8><<<grid, dim3(256), 0, a.stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a) {
   const int g = a.Hq / a.Hkv;
@@ -664,6 +916,16 @@ hipError_t launch_dequant_heads(const uint8_t* codes, const float* scale, int64_
   }
 #undef HBL_DQ
   return hipGetLastError();
+}
+
+hipError_t launch_attention_prefill(const PrefillArgs& a) {
+  if (a.B == 0 || a.Tn == 0) return hipSuccess;
+  switch (a.d) {
+    case 64: return launch_prefill_d<64>(a);
+    case 128: return launch_prefill_d<128>(a);
+    case 256: return launch_prefill_d<256>(a);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attention_decode(const AttnArgs& a) {

@@ -358,6 +358,29 @@ size_t hbl_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t d, int64_t T
   return attn_part_bytes(B, Hq, d, Tmax);
 }
 
+hbl_status hbl_attention_prefill(const void* q, int q_bits, const uint8_t* k_codes, const float* k_scale,
+                                 const uint8_t* v_codes, const float* v_scale, int kv_bits, const int32_t* start,
+                                 int64_t B, int64_t Tn, int64_t Hq, int64_t Hkv, int64_t d, int64_t Tmax, void* out,
+                                 hbl_dtype out_dtype, hipStream_t stream) {
+  if (!hbl::heads_bits_supported(kv_bits) || q_bits < 2 || q_bits > 8 || !valid_dtype(out_dtype))
+    return HBL_ERR_DTYPE;
+  if (!heads_d_ok(d) || B < 0 || B >= kCount || Tn < 0 || Tn >= kCount || Hkv <= 0 || Hq <= 0 || Hq >= kCount ||
+      Hq % Hkv != 0 || Tmax <= 0 || Tmax >= kCount || B * Hkv * Tmax > (int64_t(1) << 34) ||
+      B * Hq * ((Tn + 63) / 64) >= kCount || Tmax * (d * kv_bits / 8) >= kCount)
+    return HBL_ERR_SHAPE;
+  if (B == 0 || Tn == 0) return HBL_OK;
+  if (!q || !k_codes || !k_scale || !v_codes || !v_scale || !start || !out) return HBL_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(k_scale) || !aligned16(v_codes) || !aligned16(v_scale) ||
+      !aligned16(start) || !aligned16(out))
+    return HBL_ERR_ALIGN;
+  if (hbl_status st = check_device()) return st;
+  hbl::PrefillArgs a{};
+  a.q = q; a.qbits = q_bits; a.kc = k_codes; a.ks = k_scale; a.vc = v_codes; a.vs = v_scale; a.kvbits = kv_bits;
+  a.start = start; a.B = (int)B; a.Tn = (int)Tn; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.d = (int)d; a.Tmax = Tmax;
+  a.out = out; a.out_bf16 = out_dtype == HBL_BF16; a.stream = stream;
+  return launched(hbl::launch_attention_prefill(a));
+}
+
 hbl_status hbl_attention_decode(const void* q, int q_bits, const uint8_t* k_codes, const float* k_scale,
                                 const uint8_t* v_codes, const float* v_scale, int kv_bits, const int32_t* lens,
                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t Tmax, void* out,

@@ -116,6 +116,22 @@ bool heads_bits_supported(int bits);
 int attn_block_tokens(int d);
 void attn_plan(int64_t B, int64_t Hq, int d, int64_t Tmax, int* ct, int* nchunk);
 hipError_t launch_attention_decode(const AttnArgs& a);
+struct PrefillArgs {
+  const void* q;          // bf16 [B][Tn][Hq][d]
+  int qbits;
+  const uint8_t* kc;      // packed [B][Hkv][Tmax][d*kvbits/8]
+  const float* ks;
+  const uint8_t* vc;
+  const float* vs;
+  int kvbits;
+  const int32_t* start;   // device [B]: position of each sequence's first new token
+  int B, Tn, Hq, Hkv, d;
+  int64_t Tmax;
+  void* out;              // [B][Tn][Hq][d]
+  bool out_bf16;
+  hipStream_t stream;
+};
+hipError_t launch_attention_prefill(const PrefillArgs& a);
 
 // Backward pass (straight-through estimator).
 struct BwdArgs {

@@ -90,6 +90,19 @@ hbl_status hbl_attention_decode(const void *q, int q_bits, const uint8_t *k_code
                                 int64_t d, int64_t Tmax, void *out, hbl_dtype out_dtype,
                                 void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Causal prefill attention: q bf16 [B][Tn][Hq][d] holds Tn new tokens per
+ * sequence (post-RoPE, quantised inside with q_bits), already appended to the
+ * cache at positions start[b] .. start[b] + Tn - 1 (start: device int32 [B]);
+ * token i attends to cached tokens 0 .. start[b] + i.  out [B][Tn][Hq][d] in
+ * out_dtype.  Scores are exact integer dot products on the int8 matrix
+ * instruction; the probabilities times the value scales are rounded to bf16
+ * for the value product (bf16 matrix instruction, fp32 accumulation).
+ * d in {64, 128, 256}; positions past Tmax are clamped.  No workspace. */
+hbl_status hbl_attention_prefill(const void *q, int q_bits, const uint8_t *k_codes, const float *k_scale,
+                                 const uint8_t *v_codes, const float *v_scale, int kv_bits,
+                                 const int32_t *start, int64_t B, int64_t Tn, int64_t Hq, int64_t Hkv,
+                                 int64_t d, int64_t Tmax, void *out, hbl_dtype out_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -247,3 +247,94 @@ def test_quantize_heads_empty_and_single_row():
     c_or, s_or, _ = oracle.quant_heads(xf, 2)
     assert np.array_equal(unpack_heads(host(codes), 2, 64), c_or)
     assert host(scale)[0] == np.float32(s_or[0])
+
+
+# ----------------------------------------------------------------- prefill
+# Bar: |out - ref| <= (2^-8 + 3e-5) * max|v^| per (token, head): the scores
+# are exact integers scaled in fp32 (as in the decode step); the value
+# product rounds P * sv to bf16 (relative 2^-9), so the output moves by at
+# most 2^-9 of the largest value it averages.
+PF_TOL = 2.0 ** -8 + ATTN_TOL
+
+
+def check_prefill(got, ref, vc, vs, bits, Hq, Hkv, start, tol=PF_TOL):
+    Z = 1 << (bits - 1)
+    g = Hq // Hkv
+    B, Tn = got.shape[:2]
+    for b in range(B):
+        for i in range(Tn):
+            L = start[b] + i + 1
+            for h in range(Hq):
+                vh = (vc[b, h // g, :L].astype(np.float64) - Z) * vs[b, h // g, :L, None]
+                bound = tol * np.max(np.abs(vh))
+                err = np.max(np.abs(got[b, i, h] - ref[b, i, h]))
+                assert err <= bound, (b, i, h, err, bound)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_attention_prefill_matches_oracle(bits, d):
+    rng = np.random.default_rng(bits * 31 + d)
+    B, Hq, Hkv = 2, 4, 2
+    Tn = {64: 150, 128: 97, 256: 70}[d]          # ragged query blocks
+    start = np.array([0, 37], np.int32)
+    Tmax = Tn + 40
+    (kc, ks, kcd, ksd), (vc, vs, vcd, vsd) = make_cache(rng, B, Hkv, Tmax, d, bits)
+    qb, qf = bf16_bits(rng.normal(size=(B, Tn, Hq, d)) * 2.0)
+    ref = oracle.attention_prefill(qf, 8, kc, ks, vc, vs, bits, start)
+    got = host(hbl.attention_prefill(to_dev_bf16(qb), 8, kcd, ksd, vcd, vsd, bits, torch.from_numpy(start).cuda()))
+    check_prefill(got, ref, vc, vs, bits, Hq, Hkv, start)
+
+
+def test_attention_prefill_from_appended_cache_and_qbits():
+    # keys and values appended by the library, the oracle fed the same codes
+    rng = np.random.default_rng(5)
+    B, Tn, Hq, Hkv, d, Tmax, bits = 2, 80, 2, 2, 128, 96, 3
+    kb, kf = bf16_bits(rng.normal(size=(B, Tn, Hkv, d)))
+    vb, vf = bf16_bits(rng.normal(size=(B, Tn, Hkv, d)))
+    cache = hbl.KVCache(B, Hkv, Tmax, d, bits)
+    start = np.array([0, 10], np.int32)
+    sd = torch.from_numpy(start).cuda()
+    cache.append(to_dev_bf16(kb), to_dev_bf16(vb), sd)
+    kc = np.zeros((B, Hkv, Tmax, d), np.uint8); vc = np.zeros_like(kc)
+    ks = np.zeros((B, Hkv, Tmax), np.float32); vs = np.zeros_like(ks)
+    for b in range(B):
+        for h in range(Hkv):
+            c, s_, _ = oracle.quant_heads(kf[b, :, h], bits)
+            kc[b, h, start[b]:start[b] + Tn] = c; ks[b, h, start[b]:start[b] + Tn] = s_
+            c, s_, _ = oracle.quant_heads(vf[b, :, h], bits)
+            vc[b, h, start[b]:start[b] + Tn] = c; vs[b, h, start[b]:start[b] + Tn] = s_
+    # rows before start[1] of sequence 1 were never written: give both sides the same (zero) rows
+    qb, qf = bf16_bits(rng.normal(size=(B, Tn, Hq, d)))
+    for qbits in (8, 4):
+        ref = oracle.attention_prefill(qf, qbits, kc, ks, vc, vs, bits, start)
+        got = host(hbl.attention_prefill(to_dev_bf16(qb), qbits, cache.k_codes, cache.k_scale, cache.v_codes,
+                                         cache.v_scale, bits, sd))
+        check_prefill(got, ref, vc, vs, bits, Hq, Hkv, start)
+
+
+def test_attention_prefill_full_size_sampled():
+    """A 7B-shaped prefill (4 sequences x 2048 new tokens, 32 heads of 128,
+    3-bit cache): sampled (token, head) pairs against the oracle's decode
+    step at each token's position."""
+    rng = np.random.default_rng(123)
+    B, Tn, H, d, bits = 4, 2048, 32, 128, 3
+    Tmax = Tn
+    Z = 4
+    rb = d * bits // 8
+    codes_k = rng.integers(Z - 3, Z + 4, size=(B, H, Tmax, d)).astype(np.uint8)
+    codes_v = rng.integers(Z - 3, Z + 4, size=(B, H, Tmax, d)).astype(np.uint8)
+    ks = rng.uniform(0.02, 0.3, size=(B, H, Tmax)).astype(np.float32)
+    vs = rng.uniform(0.02, 0.3, size=(B, H, Tmax)).astype(np.float32)
+    kcd = torch.from_numpy(pack_heads(codes_k.reshape(-1, d), bits).reshape(B, H, Tmax, rb)).cuda()
+    vcd = torch.from_numpy(pack_heads(codes_v.reshape(-1, d), bits).reshape(B, H, Tmax, rb)).cuda()
+    qb, qf = bf16_bits(rng.normal(size=(B, Tn, H, d)) * 3.0)
+    start = np.zeros(B, np.int32)
+    got = host(hbl.attention_prefill(to_dev_bf16(qb), 8, kcd, torch.from_numpy(ks).cuda(), vcd,
+                                     torch.from_numpy(vs).cuda(), bits, torch.from_numpy(start).cuda()))
+    for (b, i, h) in [(0, 0, 0), (1, 63, 5), (2, 64, 17), (3, 2047, 31), (0, 1000, 9), (2, 1535, 22)]:
+        ref = oracle.attention_decode(qf[b:b + 1, i], 8, codes_k[b:b + 1], ks[b:b + 1], codes_v[b:b + 1],
+                                      vs[b:b + 1], bits, np.array([i + 1], np.int32))
+        vh = (codes_v[b, h, :i + 1].astype(np.float64) - Z) * vs[b, h, :i + 1, None]
+        err = np.max(np.abs(got[b, i, h] - ref[0, h]))
+        assert err <= PF_TOL * np.max(np.abs(vh)), (b, i, h, err)

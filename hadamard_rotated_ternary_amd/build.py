@@ -19,6 +19,11 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# Per-source additions.  The prefill attention kernel keeps its matrix-core
+# accumulators in architectural VGPRs (the default heuristic parks them in
+# accumulation registers and copies all of them back on every key block).
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+OBJ = os.path.join(HERE, "_build")
 
 
 def sources():
@@ -35,14 +40,33 @@ def stale() -> bool:
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link libhbl.so."""
+    os.makedirs(OBJ, exist_ok=True)
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    jobs = []
+    for name in SOURCES:
+        obj = os.path.join(OBJ, name + ".o")
+        cmd = [HIPCC, *compile_flags, *EXTRA.get(name, []), *inc, "-c", os.path.join(CSRC, name), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((name, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for name, _, proc in jobs:
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(name)
+    if failed:
+        raise RuntimeError("hipcc failed on " + ", ".join(failed))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(HERE, "..", "include"), *sources(), "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *[o for _, o, _ in jobs], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libhbl.so")
+        raise RuntimeError("hipcc failed linking libhbl.so")
     os.replace(tmp, LIB)
     return LIB
 

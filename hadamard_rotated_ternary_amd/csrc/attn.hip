@@ -584,45 +584,162 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Prefill (causal) attention over the quantised cache, on the matrix cores.
-// One workgroup (4 waves) per (sequence, query head, block of 64 new
-// tokens); each wave owns 16 queries.  Key blocks of 64 cached tokens:
-//   the block's key codes go to LDS as signed bytes (u - Z) and its value
-//   codes as bf16 u (exact small integers), transposed to [channel][token]
-//   because the second product contracts over tokens;
-//   scores: v_mfma_i32_16x16x64_i8 of the query codes with the key codes
-//   (exact), times sq * sk / sqrt(D), causal mask, online softmax in fp32;
-//   values: P' = P * sv rounded to bf16, v_mfma_f32_16x16x32_bf16 with u,
-//   and the (u - Z) form from the sum of P'.
-// 16x16 accumulator layout: lane l / register r hold row 4*(l/16) + r,
-// column l%16; A operands: row l%16, k block l/16; B operands: column l%16,
-// k block l/16.
-constexpr int PF_QB = 64, PF_TB = 64;
+// One workgroup (4 waves) per (sequence, query head, block of 128 new
+// tokens); each wave owns 32 queries (two 16-query tiles).  Key blocks of 64
+// cached tokens, double-buffered in LDS: the raw codes of block kb+1 are
+// loaded into registers while block kb is computed, then unpacked into the
+// other buffer, so one barrier per block suffices.
+//   keys: signed bytes u - Z, [token][channel];
+//   values: bf16 of 128 + u (bit pattern 0x4300 | u, exact for u < 128) or,
+//   for 8-bit codes, of u; stored [channel][token] so the value product
+//   contracts over tokens, tokens of a 32-token half permuted so that the 8
+//   a lane supplies to one product are adjacent (one 16-byte read);
+//   scores, transposed: S^T = K . Q^T on v_mfma_i32_16x16x64_i8 (exact), so
+//   a lane holds 4 tokens of one query per 16x16 tile; the key scale with
+//   1/sqrt(D) and log2(e) folded in multiplies the integer score, the query
+//   scale enters through one fma inside the exponential;
+//   online softmax per query with a lazily raised maximum: the accumulators
+//   are rescaled only when a block's maximum exceeds the running one by more
+//   than 2^8, which changes no result (every term is relative to the same
+//   reference) and keeps every weight below 2^8;
+//   values: O^T += V^T . P'^T on v_mfma_f32_16x16x32_bf16, with P' = P * sv
+//   rounded to bf16 taken straight from the score registers, plus one
+//   all-ones tile that yields sum P' per query; the value offset
+//   (128 + Z, or Z for 8-bit codes) is removed with that sum at the end.
+// 16x16 layouts: accumulator lane l / register r: row 4*(l/16) + r, column
+// l%16; A operand: row l%16, k block l/16; B operand: column l%16, k block l/16.
+constexpr int PF_QB = 128, PF_TB = 64;
+constexpr float kLazyMax = 8.0f;                      // log2 of the largest weight between rescalings
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct PfCfg {
-  static constexpr int KROW = D + 16;          // key tile row (bytes)
-  static constexpr int VROW = PF_TB + 8;       // value tile row (bf16 per channel)
-  static constexpr int PROW = PF_TB + 8;       // P row (bf16 per query)
-  static constexpr int QROW = D + 16;          // query codes row (bytes)
-  static constexpr int GPR = D / 32;           // 32-code groups per row
+  static constexpr int GPR = D / 32;                  // 32-code groups per row
+  static constexpr int KROW = D + 16;                 // key tile row (bytes)
+  static constexpr int VROW = PF_TB + 8;              // value tile row (bf16 per channel)
+  static constexpr int QROW = D + 16;                 // query codes row (bytes)
+  static constexpr int KT = PF_TB * KROW;             // bytes of one key tile
+  static constexpr int VT = D * VROW * 2;             // bytes of one value tile
+  static constexpr int BUF = KT + VT + 2 * PF_TB * 4; // keys, values, key and value scales
+  static constexpr int NIT = PF_TB * GPR;             // staging items per block (keys; values alike)
+  static constexpr int IPT = (NIT + 255) / 256;       // items per thread
+  static_assert(PF_QB * QROW <= BUF, "query codes reuse the second buffer");
 };
+
+// Raw codes and scales of one key block held in registers between the load
+// and the unpack into LDS.
+template <int D, int KB>
+struct PfRaw {
+  uint32_t k[PfCfg<D>::IPT][KB], v0[PfCfg<D>::IPT][KB], v1[PfCfg<D>::IPT][KB];
+  float ks, vs;
+};
+
+template <int D, int KB>
+HBL_DEV void pf_load(PfRaw<D, KB>& r, int t0, int tid, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                     __amdgpu_buffer_rsrc_t kss, __amdgpu_buffer_rsrc_t vss) {
+  using C = PfCfg<D>;
+  constexpr int RDW = D / 32 * KB;
+#pragma unroll
+  for (int u = 0; u < C::IPT; ++u) {
+    const int it = tid + 256 * u;
+    if (C::NIT % 256 == 0 || it < C::NIT) {
+      const int row = it / C::GPR, grp = it % C::GPR;
+      buffer_words<KB>(krs, ((t0 + row) * RDW + grp * KB) * 4, r.k[u]);
+      const int pr = it % 32, grp2 = it / 64;
+      buffer_words<KB>(vrs, ((t0 + 2 * pr) * RDW + grp2 * KB) * 4, r.v0[u]);
+      buffer_words<KB>(vrs, ((t0 + 2 * pr + 1) * RDW + grp2 * KB) * 4, r.v1[u]);
+    }
+  }
+  if (tid < PF_TB) {
+    r.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kss, (t0 + tid) * 4, 0, 0));
+    r.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vss, (t0 + tid) * 4, 0, 0));
+  }
+}
+
+template <int D, int KB>
+HBL_DEV void pf_store(const PfRaw<D, KB>& r, char* buf, int tid) {
+  using C = PfCfg<D>;
+  constexpr int ZK = KB == 8 ? 128 : (1 << (KB - 1));
+  constexpr float kInvSqrtD = D == 64 ? 0.125f : (D == 128 ? 0.08838834764831845f : 0.0625f);
+  int8_t* kt = reinterpret_cast<int8_t*>(buf);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(buf + C::KT);
+  float* sc = reinterpret_cast<float*>(buf + C::KT + C::VT);
+#pragma unroll
+  for (int u = 0; u < C::IPT; ++u) {
+    const int it = tid + 256 * u;
+    if (C::NIT % 256 == 0 || it < C::NIT) {
+      // keys: token row, one 32-code group
+      {
+        const int row = it / C::GPR, grp = it % C::GPR;
+        uint32_t qd[8], sb[8];
+        unpack_quads<KB>(r.k[u], qd);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if constexpr (KB == 8) sb[k] = qd[k] ^ 0x80808080u;
+          else if constexpr (KB == 3) sb[k] = __builtin_amdgcn_perm(0x03020100u, 0xFFFEFDFCu, qd[k]);   // byte table u - 4
+          else if constexpr (KB == 2) sb[k] = __builtin_amdgcn_perm(0u, 0x0100FFFEu, qd[k]);            // byte table u - 2
+          else sb[k] = ((qd[k] | 0x80808080u) - (uint32_t)ZK * 0x01010101u) ^ 0x80808080u;
+        }
+        int8_t* kd = kt + row * C::KROW + grp * 32;
+        *reinterpret_cast<uint4*>(kd) = make_uint4(sb[0], sb[1], sb[2], sb[3]);
+        *reinterpret_cast<uint4*>(kd + 16) = make_uint4(sb[4], sb[5], sb[6], sb[7]);
+      }
+      // values: token pair pr, group it / 64, quads {0,1,4,5} or {2,3,6,7}
+      // (the two halves of a wave write channels 8 apart: distinct banks)
+      {
+        const int pr = it % 32, grp = it / 64;
+        const bool h = (it / 32) & 1;
+        uint32_t d0[8], d1[8], e0[4], e1[4];
+        unpack_quads<KB>(r.v0[u], d0);
+        unpack_quads<KB>(r.v1[u], d1);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {                            // quads k0 and k0 + 2, k0 in {0, 1, 4, 5}
+          const int k0 = (kk & 1) + 4 * (kk >> 1);
+          e0[kk] = h ? d0[k0 + 2] : d0[k0];
+          e1[kk] = h ? d1[k0 + 2] : d1[k0];
+        }
+        const int t = 2 * pr;                                       // 32j + 16h' + 4g + r
+        const int pos = (t & 32) | (((t >> 2) & 3) << 3) | (((t >> 4) & 1) << 2) | (t & 3);
+        uint32_t* vd = reinterpret_cast<uint32_t*>(vt + (grp * 32 + (h ? 8 : 0)) * C::VROW + pos);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int k0 = (kk & 1) + 4 * (kk >> 1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t w;
+            if constexpr (KB == 8) {
+              const uint32_t lo = __float_as_uint((float)((e0[kk] >> (8 * i)) & 0xFFu));
+              const uint32_t hi = __float_as_uint((float)((e1[kk] >> (8 * i)) & 0xFFu));
+              w = __builtin_amdgcn_perm(hi, lo, 0x07060302u);      // high halves: bf16 of u, exact
+            } else {
+              w = __builtin_amdgcn_perm(e1[kk], e0[kk], (uint32_t)i | 0x0C00u | ((uint32_t)(4 + i) << 16) | 0x0C000000u) |
+                  0x43004300u;                                      // bf16 of 128 + u
+            }
+            vd[(4 * k0 + i) * (C::VROW / 2)] = w;
+          }
+        }
+      }
+    }
+  }
+  if (tid < PF_TB) {
+    sc[tid] = r.ks * (kInvSqrtD * kLog2e);
+    sc[PF_TB + tid] = r.vs;
+  }
+}
 
 template <int D, int KB>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
   using C = PfCfg<D>;
-  __shared__ __align__(16) int8_t kt[PF_TB * C::KROW];
-  __shared__ __align__(16) uint16_t vt[D * C::VROW];
-  __shared__ __align__(16) uint16_t pt[4 * 16 * C::PROW];
-  __shared__ __align__(16) int8_t qt[PF_QB * C::QROW];
-  __shared__ float ksc[PF_TB], vsc[PF_TB], qsc[PF_QB];
+  __shared__ __align__(16) char lds[2 * C::BUF];
 
+  const int BH = a.B * a.Hq;
   const int nqb = (a.Tn + PF_QB - 1) / PF_QB;
-  // heavy (late) query blocks first
-  const int64_t L = blockIdx.x;
-  const int qblk = nqb - 1 - (int)(L % nqb);
-  const int64_t bh = L / nqb;
-  const int hq = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const int L = blockIdx.x;
+  // heaviest query blocks first; consecutive workgroups (which land on
+  // different XCDs) take different heads of the same query block
+  const int qblk = nqb - 1 - L / BH;
+  const int bh = L % BH;
+  const int hq = bh % a.Hq, b = bh / a.Hq;
   const int hk = hq / (a.Hq / a.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -633,56 +750,6 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
   int len = start + qend;                                     // keys needed by the last query
   len = len > a.Tmax ? (int)a.Tmax : len;
 
-  // ---- queries: per-head absmax codes of the block's 64 tokens (4 threads per row)
-  {
-    const int row = tid >> 2, qq = tid & 3;
-    const int i = q0 + row;
-    float v[D / 4];
-    if (i < a.Tn) {
-      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.Tn + i) * a.Hq + hq) * D + qq * (D / 4);
-#pragma unroll
-      for (int u = 0; u < D / 32; ++u) {
-        const uint4 w = reinterpret_cast<const uint4*>(qp)[u];
-        v[8 * u + 0] = bf16_lo(w.x); v[8 * u + 1] = bf16_hi(w.x); v[8 * u + 2] = bf16_lo(w.y);
-        v[8 * u + 3] = bf16_hi(w.y); v[8 * u + 4] = bf16_lo(w.z); v[8 * u + 5] = bf16_hi(w.z);
-        v[8 * u + 6] = bf16_lo(w.w); v[8 * u + 7] = bf16_hi(w.w);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < D / 4; ++e) v[e] = 0.0f;
-    }
-    float m = 0.0f;
-#pragma unroll
-    for (int e = 0; e < D / 4; ++e) m = fmaxf(m, fabsf(v[e]));
-    m = lane_reduce<4, true>(m);
-    const float G = fmaxf(m, kEpsQ);
-    const float qb = (float)((1 << (a.qbits - 1)) - 1);
-    const float rq = qb / G;
-#pragma unroll
-    for (int e = 0; e < D / 4; e += 4) {
-      uint32_t pk = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pk |= ((uint32_t)round_ratio(v[e + k] * qb, G, v[e + k] * rq) & 0xFFu) << (8 * k);
-      *reinterpret_cast<uint32_t*>(qt + row * C::QROW + qq * (D / 4) + e) = pk;
-    }
-    if (qq == 0) qsc[row] = G / qb;
-  }
-  __syncthreads();
-  // query A operands of this wave's 16 rows: k-step s covers channels 64s .. 64s+63
-  v4i qa[D / 64];
-#pragma unroll
-  for (int s2 = 0; s2 < D / 64; ++s2)
-    qa[s2] = *reinterpret_cast<const v4i*>(qt + (wave * 16 + l16) * C::QROW + 64 * s2 + 16 * g4);
-  float sqr[4];
-  int qpos[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = wave * 16 + 4 * g4 + r;
-    sqr[r] = qsc[row];
-    qpos[r] = start + q0 + row;                 // this query's position (keys 0 .. qpos)
-  }
-  constexpr float kInvSqrtD = D == 64 ? 0.125f : (D == 128 ? 0.08838834764831845f : 0.0625f);
-
   constexpr int RDW = D / 32 * KB;
   const int64_t head_row = ((int64_t)b * a.Hkv + hk) * a.Tmax;
   const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + head_row * RDW * 4), (short)0, len * RDW * 4,
@@ -691,130 +758,207 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
                                                      kBufferFlags);
   const auto kss = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + head_row), (short)0, len * 4, kBufferFlags);
   const auto vss = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + head_row), (short)0, len * 4, kBufferFlags);
+
+  PfRaw<D, KB> raw;
+  pf_load<D, KB>(raw, 0, tid, krs, vrs, kss, vss);
+
+  // ---- query codes of the block's 128 tokens (2 threads per row, D/2 channels each), in buffer 1
+  int8_t* qt = reinterpret_cast<int8_t*>(lds + C::BUF);
+  float* qsc = reinterpret_cast<float*>(lds);                 // buffer 0 is free until the first store
+  {
+    const int row = tid >> 1, hh = tid & 1;
+    const int i = q0 + row;
+    float v[D / 2];
+    if (i < a.Tn) {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.Tn + i) * a.Hq + hq) * D + hh * (D / 2);
+#pragma unroll
+      for (int u = 0; u < D / 16; ++u) {
+        const uint4 w = reinterpret_cast<const uint4*>(qp)[u];
+        v[8 * u + 0] = bf16_lo(w.x); v[8 * u + 1] = bf16_hi(w.x); v[8 * u + 2] = bf16_lo(w.y);
+        v[8 * u + 3] = bf16_hi(w.y); v[8 * u + 4] = bf16_lo(w.z); v[8 * u + 5] = bf16_hi(w.z);
+        v[8 * u + 6] = bf16_lo(w.w); v[8 * u + 7] = bf16_hi(w.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < D / 2; ++e) v[e] = 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < D / 2; ++e) m = fmaxf(m, fabsf(v[e]));
+    m = lane_reduce<2, true>(m);
+    const float G = fmaxf(m, kEpsQ);
+    const float qb = (float)((1 << (a.qbits - 1)) - 1);
+    const float rq = qb / G;
+#pragma unroll
+    for (int e = 0; e < D / 2; e += 4) {
+      uint32_t pk = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pk |= ((uint32_t)round_ratio(v[e + k] * qb, G, v[e + k] * rq) & 0xFFu) << (8 * k);
+      *reinterpret_cast<uint32_t*>(qt + row * C::QROW + hh * (D / 2) + e) = pk;
+    }
+    if (hh == 0) qsc[row] = G / qb;
+  }
+  __syncthreads();
+  // query B operands of this wave's two 16-query tiles: column = query l16,
+  // k-step s covers channels 64s .. 64s+63
+  v4i qB[2][D / 64];
+  float sq[2];
+  int qpos[2];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const int row = wave * 32 + qi * 16 + l16;
+#pragma unroll
+    for (int s2 = 0; s2 < D / 64; ++s2) qB[qi][s2] = *reinterpret_cast<const v4i*>(qt + row * C::QROW + 64 * s2 + 16 * g4);
+    sq[qi] = qsc[row];
+    qpos[qi] = start + q0 + row;               // keys 0 .. qpos
+  }
+  __syncthreads();                             // query codes and scales read: both buffers free
+  pf_store<D, KB>(raw, lds, tid);
+  __syncthreads();
+
   constexpr int ZK = KB == 8 ? 128 : (1 << (KB - 1));
+  constexpr float kOff = KB == 8 ? (float)ZK : 128.0f + (float)ZK;
+  const bf8v ones = __builtin_bit_cast(bf8v, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
-  v4f o[D / 16];
+  v4f o[2][D / 16], os[2];                            // O^T tiles [query tile][channel tile]; sum P'
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) o[c] = v4f{0.f, 0.f, 0.f, 0.f};
-  float mrow[4], lrow[4], sprow[4];
+  for (int qi = 0; qi < 2; ++qi) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.0f; sprow[r] = 0.0f; }
+    for (int c = 0; c < D / 16; ++c) o[qi][c] = v4f{0.f, 0.f, 0.f, 0.f};
+    os[qi] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  float mq[2] = {-INFINITY, -INFINITY}, lq[2] = {0.f, 0.f};
 
+  const int wfirst = start + q0 + wave * 32;          // the wave's first and last query positions
+  const int wlast = wfirst + 31;
   const int nkb = (len + PF_TB - 1) / PF_TB;
   for (int kb = 0; kb < nkb; ++kb) {
     const int t0 = kb * PF_TB;
-    // ---- stage the key and value tiles (one 32-code group per thread and pass)
-    for (int it = tid; it < PF_TB * C::GPR; it += 256) {
-      const int row = it / C::GPR, grp = it % C::GPR;
-      const int t = t0 + row;
-      uint32_t w[KB], qd[8];
-      buffer_words<KB>(krs, (t * RDW + grp * KB) * 4, w);
-      unpack_quads<KB>(w, qd);
-      uint32_t sb[8];
+    if (kb + 1 < nkb) pf_load<D, KB>(raw, t0 + PF_TB, tid, krs, vrs, kss, vss);
+    const char* buf = lds + (kb & 1) * C::BUF;
+    const int8_t* kt = reinterpret_cast<const int8_t*>(buf);
+    const uint16_t* vt = reinterpret_cast<const uint16_t*>(buf + C::KT);
+    const float* ksl = reinterpret_cast<const float*>(buf + C::KT + C::VT);
+    const float* vsl = ksl + PF_TB;
+    if (t0 <= wlast) {
+      // ---- S^T tiles: rows = tokens nt*16 + 4*g4 + r, column = query l16; x = score * log2(e) / sq
+      float x[2][4][4];                                // [query tile][token tile][register]
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        sb[k] = KB == 8 ? (qd[k] ^ 0x80808080u) : (((qd[k] | 0x80808080u) - (uint32_t)ZK * 0x01010101u) ^ 0x80808080u);
-      int8_t* kd = kt + row * C::KROW + grp * 32;
-      *reinterpret_cast<uint4*>(kd) = make_uint4(sb[0], sb[1], sb[2], sb[3]);
-      *reinterpret_cast<uint4*>(kd + 16) = make_uint4(sb[4], sb[5], sb[6], sb[7]);
-      buffer_words<KB>(vrs, (t * RDW + grp * KB) * 4, w);
-      unpack_quads<KB>(w, qd);
+      for (int nt = 0; nt < 4; ++nt) {
+        v4i ka[D / 64];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
+        for (int s2 = 0; s2 < D / 64; ++s2)
+          ka[s2] = *reinterpret_cast<const v4i*>(kt + (nt * 16 + l16) * C::KROW + 64 * s2 + 16 * g4);
+        const float4 kf = *reinterpret_cast<const float4*>(ksl + nt * 16 + 4 * g4);
+        const float kscl[4] = {kf.x, kf.y, kf.z, kf.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float f = (float)((qd[k] >> (8 * i)) & 0xFFu);           // exact in bf16 (< 256)
-          vt[(grp * 32 + 4 * k + i) * C::VROW + row] = (uint16_t)(__float_as_uint(f) >> 16);
+        for (int qi = 0; qi < 2; ++qi) {
+          v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int s2 = 0; s2 < D / 64; ++s2) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[s2], qB[qi][s2], acc, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[qi][nt][r] = (float)acc[r] * kscl[r];
         }
-      if (grp == 0) {
-        ksc[row] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kss, t * 4, 0, 0));
-        vsc[row] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vss, t * 4, 0, 0));
+      }
+      if (t0 + PF_TB - 1 > wfirst || t0 + PF_TB > len) {   // a block on the diagonal or past the end
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = t0 + nt * 16 + 4 * g4 + r;
+              if (t > qpos[qi] || t >= len) x[qi][nt][r] = -INFINITY;
+            }
+      }
+      // ---- running maximum per query (the 16 values of a lane, then lanes l16 + 16j)
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bm = fmaxf(bm, x[qi][nt][r]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        const float zm = sq[qi] * bm;
+        if (__any(zm > mq[qi] + kLazyMax)) {
+          const float mn = fmaxf(mq[qi], zm);
+          const float fac = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mq[qi] - mn);
+          mq[qi] = mn;
+          lq[qi] *= fac;
+          os[qi] *= fac;
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) o[qi][c] *= fac;
+        }
+      }
+      // ---- P'^T as bf16 B operands (8 tokens per lane per 32-token half) and O^T += V^T P'^T
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float vsr[2][4];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float4 vf = *reinterpret_cast<const float4*>(vsl + (2 * j + h2) * 16 + 4 * g4);
+          vsr[h2][0] = vf.x; vsr[h2][1] = vf.y; vsr[h2][2] = vf.z; vsr[h2][3] = vf.w;
+        }
+        bf8v pb[2];
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi) {
+          float ls = 0.f;
+          uint32_t pk[4];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int nt = 2 * j + h2;
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[qi], x[qi][nt][r], -mq[qi]));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[qi], x[qi][nt][r + 1], -mq[qi]));
+              ls += p0;
+              ls += p1;
+              const f2 pv = {p0 * vsr[h2][r], p1 * vsr[h2][r + 1]};
+              pk[2 * h2 + r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pv, bf2));
+            }
+          }
+          pb[qi] = __builtin_bit_cast(bf8v, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+          lq[qi] += ls;
+        }
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          // V^T operand: channel c*16 + l16, the 8 adjacent positions 32j + 8*g4 .. +7
+          const bf8v va = *reinterpret_cast<const bf8v*>(vt + (c * 16 + l16) * C::VROW + 32 * j + 8 * g4);
+#pragma unroll
+          for (int qi = 0; qi < 2; ++qi) o[qi][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qi], o[qi][c], 0, 0, 0);
+        }
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi) os[qi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qi], os[qi], 0, 0, 0);
       }
     }
-    __syncthreads();
-    // ---- scores of this wave's 16 queries against the 64 keys
-    float sc[4][4];        // [key tile][register]
-    float bm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      v4i acc = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int s2 = 0; s2 < D / 64; ++s2) {
-        const v4i kb4 = *reinterpret_cast<const v4i*>(kt + (nt * 16 + l16) * C::KROW + 64 * s2 + 16 * g4);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[s2], kb4, acc, 0, 0, 0);
-      }
-      const int tcol = nt * 16 + l16;
-      const float kscale = ksc[tcol] * kInvSqrtD;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = (float)acc[r] * (sqr[r] * kscale);
-        sc[nt][r] = t0 + tcol <= qpos[r] && t0 + tcol < len ? v : -INFINITY;
-        bm[r] = fmaxf(bm[r], sc[nt][r]);
-      }
-    }
-    // row max over the 16 lanes that share the rows
-#pragma unroll
-    for (int r = 0; r < 4; ++r) bm[r] = lane_reduce<16, true>(bm[r]);
-    float fac[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mn = fmaxf(mrow[r], bm[r]);
-      fac[r] = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((mrow[r] - mn) * kLog2e);
-      mrow[r] = mn;
-      lrow[r] *= fac[r];
-      sprow[r] *= fac[r];
-    }
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[c][r] *= fac[r];
-    // P' = exp(s - m) * sv as bf16 into this wave's P tile (rows = queries)
-    uint16_t* pw = pt + wave * 16 * C::PROW;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f}, sp[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int tcol = nt * 16 + l16;
-      const float vscale = vsc[tcol];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = sc[nt][r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((sc[nt][r] - mrow[r]) * kLog2e);
-        ls[r] += pr;
-        const uint16_t pb = f32_to_bf16(pr * vscale);
-        sp[r] += __uint_as_float((uint32_t)pb << 16);
-        pw[(4 * g4 + r) * C::PROW + tcol] = pb;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      lrow[r] += lane_reduce<16, false>(ls[r]);
-      sprow[r] += lane_reduce<16, false>(sp[r]);
-    }
-    __syncthreads();   // P tiles written (and every wave past the score reads of kt)
-    // ---- O += P' . u over the 64 keys
-#pragma unroll
-    for (int s2 = 0; s2 < PF_TB / 32; ++s2) {
-      const bf8v pa = *reinterpret_cast<const bf8v*>(pw + l16 * C::PROW + 32 * s2 + 8 * g4);
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf8v vb = *reinterpret_cast<const bf8v*>(vt + (c * 16 + l16) * C::VROW + 32 * s2 + 8 * g4);
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[c], 0, 0, 0);
-      }
-    }
-    __syncthreads();   // tiles free for the next block
+    if (kb + 1 < nkb) pf_store<D, KB>(raw, lds + ((kb + 1) & 1) * C::BUF, tid);
+    __syncthreads();   // the next block is staged; this one is free for the block after
   }
-  // ---- out = (O - Z * sum P') / sum P
+  // ---- per-query sums over the 4 lanes of a column, then out = (O - off * sum P') / sum P
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = wave * 16 + 4 * g4 + r, i = q0 + row;
+  for (int qi = 0; qi < 2; ++qi) {
+    lq[qi] += __shfl_xor(lq[qi], 16, 64);
+    lq[qi] += __shfl_xor(lq[qi], 32, 64);
+    const int i = q0 + wave * 32 + qi * 16 + l16;
     if (i >= a.Tn) continue;
-    const float inv = lrow[r] > 0.0f ? 1.0f / lrow[r] : 0.0f;
-    const float zs = (float)ZK * sprow[r];
+    const float inv = lq[qi] > 0.0f ? 1.0f / lq[qi] : 0.0f;
+    const float zs = kOff * os[qi][0];
     const int64_t ob = (((int64_t)b * a.Tn + i) * a.Hq + hq) * D;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const float v = (o[c][r] - zs) * inv;
-      if (a.out_bf16) static_cast<uint16_t*>(a.out)[ob + c * 16 + l16] = f32_to_bf16(v);
-      else static_cast<float*>(a.out)[ob + c * 16 + l16] = v;
+      const int ch = c * 16 + 4 * g4;
+      const float v0 = (o[qi][c][0] - zs) * inv, v1 = (o[qi][c][1] - zs) * inv;
+      const float v2 = (o[qi][c][2] - zs) * inv, v3 = (o[qi][c][3] - zs) * inv;
+      if (a.out_bf16) {
+        uint2 pk;
+        pk.x = f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+        pk.y = f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ob + ch) = pk;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ob + ch) = make_float4(v0, v1, v2, v3);
+      }
     }
   }
 }

@@ -29,6 +29,7 @@ METRIC = "H-BitLinear tokens/s + effective int TOPS & HBM GB/s vs roofline, 7B W
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
 PEAK_FP6_TFLOPS = 10100.0    # MI355X dense fp6 / fp4 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wdown_7b_int4_hbm_traffic.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "hadamard_rotated_ternary_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
 
@@ -396,13 +397,41 @@ def attention_extra(torch, hbl, synthetic, args):
     cache_bytes = 2 * rows * row_bytes
     dec_bytes = cache_bytes + w.B * w.Hq * w.d * 4
     app_bytes = 2 * rows * w.d * 2 + cache_bytes
-    return {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "T": w.T, "kv_bits": w.kv_bits, "q_bits": w.q_bits,
-            "decode_us": t_dec, "decode_gbps": dec_bytes / (t_dec / 1e6) / 1e9,
-            "decode_hbm_frac": dec_bytes / (t_dec / 1e6) / 1e9 / PEAK_HBM_GBS,
-            "decode_traffic_bytes": stored_attn_traffic(),
-            "bf16_cache_hbm_floor_us": (2 * rows * (w.d * 2)) / (PEAK_HBM_GBS * 1e9) * 1e6,
-            "append_prefill_us": t_app, "append_gbps": app_bytes / (t_app / 1e6) / 1e9,
-            "timing": "events around back-to-back calls; cache and lengths resident in HBM"}
+    res = {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "T": w.T, "kv_bits": w.kv_bits, "q_bits": w.q_bits,
+           "decode_us": t_dec, "decode_gbps": dec_bytes / (t_dec / 1e6) / 1e9,
+           "decode_hbm_frac": dec_bytes / (t_dec / 1e6) / 1e9 / PEAK_HBM_GBS,
+           "decode_traffic_bytes": stored_attn_traffic(),
+           "bf16_cache_hbm_floor_us": (2 * rows * (w.d * 2)) / (PEAK_HBM_GBS * 1e9) * 1e6,
+           "append_prefill_us": t_app, "append_gbps": app_bytes / (t_app / 1e6) / 1e9,
+           "timing": "events around back-to-back calls; cache and lengths resident in HBM"}
+    del cache, kd, vd, qd, ws, out
+    res["prefill"] = prefill_extra(torch, hbl, synthetic, timed)
+    return res
+
+
+def prefill_extra(torch, hbl, synthetic, timed):
+    """Causal prefill of whole prompts over the 3-bit cache they were appended
+    to: integer query-key scores on the int8 matrix instruction, bf16 value
+    product.  Causal work: B*Hq*T(T+1)/2 query-key pairs, 4*d flops each, half
+    of them int8 (peak 5.0 P) and half bf16 (peak 2.5 P), so the mixed peak
+    for the whole is 1 / (0.5/5.0 + 0.5/2.5) = 3.33 PFLOP/s."""
+    w = synthetic.ATTN_WORKLOADS["prefill_attn_7b_kv3"]
+    q, k, v = synthetic.make_prefill(w)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    del q, k, v
+    cache = hbl.KVCache(w.B, w.Hkv, w.T, w.d, w.kv_bits)
+    start = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    t_app = timed(lambda: cache.append(kd, vd, start), 10)
+    out = torch.empty((w.B, w.T, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
+    t_pf = timed(lambda: hbl.attention_prefill(qd, w.q_bits, cache.k_codes, cache.k_scale, cache.v_codes,
+                                               cache.v_scale, w.kv_bits, start, out=out), 20)
+    flops = w.B * w.Hq * (w.T * (w.T + 1) / 2) * w.d * 4
+    mixed_peak = 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS)
+    return {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "kv_bits": w.kv_bits,
+            "q_bits": w.q_bits, "prefill_us": t_pf, "prefill_tflops": flops / (t_pf / 1e6) / 1e12,
+            "mixed_mfma_peak_tflops": mixed_peak, "prefill_mfma_frac": flops / (t_pf / 1e6) / 1e12 / mixed_peak,
+            "append_us": t_app, "flops_counted": "B*Hq*T(T+1)/2 pairs x 4d (scores and values, causal half)"}
 
 
 def cpu_baseline(x, wl, bits, budget_s):

@@ -141,10 +141,13 @@ class AttnWorkload:
 
 
 # A 7B-shaped model (32 heads of 128) decoding 16 sequences against 4096
-# cached tokens with the 3-bit KV cache, and a small case for tests.
+# cached tokens with the 3-bit KV cache, a small case for tests, and the
+# prefill of 4 prompts of 2048 tokens into an empty 3-bit cache (T is the
+# prompt length there).
 ATTN_WORKLOADS: Dict[str, AttnWorkload] = {
     "decode_attn_7b_kv3": AttnWorkload("decode_attn_7b_kv3", 16, 32, 32, 128, 4096, 3, 8, 4, 8.0, 11),
     "decode_attn_small": AttnWorkload("decode_attn_small", 4, 4, 2, 128, 1100, 3, 8, 4, 8.0, 12),
+    "prefill_attn_7b_kv3": AttnWorkload("prefill_attn_7b_kv3", 4, 32, 32, 128, 2048, 3, 8, 4, 8.0, 13),
 }
 
 
@@ -161,6 +164,20 @@ def make_heads(w: AttnWorkload, with_cache: bool = True):
     q = f32_to_bf16_bits(rng.standard_normal((w.B, w.Hq, w.d), dtype=np.float32))
     if not with_cache:
         return q, None, None
+    k = rng.standard_normal((w.B, w.T, w.Hkv, w.d), dtype=np.float32)
+    k[..., idx] *= np.float32(w.factor)
+    k = f32_to_bf16_bits(k)
+    v = f32_to_bf16_bits(rng.standard_normal((w.B, w.T, w.Hkv, w.d), dtype=np.float32))
+    return q, k, v
+
+
+def make_prefill(w: AttnWorkload):
+    """Draw the states of a whole prompt of w.T tokens: q [B][T][Hq][d] and
+    k, v [B][T][Hkv][d] as bf16 codes (uint16), distributed as in
+    ``make_heads``.  Draw order: outlier channels, q, k, v."""
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    idx = outlier_channels(rng, w.d, w.n_out)
+    q = f32_to_bf16_bits(rng.standard_normal((w.B, w.T, w.Hq, w.d), dtype=np.float32))
     k = rng.standard_normal((w.B, w.T, w.Hkv, w.d), dtype=np.float32)
     k[..., idx] *= np.float32(w.factor)
     k = f32_to_bf16_bits(k)

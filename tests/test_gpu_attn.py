@@ -253,7 +253,10 @@ def test_quantize_heads_empty_and_single_row():
 # Bar: |out - ref| <= (2^-8 + 3e-5) * max|v^| per (token, head): the scores
 # are exact integers scaled in fp32 (as in the decode step); the value
 # product rounds P * sv to bf16 (relative 2^-9), so the output moves by at
-# most 2^-9 of the largest value it averages.
+# most 2^-9 of the largest value it averages.  The kernel multiplies those
+# weights with 128 + u (exact in bf16) and removes 128 + Z times their sum
+# at the end; that cancellation costs fp32 accumulation error only, orders
+# of magnitude below the bar.
 PF_TOL = 2.0 ** -8 + ATTN_TOL
 
 
@@ -338,3 +341,48 @@ def test_attention_prefill_full_size_sampled():
         vh = (codes_v[b, h, :i + 1].astype(np.float64) - Z) * vs[b, h, :i + 1, None]
         err = np.max(np.abs(got[b, i, h] - ref[0, h]))
         assert err <= PF_TOL * np.max(np.abs(vh)), (b, i, h, err)
+
+
+@pytest.mark.parametrize("bits", [3, 8])
+def test_attention_prefill_rising_scores(bits):
+    """Key scales growing by 10^3 over the prompt make each key block's
+    largest score exceed the running maximum by far more than 2^8, so the
+    kernel's lazily raised maximum is raised (and the accumulators rescaled)
+    in the middle of the prompt, not only at its first block."""
+    rng = np.random.default_rng(77 + bits)
+    B, Hq, Hkv, d, Tn = 1, 2, 2, 128, 300
+    Z = 1 << (bits - 1)
+    qb_ = (1 << (bits - 1)) - 1
+    kc = rng.integers(Z - qb_, Z + qb_ + 1, size=(B, Hkv, Tn, d)).astype(np.uint8)
+    vc = rng.integers(Z - qb_, Z + qb_ + 1, size=(B, Hkv, Tn, d)).astype(np.uint8)
+    ks = (0.01 * 10.0 ** (3.0 * np.arange(Tn) / Tn)).astype(np.float32)[None, None].repeat(Hkv, 1)
+    vs = rng.uniform(0.05, 0.2, size=(B, Hkv, Tn)).astype(np.float32)
+    qb, qf = bf16_bits(rng.normal(size=(B, Tn, Hq, d)) * 3.0)
+    start = np.zeros(B, np.int32)
+    # the premise: block maxima of the scores (log2 units) rise by more than 8 between blocks
+    kh = (kc[0, 0].astype(np.float64) - Z) * ks[0, 0, :, None]
+    sc = (qf[0, -1, 0].astype(np.float64) @ kh.T) / np.sqrt(d) * np.log2(np.e)
+    bm = [sc[t:t + 64].max() for t in range(0, Tn, 64)]
+    assert max(np.diff(bm)) > 8.0
+    dev = lambda c: torch.from_numpy(pack_heads(c.reshape(-1, d), bits).reshape(B, Hkv, Tn, -1)).cuda()
+    ref = oracle.attention_prefill(qf, 8, kc, ks, vc, vs, bits, start)
+    got = host(hbl.attention_prefill(to_dev_bf16(qb), 8, dev(kc), torch.from_numpy(ks).cuda(), dev(vc),
+                                     torch.from_numpy(vs).cuda(), bits, torch.from_numpy(start).cuda()))
+    check_prefill(got, ref, vc, vs, bits, Hq, Hkv, start)
+
+
+def test_attention_prefill_empty_and_single_token():
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, d, Tmax, bits = 2, 4, 4, 64, 20, 4
+    (kc, ks, kcd, ksd), (vc, vs, vcd, vsd) = make_cache(rng, B, Hkv, Tmax, d, bits)
+    # no new tokens: nothing is launched, the output is empty
+    q0 = torch.empty((B, 0, Hq, d), dtype=torch.bfloat16, device="cuda")
+    st = torch.tensor([3, 7], dtype=torch.int32, device="cuda")
+    got0 = hbl.attention_prefill(q0, 8, kcd, ksd, vcd, vsd, bits, st)
+    assert tuple(got0.shape) == (B, 0, Hq, d)
+    # one new token at positions 3 and 19 (the last cache row)
+    start = np.array([3, 19], np.int32)
+    qb, qf = bf16_bits(rng.normal(size=(B, 1, Hq, d)))
+    ref = oracle.attention_prefill(qf, 8, kc, ks, vc, vs, bits, start)
+    got = host(hbl.attention_prefill(to_dev_bf16(qb), 8, kcd, ksd, vcd, vsd, bits, torch.from_numpy(start).cuda()))
+    check_prefill(got, ref, vc, vs, bits, Hq, Hkv, start)

@@ -584,8 +584,10 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Prefill (causal) attention over the quantised cache, on the matrix cores.
-// One workgroup (4 waves) per (sequence, query head, block of 128 new
-// tokens); each wave owns 32 queries (two 16-query tiles).  Key blocks of 64
+// One workgroup per (sequence, query head, block of new tokens): 8 waves and
+// 256 tokens for head sizes up to 128, 4 waves and 128 tokens for 256 (whose
+// registers allow one wave per SIMD); each wave owns 32 queries (two
+// 16-query tiles).  Key blocks of 64
 // cached tokens, double-buffered in LDS: the raw codes of block kb+1 are
 // loaded into registers while block kb is computed, then unpacked into the
 // other buffer, so one barrier per block suffices.
@@ -608,22 +610,28 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 //   (128 + Z, or Z for 8-bit codes) is removed with that sum at the end.
 // 16x16 layouts: accumulator lane l / register r: row 4*(l/16) + r, column
 // l%16; A operand: row l%16, k block l/16; B operand: column l%16, k block l/16.
-constexpr int PF_QB = 128, PF_TB = 64;
 constexpr float kLazyMax = 8.0f;                      // log2 of the largest weight between rescalings
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct PfCfg {
+  static constexpr int NW = D <= 128 ? 8 : 4;         // waves per workgroup
+  static constexpr int NT = 64 * NW;                  // threads
+  static constexpr int QB = 32 * NW;                  // new tokens (queries) per workgroup
+  static constexpr int TB = D <= 128 ? 128 : 64;      // cached tokens per key block
   static constexpr int GPR = D / 32;                  // 32-code groups per row
   static constexpr int KROW = D + 16;                 // key tile row (bytes)
-  static constexpr int VROW = PF_TB + 8;              // value tile row (bf16 per channel)
+  static constexpr int VROW = TB + 8;                 // value tile row (bf16 per channel)
   static constexpr int QROW = D + 16;                 // query codes row (bytes)
-  static constexpr int KT = PF_TB * KROW;             // bytes of one key tile
+  static constexpr int KT = TB * KROW;                // bytes of one key tile
   static constexpr int VT = D * VROW * 2;             // bytes of one value tile
-  static constexpr int BUF = KT + VT + 2 * PF_TB * 4; // keys, values, key and value scales
-  static constexpr int NIT = PF_TB * GPR;             // staging items per block (keys; values alike)
-  static constexpr int IPT = (NIT + 255) / 256;       // items per thread
-  static_assert(PF_QB * QROW <= BUF, "query codes reuse the second buffer");
+  static constexpr int BUF = KT + VT + 2 * TB * 4;    // keys, values, key and value scales
+  static constexpr int NIT = TB * GPR;                // staging items per block (keys; values alike)
+  // with at least twice as many threads as items, one half of the threads
+  // stages the keys and the other half the values
+  static constexpr bool SPLIT = NT >= 2 * NIT;
+  static constexpr int IPT = SPLIT ? 1 : (NIT + NT - 1) / NT;   // items per thread
+  static_assert(QB * QROW + QB * 4 <= 2 * BUF, "query codes and scales reuse the buffers");
 };
 
 // Raw codes and scales of one key block held in registers between the load
@@ -634,6 +642,18 @@ struct PfRaw {
   float ks, vs;
 };
 
+// Value staging item -> (token pair, 32-code group, half): the 64 lanes of a
+// wave take 32 consecutive token pairs twice, lanes 32..63 with the other
+// half of the group's quads (channels 8 apart: distinct LDS banks).
+template <int D>
+HBL_DEV void pf_vitem(int it, int& pr, int& grp, bool& h) {
+  constexpr int PB = PfCfg<D>::TB / 64;               // sets of 32 token pairs per block
+  const int w = it >> 6, lane = it & 63;
+  pr = (w % PB) * 32 + (lane & 31);
+  grp = w / PB;
+  h = lane >= 32;
+}
+
 template <int D, int KB>
 HBL_DEV void pf_load(PfRaw<D, KB>& r, int t0, int tid, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                      __amdgpu_buffer_rsrc_t kss, __amdgpu_buffer_rsrc_t vss) {
@@ -641,16 +661,21 @@ HBL_DEV void pf_load(PfRaw<D, KB>& r, int t0, int tid, __amdgpu_buffer_rsrc_t kr
   constexpr int RDW = D / 32 * KB;
 #pragma unroll
   for (int u = 0; u < C::IPT; ++u) {
-    const int it = tid + 256 * u;
-    if (C::NIT % 256 == 0 || it < C::NIT) {
-      const int row = it / C::GPR, grp = it % C::GPR;
+    const int itk = C::SPLIT ? tid : tid + C::NT * u;
+    const int itv = C::SPLIT ? tid - C::NIT : itk;
+    if (itk < C::NIT) {
+      const int row = itk / C::GPR, grp = itk % C::GPR;
       buffer_words<KB>(krs, ((t0 + row) * RDW + grp * KB) * 4, r.k[u]);
-      const int pr = it % 32, grp2 = it / 64;
+    }
+    if (itv >= 0 && itv < C::NIT) {
+      int pr, grp2;
+      bool h;
+      pf_vitem<D>(itv, pr, grp2, h);
       buffer_words<KB>(vrs, ((t0 + 2 * pr) * RDW + grp2 * KB) * 4, r.v0[u]);
       buffer_words<KB>(vrs, ((t0 + 2 * pr + 1) * RDW + grp2 * KB) * 4, r.v1[u]);
     }
   }
-  if (tid < PF_TB) {
+  if (tid < C::TB) {
     r.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kss, (t0 + tid) * 4, 0, 0));
     r.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vss, (t0 + tid) * 4, 0, 0));
   }
@@ -666,11 +691,12 @@ HBL_DEV void pf_store(const PfRaw<D, KB>& r, char* buf, int tid) {
   float* sc = reinterpret_cast<float*>(buf + C::KT + C::VT);
 #pragma unroll
   for (int u = 0; u < C::IPT; ++u) {
-    const int it = tid + 256 * u;
-    if (C::NIT % 256 == 0 || it < C::NIT) {
+    const int itk = C::SPLIT ? tid : tid + C::NT * u;
+    const int itv = C::SPLIT ? tid - C::NIT : itk;
+    {
       // keys: token row, one 32-code group
-      {
-        const int row = it / C::GPR, grp = it % C::GPR;
+      if (itk < C::NIT) {
+        const int row = itk / C::GPR, grp = itk % C::GPR;
         uint32_t qd[8], sb[8];
         unpack_quads<KB>(r.k[u], qd);
 #pragma unroll
@@ -686,20 +712,24 @@ HBL_DEV void pf_store(const PfRaw<D, KB>& r, char* buf, int tid) {
       }
       // values: token pair pr, group it / 64, quads {0,1,4,5} or {2,3,6,7}
       // (the two halves of a wave write channels 8 apart: distinct banks)
-      {
-        const int pr = it % 32, grp = it / 64;
-        const bool h = (it / 32) & 1;
+      if (itv >= 0 && itv < C::NIT) {
+        int pr, grp;
+        bool h;
+        pf_vitem<D>(itv, pr, grp, h);
         uint32_t d0[8], d1[8], e0[4], e1[4];
         unpack_quads<KB>(r.v0[u], d0);
         unpack_quads<KB>(r.v1[u], d1);
+        // quad k0 + 2h, k0 in {0, 1, 4, 5}: a byte permute picks one of two
+        // registers (a plain select would be folded into a runtime array index)
+        const uint32_t hsel = h ? 0x07060504u : 0x03020100u;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {                            // quads k0 and k0 + 2, k0 in {0, 1, 4, 5}
+        for (int kk = 0; kk < 4; ++kk) {
           const int k0 = (kk & 1) + 4 * (kk >> 1);
-          e0[kk] = h ? d0[k0 + 2] : d0[k0];
-          e1[kk] = h ? d1[k0 + 2] : d1[k0];
+          e0[kk] = __builtin_amdgcn_perm(d0[k0 + 2], d0[k0], hsel);
+          e1[kk] = __builtin_amdgcn_perm(d1[k0 + 2], d1[k0], hsel);
         }
         const int t = 2 * pr;                                       // 32j + 16h' + 4g + r
-        const int pos = (t & 32) | (((t >> 2) & 3) << 3) | (((t >> 4) & 1) << 2) | (t & 3);
+        const int pos = (t & ~31) | (((t >> 2) & 3) << 3) | (((t >> 4) & 1) << 2) | (t & 3);
         uint32_t* vd = reinterpret_cast<uint32_t*>(vt + (grp * 32 + (h ? 8 : 0)) * C::VROW + pos);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -721,19 +751,19 @@ HBL_DEV void pf_store(const PfRaw<D, KB>& r, char* buf, int tid) {
       }
     }
   }
-  if (tid < PF_TB) {
+  if (tid < C::TB) {
     sc[tid] = r.ks * (kInvSqrtD * kLog2e);
-    sc[PF_TB + tid] = r.vs;
+    sc[C::TB + tid] = r.vs;
   }
 }
 
 template <int D, int KB>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(PfCfg<D>::NT) void attn_prefill_kernel(PrefillArgs a) {
   using C = PfCfg<D>;
   __shared__ __align__(16) char lds[2 * C::BUF];
 
   const int BH = a.B * a.Hq;
-  const int nqb = (a.Tn + PF_QB - 1) / PF_QB;
+  const int nqb = (a.Tn + C::QB - 1) / C::QB;
   const int L = blockIdx.x;
   // heaviest query blocks first; consecutive workgroups (which land on
   // different XCDs) take different heads of the same query block
@@ -745,8 +775,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
   const int l16 = lane & 15, g4 = lane >> 4;
   int start = a.start[b];
   start = start < 0 ? 0 : start;
-  const int q0 = qblk * PF_QB;
-  const int qend = a.Tn < q0 + PF_QB ? a.Tn : q0 + PF_QB;    // new tokens q0 .. qend-1
+  const int q0 = qblk * C::QB;
+  const int qend = a.Tn < q0 + C::QB ? a.Tn : q0 + C::QB;    // new tokens q0 .. qend-1
   int len = start + qend;                                     // keys needed by the last query
   len = len > a.Tmax ? (int)a.Tmax : len;
 
@@ -762,9 +792,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
   PfRaw<D, KB> raw;
   pf_load<D, KB>(raw, 0, tid, krs, vrs, kss, vss);
 
-  // ---- query codes of the block's 128 tokens (2 threads per row, D/2 channels each), in buffer 1
-  int8_t* qt = reinterpret_cast<int8_t*>(lds + C::BUF);
-  float* qsc = reinterpret_cast<float*>(lds);                 // buffer 0 is free until the first store
+  // ---- query codes of the block's tokens (2 threads per row, D/2 channels each) and their
+  // scales, in the staging buffers (free until the first key block is stored)
+  int8_t* qt = reinterpret_cast<int8_t*>(lds);
+  float* qsc = reinterpret_cast<float*>(lds + C::QB * C::QROW);
   {
     const int row = tid >> 1, hh = tid & 1;
     const int i = q0 + row;
@@ -831,70 +862,76 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
 
   const int wfirst = start + q0 + wave * 32;          // the wave's first and last query positions
   const int wlast = wfirst + 31;
-  const int nkb = (len + PF_TB - 1) / PF_TB;
+  constexpr int TB = C::TB, NTT = TB / 16;            // key tokens per block, 16-token tiles
+  const int nkb = (len + TB - 1) / TB;
   for (int kb = 0; kb < nkb; ++kb) {
-    const int t0 = kb * PF_TB;
-    if (kb + 1 < nkb) pf_load<D, KB>(raw, t0 + PF_TB, tid, krs, vrs, kss, vss);
+    const int t0 = kb * TB;
+    if (kb + 1 < nkb) pf_load<D, KB>(raw, t0 + TB, tid, krs, vrs, kss, vss);
     const char* buf = lds + (kb & 1) * C::BUF;
     const int8_t* kt = reinterpret_cast<const int8_t*>(buf);
     const uint16_t* vt = reinterpret_cast<const uint16_t*>(buf + C::KT);
     const float* ksl = reinterpret_cast<const float*>(buf + C::KT + C::VT);
-    const float* vsl = ksl + PF_TB;
+    const float* vsl = ksl + TB;
     if (t0 <= wlast) {
-      // ---- S^T tiles: rows = tokens nt*16 + 4*g4 + r, column = query l16; x = score * log2(e) / sq
-      float x[2][4][4];                                // [query tile][token tile][register]
+      const bool edge = t0 + TB - 1 > wfirst || t0 + TB > len;   // a block on the diagonal or past the end
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        v4i ka[D / 64];
+      for (int j = 0; j < TB / 32; ++j) {
+        // ---- S^T tiles of keys 32j .. 32j+31: rows = keys 16(2j+h2) + 4*g4 + r, column = query l16;
+        // x = score * log2(e) / sq
+        float x[2][2][4];                                // [query tile][16-key tile][register]
 #pragma unroll
-        for (int s2 = 0; s2 < D / 64; ++s2)
-          ka[s2] = *reinterpret_cast<const v4i*>(kt + (nt * 16 + l16) * C::KROW + 64 * s2 + 16 * g4);
-        const float4 kf = *reinterpret_cast<const float4*>(ksl + nt * 16 + 4 * g4);
-        const float kscl[4] = {kf.x, kf.y, kf.z, kf.w};
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int nt = 2 * j + h2;
+          v4i ka[D / 64];
+#pragma unroll
+          for (int s2 = 0; s2 < D / 64; ++s2)
+            ka[s2] = *reinterpret_cast<const v4i*>(kt + (nt * 16 + l16) * C::KROW + 64 * s2 + 16 * g4);
+          const float4 kf = *reinterpret_cast<const float4*>(ksl + nt * 16 + 4 * g4);
+          const float kscl[4] = {kf.x, kf.y, kf.z, kf.w};
+#pragma unroll
+          for (int qi = 0; qi < 2; ++qi) {
+            v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int s2 = 0; s2 < D / 64; ++s2)
+              acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[s2], qB[qi][s2], acc, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[qi][h2][r] = (float)acc[r] * kscl[r];
+          }
+        }
+        if (edge) {
+#pragma unroll
+          for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int t = t0 + (2 * j + h2) * 16 + 4 * g4 + r;
+                if (t > qpos[qi] || t >= len) x[qi][h2][r] = -INFINITY;
+              }
+        }
+        // ---- the running maximum is raised (and everything rescaled) only when a
+        // score exceeds it by more than 2^kLazyMax; otherwise the weights are formed
+        // against the current one directly
 #pragma unroll
         for (int qi = 0; qi < 2; ++qi) {
-          v4i acc = v4i{0, 0, 0, 0};
+          float bm = -INFINITY;
 #pragma unroll
-          for (int s2 = 0; s2 < D / 64; ++s2) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[s2], qB[qi][s2], acc, 0, 0, 0);
+          for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[qi][nt][r] = (float)acc[r] * kscl[r];
+            for (int r = 0; r < 4; ++r) bm = fmaxf(bm, x[qi][h2][r]);
+          if (__any(sq[qi] * bm > mq[qi] + kLazyMax)) {
+            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            const float mn = fmaxf(mq[qi], sq[qi] * bm);
+            const float fac = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mq[qi] - mn);
+            mq[qi] = mn;
+            lq[qi] *= fac;
+            os[qi] *= fac;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) o[qi][c] *= fac;
+          }
         }
-      }
-      if (t0 + PF_TB - 1 > wfirst || t0 + PF_TB > len) {   // a block on the diagonal or past the end
-#pragma unroll
-        for (int qi = 0; qi < 2; ++qi)
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = t0 + nt * 16 + 4 * g4 + r;
-              if (t > qpos[qi] || t >= len) x[qi][nt][r] = -INFINITY;
-            }
-      }
-      // ---- running maximum per query (the 16 values of a lane, then lanes l16 + 16j)
-#pragma unroll
-      for (int qi = 0; qi < 2; ++qi) {
-        float bm = -INFINITY;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) bm = fmaxf(bm, x[qi][nt][r]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-        const float zm = sq[qi] * bm;
-        if (__any(zm > mq[qi] + kLazyMax)) {
-          const float mn = fmaxf(mq[qi], zm);
-          const float fac = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mq[qi] - mn);
-          mq[qi] = mn;
-          lq[qi] *= fac;
-          os[qi] *= fac;
-#pragma unroll
-          for (int c = 0; c < D / 16; ++c) o[qi][c] *= fac;
-        }
-      }
-      // ---- P'^T as bf16 B operands (8 tokens per lane per 32-token half) and O^T += V^T P'^T
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
+        // ---- P'^T as bf16 B operands (8 keys per lane) and O^T += V^T P'^T
         float vsr[2][4];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -908,11 +945,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
           uint32_t pk[4];
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
-            const int nt = 2 * j + h2;
 #pragma unroll
             for (int r = 0; r < 4; r += 2) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[qi], x[qi][nt][r], -mq[qi]));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[qi], x[qi][nt][r + 1], -mq[qi]));
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[qi], x[qi][h2][r], -mq[qi]));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[qi], x[qi][h2][r + 1], -mq[qi]));
               ls += p0;
               ls += p1;
               const f2 pv = {p0 * vsr[h2][r], p1 * vsr[h2][r + 1]};
@@ -965,18 +1001,18 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
 
 template <int D>
 hipError_t launch_prefill_d(const PrefillArgs& a) {
-  const int nqb = (a.Tn + PF_QB - 1) / PF_QB;
-  const dim3 grid((unsigned)((int64_t)a.B * a.Hq * nqb));
+  using C = PfCfg<D>;
+  const int nqb = (a.Tn + C::QB - 1) / C::QB;
+  const dim3 grid((unsigned)((int64_t)a.B * a.Hq * nqb)), block(C::NT);
   switch (a.kvbits) {
-    case 2: attn_prefill_kernel<D, 2><<<grid, dim3(256), 0, a.stream>>>(a); break;
-    case 3: attn_prefill_kernel<D, 3><<<grid, dim3(256), 0, a.stream>>>(a); break;
-    case 4: attn_prefill_kernel<D, 4><<<grid, dim3(256), 0, a.stream>>>(a); break;
-    case 8: attn_prefill_kernel<D, 8><<<grid, dim3(256), 0, a.stream>>>(a); break;
+    case 2: attn_prefill_kernel<D, 2><<<grid, block, 0, a.stream>>>(a); break;
+    case 3: attn_prefill_kernel<D, 3><<<grid, block, 0, a.stream>>>(a); break;
+    case 4: attn_prefill_kernel<D, 4><<<grid, block, 0, a.stream>>>(a); break;
+    case 8: attn_prefill_kernel<D, 8><<<grid, block, 0, a.stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
-
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a) {
   const int g = a.Hq / a.Hkv;

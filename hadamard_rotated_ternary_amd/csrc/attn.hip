@@ -635,11 +635,19 @@ struct PfCfg {
 };
 
 // Raw codes and scales of one key block held in registers between the load
-// and the unpack into LDS.
+// and the unpack into LDS.  Key words in w0; value words of the two tokens in
+// w1, w2, or, when halves of the workgroup stage keys and values separately,
+// in w0, w1 (a thread then holds only one kind).
 template <int D, int KB>
 struct PfRaw {
-  uint32_t k[PfCfg<D>::IPT][KB], v0[PfCfg<D>::IPT][KB], v1[PfCfg<D>::IPT][KB];
+  uint32_t w0[PfCfg<D>::IPT][KB], w1[PfCfg<D>::IPT][KB], w2[PfCfg<D>::IPT][KB];
   float ks, vs;
+  HBL_DEV uint32_t (&k(int u))[KB] { return w0[u]; }
+  HBL_DEV uint32_t (&v0(int u))[KB] { return PfCfg<D>::SPLIT ? w0[u] : w1[u]; }
+  HBL_DEV uint32_t (&v1(int u))[KB] { return PfCfg<D>::SPLIT ? w1[u] : w2[u]; }
+  HBL_DEV const uint32_t (&k(int u) const)[KB] { return w0[u]; }
+  HBL_DEV const uint32_t (&v0(int u) const)[KB] { return PfCfg<D>::SPLIT ? w0[u] : w1[u]; }
+  HBL_DEV const uint32_t (&v1(int u) const)[KB] { return PfCfg<D>::SPLIT ? w1[u] : w2[u]; }
 };
 
 // Value staging item -> (token pair, 32-code group, half): the 64 lanes of a
@@ -665,14 +673,14 @@ HBL_DEV void pf_load(PfRaw<D, KB>& r, int t0, int tid, __amdgpu_buffer_rsrc_t kr
     const int itv = C::SPLIT ? tid - C::NIT : itk;
     if (itk < C::NIT) {
       const int row = itk / C::GPR, grp = itk % C::GPR;
-      buffer_words<KB>(krs, ((t0 + row) * RDW + grp * KB) * 4, r.k[u]);
+      buffer_words<KB>(krs, ((t0 + row) * RDW + grp * KB) * 4, r.k(u));
     }
     if (itv >= 0 && itv < C::NIT) {
       int pr, grp2;
       bool h;
       pf_vitem<D>(itv, pr, grp2, h);
-      buffer_words<KB>(vrs, ((t0 + 2 * pr) * RDW + grp2 * KB) * 4, r.v0[u]);
-      buffer_words<KB>(vrs, ((t0 + 2 * pr + 1) * RDW + grp2 * KB) * 4, r.v1[u]);
+      buffer_words<KB>(vrs, ((t0 + 2 * pr) * RDW + grp2 * KB) * 4, r.v0(u));
+      buffer_words<KB>(vrs, ((t0 + 2 * pr + 1) * RDW + grp2 * KB) * 4, r.v1(u));
     }
   }
   if (tid < C::TB) {
@@ -698,7 +706,7 @@ HBL_DEV void pf_store(const PfRaw<D, KB>& r, char* buf, int tid) {
       if (itk < C::NIT) {
         const int row = itk / C::GPR, grp = itk % C::GPR;
         uint32_t qd[8], sb[8];
-        unpack_quads<KB>(r.k[u], qd);
+        unpack_quads<KB>(r.k(u), qd);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           if constexpr (KB == 8) sb[k] = qd[k] ^ 0x80808080u;
@@ -717,8 +725,8 @@ HBL_DEV void pf_store(const PfRaw<D, KB>& r, char* buf, int tid) {
         bool h;
         pf_vitem<D>(itv, pr, grp, h);
         uint32_t d0[8], d1[8], e0[4], e1[4];
-        unpack_quads<KB>(r.v0[u], d0);
-        unpack_quads<KB>(r.v1[u], d1);
+        unpack_quads<KB>(r.v0(u), d0);
+        unpack_quads<KB>(r.v1(u), d1);
         // quad k0 + 2h, k0 in {0, 1, 4, 5}: a byte permute picks one of two
         // registers (a plain select would be folded into a runtime array index)
         const uint32_t hsel = h ? 0x07060504u : 0x03020100u;
@@ -874,30 +882,63 @@ __global__ __launch_bounds__(PfCfg<D>::NT) void attn_prefill_kernel(PrefillArgs 
     const float* vsl = ksl + TB;
     if (t0 <= wlast) {
       const bool edge = t0 + TB - 1 > wfirst || t0 + TB > len;   // a block on the diagonal or past the end
+      // K fragments and key scales of the first 32-key half; each half then
+      // requests the next half's fragments and its own value operands before
+      // the arithmetic that waits on its scores
+      v4i ka[2][D / 64];
+      float4 kf[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+        for (int s2 = 0; s2 < D / 64; ++s2)
+          ka[h2][s2] = *reinterpret_cast<const v4i*>(kt + (h2 * 16 + l16) * C::KROW + 64 * s2 + 16 * g4);
+        kf[h2] = *reinterpret_cast<const float4*>(ksl + h2 * 16 + 4 * g4);
+      }
 #pragma unroll
       for (int j = 0; j < TB / 32; ++j) {
         // ---- S^T tiles of keys 32j .. 32j+31: rows = keys 16(2j+h2) + 4*g4 + r, column = query l16;
         // x = score * log2(e) / sq
         float x[2][2][4];                                // [query tile][16-key tile][register]
+        v4i acc[2][2];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int nt = 2 * j + h2;
-          v4i ka[D / 64];
-#pragma unroll
-          for (int s2 = 0; s2 < D / 64; ++s2)
-            ka[s2] = *reinterpret_cast<const v4i*>(kt + (nt * 16 + l16) * C::KROW + 64 * s2 + 16 * g4);
-          const float4 kf = *reinterpret_cast<const float4*>(ksl + nt * 16 + 4 * g4);
-          const float kscl[4] = {kf.x, kf.y, kf.z, kf.w};
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int qi = 0; qi < 2; ++qi) {
-            v4i acc = v4i{0, 0, 0, 0};
+            acc[h2][qi] = v4i{0, 0, 0, 0};
 #pragma unroll
             for (int s2 = 0; s2 < D / 64; ++s2)
-              acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[s2], qB[qi][s2], acc, 0, 0, 0);
+              acc[h2][qi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka[h2][s2], qB[qi][s2], acc[h2][qi], 0, 0, 0);
+          }
+        float kscl[2][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[qi][h2][r] = (float)acc[r] * kscl[r];
+        for (int h2 = 0; h2 < 2; ++h2) {
+          kscl[h2][0] = kf[h2].x; kscl[h2][1] = kf[h2].y; kscl[h2][2] = kf[h2].z; kscl[h2][3] = kf[h2].w;
+        }
+        // value operands of this half (early, except with 8-bit codes, whose
+        // wider staging registers leave no room) and key fragments of the next
+        constexpr bool kEarlyV = KB != 8;
+        bf8v va[D / 16];
+        if constexpr (kEarlyV) {
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c)
+            va[c] = *reinterpret_cast<const bf8v*>(vt + (c * 16 + l16) * C::VROW + 32 * j + 8 * g4);
+        }
+        if (j + 1 < TB / 32) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int nt = 2 * (j + 1) + h2;
+#pragma unroll
+            for (int s2 = 0; s2 < D / 64; ++s2)
+              ka[h2][s2] = *reinterpret_cast<const v4i*>(kt + (nt * 16 + l16) * C::KROW + 64 * s2 + 16 * g4);
+            kf[h2] = *reinterpret_cast<const float4*>(ksl + nt * 16 + 4 * g4);
           }
         }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[qi][h2][r] = (float)acc[h2][qi][r] * kscl[h2][r];
         if (edge) {
 #pragma unroll
           for (int qi = 0; qi < 2; ++qi)
@@ -961,9 +1002,10 @@ __global__ __launch_bounds__(PfCfg<D>::NT) void attn_prefill_kernel(PrefillArgs 
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
           // V^T operand: channel c*16 + l16, the 8 adjacent positions 32j + 8*g4 .. +7
-          const bf8v va = *reinterpret_cast<const bf8v*>(vt + (c * 16 + l16) * C::VROW + 32 * j + 8 * g4);
+          if constexpr (!kEarlyV)
+            va[c] = *reinterpret_cast<const bf8v*>(vt + (c * 16 + l16) * C::VROW + 32 * j + 8 * g4);
 #pragma unroll
-          for (int qi = 0; qi < 2; ++qi) o[qi][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qi], o[qi][c], 0, 0, 0);
+          for (int qi = 0; qi < 2; ++qi) o[qi][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[c], pb[qi], o[qi][c], 0, 0, 0);
         }
 #pragma unroll
         for (int qi = 0; qi < 2; ++qi) os[qi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qi], os[qi], 0, 0, 0);

@@ -55,7 +55,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="wdown_7b_int4")
     ap.add_argument("--no-extras", action="store_true", help="skip the INT8 and decode side measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -150,8 +150,10 @@ def main():
             "prep_gbps_impl": (M * K * 2 + M * hbl.codes_row_bytes(6 if fp6 else bits, K) + M * 4)
                               / (res["prep_ms"] / 1e3) / 1e9,
             "gemm_tops": achieved,
-            "forward_entry_ms": res["forward_ms"],
+            "step_ms_median": res["step_ms_median"], "step_ms_min": res["step_ms_min"],
+            "forward_entry_ms": res["forward_ms"], "forward_entry_calls": res["forward_calls"],
         },
+        "inputs": res["rotation"],
         "weight_ternarise_ms": wq_ms,
         "weight_rotate_ternarise_ms": wq_rot_ms,
     }
@@ -162,11 +164,27 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def rotation_sets(torch, xd, wp, total_bytes=512 << 20):
+    """Distinct input/weight copies cycled through by consecutive steps, so that
+    the working set of a step sequence exceeds the 256 MB Infinity Cache
+    (MALL): nothing is served from it across steps that a real layer stack
+    would have evicted.  Returns (xs, ws) and a description."""
+    per = xd.numel() * xd.element_size() + wp.numel()
+    n = max(1, -(-total_bytes // per))
+    xs = [xd] + [xd.clone() for _ in range(n - 1)]
+    ws = [wp] + [wp.clone() for _ in range(n - 1)]
+    return xs, ws, f"{n} activation/weight buffer sets rotated ({n * per / 2**20:.0f} MiB)"
+
+
 def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup, rotate=True):
-    """Time `steps` forwards; events between the two kernels give per-kernel times.
-    The two stage calls launch the same kernels as the single-call forward (the
-    INT4 forward of more than 64 tokens keeps its codes in the fp6 operand
-    layout, format 6)."""
+    """Per-kernel times from the two stage calls with events between the
+    kernels (their launch average is what the roofline uses); then `warmup`
+    and `steps` single-call forwards, the latter timed back to back (wall
+    clock between synchronisations).  The stage calls launch the same kernels as the
+    single-call forward (the INT4 forward of more than 64 tokens keeps its
+    codes in the fp6 operand layout, format 6).  Consecutive steps cycle through distinct activation and
+    weight copies (rotation_sets)."""
+    xs, wps, rot = rotation_sets(torch, xd, wp)
     sb = 6 if bits == 4 and M > 64 else bits
     codes = torch.empty(hbl.codes_shape(sb, M, K), dtype=torch.int8 if bits == 8 else torch.uint8, device="cuda")
     d = torch.empty(M + 4, dtype=torch.float32, device="cuda")[:M]
@@ -175,36 +193,51 @@ def time_layer(torch, hbl, xd, wp, a, M, K, N, bits, steps, warmup, rotate=True)
     wsf = torch.empty(max(hbl.workspace_bytes(hbl.OP_FORWARD_INT8 if bits == 8 else hbl.OP_FORWARD_INT4, M, K, N), 16),
                       dtype=torch.uint8, device="cuda")
 
-    def step(evs=None):
+    def step(i, evs=None):
         if evs: evs[0].record()
-        hbl.quantize_act(xd, sb, out=(codes, d), rotate=rotate)
+        hbl.quantize_act(xs[i % len(xs)], sb, out=(codes, d), rotate=rotate)
         if evs: evs[1].record()
-        hbl.matmul_dequant(codes, sb, d, wp, a, K, workspace=ws, out=y)
+        hbl.matmul_dequant(codes, sb, d, wps[i % len(wps)], a, K, workspace=ws, out=y)
         if evs: evs[2].record()
 
-    for _ in range(warmup):
-        step()
+    def forward(i):
+        hbl.forward(xs[i % len(xs)], wps[i % len(wps)], a, bits, workspace=wsf, out=y, rotate=rotate)
+
+    # per-kernel times first (untimed for the headline; it also brings the
+    # clocks to their sustained state): the same kernels through the two
+    # stage calls, events between them
+    for i in range(max(50, warmup)):
+        step(i)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    prep = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    per_step = [e[0].elapsed_time(e[2]) for e in evs]
+    # the timed region: `warmup` untimed calls, then exactly `steps` calls of the
+    # public single-call forward (hbl_forward_int4 / _int8: both kernels
+    # launched by one library call), back to back, nothing else on the stream
+    for i in range(warmup):
+        forward(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(evs[i])
+        forward(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    prep = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    # the public single-call entry point, same kernels
-    for _ in range(max(2, warmup // 2)):
-        hbl.forward(xd, wp, a, bits, workspace=wsf, out=y, rotate=rotate)
+    # >= 200 back-to-back single calls between two events
+    calls = max(200, steps)
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     f0.record()
-    for _ in range(steps):
-        hbl.forward(xd, wp, a, bits, workspace=wsf, out=y, rotate=rotate)
+    for i in range(calls):
+        forward(i)
     f1.record()
     torch.cuda.synchronize()
     return {"ms_per_step": (t1 - t0) * 1e3 / steps, "prep_ms": prep, "gemm_ms": gemm,
-            "forward_ms": f0.elapsed_time(f1) / steps}
+            "step_ms_median": float(np.median(per_step)), "step_ms_min": float(np.min(per_step)),
+            "forward_ms": f0.elapsed_time(f1) / calls, "forward_calls": calls, "rotation": rot}
 
 
 def stored_traffic(workload):
@@ -450,7 +483,19 @@ def cpu_baseline(x, wl, bits, budget_s):
     oracle.forward(x[:n], wt, alpha, bits, keep=False)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {x.shape[0]} tokens of the same workload (INT{bits}), {dt:.1f} s wall"}
+            "sample": f"first {n} of {x.shape[0]} tokens of the same workload (INT{bits}), {dt:.1f} s wall",
+            "cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

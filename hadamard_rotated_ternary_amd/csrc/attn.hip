@@ -781,8 +781,10 @@ __global__ __launch_bounds__(PfCfg<D>::NT) void attn_prefill_kernel(PrefillArgs 
   const int hk = hq / (a.Hq / a.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
+  // device-resident start, clamped to [0, Tmax]; with Tmax + Tn < 2^31 - 512
+  // (checked by the host) every position below fits in 32 bits
   int start = a.start[b];
-  start = start < 0 ? 0 : start;
+  start = start < 0 ? 0 : (start > a.Tmax ? (int)a.Tmax : start);
   const int q0 = qblk * C::QB;
   const int qend = a.Tn < q0 + C::QB ? a.Tn : q0 + C::QB;    // new tokens q0 .. qend-1
   int len = start + qend;                                     // keys needed by the last query

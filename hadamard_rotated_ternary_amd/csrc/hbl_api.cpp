@@ -366,7 +366,7 @@ hbl_status hbl_attention_prefill(const void* q, int q_bits, const uint8_t* k_cod
     return HBL_ERR_DTYPE;
   if (!heads_d_ok(d) || B < 0 || B >= kCount || Tn < 0 || Tn >= kCount || Hkv <= 0 || Hq <= 0 || Hq >= kCount ||
       Hq % Hkv != 0 || Tmax <= 0 || Tmax >= kCount || B * Hkv * Tmax > (int64_t(1) << 34) ||
-      B * Hq * ((Tn + 63) / 64) >= kCount || Tmax * (d * kv_bits / 8) >= kCount)
+      B * Hq * ((Tn + 63) / 64) >= kCount || Tmax * (d * kv_bits / 8) >= kCount || Tmax + Tn >= kCount - 512)
     return HBL_ERR_SHAPE;
   if (B == 0 || Tn == 0) return HBL_OK;
   if (!q || !k_codes || !k_scale || !v_codes || !v_scale || !start || !out) return HBL_ERR_NULL;

@@ -97,7 +97,9 @@ hbl_status hbl_attention_decode(const void *q, int q_bits, const uint8_t *k_code
  * out_dtype.  Scores are exact integer dot products on the int8 matrix
  * instruction; the probabilities times the value scales are rounded to bf16
  * for the value product (bf16 matrix instruction, fp32 accumulation).
- * d in {64, 128, 256}; positions past Tmax are clamped.  No workspace. */
+ * d in {64, 128, 256}.  start[b] is clamped to [0, Tmax] and a query whose
+ * position is Tmax or more sees the whole cache (Tmax keys); Tmax + Tn must
+ * stay below 2^31 - 512 (HBL_ERR_SHAPE).  No workspace. */
 hbl_status hbl_attention_prefill(const void *q, int q_bits, const uint8_t *k_codes, const float *k_scale,
                                  const uint8_t *v_codes, const float *v_scale, int kv_bits,
                                  const int32_t *start, int64_t B, int64_t Tn, int64_t Hq, int64_t Hkv,

@@ -191,6 +191,17 @@ def test_attention_entry_points_validate_without_device():
                                   None) == 2
     assert L.hbl_attention_decode(None, 8, None, None, None, None, 3, None, 1, 4, 2, 128, 16, None, 0, None, 0,
                                   None) == 1
+    # prefill: (q, q_bits, kc, ks, vc, vs, kv_bits, start, B, Tn, Hq, Hkv, d, Tmax, out, out_dtype, stream)
+    pf = L.hbl_attention_prefill
+    assert pf(None, 8, None, None, None, None, 5, None, 1, 4, 4, 2, 128, 16, None, 0, None) == 3   # cache width
+    assert pf(None, 9, None, None, None, None, 3, None, 1, 4, 4, 2, 128, 16, None, 0, None) == 3   # query width
+    assert pf(None, 8, None, None, None, None, 3, None, 1, 4, 4, 2, 96, 16, None, 0, None) == 2    # head size
+    assert pf(None, 8, None, None, None, None, 3, None, 1, 4, 3, 2, 128, 16, None, 0, None) == 2   # Hq % Hkv
+    assert pf(None, 8, None, None, None, None, 3, None, 1, 4, 4, 2, 128, 0, None, 0, None) == 2    # Tmax
+    assert pf(None, 8, None, None, None, None, 3, None, 1, 2**31 - 600, 4, 2, 128, 100, None, 0, None) == 2
+    assert pf(None, 8, None, None, None, None, 3, None, 1, 0, 4, 2, 128, 16, None, 0, None) == 0   # no new tokens
+    assert pf(None, 8, None, None, None, None, 3, None, 0, 4, 4, 2, 128, 16, None, 0, None) == 0   # no sequences
+    assert pf(None, 8, None, None, None, None, 3, None, 1, 4, 4, 2, 128, 16, None, 0, None) == 1   # null buffers
     # partial records: B * Hq * ceil(Tmax / 512 tokens) of (d + 4) floats, rounded up to 256 bytes
     assert L.hbl_attention_workspace_bytes(2, 8, 128, 1000) == -(-(2 * 8 * 2 * 132 * 4) // 256) * 256
     assert L.hbl_attention_workspace_bytes(1, 1, 64, 1) == 0     # one chunk: the output is written directly

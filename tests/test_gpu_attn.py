@@ -386,3 +386,26 @@ def test_attention_prefill_empty_and_single_token():
     ref = oracle.attention_prefill(qf, 8, kc, ks, vc, vs, bits, start)
     got = host(hbl.attention_prefill(to_dev_bf16(qb), 8, kcd, ksd, vcd, vsd, bits, torch.from_numpy(start).cuda()))
     check_prefill(got, ref, vc, vs, bits, Hq, Hkv, start)
+
+
+def test_attention_prefill_positions_clamped():
+    """start[b] is clamped to [0, Tmax] and a query at a position past the
+    cache sees all Tmax keys: each query against the oracle's decode step at
+    the clamped length (the oracle's prefill itself rejects such starts)."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, d, Tmax, Tn, bits = 3, 2, 1, 128, 100, 40, 3
+    (kc, ks, kcd, ksd), (vc, vs, vcd, vsd) = make_cache(rng, B, Hkv, Tmax, d, bits)
+    start = np.array([80, 150, -5], np.int32)
+    qb, qf = bf16_bits(rng.normal(size=(B, Tn, Hq, d)))
+    got = host(hbl.attention_prefill(to_dev_bf16(qb), 8, kcd, ksd, vcd, vsd, bits, torch.from_numpy(start).cuda()))
+    Z = 1 << (bits - 1)
+    for b in range(B):
+        s0 = min(max(int(start[b]), 0), Tmax)
+        for i in range(Tn):
+            L = min(s0 + i + 1, Tmax)
+            ref = oracle.attention_decode(qf[b:b + 1, i], 8, kc[b:b + 1], ks[b:b + 1], vc[b:b + 1], vs[b:b + 1],
+                                          bits, np.array([L], np.int32))
+            for h in range(Hq):
+                vh = (vc[b, h // (Hq // Hkv), :L].astype(np.float64) - Z) * vs[b, h // (Hq // Hkv), :L, None]
+                err = np.max(np.abs(got[b, i, h] - ref[0, h]))
+                assert err <= PF_TOL * np.max(np.abs(vh)), (b, i, h, err)

@@ -536,7 +536,7 @@ static DecodePlan decode_plan(int M, int K) {
 #ifdef HBL_DECODE_PLAN
   DecodePlan p = HBL_DECODE_PLAN(M);
 #else
-  DecodePlan p = M <= 16 ? DecodePlan{1, 1, 1, 8} : DecodePlan{4, 4, 4, 4};
+  DecodePlan p = M <= 16 ? DecodePlan{1, 1, 1, 8} : DecodePlan{4, 4, 4, 8};
 #endif
   while (p.S > 1 && K / p.S < DKB) p.S /= 2;
   return p;
@@ -549,7 +549,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
     int32_t* __restrict__ partial) {
   // Blocks held per wave per round: their loads need MAXB * (CPW + MB*BITS/2)
   // uint4 registers, kept near 48 (192 VGPRs).
-  constexpr int MAXB = (48 / (CPW + MB * BITS / 2)) >= 8 ? 8 : (48 / (CPW + MB * BITS / 2)) >= 4 ? 4 : 2;
+  // (two with four token groups: 8 waves of 184 registers, two per SIMD, so
+  // one wave's MFMAs cover another's waits)
+  constexpr int MAXB = MB == 4 ? 2 : (48 / (CPW + MB * BITS / 2)) >= 8 ? 8 : (48 / (CPW + MB * BITS / 2)) >= 4 ? 4 : 2;
   constexpr int CH = 16 * CPW;
   // Partial sums per (token, channel), rows of RL ints.  Inside each block of
   // 16 channels column 4r + q holds channel 4q + r, and RL = 4 (mod 64): the
@@ -810,7 +812,7 @@ static void launch_decode_t(const GemmArgs& a) {
   HBL_DECODE_VARIANTS
 #endif
   if (p.mb == 1) launch_decode_p<BITS, 1, 1, 8, OUT>(a, p.S);
-  else launch_decode_p<BITS, 4, 4, 4, OUT>(a, p.S);
+  else launch_decode_p<BITS, 4, 4, 8, OUT>(a, p.S);
 }
 
 // INT4 stages hold 256 k (3 x 48 KiB of LDS), INT8 stages 128 k (3 x 40 KiB).

@@ -115,19 +115,30 @@ __global__ __launch_bounds__(256) void tr_kernel(const void* __restrict__ src, c
 
 // ---------------------------------------------------------------------------
 // bf16 NT product: out[i][j] = s * sum_c A[i][c] B[j][c], fp32 out.
-// 256 x 256 tile per 4-wave workgroup (2 x 2 waves of 128 x 128, each 4 x 4
-// v_mfma_f32_32x32x16_bf16 tiles), 32 c per stage in a three-deep LDS ring
+// 256 x 256 tile per workgroup (8 waves of 64 x 128, each 2 x 4
+// v_mfma_f32_32x32x16_bf16 tiles; 4 waves of 128 x 128 also build), 32 c per stage in a three-deep LDS ring
 // filled by global_load_lds_dwordx4 (each stage requested two ahead).  Rows
 // of 64 bytes, 16-byte units XOR-swizzled so the fragment reads (16 lanes:
 // rows r..r+15 of one unit column) and the copies hit distinct banks.
+#ifndef HBL_BF16_NW
+#define HBL_BF16_NW 8   // waves per workgroup of the bf16 product (4 or 8)
+#endif
 constexpr int GT = 256, GBK = 32, GROW = GBK * 2, GUNITS = GROW / 16;
 constexpr int G_A_STAGE = GT * GROW, G_STAGE = 2 * G_A_STAGE;
 HBL_DEV int gswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-__global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A,
-                                                              const uint16_t* __restrict__ B,
-                                                              const float* __restrict__ sptr, float* __restrict__ out,
-                                                              int I, int J, int Cn, int tiles_i, int tiles_j) {
+// NW = 4: 2 x 2 waves of 128 x 128 (one wave per SIMD); NW = 8: 4 x 2 waves
+// of 64 x 128, whose accumulators take half the registers, so two waves
+// share a SIMD and one's MFMAs cover the other's waits.
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A,
+                                                                  const uint16_t* __restrict__ B,
+                                                                  const float* __restrict__ sptr,
+                                                                  float* __restrict__ out, int I, int J, int Cn,
+                                                                  int tiles_i, int tiles_j) {
+  constexpr int WI = NW / 2;                  // wave rows
+  constexpr int RB = GT / WI / 32;            // 32-row blocks per wave
+  constexpr int CP = 16 / NW;                 // 1 KiB copies per wave per operand per stage
   __shared__ __attribute__((aligned(16))) uint8_t smem[3 * G_STAGE];
   const int bid = blockIdx.x, total = tiles_i * tiles_j;
   // XCD-aware order (8 consecutive ids go to 8 XCDs): contiguous runs of
@@ -145,39 +156,39 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(const uint16_t* __
   const int wi = wave >> 1, wj = wave & 1;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // Per stage: A 16 KiB + B 16 KiB = 32 copies of 1 KiB; 4 A + 4 B per wave.
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[4];
+  // Per stage: A 16 KiB + B 16 KiB = 32 copies of 1 KiB; CP of each per wave.
+  const uint16_t* a_src[CP];
+  const uint16_t* b_src[CP];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int P = (j * 4 + wave) * 64 + lane, row = P / GUNITS, u = (P % GUNITS) ^ gswz(row);
+  for (int j = 0; j < CP; ++j) {
+    const int P = (j * NW + wave) * 64 + lane, row = P / GUNITS, u = (P % GUNITS) ^ gswz(row);
     a_src[j] = A + (size_t)min(i0 + row, I - 1) * Cn + 8 * u;
     b_src[j] = B + (size_t)min(j0 + row, J - 1) * Cn + 8 * u;
   }
   auto dma = [&](int kt, int buf) {
     uint8_t* base = smem + buf * G_STAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_copy16(a_src[j] + (size_t)kt * GBK, base + (j * 4 + wave) * 1024);
+    for (int j = 0; j < CP; ++j) lds_copy16(a_src[j] + (size_t)kt * GBK, base + (j * NW + wave) * 1024);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_copy16(b_src[j] + (size_t)kt * GBK, base + G_A_STAGE + (j * 4 + wave) * 1024);
+    for (int j = 0; j < CP; ++j) lds_copy16(b_src[j] + (size_t)kt * GBK, base + G_A_STAGE + (j * NW + wave) * 1024);
   };
 
-  v16f acc[4][4];
+  v16f acc[RB][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  // Fragments of one 16-wide k-step: 4 A row blocks and 4 B column blocks.
+  // Fragments of one 16-wide k-step: RB A row blocks and 4 B column blocks.
   struct GFrag {
-    bf8v a[4], b[4];
+    bf8v a[RB], b[4];
   };
   auto read_frag = [&](GFrag& f, int buf, int ks) __attribute__((always_inline)) {
     const uint8_t* sa = smem + buf * G_STAGE;
     const uint8_t* sb = sa + G_A_STAGE;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int row = wi * 128 + rb * 32 + l32;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = wi * (32 * RB) + rb * 32 + l32;
       f.a[rb] = *reinterpret_cast<const bf8v*>(sa + row * GROW + 16 * ((2 * ks + g) ^ gswz(row)));
     }
 #pragma unroll
@@ -188,7 +199,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(const uint16_t* __
   };
   auto mfmas = [&](const GFrag& f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
         acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(const uint16_t* __
   // stage kt+3 is requested into that buffer; the fragments of stage kt+1's
   // k-step 0 are read while the k-step 1 MFMAs run.  Copies are thus issued
   // two stages ahead of their use.
-  constexpr int NL = 8;   // copy instructions per wave per stage
+  constexpr int NL = 2 * CP;   // copy instructions per wave per stage
   const int KT = Cn / GBK;
   GFrag f0, f1;
   dma(0, 0);
@@ -236,12 +247,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_nt_kernel(const uint16_t* __
   // 8*(r/4) + 4*(l/32) + r%4, column l%32.
   const float s = sptr ? fmaxf(sptr[0], kEpsQ) : 1.0f;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = i0 + wi * 128 + rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int row = i0 + wi * (32 * RB) + rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
         const int col = j0 + wj * 128 + cb * 32 + l32;
         if (row < I && col < J) out[(size_t)row * J + col] = acc[rb][cb][r] * s;
       }
@@ -483,7 +494,8 @@ hipError_t launch_transpose_tokens(int kind, const void* src, const float* dscal
 hipError_t launch_gemm_bf16_nt(const uint16_t* A, const uint16_t* B, const float* scale, float* out, int I, int J,
                                int Cn, hipStream_t stream) {
   const int ti = (I + GT - 1) / GT, tj = (J + GT - 1) / GT;
-  hipLaunchKernelGGL(gemm_bf16_nt_kernel, dim3(ti * tj), dim3(256), 0, stream, A, B, scale, out, I, J, Cn, ti, tj);
+  hipLaunchKernelGGL(gemm_bf16_nt_kernel<HBL_BF16_NW>, dim3(ti * tj), dim3(64 * HBL_BF16_NW), 0, stream, A, B, scale,
+                     out, I, J, Cn, ti, tj);
   return hipGetLastError();
 }
 

@@ -26,21 +26,21 @@ typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 // Ternary weights -> W_t^T as bf16 [K][N] (values -1, 0, +1; the scale a is
 // applied in the product's epilogue).  One thread per 8 consecutive n of one
 // k: the packed code of (n, k) is field (k % 16) / 4 of byte k % 4 of word
-// k / 16 of row n.
+// k / 16 of row n (word position: wword).
 __global__ __launch_bounds__(256) void wbt_kernel(const uint8_t* __restrict__ wpack, int N, int K,
                                                   uint16_t* __restrict__ wbt) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int ng = N / 8;
   if (t >= (int64_t)K * ng) return;
   const int k = (int)(t / ng), n0 = (int)(t % ng) * 8;
-  const int byte = (k >> 4) * 4 + (k & 3), sh = 2 * ((k & 15) >> 2);
+  const int sh = 2 * ((k & 15) >> 2);
   uint32_t o[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     uint32_t h = 0;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const uint32_t c = (wpack[(size_t)(n0 + 2 * p + e) * (K / 4) + byte] >> sh) & 3u;
+      const uint32_t c = (wpack[wword(n0 + 2 * p + e, k >> 4, K) * 4 + (k & 3)] >> sh) & 3u;
       const uint32_t bf = (c & 1u) ? (0x3F80u | ((c & 2u) << 14)) : 0u;   // 01 -> +1, 11 -> -1, 00 -> 0
       h |= bf << (16 * e);
     }

@@ -19,6 +19,18 @@ namespace hbl {
 
 constexpr float kEpsNorm = 1e-6f;   // RMSNorm epsilon, added to the mean square
 constexpr float kEpsQ = 1e-5f;      // floor of the per-token and per-tensor statistics
+
+// Packed ternary weights: one 32-bit word per 16 consecutive k of a row, laid
+// out in tiles of 16 rows x 256 k (16 x 16 words = 1 KiB), tiles row-block
+// major; inside a tile the 16 words of a row are contiguous (64 bytes).  So a
+// run of 16 rows' 64-byte segments is one contiguous KiB.  Word index of word
+// w (k = 16w .. 16w+15) of row n:
+HBL_DEV size_t wword(int n, int w, int K) {
+  return ((size_t)(n >> 4) * (size_t)(K >> 8) + (size_t)(w >> 4)) * 256 + (size_t)(n & 15) * 16 + (size_t)(w & 15);
+}
+// Byte offset of the tile row block holding row n (rows n & ~15 .. +15) and of
+// the row's segment inside every tile of that block.
+HBL_DEV size_t wrow_base(int n, int K) { return (size_t)(n >> 4) * (size_t)K * 4 + (size_t)(n & 15) * 64; }
 constexpr float kQ8 = 127.0f;       // INT8 absmax: max|x| maps to code 127
 constexpr float kQ4 = 2.6457513110645906f;  // INT4 absmean multiplier sqrt(7), rounded to fp32
 // Adding 1.5 * 2^23 rounds a float of magnitude < 2^22 to the nearest integer

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
 #pragma unroll
   for (int i = 0; i < MAXB; ++i) {
     const int b = wave + FD_NW * i;
-    wq[i] = *reinterpret_cast<const uint4*>(W + (size_t)n * (K / 4) + (size_t)b * (FD_DKB / 4) + 16 * g);
+    wq[i] = *reinterpret_cast<const uint4*>(W + wrow_base(n, K) + (size_t)b * 1024 + 16 * g);
   }
 
   // ---- quantised activations of the M tokens, into LDS

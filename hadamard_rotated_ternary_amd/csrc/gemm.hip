@@ -92,7 +92,6 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
   const int wm = wave / WNW, wn = wave % WNW;
   const int l32 = lane & 31, g = lane >> 5;
   const size_t arow = BITS == 8 ? (size_t)K : (size_t)K / 2;
-  const size_t wrow = (size_t)K / 4;
 
   // Global -> LDS directly (global_load_lds_dwordx4: no staging registers),
   // three LDS stages in a ring so every stage is requested two stages before
@@ -111,8 +110,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
     const int P = (j * NWV + wave) * 64 + lane, row = P / C::BUNITS, u = (P % C::BUNITS) ^ swz<C::BUNITS>(row);
-    b_src[j] = W + (size_t)min(n0 + row, N - 1) * wrow + 16 * u;
+    b_src[j] = W + wrow_base(min(n0 + row, N - 1), K) + 16 * u;
   }
+  // packed weights of stage kt: BK = 256 is one 64-byte segment per row
+  // (tiles 1 KiB apart), BK = 128 half of one
+  auto bstage = [](int kt) -> size_t {
+    return BK == 256 ? (size_t)kt * 1024 : (size_t)(kt >> 1) * 1024 + (size_t)(kt & 1) * 32;
+  };
   auto dma = [&](int kt, int buf) {
     uint8_t* base = smem + buf * C::STAGE;
 #pragma unroll
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
       lds_copy16(a_src[j] + (size_t)kt * C::ABYTES, base + (j * NWV + wave) * 1024);
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j)
-      lds_copy16(b_src[j] + (size_t)kt * C::BBYTES, base + C::A_STAGE + (j * NWV + wave) * 1024);
+      lds_copy16(b_src[j] + bstage(kt), base + C::A_STAGE + (j * NWV + wave) * 1024);
   };
 
   v16i acc[4][CB];
@@ -313,9 +317,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   // A is blocked by 128 k: stage kt of the tile is the contiguous run of
   // 256 x 96 bytes at (kt * M + m0) * 96.
   const size_t a_stage = (size_t)M * F6_AROW;
-  const uint32_t wrow = (uint32_t)K / 4;
   const uint8_t* a_tile = A + (size_t)m0 * F6_AROW;
-  const uint8_t* b_tile = W + (size_t)n0 * wrow;
+  const uint8_t* b_tile = W + wrow_base(n0, K);     // n0 is a multiple of 16
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
   // copy P of a stage fills LDS bytes 16P..16P+15 (wave instruction = 1 KiB);
@@ -332,7 +335,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
     const int P = (j * 4 + wave) * 64 + lane, col = P >> 2, u = (P & 3) ^ f6_bswz(col);
-    b_off[j] = (uint32_t)(min(n0 + col, N - 1) - n0) * wrow + 16 * u;
+    const int nr = min(n0 + col, N - 1) - n0;       // tiled: 16-row blocks of 4K bytes, 64-byte row segments
+    b_off[j] = (uint32_t)(nr >> 4) * (uint32_t)K * 4u + (uint32_t)(nr & 15) * 64u + 16u * u;
   }
   // A copy j (0..5) of stage kt into A buffer buf; B copy j (0..3) of stage
   // pair p into B slot sl
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
     lds_copy16s(a_tile + (size_t)kt * a_stage, a_off[j], lds0 + buf * F6_A_STAGE + (j * 4 + wave_s) * 1024);
   };
   auto dmaB = [&](int j, int p, int sl) __attribute__((always_inline)) {
-    lds_copy16s(b_tile + (size_t)p * F6_BPROW, b_off[j], lds0 + F6_B_BASE + sl * F6_B_PAIR + (j * 4 + wave_s) * 1024);
+    lds_copy16s(b_tile + (size_t)p * 1024, b_off[j], lds0 + F6_B_BASE + sl * F6_B_PAIR + (j * 4 + wave_s) * 1024);
   };
 
   v16f acc[4][4];
@@ -451,7 +455,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
           if (i < B_LOADS) dmaB(i, bp, ((u + 3) >> 1) & 1);
           else if (i < B_LOADS + A_LOADS) dmaA(i - B_LOADS, akt, u & (F6_NBUF - 1));
         } else {
-          if (i & 1) dmaA(i >> 1, akt, u & (F6_NBUF - 1));
+          // even stage: the A_LOADS copies of stage kt+4 after MFMAs 1, 3, ..., 2*A_LOADS-1
+          if ((i & 1) && (i >> 1) < A_LOADS) dmaA(i >> 1, akt, u & (F6_NBUF - 1));
         }
         if (i >= 8 && !(i & 1)) bf0[(i - 8) >> 1] = bexp1(nxt, 0, (i - 8) >> 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -595,7 +600,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
 #pragma unroll
       for (int cp = 0; cp < CPW; ++cp) {
         const int n = min(ch0 + 16 * cp + c, N - 1);
-        wq[i][cp] = *reinterpret_cast<const uint4*>(W + (size_t)n * (K / 4) + kb / 4);
+        wq[i][cp] = *reinterpret_cast<const uint4*>(W + wrow_base(n, K) + (size_t)((kbeg + b * DKB) >> 8) * 1024 + 16 * g);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -691,7 +696,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_few_kernel(
 #pragma unroll
   for (int i = 0; i < MAXB; ++i) {
     const int b = min(wave + NW * i, nblk - 1);
-    wq[i] = *reinterpret_cast<const uint4*>(W + (size_t)n * (K / 4) + (size_t)b * (DKB / 4) + 16 * g);
+    wq[i] = *reinterpret_cast<const uint4*>(W + wrow_base(n, K) + (size_t)b * 1024 + 16 * g);
   }
   // ---- operand form of the staged codes, token rows of K bytes
   const int opr = K;

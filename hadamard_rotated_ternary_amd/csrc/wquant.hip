@@ -66,7 +66,8 @@ __global__ __launch_bounds__(256) void walpha_kernel(const double* __restrict__ 
   if (threadIdx.x == 0) walpha[0] = (float)(s / ((double)N * (double)K));
 }
 
-// One thread per packed 32-bit word (16 consecutive k of one row).
+// One thread per packed 32-bit word (16 consecutive k of one row), stored at
+// its tiled position (wword).
 __global__ __launch_bounds__(256) void wpack_kernel(const float* __restrict__ w, int N, int K,
                                                    const float* __restrict__ walpha,
                                                    uint32_t* __restrict__ wpack) {
@@ -89,7 +90,8 @@ __global__ __launch_bounds__(256) void wpack_kernel(const float* __restrict__ w,
       word |= code << (8 * i + 2 * j);
     }
   }
-  wpack[q] = word;
+  const int wpr = K / 16;
+  wpack[wword((int)(q / wpr), (int)(q % wpr), K)] = word;
 }
 
 __global__ __launch_bounds__(256) void wunpack_kernel(const uint32_t* __restrict__ wpack, int N, int K,
@@ -97,7 +99,8 @@ __global__ __launch_bounds__(256) void wunpack_kernel(const uint32_t* __restrict
   const size_t words = (size_t)N * (K / 16);
   const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= words) return;
-  const uint32_t p = wpack[q];
+  const int wpr = K / 16;
+  const uint32_t p = wpack[wword((int)(q / wpr), (int)(q % wpr), K)];
   uint32_t out[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)

@@ -37,10 +37,16 @@
  *   - Only gfx950 devices are supported (HBL_ERR_DEVICE otherwise).
  *
  * Data formats:
- *   packed ternary weights  uint8 [N][K/4]: for each row, one little-endian
- *       32-bit word per 16 consecutive k; the code of k0 + 4*j + i (i, j in
- *       0..3) occupies bits 8*i + 2*j .. 8*i + 2*j + 1 of the word of k0, with
- *       the 2-bit codes 0b00 = 0, 0b01 = +1, 0b11 = -1 (0b10 never written).
+ *   packed ternary weights  N*K/4 bytes (uint8 [N][K/4] in size): one
+ *       little-endian 32-bit word per 16 consecutive k of a row; the code of
+ *       k0 + 4*j + i (i, j in 0..3) occupies bits 8*i + 2*j .. 8*i + 2*j + 1
+ *       of the word of k0, with the 2-bit codes 0b00 = 0, 0b01 = +1,
+ *       0b11 = -1 (0b10 never written).  The words are tiled: tiles of 16
+ *       rows x 256 k (16 x 16 words, 1 KiB) in row-block-major order, and
+ *       inside a tile the 16 words of each row contiguous, so word w of row
+ *       n (k = 16w .. 16w+15) is word ((n/16)*(K/256) + w/16)*256 +
+ *       (n%16)*16 + w%16.  (Sixteen rows' 64-byte segments of one 256-k
+ *       block are one contiguous KiB, read whole by the matmuls.)
  *   INT8 activation codes   int8 [M][K], two's complement.
  *   INT4 activation codes   uint8 [M][K/2]: for each row, one little-endian
  *       32-bit word per 8 consecutive k; the code of k0 + 4*j + i (i in 0..3,

@@ -7,22 +7,34 @@ and to read the GPU's packed outputs back.
 import numpy as np
 
 
-def pack_ternary(wt: np.ndarray) -> np.ndarray:
-    """int8 [N][K] in {-1,0,1} -> uint8 [N][K/4]; per 16 k one LE word,
-    code of k0+4j+i at bits 8i+2j, 2-bit codes 00=0, 01=+1, 11=-1."""
+def _ternary_words(wt: np.ndarray) -> np.ndarray:
+    """int8 [N][K] in {-1,0,1} -> row-major words [N][K/16]: per 16 k one
+    word, code of k0+4j+i at bits 8i+2j, 2-bit codes 00=0, 01=+1, 11=-1."""
     wt = np.asarray(wt, dtype=np.int8)
     N, K = wt.shape
     code = np.where(wt == 1, 1, np.where(wt == -1, 3, 0)).astype(np.uint32)
     g = code.reshape(N, K // 16, 4, 4)          # [.., j, i] -> k0 + 4j + i
     shifts = (8 * np.arange(4)[None, :] + 2 * np.arange(4)[:, None]).astype(np.uint32)  # [j, i]
-    words = (g << shifts).sum(axis=(2, 3), dtype=np.uint64).astype(np.uint32)
-    return words.view(np.uint8).reshape(N, K // 4)
+    return (g << shifts).sum(axis=(2, 3), dtype=np.uint64).astype(np.uint32)
+
+
+def pack_ternary(wt: np.ndarray) -> np.ndarray:
+    """int8 [N][K] in {-1,0,1} -> the packed buffer, uint8 [N][K/4] in size:
+    the words of _ternary_words in tiles of 16 rows x 256 k (16 x 16 words,
+    1 KiB), tiles in row-block-major order, inside a tile row by row (the 16
+    words of a row contiguous).  N % 16 == 0 and K % 256 == 0."""
+    N, K = np.shape(wt)
+    if N % 16 or K % 256:
+        raise ValueError("tiled packing needs N % 16 == 0 and K % 256 == 0")
+    words = _ternary_words(wt).reshape(N // 16, 16, K // 256, 16)      # [row block, row, k block, word]
+    tiled = np.ascontiguousarray(words.transpose(0, 2, 1, 3))         # [row block, k block, row, word]
+    return tiled.view(np.uint8).reshape(N, K // 4)
 
 
 def unpack_ternary(wp: np.ndarray, K: int) -> np.ndarray:
     wp = np.ascontiguousarray(wp, dtype=np.uint8)
-    N = wp.shape[0]
-    words = wp.view(np.uint32).reshape(N, K // 16, 1, 1)
+    N = wp.size * 4 // K
+    words = wp.view(np.uint32).reshape(N // 16, K // 256, 16, 16).transpose(0, 2, 1, 3).reshape(N, K // 16, 1, 1)
     shifts = (8 * np.arange(4)[None, :] + 2 * np.arange(4)[:, None]).astype(np.uint32)
     code = (words >> shifts) & 3
     if np.any(code == 2):

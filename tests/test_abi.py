@@ -116,14 +116,21 @@ def test_stage_validation(L):
 
 def test_layout_codecs_hand_examples():
     # ternary: k0..k15 = +1, -1, 0, 0 | 0 ... ; code of k (=4j+i) at bits 8i+2j
-    wt = np.zeros((1, 16), np.int8)
+    wt = np.zeros((16, 256), np.int8)
     wt[0, 0] = 1    # i=0 j=0 -> bits 0-1 = 01
     wt[0, 1] = -1   # i=1 j=0 -> bits 8-9 = 11
     wt[0, 4] = -1   # i=0 j=1 -> bits 2-3 = 11
     wt[0, 15] = 1   # i=3 j=3 -> bits 30-31 = 01
     p = pack_ternary(wt)
-    assert p.view(np.uint32)[0, 0] == 0b01 | (0b11 << 8) | (0b11 << 2) | (0b01 << 30)
-    np.testing.assert_array_equal(unpack_ternary(p, 16), wt)
+    assert p.view(np.uint32).reshape(-1)[0] == 0b01 | (0b11 << 8) | (0b11 << 2) | (0b01 << 30)
+    np.testing.assert_array_equal(unpack_ternary(p, 256), wt)
+    # tiles of 16 rows x 256 k: word w of row n at ((n/16)(K/256) + w/16) * 256 + (n%16) * 16 + w%16
+    wt = np.zeros((32, 512), np.int8)
+    wt[17, 256 + 16 * 3] = 1     # row 17 (block 1, row 1), word 19 (k block 1, word 3)
+    words = pack_ternary(wt).view(np.uint32).reshape(-1)
+    assert np.flatnonzero(words).tolist() == [(1 * 2 + 1) * 256 + 1 * 16 + 3] and words[(1 * 2 + 1) * 256 + 19] == 1
+    with pytest.raises(ValueError):
+        pack_ternary(np.zeros((8, 256), np.int8))
     # int4: code of k (=4j+i) at bits 8i+4j
     q = np.array([[1, -1, 7, -8, 2, 0, 0, 3]], np.int8)
     w = pack_int4(q).view(np.uint32)[0, 0]
@@ -132,8 +139,8 @@ def test_layout_codecs_hand_examples():
     rng = np.random.default_rng(0)
     q = rng.integers(-8, 8, (5, 64)).astype(np.int8)
     np.testing.assert_array_equal(unpack_int4(pack_int4(q), 64), q)
-    wt = rng.integers(-1, 2, (3, 256)).astype(np.int8)
-    np.testing.assert_array_equal(unpack_ternary(pack_ternary(wt), 256), wt)
+    wt = rng.integers(-1, 2, (48, 768)).astype(np.int8)
+    np.testing.assert_array_equal(unpack_ternary(pack_ternary(wt), 768), wt)
     # fp6 operand layout: field p = h + 2b + 8d0 + 16d1 carries k = b + 4d0 + 8h + 16d1,
     # as the e2m3 code of q/2 (q=7 -> 3.5 = 1.75*2 -> 0b010110; q=-8 -> -4 -> 0b111000;
     # q=1 -> 0.5, subnormal 4/8 -> 0b000100; q=-3 -> -1.5 -> 0b101100)

@@ -331,6 +331,26 @@ def test_single_launch_decode(bits, M, K, N, xdt, gain):
     assert rel_l2(yh, y2) <= 1e-3, rel_l2(yh, y2)
 
 
+def test_fp6_matmul_repeatable_with_fresh_buffers():
+    """Regression: the fp6 x fp4 matmul once issued two extra copies per even
+    stage into the LDS buffer being read, which corrupted outputs only when
+    the copies happened to land first.  At the 7B Wdown shape, repeated
+    stage calls with freshly allocated codes, scales and outputs must equal
+    the single-call forward every time."""
+    M, K, N = 8192, 16384, 4096
+    w = synthetic.Workload("t", M, K, N, 4, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, 7)
+    x, xb, wl = synthetic.make_inputs(w)
+    xd = x_to_dev(x, xb)
+    wd = dev(wl)
+    for _ in range(6):
+        wp, a = hbl.quantize_weights(wd)
+        y = hbl.forward(xd, wp, a, 4)
+        c6, d6 = hbl.quantize_act(xd, 6)
+        y6 = hbl.matmul_dequant(c6, 6, d6, wp, a, K)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y6.view(torch.int16))
+
+
 @pytest.mark.parametrize("M,K,N", [(65, 256, 16), (257, 1024, 272), (300, 2048, 512), (513, 16384, 256),
                                    (1000, 4096, 4096), (8192, 16384, 4096)])
 def test_int4_prefill_fp6_path_equals_int8_instruction_path(M, K, N):

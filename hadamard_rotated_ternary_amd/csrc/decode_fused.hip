@@ -46,7 +46,7 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
 
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   float* region = reinterpret_cast<float*>(dyn);               // transform exchange
-  uint8_t* slab = dyn + REGION_BYTES;                          // [M][K] operand bytes, then a zero row
+  uint8_t* slab = dyn + REGION_BYTES;                          // [M][K] operand bytes (opswz order), then a zero row
   __shared__ float red[32];
   __shared__ int part[16 * 16];
   __shared__ float dtok[FD_MAXM];
@@ -60,14 +60,17 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
   // stream could only be used once the whole stream had arrived
   const int base0 = P0::thr_idx(tid);
   const int baseL = PL::thr_idx(tid);
+  // (only the M tokens present: every load instruction costs the CU's
+  // address unit 16 cycles, and at M = 1 three redundant tokens would delay
+  // the weight requests queued behind them)
   uint4 xr[XBF16 ? FD_MAXM : 1][E / 8];
   if constexpr (XBF16) {
 #pragma unroll
     for (int t = 0; t < FD_MAXM; ++t) {
-      const int tt = min(t, M - 1);
+      if (t >= M) break;                                   // uniform
 #pragma unroll
       for (int gi = 0; gi < E / 8; ++gi)
-        xr[t][gi] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (size_t)tt * K + base0 +
+        xr[t][gi] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (size_t)t * K + base0 +
                                                     P0::reg_idx(8 * gi));
     }
   }
@@ -145,14 +148,17 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
     const float cs = cc * (Q / G);
     if (tid == 0) dtok[t] = G / Q;
     // round to nearest even in the adder (fma with 1.5 * 2^23), clamp INT4,
-    // keep the low byte; operand bytes are q (INT8) or 16 q (INT4)
-    uint8_t* row = slab + t * K;
+    // keep the low byte: the operand byte is q itself for both widths (the
+    // codes never take the packed nibble form here), so the accumulators
+    // hold 64 * acc either way
+    // (opswz order; the thread and register parts of an index have disjoint
+    // bits, so each part is permuted on its own)
+    uint8_t* row = slab + t * K + opswz(baseL);
 #pragma unroll
     for (int r = 0; r < E; ++r) {
       float q = __builtin_fmaf(v[r], cs, kRoundMagic);
       if constexpr (BITS == 4) q = fminf(fmaxf(q, kRoundMagic - 8.0f), kRoundMagic + 7.0f);
-      const uint32_t b = __float_as_uint(q);
-      row[baseL + PL::reg_idx(r)] = (uint8_t)(BITS == 8 ? b : (b << 4));
+      row[opswz(PL::reg_idx(r))] = (uint8_t)__float_as_uint(q);
     }
   }
   if (tid < 4) reinterpret_cast<uint4*>(slab + M * K)[tid] = make_uint4(0, 0, 0, 0);
@@ -167,12 +173,12 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
   for (int i = 0; i < MAXB; ++i) {
     const int b = wave + FD_NW * i;
     const uint4* ap = reinterpret_cast<const uint4*>(arow + astep * b * FD_DKB);
-    const uint4 a0 = ap[0], a1 = ap[1], a2 = ap[2], a3 = ap[3];
     const uint4 p = wq[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const v4i wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
-      const v4i aop = v4i{(int)u4get(a0, j), (int)u4get(a1, j), (int)u4get(a2, j), (int)u4get(a3, j)};
+      const uint4 a = ap[j];                               // opswz order: step j's operand
+      const v4i aop = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc, 0, 0, 0);
     }
   }
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
   __syncthreads();
   if (tid < M * 16) {
     const int t = tid / 16, nn = ch0 + tid % 16;
-    if (nn < N) store_out<OUT>(Y, (size_t)t * N + nn, unscale<BITS>(part[tid]), dtok[t] * fmaxf(walpha[0], kEpsQ));
+    if (nn < N) store_out<OUT>(Y, (size_t)t * N + nn, unscale<8>(part[tid]), dtok[t] * fmaxf(walpha[0], kEpsQ));
   }
 }
 

@@ -672,7 +672,7 @@ template <int BITS, int NW, int UPT, int OUT>
 __global__ __launch_bounds__(64 * NW) void gemm_decode_few_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t slab[];   // [M][K] int8 operands, then 64 zero bytes
+  extern __shared__ __attribute__((aligned(16))) uint8_t slab[];   // [M][K] int8 operands (opswz order), then 64 zero bytes
   __shared__ int red[16 * 16];
   constexpr int MAXB = 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -706,8 +706,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_few_kernel(
     const int u = q * 64 * NW + tid;
     if (u >= units) continue;
     const int t = u / upr, ub = u % upr;
+    // operand rows in opswz order
     if constexpr (BITS == 8) {
-      *reinterpret_cast<uint4*>(slab + t * opr + 16 * ub) = st[q];
+      opstore16(slab + t * opr, ub, st[q]);
     } else {
       // 32 INT4 codes -> 32 operand bytes 16*q in k order
       const uint32_t w[4] = {st[q].x, st[q].y, st[q].z, st[q].w};
@@ -716,8 +717,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_few_kernel(
       o0.z = (w[1] << 4) & 0xF0F0F0F0u; o0.w = w[1] & 0xF0F0F0F0u;
       o1.x = (w[2] << 4) & 0xF0F0F0F0u; o1.y = w[2] & 0xF0F0F0F0u;
       o1.z = (w[3] << 4) & 0xF0F0F0F0u; o1.w = w[3] & 0xF0F0F0F0u;
-      *reinterpret_cast<uint4*>(slab + t * opr + 32 * ub) = o0;
-      *reinterpret_cast<uint4*>(slab + t * opr + 32 * ub + 16) = o1;
+      opstore16(slab + t * opr, 2 * ub, o0);
+      opstore16(slab + t * opr, 2 * ub + 1, o1);
     }
   }
   if (tid < 4) reinterpret_cast<uint4*>(slab + M * opr)[tid] = make_uint4(0, 0, 0, 0);
@@ -732,12 +733,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_few_kernel(
     const int b = wave + NW * i;
     if (b >= nblk) continue;                               // wave-uniform
     const uint4* ap = reinterpret_cast<const uint4*>(arow_lds + astep * b * DKB);
-    const uint4 a0 = ap[0], a1 = ap[1], a2 = ap[2], a3 = ap[3];
     const uint4 p = wq[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const v4i wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
-      const v4i aop = v4i{(int)u4get(a0, j), (int)u4get(a1, j), (int)u4get(a2, j), (int)u4get(a3, j)};
+      const uint4 a = ap[j];                               // opswz order: step j's operand
+      const v4i aop = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc, 0, 0, 0);
     }
   }

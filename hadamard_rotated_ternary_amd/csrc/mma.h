@@ -32,6 +32,21 @@ template <int BITS>
 HBL_DEV int unscale(int v) { return BITS == 8 ? (v >> 6) : (v >> 10); }
 HBL_DEV uint32_t u4get(const uint4& u, int j) { return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w; }
 
+// Order of the int8 operand rows the decode kernels stage in LDS: inside each
+// 64-byte group byte-address bits 2-3 and 4-5 trade places.  A lane's operand
+// of MFMA step j is dword j of each of its four 16-byte chunks (the pairing
+// wfield() fixes); in this order those four dwords are the contiguous 16 bytes
+// at 16 j, one ds_read_b128 straight into the operand registers.
+HBL_DEV constexpr int opswz(int a) { return (a & ~0x3C) | ((a & 0x0C) << 2) | ((a & 0x30) >> 2); }
+// Store 16-byte chunk ch (k order) of an operand row in that order.
+HBL_DEV void opstore16(uint8_t* row, int ch, const uint4& v) {
+  uint8_t* p = row + 64 * (ch >> 2) + 4 * (ch & 3);
+  reinterpret_cast<uint32_t*>(p)[0] = v.x;
+  reinterpret_cast<uint32_t*>(p + 16)[0] = v.y;
+  reinterpret_cast<uint32_t*>(p + 32)[0] = v.z;
+  reinterpret_cast<uint32_t*>(p + 48)[0] = v.w;
+}
+
 // Copy 16 bytes per lane from global memory straight into LDS: the wave's
 // 64 lanes fill 1 KiB at lds_base (wave-uniform), lane L at +16L.  Issued from
 // inline asm so the compiler does not track it (it cannot tell which LDS

@@ -39,6 +39,11 @@ constexpr int prep_wg(int logk, int loge) { return (1 << (logk - loge)) < 64 ? 6
 // Persistent: a workgroup walks tokens blockIdx.x*TPB + tok, then + gridDim.x*TPB,
 // ...; the next token's activations are requested right after the current
 // ones have been unpacked, so their HBM latency hides behind the transform.
+// With a gain, its slice is requested once the activations are unpacked and
+// applied before the next token's prefetch is issued: loads return in issue
+// order, so a gain load queued behind the prefetch would wait for that whole
+// HBM round trip (and holding the slice across the unpack costs registers
+// and occupancy).
 template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int MODE, bool ROT>
 __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
     const void* __restrict__ x, const float* __restrict__ gain, int M,
@@ -108,7 +113,6 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
         v[8 * gi + 6] = __uint_as_float(b.z); v[8 * gi + 7] = __uint_as_float(b.w);
       }
     }
-    if (it + 1 < iters) load(m + stride);
     if (!valid) {
 #pragma unroll
       for (int r = 0; r < E; ++r) v[r] = 0.f;
@@ -121,13 +125,13 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
     if (gain != nullptr) {
 #pragma unroll
       for (int gi = 0; gi < E / 8; ++gi) {
-        const int idx = base0 + P0::reg_idx(8 * gi);
-        const float4* p = reinterpret_cast<const float4*>(gain + idx);
+        const float4* p = reinterpret_cast<const float4*>(gain + base0 + P0::reg_idx(8 * gi));
         const float4 a = p[0], b = p[1];
         v[8 * gi + 0] *= a.x; v[8 * gi + 1] *= a.y; v[8 * gi + 2] *= a.z; v[8 * gi + 3] *= a.w;
         v[8 * gi + 4] *= b.x; v[8 * gi + 5] *= b.y; v[8 * gi + 6] *= b.z; v[8 * gi + 7] *= b.w;
       }
     }
+    if (it + 1 < iters) load(m + stride);
     // ---- Walsh-Hadamard transform (unnormalised) of x*g
     if constexpr (ROT) run_passes<LOGK, LOGE, P2, 0>(v, region, tau);
 
@@ -270,9 +274,14 @@ namespace hbl {
 template <int LOGK, int LOGE, int P2>
 static hipError_t launch_prep_t(const PrepArgs& a) {
   using C = PrepCfg<LOGK, LOGE, P2>;
-  // persistent grid: enough workgroups to fill every CU at the occupancy the
-  // LDS footprint allows (two workgroups per CU for the prefill dealings)
-  const int per_cu = (160 * 1024) / (int)(sizeof(float) * C::REGION * C::TPB + 64) >= 2 ? 2 : 1;
+  // persistent grid: about 24 waves per CU (six per SIMD) where the LDS
+  // footprint allows -- the transform's exchanges, barriers and reductions
+  // stall a wave often, and only other resident waves hide that
+  const int fit = (160 * 1024) / (int)(sizeof(float) * C::REGION * C::TPB + 64);
+  const int waves = C::WG / 64;
+  int per_cu = (24 + waves - 1) / waves;
+  if (per_cu > fit) per_cu = fit;
+  if (per_cu < 1) per_cu = 1;
   const int want = (a.M + C::TPB - 1) / C::TPB;
   const int grid = want < a.cus * per_cu ? want : a.cus * per_cu;
   if (grid == 0) return hipSuccess;
@@ -297,18 +306,21 @@ static hipError_t launch_prep_t(const PrepArgs& a) {
   return hipGetLastError();
 }
 
-// Dealing per K: one LDS exchange for the prefill shapes (E >= T), more
-// threads per token for small M so a single token is not latency bound.
+// Dealing per K.  Few values per thread (16 or 32) and many resident waves
+// beat fewer LDS exchanges: at 8192 tokens, 128 values per thread (one
+// exchange, one wave per SIMD) took 125 / 104 / 57 us at K = 16384 / 8192 /
+// 4096 against 108 / 50 / 27 us here.  Small M takes 16 values per thread so
+// that a single token is spread over more threads.
 hipError_t launch_prep(const PrepArgs& a) {
   const bool small = a.M <= 64;
   switch (a.logk) {
     case 8:  return launch_prep_t<8, 4, 6>(a);
     case 9:  return launch_prep_t<9, 5, 6>(a);
     case 10: return launch_prep_t<10, 5, 7>(a);
-    case 11: return launch_prep_t<11, 6, 7>(a);
-    case 12: return small ? launch_prep_t<12, 4, 6>(a) : launch_prep_t<12, 6, 8>(a);
-    case 13: return small ? launch_prep_t<13, 4, 6>(a) : launch_prep_t<13, 7, 8>(a);
-    case 14: return small ? launch_prep_t<14, 4, 6>(a) : launch_prep_t<14, 7, 9>(a);
+    case 11: return launch_prep_t<11, 4, 6>(a);
+    case 12: return launch_prep_t<12, 4, 6>(a);
+    case 13: return small ? launch_prep_t<13, 4, 6>(a) : launch_prep_t<13, 5, 7>(a);
+    case 14: return small ? launch_prep_t<14, 4, 6>(a) : launch_prep_t<14, 5, 7>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -143,6 +143,29 @@ def test_codes_match_oracle(K, bits, M):
     np.testing.assert_allclose(host(d), d_or, rtol=1e-5)
 
 
+@pytest.mark.parametrize("K,M,bf16", [(16384, 1100, True), (16384, 1100, False), (8192, 2100, True),
+                                      (4096, 3200, True), (2048, 6200, True)])
+@pytest.mark.parametrize("bits", [8, 4, 6])
+def test_codes_with_gain_over_persistent_iterations(K, M, bf16, bits):
+    """RMSNorm gain at prefill token counts: enough tokens that every
+    workgroup of the persistent grid walks two or more of them (gain loads
+    and the next token's prefetch in flight together).  Evenly spaced
+    sampled rows against the oracle."""
+    x, xb = make_x(M, K, 11 * K + M + bits, bf16=bf16)
+    g = synthetic.make_gain(K, K + 1)
+    codes, d = hbl.quantize_act(x_to_dev(x, xb), bits, gain=dev(g))
+    rows = synthetic.sample_rows(M, 24)
+    c = host(codes)
+    if bits == 6:   # [K/128][M][96]: the sampled rows of every 128-k block
+        q = unpack_int4_fp6(np.ascontiguousarray(c.reshape(K // 128, M, 96)[:, rows]), K)
+    else:
+        q = c[rows].astype(np.int8) if bits == 8 else unpack_int4(c[rows], K)
+    xt = oracle.hadamard_rotate(oracle.rmsnorm(x[rows], g))
+    q_or, d_or, pre = oracle.quant_act(xt, 8 if bits == 8 else 4)
+    check_codes(q, q_or, pre)
+    np.testing.assert_allclose(host(d)[rows], d_or, rtol=1e-5)
+
+
 def test_zero_token_and_tiny_token():
     K = 1024
     x = np.zeros((3, K), np.float32)

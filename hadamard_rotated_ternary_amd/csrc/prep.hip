@@ -113,7 +113,8 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
         v[8 * gi + 6] = __uint_as_float(b.z); v[8 * gi + 7] = __uint_as_float(b.w);
       }
     }
-    if (!valid) {
+    // (with one token per workgroup every token the loop visits exists)
+    if (C::TPB > 1 && !valid) {
 #pragma unroll
       for (int r = 0; r < E; ++r) v[r] = 0.f;
     }
@@ -131,6 +132,10 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
         v[8 * gi + 4] *= b.x; v[8 * gi + 5] *= b.y; v[8 * gi + 6] *= b.z; v[8 * gi + 7] *= b.w;
       }
     }
+    // the squares are summed before the prefetch is issued (an empty asm
+    // consumes ss): otherwise they are sunk below it, the raw registers stay
+    // live across the load, and the loop-carried buffer gets copied twice
+    __asm__ volatile("" : : "v"(ss));
     if (it + 1 < iters) load(m + stride);
     // ---- Walsh-Hadamard transform (unnormalised) of x*g
     if constexpr (ROT) run_passes<LOGK, LOGE, P2, 0>(v, region, tau);

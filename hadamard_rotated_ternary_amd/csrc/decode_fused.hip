@@ -46,7 +46,7 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
 
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   float* region = reinterpret_cast<float*>(dyn);               // transform exchange
-  uint8_t* slab = dyn + REGION_BYTES;                          // [M][K] operand bytes (opswz order), then a zero row
+  uint8_t* slab = dyn + REGION_BYTES;                          // [M][K] operand bytes, then a zero row
   __shared__ float red[32];
   __shared__ int part[16 * 16];
   __shared__ float dtok[FD_MAXM];
@@ -151,14 +151,12 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
     // keep the low byte: the operand byte is q itself for both widths (the
     // codes never take the packed nibble form here), so the accumulators
     // hold 64 * acc either way
-    // (opswz order; the thread and register parts of an index have disjoint
-    // bits, so each part is permuted on its own)
-    uint8_t* row = slab + t * K + opswz(baseL);
+    uint8_t* row = slab + t * K;
 #pragma unroll
     for (int r = 0; r < E; ++r) {
       float q = __builtin_fmaf(v[r], cs, kRoundMagic);
       if constexpr (BITS == 4) q = fminf(fmaxf(q, kRoundMagic - 8.0f), kRoundMagic + 7.0f);
-      row[opswz(PL::reg_idx(r))] = (uint8_t)__float_as_uint(q);
+      row[baseL + PL::reg_idx(r)] = (uint8_t)__float_as_uint(q);
     }
   }
   if (tid < 4) reinterpret_cast<uint4*>(slab + M * K)[tid] = make_uint4(0, 0, 0, 0);
@@ -176,9 +174,8 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
     const uint4 p = wq[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const v4i wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
-      const uint4 a = ap[j];                               // opswz order: step j's operand
-      const v4i aop = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+      const v4i wop = wstep(u4get(p, j));
+      const v4i aop = as_v4i(ap[j]);                       // codes 16j .. 16j+15 of the lane's 64
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc, 0, 0, 0);
     }
   }

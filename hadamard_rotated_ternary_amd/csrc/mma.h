@@ -12,16 +12,23 @@ namespace hbl {
 // A packed weight word holds the 2-bit two's complement codes of 16
 // consecutive k, the code of k0+4j+i in bits 8i+2j (field j of byte i).
 // Shifting field j to the top of its byte and masking gives, byte by byte,
-// exactly 64*w as a signed int8 (0x40 = +64, 0xC0 = -64).  MFMA step j of a
-// 64-k group takes field j of four packed words, so its operand covers codes
-// 16d + 4j + i (d = word, i = byte): 1-2 VALU ops per operand dword.
+// exactly 64*w as a signed int8 (0x40 = +64, 0xC0 = -64).
 HBL_DEV uint32_t wfield(uint32_t p, int j) {
   return (j == 3 ? p : (p << (6 - 2 * j))) & 0xC0C0C0C0u;
 }
-// INT4 activation words hold codes 8 at a time, the code of k0+4j+i in bits
-// 8i+4j.  Moving a nibble to the top of its byte gives 16*q as a signed int8.
-// For the same code set 16d + 4j + i, step j takes the low (j even) or high
-// (j odd) nibbles of word 2d + j/2.
+// MFMA step s (0..3) of a lane's 64-k group takes the four fields of packed
+// word s: operand register r = field r, whose byte i holds code
+// k0 + 16s + 4r + i.  Those are the 16 consecutive codes k0+16s .. k0+16s+15,
+// so int8 activations are the other operand exactly as stored (16 bytes from
+// offset 16s, no regrouping); 7 VALU ops per weight word.
+HBL_DEV v4i wstep(uint32_t p) { return v4i{(int)wfield(p, 0), (int)wfield(p, 1), (int)wfield(p, 2), (int)wfield(p, 3)}; }
+HBL_DEV v4i as_v4i(const uint4& u) { return v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w}; }
+// The INT4 matmuls pair the other way: step j takes field j of four packed
+// words (codes 16d + 4j + i, d = word, i = byte) against the same codes of
+// the INT4 activations.  Those words hold codes 8 at a time, the code of
+// k0+4j+i in bits 8i+4j; step j takes the low (j even) or high (j odd)
+// nibbles of word 2d + j/2, moved to the top of each byte: 16*q as a signed
+// int8.
 HBL_DEV uint32_t a4field(uint32_t w, int j) {
   return ((j & 1) ? w : (w << 4)) & 0xF0F0F0F0u;
 }
@@ -31,21 +38,6 @@ HBL_DEV uint32_t a4field(uint32_t w, int j) {
 template <int BITS>
 HBL_DEV int unscale(int v) { return BITS == 8 ? (v >> 6) : (v >> 10); }
 HBL_DEV uint32_t u4get(const uint4& u, int j) { return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w; }
-
-// Order of the int8 operand rows the decode kernels stage in LDS: inside each
-// 64-byte group byte-address bits 2-3 and 4-5 trade places.  A lane's operand
-// of MFMA step j is dword j of each of its four 16-byte chunks (the pairing
-// wfield() fixes); in this order those four dwords are the contiguous 16 bytes
-// at 16 j, one ds_read_b128 straight into the operand registers.
-HBL_DEV constexpr int opswz(int a) { return (a & ~0x3C) | ((a & 0x0C) << 2) | ((a & 0x30) >> 2); }
-// Store 16-byte chunk ch (k order) of an operand row in that order.
-HBL_DEV void opstore16(uint8_t* row, int ch, const uint4& v) {
-  uint8_t* p = row + 64 * (ch >> 2) + 4 * (ch & 3);
-  reinterpret_cast<uint32_t*>(p)[0] = v.x;
-  reinterpret_cast<uint32_t*>(p + 16)[0] = v.y;
-  reinterpret_cast<uint32_t*>(p + 32)[0] = v.z;
-  reinterpret_cast<uint32_t*>(p + 48)[0] = v.w;
-}
 
 // Copy 16 bytes per lane from global memory straight into LDS: the wave's
 // 64 lanes fill 1 KiB at lds_base (wave-uniform), lane L at +16L.  Issued from

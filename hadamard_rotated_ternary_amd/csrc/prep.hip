@@ -314,8 +314,9 @@ static hipError_t launch_prep_t(const PrepArgs& a) {
 // Dealing per K.  Few values per thread (16 or 32) and many resident waves
 // beat fewer LDS exchanges: at 8192 tokens, 128 values per thread (one
 // exchange, one wave per SIMD) took 125 / 104 / 57 us at K = 16384 / 8192 /
-// 4096 against 108 / 50 / 27 us here.  Small M takes 16 values per thread so
-// that a single token is spread over more threads.
+// 4096 against 108 / 50 / 27 us here.  At K = 8192 small M takes 16 values
+// per thread (no measurable difference); at K = 16384 32 values per thread
+// also serve 8 to 64 tokens best (4.8 us instead of 5.4 us with 16).
 hipError_t launch_prep(const PrepArgs& a) {
   const bool small = a.M <= 64;
   switch (a.logk) {
@@ -325,7 +326,7 @@ hipError_t launch_prep(const PrepArgs& a) {
     case 11: return launch_prep_t<11, 4, 6>(a);
     case 12: return launch_prep_t<12, 4, 6>(a);
     case 13: return small ? launch_prep_t<13, 4, 6>(a) : launch_prep_t<13, 5, 7>(a);
-    case 14: return small ? launch_prep_t<14, 4, 6>(a) : launch_prep_t<14, 5, 7>(a);
+    case 14: return launch_prep_t<14, 5, 7>(a);
     default: return hipErrorInvalidValue;
   }
 }

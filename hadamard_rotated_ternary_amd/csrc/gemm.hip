@@ -543,6 +543,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
 constexpr int DKB = 256;
 
 struct DecodePlan { int cpw, S, mb, nw; };
+constexpr int kDecodeMaxSplit = 4;   // split-K ways the in-kernel reduction handles
 static DecodePlan decode_plan(int M, int K) {
 #ifdef HBL_DECODE_PLAN
   DecodePlan p = HBL_DECODE_PLAN(M);
@@ -553,11 +554,22 @@ static DecodePlan decode_plan(int M, int K) {
   return p;
 }
 
+// With S > 1 the S workgroups of a channel tile write int32 partial sums.
+// tile_count == nullptr: decode_reduce_kernel sums them.  Otherwise (the
+// counters zeroed before the launch) each workgroup stores its partial rows,
+// waits until those stores have completed, and counts itself in; the one
+// that arrives last sums the S partials, dequantises and stores, then leaves
+// its counter zero.  Nothing waits on another workgroup.  Partials are
+// stored and re-read as device-scope atomics, which write through and bypass
+// the per-XCD L2s, so no cache-wide fence is needed (a device-scope fence
+// writes back and invalidates the whole L2 of the XCD, which cost the
+// 64-token forward 55 us instead of 21 us: every workgroup threw away the
+// activation codes the others were still reading).
 template <int BITS, int MB, int CPW, int NW, int OUT>
 __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int S,
-    int32_t* __restrict__ partial) {
+    int32_t* __restrict__ partial, uint32_t* __restrict__ tile_count) {
   // Blocks held per wave per round: their loads need MAXB * (CPW + MB*BITS/2)
   // uint4 registers, kept near 48 (192 VGPRs).
   // (two with four token groups: 8 waves of 184 registers, two per SIMD, so
@@ -570,6 +582,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
   // banks (4c + g), where plain rows of CH ints would put 16 lanes on one.
   constexpr int RL = CH + 4;
   __shared__ int red[MB * 16 * RL];
+  __shared__ int is_last;
   auto red_col = [](int nl) { return (nl & ~15) | ((nl & 3) << 2) | ((nl >> 2) & 3); };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -674,8 +687,45 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
     if (n >= N) continue;
     const int v = red[t * RL + red_col(e % CH)];
     if (S == 1) store_out<OUT>(Y, (size_t)t * N + n, unscale<BITS>(v), ds_pre[q] * aw);
-    else partial[((size_t)s * M + t) * N + n] = v;
+    else if constexpr (MB == 1) partial[((size_t)s * M + t) * N + n] = v;
+    else __hip_atomic_store(&partial[((size_t)s * M + t) * N + n], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // (the single-token-group instantiation serves M <= 16, which the plan
+  // never splits; it keeps the separate reduction for any split it is given)
+  if constexpr (MB == 1) return;
+  if (S == 1 || tile_count == nullptr) return;
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+  __syncthreads();
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(&tile_count[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (uint32_t)(S - 1);
+  __syncthreads();
+  if (!is_last) return;
+  // every partial this thread sums is requested before any is waited for
+  // (clamped, always in-bounds addresses; splits past S count zero)
+  constexpr int NQ = (MB * 16 * CH + 64 * NW - 1) / (64 * NW);
+  int sum[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = q * 64 * NW + tid;
+    const int t = min(e / CH, M - 1), n = min(ch0 + e % CH, N - 1);
+    sum[q] = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < kDecodeMaxSplit; ++s2) {
+      const int v = __hip_atomic_load(&partial[((size_t)min(s2, S - 1) * M + t) * N + n], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      sum[q] += s2 < S ? v : 0;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = q * 64 * NW + tid;
+    if (e >= M * CH) continue;
+    const int t = e / CH, n = ch0 + e % CH;
+    if (n >= N) continue;
+    store_out<OUT>(Y, (size_t)t * N + n, unscale<BITS>(sum[q]), ds_pre[q] * aw);
+  }
+  if (tid == 0) __hip_atomic_store(&tile_count[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Few tokens (M <= 4): one workgroup of NW waves per 16 channels and the whole
@@ -784,10 +834,25 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const int32_t* __res
 // ===========================================================================
 // Host side
 
+// Split-K decode workspace: int32 partials [S][M][N], then one arrival
+// counter per channel tile.
+static size_t partials_bytes(const DecodePlan& p, int64_t M, int64_t N) {
+  return p.S > 1 ? (((size_t)p.S * M * N * 4 + 255) & ~(size_t)255) : 0;
+}
+int gemm_tile_counters(int64_t M, int64_t K, int64_t N) {
+  if (M > 64 || M <= 4) return 0;
+  const DecodePlan p = decode_plan((int)M, (int)K);
+  return p.S > 1 ? (int)((N + 16 * p.cpw - 1) / (16 * p.cpw)) : 0;
+}
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   if (M > 64 || M <= 0) return 0;
   const DecodePlan p = decode_plan((int)M, (int)K);
-  return p.S > 1 ? (((size_t)p.S * M * N * 4 + 255) & ~(size_t)255) : 0;
+  const size_t nc = (size_t)gemm_tile_counters(M, K, N);
+  return partials_bytes(p, M, N) + ((nc * 4 + 255) & ~(size_t)255);
+}
+uint32_t* gemm_tile_counter_ptr(void* ws, int64_t M, int64_t K, int64_t N) {
+  if (gemm_tile_counters(M, K, N) == 0 || ws == nullptr) return nullptr;
+  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + partials_bytes(decode_plan((int)M, (int)K), M, N));
 }
 
 template <int BITS, int MB, int CPW, int NW, int OUT>
@@ -795,9 +860,10 @@ static void launch_decode_p(const GemmArgs& a, int S) {
   constexpr int CH = 16 * CPW;
   dim3 grid((a.N + CH - 1) / CH, S);
   int32_t* part = static_cast<int32_t*>(a.ws);
+  uint32_t* counts = MB > 1 && S > 1 && S <= kDecodeMaxSplit ? a.tile_count : nullptr;
   hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, NW, OUT>), grid, dim3(64 * NW), 0, a.stream, a.codes,
-                     a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K, S, part);
-  if (S > 1)
+                     a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K, S, part, counts);
+  if (S > 1 && counts == nullptr)
     hipLaunchKernelGGL((decode_reduce_kernel<BITS, OUT>), dim3((a.M * a.N + 255) / 256), dim3(256), 0, a.stream,
                        part, S, a.M, a.N, a.dscale, a.walpha, a.out);
 }

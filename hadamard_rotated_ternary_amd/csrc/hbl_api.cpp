@@ -115,17 +115,23 @@ hbl_status forward(int bits, bool rotate, const void* x, hbl_dtype x_dtype, cons
   void* gws = ws + codes_bytes(bits, M, K) + scales_bytes(M);
   const size_t gws_bytes = hbl::gemm_workspace_bytes(M, K, N);
 
+  // split-K decode shapes: prep clears the matmul's arrival counters, so the
+  // matmul's last workgroup per tile reduces (no separate reduction launch)
+  const bool fp6 = fp6_path(bits, M);
+  uint32_t* counts = fp6 ? nullptr : hbl::gemm_tile_counter_ptr(gws, M, K, N);
+
   hbl::PrepArgs p{};
   p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
-  p.bits = bits; p.mode = fp6_path(bits, M) ? 2 : 0; p.rotate = rotate; p.codes = codes; p.dscale = dscale;
-  p.xt = nullptr; p.stream = stream;
+  p.bits = bits; p.mode = fp6 ? 2 : 0; p.rotate = rotate; p.codes = codes; p.dscale = dscale;
+  p.xt = nullptr; p.zero = counts; p.nzero = counts ? hbl::gemm_tile_counters(M, K, N) : 0; p.stream = stream;
   if (hipError_t e = hbl::launch_prep(p)) return launched(e);
 
   hbl::GemmArgs g{};
   g.codes = codes; g.bits = bits; g.wpack = w_packed; g.dscale = dscale; g.walpha = w_alpha; g.out = y;
   g.out_kind = y_dtype == HBL_BF16 ? hbl::OUT_BF16 : hbl::OUT_F32;
-  g.M = (int)M; g.N = (int)N; g.K = (int)K; g.ws = gws; g.ws_bytes = gws_bytes; g.stream = stream;
-  return launched(fp6_path(bits, M) ? hbl::launch_gemm_fp6(g) : hbl::launch_gemm(g));
+  g.M = (int)M; g.N = (int)N; g.K = (int)K; g.ws = gws; g.ws_bytes = gws_bytes; g.tile_count = counts;
+  g.stream = stream;
+  return launched(fp6 ? hbl::launch_gemm_fp6(g) : hbl::launch_gemm(g));
 }
 
 }  // namespace

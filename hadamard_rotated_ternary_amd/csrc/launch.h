@@ -20,6 +20,8 @@ struct PrepArgs {
   uint8_t* codes;
   float* dscale;
   float* xt;
+  uint32_t* zero;    // words the first workgroup clears (the matmul's split-K counters), or nullptr
+  int nzero;
   hipStream_t stream;
 };
 hipError_t launch_prep(const PrepArgs& a);
@@ -37,6 +39,7 @@ struct GemmArgs {
   int M, N, K;
   void* ws;               // split-K partials (decode path)
   size_t ws_bytes;
+  uint32_t* tile_count;   // zeroed split-K arrival counters (or nullptr: separate reduction kernel)
   hipStream_t stream;
 };
 hipError_t launch_gemm(const GemmArgs& a);
@@ -46,6 +49,10 @@ constexpr int kFp6MinM = 64;
 hipError_t launch_gemm_fp6(const GemmArgs& a);
 // Workspace bytes the matmul needs beyond the codes and scales.
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+// Split-K arrival counters inside that workspace (count 0 / nullptr when the
+// shape needs none); they must be zero when the matmul starts.
+int gemm_tile_counters(int64_t M, int64_t K, int64_t N);
+uint32_t* gemm_tile_counter_ptr(void* ws, int64_t M, int64_t K, int64_t N);
 
 // Single-launch forward for 1..4 tokens with K = 8192 or 16384 (decode):
 // transform, quantiser and matmul in one kernel.

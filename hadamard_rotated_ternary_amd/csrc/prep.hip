@@ -47,7 +47,8 @@ constexpr int prep_wg(int logk, int loge) { return (1 << (logk - loge)) < 64 ? 6
 template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int MODE, bool ROT>
 __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
     const void* __restrict__ x, const float* __restrict__ gain, int M,
-    uint8_t* __restrict__ codes, float* __restrict__ dscale, float* __restrict__ xt) {
+    uint8_t* __restrict__ codes, float* __restrict__ dscale, float* __restrict__ xt,
+    uint32_t* __restrict__ zero, int nzero) {
   using C = PrepCfg<LOGK, LOGE, P2>;
   static_assert(ROT || (MODE == 0 || MODE == 2), "only the quantising modes run without the transform");
   using P0 = Pass<LOGK, LOGE, 0>;
@@ -83,6 +84,10 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
     }
   };
   if (iters > 0) load(first + tok);
+  // the following matmul's split-K counters start at zero (here, behind the
+  // first activation load, whose latency covers it)
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0u;
 
   for (int it = 0; it < iters; ++it) {
     const int m = first + tok + it * stride;
@@ -289,10 +294,10 @@ static hipError_t launch_prep_t(const PrepArgs& a) {
   if (per_cu < 1) per_cu = 1;
   const int want = (a.M + C::TPB - 1) / C::TPB;
   const int grid = want < a.cus * per_cu ? want : a.cus * per_cu;
-  if (grid == 0) return hipSuccess;
+  if (grid == 0) return hipSuccess;   // (M == 0: no matmul follows either)
 #define HBL_PREP(BITS, BF, MODE, ROT)                                                           \
   hipLaunchKernelGGL((prep_kernel<LOGK, LOGE, P2, BITS, BF, MODE, ROT>), dim3(grid), dim3(C::WG), 0, \
-                     a.stream, a.x, a.gain, a.M, a.codes, a.dscale, a.xt)
+                     a.stream, a.x, a.gain, a.M, a.codes, a.dscale, a.xt, a.zero, a.zero ? a.nzero : 0)
 #define HBL_PREP_R(BITS, BF, MODE) \
   if (a.rotate) HBL_PREP(BITS, BF, MODE, true); else HBL_PREP(BITS, BF, MODE, false)
   if (a.mode == 1) {

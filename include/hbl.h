@@ -129,7 +129,11 @@ hbl_status hbl_quantize_weights(const float *w, int64_t N, int64_t K,
  *   w_packed  uint8 [N][K/4] from hbl_quantize_weights;  w_alpha fp32 [1]
  *   y         [M][N] output, dtype y_dtype (fp32 or bf16; bf16 rounds to nearest even)
  *   workspace at least hbl_workspace_bytes(HBL_OP_FORWARD_INT8, M, K, N) bytes;
- *             holds the activation codes and scales between the two kernels.
+ *             holds the activation codes and scales between the two kernels,
+ *             and for 17..64 tokens the split-K partial sums plus one arrival
+ *             counter per 64-channel tile, which the first kernel of each call
+ *             clears (the workspace needs no initialisation; calls sharing one
+ *             workspace must be stream-ordered).
  */
 hbl_status hbl_forward_int8(const void *x, hbl_dtype x_dtype, const float *gain,
                             const uint8_t *w_packed, const float *w_alpha,

@@ -354,6 +354,33 @@ def test_single_launch_decode(bits, M, K, N, xdt, gain):
     assert rel_l2(yh, y2) <= 1e-3, rel_l2(yh, y2)
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,K,N", [(17, 4096, 272), (33, 16384, 4096), (64, 16384, 4096), (64, 1024, 48)])
+def test_split_k_decode_reduction_in_kernel(bits, M, K, N):
+    """17..64 tokens: the forward's matmul splits K and the last workgroup of
+    each channel tile sums the partials; the stage calls sum them in a
+    separate reduction kernel.  Same codes, exact integer sums: equal bit for
+    bit, with a workspace that starts full of 0xFF (the first kernel clears
+    the arrival counters) and over repeated calls on it whose inputs
+    alternate in sign, so partial sums left over from the call before would
+    show."""
+    w = synthetic.Workload("t", M, K, N, bits, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, 9 * M + K + N)
+    x, xb, wl = synthetic.make_inputs(w)
+    wp, a = hbl.quantize_weights(dev(wl))
+    xds = [x_to_dev(x, xb), -x_to_dev(x, xb)]
+    y_refs = []
+    for xd in xds:
+        codes, d = hbl.quantize_act(xd, bits)
+        y_refs.append(hbl.matmul_dequant(codes, bits, d, wp, a, K, out_dtype=torch.bfloat16))
+    assert not torch.equal(y_refs[0], y_refs[1])
+    op = hbl.OP_FORWARD_INT8 if bits == 8 else hbl.OP_FORWARD_INT4
+    ws = torch.full((hbl.workspace_bytes(op, M, K, N),), 0xFF, dtype=torch.uint8, device="cuda")
+    for i in range(6):
+        y = hbl.forward(xds[i % 2], wp, a, bits, out_dtype=torch.bfloat16, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_refs[i % 2].view(torch.int16)), i
+
+
 def test_fp6_matmul_repeatable_with_fresh_buffers():
     """Regression: the fp6 x fp4 matmul once issued two extra copies per even
     stage into the LDS buffer being read, which corrupted outputs only when

@@ -871,12 +871,14 @@ static void launch_decode_p(const GemmArgs& a, int S) {
 template <int BITS, int UPT, int OUT>
 static void launch_decode_few_u(const GemmArgs& a) {
   const size_t lds = (size_t)a.M * a.K + 64;
-  static bool attr = false;   // same value from every thread; set before the first launch
-  if (!attr) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode_few_kernel<BITS, 8, UPT, OUT>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    attr = true;
-  }
+  // more than 64 KiB of dynamic LDS needs the function's limit raised, once
+  // per device (a failure shows as the launch's error)
+  static bool attr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr[dev] &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode_few_kernel<BITS, 8, UPT, OUT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) == hipSuccess)
+    attr[dev] = true;
   hipLaunchKernelGGL((gemm_decode_few_kernel<BITS, 8, UPT, OUT>), dim3((a.N + 15) / 16), dim3(512), lds,
                      a.stream, a.codes, a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K);
 }

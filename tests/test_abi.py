@@ -50,6 +50,11 @@ def test_workspace_sizes(L):
     assert ws4 < ws8
     assert L.hbl_workspace_bytes(0, 0, 16384, 4096) >= 4096 * 8
     assert L.hbl_workspace_bytes(1, 64, 16384, 4096) > 0      # split-K scratch of the small-M path
+    # 17..64 tokens: int32 partials [S][M][N] (256-aligned), then one arrival
+    # counter per 64-channel tile (256-aligned); S = 4, halved while K / S < 256
+    assert L.hbl_workspace_bytes(1, 64, 16384, 4096) == 4 * 64 * 4096 * 4 + 256
+    assert L.hbl_workspace_bytes(1, 40, 512, 96) == 2 * 40 * 96 * 4 + 256
+    assert L.hbl_workspace_bytes(1, 16, 16384, 4096) == 0      # up to 16 tokens: no split
     assert L.hbl_workspace_bytes(1, 1, 16384, 4096) == 0      # one token: no split
     assert L.hbl_workspace_bytes(1, 8192, 16384, 4096) == 0
     assert L.hbl_workspace_bytes(3, 1, 256, 16) == 0

@@ -355,7 +355,8 @@ def test_single_launch_decode(bits, M, K, N, xdt, gain):
 
 
 @pytest.mark.parametrize("bits", [8, 4])
-@pytest.mark.parametrize("M,K,N", [(17, 4096, 272), (33, 16384, 4096), (64, 16384, 4096), (64, 1024, 48)])
+@pytest.mark.parametrize("M,K,N", [(17, 4096, 272), (33, 16384, 4096), (64, 16384, 4096), (64, 1024, 48),
+                                   (40, 512, 96)])
 def test_split_k_decode_reduction_in_kernel(bits, M, K, N):
     """17..64 tokens: the forward's matmul splits K and the last workgroup of
     each channel tile sums the partials; the stage calls sum them in a

@@ -2,8 +2,9 @@
 """Benchmark of the H-BitLinear forward (BitNet v2) on one MI355X.
 
 A step is one pass of the whole layer over one batch: the fused RMSNorm +
-Hadamard + quantisation kernel, then the ternary int8-MFMA matmul with its
-dequant epilogue (the two kernels hbl_forward_int{8,4} launches).  Inputs are
+Hadamard + quantisation kernel, then the ternary matmul with its dequant
+epilogue (fp6 x fp4 matrix instruction for INT4 activations at prefill sizes,
+int8 MFMA otherwise): the two kernels hbl_forward_int{8,4} launches.  Inputs are
 seeded synthetic data already resident in device memory when timing starts.
 Default workload: 7B-shaped FFN down projection, M=8192 tokens, K=16384,
 N=4096, INT4 activations, bf16 in/out.

@@ -382,6 +382,40 @@ def test_split_k_decode_reduction_in_kernel(bits, M, K, N):
         assert torch.equal(y.view(torch.int16), y_refs[i % 2].view(torch.int16)), i
 
 
+@pytest.mark.parametrize("M", [1, 40, 64])
+def test_forward_graph_replays(M):
+    """The forward captured once in a HIP graph and replayed with new inputs
+    written into the captured buffers between replays (eager work and a
+    synchronisation in between): every replay equals the eager forward on the
+    same input.  Covers the one-kernel decode (M = 1) and the split-K decode
+    whose arrival counters the prep kernel clears inside the graph."""
+    K, N, bits = 16384, 4096, 4
+    w = synthetic.Workload("t", M, K, N, bits, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, 13 * M + 5)
+    x, xb, wl = synthetic.make_inputs(w)
+    wp, a = hbl.quantize_weights(dev(wl))
+    inputs = [x_to_dev(x, xb), -x_to_dev(x, xb), x_to_dev(x, xb) * 0.5]
+    refs = [hbl.forward(xi, wp, a, bits) for xi in inputs]
+    torch.cuda.synchronize()
+    xbuf = inputs[0].clone()
+    ybuf = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(hbl.workspace_bytes(hbl.OP_FORWARD_INT4, M, K, N) + 16, dtype=torch.uint8, device="cuda")
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        hbl.forward(xbuf, wp, a, bits, workspace=ws, out=ybuf)   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s_)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hbl.forward(xbuf, wp, a, bits, workspace=ws, out=ybuf)
+    for i in range(6):
+        xbuf.copy_(inputs[i % 3])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ybuf.view(torch.int16), refs[i % 3].view(torch.int16)), i
+
+
 def test_fp6_matmul_repeatable_with_fresh_buffers():
     """Regression: the fp6 x fp4 matmul once issued two extra copies per even
     stage into the LDS buffer being read, which corrupted outputs only when

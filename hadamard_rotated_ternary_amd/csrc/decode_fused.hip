@@ -6,19 +6,23 @@
 // normalisation, the online Hadamard transform, activation quantisation, the
 // ternary matmul and dequantisation; 新智元 article "微软再放LLM量化大招",
 // section H-BitLinear模块, for the transform applied to the activations ahead
-// of the quantiser.  With one to four tokens the matmul streams the packed
-// weights once (16 MiB at the 7B down-projection shape) and the activation
-// side is tiny; run as two kernels, the quantiser's latency chain adds a
-// second launch and ~5 us in front of the weight stream.
+// of the quantiser.  For a single token the matmul streams the packed weights
+// once (16 MiB at the 7B down-projection shape) and the activation side is
+// tiny; run as two kernels, the quantiser's latency chain adds a second
+// launch and ~3 us in front of the weight stream.
 //
 // Here every workgroup owns 16 output channels (N/16 workgroups, one per CU
 // at N = 4096).  It first requests its whole slice of the weight stream
 // (16 bytes per lane per 256-k block, straight into registers), then computes
-// the quantised activations of all M tokens itself -- the same transform as
+// the quantised activations of the M tokens itself -- the same transform as
 // the prep kernel, T = 512 threads per token -- while the weights are in
-// flight, and keeps them in LDS in int8 operand form.  Redundant across
-// workgroups (each reads the M tokens from L2), but it hides under the
-// weight stream.  The matmul part is the few-token decode kernel's:
+// flight, and keeps them in LDS in int8 operand form.  That transform runs on
+// every CU and is VALU- and LDS-bound (~4.5 us per token at K = 16384), so
+// the kernel's time grows with M: at K = 16384 it takes 8.4 / 12.6 / 17.2 /
+// 21.6 us for 1-4 tokens where prep + matmul take 11.4 / 11.7 / 12.1 /
+// 12.6 us (at K = 8192: 5.0 / 7.2 / 10.2 us against 8.3 / 8.8 / 8.9 us).
+// The forward uses it while M * K <= 16384 (without the transform, for up
+// to four tokens).  The matmul part is the few-token decode kernel's:
 // v_mfma_i32_16x16x64_i8 with channels on the instruction's M side and the
 // tokens on its N side, integer partials of the 8 waves combined with LDS
 // atomics, then the dequant epilogue.
@@ -226,10 +230,13 @@ static hipError_t launch_fd_k(const FusedDecodeArgs& a) {
 #undef HBL_FD
 }
 
-bool decode_fused_supported(int M, int logk) { return M >= 1 && M <= FD_MAXM && (logk == 13 || logk == 14); }
+bool decode_fused_supported(int M, int logk, bool rotate) {
+  // without the transform the per-token work on each CU is small: up to FD_MAXM tokens
+  return M >= 1 && M <= FD_MAXM && (logk == 13 || logk == 14) && (!rotate || ((int64_t)M << logk) <= 16384);
+}
 
 hipError_t launch_decode_fused(const FusedDecodeArgs& a) {
-  if (!decode_fused_supported(a.M, a.logk)) return hipErrorInvalidValue;
+  if (!decode_fused_supported(a.M, a.logk, a.rotate)) return hipErrorInvalidValue;
   // T = 512 threads per token: E = K / 512 values per thread
   if (a.logk == 14) return a.rotate ? launch_fd_k<14, 5, 8, true>(a) : launch_fd_k<14, 5, 8, false>(a);
   return a.rotate ? launch_fd_k<13, 4, 6, true>(a) : launch_fd_k<13, 4, 6, false>(a);

@@ -102,7 +102,7 @@ hbl_status forward(int bits, bool rotate, const void* x, hbl_dtype x_dtype, cons
   int cus = 0;
   if (hbl_status s = check_device(&cus)) return s;
 
-  if (hbl::decode_fused_supported((int)M, log2_exact(K))) {
+  if (hbl::decode_fused_supported((int)M, log2_exact(K), rotate)) {
     hbl::FusedDecodeArgs f{};
     f.x = x; f.x_bf16 = x_dtype == HBL_BF16; f.gain = gain; f.wpack = w_packed; f.walpha = w_alpha; f.out = y;
     f.out_kind = y_dtype == HBL_BF16 ? hbl::OUT_BF16 : hbl::OUT_F32;

@@ -68,7 +68,7 @@ struct FusedDecodeArgs {
   bool rotate;            // false: BitLinear without the transform
   hipStream_t stream;
 };
-bool decode_fused_supported(int M, int logk);
+bool decode_fused_supported(int M, int logk, bool rotate);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a);
 
 struct WquantArgs {

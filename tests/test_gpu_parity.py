@@ -336,13 +336,16 @@ def test_rotated_weights_layer(bits):
 # ------------------------------------------------------------------ invariants of the GPU path
 
 @pytest.mark.parametrize("bits", [8, 4])
-@pytest.mark.parametrize("M,K,N,xdt,gain", [(1, 16384, 4096, "bf16", False), (2, 16384, 272, "bf16", True),
+@pytest.mark.parametrize("M,K,N,xdt,gain", [(1, 16384, 4096, "bf16", False), (1, 16384, 48, "f32", True),
+                                            (1, 8192, 48, "bf16", True), (2, 8192, 4096, "f32", True),
+                                            (2, 8192, 272, "bf16", False), (2, 16384, 272, "bf16", True),
                                             (3, 8192, 4096, "f32", False), (4, 16384, 16, "f32", True),
-                                            (4, 8192, 528, "bf16", False), (1, 8192, 48, "bf16", True)])
+                                            (4, 8192, 528, "bf16", False)])
 def test_single_launch_decode(bits, M, K, N, xdt, gain):
-    """1..4 tokens at K = 8192 / 16384 run as one kernel (transform, quantiser
-    and matmul together).  Against the oracle at the layer bar, and against the
-    two-kernel stage path on the same inputs (the transform's summation order
+    """A few tokens at K = 8192 / 16384: while M * K <= 16384 the forward is
+    one kernel (transform, quantiser and matmul together), beyond that prep +
+    matmul.  Against the oracle at the layer bar, and against the two-kernel
+    stage path on the same inputs (the one-kernel transform's summation order
     differs, so codes may differ at rounding ties only)."""
     w = synthetic.Workload("t", M, K, N, bits, xdt, "laplace", 0.05, max(1, K // 200), 100.0, 5 * M + K + N)
     g = synthetic.make_gain(K, M) if gain else None

@@ -21,11 +21,11 @@
 // the kernel's time grows with M: at K = 16384 it takes 8.4 / 12.6 / 17.2 /
 // 21.6 us for 1-4 tokens where prep + matmul take 11.4 / 11.7 / 12.1 /
 // 12.6 us (at K = 8192: 5.0 / 7.2 / 10.2 us against 8.3 / 8.8 / 8.9 us).
-// The forward uses it while M * K <= 16384 (without the transform, for up
-// to four tokens).  The matmul part is the few-token decode kernel's:
-// v_mfma_i32_16x16x64_i8 with channels on the instruction's M side and the
-// tokens on its N side, integer partials of the 8 waves combined with LDS
-// atomics, then the dequant epilogue.
+// The forward uses it while M * K <= 16384 (49152 without the transform).
+// The matmul part is the few-token decode kernel's: v_mfma_i32_16x16x64_i8
+// with channels on the instruction's M side and the tokens on its N side,
+// integer partials of the 8 waves combined with LDS atomics, then the
+// dequant epilogue.
 #include "fwht.h"
 #include "mma.h"
 
@@ -231,8 +231,11 @@ static hipError_t launch_fd_k(const FusedDecodeArgs& a) {
 }
 
 bool decode_fused_supported(int M, int logk, bool rotate) {
-  // without the transform the per-token work on each CU is small: up to FD_MAXM tokens
-  return M >= 1 && M <= FD_MAXM && (logk == 13 || logk == 14) && (!rotate || ((int64_t)M << logk) <= 16384);
+  // without the transform the per-token work on each CU is smaller: one
+  // kernel wins while M * K <= 49152 (at K = 16384, 6.5 / 8.0 / 10.0 / 11.7 us
+  // for 1-4 tokens against 9.6 / 9.8 / 10.2 / 10.7 us for prep + matmul)
+  return M >= 1 && M <= FD_MAXM && (logk == 13 || logk == 14) &&
+         ((int64_t)M << logk) <= (rotate ? 16384 : 49152);
 }
 
 hipError_t launch_decode_fused(const FusedDecodeArgs& a) {

@@ -277,11 +277,12 @@ def test_unrotated_codes_match_oracle(K, bits, M):
 
 
 @pytest.mark.parametrize("bits", [8, 4])
-@pytest.mark.parametrize("M,K,N", [(1, 16384, 4096), (3, 8192, 272), (16, 4096, 512), (64, 2048, 256),
-                                   (300, 4096, 528), (2048, 4096, 4096)])
+@pytest.mark.parametrize("M,K,N", [(1, 16384, 4096), (3, 8192, 272), (4, 8192, 48), (3, 16384, 272),
+                                   (4, 16384, 96), (16, 4096, 512), (64, 2048, 256), (300, 4096, 528),
+                                   (2048, 4096, 4096)])
 def test_unrotated_layer(bits, M, K, N):
-    """BitLinear without the transform (one-launch decode, decode, int8 and fp6
-    prefill matmuls) against the oracle at the layer bar."""
+    """BitLinear without the transform (one-launch decode while M * K <= 49152,
+    decode, int8 and fp6 prefill matmuls) against the oracle at the layer bar."""
     w = gaussian_workload(M, K, N, bits, M + K + N)
     x, xb, wl = synthetic.make_inputs(w)
     wt, alpha = oracle.quantize_weights(wl)

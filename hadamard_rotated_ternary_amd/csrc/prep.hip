@@ -204,35 +204,32 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
       __syncthreads();
       if (valid) {
         if constexpr (MODE == 2) {
-          // 64 codes (two 32-k groups) per step -> 48 bytes.  Byte pairs
+          // 32 codes (one 32-k group) per step -> 24 bytes.  Byte pairs
           // become f16 pairs 1024 + n (byte permute next to the constant
           // 0x64), then q/2 = 0.5 * (1024 + n) - 516 exactly, then one packed
           // conversion turns 32 halves into 32 fp6 fields (exact: every q/2
           // in [-4, 3.5] is an e2m3 value).
           uint8_t* out = codes + (size_t)m * 96;
           const size_t kb_stride = (size_t)M * 96;
-          for (int cp = tau; cp < K / 64; cp += T) {
-            uint32_t o[12];
+          // one 32-k group (24 output bytes) per thread and step: K/32 groups
+          // keep every thread of the token busy (K/64 pairs left half idle)
+          for (int u = tau; u < K / 32; u += T) {
+            const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(32 * u));
+            h32 hv;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(64 * cp + 32 * c));
-              h32 hv;
-#pragma unroll
-              for (int e = 0; e < 16; ++e) {
-                const uint32_t pr = __builtin_amdgcn_perm(0x64646464u, s4[e >> 1], (e & 1) ? 0x04030402u : 0x04010400u);
-                const h2 x = __builtin_elementwise_fma(__builtin_bit_cast(h2, pr), h2{(_Float16)0.5f, (_Float16)0.5f},
-                                                       h2{(_Float16)-516.0f, (_Float16)-516.0f});
-                hv[2 * e] = x[0];
-                hv[2 * e + 1] = x[1];
-              }
-              const u6 f = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(hv, 1.0f);
-#pragma unroll
-              for (int i = 0; i < 6; ++i) o[6 * c + i] = f[i];
+            for (int e = 0; e < 16; ++e) {
+              const uint32_t pr = __builtin_amdgcn_perm(0x64646464u, s4[e >> 1], (e & 1) ? 0x04030402u : 0x04010400u);
+              const h2 x = __builtin_elementwise_fma(__builtin_bit_cast(h2, pr), h2{(_Float16)0.5f, (_Float16)0.5f},
+                                                     h2{(_Float16)-516.0f, (_Float16)-516.0f});
+              hv[2 * e] = x[0];
+              hv[2 * e + 1] = x[1];
             }
-            uint4* dst = reinterpret_cast<uint4*>(out + (size_t)(cp >> 1) * kb_stride + 48 * (cp & 1));
-            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-            dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
+            const u6 f = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(hv, 1.0f);
+            // group u: block u/4 of 128 k, 24 bytes at 24 (u % 4) of the token's 96
+            uint2* dst = reinterpret_cast<uint2*>(out + (size_t)(u >> 2) * kb_stride + 24 * (u & 3));
+            dst[0] = make_uint2(f[0], f[1]);
+            dst[1] = make_uint2(f[2], f[3]);
+            dst[2] = make_uint2(f[4], f[5]);
           }
         } else if constexpr (BITS == 8) {
           // int8 codes: thread tau stores 16-byte chunks j*T + tau

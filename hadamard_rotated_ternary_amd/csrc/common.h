@@ -46,6 +46,10 @@ HBL_DEV uint16_t f32_to_bf16(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+// The same rounding (nearest, ties to even) by the hardware conversion
+// (v_cvt_pk_bf16_f32): one instruction instead of four; equal to the above
+// for every finite input.
+HBL_DEV uint16_t f32_to_bf16_hw(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <int W>
 HBL_DEV float xor_sum(float v) {

@@ -96,7 +96,7 @@ HBL_DEV void store_bf16_staged(uint8_t* stage, uint16_t* Y, const float* __restr
         const float t = dscale[min(mrow0 + 64 * hf + rl, M - 1)] * aw;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
-          *reinterpret_cast<uint16_t*>(stage + rl * ER + (cb * 32 + l32) * 2) = f32_to_bf16(getv(rb, cb, r) * t);
+          *reinterpret_cast<uint16_t*>(stage + rl * ER + (cb * 32 + l32) * 2) = f32_to_bf16_hw(getv(rb, cb, r) * t);
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");

@@ -4,8 +4,10 @@
 // "微软再放LLM量化大招", section H-BitLinear模块: weights are mapped to
 // {-1, 0, 1} with a single per-tensor scale, the mean of |W|.
 //
-// The sum of |W| is taken in fp64 in a fixed order (each row left to right,
-// then the row sums in row order) so alpha is reproducible to the last bit.
+// The sum of |W| is taken in fp64 in a fixed order (64-column blocks of each
+// row, the block sums in order, then the row sums in row order), so alpha is
+// reproducible from call to call; any fp64 order is far more precise than the
+// fp32 result, which stays within one ulp of the exactly rounded mean.
 // Code(w) = round-half-even(w / a) clamped to [-1, 1] is nonzero exactly when
 // |w| > a / 2 (a tie rounds to 0), and 0.5f * a is exact in fp32, so the
 // kernel decides with one comparison instead of a division.

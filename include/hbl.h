@@ -112,8 +112,10 @@ size_t hbl_workspace_bytes(int op, int64_t M, int64_t K, int64_t N);
  *   w         fp32 [N][K] latent weights (device, read only)
  *   w_packed  uint8 [N][K/4] packed ternary codes (device, written)
  *   w_alpha   fp32 [1] alpha = mean|W| (device, written).  The sum of |W| is
- *             taken in fp64, each row in order and then the rows in order,
- *             so alpha is reproducible to the last bit.
+ *             taken in fp64 in a fixed order (64-column blocks of each row
+ *             left to right, the block sums in order, then the row sums in
+ *             row order), so alpha is reproducible from call to call and
+ *             within one fp32 ulp of the exactly rounded mean.
  *   workspace at least hbl_workspace_bytes(HBL_OP_QUANTIZE_WEIGHTS, 0, K, N) bytes.
  */
 hbl_status hbl_quantize_weights(const float *w, int64_t N, int64_t K,

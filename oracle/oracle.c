@@ -63,35 +63,26 @@ static double clampd(double v, double lo, double hi) {
 /* ---------------------------------------------------------------------------
  * Weights: per-tensor absmean ternarisation to {-1, 0, 1}.
  * [QbitAI §引入H-BitLinear模块], [XZY §H-BitLinear模块], [AINEWS].
- *   S      = sum of |w| in double, in a fixed order: each row in blocks of
- *            64 consecutive columns (the last one may be shorter), each block
- *            summed left to right, the block sums added left to right, then
- *            the row sums added in row order;
+ *   S      = sum of |w| over the whole tensor in double: each row summed
+ *            left to right, then the row sums added in row order (a plain
+ *            ordered sum; its rounding error is far below fp32's);
  *   alpha  = (float)(S / (N*K))       -- the stored per-tensor scale (fp32);
  *   a      = max(alpha, EPS_Q);
  *   w_t    = clamp(round(w / a), -1, 1)  (w / a in double).
  * Returns 0, or -1 on bad arguments.
  * ------------------------------------------------------------------------- */
-/* Sum of |v| over one row in the order above. */
+/* Sum of |v| over one row, left to right. */
 static double row_abs_sum_f(const float *v, int64_t K)
 {
     double row = 0.0;
-    for (int64_t b0 = 0; b0 < K; b0 += 64) {
-        double blk = 0.0;
-        for (int64_t k = b0; k < K && k < b0 + 64; ++k) blk += fabs((double)v[k]);
-        row += blk;
-    }
+    for (int64_t k = 0; k < K; ++k) row += fabs((double)v[k]);
     return row;
 }
 
 static double row_abs_sum_d(const double *v, int64_t K)
 {
     double row = 0.0;
-    for (int64_t b0 = 0; b0 < K; b0 += 64) {
-        double blk = 0.0;
-        for (int64_t k = b0; k < K && k < b0 + 64; ++k) blk += fabs(v[k]);
-        row += blk;
-    }
+    for (int64_t k = 0; k < K; ++k) row += fabs(v[k]);
     return row;
 }
 
@@ -309,7 +300,7 @@ int oracle_forward(const float *x, const float *g, const int8_t *wt, float alpha
  * in exact arithmetic (H symmetric, H H = K I); the rotated rows are then
  * ternarised as usual:
  *   wr[n] = H_K w[n] / sqrt(K)   (double),
- *   S = sum |wr| (rows in order, then the row sums in order, double),
+ *   S = sum |wr| (each row left to right, then the row sums in row order, double),
  *   alpha = (float)(S / (N K)),  a = max(alpha, EPS_Q),
  *   w_t = clamp(round(wr / a), -1, 1).
  * wr (optional) receives the rotated rows.

@@ -189,6 +189,35 @@ def test_ternary_statistics_gaussian():
     np.testing.assert_array_equal(wt[wt != 0], np.sign(w[wt != 0]))
 
 
+def fp32_ulp(v):
+    v = np.float32(v)
+    return float(np.spacing(np.abs(v)))
+
+
+def test_ternary_scale_is_the_mean_abs():
+    """alpha is the per-tensor mean of |W| rounded to fp32, whatever the
+    summation order: (a) weights on a coarse binary grid, whose sum is exact
+    in fp64 in any order, give exactly fp32(sum / NK), the sum taken as an
+    exact rational; (b) Gaussian weights give fp32 of the correctly rounded
+    mean (math.fsum) to within one fp32 ulp (the fp64 sum's own rounding is
+    ~1e-12 relative; only a near-midpoint can move the fp32 rounding)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    N, K = 96, 1024
+    w = (rng.integers(-4096, 4097, (N, K)) / 4096.0 * 0.05).astype(np.float32)
+    _, alpha = oracle.quantize_weights(w)
+    exact = sum(Fraction(float(abs(v))) for v in w.ravel()) / (N * K)
+    assert alpha == np.float32(float(exact))
+    w = rng.normal(0, 0.02, (512, 4096)).astype(np.float32)
+    _, alpha = oracle.quantize_weights(w)
+    mean = math.fsum(np.abs(w.astype(np.float64)).ravel()) / w.size
+    assert abs(float(alpha) - mean) <= fp32_ulp(mean)
+    # reversing the tensor changes the order of the oracle's sum, not alpha
+    # beyond one ulp
+    _, alpha_r = oracle.quantize_weights(np.ascontiguousarray(w[::-1, ::-1]))
+    assert abs(float(alpha_r) - float(alpha)) <= fp32_ulp(mean)
+
+
 def test_ternary_constant_and_zero():
     wt, alpha = oracle.quantize_weights(np.full((4, 8), -0.3, np.float32))
     assert alpha == np.float32(0.3) or abs(alpha - 0.3) < 1e-7

@@ -21,7 +21,8 @@ HBL_F32, HBL_BF16 = 0, 1
 OP_QUANTIZE_WEIGHTS, OP_MATMUL, OP_QUANTIZE_WEIGHTS_ROTATED, OP_FORWARD_INT4, OP_FORWARD_INT8 = 0, 1, 2, 4, 8
 OP_BACKWARD = 16
 STATUS = {0: "HBL_OK", 1: "HBL_ERR_NULL", 2: "HBL_ERR_SHAPE", 3: "HBL_ERR_DTYPE", 4: "HBL_ERR_ALIGN",
-          5: "HBL_ERR_WORKSPACE", 6: "HBL_ERR_LAUNCH", 7: "HBL_ERR_DEVICE"}
+          5: "HBL_ERR_WORKSPACE", 6: "HBL_ERR_LAUNCH", 7: "HBL_ERR_DEVICE", 8: "HBL_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20   # HBL_NOALLOC_SCRATCH_BYTES
 
 
 class HBLError(RuntimeError):
@@ -38,6 +39,7 @@ SIGNATURES = {
     "hbl_quantize_weights": ([P, I64, I64, P, P, P, SZ, P], I),
     "hbl_forward_int8": ([P, I, P, P, P, I64, I64, I64, P, I, P, SZ, P], I),
     "hbl_forward_int4": ([P, I, P, P, P, I64, I64, I64, P, I, P, SZ, P], I),
+    "hbl_forward_noalloc": ([I, P, I, P, P, P, I64, I64, I64, P, I, P], I),
     "hbl_quantize_act": ([P, I, P, I64, I64, I, P, P, P], I),
     "hbl_matmul_dequant": ([P, I, P, P, P, I64, I64, I64, P, I, P, SZ, P], I),
     "hbl_rmsnorm_fwht": ([P, I, P, I64, I64, P, P], I),
@@ -154,6 +156,21 @@ def forward(x: torch.Tensor, w_packed: torch.Tensor, w_alpha: torch.Tensor, bits
     else:
         _call("hbl_bitlinear_forward", _ptr(x), _dtype_code(x.dtype), _ptr(gain), _ptr(w_packed), _ptr(w_alpha),
               M, K, N, bits, _ptr(y), _dtype_code(out_dtype), _ptr(ws), ws.numel(), _stream())
+    return y
+
+
+def forward_noalloc(x: torch.Tensor, w_packed: torch.Tensor, w_alpha: torch.Tensor, bits: int,
+                    gain: torch.Tensor | None = None, out_dtype=None, out=None) -> torch.Tensor:
+    """The H-BitLinear forward with the library's static scratch instead of a
+    workspace (no device allocation inside the call; `out` may be given so
+    that the call allocates nothing at all)."""
+    _dev(x, "x")
+    M, K = x.shape
+    N = w_packed.shape[0]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    y = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
+    _call("hbl_forward_noalloc", bits, _ptr(x), _dtype_code(x.dtype), _ptr(gain), _ptr(w_packed), _ptr(w_alpha),
+          M, K, N, _ptr(y), _dtype_code(y.dtype), _stream())
     return y
 
 

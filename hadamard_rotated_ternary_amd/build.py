@@ -8,7 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhbl.so")
-SOURCES = ["hbl_api.cpp", "prep.hip", "wquant.hip", "gemm.hip", "decode_fused.hip", "attn.hip", "bwd.hip"]
+SOURCES = ["hbl_api.cpp", "prep.hip", "wquant.hip", "gemm.hip", "decode_fused.hip", "attn.hip", "bwd.hip",
+           "noalloc.hip"]
 HEADERS = ["common.h", "launch.h", "mma.h", "fwht.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

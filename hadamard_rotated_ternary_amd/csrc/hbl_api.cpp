@@ -86,17 +86,31 @@ BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N) {
   return L;
 }
 
+}  // namespace
+
+// Every check of the forward's arguments except the workspace's (host only).
+hbl_status hbl::forward_check(int bits, const void* x, hbl_dtype x_dtype, const float* gain,
+                              const uint8_t* w_packed, const float* w_alpha, int64_t M, int64_t K, int64_t N,
+                              const void* y, hbl_dtype y_dtype) {
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype) || (bits != 8 && bits != 4)) return HBL_ERR_DTYPE;
+  if (hbl_status s = check_shape(M, K, N)) return s;
+  if (M == 0) return HBL_OK;
+  if (!x || !w_packed || !w_alpha || !y) return HBL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_packed) || !aligned16(w_alpha) || !aligned16(y) || (gain && !aligned16(gain)))
+    return HBL_ERR_ALIGN;
+  return HBL_OK;
+}
+
+namespace {
+
 // H-BitLinear forward (rotate) or BitLinear without the transform.
 hbl_status forward(int bits, bool rotate, const void* x, hbl_dtype x_dtype, const float* gain,
                    const uint8_t* w_packed, const float* w_alpha, int64_t M, int64_t K, int64_t N, void* y,
                    hbl_dtype y_dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype) || (bits != 8 && bits != 4)) return HBL_ERR_DTYPE;
-  if (hbl_status s = check_shape(M, K, N)) return s;
+  if (hbl_status s = hbl::forward_check(bits, x, x_dtype, gain, w_packed, w_alpha, M, K, N, y, y_dtype)) return s;
   if (M == 0) return HBL_OK;
-  if (!x || !w_packed || !w_alpha || !y || !workspace) return HBL_ERR_NULL;
-  if (!aligned16(x) || !aligned16(w_packed) || !aligned16(w_alpha) || !aligned16(y) || !aligned16(workspace) ||
-      (gain && !aligned16(gain)))
-    return HBL_ERR_ALIGN;
+  if (!workspace) return HBL_ERR_NULL;
+  if (!aligned16(workspace)) return HBL_ERR_ALIGN;
   if (ws_bytes < hbl_workspace_bytes(bits == 8 ? HBL_OP_FORWARD_INT8 : HBL_OP_FORWARD_INT4, M, K, N))
     return HBL_ERR_WORKSPACE;
   int cus = 0;
@@ -148,6 +162,7 @@ const char* hbl_status_string(hbl_status s) {
     case HBL_ERR_WORKSPACE: return "workspace too small";
     case HBL_ERR_LAUNCH: return "kernel launch failed";
     case HBL_ERR_DEVICE: return "no gfx950 device";
+    case HBL_ERR_SCRATCH: return "problem needs more scratch than the no-alloc forward's static array";
   }
   return "unknown status";
 }

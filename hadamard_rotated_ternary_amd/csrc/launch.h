@@ -3,7 +3,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/hbl.h"
+
 namespace hbl {
+
+// Every check of the forward's arguments except the workspace's (host only,
+// touches no device): HBL_OK or the first error.
+hbl_status forward_check(int bits, const void* x, hbl_dtype x_dtype, const float* gain, const uint8_t* w_packed,
+                         const float* w_alpha, int64_t M, int64_t K, int64_t N, const void* y, hbl_dtype y_dtype);
 
 struct PrepArgs {
   const void* x;

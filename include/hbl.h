@@ -86,7 +86,9 @@ typedef enum {
     HBL_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned */
     HBL_ERR_WORKSPACE = 5,  /* workspace smaller than hbl_workspace_bytes() */
     HBL_ERR_LAUNCH = 6,     /* the HIP runtime reported an error at launch */
-    HBL_ERR_DEVICE = 7      /* no current device, or it is not gfx950 */
+    HBL_ERR_DEVICE = 7,     /* no current device, or it is not gfx950 */
+    HBL_ERR_SCRATCH = 8     /* hbl_forward_noalloc: the problem needs more than
+                               HBL_NOALLOC_SCRATCH_BYTES of scratch */
 } hbl_status;
 
 typedef enum { HBL_F32 = 0, HBL_BF16 = 1 } hbl_dtype;
@@ -149,6 +151,27 @@ hbl_status hbl_forward_int4(const void *x, hbl_dtype x_dtype, const float *gain,
                             int64_t M, int64_t K, int64_t N,
                             void *y, hbl_dtype y_dtype,
                             void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels as hbl_forward_int8 (bits = 8) and hbl_forward_int4 (bits = 4),
+ * with the same arguments and results, but no workspace argument.  Its
+ * scratch (activation codes, scales, split-K partials and arrival counters)
+ * is a static device array of HBL_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends; the call itself allocates
+ * nothing.  A problem whose workspace (hbl_workspace_bytes(HBL_OP_FORWARD_INT8
+ * or _INT4, M, K, N)) exceeds that size returns HBL_ERR_SCRATCH before
+ * anything touches the device.  The array keeps the last call's contents; the
+ * kernels clear what must start at zero.  Every call on one GPU shares that
+ * GPU's array, so calls that may overlap on one GPU (different streams, or
+ * different host threads without ordering) race: serialise them.
+ */
+#define HBL_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+hbl_status hbl_forward_noalloc(int bits, const void *x, hbl_dtype x_dtype, const float *gain,
+                               const uint8_t *w_packed, const float *w_alpha,
+                               int64_t M, int64_t K, int64_t N,
+                               void *y, hbl_dtype y_dtype, hipStream_t stream);
 
 /* ---- variants beside H-BitLinear ---- */
 

@@ -38,7 +38,7 @@ def test_header_entry_points_are_exported(L):
 
 
 def test_status_strings(L):
-    for code in range(8):
+    for code in range(9):
         assert L.hbl_status_string(code)
     assert L.hbl_status_string(99) == b"unknown status"
 
@@ -85,6 +85,22 @@ def test_forward_validation(L, bits):
     assert fwd(L, bits, wsb=16) == WORKSPACE
     # empty input: valid, nothing launched
     assert fwd(L, bits, M=0) == OK
+
+
+def test_noalloc_forward_validation(L):
+    """hbl_forward_noalloc checks every argument, and that the problem fits
+    its static scratch, before anything touches the device (no GPU here)."""
+    SCRATCH = 8
+    f = L.hbl_forward_noalloc
+    assert f(8, A, 1, None, A, A, 8192, 16384, 4096, A2, 1, S) == SCRATCH      # needs > 32 MiB
+    assert f(4, A, 1, None, A, A, 8192, 16384, 4096, A2, 1, S) == SCRATCH
+    assert L.hbl_workspace_bytes(8, 8192, 16384, 4096) > hbl.NOALLOC_SCRATCH_BYTES
+    assert f(5, A, 1, None, A, A, 8, 256, 256, A2, 1, S) == DTYPE
+    assert f(8, A, 1, None, A, A, 8, 300, 256, A2, 1, S) == SHAPE
+    assert f(8, None, 1, None, A, A, 8, 256, 256, A2, 1, S) == NULL
+    assert f(4, BAD, 1, None, A, A, 8, 256, 256, A2, 1, S) == ALIGN
+    assert f(4, A, 1, None, A, A, 0, 256, 256, A2, 1, S) == OK                  # empty: nothing launched
+    assert L.hbl_status_string(SCRATCH).startswith(b"problem needs more scratch")
 
 
 def test_stage_validation(L):

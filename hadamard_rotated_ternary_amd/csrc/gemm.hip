@@ -605,36 +605,40 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[cp][mb] = v4i{};
 
-  // Blocks b = wave + NW*i, taken MAXB at a time.
-  for (int b0 = wave; b0 < nblk; b0 += NW * MAXB) {
-    uint4 wq[MAXB][CPW];
-    uint4 aq[MAXB][MB][BITS / 2];
-    // Loads are unconditional (out-of-range indices are clamped to valid
-    // addresses and the values discarded), so the compiler can release block i
-    // with a partial vmcnt wait instead of waiting for every load.
-#pragma unroll
-    for (int i = 0; i < MAXB; ++i) {
-      const int b = min(b0 + NW * i, nblk - 1);
-      const int kb = kbeg + b * DKB + 64 * g;                 // this lane's 64 codes of block b
-#pragma unroll
+  if constexpr (MB == 1) {
+    // Blocks b = wave + NW*i (i < MAXB: K / S <= NW * MAXB * 256), consumed in
+    // order, with only RING blocks per wave requested ahead: block i + RING is
+    // requested once block i has been consumed.  Requesting the whole weight
+    // stream at once made every request wait behind the full queue, so a
+    // wave's blocks all arrived at the end of the stream and the matrix work
+    // only started then; with a short ring the blocks arrive spread over the
+    // stream and the work overlaps it.  Loads are unconditional (out-of-range
+    // indices are clamped to valid addresses and the values discarded), so the
+    // compiler releases block i with a partial vmcnt wait.
+    constexpr int RING = MAXB < 4 ? MAXB : 4;
+    uint4 wq[RING][CPW];
+    uint4 aq[RING][MB][BITS / 2];
+    auto load = [&](int i, int slot) __attribute__((always_inline)) {
+      const int b = min(wave + NW * i, nblk - 1);
+      const int kb = kbeg + b * DKB + 64 * g;                   // this lane's 64 codes of block b
+  #pragma unroll
       for (int cp = 0; cp < CPW; ++cp) {
         const int n = min(ch0 + 16 * cp + c, N - 1);
-        wq[i][cp] = *reinterpret_cast<const uint4*>(W + wrow_base(n, K) + (size_t)((kbeg + b * DKB) >> 8) * 1024 + 16 * g);
+        wq[slot][cp] =
+            *reinterpret_cast<const uint4*>(W + wrow_base(n, K) + (size_t)((kbeg + b * DKB) >> 8) * 1024 + 16 * g);
       }
-#pragma unroll
+  #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int t = min(16 * mb + c, M - 1);
         const uint4* ap = reinterpret_cast<const uint4*>(A + (size_t)t * arow + (size_t)kb * BITS / 8);
-#pragma unroll
-        for (int d = 0; d < BITS / 2; ++d) aq[i][mb][d] = ap[d];
+  #pragma unroll
+        for (int d = 0; d < BITS / 2; ++d) aq[slot][mb][d] = ap[d];
       }
-    }
-#pragma unroll
-    for (int i = 0; i < MAXB; ++i) {
-      if (b0 + NW * i >= nblk) continue;   // wave-uniform; keeps the loop unrolled (registers, no scratch)
-#pragma unroll
+    };
+    auto compute = [&](int slot) __attribute__((always_inline)) {
+  #pragma unroll
       for (int j = 0; j < 4; ++j) {
-#pragma unroll
+  #pragma unroll
         for (int cp = 0; cp < CPW; ++cp) {
           // INT8: step j = weight word j against the 16 codes it covers (the
           // codes as loaded).  INT4 keeps the other pairing -- step j = field j
@@ -643,19 +647,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
           // 64-token decode runs 15.1 us instead of 17.1 us.
           v4i wop;
           if constexpr (BITS == 8) {
-            wop = wstep(u4get(wq[i][cp], j));
+            wop = wstep(u4get(wq[slot][cp], j));
           } else {
-            const uint4 p = wq[i][cp];
+            const uint4 p = wq[slot][cp];
             wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
           }
-#pragma unroll
+  #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             v4i aop;
             if constexpr (BITS == 8) {
-              aop = as_v4i(aq[i][mb][j]);
+              aop = as_v4i(aq[slot][mb][j]);
             } else {
               // codes 16d + 4j + i: nibble j%2 of word 2d + j/2
-              const uint4 q0 = aq[i][mb][0], q1 = aq[i][mb][1];
+              const uint4 q0 = aq[slot][mb][0], q1 = aq[slot][mb][1];
               const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
               aop = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
                         (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
@@ -663,6 +667,80 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
             // padding tokens (16*mb + c >= M) read token M-1's codes; their
             // sums are never stored
             acc[cp][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc[cp][mb], 0, 0, 0);
+          }
+        }
+      }
+    };
+  #pragma unroll
+    for (int i = 0; i < RING; ++i) load(i, i);
+  #pragma unroll
+    for (int i = 0; i < MAXB; ++i) {
+      if (wave + NW * i < nblk) compute(i % RING);      // wave-uniform
+      if (i + RING < MAXB) {
+        load(i + RING, i % RING);
+        __builtin_amdgcn_sched_barrier(0);              // keep the requests where they are issued
+      }
+    }
+  } else {
+    // Blocks b = wave + NW*i, taken MAXB at a time.
+    for (int b0 = wave; b0 < nblk; b0 += NW * MAXB) {
+      uint4 wq[MAXB][CPW];
+      uint4 aq[MAXB][MB][BITS / 2];
+      // Loads are unconditional (out-of-range indices are clamped to valid
+      // addresses and the values discarded), so the compiler can release block i
+      // with a partial vmcnt wait instead of waiting for every load.
+  #pragma unroll
+      for (int i = 0; i < MAXB; ++i) {
+        const int b = min(b0 + NW * i, nblk - 1);
+        const int kb = kbeg + b * DKB + 64 * g;                 // this lane's 64 codes of block b
+  #pragma unroll
+        for (int cp = 0; cp < CPW; ++cp) {
+          const int n = min(ch0 + 16 * cp + c, N - 1);
+          wq[i][cp] = *reinterpret_cast<const uint4*>(W + wrow_base(n, K) + (size_t)((kbeg + b * DKB) >> 8) * 1024 + 16 * g);
+        }
+  #pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int t = min(16 * mb + c, M - 1);
+          const uint4* ap = reinterpret_cast<const uint4*>(A + (size_t)t * arow + (size_t)kb * BITS / 8);
+  #pragma unroll
+          for (int d = 0; d < BITS / 2; ++d) aq[i][mb][d] = ap[d];
+        }
+      }
+  #pragma unroll
+      for (int i = 0; i < MAXB; ++i) {
+        if (b0 + NW * i >= nblk) continue;   // wave-uniform; keeps the loop unrolled (registers, no scratch)
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+  #pragma unroll
+          for (int cp = 0; cp < CPW; ++cp) {
+            // INT8: step j = weight word j against the 16 codes it covers (the
+            // codes as loaded).  INT4 keeps the other pairing -- step j = field j
+            // of all four weight words against the matching nibbles of all four
+            // activation words (1 op per operand dword either way): with it the
+            // 64-token decode runs 15.1 us instead of 17.1 us.
+            v4i wop;
+            if constexpr (BITS == 8) {
+              wop = wstep(u4get(wq[i][cp], j));
+            } else {
+              const uint4 p = wq[i][cp];
+              wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
+            }
+  #pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              v4i aop;
+              if constexpr (BITS == 8) {
+                aop = as_v4i(aq[i][mb][j]);
+              } else {
+                // codes 16d + 4j + i: nibble j%2 of word 2d + j/2
+                const uint4 q0 = aq[i][mb][0], q1 = aq[i][mb][1];
+                const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                aop = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
+                          (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
+              }
+              // padding tokens (16*mb + c >= M) read token M-1's codes; their
+              // sums are never stored
+              acc[cp][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc[cp][mb], 0, 0, 0);
+            }
           }
         }
       }
@@ -756,14 +834,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_few_kernel(
   uint4 st[UPT];
 #pragma unroll
   for (int q = 0; q < UPT; ++q) st[q] = reinterpret_cast<const uint4*>(A)[min(q * 64 * NW + tid, units - 1)];
-  // ---- weight stream: blocks b = wave + NW*i (NW*MAXB*256 >= K for K <= 16384)
-  uint4 wq[MAXB];
+  // ---- weight stream: blocks b = wave + NW*i (NW*MAXB*256 >= K for K <= 16384),
+  // RING of them requested ahead (the decode kernel above explains why)
+  constexpr int RING = 4;
+  uint4 wq[RING];
   const int n = min(ch0 + c, N - 1);
-#pragma unroll
-  for (int i = 0; i < MAXB; ++i) {
+  auto load = [&](int i) __attribute__((always_inline)) {
     const int b = min(wave + NW * i, nblk - 1);
-    wq[i] = *reinterpret_cast<const uint4*>(W + wrow_base(n, K) + (size_t)b * 1024 + 16 * g);
-  }
+    wq[i % RING] = *reinterpret_cast<const uint4*>(W + wrow_base(n, K) + (size_t)b * 1024 + 16 * g);
+  };
+#pragma unroll
+  for (int i = 0; i < RING; ++i) load(i);
   // ---- operand form of the staged codes, token rows of K bytes
   const int opr = K;
   const int upr = (int)(arow / 16);                        // packed units per token row
@@ -796,15 +877,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_few_kernel(
 #pragma unroll
   for (int i = 0; i < MAXB; ++i) {
     const int b = wave + NW * i;
-    if (b >= nblk) continue;                               // wave-uniform
-    const uint4* ap = reinterpret_cast<const uint4*>(arow_lds + astep * b * DKB);
-    const uint4 p = wq[i];
+    if (b < nblk) {                                        // wave-uniform
+      const uint4* ap = reinterpret_cast<const uint4*>(arow_lds + astep * b * DKB);
+      const uint4 p = wq[i % RING];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i wop = wstep(u4get(p, j));
-      const v4i aop = as_v4i(ap[j]);                       // codes 16j .. 16j+15 of the lane's 64
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const v4i wop = wstep(u4get(p, j));
+        const v4i aop = as_v4i(ap[j]);                     // codes 16j .. 16j+15 of the lane's 64
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc, 0, 0, 0);
+      }
     }
+    if (i + RING < MAXB) load(i + RING);
+    __builtin_amdgcn_sched_barrier(0);                     // keep the requests where they are issued
   }
   __syncthreads();
 #pragma unroll

@@ -544,13 +544,18 @@ constexpr int DKB = 256;
 
 struct DecodePlan { int cpw, S, mb, nw; };
 constexpr int kDecodeMaxSplit = 4;   // split-K ways the in-kernel reduction handles
-static DecodePlan decode_plan(int M, int K) {
-#ifdef HBL_DECODE_PLAN
-  DecodePlan p = HBL_DECODE_PLAN(M);
-#else
-  DecodePlan p = M <= 16 ? DecodePlan{1, 1, 1, 8} : DecodePlan{4, 4, 4, 8};
-#endif
+// Up to 32 tokens: 16 channels per workgroup over the whole K, one or two
+// token groups.  33..64: 64 channels per workgroup and K split four ways, so
+// each INT4 activation operand expanded in registers feeds four channel
+// groups (with one group per workgroup the expansion was repeated for every
+// 16 channels: 64 tokens took 18.0 us unsplit against 13.5 us split), at the
+// price of the cross-workgroup reduction.  Measured at K = 16384, N = 4096:
+// 17 / 32 tokens 8.2 / 10.8 us unsplit against ~12.5 us split.
+static DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
+  DecodePlan p = M <= 16 ? DecodePlan{1, 1, 1, 8} : M <= 32 ? DecodePlan{1, 1, 2, 8} : DecodePlan{4, 4, 4, 8};
   while (p.S > 1 && K / p.S < DKB) p.S /= 2;
+  // split-K partials are addressed with 32-bit byte offsets
+  if (p.S > 1 && (int64_t)p.S * M * N * 4 >= (int64_t(1) << 31)) p.S = 1;
   return p;
 }
 
@@ -574,30 +579,40 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
   // uint4 registers, kept near 48 (192 VGPRs).
   // (two with four token groups: 8 waves of 184 registers, two per SIMD, so
   // one wave's MFMAs cover another's waits)
-  constexpr int MAXB = MB == 4 ? 2 : (48 / (CPW + MB * BITS / 2)) >= 8 ? 8 : (48 / (CPW + MB * BITS / 2)) >= 4 ? 4 : 2;
+  // One 16-channel group (CPW == 1, K unsplit): blocks stream through a ring
+  // (below), at most 8 per wave (K <= 16384 with 8 waves).  Four groups
+  // (CPW == 4, K split four ways): two blocks per wave per round, all
+  // requested at once (8 waves of ~160 registers, two per SIMD, so one wave's
+  // MFMAs cover another's waits).
+  constexpr int MAXB = CPW == 1 ? 8 : 2;
   constexpr int CH = 16 * CPW;
-  // Partial sums per (token, channel), rows of RL ints.  Inside each block of
-  // 16 channels column 4r + q holds channel 4q + r, and RL = 4 (mod 64): the
-  // 64 lanes of one accumulate (token c, channel 4g + r) then hit 64 distinct
-  // banks (4c + g), where plain rows of CH ints would put 16 lanes on one.
-  constexpr int RL = CH + 4;
-  __shared__ int red[MB * 16 * RL];
+  // Reduction over the waves (which split K): each wave stores its
+  // accumulators, 16 bytes per lane per 16x16 block, into its own LDS slice
+  // (plain stores, one instruction writes 1 KiB without bank conflicts); then
+  // every thread sums the NW slices of GPT groups of four outputs (four
+  // consecutive channels of one token), 16 bytes per slice.  Integer atomics
+  // into one shared tile (64 per lane at 64 tokens) took 2.2 us of a 12 us
+  // launch.  Group p: 16x16 block p / 64 = cp * MB + mb, lane p % 64, i.e.
+  // token 16 mb + p % 16, channels 16 cp + 4 (p % 64 / 16) + 0..3.
+  constexpr int GROUPS = CPW * MB * 64;
+  constexpr int GPT = (GROUPS + 64 * NW - 1) / (64 * NW);
+  __shared__ v4i slices[NW][GROUPS];
   __shared__ int is_last;
-  auto red_col = [](int nl) { return (nl & ~15) | ((nl & 3) << 2) | ((nl >> 2) & 3); };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int ch0 = blockIdx.x * CH, s = blockIdx.y;
   const int Kr = K / S, kbeg = s * Kr;
   const int nblk = Kr / DKB;                                   // 256-k blocks in this range
   const size_t arow = (size_t)K * BITS / 8;
+  auto group_token = [](int p) { return 16 * ((p >> 6) % MB) + (p & 15); };
+  auto group_channel = [](int p) { return 16 * ((p >> 6) / MB) + 4 * ((p & 63) >> 4); };
 
-  for (int i = tid; i < MB * 16 * RL; i += 64 * NW) red[i] = 0;
   // epilogue scales fetched up front (their latency is not paid at the end)
   const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
-  float ds_pre[(MB * 16 * CH + 64 * NW - 1) / (64 * NW)];
+  float ds_pre[GPT];
 #pragma unroll
-  for (int q = 0; q < (MB * 16 * CH + 64 * NW - 1) / (64 * NW); ++q)
-    ds_pre[q] = OUT == OUT_ACC_I32 ? 0.f : dscale[min((q * 64 * NW + tid) / CH, M - 1)];
+  for (int h = 0; h < GPT; ++h)
+    ds_pre[h] = OUT == OUT_ACC_I32 ? 0.f : dscale[min(group_token(min(h * 64 * NW + tid, GROUPS - 1)), M - 1)];
 
   v4i acc[CPW][MB];
 #pragma unroll
@@ -605,7 +620,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[cp][mb] = v4i{};
 
-  if constexpr (MB == 1) {
+  if constexpr (CPW == 1) {
     // Blocks b = wave + NW*i (i < MAXB: K / S <= NW * MAXB * 256), consumed in
     // order, with only RING blocks per wave requested ahead: block i + RING is
     // requested once block i has been consumed.  Requesting the whole weight
@@ -615,7 +630,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
     // stream and the work overlaps it.  Loads are unconditional (out-of-range
     // indices are clamped to valid addresses and the values discarded), so the
     // compiler releases block i with a partial vmcnt wait.
-    constexpr int RING = MAXB < 4 ? MAXB : 4;
+    constexpr int RING = MB == 1 ? 4 : 2;
     uint4 wq[RING][CPW];
     uint4 aq[RING][MB][BITS / 2];
     auto load = [&](int i, int slot) __attribute__((always_inline)) {
@@ -746,33 +761,69 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
       }
     }
   }
-  __syncthreads();
-  // 16x16 accumulator layout: lane l / register r hold channel 4*(l/16)+r, token l%16
+  // 16x16 accumulator layout: lane l / register r hold channel 4*(l/16)+r,
+  // token l%16, so a lane's four registers are group (cp * MB + mb) * 64 + l
 #pragma unroll
   for (int cp = 0; cp < CPW; ++cp)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * mb + c < M) atomicAdd(&red[(16 * mb + c) * RL + 16 * cp + 4 * r + g], acc[cp][mb][r]);
+    for (int mb = 0; mb < MB; ++mb) slices[wave][(cp * MB + mb) * 64 + lane] = acc[cp][mb];
   __syncthreads();
-
+  v4i sum[GPT];
 #pragma unroll
-  for (int q = 0; q < (MB * 16 * CH + 64 * NW - 1) / (64 * NW); ++q) {
-    const int e = q * 64 * NW + tid;
-    if (e >= M * CH) continue;
-    const int t = e / CH, n = ch0 + e % CH;
-    if (n >= N) continue;
-    const int v = red[t * RL + red_col(e % CH)];
-    if (S == 1) store_out<OUT>(Y, (size_t)t * N + n, unscale<BITS>(v), ds_pre[q] * aw);
-    else if constexpr (MB == 1) partial[((size_t)s * M + t) * N + n] = v;
-    else __hip_atomic_store(&partial[((size_t)s * M + t) * N + n], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int h = 0; h < GPT; ++h) {
+    const int p = min(h * 64 * NW + tid, GROUPS - 1);
+    v4i v = slices[0][p];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += slices[w][p];
+    sum[h] = v;
   }
-  // (the single-token-group instantiation serves M <= 16, which the plan
-  // never splits; it keeps the separate reduction for any split it is given)
-  if constexpr (MB == 1) return;
-  if (S == 1 || tile_count == nullptr) return;
-  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+  // a group is stored when it exists, its token is present and its channels
+  // are (N % 16 == 0: four channels are all inside or all outside)
+  auto live = [&](int h) {
+    const int p = h * 64 * NW + tid;
+    return p < GROUPS && group_token(p) < M && ch0 + group_channel(p) < N;
+  };
+  if (S == 1) {
+#pragma unroll
+    for (int h = 0; h < GPT; ++h) {
+      if (!live(h)) continue;
+      const int p = h * 64 * NW + tid;
+      store_out4<OUT>(Y, (size_t)group_token(p) * N + ch0 + group_channel(p), unscale4<BITS>(sum[h]), ds_pre[h] * aw);
+    }
+    return;
+  }
+  // Split K: this workgroup's partial sums [S][M][N] (int32), 16 bytes per
+  // group, stored with the sc1 cache policy: the stores write through the
+  // XCD's L2, whose contents other XCDs do not see, to the device's point of
+  // coherence (the policy of an agent-scope atomic store, four words wide).
+  // The host keeps S * M * N * 4 below 2^31 on this path (32-bit offsets).
+  const auto prs = __builtin_amdgcn_make_buffer_rsrc(partial, (short)0, 0x7fffffff, kBufferFlags);
+#pragma unroll
+  for (int h = 0; h < GPT; ++h) {
+    if (!live(h)) continue;
+    const int p = h * 64 * NW + tid;
+    const uint32_t off = (uint32_t)((((size_t)s * M + group_token(p)) * N + ch0 + group_channel(p)) * 4);
+    __builtin_amdgcn_raw_buffer_store_b128(sum[h], prs, off, 0, kCachePolicySc1);
+  }
+  // (the one-channel-group instantiations serve M <= 32, which the plan
+  // never splits; they keep the separate reduction for any split given)
+  if constexpr (CPW == 1) return;
+  if (tile_count == nullptr) return;
+  // Hand-off to the last workgroup of the channel tile.  Every thread waits
+  // until its partial stores have completed (reached the point of
+  // coherence), the barrier makes that true for the whole workgroup, and
+  // only then does one thread count the workgroup in with an agent-scope
+  // atomic (performed at that same point).  The workgroup that sees the
+  // count reach S - 1 reads the partials with sc1 loads, which are served
+  // from the point of coherence and not from a possibly stale L2 line.  This
+  // is the ordering that the release / acquire pair of the memory model
+  // provides (L2 write-back before the atomic, L2 invalidate after it), with
+  // the write-back and invalidate replaced by accesses that bypass the
+  // non-coherent L2 for exactly the data handed over: a write-back and
+  // invalidate of the whole L2 in every workgroup slowed the 64-token forward
+  // from 21 to 55 us (the invalidate discarded the codes other workgroups of
+  // the XCD were still reading).
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0)
     is_last = __hip_atomic_fetch_add(&tile_count[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -780,28 +831,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
   __syncthreads();
   if (!is_last) return;
   // every partial this thread sums is requested before any is waited for
-  // (clamped, always in-bounds addresses; splits past S count zero)
-  constexpr int NQ = (MB * 16 * CH + 64 * NW - 1) / (64 * NW);
-  int sum[NQ];
+  // (clamped, always in-bounds offsets; splits past S count zero)
+  v4i tot[GPT];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int e = q * 64 * NW + tid;
-    const int t = min(e / CH, M - 1), n = min(ch0 + e % CH, N - 1);
-    sum[q] = 0;
+  for (int h = 0; h < GPT; ++h) {
+    const int p = min(h * 64 * NW + tid, GROUPS - 1);
+    const int t = min(group_token(p), M - 1), n = min(ch0 + group_channel(p), N - 4);
+    tot[h] = v4i{};
 #pragma unroll
     for (int s2 = 0; s2 < kDecodeMaxSplit; ++s2) {
-      const int v = __hip_atomic_load(&partial[((size_t)min(s2, S - 1) * M + t) * N + n], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-      sum[q] += s2 < S ? v : 0;
+      const uint32_t off = (uint32_t)((((size_t)min(s2, S - 1) * M + t) * N + n) * 4);
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCachePolicySc1);
+      if (s2 < S) tot[h] += v;
     }
   }
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int e = q * 64 * NW + tid;
-    if (e >= M * CH) continue;
-    const int t = e / CH, n = ch0 + e % CH;
-    if (n >= N) continue;
-    store_out<OUT>(Y, (size_t)t * N + n, unscale<BITS>(sum[q]), ds_pre[q] * aw);
+  for (int h = 0; h < GPT; ++h) {
+    if (!live(h)) continue;
+    const int p = h * 64 * NW + tid;
+    store_out4<OUT>(Y, (size_t)group_token(p) * N + ch0 + group_channel(p), unscale4<BITS>(tot[h]), ds_pre[h] * aw);
   }
   if (tid == 0) __hip_atomic_store(&tile_count[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -925,18 +973,18 @@ static size_t partials_bytes(const DecodePlan& p, int64_t M, int64_t N) {
 }
 int gemm_tile_counters(int64_t M, int64_t K, int64_t N) {
   if (M > 64 || M <= 4) return 0;
-  const DecodePlan p = decode_plan((int)M, (int)K);
+  const DecodePlan p = decode_plan(M, K, N);
   return p.S > 1 ? (int)((N + 16 * p.cpw - 1) / (16 * p.cpw)) : 0;
 }
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   if (M > 64 || M <= 0) return 0;
-  const DecodePlan p = decode_plan((int)M, (int)K);
+  const DecodePlan p = decode_plan(M, K, N);
   const size_t nc = (size_t)gemm_tile_counters(M, K, N);
   return partials_bytes(p, M, N) + ((nc * 4 + 255) & ~(size_t)255);
 }
 uint32_t* gemm_tile_counter_ptr(void* ws, int64_t M, int64_t K, int64_t N) {
   if (gemm_tile_counters(M, K, N) == 0 || ws == nullptr) return nullptr;
-  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + partials_bytes(decode_plan((int)M, (int)K), M, N));
+  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + partials_bytes(decode_plan(M, K, N), M, N));
 }
 
 template <int BITS, int MB, int CPW, int NW, int OUT>
@@ -979,11 +1027,9 @@ static void launch_decode_few(const GemmArgs& a) {
 template <int BITS, int OUT>
 static void launch_decode_t(const GemmArgs& a) {
   if (a.M <= 4) { launch_decode_few<BITS, OUT>(a); return; }
-  const DecodePlan p = decode_plan(a.M, a.K);
-#ifdef HBL_DECODE_VARIANTS
-  HBL_DECODE_VARIANTS
-#endif
+  const DecodePlan p = decode_plan(a.M, a.K, a.N);
   if (p.mb == 1) launch_decode_p<BITS, 1, 1, 8, OUT>(a, p.S);
+  else if (p.mb == 2) launch_decode_p<BITS, 2, 1, 8, OUT>(a, p.S);
   else launch_decode_p<BITS, 4, 4, 8, OUT>(a, p.S);
 }
 

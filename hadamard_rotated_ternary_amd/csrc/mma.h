@@ -69,6 +69,29 @@ HBL_DEV void store_out(void* Y, size_t off, int acc, float t) {
   }
 }
 
+// Four consecutive outputs (16-byte aligned for int32 / fp32, 8-byte for bf16).
+template <int OUT>
+HBL_DEV void store_out4(void* Y, size_t off, v4i acc, float t) {
+  if constexpr (OUT == OUT_ACC_I32) {
+    *reinterpret_cast<v4i*>(static_cast<int32_t*>(Y) + off) = acc;
+  } else if constexpr (OUT == OUT_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(Y) + off) =
+        make_float4((float)acc[0] * t, (float)acc[1] * t, (float)acc[2] * t, (float)acc[3] * t);
+  } else {
+    const uint32_t lo = f32_to_bf16((float)acc[0] * t) | ((uint32_t)f32_to_bf16((float)acc[1] * t) << 16);
+    const uint32_t hi = f32_to_bf16((float)acc[2] * t) | ((uint32_t)f32_to_bf16((float)acc[3] * t) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + off) = make_uint2(lo, hi);
+  }
+}
+template <int BITS>
+HBL_DEV v4i unscale4(v4i v) { return v4i{unscale<BITS>(v[0]), unscale<BITS>(v[1]), unscale<BITS>(v[2]), unscale<BITS>(v[3])}; }
+
+// Raw buffer resources: dword 3 of the descriptor for untyped 32-bit access.
+constexpr int kBufferFlags = 0x00020000;
+// Cache policy of a buffer access (the aux operand): sc1, the policy of
+// agent-scope atomic loads and stores on gfx950.
+constexpr int kCachePolicySc1 = 16;
+
 // bf16 output of a wave's 128 x (32*CB) accumulator block through LDS: the
 // block is rounded into the wave's own LDS rows, 64 rows at a time, then
 // written with 16-byte stores as whole row segments (instead of 2-byte

@@ -197,7 +197,7 @@ def test_zero_token_and_tiny_token():
 
 @pytest.mark.parametrize("bits", [8, 4, 6])
 @pytest.mark.parametrize("M,K,N", [(1, 256, 16), (2, 1024, 48), (4, 16384, 272), (3, 8192, 4096),
-                                   (7, 512, 272), (16, 2048, 512), (33, 4096, 64),
+                                   (7, 512, 272), (16, 2048, 512), (20, 4096, 272), (32, 16384, 528), (33, 4096, 64),
                                    (64, 16384, 128), (65, 256, 256), (300, 1024, 272), (512, 2048, 512),
                                    (257, 16384, 528)])
 def test_matmul_bit_exact(bits, M, K, N):
@@ -258,7 +258,7 @@ def check_layer(yh, y_ref, ref, tol=2e-3, tie_tol=1e-4):
 
 
 @pytest.mark.parametrize("bits", [8, 4])
-@pytest.mark.parametrize("M,K,N", [(8, 256, 256), (1, 16384, 4096), (17, 4096, 272), (64, 8192, 512),
+@pytest.mark.parametrize("M,K,N", [(8, 256, 256), (1, 16384, 4096), (17, 4096, 272), (32, 16384, 4096), (64, 8192, 512),
                                    (300, 2048, 272), (513, 16384, 256)])
 def test_layer_small(bits, M, K, N):
     w = synthetic.Workload("t", M, K, N, bits, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, M + K + N)
@@ -403,9 +403,10 @@ def test_single_launch_decode(bits, M, K, N, xdt, gain):
 @pytest.mark.parametrize("M,K,N", [(17, 4096, 272), (33, 16384, 4096), (64, 16384, 4096), (64, 1024, 48),
                                    (40, 512, 96)])
 def test_split_k_decode_reduction_in_kernel(bits, M, K, N):
-    """17..64 tokens: the forward's matmul splits K and the last workgroup of
+    """33..64 tokens: the forward's matmul splits K and the last workgroup of
     each channel tile sums the partials; the stage calls sum them in a
-    separate reduction kernel.  Same codes, exact integer sums: equal bit for
+    separate reduction kernel (17..32 tokens run unsplit: the 17-token case
+    checks that path the same way).  Same codes, exact integer sums: equal bit for
     bit, with a workspace that starts full of 0xFF (the first kernel clears
     the arrival counters) and over repeated calls on it whose inputs
     alternate in sign, so partial sums left over from the call before would
@@ -427,7 +428,7 @@ def test_split_k_decode_reduction_in_kernel(bits, M, K, N):
         assert torch.equal(y.view(torch.int16), y_refs[i % 2].view(torch.int16)), i
 
 
-@pytest.mark.parametrize("M", [1, 40, 64])
+@pytest.mark.parametrize("M", [1, 24, 40, 64])
 def test_forward_graph_replays(M):
     """The forward captured once in a HIP graph and replayed with new inputs
     written into the captured buffers between replays (eager work and a

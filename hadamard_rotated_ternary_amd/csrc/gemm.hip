@@ -587,16 +587,30 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
   constexpr int MAXB = CPW == 1 ? 8 : 2;
   constexpr int CH = 16 * CPW;
   // Reduction over the waves (which split K): each wave stores its
-  // accumulators, 16 bytes per lane per 16x16 block, into its own LDS slice
-  // (plain stores, one instruction writes 1 KiB without bank conflicts); then
-  // every thread sums the NW slices of GPT groups of four outputs (four
+  // accumulators, 16 bytes per lane per 16x16 block, into its own LDS slice,
+  // then every thread sums the NW slices of GPT groups of four outputs (four
   // consecutive channels of one token), 16 bytes per slice.  Integer atomics
   // into one shared tile (64 per lane at 64 tokens) took 2.2 us of a 12 us
-  // launch.  Group p: 16x16 block p / 64 = cp * MB + mb, lane p % 64, i.e.
-  // token 16 mb + p % 16, channels 16 cp + 4 (p % 64 / 16) + 0..3.
-  constexpr int GROUPS = CPW * MB * 64;
+  // launch.  Group p is token p / Q, channel quad p % Q (Q = 4 CPW quads per
+  // token), so the threads of a wave cover whole rows of the partials and the
+  // output (a first numbering in the accumulator order put 16 token rows
+  // under each 16-byte access, and the split-K hand-off took 1 us longer).
+  // Slice rows of Q + 1 quads keep both the accumulator stores (16 tokens x
+  // 4 quads per instruction) and the row reads free of bank conflicts.
+  constexpr int Q = 4 * CPW;
+  constexpr int GROUPS = MB * 16 * Q;
   constexpr int GPT = (GROUPS + 64 * NW - 1) / (64 * NW);
-  __shared__ v4i slices[NW][GROUPS];
+  __shared__ v4i slices[CPW == 1 ? NW : 1][CPW == 1 ? MB * 16 * (Q + 1) : 1];
+  // The split configuration (CPW == 4) reduces over the waves with integer
+  // atomics into one tile of rows of RL ints instead (measured faster there
+  // with its partials handed over element by element: 64 tokens 19.5 against
+  // 20.1 us forward): inside each block of 16 channels column 4r + q holds
+  // channel 4q + r, and RL = 4 (mod 64), so the 64 lanes of one accumulate
+  // (token c, channel 4g + r) hit 64 distinct banks (4c + g).
+  constexpr int RL = CH + 4;
+  constexpr int NQ = (MB * 16 * CH + 64 * NW - 1) / (64 * NW);   // outputs per thread, split configuration
+  __shared__ int red[CPW == 1 ? 1 : MB * 16 * RL];
+  auto red_col = [](int nl) { return (nl & ~15) | ((nl & 3) << 2) | ((nl >> 2) & 3); };
   __shared__ int is_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -604,15 +618,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
   const int Kr = K / S, kbeg = s * Kr;
   const int nblk = Kr / DKB;                                   // 256-k blocks in this range
   const size_t arow = (size_t)K * BITS / 8;
-  auto group_token = [](int p) { return 16 * ((p >> 6) % MB) + (p & 15); };
-  auto group_channel = [](int p) { return 16 * ((p >> 6) / MB) + 4 * ((p & 63) >> 4); };
+  auto group_token = [](int p) { return p / Q; };
+  auto group_channel = [](int p) { return 4 * (p % Q); };
 
   // epilogue scales fetched up front (their latency is not paid at the end)
   const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
-  float ds_pre[GPT];
+  constexpr int NPRE = CPW == 1 ? GPT : NQ;
+  float ds_pre[NPRE];
 #pragma unroll
-  for (int h = 0; h < GPT; ++h)
-    ds_pre[h] = OUT == OUT_ACC_I32 ? 0.f : dscale[min(group_token(min(h * 64 * NW + tid, GROUPS - 1)), M - 1)];
+  for (int h = 0; h < NPRE; ++h) {
+    const int t = CPW == 1 ? group_token(min(h * 64 * NW + tid, GROUPS - 1)) : (h * 64 * NW + tid) / CH;
+    ds_pre[h] = OUT == OUT_ACC_I32 ? 0.f : dscale[min(t, M - 1)];
+  }
+  if constexpr (CPW != 1)
+    for (int i = tid; i < MB * 16 * RL; i += 64 * NW) red[i] = 0;
 
   v4i acc[CPW][MB];
 #pragma unroll
@@ -697,161 +716,230 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
       }
     }
   } else {
-    // Blocks b = wave + NW*i, taken MAXB at a time.
+    // Blocks b = wave + NW*i, taken MAXB at a time.  Loads are unconditional
+    // (out-of-range indices are clamped to valid addresses and the values
+    // discarded), so the compiler can release block i with a partial vmcnt
+    // wait instead of waiting for every load.
+    // BITS == 6: INT4 codes in the fp6 operand layout ([K/128][M][96]) on the
+    // fp6 x fp4 instruction (v_mfma_scale_f32_16x16x128_f8f6f4, unit scales):
+    // lane group g takes the 32-k groups 8b + 2g and 8b + 2g + 1 of 256-k
+    // block b in steps 0 and 1 -- from the packed weights words 4g, 4g + 1
+    // and 4g + 2, 4g + 3 turned into e2m1 nibbles of 2w, from the codes the
+    // 48 contiguous bytes of token t's 128-k block 2b + g/2 at byte 48 (g & 1).
+    // Half the matrix instructions of the int8 form and no activation
+    // expansion; the fp32 sums are exact integers (|acc| <= 8 K < 2^24).
+    constexpr int AU = BITS == 6 ? 3 : BITS / 2;                // 16-byte activation units per token group
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    v4f accf[CPW][MB];
+    if constexpr (BITS == 6) {
+#pragma unroll
+      for (int cp = 0; cp < CPW; ++cp)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) accf[cp][mb] = v4f{};
+    }
     for (int b0 = wave; b0 < nblk; b0 += NW * MAXB) {
       uint4 wq[MAXB][CPW];
-      uint4 aq[MAXB][MB][BITS / 2];
-      // Loads are unconditional (out-of-range indices are clamped to valid
-      // addresses and the values discarded), so the compiler can release block i
-      // with a partial vmcnt wait instead of waiting for every load.
-  #pragma unroll
+      uint4 aq[MAXB][MB][AU];
+#pragma unroll
       for (int i = 0; i < MAXB; ++i) {
         const int b = min(b0 + NW * i, nblk - 1);
-        const int kb = kbeg + b * DKB + 64 * g;                 // this lane's 64 codes of block b
-  #pragma unroll
+        const int gb = (kbeg >> 8) + b;                           // 256-k block over K
+#pragma unroll
         for (int cp = 0; cp < CPW; ++cp) {
           const int n = min(ch0 + 16 * cp + c, N - 1);
-          wq[i][cp] = *reinterpret_cast<const uint4*>(W + wrow_base(n, K) + (size_t)((kbeg + b * DKB) >> 8) * 1024 + 16 * g);
+          wq[i][cp] = *reinterpret_cast<const uint4*>(W + wrow_base(n, K) + (size_t)gb * 1024 + 16 * g);
         }
-  #pragma unroll
+#pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int t = min(16 * mb + c, M - 1);
-          const uint4* ap = reinterpret_cast<const uint4*>(A + (size_t)t * arow + (size_t)kb * BITS / 8);
-  #pragma unroll
-          for (int d = 0; d < BITS / 2; ++d) aq[i][mb][d] = ap[d];
+          const uint4* ap =
+              BITS == 6 ? reinterpret_cast<const uint4*>(A + ((size_t)(2 * gb + (g >> 1)) * M + t) * 96 + 48 * (g & 1))
+                        : reinterpret_cast<const uint4*>(A + (size_t)t * arow + (size_t)(gb * DKB + 64 * g) * BITS / 8);
+#pragma unroll
+          for (int d = 0; d < AU; ++d) aq[i][mb][d] = ap[d];
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < MAXB; ++i) {
         if (b0 + NW * i >= nblk) continue;   // wave-uniform; keeps the loop unrolled (registers, no scratch)
-  #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-  #pragma unroll
-          for (int cp = 0; cp < CPW; ++cp) {
-            // INT8: step j = weight word j against the 16 codes it covers (the
-            // codes as loaded).  INT4 keeps the other pairing -- step j = field j
-            // of all four weight words against the matching nibbles of all four
-            // activation words (1 op per operand dword either way): with it the
-            // 64-token decode runs 15.1 us instead of 17.1 us.
-            v4i wop;
-            if constexpr (BITS == 8) {
-              wop = wstep(u4get(wq[i][cp], j));
-            } else {
-              const uint4 p = wq[i][cp];
-              wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
-            }
-  #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-              v4i aop;
-              if constexpr (BITS == 8) {
-                aop = as_v4i(aq[i][mb][j]);
-              } else {
-                // codes 16d + 4j + i: nibble j%2 of word 2d + j/2
-                const uint4 q0 = aq[i][mb][0], q1 = aq[i][mb][1];
-                const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-                aop = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
-                          (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
+        if constexpr (BITS == 6) {
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int cp = 0; cp < CPW; ++cp) {
+              const uint32_t w0 = st ? wq[i][cp].z : wq[i][cp].x, w1 = st ? wq[i][cp].w : wq[i][cp].y;
+              const v8i wop = v8i{(int)((w0 << 2) & 0xCCCCCCCCu), (int)(w0 & 0xCCCCCCCCu),
+                                  (int)((w1 << 2) & 0xCCCCCCCCu), (int)(w1 & 0xCCCCCCCCu), 0, 0, 0, 0};
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb) {
+                const uint4 a0 = aq[i][mb][0], a1 = aq[i][mb][1], a2 = aq[i][mb][2];
+                const v8i aop = st == 0 ? v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, 0, 0}
+                                        : v8i{(int)a1.z, (int)a1.w, (int)a2.x, (int)a2.y, (int)a2.z, (int)a2.w, 0, 0};
+                accf[cp][mb] =
+                    __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop, aop, accf[cp][mb], 4, 2, 0, 127, 0, 127);
               }
-              // padding tokens (16*mb + c >= M) read token M-1's codes; their
-              // sums are never stored
-              acc[cp][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc[cp][mb], 0, 0, 0);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int cp = 0; cp < CPW; ++cp) {
+              // INT8: step j = weight word j against the 16 codes it covers
+              // (the codes as loaded).  INT4 keeps the other pairing -- step j
+              // = field j of all four weight words against the matching
+              // nibbles of all four activation words (1 op per operand dword
+              // either way): with it the 64-token decode ran 15.1 us instead
+              // of 17.1 us.
+              v4i wop;
+              if constexpr (BITS == 8) {
+                wop = wstep(u4get(wq[i][cp], j));
+              } else {
+                const uint4 p = wq[i][cp];
+                wop = v4i{(int)wfield(p.x, j), (int)wfield(p.y, j), (int)wfield(p.z, j), (int)wfield(p.w, j)};
+              }
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb) {
+                v4i aop;
+                if constexpr (BITS == 8) {
+                  aop = as_v4i(aq[i][mb][j]);
+                } else {
+                  // codes 16d + 4j + i: nibble j%2 of word 2d + j/2
+                  const uint4 q0 = aq[i][mb][0], q1 = aq[i][mb][1];
+                  const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                  aop = v4i{(int)a4field(w[0 + (j >> 1)], j), (int)a4field(w[2 + (j >> 1)], j),
+                            (int)a4field(w[4 + (j >> 1)], j), (int)a4field(w[6 + (j >> 1)], j)};
+                }
+                // padding tokens (16*mb + c >= M) read token M-1's codes;
+                // their sums are never stored
+                acc[cp][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop, acc[cp][mb], 0, 0, 0);
+              }
             }
           }
         }
       }
     }
+    if constexpr (BITS == 6) {
+#pragma unroll
+      for (int cp = 0; cp < CPW; ++cp)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[cp][mb] = v4i{(int)accf[cp][mb][0], (int)accf[cp][mb][1], (int)accf[cp][mb][2], (int)accf[cp][mb][3]};
+    }
   }
-  // 16x16 accumulator layout: lane l / register r hold channel 4*(l/16)+r,
-  // token l%16, so a lane's four registers are group (cp * MB + mb) * 64 + l
-#pragma unroll
-  for (int cp = 0; cp < CPW; ++cp)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) slices[wave][(cp * MB + mb) * 64 + lane] = acc[cp][mb];
-  __syncthreads();
-  v4i sum[GPT];
-#pragma unroll
-  for (int h = 0; h < GPT; ++h) {
-    const int p = min(h * 64 * NW + tid, GROUPS - 1);
-    v4i v = slices[0][p];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) v += slices[w][p];
-    sum[h] = v;
-  }
-  // a group is stored when it exists, its token is present and its channels
-  // are (N % 16 == 0: four channels are all inside or all outside)
-  auto live = [&](int h) {
-    const int p = h * 64 * NW + tid;
-    return p < GROUPS && group_token(p) < M && ch0 + group_channel(p) < N;
-  };
-  if (S == 1) {
-#pragma unroll
+  if constexpr (CPW == 1) {
+    // 16x16 accumulator layout: lane l / register r hold channel 4*(l/16)+r,
+    // token l%16, so a lane's four registers are token 16 mb + c, quad 4 cp + g
+  #pragma unroll
+    for (int cp = 0; cp < CPW; ++cp)
+  #pragma unroll
+      for (int mb = 0; mb < MB; ++mb) slices[wave][(16 * mb + c) * (Q + 1) + 4 * cp + g] = acc[cp][mb];
+    __syncthreads();
+    v4i sum[GPT];
+  #pragma unroll
+    for (int h = 0; h < GPT; ++h) {
+      const int p = min(h * 64 * NW + tid, GROUPS - 1);
+      const int slot = group_token(p) * (Q + 1) + p % Q;
+      v4i v = slices[0][slot];
+  #pragma unroll
+      for (int w = 1; w < NW; ++w) v += slices[w][slot];
+      sum[h] = v;
+    }
+    // a group is stored when it exists, its token is present and its channels
+    // are (N % 16 == 0: four channels are all inside or all outside)
+    auto live = [&](int h) {
+      const int p = h * 64 * NW + tid;
+      return p < GROUPS && group_token(p) < M && ch0 + group_channel(p) < N;
+    };
+    if (S == 1) {
+  #pragma unroll
+      for (int h = 0; h < GPT; ++h) {
+        if (!live(h)) continue;
+        const int p = h * 64 * NW + tid;
+        store_out4<OUT>(Y, (size_t)group_token(p) * N + ch0 + group_channel(p), unscale4<BITS>(sum[h]), ds_pre[h] * aw);
+      }
+      return;
+    }
+    // (the plan never splits these configurations; a split given anyway is
+    // summed by the separate reduction kernel)
+  #pragma unroll
     for (int h = 0; h < GPT; ++h) {
       if (!live(h)) continue;
       const int p = h * 64 * NW + tid;
-      store_out4<OUT>(Y, (size_t)group_token(p) * N + ch0 + group_channel(p), unscale4<BITS>(sum[h]), ds_pre[h] * aw);
+      *reinterpret_cast<v4i*>(partial + ((size_t)s * M + group_token(p)) * N + ch0 + group_channel(p)) = sum[h];
     }
-    return;
-  }
-  // Split K: this workgroup's partial sums [S][M][N] (int32), 16 bytes per
-  // group, stored with the sc1 cache policy: the stores write through the
-  // XCD's L2, whose contents other XCDs do not see, to the device's point of
-  // coherence (the policy of an agent-scope atomic store, four words wide).
-  // The host keeps S * M * N * 4 below 2^31 on this path (32-bit offsets).
-  const auto prs = __builtin_amdgcn_make_buffer_rsrc(partial, (short)0, 0x7fffffff, kBufferFlags);
-#pragma unroll
-  for (int h = 0; h < GPT; ++h) {
-    if (!live(h)) continue;
-    const int p = h * 64 * NW + tid;
-    const uint32_t off = (uint32_t)((((size_t)s * M + group_token(p)) * N + ch0 + group_channel(p)) * 4);
-    __builtin_amdgcn_raw_buffer_store_b128(sum[h], prs, off, 0, kCachePolicySc1);
-  }
-  // (the one-channel-group instantiations serve M <= 32, which the plan
-  // never splits; they keep the separate reduction for any split given)
-  if constexpr (CPW == 1) return;
-  if (tile_count == nullptr) return;
-  // Hand-off to the last workgroup of the channel tile.  Every thread waits
-  // until its partial stores have completed (reached the point of
-  // coherence), the barrier makes that true for the whole workgroup, and
-  // only then does one thread count the workgroup in with an agent-scope
-  // atomic (performed at that same point).  The workgroup that sees the
-  // count reach S - 1 reads the partials with sc1 loads, which are served
-  // from the point of coherence and not from a possibly stale L2 line.  This
-  // is the ordering that the release / acquire pair of the memory model
-  // provides (L2 write-back before the atomic, L2 invalidate after it), with
-  // the write-back and invalidate replaced by accesses that bypass the
-  // non-coherent L2 for exactly the data handed over: a write-back and
-  // invalidate of the whole L2 in every workgroup slowed the 64-token forward
-  // from 21 to 55 us (the invalidate discarded the codes other workgroups of
-  // the XCD were still reading).
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0)
-    is_last = __hip_atomic_fetch_add(&tile_count[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              (uint32_t)(S - 1);
-  __syncthreads();
-  if (!is_last) return;
-  // every partial this thread sums is requested before any is waited for
-  // (clamped, always in-bounds offsets; splits past S count zero)
-  v4i tot[GPT];
-#pragma unroll
-  for (int h = 0; h < GPT; ++h) {
-    const int p = min(h * 64 * NW + tid, GROUPS - 1);
-    const int t = min(group_token(p), M - 1), n = min(ch0 + group_channel(p), N - 4);
-    tot[h] = v4i{};
-#pragma unroll
-    for (int s2 = 0; s2 < kDecodeMaxSplit; ++s2) {
-      const uint32_t off = (uint32_t)((((size_t)min(s2, S - 1) * M + t) * N + n) * 4);
-      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCachePolicySc1);
-      if (s2 < S) tot[h] += v;
+  } else {
+    __syncthreads();
+    // 16x16 accumulator layout: lane l / register r hold channel 4*(l/16)+r, token l%16
+    // (every lane adds when the matrix work is the fp6 x fp4 instruction: the
+    // compiler would otherwise move that work into the branch of the lanes whose
+    // token is present, leaving the other lanes' operands unset)
+  #pragma unroll
+    for (int cp = 0; cp < CPW; ++cp)
+  #pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (BITS == 6 || 16 * mb + c < M) atomicAdd(&red[(16 * mb + c) * RL + 16 * cp + 4 * r + g], acc[cp][mb][r]);
+    __syncthreads();
+  #pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = q * 64 * NW + tid;
+      if (e >= M * CH) continue;
+      const int t = e / CH, n = ch0 + e % CH;
+      if (n >= N) continue;
+      const int v = red[t * RL + red_col(e % CH)];
+      if (S == 1) store_out<OUT>(Y, (size_t)t * N + n, unscale<BITS>(v), ds_pre[q] * aw);
+      else __hip_atomic_store(&partial[((size_t)s * M + t) * N + n], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (S == 1 || tile_count == nullptr) return;
+    // Hand-off to the last workgroup of the channel tile.  Every thread waits
+    // until its partial stores (agent-scope atomic stores: written through the
+    // XCD's L2, whose contents other XCDs do not see, to the device's point of
+    // coherence) have completed, the barrier makes that true for the whole
+    // workgroup, and only then does one thread count the workgroup in with an
+    // agent-scope atomic, performed at that same point.  The workgroup that
+    // sees the count reach S - 1 reads the partials with agent-scope atomic
+    // loads, served from the point of coherence and not from a possibly stale
+    // L2 line.  This gives the ordering of the memory model's release /
+    // acquire pair (an L2 write-back before the atomic, an L2 invalidate after
+    // it) with the write-back and invalidate replaced by accesses that bypass
+    // the non-coherent L2 for exactly the data handed over: a device-scope
+    // fence in every workgroup slowed the 64-token forward from 21 to 55 us
+    // (its invalidate discarded the codes other workgroups of the XCD were
+    // still reading).  Nothing waits on another workgroup.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      is_last = __hip_atomic_fetch_add(&tile_count[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)(S - 1);
+    __syncthreads();
+    if (!is_last) return;
+    // every partial this thread sums is requested before any is waited for
+    // (clamped, always in-bounds addresses; splits past S count zero)
+    int tot[NQ];
+  #pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = q * 64 * NW + tid;
+      const int t = min(e / CH, M - 1), n = min(ch0 + e % CH, N - 1);
+      tot[q] = 0;
+  #pragma unroll
+      for (int s2 = 0; s2 < kDecodeMaxSplit; ++s2) {
+        const int v = __hip_atomic_load(&partial[((size_t)min(s2, S - 1) * M + t) * N + n], __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+        tot[q] += s2 < S ? v : 0;
+      }
+    }
+  #pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = q * 64 * NW + tid;
+      if (e >= M * CH) continue;
+      const int t = e / CH, n = ch0 + e % CH;
+      if (n >= N) continue;
+      store_out<OUT>(Y, (size_t)t * N + n, unscale<BITS>(tot[q]), ds_pre[q] * aw);
+    }
+    if (tid == 0) __hip_atomic_store(&tile_count[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-#pragma unroll
-  for (int h = 0; h < GPT; ++h) {
-    if (!live(h)) continue;
-    const int p = h * 64 * NW + tid;
-    store_out4<OUT>(Y, (size_t)group_token(p) * N + ch0 + group_channel(p), unscale4<BITS>(tot[h]), ds_pre[h] * aw);
-  }
-  if (tid == 0) __hip_atomic_store(&tile_count[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Few tokens (M <= 4): one workgroup of NW waves per 16 channels and the whole
@@ -1055,8 +1143,25 @@ static void launch_t(const GemmArgs& a) {
   else launch_prefill_t<BITS, OUT>(a);
 }
 
+// fp6 codes with at most 64 tokens: the split decode matmul (64 channels per
+// workgroup; K split as the plan says above 32 tokens, unsplit below, where
+// only stage calls bring fp6 codes).
+template <int OUT>
+static void launch_decode_fp6(const GemmArgs& a) {
+  const DecodePlan p = decode_plan(a.M, a.K, a.N);
+  launch_decode_p<6, 4, 4, 8, OUT>(a, p.cpw == 4 ? p.S : 1);
+}
+
 hipError_t launch_gemm_fp6(const GemmArgs& a) {
   if (a.M == 0) return hipSuccess;
+  if (a.M <= 64) {
+    switch (a.out_kind) {
+      case OUT_ACC_I32: launch_decode_fp6<OUT_ACC_I32>(a); break;
+      case OUT_F32: launch_decode_fp6<OUT_F32>(a); break;
+      default: launch_decode_fp6<OUT_BF16>(a); break;
+    }
+    return hipGetLastError();
+  }
   const int tm = (a.M + PBM - 1) / PBM, tn = (a.N + PBN - 1) / PBN;
 #define HBL_F6(OUT)                                                                                          \
   if (a.K == 256)                                                                                                \

@@ -132,7 +132,7 @@ hbl_status forward(int bits, bool rotate, const void* x, hbl_dtype x_dtype, cons
   // split-K decode shapes: prep clears the matmul's arrival counters, so the
   // matmul's last workgroup per tile reduces (no separate reduction launch)
   const bool fp6 = fp6_path(bits, M);
-  uint32_t* counts = fp6 ? nullptr : hbl::gemm_tile_counter_ptr(gws, M, K, N);
+  uint32_t* counts = hbl::gemm_tile_counter_ptr(gws, M, K, N);
 
   hbl::PrepArgs p{};
   p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
@@ -280,7 +280,7 @@ static hbl_status matmul(const void* codes, int bits, const float* dscale, const
   if (!codes || !w_packed || !out) return HBL_ERR_NULL;
   if (out_kind != hbl::OUT_ACC_I32 && (!dscale || !w_alpha)) return HBL_ERR_NULL;
   const bool fp6 = bits == HBL_BITS_INT4_FP6;
-  const size_t need = fp6 ? 0 : align256(hbl::gemm_workspace_bytes(M, K, N));
+  const size_t need = align256(hbl::gemm_workspace_bytes(M, K, N));
   if (need && !workspace) return HBL_ERR_NULL;
   if (!aligned16(codes) || !aligned16(w_packed) || !aligned16(out) || (dscale && !aligned16(dscale)) ||
       (w_alpha && !aligned16(w_alpha)) || (workspace && !aligned16(workspace)))

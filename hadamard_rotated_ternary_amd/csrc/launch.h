@@ -50,8 +50,10 @@ struct GemmArgs {
   hipStream_t stream;
 };
 hipError_t launch_gemm(const GemmArgs& a);
-// INT4 prefill on the fp6 x fp4 matrix instruction: codes in the fp6 operand
-// layout that prep mode 2 writes, [M][K*3/4].  Used for M > kFp6MinM.
+// INT4 on the fp6 x fp4 matrix instruction: codes in the fp6 operand layout
+// that prep mode 2 writes, [K/128][M][96].  The forward uses it for
+// M > kFp6MinM: the split decode matmul up to 64 tokens, the prefill matmul
+// beyond.
 constexpr int kFp6MinM = 64;
 hipError_t launch_gemm_fp6(const GemmArgs& a);
 // Workspace bytes the matmul needs beyond the codes and scales.

@@ -34,9 +34,11 @@ HBL_DEV uint32_t a4field(uint32_t w, int j) {
 }
 // The accumulators therefore hold 64 * acc (INT8 path) or 1024 * acc (INT4),
 // exact multiples whose magnitude stays below 2^27 for K <= 16384 (|q| <= 128
-// after scaling, |w| = 64): an arithmetic shift recovers acc exactly.
+// after scaling, |w| = 64): an arithmetic shift recovers acc exactly.  The
+// fp6 x fp4 instruction (BITS == 6: codes q/2 against weights 2w) sums acc
+// itself.
 template <int BITS>
-HBL_DEV int unscale(int v) { return BITS == 8 ? (v >> 6) : (v >> 10); }
+HBL_DEV int unscale(int v) { return BITS == 8 ? (v >> 6) : BITS == 4 ? (v >> 10) : v; }
 HBL_DEV uint32_t u4get(const uint4& u, int j) { return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w; }
 
 // Copy 16 bytes per lane from global memory straight into LDS: the wave's
@@ -86,11 +88,6 @@ HBL_DEV void store_out4(void* Y, size_t off, v4i acc, float t) {
 template <int BITS>
 HBL_DEV v4i unscale4(v4i v) { return v4i{unscale<BITS>(v[0]), unscale<BITS>(v[1]), unscale<BITS>(v[2]), unscale<BITS>(v[3])}; }
 
-// Raw buffer resources: dword 3 of the descriptor for untyped 32-bit access.
-constexpr int kBufferFlags = 0x00020000;
-// Cache policy of a buffer access (the aux operand): sc1, the policy of
-// agent-scope atomic loads and stores on gfx950.
-constexpr int kCachePolicySc1 = 16;
 
 // bf16 output of a wave's 128 x (32*CB) accumulator block through LDS: the
 // block is rounded into the wave's own LDS rows, 64 rows at a time, then

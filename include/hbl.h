@@ -63,7 +63,7 @@
  *       (b in 0..3; h, d0, d1 in 0..1).  This is the operand layout of the
  *       gfx950 fp6 x fp4 matrix instruction for the weights' packed order,
  *       blocked so that 128 k of consecutive tokens are contiguous; the INT4
- *       forward uses it internally for M > 64.
+ *       forward uses it internally for M > 32.
  *   per-token dequant scales d   fp32 [M].
  *   per-tensor weight scale      fp32 [1] (alpha; the floor 1e-5 is applied on use).
  */
@@ -234,7 +234,7 @@ hbl_status hbl_quantize_act(const void *x, hbl_dtype x_dtype, const float *gain,
  * Stage 2: ternary integer matmul of the codes with dequant epilogue.
  *   codes, dscale as written by hbl_quantize_act;  y [M][N] of y_dtype.
  *   bits      8 and 4 run on the int8 matrix instruction (any M); 6 runs on
- *             the fp6 x fp4 instruction (made for M > 64; any M works).
+ *             the fp6 x fp4 instruction (made for M > 32; any M works).
  *   workspace at least hbl_workspace_bytes(HBL_OP_MATMUL, M, K, N) bytes (split-K
  *             scratch of the small-M path; may be NULL when that size is 0).
  *   Calls sharing one workspace must be stream-ordered.

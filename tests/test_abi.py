@@ -116,7 +116,8 @@ def test_stage_validation(L):
     assert L.hbl_gemm_ternary(A, 8, A, 4, 256, 250, A, None, 0, S) == SHAPE
     assert L.hbl_gemm_ternary(A, 8, A, 64, 1024, 256, A, None, 0, S) == NULL     # split small-M needs scratch
     assert L.hbl_gemm_ternary(A, 8, A, 64, 1024, 256, A, A2, 16, S) == WORKSPACE
-    assert L.hbl_gemm_ternary(A, 6, A, 64, 1024, 256, BAD, None, 0, S) == ALIGN   # fp6 path: no scratch
+    assert L.hbl_gemm_ternary(A, 6, A, 65, 1024, 256, BAD, None, 0, S) == ALIGN   # fp6 prefill: no scratch
+    assert L.hbl_gemm_ternary(A, 6, A, 64, 1024, 256, A, None, 0, S) == NULL      # fp6 split decode needs scratch
     assert L.hbl_matmul_dequant(A, 8, None, A, A, 100, 256, 256, A, 1, None, 0, S) == NULL
     assert L.hbl_quantize_weights(A, 256, 255, A, A, A, 1 << 20, S) == SHAPE
     assert L.hbl_quantize_weights(A, 256, 256, A, A, A, 8, S) == WORKSPACE

@@ -26,6 +26,8 @@
 // with channels on the instruction's M side and the tokens on its N side,
 // integer partials of the 8 waves combined with LDS atomics, then the
 // dequant epilogue.
+#include <mutex>
+
 #include "fwht.h"
 #include "mma.h"
 
@@ -201,16 +203,16 @@ static hipError_t launch_fd_t(const FusedDecodeArgs& a) {
   const size_t lds = (size_t)((C::REGION * 4 + 15) & ~15) + (size_t)a.M * C::K + 64;
   auto kern = &decode_fused_kernel<LOGK, LOGE, P2, BITS, XBF16, OUT, ROT>;
   // more than 64 KiB of dynamic LDS needs the per-function limit raised,
-  // once per device and instantiation
-  static bool attr[64] = {};
+  // once per device and instantiation (thread-safe)
+  static std::once_flag once[64];
+  static hipError_t set_err[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr[dev]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       146 * 1024);
-    if (e != hipSuccess) return e;
-    attr[dev] = true;
-  }
+  std::call_once(once[dev], [dev, kern] {
+    set_err[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 146 * 1024);
+  });
+  if (set_err[dev] != hipSuccess) return set_err[dev];
   hipLaunchKernelGGL(kern, dim3((a.N + 15) / 16), dim3(64 * FD_NW), lds, a.stream, a.x, a.gain, a.wpack, a.walpha,
                      a.out, a.M, a.N);
   return hipGetLastError();

@@ -27,6 +27,8 @@
 // k order across the K loop is free.  Per 128-k stage, lane group g of the
 // 32x32x32 MFMA covers k-chunks 4g..4g+3 (16 k each), one chunk per MFMA step;
 // that makes every weight fragment one contiguous 16-byte read.
+#include <mutex>
+
 #include "mma.h"
 
 namespace hbl {
@@ -84,6 +86,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
   const int in_g = logical % per_group;
   const int m0 = (first_m + in_g % gm) * PBM;
   const int n0 = (in_g / gm) * PBN;
+  __shared__ __attribute__((aligned(16))) float srow[PBM];   // epilogue row scales (row_scale_copy)
 
   constexpr int NT = 64 * NWV;                 // threads
   constexpr int WNW = NWV / 2;                 // waves along N
@@ -210,6 +213,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
     if (kt + 2 < KT) dma(kt + 2, buf == 0 ? 2 : buf - 1);
     compute(buf);
   };
+  if (OUT != OUT_ACC_I32) row_scale_copy(dscale, m0, M, srow, wave, lane);
   dma(0, 0);
   if (KT > 1) dma(1, 1);
   for (int kt = 0; kt < KT; kt += 3) {
@@ -224,18 +228,20 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
   if constexpr (OUT == OUT_BF16) {
     static_assert(NWV * 64 * (CB * 64 + 32) <= 3 * C::STAGE, "staging fits the ring");
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");   // every wave is done with the ring
-    store_bf16_staged<CB>(smem + wave * (64 * (CB * 64 + 32)), static_cast<uint16_t*>(Y), dscale, aw, M, N,
+    store_bf16_staged<CB>(smem + wave * (64 * (CB * 64 + 32)), static_cast<uint16_t*>(Y), srow + wm * 128, aw, M, N,
                           m0 + wm * 128, n0 + wn * (32 * CB), lane,
                           [&](int rb, int cb, int r) { return (float)unscale<BITS>(acc[rb][cb][r]); });
     return;
   }
+  __syncthreads();
 #pragma unroll
   for (int rbk = 0; rbk < 4; ++rbk) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 128 + rbk * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      const int rl = wm * 128 + rbk * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      const int m = m0 + rl;
       if (m >= M) continue;
-      const float t = OUT == OUT_ACC_I32 ? 0.f : dscale[m] * aw;
+      const float t = OUT == OUT_ACC_I32 ? 0.f : srow[rl] * aw;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int n = n0 + wn * (32 * CB) + cb * 32 + l32;
@@ -315,6 +321,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   const int in_g = logical % per_group;
   const int m0 = (first_m + in_g % gm) * PBM;
   const int n0 = (in_g / gm) * PBN;
+  __shared__ __attribute__((aligned(16))) float srow[PBM];   // epilogue row scales (row_scale_copy)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -480,6 +487,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j) dmaB(j, min(p, KP - 1), p);
   };
+  if (OUT != OUT_ACC_I32) row_scale_copy(dscale, m0, M, srow, wave, lane);
   dmaA_all(0); dmaB_all(0); dmaA_all(1); dmaA_all(2); dmaB_all(1); dmaA_all(3);
   wait_vmcnt<3 * A_LOADS + B_LOADS>();     // A0 and B0 have landed
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
@@ -504,17 +512,19 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
   if constexpr (OUT == OUT_BF16) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");   // every wave is done with the ring
-    store_bf16_staged<4>(smem + wave * (64 * (4 * 64 + 32)), static_cast<uint16_t*>(Y), dscale, aw, M, N,
+    store_bf16_staged<4>(smem + wave * (64 * (4 * 64 + 32)), static_cast<uint16_t*>(Y), srow + wm * 128, aw, M, N,
                          m0 + wm * 128, n0 + wn * 128, lane,
                          [&](int rb, int cb, int r) { return acc[rb][cb][r]; });
   } else {
+    __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 128 + rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int rl = wm * 128 + rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int m = m0 + rl;
         if (m >= M) continue;
-        const float t = OUT == OUT_ACC_I32 ? 0.f : dscale[m] * aw;
+        const float t = OUT == OUT_ACC_I32 ? 0.f : srow[rl] * aw;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           const int n = n0 + wn * 128 + cb * 32 + l32;
@@ -1092,13 +1102,15 @@ template <int BITS, int UPT, int OUT>
 static void launch_decode_few_u(const GemmArgs& a) {
   const size_t lds = (size_t)a.M * a.K + 64;
   // more than 64 KiB of dynamic LDS needs the function's limit raised, once
-  // per device (a failure shows as the launch's error)
-  static bool attr[64] = {};
+  // per device and instantiation (thread-safe; a failure shows as the
+  // launch's error)
+  static std::once_flag once[64];
   int dev = 0;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr[dev] &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode_few_kernel<BITS, 8, UPT, OUT>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) == hipSuccess)
-    attr[dev] = true;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64)
+    std::call_once(once[dev], [] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode_few_kernel<BITS, 8, UPT, OUT>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    });
   hipLaunchKernelGGL((gemm_decode_few_kernel<BITS, 8, UPT, OUT>), dim3((a.N + 15) / 16), dim3(512), lds,
                      a.stream, a.codes, a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K);
 }

@@ -52,6 +52,11 @@ HBL_DEV void lds_copy16(const void* gsrc, void* lds_base) {
   const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(l), "v"(gsrc) : "memory", "m0");
 }
+// The same for 4 bytes per lane: the wave fills 256 bytes at lds_base.
+HBL_DEV void lds_copy4(const void* gsrc, void* lds_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(l), "v"(gsrc) : "memory", "m0");
+}
 // Wait until at most N vector-memory operations of this wave are in flight
 // (gfx9 s_waitcnt encoding: vmcnt[3:0] and [15:14], expcnt and lgkmcnt at max).
 template <int N>
@@ -89,18 +94,32 @@ template <int BITS>
 HBL_DEV v4i unscale4(v4i v) { return v4i{unscale<BITS>(v[0]), unscale<BITS>(v[1]), unscale<BITS>(v[2]), unscale<BITS>(v[3])}; }
 
 
+// Row scales d of a 256-row output tile in LDS for the epilogue: waves 0-3
+// each copy 64 of them with one global-to-LDS instruction (lane L: row
+// 64 * wave + L, clamped to the last row, so nothing past d[M-1] is read),
+// issued before the tile's first operand copies, so every later wait for
+// those copies also covers it and no register holds it through the main
+// loop.  Reading d from global memory in the epilogue itself put four
+// dependent batches of loads, each a full memory latency with one wave per
+// SIMD, into every tile (9.7 us of a 107 us tile); a register-held d
+// lengthened the main loop instead.
+HBL_DEV void row_scale_copy(const float* __restrict__ dscale, int m0, int M, float* srow, int wave, int lane) {
+  if (wave < 4) lds_copy4(dscale + min(m0 + 64 * wave + lane, M - 1), srow + 64 * wave);
+}
+
 // bf16 output of a wave's 128 x (32*CB) accumulator block through LDS: the
 // block is rounded into the wave's own LDS rows, 64 rows at a time, then
 // written with 16-byte stores as whole row segments (instead of 2-byte
 // stores scattered over 64 rows).  getv(rb, cb, r) returns the unscaled
 // accumulator of 32x32 block (rb, cb), register r; lane l / register r hold
-// row 8*(r/4) + 4*(l/32) + r%4, column l%32.  Staged rows are CB*64 + 32
-// bytes, so the two rows one store instruction touches start 32 banks apart.
-// The caller makes sure no other wave still uses the stage area.  N % 16 == 0,
-// so 8-column chunks are either whole or outside.
+// row 8*(r/4) + 4*(l/32) + r%4, column l%32.  srow holds the scales of the
+// block's 128 rows (d, in LDS) and aw the weight scale max(alpha, 1e-5).  Staged rows are CB*64 + 32 bytes, so the
+// two rows one store instruction touches start 32 banks apart.  The caller
+// makes sure no other wave still uses the stage area.  N % 16 == 0, so
+// 8-column chunks are either whole or outside.
 template <int CB, typename GetV>
-HBL_DEV void store_bf16_staged(uint8_t* stage, uint16_t* Y, const float* __restrict__ dscale, float aw, int M,
-                               int N, int mrow0, int ncol0, int lane, GetV getv) {
+HBL_DEV void store_bf16_staged(uint8_t* stage, uint16_t* Y, const float* srow, float aw, int M, int N, int mrow0,
+                               int ncol0, int lane, GetV getv) {
   constexpr int ER = CB * 64 + 32;             // staged row bytes
   constexpr int LPR = CB * 4;                  // lanes per row on the way out (16 bytes each)
   constexpr int RPI = 64 / LPR;                // rows per store instruction
@@ -113,7 +132,7 @@ HBL_DEV void store_bf16_staged(uint8_t* stage, uint16_t* Y, const float* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rl = rh * 32 + 8 * (r >> 2) + 4 * g + (r & 3);     // row within the half
-        const float t = dscale[min(mrow0 + 64 * hf + rl, M - 1)] * aw;
+        const float t = srow[64 * hf + rl] * aw;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
           *reinterpret_cast<uint16_t*>(stage + rl * ER + (cb * 32 + l32) * 2) = f32_to_bf16_hw(getv(rb, cb, r) * t);

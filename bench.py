@@ -32,7 +32,8 @@ PEAK_FP6_TFLOPS = 10100.0    # MI355X dense fp6 / fp4 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wdown_7b_int4_hbm_traffic.txt")
-GEMM_SOURCES = [os.path.join(ROOT, "hadamard_rotated_ternary_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+GEMM_SOURCES = [os.path.join(ROOT, "hadamard_rotated_ternary_amd", "csrc", f)
+                for f in ("gemm.hip", "common.h", "mma.h", "copy_schedule.h")]
 
 
 def log(*a):
@@ -281,8 +282,97 @@ def stored_attn_traffic():
     return int(kv["attn_bytes_per_launch"])
 
 
+def layer_config_extra(torch, hbl, synthetic, name, steps):
+    """One prefill-shaped configuration end to end: tokens/s of the
+    single-call forward, per-kernel times from the stage calls, effective int
+    TOPS (2MNK per step), the matmul against its instruction's peak (fp6 x fp4
+    10.1 P for INT4 beyond 64 tokens, int8 5.0 P otherwise) and prep against
+    8 TB/s (its own bytes: activations in, codes and scales out)."""
+    w = synthetic.WORKLOADS[name]
+    x, xb, wl = synthetic.make_inputs(w)
+    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16) if xb is not None else torch.from_numpy(x).cuda()
+    wp, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
+    r = time_layer(torch, hbl, xd, wp, a, w.M, w.K, w.N, w.bits, steps, 5)
+    ops = 2.0 * w.M * w.N * w.K
+    fp6 = w.bits == 4 and w.M > 64
+    peak = PEAK_FP6_TFLOPS if fp6 else PEAK_INT8_TOPS
+    xb_ = xd.element_size()
+    prep_bytes = w.M * w.K * xb_ + w.M * hbl.codes_row_bytes(6 if fp6 else w.bits, w.K) + w.M * 4
+    gemm_tops = ops / (r["gemm_ms"] / 1e3) / 1e12
+    res = {"M": w.M, "K": w.K, "N": w.N, "activation_bits": w.bits,
+           "matmul": "fp6xfp4" if fp6 else "i8",
+           "tokens_per_s": w.M / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
+           "effective_int_tops": ops / (r["ms_per_step"] / 1e3) / 1e12,
+           "hbm_gbps_algorithmic": algorithmic_bytes(w.M, w.K, w.N, xb_, xb_) / (r["ms_per_step"] / 1e3) / 1e9,
+           "prep_ms": r["prep_ms"], "gemm_ms": r["gemm_ms"],
+           "gemm_tops": gemm_tops, "gemm_peak_tops": peak, "gemm_frac": gemm_tops / peak,
+           "prep_gbps": prep_bytes / (r["prep_ms"] / 1e3) / 1e9,
+           "prep_hbm_frac": prep_bytes / (r["prep_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS}
+    del xd, wp
+    return res
+
+
+def int4_on_int8_extra(torch, hbl, synthetic, steps):
+    """The 7B Wdown INT4 matmul on the int8 matrix instruction (INT4 nibble
+    codes unpacked to int8 in registers, 2-bit weights expanded in
+    registers): the stage call with format 4, against the 5.0 P dense int8
+    peak.  The forward runs this shape on the fp6 x fp4 instruction instead
+    (bit-identical results at twice the instruction rate)."""
+    w = synthetic.WORKLOADS["wdown_7b_int4"]
+    x, xb, wl = synthetic.make_inputs(w)
+    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    wp, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
+    codes, d = hbl.quantize_act(xd, 4)
+    y = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(hbl.workspace_bytes(hbl.OP_MATMUL, w.M, w.K, w.N), 16), dtype=torch.uint8, device="cuda")
+    wps = [wp, wp.clone()]
+    for i in range(5):
+        hbl.matmul_dequant(codes, 4, d, wps[i % 2], a, w.K, workspace=ws, out=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        hbl.matmul_dequant(codes, 4, d, wps[i % 2], a, w.K, workspace=ws, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tops = 2.0 * w.M * w.N * w.K / (ms / 1e3) / 1e12
+    del xd, wp, wps, codes
+    return {"M": w.M, "K": w.K, "N": w.N, "kernel": "gemm_prefill_kernel (INT4 codes, int8 MFMA)", "gemm_ms": ms,
+            "gemm_tops": tops, "gemm_frac_int8_peak": tops / PEAK_INT8_TOPS}
+
+
+def tiny_extra(torch, hbl, synthetic):
+    """The smallest configuration (8 tokens, K = N = 256, fp32): per-call
+    time of the single-call forward (latency; 1 us is a launch)."""
+    w = synthetic.WORKLOADS["tiny_int8"]
+    x, _, wl = synthetic.make_inputs(w)
+    xd = torch.from_numpy(x).cuda()
+    wp, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
+    y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(hbl.workspace_bytes(hbl.OP_FORWARD_INT8, w.M, w.K, w.N), 16), dtype=torch.uint8, device="cuda")
+    for _ in range(20):
+        hbl.forward(xd, wp, a, 8, workspace=ws, out=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(200):
+        hbl.forward(xd, wp, a, 8, workspace=ws, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / 200
+    return {"M": w.M, "K": w.K, "N": w.N, "forward_us": us, "tokens_per_s": w.M / (us / 1e6),
+            "timing": "events around 200 back-to-back calls (host launch rate included)"}
+
+
 def extras(torch, hbl, synthetic, args):
     out = {}
+    steps = max(10, args.steps // 2)
+    # every other configuration of the layer, end to end
+    for name in ("wo_1p3b_int4", "wdown_3b_int4", "wo_7b_int8", "wo_7b_int4"):
+        out[name] = layer_config_extra(torch, hbl, synthetic, name, steps)
+    out["wdown_7b_int4_on_int8_mfma"] = int4_on_int8_extra(torch, hbl, synthetic, steps)
+    out["tiny_int8"] = tiny_extra(torch, hbl, synthetic)
     # INT8 activations on the same 7B Wdown shape
     w8 = synthetic.WORKLOADS["wdown_7b_int8"]
     x, xb, wl = synthetic.make_inputs(w8)

@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhbl.so")
 SOURCES = ["hbl_api.cpp", "prep.hip", "wquant.hip", "gemm.hip", "decode_fused.hip", "attn.hip", "bwd.hip",
            "noalloc.hip"]
-HEADERS = ["common.h", "launch.h", "mma.h", "fwht.h"]
+HEADERS = ["common.h", "launch.h", "mma.h", "fwht.h", "copy_schedule.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

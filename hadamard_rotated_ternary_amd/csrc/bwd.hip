@@ -453,8 +453,8 @@ hipError_t launch_bwd_prep_t(const BwdArgs& a, int grid, float* dgpart) {
                        dim3(PrepCfg<LK, LE, P2>::WG), 0, a.stream, a.dxh, a.x, a.gain, a.M, a.dx, dgpart); \
     break;
   switch (a.logk) {
-    HBL_BP(8, 4, 6) HBL_BP(9, 5, 6) HBL_BP(10, 5, 7) HBL_BP(11, 6, 7) HBL_BP(12, 4, 6) HBL_BP(13, 4, 6)
-    HBL_BP(14, 4, 6)
+    HBL_BP(6, 4, 6) HBL_BP(7, 4, 6) HBL_BP(8, 4, 6) HBL_BP(9, 5, 6) HBL_BP(10, 5, 7) HBL_BP(11, 6, 7)
+    HBL_BP(12, 4, 6) HBL_BP(13, 4, 6) HBL_BP(14, 4, 6) HBL_BP(15, 5, 7)
     default: return hipErrorInvalidValue;
   }
 #undef HBL_BP
@@ -465,6 +465,8 @@ hipError_t launch_bwd_prep_t(const BwdArgs& a, int grid, float* dgpart) {
 
 int bwd_prep_tpb(int logk) {
   switch (logk) {
+    case 6: return PrepCfg<6, 4, 6>::TPB;
+    case 7: return PrepCfg<7, 4, 6>::TPB;
     case 8: return PrepCfg<8, 4, 6>::TPB;
     case 9: return PrepCfg<9, 5, 6>::TPB;
     case 10: return PrepCfg<10, 5, 7>::TPB;
@@ -472,6 +474,7 @@ int bwd_prep_tpb(int logk) {
     case 12: return PrepCfg<12, 4, 6>::TPB;
     case 13: return PrepCfg<13, 4, 6>::TPB;
     case 14: return PrepCfg<14, 4, 6>::TPB;
+    case 15: return PrepCfg<15, 5, 7>::TPB;
     default: return 0;
   }
 }

@@ -7,28 +7,37 @@
 // dequantisation; 新智元 article, section 原生4比特盘算: dense compute suits
 // batched inference.
 //
-// Two kernels:
-//  * prefill (large M): 256x256 output tile per 256-thread workgroup, 2x2
-//    waves of 128x128, v_mfma_i32_32x32x32_i8, K staged 128 at a time through
-//    double-buffered LDS.  Packed 2-bit weights stay packed in LDS (a quarter
-//    of the bytes) and are expanded to int8 in registers right before the
-//    MFMA with one byte-permute lookup per dword; INT4 activation codes are
-//    likewise kept packed and sign-extended in registers.
+// Three kernel families:
+//  * prefill on the int8 instruction (INT8 codes; INT4 codes in format 4):
+//    256x256 output tile per workgroup, v_mfma_i32_32x32x32_i8, 4 waves of
+//    128x128 (INT8) or 8 waves of 128x64 (INT4).  K is staged BK = 128 (INT8)
+//    or 256 (INT4) codes at a time through a ring of three LDS stages filled
+//    by direct global-to-LDS copies.  Packed 2-bit weights stay packed in LDS
+//    (a quarter of the bytes) and are expanded to int8 in registers right
+//    before the MFMA with shifts and masks (wstep / wfield); INT4 activation
+//    codes likewise stay packed and each nibble is moved to the top of its
+//    byte (a4field).
+//  * prefill on the fp6 x fp4 instruction (INT4 codes in format 6, more than
+//    64 tokens): described with gemm_fp6_kernel below.
 //  * decode (M <= 64): weight streaming.  Every wave owns 16 output channels
-//    and one K slab, loads its packed weights with 16-byte loads straight into
-//    registers (each weight byte is read from HBM once), and runs
-//    v_mfma_i32_16x16x64_i8 with the channels on the MFMA's M side and up to
-//    16 tokens on its N side.  The K slabs of one channel block are reduced
-//    exactly in int32 by the last workgroup to finish, which also dequantises.
+//    (64 per workgroup above 32 tokens) and a share of the 256-k blocks of its
+//    K range; its packed weights are loaded with 16-byte loads straight into
+//    registers (each weight byte is read from HBM once), and
+//    v_mfma_i32_16x16x64_i8 runs with the channels on the MFMA's M side and 16
+//    tokens on its N side per token group.  When K is split, the partials of
+//    one channel tile are summed exactly in int32 by the last workgroup to
+//    finish, which also dequantises.  Up to 4 tokens, gemm_decode_few_kernel
+//    stages the codes once per workgroup in LDS instead.
 //
 // Inside one MFMA the pairing of A and B bytes is what matters: lane group g
 // (lanes 32g..32g+31, or 16g.. for 16x16x64) byte b of A meets byte b of B.
 // Both operands are therefore fed the same k for every (group, byte), and the
-// k order across the K loop is free.  Per 128-k stage, lane group g of the
-// 32x32x32 MFMA covers k-chunks 4g..4g+3 (16 k each), one chunk per MFMA step;
-// that makes every weight fragment one contiguous 16-byte read.
+// k order across the K loop is free.  Per 128-k half-stage, lane group g of
+// the 32x32x32 MFMA covers k-chunks 4g..4g+3 (16 k each), one chunk per MFMA
+// step; that makes every weight fragment one contiguous 16-byte read.
 #include <mutex>
 
+#include "copy_schedule.h"
 #include "mma.h"
 
 namespace hbl {
@@ -206,11 +215,16 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_prefill_kernel(
   // guarantees that all waves are done with stage kt-1, whose buffer is then
   // refilled with stage kt+2.
   constexpr int NL = A_LOADS + B_LOADS;   // copy instructions per wave per stage
+  using R = sched::Ring3;
+  static_assert(R::NBUF == 3 && R::AHEAD == 2, "the loop below unrolls a ring of three, two stages ahead");
+  static_assert(sched::ring_ok<R>(1, NL) && sched::ring_ok<R>(2, NL) && sched::ring_ok<R>(3, NL) &&
+                    sched::ring_ok<R>(4, NL) && sched::ring_ok<R>(7, NL) && sched::ring_ok<R>(256, NL),
+                "copy schedule: a wait leaves a needed copy in flight or a copy targets a buffer in use");
   const int KT = K / BK;
   auto phase = [&](int kt, int buf) {
-    if (kt + 1 < KT) wait_vmcnt<NL>(); else wait_vmcnt<0>();
+    if (kt + 1 < KT) wait_vmcnt<R::wait_steady(NL)>(); else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (kt + 2 < KT) dma(kt + 2, buf == 0 ? 2 : buf - 1);
+    if (kt + R::AHEAD < KT) dma(kt + R::AHEAD, R::write_buf(buf));
     compute(buf);
   };
   if (OUT != OUT_ACC_I32) row_scale_copy(dscale, m0, M, srow, wave, lane);
@@ -311,6 +325,13 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[F6_LDS];
   constexpr int A_LOADS = F6_A_STAGE / 16 / 256, B_LOADS = F6_B_PAIR / 16 / 256;   // 6 and 4
+  using S6 = sched::Fp6;
+  static_assert(S6::NBUF == F6_NBUF && S6::WAVES == 4 && S6::A_COPIES == A_LOADS && S6::B_COPIES == B_LOADS &&
+                    S6::MFMAS == 16,
+                "schedule model and kernel geometry agree");
+  static_assert(sched::fp6_ok<S6>(2) && sched::fp6_ok<S6>(4) && sched::fp6_ok<S6>(8) && sched::fp6_ok<S6>(20) &&
+                    sched::fp6_ok<S6>(256),
+                "copy schedule: a wait leaves a needed copy in flight or a copy targets a buffer in use");
 
   const int bid = blockIdx.x, total = tiles_m * tiles_n;
   const int logical = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
@@ -451,10 +472,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (u & 1) wait_vmcnt<2 * A_LOADS>(); else wait_vmcnt<2 * A_LOADS + B_LOADS>();
+    if (u & 1) wait_vmcnt<S6::wait(true)>(); else wait_vmcnt<S6::wait(false)>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-    const int akt = min(kt + F6_NBUF, KT - 1);
-    const int bp = min((kt + 3) >> 1, KP - 1);
+    const int akt = S6::a_stage(kt, KT);
+    const int bp = S6::b_pair(kt, KT);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const v8i af = aop(cur, 1, rb);
@@ -463,14 +484,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
         const int i = rb * 4 + cb;
         mfma(af, bf1[cb], acc[rb][cb]);
         read1(nxt, i, u + 1);
-        if (u & 1) {
-          // odd stage: B pair into the slot this pair of stages used, then A
-          if (i < B_LOADS) dmaB(i, bp, ((u + 3) >> 1) & 1);
-          else if (i < B_LOADS + A_LOADS) dmaA(i - B_LOADS, akt, u & (F6_NBUF - 1));
-        } else {
-          // even stage: the A_LOADS copies of stage kt+4 after MFMAs 1, 3, ..., 2*A_LOADS-1
-          if ((i & 1) && (i >> 1) < A_LOADS) dmaA(i >> 1, akt, u & (F6_NBUF - 1));
-        }
+        // odd stage: B pair into the slot this pair of stages used, then A;
+        // even stage: the A copies of stage kt+4 after MFMAs 1, 3, ..., 11
+        // (u is kt modulo a multiple of 4, or kt itself when K = 256)
+        const sched::Copy cp = S6::after(i, u & 1);
+        if (cp.kind == 2) dmaB(cp.j, bp, S6::b_slot(u));
+        else if (cp.kind == 1) dmaA(cp.j, akt, S6::a_buf(u));
         if (i >= 8 && !(i & 1)) bf0[(i - 8) >> 1] = bexp1(nxt, 0, (i - 8) >> 1);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -488,8 +507,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
     for (int j = 0; j < B_LOADS; ++j) dmaB(j, min(p, KP - 1), p);
   };
   if (OUT != OUT_ACC_I32) row_scale_copy(dscale, m0, M, srow, wave, lane);
-  dmaA_all(0); dmaB_all(0); dmaA_all(1); dmaA_all(2); dmaB_all(1); dmaA_all(3);
-  wait_vmcnt<3 * A_LOADS + B_LOADS>();     // A0 and B0 have landed
+#pragma unroll
+  for (int p = 0; p < S6::PROLOGUE; ++p) {    // A0 B0 A1 A2 B1 A3
+    const sched::Copy cp = S6::prologue(p);
+    if (cp.kind == 1) dmaA_all(cp.j); else dmaB_all(cp.j);
+  }
+  wait_vmcnt<S6::wait_prologue()>();       // A0 and B0 have landed
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 #pragma unroll
   for (int r = 0; r < 16; ++r) read1(f0, r, 0);
@@ -580,7 +603,7 @@ static DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
 // writes back and invalidates the whole L2 of the XCD, which cost the
 // 64-token forward 55 us instead of 21 us: every workgroup threw away the
 // activation codes the others were still reading).
-template <int BITS, int MB, int CPW, int NW, int OUT>
+template <int BITS, int MB, int CPW, int NW, int OUT, int KB1 = 8>
 __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int S,
@@ -590,11 +613,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
   // (two with four token groups: 8 waves of 184 registers, two per SIMD, so
   // one wave's MFMAs cover another's waits)
   // One 16-channel group (CPW == 1, K unsplit): blocks stream through a ring
-  // (below), at most 8 per wave (K <= 16384 with 8 waves).  Four groups
+  // (below), at most KB1 per wave (8: K <= 16384 with 8 waves; 16 up to
+  // 32768; only the unrolled loop grows, not the registers).  Four groups
   // (CPW == 4, K split four ways): two blocks per wave per round, all
   // requested at once (8 waves of ~160 registers, two per SIMD, so one wave's
   // MFMAs cover another's waits).
-  constexpr int MAXB = CPW == 1 ? 8 : 2;
+  constexpr int MAXB = CPW == 1 ? KB1 : 2;
   constexpr int CH = 16 * CPW;
   // Reduction over the waves (which split K): each wave stores its
   // accumulators, 16 bytes per lane per 16x16 block, into its own LDS slice,
@@ -1062,6 +1086,65 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const int32_t* __res
 }
 
 // ===========================================================================
+// Short rows (K = 64 or 128), any M.  The packed weights are then plain
+// row-major (K/4 bytes per channel), and one v_mfma_i32_16x16x64_i8 step
+// covers 64 k: lane group g takes weight word 4j + g (k = 64j + 16g .. +15)
+// and the same 16 codes of its token, both in natural order (wstep; INT4
+// nibbles moved to the top of each byte, a4field).  Each wave computes 16
+// channels x 64 tokens (four token groups), a 256-thread workgroup a 64 x 64
+// output tile, channel tiles fastest so that neighbouring workgroups share
+// their tokens' codes in L2.  At these K the outputs (2N bytes per token in
+// bf16) outweigh the codes (K or K/2 bytes), so this is a plain streaming
+// kernel: operands straight from global memory into registers, no LDS.
+template <int BITS, int KS, int OUT>
+__global__ __launch_bounds__(256) void gemm_smallk_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W,
+                                                          const float* __restrict__ dscale,
+                                                          const float* __restrict__ walpha, void* __restrict__ Y,
+                                                          int M, int N, int tiles_n) {
+  static_assert(KS == 64 || KS == 128, "short rows only");
+  constexpr int STEPS = KS / 64;
+  constexpr int AROW = KS * BITS / 8;            // code bytes per token
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int t0 = (int)(blockIdx.x / tiles_n) * 64;
+  const int ch0 = (int)(blockIdx.x % tiles_n) * 64 + 16 * wave;
+  if (ch0 >= N) return;                          // whole wave past the last channel (N % 16 == 0)
+  const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
+  const uint32_t* wrow = reinterpret_cast<const uint32_t*>(W + (size_t)(ch0 + c) * (KS / 4));
+  uint32_t wp[STEPS];
+#pragma unroll
+  for (int j = 0; j < STEPS; ++j) wp[j] = wrow[4 * j + g];
+  float ds[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) ds[mb] = OUT == OUT_ACC_I32 ? 0.f : dscale[min(t0 + 16 * mb + c, M - 1)];
+  v4i acc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    // tokens past M read token M-1's codes; their sums are never stored
+    const uint8_t* arow = A + (size_t)min(t0 + 16 * mb + c, M - 1) * AROW;
+    acc[mb] = v4i{};
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) {
+      v4i aop;
+      if constexpr (BITS == 8) {
+        aop = as_v4i(*reinterpret_cast<const uint4*>(arow + 64 * j + 16 * g));
+      } else {
+        // codes k0 .. k0+15: word 0 holds k0 .. k0+7 (k0+4h+i at bits 8i+4h), word 1 the next 8
+        const uint2 q = *reinterpret_cast<const uint2*>(arow + 32 * j + 8 * g);
+        aop = v4i{(int)a4field(q.x, 0), (int)a4field(q.x, 1), (int)a4field(q.y, 0), (int)a4field(q.y, 1)};
+      }
+      acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wstep(wp[j]), aop, acc[mb], 0, 0, 0);
+    }
+  }
+  // 16x16 accumulator layout: lane l / register r hold channel 4*(l/16)+r, token l%16
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int t = t0 + 16 * mb + c;
+    if (t < M) store_out4<OUT>(Y, (size_t)t * N + ch0 + 4 * g, unscale4<BITS>(acc[mb]), ds[mb] * aw);
+  }
+}
+
+// ===========================================================================
 // Host side
 
 // Split-K decode workspace: int32 partials [S][M][N], then one arrival
@@ -1090,9 +1173,18 @@ static void launch_decode_p(const GemmArgs& a, int S) {
   constexpr int CH = 16 * CPW;
   dim3 grid((a.N + CH - 1) / CH, S);
   int32_t* part = static_cast<int32_t*>(a.ws);
-  uint32_t* counts = MB > 1 && S > 1 && S <= kDecodeMaxSplit ? a.tile_count : nullptr;
-  hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, NW, OUT>), grid, dim3(64 * NW), 0, a.stream, a.codes,
-                     a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K, S, part, counts);
+  // only the four-group configuration hands its partials over in the kernel
+  uint32_t* counts = CPW > 1 && S > 1 && S <= kDecodeMaxSplit ? a.tile_count : nullptr;
+  bool long_rows = false;   // more than 8 blocks of 256 k per wave (K / S > 16384)
+  if constexpr (CPW == 1) {
+    long_rows = a.K / S > NW * 8 * DKB;
+    if (long_rows)
+      hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, NW, OUT, 16>), grid, dim3(64 * NW), 0, a.stream,
+                         a.codes, a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K, S, part, counts);
+  }
+  if (!long_rows)
+    hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, NW, OUT>), grid, dim3(64 * NW), 0, a.stream, a.codes,
+                       a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K, S, part, counts);
   if (S > 1 && counts == nullptr)
     hipLaunchKernelGGL((decode_reduce_kernel<BITS, OUT>), dim3((a.M * a.N + 255) / 256), dim3(256), 0, a.stream,
                        part, S, a.M, a.N, a.dscale, a.walpha, a.out);
@@ -1126,7 +1218,8 @@ static void launch_decode_few(const GemmArgs& a) {
 
 template <int BITS, int OUT>
 static void launch_decode_t(const GemmArgs& a) {
-  if (a.M <= 4) { launch_decode_few<BITS, OUT>(a); return; }
+  // (the few-token kernel stages all codes in LDS and streams at most 16384 k)
+  if (a.M <= 4 && a.K <= 16384) { launch_decode_few<BITS, OUT>(a); return; }
   const DecodePlan p = decode_plan(a.M, a.K, a.N);
   if (p.mb == 1) launch_decode_p<BITS, 1, 1, 8, OUT>(a, p.S);
   else if (p.mb == 2) launch_decode_p<BITS, 2, 1, 8, OUT>(a, p.S);
@@ -1150,8 +1243,20 @@ static void launch_prefill_t(const GemmArgs& a) {
 }
 
 template <int BITS, int OUT>
+static void launch_smallk(const GemmArgs& a) {
+  const int tm = (a.M + 63) / 64, tn = (a.N + 63) / 64;
+  if (a.K == 64)
+    hipLaunchKernelGGL((gemm_smallk_kernel<BITS, 64, OUT>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,
+                       a.dscale, a.walpha, a.out, a.M, a.N, tn);
+  else
+    hipLaunchKernelGGL((gemm_smallk_kernel<BITS, 128, OUT>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,
+                       a.dscale, a.walpha, a.out, a.M, a.N, tn);
+}
+
+template <int BITS, int OUT>
 static void launch_t(const GemmArgs& a) {
-  if (a.M <= 64) launch_decode_t<BITS, OUT>(a);
+  if (a.K < 256) launch_smallk<BITS, OUT>(a);
+  else if (a.M <= 64) launch_decode_t<BITS, OUT>(a);
   else launch_prefill_t<BITS, OUT>(a);
 }
 

@@ -38,7 +38,7 @@ int log2_exact(int64_t k) {
   return l;
 }
 
-constexpr int64_t kMinK = 256, kMaxK = 16384;
+constexpr int64_t kMinK = 64, kMaxK = 32768;
 
 hbl_status check_shape(int64_t M, int64_t K, int64_t N) {
   if (M < 0 || M >= (int64_t(1) << 31)) return HBL_ERR_SHAPE;
@@ -55,9 +55,9 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // Forward workspace: [codes][scales][matmul scratch].  The INT4 prefill
 // (M > kFp6MinM) keeps its codes in the six-bit operand layout of the fp6 x
 // fp4 matrix instruction.
-bool fp6_path(int bits, int64_t M) { return bits == 4 && M > hbl::kFp6MinM; }
+bool fp6_path(int bits, int64_t M, int64_t K) { return bits == 4 && M > hbl::kFp6MinM && K >= hbl::kFp6MinK; }
 size_t codes_bytes(int bits, int64_t M, int64_t K) {
-  return align256((size_t)M * K * (fp6_path(bits, M) ? 6 : bits) / 8);
+  return align256((size_t)M * K * (fp6_path(bits, M, K) ? 6 : bits) / 8);
 }
 size_t scales_bytes(int64_t M) { return align256((size_t)M * 4); }
 
@@ -131,7 +131,7 @@ hbl_status forward(int bits, bool rotate, const void* x, hbl_dtype x_dtype, cons
 
   // split-K decode shapes: prep clears the matmul's arrival counters, so the
   // matmul's last workgroup per tile reduces (no separate reduction launch)
-  const bool fp6 = fp6_path(bits, M);
+  const bool fp6 = fp6_path(bits, M, K);
   uint32_t* counts = hbl::gemm_tile_counter_ptr(gws, M, K, N);
 
   hbl::PrepArgs p{};
@@ -228,6 +228,7 @@ static hbl_status quantize_act(bool rotate, const void* x, hbl_dtype x_dtype, co
                                int64_t K, int bits, void* codes, float* dscale, hipStream_t stream) {
   if (!valid_dtype(x_dtype) || (bits != 8 && bits != 4 && bits != HBL_BITS_INT4_FP6)) return HBL_ERR_DTYPE;
   if (hbl_status s = check_shape(M, K, 16)) return s;
+  if (bits == HBL_BITS_INT4_FP6 && K < hbl::kFp6MinK) return HBL_ERR_SHAPE;
   if (M == 0) return HBL_OK;
   if (!x || !codes || !dscale) return HBL_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(dscale) || (gain && !aligned16(gain))) return HBL_ERR_ALIGN;
@@ -276,6 +277,7 @@ static hbl_status matmul(const void* codes, int bits, const float* dscale, const
                          void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (bits != 8 && bits != 4 && bits != HBL_BITS_INT4_FP6) return HBL_ERR_DTYPE;
   if (hbl_status s = check_shape(M, K, N)) return s;
+  if (bits == HBL_BITS_INT4_FP6 && K < hbl::kFp6MinK) return HBL_ERR_SHAPE;
   if (M == 0) return HBL_OK;
   if (!codes || !w_packed || !out) return HBL_ERR_NULL;
   if (out_kind != hbl::OUT_ACC_I32 && (!dscale || !w_alpha)) return HBL_ERR_NULL;

@@ -51,10 +51,14 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a);
 // INT4 on the fp6 x fp4 matrix instruction: codes in the fp6 operand layout
-// that prep mode 2 writes, [K/128][M][96].  The forward uses it for
-// M > kFp6MinM: the split decode matmul up to 64 tokens, the prefill matmul
-// beyond.
+// that prep mode 2 writes, [K/128][M][96].  Up to 64 tokens the split decode
+// matmul runs it, beyond that the prefill matmul; the INT4 forward takes this
+// path for M > kFp6MinM only (at 64 tokens and fewer the int8 decode matmul
+// measured faster).
 constexpr int kFp6MinM = 64;
+// The fp6 operand layout is blocked by 128 k and its matmul stages two such
+// blocks per step, so format 6 needs K >= 256 (shorter rows use format 4).
+constexpr int kFp6MinK = 256;
 hipError_t launch_gemm_fp6(const GemmArgs& a);
 // Workspace bytes the matmul needs beyond the codes and scales.
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);

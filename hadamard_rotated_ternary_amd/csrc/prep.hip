@@ -322,6 +322,8 @@ static hipError_t launch_prep_t(const PrepArgs& a) {
 hipError_t launch_prep(const PrepArgs& a) {
   const bool small = a.M <= 64;
   switch (a.logk) {
+    case 6:  return launch_prep_t<6, 4, 6>(a);
+    case 7:  return launch_prep_t<7, 4, 6>(a);
     case 8:  return launch_prep_t<8, 4, 6>(a);
     case 9:  return launch_prep_t<9, 5, 6>(a);
     case 10: return launch_prep_t<10, 5, 7>(a);
@@ -329,6 +331,8 @@ hipError_t launch_prep(const PrepArgs& a) {
     case 12: return launch_prep_t<12, 4, 6>(a);
     case 13: return small ? launch_prep_t<13, 4, 6>(a) : launch_prep_t<13, 5, 7>(a);
     case 14: return launch_prep_t<14, 5, 7>(a);
+    // one token per 1024-thread workgroup, 148 KiB of LDS: one workgroup per CU
+    case 15: return launch_prep_t<15, 5, 7>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -18,32 +18,36 @@ namespace hbl {
 
 // Row sums of |w| in fp64 in a fixed order: 64-column blocks, each summed
 // left to right, block sums added left to right.  One 256-thread workgroup
-// per row (K <= 16384, so at most 256 blocks): the row is staged through LDS
-// with coalesced 16-byte loads (blocks padded to 65 floats so the per-block
-// walks hit distinct banks), thread b sums block b, thread 0 adds the block
-// sums in order.
+// per row: the row is staged through LDS 16384 columns at a time with
+// coalesced 16-byte loads (blocks padded to 65 floats so the per-block walks
+// hit distinct banks), thread b sums block b of the chunk, and thread 0 adds
+// all block sums (at most 512, K <= 32768) in order.
 __global__ __launch_bounds__(256) void wrowsum_kernel(const float* __restrict__ w, int N, int K,
                                                      double* __restrict__ rowsum) {
+  constexpr int CHUNK = 16384;
   __shared__ float row[256 * 65];
-  __shared__ double bsum[256];
+  __shared__ double bsum[512];
   const int n = blockIdx.x, t = threadIdx.x;
-  const float4* src = reinterpret_cast<const float4*>(w + (size_t)n * K);
-  for (int i = t; i < K / 4; i += 256) {
-    const float4 v = src[i];
-    const int e = 4 * i, b = e >> 6, o = e & 63;
-    float* d = row + b * 65 + o;
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  for (int c0 = 0; c0 < K; c0 += CHUNK) {
+    const int len = K - c0 < CHUNK ? K - c0 : CHUNK;
+    const float4* src = reinterpret_cast<const float4*>(w + (size_t)n * K + c0);
+    for (int i = t; i < len / 4; i += 256) {
+      const float4 v = src[i];
+      const int e = 4 * i, b = e >> 6, o = e & 63;
+      float* d = row + b * 65 + o;
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    __syncthreads();
+    if (t < (len + 63) / 64) {
+      const int bl = len - 64 * t < 64 ? len - 64 * t : 64;
+      double acc = 0.0;
+      for (int o = 0; o < bl; ++o) acc += (double)fabsf(row[t * 65 + o]);
+      bsum[c0 / 64 + t] = acc;
+    }
+    __syncthreads();   // the row buffer is refilled by the next chunk
   }
-  __syncthreads();
-  const int nb = (K + 63) / 64;
-  if (t < nb) {
-    const int len = K - 64 * t < 64 ? K - 64 * t : 64;
-    double acc = 0.0;
-    for (int o = 0; o < len; ++o) acc += (double)fabsf(row[t * 65 + o]);
-    bsum[t] = acc;
-  }
-  __syncthreads();
   if (t == 0) {
+    const int nb = (K + 63) / 64;
     double acc = 0.0;
     for (int b = 0; b < nb; ++b) acc += bsum[b];
     rowsum[n] = acc;

@@ -28,8 +28,9 @@
  *     reported as HBL_ERR_LAUNCH.  Nothing aborts or throws across the ABI.
  *   - M == 0 is valid: after the dtype and shape checks the call returns
  *     HBL_OK without launching anything (pointers may then be NULL).
- *   - Shapes: K is a power of two with 256 <= K <= 16384; N % 16 == 0 and
- *     N > 0; 0 <= M < 2^31; M * max(K, N) < 2^40.
+ *   - Shapes: K is a power of two with 64 <= K <= 32768; N % 16 == 0 and
+ *     N > 0; 0 <= M < 2^31; M * max(K, N) < 2^40.  Codes in the fp6 operand
+ *     layout (bits = HBL_BITS_INT4_FP6) need K >= 256 (HBL_ERR_SHAPE below).
  *   - Alignment: every pointer must be 16-byte aligned (HBL_ERR_ALIGN).
  *   - The library keeps no mutable global state other than a per-device
  *     cache of device properties filled on first use; distinct streams may
@@ -42,11 +43,12 @@
  *       k0 + 4*j + i (i, j in 0..3) occupies bits 8*i + 2*j .. 8*i + 2*j + 1
  *       of the word of k0, with the 2-bit codes 0b00 = 0, 0b01 = +1,
  *       0b11 = -1 (0b10 never written).  The words are tiled: tiles of 16
- *       rows x 256 k (16 x 16 words, 1 KiB) in row-block-major order, and
- *       inside a tile the 16 words of each row contiguous, so word w of row
- *       n (k = 16w .. 16w+15) is word ((n/16)*(K/256) + w/16)*256 +
- *       (n%16)*16 + w%16.  (Sixteen rows' 64-byte segments of one 256-k
- *       block are one contiguous KiB, read whole by the matmuls.)
+ *       rows x TW k, TW = min(K, 256), in row-block-major order, and inside
+ *       a tile the TW/16 words of each row contiguous, so with T = TW/16 word
+ *       w of row n (k = 16w .. 16w+15) is word ((n/16)*(K/TW) + w/T)*16*T +
+ *       (n%16)*T + w%T.  (Sixteen rows' 64-byte segments of one 256-k block
+ *       are one contiguous KiB, read whole by the matmuls; for K <= 256 the
+ *       layout is plain row-major.)
  *   INT8 activation codes   int8 [M][K], two's complement.
  *   INT4 activation codes   uint8 [M][K/2]: for each row, one little-endian
  *       32-bit word per 8 consecutive k; the code of k0 + 4*j + i (i in 0..3,
@@ -63,7 +65,7 @@
  *       (b in 0..3; h, d0, d1 in 0..1).  This is the operand layout of the
  *       gfx950 fp6 x fp4 matrix instruction for the weights' packed order,
  *       blocked so that 128 k of consecutive tokens are contiguous; the INT4
- *       forward uses it internally for M > 32.
+ *       forward uses it internally for M > 64 and K >= 256.
  *   per-token dequant scales d   fp32 [M].
  *   per-tensor weight scale      fp32 [1] (alpha; the floor 1e-5 is applied on use).
  */
@@ -182,7 +184,7 @@ hbl_status hbl_forward_noalloc(int bits, const void *x, hbl_dtype x_dtype, const
  *     y = dequant( Q_act( RMSNorm(x) ) . W_t^T )
  * with the same quantisers, weights, formats and conventions as the H-BitLinear
  * forward.  bits is 8 or 4; the workspace is sized with HBL_OP_FORWARD_INT8 or
- * HBL_OP_FORWARD_INT4.  K must still be a power of two in [256, 16384].
+ * HBL_OP_FORWARD_INT4.  K must still be a power of two in [64, 32768].
  */
 hbl_status hbl_bitlinear_forward(const void *x, hbl_dtype x_dtype, const float *gain,
                                  const uint8_t *w_packed, const float *w_alpha,
@@ -221,7 +223,8 @@ hbl_status hbl_quantize_weights_rotated(const float *w, int64_t N, int64_t K,
  * Stage 1: RMSNorm -> Hadamard rotation -> per-token quantisation, one fused
  * kernel (新智元 article, section H-BitLinear模块: the transform is applied to
  * the activations before they are quantised).
- *   bits      8, 4 or HBL_BITS_INT4_FP6 (6: INT4 codes in the fp6 operand layout)
+ *   bits      8, 4 or HBL_BITS_INT4_FP6 (6: INT4 codes in the fp6 operand layout,
+ *             K >= 256)
  *   codes     INT8: int8 [M][K];  INT4: uint8 [M][K/2];  6: uint8 [K/128][M][96]
  *             (formats above)
  *   dscale    fp32 [M] per-token dequant scales d
@@ -234,7 +237,8 @@ hbl_status hbl_quantize_act(const void *x, hbl_dtype x_dtype, const float *gain,
  * Stage 2: ternary integer matmul of the codes with dequant epilogue.
  *   codes, dscale as written by hbl_quantize_act;  y [M][N] of y_dtype.
  *   bits      8 and 4 run on the int8 matrix instruction (any M); 6 runs on
- *             the fp6 x fp4 instruction (made for M > 32; any M works).
+ *             the fp6 x fp4 instruction (made for prefill token counts; any
+ *             M works, K >= 256).
  *   workspace at least hbl_workspace_bytes(HBL_OP_MATMUL, M, K, N) bytes (split-K
  *             scratch of the small-M path; may be NULL when that size is 0).
  *   Calls sharing one workspace must be stream-ordered.

@@ -20,21 +20,25 @@ def _ternary_words(wt: np.ndarray) -> np.ndarray:
 
 def pack_ternary(wt: np.ndarray) -> np.ndarray:
     """int8 [N][K] in {-1,0,1} -> the packed buffer, uint8 [N][K/4] in size:
-    the words of _ternary_words in tiles of 16 rows x 256 k (16 x 16 words,
-    1 KiB), tiles in row-block-major order, inside a tile row by row (the 16
-    words of a row contiguous).  N % 16 == 0 and K % 256 == 0."""
+    the words of _ternary_words in tiles of 16 rows x TW k, TW = min(K, 256)
+    (16 x TW/16 words), tiles in row-block-major order, inside a tile row by
+    row (the TW/16 words of a row contiguous).  For K <= 256 that is plain
+    row-major.  N % 16 == 0, K a multiple of 16 and of TW."""
     N, K = np.shape(wt)
-    if N % 16 or K % 256:
-        raise ValueError("tiled packing needs N % 16 == 0 and K % 256 == 0")
-    words = _ternary_words(wt).reshape(N // 16, 16, K // 256, 16)      # [row block, row, k block, word]
-    tiled = np.ascontiguousarray(words.transpose(0, 2, 1, 3))         # [row block, k block, row, word]
+    tw = min(K, 256)
+    if N % 16 or K % 16 or K % tw:
+        raise ValueError("tiled packing needs N % 16 == 0 and K a multiple of min(K, 256)")
+    words = _ternary_words(wt).reshape(N // 16, 16, K // tw, tw // 16)   # [row block, row, k block, word]
+    tiled = np.ascontiguousarray(words.transpose(0, 2, 1, 3))           # [row block, k block, row, word]
     return tiled.view(np.uint8).reshape(N, K // 4)
 
 
 def unpack_ternary(wp: np.ndarray, K: int) -> np.ndarray:
     wp = np.ascontiguousarray(wp, dtype=np.uint8)
     N = wp.size * 4 // K
-    words = wp.view(np.uint32).reshape(N // 16, K // 256, 16, 16).transpose(0, 2, 1, 3).reshape(N, K // 16, 1, 1)
+    tw = min(K, 256)
+    words = (wp.view(np.uint32).reshape(N // 16, K // tw, 16, tw // 16).transpose(0, 2, 1, 3)
+             .reshape(N, K // 16, 1, 1))
     shifts = (8 * np.arange(4)[None, :] + 2 * np.arange(4)[:, None]).astype(np.uint32)
     code = (words >> shifts) & 3
     if np.any(code == 2):

@@ -75,8 +75,11 @@ def test_forward_validation(L, bits):
     assert fwd(L, bits, ws=None) == NULL
     assert fwd(L, bits, xd=5) == DTYPE
     assert fwd(L, bits, yd=-1) == DTYPE
-    for K in (128, 300, 32768, 0):
+    # K: a power of two from 64 to 32768
+    for K in (32, 48, 300, 65536, 0):
         assert fwd(L, bits, K=K, wsb=1 << 40) == SHAPE
+    for K in (64, 128, 256, 32768):
+        assert fwd(L, bits, K=K, wsb=16) == WORKSPACE      # shape accepted, workspace checked next
     for N in (0, 8, 250):
         assert fwd(L, bits, N=N, wsb=1 << 40) == SHAPE
     assert fwd(L, bits, M=-1, wsb=1 << 40) == SHAPE
@@ -119,6 +122,11 @@ def test_stage_validation(L):
     assert L.hbl_gemm_ternary(A, 6, A, 65, 1024, 256, BAD, None, 0, S) == ALIGN   # fp6 prefill: no scratch
     assert L.hbl_gemm_ternary(A, 6, A, 64, 1024, 256, A, None, 0, S) == NULL      # fp6 split decode needs scratch
     assert L.hbl_matmul_dequant(A, 8, None, A, A, 100, 256, 256, A, 1, None, 0, S) == NULL
+    # format 6 needs K >= 256 (the fp6 operand is blocked by 128 k, two blocks per step)
+    assert L.hbl_quantize_act(A, 1, None, 4, 128, 6, A, A2, S) == SHAPE
+    assert L.hbl_gemm_ternary(A, 6, A, 100, 128, 256, A, None, 0, S) == SHAPE
+    assert L.hbl_quantize_act(A, 1, None, 4, 128, 4, BAD, A2, S) == ALIGN      # format 4 at K = 128 is fine
+    assert L.hbl_gemm_ternary(A, 4, A, 100, 64, 256, BAD, None, 0, S) == ALIGN
     assert L.hbl_quantize_weights(A, 256, 255, A, A, A, 1 << 20, S) == SHAPE
     assert L.hbl_quantize_weights(A, 256, 256, A, A, A, 8, S) == WORKSPACE
     assert L.hbl_unpack_weights(A, 16, 256, None, S) == NULL
@@ -153,6 +161,19 @@ def test_layout_codecs_hand_examples():
     assert np.flatnonzero(words).tolist() == [(1 * 2 + 1) * 256 + 1 * 16 + 3] and words[(1 * 2 + 1) * 256 + 19] == 1
     with pytest.raises(ValueError):
         pack_ternary(np.zeros((8, 256), np.int8))
+    # K < 256: one tile spans the row, so the layout is plain row-major
+    for K in (64, 128):
+        wt = np.random.default_rng(K).integers(-1, 2, (32, K)).astype(np.int8)
+        words = pack_ternary(wt).view(np.uint32).reshape(32, K // 16)
+        for n in (0, 5, 17, 31):
+            for w in range(K // 16):
+                expect = 0
+                for j in range(4):
+                    for i in range(4):
+                        c = int(wt[n, 16 * w + 4 * j + i])
+                        expect |= (1 if c == 1 else 3 if c == -1 else 0) << (8 * i + 2 * j)
+                assert words[n, w] == expect
+        np.testing.assert_array_equal(unpack_ternary(pack_ternary(wt), K), wt)
     # int4: code of k (=4j+i) at bits 8i+4j
     q = np.array([[1, -1, 7, -8, 2, 0, 0, 3]], np.int8)
     w = pack_int4(q).view(np.uint32)[0, 0]

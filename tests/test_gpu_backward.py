@@ -132,6 +132,22 @@ def test_backward_matches_oracle(name, bits, M, rotate):
     assert rel_l2(dg, rdg) <= 2e-5
 
 
+@pytest.mark.parametrize("K,N,M,bits", [(64, 64, 50, 8), (128, 96, 70, 4), (32768, 64, 5, 4)])
+def test_backward_short_and_long_rows(K, N, M, bits):
+    """The shortest and longest rows the library takes (K = 64, 128, 32768):
+    the transposed bf16 weights bit-exact, dx, dW and dgain against the
+    oracle at the bars above."""
+    w = synthetic.Workload("t", M, K, N, bits, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, K + N + M)
+    s = setup(w, bits, dy_seed=K)
+    wbt, dx, dw, dg = run_gpu(s, bits)
+    got = host(wbt.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(got, synthetic.f32_to_bf16_bits(s["wt"].T.astype(np.float32)))
+    rdx, rdw, rdg, _ = oracle_bwd(s, True)
+    check_dx(dx, rdx)
+    check_dw(dw, rdw, s["q"], s["d32"], s["dyf"])
+    assert rel_l2(dg, rdg) <= 2e-5
+
+
 def test_backward_no_gain_bf16_dx_fp32_x():
     w = synthetic.WORKLOADS["wo_1p3b_int4"]
     s = setup(w, 4, M=65, gain=False)

@@ -85,7 +85,8 @@ def pack_codes(q, bits):
 
 # ------------------------------------------------------------------ weights
 
-@pytest.mark.parametrize("N,K", [(16, 256), (272, 2048), (4096, 4096), (3072, 8192), (4096, 16384)])
+@pytest.mark.parametrize("N,K", [(16, 64), (48, 128), (16, 256), (272, 2048), (4096, 4096), (3072, 8192), (4096, 16384),
+                                 (272, 32768)])
 def test_weight_ternarisation(N, K):
     """alpha within one fp32 ulp of the oracle's (the GPU sums |W| in fp64 in
     another order; both are far more precise than fp32); codes exactly the
@@ -122,7 +123,7 @@ def test_weight_ternarisation_ties_and_zero():
 
 # ------------------------------------------------------------------ rotation and quantisation
 
-KS = [256, 512, 1024, 2048, 4096, 8192, 16384]
+KS = [64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768]
 
 
 def make_x(M, K, seed, dist="laplace", bf16=True):
@@ -147,6 +148,8 @@ def test_rotation_matches_oracle(K, M):
 @pytest.mark.parametrize("bits", [8, 4, 6])
 @pytest.mark.parametrize("M", [1, 5, 64, 129])
 def test_codes_match_oracle(K, bits, M):
+    if bits == 6 and K < 256:
+        pytest.skip("format 6 needs K >= 256")
     x, xb = make_x(M, K, 7 * K + M, dist="normal" if K % 3 else "laplace", bf16=(M != 5))
     codes, d = hbl.quantize_act(x_to_dev(x, xb), bits)
     q = gpu_codes_unpacked(codes, bits, K)
@@ -199,8 +202,15 @@ def test_zero_token_and_tiny_token():
 @pytest.mark.parametrize("M,K,N", [(1, 256, 16), (2, 1024, 48), (4, 16384, 272), (3, 8192, 4096),
                                    (7, 512, 272), (16, 2048, 512), (20, 4096, 272), (32, 16384, 528), (33, 4096, 64),
                                    (64, 16384, 128), (65, 256, 256), (300, 1024, 272), (512, 2048, 512),
-                                   (257, 16384, 528)])
+                                   (257, 16384, 528),
+                                   # short rows (one matmul kernel for every M) and the longest rows
+                                   (1, 64, 16), (5, 64, 48), (64, 64, 272), (65, 64, 80), (300, 64, 272),
+                                   (3, 128, 16), (70, 128, 528), (129, 128, 64),
+                                   (1, 32768, 272), (3, 32768, 64), (20, 32768, 272), (40, 32768, 528),
+                                   (300, 32768, 256)])
 def test_matmul_bit_exact(bits, M, K, N):
+    if bits == 6 and K < 256:
+        pytest.skip("format 6 needs K >= 256")
     rng = np.random.default_rng(M * 7 + K + N + bits)
     lo, hi = (-128, 128) if bits == 8 else (-8, 8)
     q = rng.integers(lo, hi, (M, K)).astype(np.int8)
@@ -259,7 +269,9 @@ def check_layer(yh, y_ref, ref, tol=2e-3, tie_tol=1e-4):
 
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("M,K,N", [(8, 256, 256), (1, 16384, 4096), (17, 4096, 272), (32, 16384, 4096), (64, 8192, 512),
-                                   (300, 2048, 272), (513, 16384, 256)])
+                                   (300, 2048, 272), (513, 16384, 256),
+                                   (8, 64, 256), (100, 64, 48), (3, 128, 272), (300, 128, 272),
+                                   (1, 32768, 272), (40, 32768, 272), (300, 32768, 256)])
 def test_layer_small(bits, M, K, N):
     w = synthetic.Workload("t", M, K, N, bits, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, M + K + N)
     yh, y_ref, ref, xd, wp, a, rows = run_layer(w)
@@ -304,10 +316,12 @@ def gaussian_workload(M, K, N, bits, seed, xdt="bf16"):
     return synthetic.Workload("g", M, K, N, bits, xdt, "normal", 1.0, 1, 1.0, seed)
 
 
-@pytest.mark.parametrize("K", [256, 2048, 16384])
+@pytest.mark.parametrize("K", [64, 256, 2048, 16384, 32768])
 @pytest.mark.parametrize("bits", [8, 4, 6])
 @pytest.mark.parametrize("M", [1, 5, 129])
 def test_unrotated_codes_match_oracle(K, bits, M):
+    if bits == 6 and K < 256:
+        pytest.skip("format 6 needs K >= 256")
     w = gaussian_workload(M, K, 16, 4, 3 * K + M + bits)
     x, xb, _ = synthetic.make_inputs(w, with_weights=False)
     codes, d = hbl.quantize_act(x_to_dev(x, xb), bits, rotate=False)
@@ -320,7 +334,7 @@ def test_unrotated_codes_match_oracle(K, bits, M):
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("M,K,N", [(1, 16384, 4096), (3, 8192, 272), (4, 8192, 48), (3, 16384, 272),
                                    (4, 16384, 96), (16, 4096, 512), (64, 2048, 256), (300, 4096, 528),
-                                   (2048, 4096, 4096)])
+                                   (2048, 4096, 4096), (100, 64, 272), (5, 128, 48), (2, 32768, 272)])
 def test_unrotated_layer(bits, M, K, N):
     """BitLinear without the transform (one-launch decode while M * K <= 49152,
     decode, int8 and fp6 prefill matmuls) against the oracle at the layer bar."""
@@ -349,7 +363,8 @@ def check_ternary_near_ties(wt_gpu, wt_or, ratio_or, tie_tol=1e-5, max_frac=1e-4
     assert n <= max(1, max_frac * wt_or.size), f"{n} of {wt_or.size}"
 
 
-@pytest.mark.parametrize("N,K", [(16, 256), (272, 2048), (4096, 4096), (3072, 8192), (512, 16384)])
+@pytest.mark.parametrize("N,K", [(16, 64), (16, 256), (272, 2048), (4096, 4096), (3072, 8192), (512, 16384),
+                                 (64, 32768)])
 def test_rotated_weights_match_oracle(N, K):
     rng = np.random.default_rng(N + K)
     w = rng.normal(0, 0.02, (N, K)).astype(np.float32)

@@ -361,8 +361,28 @@ def tiny_extra(torch, hbl, synthetic):
     e1.record()
     torch.cuda.synchronize()
     us = 1e3 * e0.elapsed_time(e1) / 200
+    # the same calls replayed from a captured graph (device time, no host launch cost)
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        hbl.forward(xd, wp, a, 8, workspace=ws, out=y)
+    torch.cuda.current_stream().wait_stream(s_)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(40):
+            hbl.forward(xd, wp, a, 8, workspace=ws, out=y)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    gus = 1e3 * e0.elapsed_time(e1) / 400
     return {"M": w.M, "K": w.K, "N": w.N, "forward_us": us, "tokens_per_s": w.M / (us / 1e6),
-            "timing": "events around 200 back-to-back calls (host launch rate included)"}
+            "forward_us_graph": gus, "tokens_per_s_graph": w.M / (gus / 1e6),
+            "timing": "events around 200 back-to-back calls (host launch rate included); graph: 40 calls "
+                      "replayed 10 times"}
 
 
 def extras(torch, hbl, synthetic, args):
@@ -449,6 +469,39 @@ def extras(torch, hbl, synthetic, args):
                                   "gemm_hbm_frac": gbytes / (res["gemm"] / 1e6) / 1e9 / PEAK_HBM_GBS,
                                   "forward_us": res["forward"], "tokens_per_s": M / (res["forward"] / 1e6),
                                   "timing": f"graph replay of {R} back-to-back calls over {R} weight copies"}
+    # the box's floor for these shapes: a plain read of one 16 MiB weight copy
+    # per call (a torch max-reduction over it; the value is not used) in the
+    # same graph-replay harness over the same 40 copies
+    red = torch.empty((), dtype=torch.int64, device="cuda")
+
+    def read_body(i):
+        torch.amax(wps[i % R].view(torch.int64).view(-1), dim=0, out=red)
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        for i in range(3):
+            read_body(i)
+    torch.cuda.current_stream().wait_stream(s_)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(R):
+            read_body(i)
+    g.replay()
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(10):
+        g.replay()
+    f1.record()
+    torch.cuda.synchronize()
+    read_us = 1e3 * f0.elapsed_time(f1) / (10 * R)
+    wbytes = base.N * base.K / 4
+    out["plain_read_16mib"] = {"us": read_us, "gbps": wbytes / (read_us / 1e6) / 1e9,
+                               "hbm_frac": wbytes / (read_us / 1e6) / 1e9 / PEAK_HBM_GBS,
+                               "timing": f"graph replay of {R} torch max-reductions, one {R}-way rotated weight "
+                                         "copy each (the read floor of the decode matmul's weight stream)"}
+    for M in (1, 16, 64):
+        out[f"decode_7b_m{M}"]["gemm_over_plain_read"] = out[f"decode_7b_m{M}"]["gemm_us"] / read_us
     out["decode_attn_7b_kv3"] = attention_extra(torch, hbl, synthetic, args)
     out["backward_wdown_7b_int4"] = backward_extra(torch, hbl, synthetic, args)
     return out

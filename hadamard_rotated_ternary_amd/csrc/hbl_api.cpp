@@ -163,6 +163,7 @@ const char* hbl_status_string(hbl_status s) {
     case HBL_ERR_LAUNCH: return "kernel launch failed";
     case HBL_ERR_DEVICE: return "no gfx950 device";
     case HBL_ERR_SCRATCH: return "problem needs more scratch than the no-alloc forward's static array";
+    default: break;
   }
   return "unknown status";
 }

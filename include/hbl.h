@@ -89,11 +89,20 @@ typedef enum {
     HBL_ERR_WORKSPACE = 5,  /* workspace smaller than hbl_workspace_bytes() */
     HBL_ERR_LAUNCH = 6,     /* the HIP runtime reported an error at launch */
     HBL_ERR_DEVICE = 7,     /* no current device, or it is not gfx950 */
-    HBL_ERR_SCRATCH = 8     /* hbl_forward_noalloc: the problem needs more than
+    HBL_ERR_SCRATCH = 8,    /* hbl_forward_noalloc: the problem needs more than
                                HBL_NOALLOC_SCRATCH_BYTES of scratch */
+    /* range markers, never returned: with them every int is a value of the
+       type, so C++ code may hold any value a C caller passes */
+    HBL_STATUS_RANGE_MIN_ = -2147483647 - 1, HBL_STATUS_RANGE_MAX_ = 2147483647
 } hbl_status;
 
-typedef enum { HBL_F32 = 0, HBL_BF16 = 1 } hbl_dtype;
+/* Element types.  Any other value is rejected with HBL_ERR_DTYPE; the range
+ * markers (never valid arguments) make every int a value of the type, so that
+ * rejection is well defined in the C++ implementation. */
+typedef enum {
+    HBL_F32 = 0, HBL_BF16 = 1,
+    HBL_DTYPE_RANGE_MIN_ = -2147483647 - 1, HBL_DTYPE_RANGE_MAX_ = 2147483647
+} hbl_dtype;
 
 /* Activation code formats (the `bits` argument of the stage calls). */
 enum { HBL_BITS_INT4 = 4, HBL_BITS_INT4_FP6 = 6, HBL_BITS_INT8 = 8 };

@@ -628,7 +628,28 @@ def cpu_baseline(x, wl, bits, budget_s):
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of {x.shape[0]} tokens of the same workload (INT{bits}), {dt:.1f} s wall",
-            "cpu": cpu_model()}
+            "cpu": cpu_model(), "single_thread": single_thread_baselines(oracle)}
+
+
+def single_thread_baselines(oracle):
+    """The oracle on one thread for the smallest configuration (8 tokens,
+    K = N = 256, INT8, fp32) and one-token decode (K = 16384, N = 4096,
+    INT4), each repeated to about half a second."""
+    import synthetic
+    out = {}
+    for name in ("tiny_int8", "decode_7b_m1"):
+        w = synthetic.WORKLOADS[name]
+        x, _, wl = synthetic.make_inputs(w)
+        wt, alpha = oracle.quantize_weights(wl)
+        reps, dt = 0, 0.0
+        t0 = time.perf_counter()
+        while dt < 0.5 or reps < 2:
+            oracle.forward(x, wt, alpha, w.bits, keep=False, nthreads=1)
+            reps += 1
+            dt = time.perf_counter() - t0
+        out[name] = {"tokens_per_s": reps * w.M / dt, "ms_per_call": 1e3 * dt / reps, "calls": reps,
+                     "M": w.M, "K": w.K, "N": w.N, "bits": w.bits, "threads": 1}
+    return out
 
 
 def cpu_model() -> str:

@@ -53,30 +53,52 @@ __global__ __launch_bounds__(256) void wbt_kernel(const uint8_t* __restrict__ wp
 // Token-last copies for the weight gradient, through 64 x 64 LDS tiles:
 //   dyT[n][m] = dy[m][n]               (bf16)
 //   xhT[k][m] = bf16(q[m][k] * d[m])    (codes INT8 [M][K] or INT4 [M][K/2])
-// m runs to Mp (a multiple of 64); columns past M are zero.  Loads read 16
-// bytes per lane along a source row; stores write 16 bytes (8 tokens) per
-// lane along a destination row.  C % 8 == 0 (C is N or K here).
+// m runs to Mp (a multiple of 64); columns past M are zero.  C % 8 == 0 (C
+// is N or K here).
+//
+// The tile is held transposed, as token pairs: LDS row c holds 32 dwords,
+// dword p = tokens 2p (low half) and 2p+1 (high half) of column c, so the
+// transpose itself happens in registers and every LDS access is a whole
+// dword or a 16-byte chunk (a first version moved single bf16 values down
+// LDS columns and spent 40-50 % of its cycles on bank conflicts).  Rows are
+// 36 dwords apart (8 rows = 288 dwords = 32 banks apart) and row r's 16-byte
+// chunks are rotated by 2 * ((r >> 4) & 3), which makes both phases
+// conflict-free: a dword write instruction covers rows 8j + e (j = 0..7) at
+// 8 consecutive pair columns, 64 distinct banks; a chunk read instruction
+// gives 8 lanes the 8 chunks of one row and the next 8 lanes those of the
+// row 8 further on, the other half of the banks.
+// Load: lane L of wave w takes columns 8 (L % 8) .. +7 of tokens
+// 2 (L / 8 + 8 w) and the next (16 contiguous bytes of bf16 per lane,
+// coalesced along the source row).  Store: 16 bytes (8 tokens) per lane
+// along a destination row.
 template <int KIND>   // 0: dy (bf16), 8: INT8 codes, 4: INT4 codes
 __global__ __launch_bounds__(256) void tr_kernel(const void* __restrict__ src, const float* __restrict__ dscale,
                                                  int M, int C, int Mp, uint16_t* __restrict__ dst) {
-  __shared__ uint16_t tile[64][72];   // [m][c], rows padded to 144 bytes
+  constexpr int P = 36;                       // dwords per LDS row
+  __shared__ __attribute__((aligned(16))) uint32_t tile[64 * P];
   const int c0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
-  // load: 8 columns (16 bytes of bf16 / 8 bytes of int8 / 4 bytes of int4) per item
-  for (int it = threadIdx.x; it < 64 * 8; it += 256) {
-    const int mr = it >> 3, cg = (it & 7) * 8;
-    const int m = m0 + mr, c = c0 + cg;
-    uint16_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (m < M && c < C) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto rot = [](int r) { return 8 * ((r >> 4) & 3); };   // dword rotation of row r (two chunks per step)
+  // ---- load one token pair x 8 columns
+  const int cg = lane & 7, pp = (lane >> 3) + 8 * wave;   // column group, token pair
+  const int cc = c0 + 8 * cg;
+  uint16_t v[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int m = m0 + 2 * pp + h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[h][e] = 0;
+    if (m < M && cc < C) {
       if constexpr (KIND == 0) {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (size_t)m * C + c);
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (size_t)m * C + cc);
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { v[2 * e] = (uint16_t)w[e]; v[2 * e + 1] = (uint16_t)(w[e] >> 16); }
+        for (int e = 0; e < 4; ++e) { v[h][2 * e] = (uint16_t)w[e]; v[h][2 * e + 1] = (uint16_t)(w[e] >> 16); }
       } else {
         const float dm = dscale[m];
         int q[8];
         if constexpr (KIND == 8) {
-          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(src) + (size_t)m * C + c);
+          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(src) + (size_t)m * C + cc);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             q[e] = (int)(int8_t)(u.x >> (8 * e));
@@ -85,31 +107,32 @@ __global__ __launch_bounds__(256) void tr_kernel(const void* __restrict__ src, c
         } else {
           // INT4: one LE word per 8 k; code of k0 + 4j + i at bits 8i + 4j
           const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(src) +
-                                                                (size_t)m * (C / 2) + c / 2);
+                                                                (size_t)m * (C / 2) + cc / 2);
 #pragma unroll
           for (int e = 0; e < 8; ++e) q[e] = ((int)(((u >> (8 * (e & 3) + 4 * (e >> 2))) & 15u) << 28)) >> 28;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16((float)q[e] * dm);
+        for (int e = 0; e < 8; ++e) v[h][e] = f32_to_bf16((float)q[e] * dm);
       }
     }
-    uint4 pk;
-    pk.x = v[0] | ((uint32_t)v[1] << 16); pk.y = v[2] | ((uint32_t)v[3] << 16);
-    pk.z = v[4] | ((uint32_t)v[5] << 16); pk.w = v[6] | ((uint32_t)v[7] << 16);
-    *reinterpret_cast<uint4*>(&tile[mr][cg]) = pk;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = 8 * cg + e;
+    tile[r * P + ((pp + rot(r)) & 31)] = (uint32_t)v[0][e] | ((uint32_t)v[1][e] << 16);
   }
   __syncthreads();
-  // store: destination row c0 + cr, tokens m0 + mg .. +7
-  for (int it = threadIdx.x; it < 64 * 8; it += 256) {
-    const int cr = it >> 3, mg = (it & 7) * 8;
-    const int c = c0 + cr;
-    if (c >= C) continue;
-    uint4 pk;
-    pk.x = tile[mg + 0][cr] | ((uint32_t)tile[mg + 1][cr] << 16);
-    pk.y = tile[mg + 2][cr] | ((uint32_t)tile[mg + 3][cr] << 16);
-    pk.z = tile[mg + 4][cr] | ((uint32_t)tile[mg + 5][cr] << 16);
-    pk.w = tile[mg + 6][cr] | ((uint32_t)tile[mg + 7][cr] << 16);
-    *reinterpret_cast<uint4*>(dst + (size_t)c * Mp + m0 + mg) = pk;
+  // ---- store: instruction j of wave w covers rows b, b+8, b+1, b+9, ..., b+3, b+11
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int idx = wave + 4 * j;
+    const int b = 16 * (idx >> 1) + 4 * (idx & 1);
+    const int g = lane >> 3;                              // 0..7
+    const int r = b + (g >> 1) + 8 * (g & 1);
+    const int k = lane & 7;                               // chunk: tokens 8k .. 8k+7
+    const int c = c0 + r;
+    const uint4 val = *reinterpret_cast<const uint4*>(&tile[r * P + ((4 * k + rot(r)) & 31)]);
+    if (c < C) *reinterpret_cast<uint4*>(dst + (size_t)c * Mp + m0 + 8 * k) = val;
   }
 }
 
@@ -118,14 +141,16 @@ __global__ __launch_bounds__(256) void tr_kernel(const void* __restrict__ src, c
 // 256 x 256 tile per workgroup (8 waves of 64 x 128, each 2 x 4
 // v_mfma_f32_32x32x16_bf16 tiles; 4 waves of 128 x 128 also build), 32 c per stage in a three-deep LDS ring
 // filled by global_load_lds_dwordx4 (each stage requested two ahead).  Rows
-// of 64 bytes, 16-byte units XOR-swizzled so the fragment reads (16 lanes:
-// rows r..r+15 of one unit column) and the copies hit distinct banks.
+// of 64 bytes, 16-byte units XOR-swizzled by row bits 2-3, which the
+// bank-conflict counter shows conflict-free for the fragment reads (rows
+// r..r+31 of one unit column, both k halves); a swizzle by row bits 1 and 3
+// spent 100 M conflict cycles per 1 ms product (20 % of its LDS cycles).
 #ifndef HBL_BF16_NW
 #define HBL_BF16_NW 8   // waves per workgroup of the bf16 product (4 or 8)
 #endif
 constexpr int GT = 256, GBK = 32, GROW = GBK * 2, GUNITS = GROW / 16;
 constexpr int G_A_STAGE = GT * GROW, G_STAGE = 2 * G_A_STAGE;
-HBL_DEV int gswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+HBL_DEV int gswz(int row) { return (row >> 2) & 3; }
 
 // NW = 4: 2 x 2 waves of 128 x 128 (one wave per SIMD); NW = 8: 4 x 2 waves
 // of 64 x 128, whose accumulators take half the registers, so two waves

@@ -64,12 +64,14 @@ struct PCfg {
 };
 
 // XOR swizzles of the 16-byte units of an LDS row (U units per row), chosen
-// so that the MFMA fragment reads (8 or 16 lanes per LDS cycle: rows r..r+7 or
-// r..r+15 of one unit column) and the copies hit distinct banks.
+// so that the MFMA fragment reads (rows r..r+31 of one unit column) and the
+// copies hit distinct banks.  Rows of 4 units swizzle by row bits 2-3: the
+// bank-conflict counter shows that conflict-free, while bits 1 and 3 (the
+// former choice) conflicted on every read.
 template <int U>
 HBL_DEV int swz(int row) {
   if constexpr (U == 8) return (row ^ (row >> 3)) & 7;
-  else if constexpr (U == 4) return ((row >> 1) ^ (row >> 3)) & 3;
+  else if constexpr (U == 4) return (row >> 2) & 3;
   else return ((row >> 2) ^ (row >> 3)) & 1;
 }
 

@@ -72,6 +72,27 @@ struct Fp6 {
   static constexpr int wait_prologue() { return 3 * A_COPIES + B_COPIES; }
 };
 
+// gemm_fp6_kernel with 128x128 tiles (four waves of 64x64): an A stage is 3
+// copies per wave and a B pair 2; the second MFMA step has 4 matrix
+// instructions with two issue slots after each (8 slots): even stages take
+// the A copies in slots 1, 3, 5; odd stages the B copies in slots 0-1 and the
+// A copies in slots 2-4.  Buffers, slots, stage choice and prologue as Fp6.
+struct Fp6Small : Fp6 {
+  static constexpr int A_COPIES = 3, B_COPIES = 2;
+  static constexpr int MFMAS = 8;                    // issue slots of the second step
+  static constexpr Copy after(int i, bool odd) {
+    if (odd) {
+      if (i < B_COPIES) return {2, i};
+      if (i < B_COPIES + A_COPIES) return {1, i - B_COPIES};
+      return {0, 0};
+    }
+    if ((i & 1) && (i >> 1) < A_COPIES) return {1, i >> 1};
+    return {0, 0};
+  }
+  static constexpr int wait(bool odd) { return odd ? 2 * A_COPIES : 2 * A_COPIES + B_COPIES; }
+  static constexpr int wait_prologue() { return 3 * A_COPIES + B_COPIES; }
+};
+
 // Issue log of one wave's copy instructions.
 struct Log {
   static constexpr int CAP = 4096;

@@ -36,6 +36,7 @@
 // the 32x32x32 MFMA covers k-chunks 4g..4g+3 (16 k each), one chunk per MFMA
 // step; that makes every weight fragment one contiguous 16-byte read.
 #include <mutex>
+#include <type_traits>
 
 #include "copy_schedule.h"
 #include "mma.h"
@@ -302,6 +303,20 @@ constexpr int F6_BPROW = 2 * F6_BK / 4;            // 64 bytes of packed weights
 constexpr int F6_B_PAIR = PBN * F6_BPROW;          // 16 KiB
 constexpr int F6_B_BASE = F6_NBUF * F6_A_STAGE;    // B slots after the A ring
 constexpr int F6_LDS = F6_B_BASE + 2 * F6_B_PAIR;  // 128 KiB
+// The same pipeline on T x T tiles (T = 256 above, or 128: four waves of
+// 64 x 64, for problems with fewer 256 x 256 tiles than compute units).
+template <int T>
+struct F6Geo {
+  static constexpr int RB = T / 64;                  // 32-row (and 32-column) blocks per wave
+  static constexpr int A_STAGE = T * F6_AROW;        // bytes of one A stage
+  static constexpr int B_PAIR = T * F6_BPROW;        // bytes of one B stage pair
+  static constexpr int B_BASE = F6_NBUF * A_STAGE;
+  static constexpr int LDS = B_BASE + 2 * B_PAIR;
+  static constexpr int A_LOADS = A_STAGE / 1024 / 4, B_LOADS = B_PAIR / 1024 / 4;
+  static constexpr int READS = RB + 3 * RB;          // LDS reads per stage: B blocks, then A units
+};
+static_assert(F6Geo<256>::LDS == F6_LDS && F6Geo<256>::A_STAGE == F6_A_STAGE && F6Geo<256>::B_PAIR == F6_B_PAIR,
+              "256-tile geometry");
 
 // gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16 consecutive
 // lanes per cycle, so 16 consecutive rows reading the same logical unit must
@@ -320,16 +335,19 @@ HBL_DEV void lds_copy16s(const void* gbase, uint32_t voff, uint32_t lds_base) {
 }
 
 // US: stages per loop trip (4; 2 when K = 256), so that LDS buffer numbers are
-// compile-time constants.
-template <int OUT, int US>
-__global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
+// compile-time constants.  T: tile size (256, or 128 with two workgroups per CU).
+template <int OUT, int US, int T = 256>
+__global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[F6_LDS];
-  constexpr int A_LOADS = F6_A_STAGE / 16 / 256, B_LOADS = F6_B_PAIR / 16 / 256;   // 6 and 4
-  using S6 = sched::Fp6;
+  using G = F6Geo<T>;
+  constexpr int RB = G::RB;                          // 32 x 32 blocks per wave: RB x RB
+  constexpr int WT = T / 2;                          // wave tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
+  constexpr int A_LOADS = G::A_LOADS, B_LOADS = G::B_LOADS;   // 6 and 4 (T = 256), 3 and 2 (T = 128)
+  using S6 = std::conditional_t<T == 256, sched::Fp6, sched::Fp6Small>;
   static_assert(S6::NBUF == F6_NBUF && S6::WAVES == 4 && S6::A_COPIES == A_LOADS && S6::B_COPIES == B_LOADS &&
-                    S6::MFMAS == 16,
+                    S6::MFMAS == (T == 256 ? 16 : 8),
                 "schedule model and kernel geometry agree");
   static_assert(sched::fp6_ok<S6>(2) && sched::fp6_ok<S6>(4) && sched::fp6_ok<S6>(8) && sched::fp6_ok<S6>(20) &&
                     sched::fp6_ok<S6>(256),
@@ -342,16 +360,16 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   const int first_m = (logical / per_group) * GM;
   const int gm = min(tiles_m - first_m, GM);
   const int in_g = logical % per_group;
-  const int m0 = (first_m + in_g % gm) * PBM;
-  const int n0 = (in_g / gm) * PBN;
-  __shared__ __attribute__((aligned(16))) float srow[PBM];   // epilogue row scales (row_scale_copy)
+  const int m0 = (first_m + in_g % gm) * T;
+  const int n0 = (in_g / gm) * T;
+  __shared__ __attribute__((aligned(16))) float srow[T];   // epilogue row scales (row_scale_copy)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, g = lane >> 5;
   // A is blocked by 128 k: stage kt of the tile is the contiguous run of
-  // 256 x 96 bytes at (kt * M + m0) * 96.
+  // T x 96 bytes at (kt * M + m0) * 96.
   const size_t a_stage = (size_t)M * F6_AROW;
   const uint8_t* a_tile = A + (size_t)m0 * F6_AROW;
   const uint8_t* b_tile = W + wrow_base(n0, K);     // n0 is a multiple of 16
@@ -377,17 +395,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   // A copy j (0..5) of stage kt into A buffer buf; B copy j (0..3) of stage
   // pair p into B slot sl
   auto dmaA = [&](int j, int kt, int buf) __attribute__((always_inline)) {
-    lds_copy16s(a_tile + (size_t)kt * a_stage, a_off[j], lds0 + buf * F6_A_STAGE + (j * 4 + wave_s) * 1024);
+    lds_copy16s(a_tile + (size_t)kt * a_stage, a_off[j], lds0 + buf * G::A_STAGE + (j * 4 + wave_s) * 1024);
   };
   auto dmaB = [&](int j, int p, int sl) __attribute__((always_inline)) {
-    lds_copy16s(b_tile + (size_t)p * 1024, b_off[j], lds0 + F6_B_BASE + sl * F6_B_PAIR + (j * 4 + wave_s) * 1024);
+    lds_copy16s(b_tile + (size_t)p * 1024, b_off[j], lds0 + G::B_BASE + sl * G::B_PAIR + (j * 4 + wave_s) * 1024);
   };
 
-  v16f acc[4][4];
+  v16f acc[RB][RB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < RB; ++j) acc[i][j] = v16f{};
 
   // Register fragments of one stage: per lane 48 A bytes (32-k groups 2g and
   // 2g+1 of four 32-row blocks), kept as one 12-dword vector per block so the
@@ -396,19 +414,19 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   // (the same groups of four 32-column blocks).  Read r of a stage: r < 4 the
   // B block r, else A block (r-4)/3, unit (r-4)%3.
   struct Frag {
-    v16i a[4];
-    v4i b[4];
+    v16i a[RB];
+    v4i b[RB];
   };
   // read r of stage kt (A buffer kt % 4, B slot (kt / 2) % 2, half kt % 2)
   auto read1 = [&](Frag& f, int r, int kt) __attribute__((always_inline)) {
-    const uint8_t* sa = smem + (kt & (F6_NBUF - 1)) * F6_A_STAGE;
-    if (r < 4) {
-      const int n = wn * 128 + r * 32 + l32;
-      const uint8_t* sb = smem + F6_B_BASE + ((kt >> 1) & 1) * F6_B_PAIR;
+    const uint8_t* sa = smem + (kt & (F6_NBUF - 1)) * G::A_STAGE;
+    if (r < RB) {
+      const int n = wn * WT + r * 32 + l32;
+      const uint8_t* sb = smem + G::B_BASE + ((kt >> 1) & 1) * G::B_PAIR;
       f.b[r] = *reinterpret_cast<const v4i*>(sb + n * F6_BPROW + 16 * ((2 * (kt & 1) + g) ^ f6_bswz(n)));
     } else {
-      const int rb = (r - 4) / 3, t = (r - 4) % 3;
-      const int row = wm * 128 + rb * 32 + l32;
+      const int rb = (r - RB) / 3, t = (r - RB) % 3;
+      const int row = wm * WT + rb * 32 + l32;
       int pu = 3 * g + t + f6_arot(row);
       if (pu >= 6) pu -= 6;
       const v4i x = *reinterpret_cast<const v4i*>(sa + row * F6_AROW + 16 * pu);
@@ -465,10 +483,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   auto stage = [&](int kt, int u, const Frag& cur, Frag& nxt, v8i* bf0, v8i* bf1) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       const v8i af = aop(cur, 0, rb);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < RB; ++cb) {
         mfma(af, bf0[cb], acc[rb][cb]);
         if (cb == 1) bf1[rb] = bexp1(cur, 1, rb);
         __builtin_amdgcn_sched_barrier(0);
@@ -479,20 +497,33 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
     const int akt = S6::a_stage(kt, KT);
     const int bp = S6::b_pair(kt, KT);
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       const v8i af = aop(cur, 1, rb);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int i = rb * 4 + cb;
+      for (int cb = 0; cb < RB; ++cb) {
+        const int i = rb * RB + cb;
         mfma(af, bf1[cb], acc[rb][cb]);
-        read1(nxt, i, u + 1);
-        // odd stage: B pair into the slot this pair of stages used, then A;
-        // even stage: the A copies of stage kt+4 after MFMAs 1, 3, ..., 11
-        // (u is kt modulo a multiple of 4, or kt itself when K = 256)
-        const sched::Copy cp = S6::after(i, u & 1);
-        if (cp.kind == 2) dmaB(cp.j, bp, S6::b_slot(u));
-        else if (cp.kind == 1) dmaA(cp.j, akt, S6::a_buf(u));
-        if (i >= 8 && !(i & 1)) bf0[(i - 8) >> 1] = bexp1(nxt, 0, (i - 8) >> 1);
+        if constexpr (T == 256) {
+          read1(nxt, i, u + 1);
+          // odd stage: B pair into the slot this pair of stages used, then A;
+          // even stage: the A copies of stage kt+4 after MFMAs 1, 3, ..., 11
+          // (u is kt modulo a multiple of 4, or kt itself when K = 256)
+          const sched::Copy cp = S6::after(i, u & 1);
+          if (cp.kind == 2) dmaB(cp.j, bp, S6::b_slot(u));
+          else if (cp.kind == 1) dmaA(cp.j, akt, S6::a_buf(u));
+          if (i >= 8 && !(i & 1)) bf0[(i - 8) >> 1] = bexp1(nxt, 0, (i - 8) >> 1);
+        } else {
+          // four MFMAs: two reads and two copy slots after each; the next
+          // stage's B expansion after the last two (its B reads came first)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            read1(nxt, 2 * i + h, u + 1);
+            const sched::Copy cp = S6::after(2 * i + h, u & 1);
+            if (cp.kind == 2) dmaB(cp.j, bp, S6::b_slot(u));
+            else if (cp.kind == 1) dmaA(cp.j, akt, S6::a_buf(u));
+          }
+          if (i >= 2) bf0[i - 2] = bexp1(nxt, 0, i - 2);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -508,7 +539,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j) dmaB(j, min(p, KP - 1), p);
   };
-  if (OUT != OUT_ACC_I32) row_scale_copy(dscale, m0, M, srow, wave, lane);
+  if (OUT != OUT_ACC_I32) row_scale_copy<T>(dscale, m0, M, srow, wave, lane);
 #pragma unroll
   for (int p = 0; p < S6::PROLOGUE; ++p) {    // A0 B0 A1 A2 B1 A3
     const sched::Copy cp = S6::prologue(p);
@@ -517,10 +548,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   wait_vmcnt<S6::wait_prologue()>();       // A0 and B0 have landed
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 #pragma unroll
-  for (int r = 0; r < 16; ++r) read1(f0, r, 0);
-  v8i bf0[4], bf1[4];
+  for (int r = 0; r < G::READS; ++r) read1(f0, r, 0);
+  v8i bf0[RB], bf1[RB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) bf0[cb] = bexp1(f0, 0, cb);
+  for (int cb = 0; cb < RB; ++cb) bf0[cb] = bexp1(f0, 0, cb);
   for (int kt = 0; kt < KT; kt += US) {
 #pragma unroll
     for (int u = 0; u < US; u += 2) {
@@ -537,22 +568,23 @@ __global__ __launch_bounds__(256, 1) void gemm_fp6_kernel(
   const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
   if constexpr (OUT == OUT_BF16) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");   // every wave is done with the ring
-    store_bf16_staged<4>(smem + wave * (64 * (4 * 64 + 32)), static_cast<uint16_t*>(Y), srow + wm * 128, aw, M, N,
-                         m0 + wm * 128, n0 + wn * 128, lane,
-                         [&](int rb, int cb, int r) { return acc[rb][cb][r]; });
+    static_assert(4 * 64 * (RB * 64 + 32) <= G::LDS, "staging fits the ring");
+    store_bf16_staged<RB, RB / 2>(smem + wave * (64 * (RB * 64 + 32)), static_cast<uint16_t*>(Y), srow + wm * WT, aw,
+                                  M, N, m0 + wm * WT, n0 + wn * WT, lane,
+                                  [&](int rb, int cb, int r) { return acc[rb][cb][r]; });
   } else {
     __syncthreads();
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rl = wm * 128 + rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int rl = wm * WT + rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
         const int m = m0 + rl;
         if (m >= M) continue;
         const float t = OUT == OUT_ACC_I32 ? 0.f : srow[rl] * aw;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const int n = n0 + wn * 128 + cb * 32 + l32;
+        for (int cb = 0; cb < RB; ++cb) {
+          const int n = n0 + wn * WT + cb * 32 + l32;
           if (n < N) store_out<OUT>(Y, (size_t)m * N + n, (int)acc[rb][cb][r], t);
         }
       }
@@ -1271,6 +1303,19 @@ static void launch_decode_fp6(const GemmArgs& a) {
   launch_decode_p<6, 4, 4, 8, OUT>(a, p.cpw == 4 ? p.S : 1);
 }
 
+constexpr int kFp6SmallTileBelow = 256;
+
+template <int OUT, int T>
+static void launch_fp6_t(const GemmArgs& a) {
+  const int tm = (a.M + T - 1) / T, tn = (a.N + T - 1) / T;
+  if (a.K == 256)
+    hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 2, T>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack, a.dscale,
+                       a.walpha, a.out, a.M, a.N, a.K, tm, tn);
+  else
+    hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 4, T>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack, a.dscale,
+                       a.walpha, a.out, a.M, a.N, a.K, tm, tn);
+}
+
 hipError_t launch_gemm_fp6(const GemmArgs& a) {
   if (a.M == 0) return hipSuccess;
   if (a.M <= 64) {
@@ -1281,20 +1326,14 @@ hipError_t launch_gemm_fp6(const GemmArgs& a) {
     }
     return hipGetLastError();
   }
-  const int tm = (a.M + PBM - 1) / PBM, tn = (a.N + PBN - 1) / PBN;
-#define HBL_F6(OUT)                                                                                          \
-  if (a.K == 256)                                                                                                \
-    hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 2>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,         \
-                       a.dscale, a.walpha, a.out, a.M, a.N, a.K, tm, tn);                                          \
-  else                                                                                                           \
-    hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 4>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,         \
-                       a.dscale, a.walpha, a.out, a.M, a.N, a.K, tm, tn)
+  // 256 x 256 tiles unless they would leave compute units idle (fewer tiles
+  // than the 256 CUs of the part): then 128 x 128 tiles, four times as many
+  const bool small = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256) < kFp6SmallTileBelow;
   switch (a.out_kind) {
-    case OUT_ACC_I32: HBL_F6(OUT_ACC_I32); break;
-    case OUT_F32: HBL_F6(OUT_F32); break;
-    default: HBL_F6(OUT_BF16); break;
+    case OUT_ACC_I32: small ? launch_fp6_t<OUT_ACC_I32, 128>(a) : launch_fp6_t<OUT_ACC_I32, 256>(a); break;
+    case OUT_F32: small ? launch_fp6_t<OUT_F32, 128>(a) : launch_fp6_t<OUT_F32, 256>(a); break;
+    default: small ? launch_fp6_t<OUT_BF16, 128>(a) : launch_fp6_t<OUT_BF16, 256>(a); break;
   }
-#undef HBL_F6
   return hipGetLastError();
 }
 

@@ -94,8 +94,8 @@ template <int BITS>
 HBL_DEV v4i unscale4(v4i v) { return v4i{unscale<BITS>(v[0]), unscale<BITS>(v[1]), unscale<BITS>(v[2]), unscale<BITS>(v[3])}; }
 
 
-// Row scales d of a 256-row output tile in LDS for the epilogue: waves 0-3
-// each copy 64 of them with one global-to-LDS instruction (lane L: row
+// Row scales d of a ROWS-row output tile in LDS for the epilogue: waves 0..
+// ROWS/64 - 1 each copy 64 of them with one global-to-LDS instruction (lane L: row
 // 64 * wave + L, clamped to the last row, so nothing past d[M-1] is read),
 // issued before the tile's first operand copies, so every later wait for
 // those copies also covers it and no register holds it through the main
@@ -103,12 +103,13 @@ HBL_DEV v4i unscale4(v4i v) { return v4i{unscale<BITS>(v[0]), unscale<BITS>(v[1]
 // dependent batches of loads, each a full memory latency with one wave per
 // SIMD, into every tile (9.7 us of a 107 us tile); a register-held d
 // lengthened the main loop instead.
+template <int ROWS = 256>
 HBL_DEV void row_scale_copy(const float* __restrict__ dscale, int m0, int M, float* srow, int wave, int lane) {
-  if (wave < 4) lds_copy4(dscale + min(m0 + 64 * wave + lane, M - 1), srow + 64 * wave);
+  if (wave < ROWS / 64) lds_copy4(dscale + min(m0 + 64 * wave + lane, M - 1), srow + 64 * wave);
 }
 
-// bf16 output of a wave's 128 x (32*CB) accumulator block through LDS: the
-// block is rounded into the wave's own LDS rows, 64 rows at a time, then
+// bf16 output of a wave's (64*HALVES) x (32*CB) accumulator block through
+// LDS: the block is rounded into the wave's own LDS rows, 64 rows at a time, then
 // written with 16-byte stores as whole row segments (instead of 2-byte
 // stores scattered over 64 rows).  getv(rb, cb, r) returns the unscaled
 // accumulator of 32x32 block (rb, cb), register r; lane l / register r hold
@@ -117,7 +118,7 @@ HBL_DEV void row_scale_copy(const float* __restrict__ dscale, int m0, int M, flo
 // two rows one store instruction touches start 32 banks apart.  The caller
 // makes sure no other wave still uses the stage area.  N % 16 == 0, so
 // 8-column chunks are either whole or outside.
-template <int CB, typename GetV>
+template <int CB, int HALVES = 2, typename GetV>
 HBL_DEV void store_bf16_staged(uint8_t* stage, uint16_t* Y, const float* srow, float aw, int M, int N, int mrow0,
                                int ncol0, int lane, GetV getv) {
   constexpr int ER = CB * 64 + 32;             // staged row bytes
@@ -125,7 +126,7 @@ HBL_DEV void store_bf16_staged(uint8_t* stage, uint16_t* Y, const float* srow, f
   constexpr int RPI = 64 / LPR;                // rows per store instruction
   const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
+  for (int hf = 0; hf < HALVES; ++hf) {
 #pragma unroll
     for (int rh = 0; rh < 2; ++rh) {
       const int rb = 2 * hf + rh;

@@ -207,7 +207,7 @@ def test_zero_token_and_tiny_token():
                                    (1, 64, 16), (5, 64, 48), (64, 64, 272), (65, 64, 80), (300, 64, 272),
                                    (3, 128, 16), (70, 128, 528), (129, 128, 64),
                                    (1, 32768, 272), (3, 32768, 64), (20, 32768, 272), (40, 32768, 528),
-                                   (300, 32768, 256)])
+                                   (300, 32768, 256), (200, 2048, 144), (4096, 256, 4096)])
 def test_matmul_bit_exact(bits, M, K, N):
     if bits == 6 and K < 256:
         pytest.skip("format 6 needs K >= 256")
@@ -498,12 +498,14 @@ def test_fp6_matmul_repeatable_with_fresh_buffers():
 
 
 @pytest.mark.parametrize("M,K,N", [(65, 256, 16), (257, 1024, 272), (300, 2048, 512), (513, 16384, 256),
-                                   (1000, 4096, 4096), (8192, 16384, 4096)])
+                                   (1000, 4096, 4096), (1023, 2048, 1040), (4096, 1024, 4096), (8192, 16384, 4096)])
 def test_int4_prefill_fp6_path_equals_int8_instruction_path(M, K, N):
     """The fused INT4 forward for more than 64 tokens runs its matmul on the
     fp6 x fp4 instruction; the stage calls run the same codes through the
     int8 instruction (bit-exact against the oracle above).  Same codes, exact
-    integer accumulators and the same dequantisation: equal bit for bit."""
+    integer accumulators and the same dequantisation: equal bit for bit.
+    Shapes with fewer than 256 tiles of 256 x 256 take 128 x 128 tiles (ragged
+    edges included); 4096 x 4096 and the 7B shape take 256 x 256."""
     w = synthetic.Workload("t", M, K, N, 4, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, M + 3 * K + N)
     x, xb, wl = synthetic.make_inputs(w)
     wp, a = hbl.quantize_weights(dev(wl))

@@ -7,7 +7,8 @@ Here the host compiler checks that the shipped schedules pass and that
 schedules with a planted mistake -- more copies than a stage has (the race
 of an earlier fp6 schedule: two extra copies landed in the buffer being
 read), a wait that leaves a needed copy in flight, a copy into the buffer
-being read, a ring too short for its lead -- fail to compile.
+being read, a ring too short for its lead, the 256-tile counts applied to
+the 128-tile schedule -- fail to compile.
 """
 import os
 import shutil
@@ -32,6 +33,9 @@ def compiles(body: str) -> bool:
 def test_shipped_schedules_pass():
     assert compiles("""
         static_assert(fp6_ok<Fp6>(2) && fp6_ok<Fp6>(4) && fp6_ok<Fp6>(16) && fp6_ok<Fp6>(128), "");
+        // the 128x128 tile of the same kernel
+        static_assert(fp6_ok<Fp6Small>(2) && fp6_ok<Fp6Small>(6) && fp6_ok<Fp6Small>(16)
+                      && fp6_ok<Fp6Small>(128), "");
         // the int8 instruction kernel: 10 copies per stage (INT8), 6 (INT4)
         static_assert(ring_ok<Ring3>(1, 10) && ring_ok<Ring3>(2, 10) && ring_ok<Ring3>(64, 10), "");
         static_assert(ring_ok<Ring3>(5, 6) && ring_ok<Ring3>(64, 6), "");
@@ -70,6 +74,30 @@ def test_the_checker_itself_compiles_and_rejects():
         struct Bad : Fp6 { static constexpr int a_stage(int kt, int KT) { return cmin(kt + 5, KT - 1); } };"""),
 ])
 def test_broken_fp6_schedules_fail(name, body):
+    assert not compiles(body + '\nstatic_assert(fp6_ok<Bad>(16), "");'), name
+
+
+@pytest.mark.parametrize("name,body", [
+    ("a fourth A copy per stage (the 256-tile count leaking in)", """
+        struct Bad : Fp6Small {
+          static constexpr Copy after(int i, bool odd) {
+            if (!odd && i == 7) return {1, 3};
+            return Fp6Small::after(i, odd);
+          }
+        };"""),
+    ("B copies missing on odd stages", """
+        struct Bad : Fp6Small {
+          static constexpr Copy after(int i, bool odd) {
+            if (odd && i == 1) return {0, 0};
+            return Fp6Small::after(i, odd);
+          }
+        };"""),
+    ("wait counts of the 256 tile", """
+        struct Bad : Fp6Small { static constexpr int wait(bool odd) { return Fp6::wait(odd); } };"""),
+    ("prologue wait of the 256 tile", """
+        struct Bad : Fp6Small { static constexpr int wait_prologue() { return Fp6::wait_prologue(); } };"""),
+])
+def test_broken_small_tile_schedules_fail(name, body):
     assert not compiles(body + '\nstatic_assert(fp6_ok<Bad>(16), "");'), name
 
 

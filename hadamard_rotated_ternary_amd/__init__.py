@@ -41,6 +41,7 @@ SIGNATURES = {
     "hbl_forward_int4": ([P, I, P, P, P, I64, I64, I64, P, I, P, SZ, P], I),
     "hbl_forward_noalloc": ([I, P, I, P, P, P, I64, I64, I64, P, I, P], I),
     "hbl_quantize_act": ([P, I, P, I64, I64, I, P, P, P], I),
+    "hbl_quantize_rotated": ([P, I64, I64, I, P, P, P], I),
     "hbl_matmul_dequant": ([P, I, P, P, P, I64, I64, I64, P, I, P, SZ, P], I),
     "hbl_rmsnorm_fwht": ([P, I, P, I64, I64, P, P], I),
     "hbl_gemm_ternary": ([P, I, P, I64, I64, I64, P, P, SZ, P], I),
@@ -204,6 +205,23 @@ def quantize_act(x: torch.Tensor, bits: int, gain: torch.Tensor | None = None, o
         d = torch.empty(M + 4, dtype=torch.float32, device=x.device)[:M]
     _call("hbl_quantize_act" if rotate else "hbl_quantize_act_unrotated", _ptr(x), _dtype_code(x.dtype), _ptr(gain),
           M, K, bits, _ptr(codes), _ptr(d), _stream())
+    return codes, d
+
+
+def quantize_rotated(xt: torch.Tensor, bits: int, out=None):
+    """Stage 1 from the rotated activations xt fp32 [M][K] (as rmsnorm_fwht
+    returns them): the quantiser alone -> (codes, per-token scales fp32 [M])."""
+    _dev(xt, "xt")
+    if xt.dtype != torch.float32:
+        raise ValueError("xt must be float32")
+    M, K = xt.shape
+    if out is not None:
+        codes, d = out
+    else:
+        codes = torch.empty(codes_shape(bits, M, K), dtype=torch.int8 if bits == 8 else torch.uint8,
+                            device=xt.device)
+        d = torch.empty(M + 4, dtype=torch.float32, device=xt.device)[:M]
+    _call("hbl_quantize_rotated", _ptr(xt), M, K, bits, _ptr(codes), _ptr(d), _stream())
     return codes, d
 
 

@@ -252,6 +252,23 @@ hbl_status hbl_quantize_act_unrotated(const void* x, hbl_dtype x_dtype, const fl
   return quantize_act(false, x, x_dtype, gain, M, K, bits, codes, dscale, stream);
 }
 
+hbl_status hbl_quantize_rotated(const float* xt, int64_t M, int64_t K, int bits, void* codes, float* dscale,
+                                hipStream_t stream) {
+  if (bits != 8 && bits != 4 && bits != HBL_BITS_INT4_FP6) return HBL_ERR_DTYPE;
+  if (hbl_status s = check_shape(M, K, 16)) return s;
+  if (bits == HBL_BITS_INT4_FP6 && K < hbl::kFp6MinK) return HBL_ERR_SHAPE;
+  if (M == 0) return HBL_OK;
+  if (!xt || !codes || !dscale) return HBL_ERR_NULL;
+  if (!aligned16(xt) || !aligned16(codes) || !aligned16(dscale)) return HBL_ERR_ALIGN;
+  int cus = 0;
+  if (hbl_status s = check_device(&cus)) return s;
+  hbl::PrepArgs p{};
+  p.x = xt; p.x_bf16 = false; p.gain = nullptr; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
+  p.bits = bits == 8 ? 8 : 4; p.mode = bits == HBL_BITS_INT4_FP6 ? 2 : 0; p.rotate = false; p.as_given = true;
+  p.codes = static_cast<uint8_t*>(codes); p.dscale = dscale; p.stream = stream;
+  return launched(hbl::launch_prep(p));
+}
+
 hbl_status hbl_bitlinear_forward(const void* x, hbl_dtype x_dtype, const float* gain, const uint8_t* w_packed,
                                  const float* w_alpha, int64_t M, int64_t K, int64_t N, int bits, void* y,
                                  hbl_dtype y_dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {

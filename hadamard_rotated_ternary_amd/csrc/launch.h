@@ -24,6 +24,8 @@ struct PrepArgs {
                      // 2: INT4 codes in the fp6 operand layout + scales,
                      // 3: rows rotated without normalisation (fp32, x fp32)
   bool rotate;       // modes 0 and 2: false leaves the transform out
+  bool as_given;     // modes 0 and 2, fp32 x, no transform: quantise x as given
+                     // (no RMSNorm either: x is already the rotated activation)
   uint8_t* codes;
   float* dscale;
   float* xt;

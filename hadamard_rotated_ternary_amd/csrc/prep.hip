@@ -23,6 +23,9 @@ namespace hbl {
 // ROT = false leaves the transform out (BitLinear for the layers whose inputs
 // are already close to Gaussian, 新智元 article, section H-BitLinear模块): the
 // quantiser then sees RMSNorm(x) = x / r in the load's own dealing.
+// NORM = false (with ROT = false, fp32 input, MODE 0 or 2) leaves RMSNorm out
+// too: the quantiser sees x as given, for callers that hold the rotated
+// activations xt already (the second of the layer's two stages on its own).
 // MODE 2 (INT4 only): write the codes as the fp6 (e2m3) operand of the
 // fp6 x fp4 matrix instruction, plus the scales.  One 24-byte group per token
 // and 32 consecutive k (k0 = 32c) holds q/2 for the 32 codes as six-bit
@@ -44,13 +47,14 @@ constexpr int prep_wg(int logk, int loge) { return (1 << (logk - loge)) < 64 ? 6
 // order, so a gain load queued behind the prefetch would wait for that whole
 // HBM round trip (and holding the slice across the unpack costs registers
 // and occupancy).
-template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int MODE, bool ROT>
+template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int MODE, bool ROT, bool NORM = true>
 __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
     const void* __restrict__ x, const float* __restrict__ gain, int M,
     uint8_t* __restrict__ codes, float* __restrict__ dscale, float* __restrict__ xt,
     uint32_t* __restrict__ zero, int nzero) {
   using C = PrepCfg<LOGK, LOGE, P2>;
   static_assert(ROT || (MODE == 0 || MODE == 2), "only the quantising modes run without the transform");
+  static_assert(NORM || (!ROT && !XBF16 && (MODE == 0 || MODE == 2)), "quantising fp32 rows as given only");
   using P0 = Pass<LOGK, LOGE, 0>;
   using PL = Pass<LOGK, LOGE, ROT ? C::NP - 1 : 0>;
   constexpr int K = C::K, E = C::E, T = C::T;
@@ -147,6 +151,7 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
 
     // c = 1 / (r * sqrt(K)) (1 / r without the transform), r = sqrt(mean x^2 + eps)
     auto scale_c = [&](float sst) {
+      if constexpr (!NORM) return 1.0f;
       const float r = sqrtf(sst * (1.0f / K) + kEpsNorm);
       return ROT ? 1.0f / (r * sqrtf((float)K)) : 1.0f / r;
     };
@@ -297,7 +302,13 @@ static hipError_t launch_prep_t(const PrepArgs& a) {
                      a.stream, a.x, a.gain, a.M, a.codes, a.dscale, a.xt, a.zero, a.zero ? a.nzero : 0)
 #define HBL_PREP_R(BITS, BF, MODE) \
   if (a.rotate) HBL_PREP(BITS, BF, MODE, true); else HBL_PREP(BITS, BF, MODE, false)
-  if (a.mode == 1) {
+#define HBL_PREP_G(BITS, MODE)                                                                            \
+  hipLaunchKernelGGL((prep_kernel<LOGK, LOGE, P2, BITS, false, MODE, false, false>), dim3(grid), dim3(C::WG), 0, \
+                     a.stream, a.x, nullptr, a.M, a.codes, a.dscale, nullptr, a.zero, a.zero ? a.nzero : 0)
+  if (a.as_given) {
+    if (a.x_bf16 || a.rotate || (a.mode != 0 && a.mode != 2)) return hipErrorInvalidValue;
+    if (a.mode == 2) HBL_PREP_G(4, 2); else if (a.bits == 8) HBL_PREP_G(8, 0); else HBL_PREP_G(4, 0);
+  } else if (a.mode == 1) {
     if (a.x_bf16) HBL_PREP(8, true, 1, true); else HBL_PREP(8, false, 1, true);
   } else if (a.mode == 3) {
     HBL_PREP(8, false, 3, true);
@@ -308,6 +319,7 @@ static hipError_t launch_prep_t(const PrepArgs& a) {
   } else {
     if (a.x_bf16) { HBL_PREP_R(4, true, 0); } else { HBL_PREP_R(4, false, 0); }
   }
+#undef HBL_PREP_G
 #undef HBL_PREP_R
 #undef HBL_PREP
   return hipGetLastError();

@@ -243,6 +243,24 @@ hbl_status hbl_quantize_act(const void *x, hbl_dtype x_dtype, const float *gain,
                             void *codes, float *dscale, hipStream_t stream);
 
 /*
+ * Stage 1 from the rotated activations: the per-token quantiser alone, on
+ * xt = H_K RMSNorm(x) / sqrt(K) held by the caller (as hbl_rmsnorm_fwht
+ * writes it).  The same quantisers as hbl_quantize_act (QbitAI article on
+ * BitNet v2, section 引入H-BitLinear模块, and 新智元 article, section
+ * H-BitLinear模块: INT8 per-token absmax, INT4 per-token absmean), with no
+ * normalisation or transform in front.
+ *   xt        fp32 [M][K], device, 16-byte aligned
+ *   bits      8, 4 or HBL_BITS_INT4_FP6 (6, K >= 256); codes and dscale as
+ *             for hbl_quantize_act
+ * The fused hbl_quantize_act scales the unnormalised transform once, so its
+ * codes may differ from these by one at rounding ties of the quantiser.
+ * Errors: HBL_ERR_DTYPE (bits), HBL_ERR_SHAPE (K, or K < 256 with bits 6),
+ * HBL_ERR_NULL, HBL_ERR_ALIGN, HBL_ERR_DEVICE, HBL_ERR_LAUNCH; M = 0 is a no-op.
+ */
+hbl_status hbl_quantize_rotated(const float *xt, int64_t M, int64_t K, int bits,
+                                void *codes, float *dscale, hipStream_t stream);
+
+/*
  * Stage 2: ternary integer matmul of the codes with dequant epilogue.
  *   codes, dscale as written by hbl_quantize_act;  y [M][N] of y_dtype.
  *   bits      8 and 4 run on the int8 matrix instruction (any M); 6 runs on

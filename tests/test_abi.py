@@ -137,6 +137,16 @@ def test_stage_validation(L):
     assert L.hbl_bitlinear_forward(A, 1, None, A, A, 0, 256, 256, 4, None, 1, None, 0, S) == OK
     assert L.hbl_quantize_act_unrotated(A, 1, None, 0, 256, 6, A, A2, S) == OK
     assert L.hbl_quantize_act_unrotated(A, 1, None, 4, 256, 7, A, A2, S) == DTYPE
+    # the quantiser alone, from rotated fp32 activations
+    assert L.hbl_quantize_rotated(A, 4, 256, 5, A, A2, S) == DTYPE
+    assert L.hbl_quantize_rotated(A, 4, 200, 8, A, A2, S) == SHAPE
+    assert L.hbl_quantize_rotated(A, 4, 65536, 8, A, A2, S) == SHAPE
+    assert L.hbl_quantize_rotated(A, 4, 128, 6, A, A2, S) == SHAPE          # format 6 needs K >= 256
+    assert L.hbl_quantize_rotated(None, 4, 256, 4, A, A2, S) == NULL
+    assert L.hbl_quantize_rotated(A, 4, 256, 4, A, None, S) == NULL
+    assert L.hbl_quantize_rotated(BAD, 4, 256, 8, A, A2, S) == ALIGN
+    assert L.hbl_quantize_rotated(A, 4, 64, 4, BAD, A2, S) == ALIGN
+    assert L.hbl_quantize_rotated(A, 0, 256, 6, A, A2, S) == OK              # empty: nothing launched
     need = L.hbl_workspace_bytes(2, 0, 1024, 64)
     assert need >= 64 * 1024 * 4 + 64 * 8
     assert L.hbl_quantize_weights_rotated(A, 64, 1024, A, A, A, need - 1, S) == WORKSPACE

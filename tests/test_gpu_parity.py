@@ -182,6 +182,55 @@ def test_codes_with_gain_over_persistent_iterations(K, M, bf16, bits):
     np.testing.assert_allclose(host(d)[rows], d_or, rtol=1e-5)
 
 
+@pytest.mark.parametrize("K", [64, 256, 4096, 16384, 32768])
+@pytest.mark.parametrize("bits", [8, 4, 6])
+@pytest.mark.parametrize("M", [1, 5, 129])
+def test_quantize_rotated_matches_oracle(K, bits, M):
+    """The quantiser alone, on rotated fp32 activations: the oracle's
+    quantiser applied to the same fp32 values."""
+    if bits == 6 and K < 256:
+        pytest.skip("format 6 needs K >= 256")
+    x, _ = make_x(M, K, 5 * K + M + bits, dist="laplace" if K % 3 else "normal", bf16=False)
+    xt = oracle.hadamard_rotate(oracle.rmsnorm(x)).astype(np.float32)
+    codes, d = hbl.quantize_rotated(dev(xt), bits)
+    q = gpu_codes_unpacked(codes, bits, K)
+    q_or, d_or, pre = oracle.quant_act(xt.astype(np.float64), 8 if bits == 8 else 4)
+    check_codes(q, q_or, pre)
+    np.testing.assert_allclose(host(d), d_or, rtol=1e-5)
+
+
+@pytest.mark.parametrize("bits", [8, 4, 6])
+def test_stages_rotation_then_quantiser(bits):
+    """rmsnorm_fwht then quantize_rotated, at a token count where the
+    persistent grid walks several tokens per workgroup: codes against the
+    oracle's quantiser of the oracle's rotation (and equal to the fused
+    stage's except at rounding ties), then the matmul of those codes."""
+    M, K, N = 1100, 16384, 272
+    x, xb = make_x(M, K, 13 + bits)
+    xt = hbl.rmsnorm_fwht(x_to_dev(x, xb))
+    codes, d = hbl.quantize_rotated(xt, bits)
+    codes_f, d_f = hbl.quantize_act(x_to_dev(x, xb), bits)
+    rows = synthetic.sample_rows(M, 24)
+    c, cf = host(codes), host(codes_f)
+    if bits == 6:
+        pick = lambda a: unpack_int4_fp6(np.ascontiguousarray(a.reshape(K // 128, M, 96)[:, rows]), K)
+    else:
+        pick = lambda a: a[rows].astype(np.int8) if bits == 8 else unpack_int4(a[rows], K)
+    q, qf = pick(c), pick(cf)
+    xt_or = oracle.hadamard_rotate(oracle.rmsnorm(x[rows]))
+    q_or, d_or, pre = oracle.quant_act(xt_or, 8 if bits == 8 else 4)
+    check_codes(q, q_or, pre)
+    check_codes(qf, q_or, pre)
+    np.testing.assert_allclose(host(d)[rows], d_or, rtol=1e-5)
+    np.testing.assert_allclose(host(d), host(d_f), rtol=1e-5)
+    # the matmul takes these codes like the fused stage's
+    wl = synthetic.make_inputs(gaussian_workload(1, K, N, 4, 99 + bits))[2]
+    wt, alpha = oracle.quantize_weights(wl)
+    wp, wa = oracle_weights_dev(wt, alpha)
+    acc = host(hbl.gemm_ternary(codes, bits, wp, K))
+    np.testing.assert_array_equal(acc[rows], oracle.gemm_ternary(q, wt))
+
+
 def test_zero_token_and_tiny_token():
     K = 1024
     x = np.zeros((3, K), np.float32)

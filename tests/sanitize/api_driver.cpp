@@ -123,6 +123,10 @@ int main() {
     EXPECT(hbl_quantize_act(A, HBL_BF16, nullptr, 0, 256, bits, nullptr, nullptr, S), HBL_OK);
     EXPECT(hbl_quantize_act(A, HBL_BF16, nullptr, 4, 128, bits, A, F, S), bits == 6 ? HBL_ERR_SHAPE : HBL_ERR_DEVICE);
     EXPECT(hbl_quantize_act_unrotated(A, HBL_F32, F, 3, 32768, bits, A, F, S), HBL_ERR_DEVICE);
+    EXPECT(hbl_quantize_rotated(F, 4, 200, bits, A, F, S), HBL_ERR_SHAPE);
+    EXPECT(hbl_quantize_rotated(F, 0, 256, bits, nullptr, nullptr, S), HBL_OK);
+    EXPECT(hbl_quantize_rotated(F, 4, 128, bits, A, F, S), bits == 6 ? HBL_ERR_SHAPE : HBL_ERR_DEVICE);
+    EXPECT(hbl_quantize_rotated(F, 4, 256, bits, A, nullptr, S), HBL_ERR_NULL);
     EXPECT(hbl_gemm_ternary(A, bits, U, 4, 256, 250, (int32_t*)A, nullptr, 0, S), HBL_ERR_SHAPE);
     EXPECT(hbl_gemm_ternary(A, bits, U, 300, 64, 256, (int32_t*)A, nullptr, 0, S),
            bits == 6 ? HBL_ERR_SHAPE : HBL_ERR_DEVICE);

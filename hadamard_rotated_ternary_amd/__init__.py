@@ -115,6 +115,15 @@ def workspace_bytes(op: int, M: int, K: int, N: int) -> int:
     return int(lib().hbl_workspace_bytes(op, M, K, N))
 
 
+def _out(t, shape, name="out"):
+    """A caller-given output: a contiguous device tensor of the expected shape
+    (its dtype is what the call writes)."""
+    _dev(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    return t
+
+
 def _workspace(nbytes, device, workspace=None):
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
@@ -146,8 +155,13 @@ def forward(x: torch.Tensor, w_packed: torch.Tensor, w_alpha: torch.Tensor, bits
     _dev(x, "x")
     M, K = x.shape
     N = w_packed.shape[0]
-    out_dtype = x.dtype if out_dtype is None else out_dtype
-    y = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
+    if out is None:
+        y = torch.empty((M, N), dtype=x.dtype if out_dtype is None else out_dtype, device=x.device)
+    else:
+        y = _out(out, (M, N))
+        if out_dtype is not None and out_dtype != y.dtype:
+            raise ValueError("out_dtype differs from out.dtype")
+    out_dtype = y.dtype
     op = OP_FORWARD_INT8 if bits == 8 else OP_FORWARD_INT4
     ws = _workspace(workspace_bytes(op, M, K, N), x.device, workspace)
     if rotate:
@@ -168,8 +182,12 @@ def forward_noalloc(x: torch.Tensor, w_packed: torch.Tensor, w_alpha: torch.Tens
     _dev(x, "x")
     M, K = x.shape
     N = w_packed.shape[0]
-    out_dtype = x.dtype if out_dtype is None else out_dtype
-    y = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
+    if out is None:
+        y = torch.empty((M, N), dtype=x.dtype if out_dtype is None else out_dtype, device=x.device)
+    else:
+        y = _out(out, (M, N))
+        if out_dtype is not None and out_dtype != y.dtype:
+            raise ValueError("out_dtype differs from out.dtype")
     _call("hbl_forward_noalloc", bits, _ptr(x), _dtype_code(x.dtype), _ptr(gain), _ptr(w_packed), _ptr(w_alpha),
           M, K, N, _ptr(y), _dtype_code(y.dtype), _stream())
     return y
@@ -229,7 +247,7 @@ def matmul_dequant(codes, bits, dscale, w_packed, w_alpha, K, out_dtype=torch.bf
     """Stage 2: codes -> y [M][N]."""
     M = _codes_m(codes, bits)
     N = w_packed.shape[0]
-    y = torch.empty((M, N), dtype=out_dtype, device=codes.device) if out is None else out
+    y = torch.empty((M, N), dtype=out_dtype, device=codes.device) if out is None else _out(out, (M, N))
     out_dtype = y.dtype
     ws = _workspace(workspace_bytes(OP_MATMUL, M, K, N), codes.device, workspace)
     _call("hbl_matmul_dequant", _ptr(codes), bits, _ptr(dscale), _ptr(w_packed), _ptr(w_alpha), M, K, N,
@@ -369,6 +387,8 @@ def attention_decode(q: torch.Tensor, q_bits: int, k_codes, k_scale, v_codes, v_
     ws = _workspace(attention_workspace_bytes(B, Hq, d, Tmax), q.device, workspace)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
+    else:
+        _out(out, (B, Hq, d))
     _call("hbl_attention_decode", _ptr(q), q_bits, _ptr(k_codes), _ptr(k_scale), _ptr(v_codes), _ptr(v_scale),
           kv_bits, _ptr(lens), B, Hq, Hkv, d, Tmax, _ptr(out), _dtype_code(out.dtype), _ptr(ws),
           ws.numel() * ws.element_size(), _stream())
@@ -387,6 +407,8 @@ def attention_prefill(q: torch.Tensor, q_bits: int, k_codes, k_scale, v_codes, v
     Hkv, Tmax = k_scale.shape[1], k_scale.shape[2]
     if out is None:
         out = torch.empty((B, Tn, Hq, d), dtype=out_dtype, device=q.device)
+    else:
+        _out(out, (B, Tn, Hq, d))
     _call("hbl_attention_prefill", _ptr(q), q_bits, _ptr(k_codes), _ptr(k_scale), _ptr(v_codes), _ptr(v_scale),
           kv_bits, _ptr(start), B, Tn, Hq, Hkv, d, Tmax, _ptr(out), _dtype_code(out.dtype), _stream())
     return out

@@ -1120,8 +1120,10 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const int32_t* __res
 }
 
 // ===========================================================================
-// Short rows (K = 64 or 128), any M.  The packed weights are then plain
-// row-major (K/4 bytes per channel), and one v_mfma_i32_16x16x64_i8 step
+// Short rows: K = 64 or 128 at any M, and K = 256 for 5 to 64 tokens.  The
+// packed weights are then plain row-major (K/4 bytes per channel; at K = 256
+// the 16-row tiles of the layout are exactly that), and one
+// v_mfma_i32_16x16x64_i8 step
 // covers 64 k: lane group g takes weight word 4j + g (k = 64j + 16g .. +15)
 // and the same 16 codes of its token, both in natural order (wstep; INT4
 // nibbles moved to the top of each byte, a4field).  Each wave computes 16
@@ -1135,7 +1137,7 @@ __global__ __launch_bounds__(256) void gemm_smallk_kernel(const uint8_t* __restr
                                                           const float* __restrict__ dscale,
                                                           const float* __restrict__ walpha, void* __restrict__ Y,
                                                           int M, int N, int tiles_n) {
-  static_assert(KS == 64 || KS == 128, "short rows only");
+  static_assert(KS == 64 || KS == 128 || KS == 256, "short rows only");
   constexpr int STEPS = KS / 64;
   constexpr int AROW = KS * BITS / 8;            // code bytes per token
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1282,6 +1284,9 @@ static void launch_smallk(const GemmArgs& a) {
   if (a.K == 64)
     hipLaunchKernelGGL((gemm_smallk_kernel<BITS, 64, OUT>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,
                        a.dscale, a.walpha, a.out, a.M, a.N, tn);
+  else if (a.K == 256)
+    hipLaunchKernelGGL((gemm_smallk_kernel<BITS, 256, OUT>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,
+                       a.dscale, a.walpha, a.out, a.M, a.N, tn);
   else
     hipLaunchKernelGGL((gemm_smallk_kernel<BITS, 128, OUT>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,
                        a.dscale, a.walpha, a.out, a.M, a.N, tn);
@@ -1289,7 +1294,11 @@ static void launch_smallk(const GemmArgs& a) {
 
 template <int BITS, int OUT>
 static void launch_t(const GemmArgs& a) {
-  if (a.K < 256) launch_smallk<BITS, OUT>(a);
+  // K = 256 with 5..64 tokens: the whole row is one MFMA k-loop of four steps,
+  // and the short-row kernel (no K split, no LDS) beats the decode kernels
+  // (8 tokens, N = 256: forward 8.7 -> 5.5 us in graph replay; at 1 token the
+  // few-token kernel stays ahead)
+  if (a.K < 256 || (a.K == 256 && a.M > 4 && a.M <= 64)) launch_smallk<BITS, OUT>(a);
   else if (a.M <= 64) launch_decode_t<BITS, OUT>(a);
   else launch_prefill_t<BITS, OUT>(a);
 }

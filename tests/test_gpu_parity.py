@@ -248,7 +248,8 @@ def test_zero_token_and_tiny_token():
 # ------------------------------------------------------------------ integer matmul
 
 @pytest.mark.parametrize("bits", [8, 4, 6])
-@pytest.mark.parametrize("M,K,N", [(1, 256, 16), (2, 1024, 48), (4, 16384, 272), (3, 8192, 4096),
+@pytest.mark.parametrize("M,K,N", [(1, 256, 16), (5, 256, 48), (17, 256, 272), (64, 256, 4096),
+                                   (2, 1024, 48), (4, 16384, 272), (3, 8192, 4096),
                                    (7, 512, 272), (16, 2048, 512), (20, 4096, 272), (32, 16384, 528), (33, 4096, 64),
                                    (64, 16384, 128), (65, 256, 256), (300, 1024, 272), (512, 2048, 512),
                                    (257, 16384, 528),
@@ -592,6 +593,29 @@ def test_token_permutation_equivariance():
     yp = hbl.forward(xd[perm].contiguous(), wp, a, 4)
     torch.cuda.synchronize()
     assert torch.equal(yp, y[perm])
+
+
+def test_forward_writes_the_given_output_dtype():
+    """A caller-given output of another dtype than x: the call writes that
+    dtype (fp32 x into a bf16 output equals the bf16 output asked for by
+    out_dtype), and outputs of the wrong shape or a conflicting out_dtype
+    are refused before anything is launched."""
+    M, K, N = 8, 256, 256
+    x, _ = make_x(M, K, 77, bf16=False)
+    wl = synthetic.make_inputs(gaussian_workload(1, K, N, 8, 78))[2]
+    wp, a = hbl.quantize_weights(dev(wl))
+    xd = dev(x)
+    for bits in (8, 4):
+        ref = hbl.forward(xd, wp, a, bits, out_dtype=torch.bfloat16)
+        guard = torch.full((M + 8, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        y = guard[:M]
+        hbl.forward(xd, wp, a, bits, out=y)
+        assert torch.equal(y, ref)
+        assert torch.all(guard[M:] == 7.0), "wrote past the output"
+        with pytest.raises(ValueError):
+            hbl.forward(xd, wp, a, bits, out=torch.empty((M, N + 16), dtype=torch.bfloat16, device="cuda"))
+        with pytest.raises(ValueError):
+            hbl.forward(xd, wp, a, bits, out=y, out_dtype=torch.float32)
 
 
 def test_empty_batch():

@@ -36,6 +36,20 @@ HBL_DEV size_t wword(int n, int w, int K) {
 HBL_DEV size_t wrow_base(int n, int K) {
   return (size_t)(n >> 4) * (size_t)K * 4 + (size_t)(n & 15) * (size_t)((K < 256 ? K : 256) / 4);
 }
+// Decode-blocked activation codes: the forward's own layout for 5..64 tokens
+// (the stage calls keep row-major codes).  Per 256-k block gb and 16-token
+// group, BITS/2 runs of 1 KiB; run d holds, lane by lane (lane = 16 g + c),
+// token c's 16 bytes at byte 16 d of its codes for k = 256 gb + 64 g ..
+// + 63 -- exactly the 16 bytes lane (c, g) of the decode matmul loads as its
+// d-th activation fragment, so every fragment load is one contiguous KiB.
+// Byte offset of the codes starting at k0 (a multiple of 8 for INT4 and 4
+// for INT8) of token t, with mbt 16-token groups:
+HBL_DEV size_t dblk_offset(int bits, int mbt, int t, int k0) {
+  const int nb = bits / 2, cpc = 128 / bits;          // 1 KiB runs per group, codes per 16 bytes
+  const int kk = k0 & 255, ci = kk / cpc, g = ci / nb, d = ci % nb;
+  return (((size_t)(k0 >> 8) * mbt + (t >> 4)) * nb + d) * 1024 + (size_t)(g * 16 + (t & 15)) * 16 +
+         (size_t)(kk % cpc) * bits / 8;
+}
 constexpr float kQ8 = 127.0f;       // INT8 absmax: max|x| maps to code 127
 constexpr float kQ4 = 2.6457513110645906f;  // INT4 absmean multiplier sqrt(7), rounded to fp32
 // Adding 1.5 * 2^23 rounds a float of magnitude < 2^22 to the nearest integer

@@ -637,7 +637,11 @@ static DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
 // writes back and invalidates the whole L2 of the XCD, which cost the
 // 64-token forward 55 us instead of 21 us: every workgroup threw away the
 // activation codes the others were still reading).
-template <int BITS, int MB, int CPW, int NW, int OUT, int KB1 = 8>
+// BLK: the codes are in the decode-blocked layout (dblk_offset: each
+// activation fragment load one contiguous KiB; with the row-major codes a
+// fragment load touches 16 token rows, and at 32 tokens the matmul took
+// 11.2 us instead of 8.4 us); bits 8 and 4 only.
+template <int BITS, int MB, int CPW, int NW, int OUT, int KB1 = 8, bool BLK = false>
 __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int S,
@@ -732,9 +736,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
   #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int t = min(16 * mb + c, M - 1);
-        const uint4* ap = reinterpret_cast<const uint4*>(A + (size_t)t * arow + (size_t)kb * BITS / 8);
+        if constexpr (BLK) {
+          const uint8_t* ap = A + dblk_offset(BITS, (M + 15) >> 4, t, kb);   // run d: + 1 KiB each
   #pragma unroll
-        for (int d = 0; d < BITS / 2; ++d) aq[slot][mb][d] = ap[d];
+          for (int d = 0; d < BITS / 2; ++d) aq[slot][mb][d] = *reinterpret_cast<const uint4*>(ap + 1024 * d);
+        } else {
+          const uint4* ap = reinterpret_cast<const uint4*>(A + (size_t)t * arow + (size_t)kb * BITS / 8);
+  #pragma unroll
+          for (int d = 0; d < BITS / 2; ++d) aq[slot][mb][d] = ap[d];
+        }
       }
     };
     auto compute = [&](int slot) __attribute__((always_inline)) {
@@ -823,8 +833,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(
           const uint4* ap =
               BITS == 6 ? reinterpret_cast<const uint4*>(A + ((size_t)(2 * gb + (g >> 1)) * M + t) * 96 + 48 * (g & 1))
                         : reinterpret_cast<const uint4*>(A + (size_t)t * arow + (size_t)(gb * DKB + 64 * g) * BITS / 8);
+          if constexpr (BLK && BITS != 6) {
+            const uint8_t* bp = A + dblk_offset(BITS, (M + 15) >> 4, t, gb * DKB + 64 * g);
 #pragma unroll
-          for (int d = 0; d < AU; ++d) aq[i][mb][d] = ap[d];
+            for (int d = 0; d < AU; ++d) aq[i][mb][d] = *reinterpret_cast<const uint4*>(bp + 1024 * d);
+          } else {
+#pragma unroll
+            for (int d = 0; d < AU; ++d) aq[i][mb][d] = ap[d];
+          }
         }
       }
 #pragma unroll
@@ -1204,7 +1220,7 @@ uint32_t* gemm_tile_counter_ptr(void* ws, int64_t M, int64_t K, int64_t N) {
   return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + partials_bytes(decode_plan(M, K, N), M, N));
 }
 
-template <int BITS, int MB, int CPW, int NW, int OUT>
+template <int BITS, int MB, int CPW, int NW, int OUT, bool BLK = false>
 static void launch_decode_p(const GemmArgs& a, int S) {
   constexpr int CH = 16 * CPW;
   dim3 grid((a.N + CH - 1) / CH, S);
@@ -1215,11 +1231,11 @@ static void launch_decode_p(const GemmArgs& a, int S) {
   if constexpr (CPW == 1) {
     long_rows = a.K / S > NW * 8 * DKB;
     if (long_rows)
-      hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, NW, OUT, 16>), grid, dim3(64 * NW), 0, a.stream,
+      hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, NW, OUT, 16, BLK>), grid, dim3(64 * NW), 0, a.stream,
                          a.codes, a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K, S, part, counts);
   }
   if (!long_rows)
-    hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, NW, OUT>), grid, dim3(64 * NW), 0, a.stream, a.codes,
+    hipLaunchKernelGGL((gemm_decode_kernel<BITS, MB, CPW, NW, OUT, 8, BLK>), grid, dim3(64 * NW), 0, a.stream, a.codes,
                        a.wpack, a.dscale, a.walpha, a.out, a.M, a.N, a.K, S, part, counts);
   if (S > 1 && counts == nullptr)
     hipLaunchKernelGGL((decode_reduce_kernel<BITS, OUT>), dim3((a.M * a.N + 255) / 256), dim3(256), 0, a.stream,
@@ -1257,6 +1273,12 @@ static void launch_decode_t(const GemmArgs& a) {
   // (the few-token kernel stages all codes in LDS and streams at most 16384 k)
   if (a.M <= 4 && a.K <= 16384) { launch_decode_few<BITS, OUT>(a); return; }
   const DecodePlan p = decode_plan(a.M, a.K, a.N);
+  if (a.codes_blocked) {
+    if (p.mb == 1) launch_decode_p<BITS, 1, 1, 8, OUT, true>(a, p.S);
+    else if (p.mb == 2) launch_decode_p<BITS, 2, 1, 8, OUT, true>(a, p.S);
+    else launch_decode_p<BITS, 4, 4, 8, OUT, true>(a, p.S);
+    return;
+  }
   if (p.mb == 1) launch_decode_p<BITS, 1, 1, 8, OUT>(a, p.S);
   else if (p.mb == 2) launch_decode_p<BITS, 2, 1, 8, OUT>(a, p.S);
   else launch_decode_p<BITS, 4, 4, 8, OUT>(a, p.S);

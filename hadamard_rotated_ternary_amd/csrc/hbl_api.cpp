@@ -56,8 +56,12 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // (M > kFp6MinM) keeps its codes in the six-bit operand layout of the fp6 x
 // fp4 matrix instruction.
 bool fp6_path(int bits, int64_t M, int64_t K) { return bits == 4 && M > hbl::kFp6MinM && K >= hbl::kFp6MinK; }
+// 5..64 tokens (not the few-token and short-row kernels): the decode matmul
+// reads the codes in the decode-blocked layout, 16-token groups
+bool blocked_path(int bits, int64_t M, int64_t K) { return !fp6_path(bits, M, K) && M >= 5 && M <= 64 && K >= 512; }
 size_t codes_bytes(int bits, int64_t M, int64_t K) {
-  return align256((size_t)M * K * (fp6_path(bits, M, K) ? 6 : bits) / 8);
+  const int64_t rows = blocked_path(bits, M, K) ? (M + 15) / 16 * 16 : M;
+  return align256((size_t)rows * K * (fp6_path(bits, M, K) ? 6 : bits) / 8);
 }
 size_t scales_bytes(int64_t M) { return align256((size_t)M * 4); }
 
@@ -136,7 +140,8 @@ hbl_status forward(int bits, bool rotate, const void* x, hbl_dtype x_dtype, cons
 
   hbl::PrepArgs p{};
   p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
-  p.bits = bits; p.mode = fp6 ? 2 : 0; p.rotate = rotate; p.codes = codes; p.dscale = dscale;
+  const bool blocked = blocked_path(bits, M, K);
+  p.bits = bits; p.mode = fp6 ? 2 : 0; p.rotate = rotate; p.codes = codes; p.dscale = dscale; p.blocked = blocked;
   p.xt = nullptr; p.zero = counts; p.nzero = counts ? hbl::gemm_tile_counters(M, K, N) : 0; p.stream = stream;
   if (hipError_t e = hbl::launch_prep(p)) return launched(e);
 
@@ -144,7 +149,7 @@ hbl_status forward(int bits, bool rotate, const void* x, hbl_dtype x_dtype, cons
   g.codes = codes; g.bits = bits; g.wpack = w_packed; g.dscale = dscale; g.walpha = w_alpha; g.out = y;
   g.out_kind = y_dtype == HBL_BF16 ? hbl::OUT_BF16 : hbl::OUT_F32;
   g.M = (int)M; g.N = (int)N; g.K = (int)K; g.ws = gws; g.ws_bytes = gws_bytes; g.tile_count = counts;
-  g.stream = stream;
+  g.codes_blocked = blocked; g.stream = stream;
   return launched(fp6 ? hbl::launch_gemm_fp6(g) : hbl::launch_gemm(g));
 }
 

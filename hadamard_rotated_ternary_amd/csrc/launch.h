@@ -24,6 +24,7 @@ struct PrepArgs {
                      // 2: INT4 codes in the fp6 operand layout + scales,
                      // 3: rows rotated without normalisation (fp32, x fp32)
   bool rotate;       // modes 0 and 2: false leaves the transform out
+  bool blocked;      // mode 0: codes in the decode-blocked layout (dblk_offset), 5..64 tokens
   bool as_given;     // modes 0 and 2, fp32 x, no transform: quantise x as given
                      // (no RMSNorm either: x is already the rotated activation)
   uint8_t* codes;
@@ -49,6 +50,7 @@ struct GemmArgs {
   void* ws;               // split-K partials (decode path)
   size_t ws_bytes;
   uint32_t* tile_count;   // zeroed split-K arrival counters (or nullptr: separate reduction kernel)
+  bool codes_blocked;     // codes in the decode-blocked layout (5..64 tokens, K >= 512, bits 8 or 4)
   hipStream_t stream;
 };
 hipError_t launch_gemm(const GemmArgs& a);

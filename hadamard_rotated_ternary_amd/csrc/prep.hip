@@ -51,7 +51,7 @@ template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int MODE, bool ROT, 
 __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
     const void* __restrict__ x, const float* __restrict__ gain, int M,
     uint8_t* __restrict__ codes, float* __restrict__ dscale, float* __restrict__ xt,
-    uint32_t* __restrict__ zero, int nzero) {
+    uint32_t* __restrict__ zero, int nzero, int blocked) {
   using C = PrepCfg<LOGK, LOGE, P2>;
   static_assert(ROT || (MODE == 0 || MODE == 2), "only the quantising modes run without the transform");
   static_assert(NORM || (!ROT && !XBF16 && (MODE == 0 || MODE == 2)), "quantising fp32 rows as given only");
@@ -237,17 +237,21 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
             dst[2] = make_uint2(f[4], f[5]);
           }
         } else if constexpr (BITS == 8) {
-          // int8 codes: thread tau stores 16-byte chunks j*T + tau
+          // int8 codes: thread tau stores 16-byte chunks j*T + tau (row-major,
+          // or each chunk at its place in the decode-blocked layout)
           uint8_t* out = codes + (size_t)m * K;
+          const int mbt = (M + 15) >> 4;
 #pragma unroll
           for (int j = 0; j < E / 16; ++j) {
             const int ch = j * T + tau;
             const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(16 * ch));
-            *reinterpret_cast<uint4*>(out + 16 * ch) = make_uint4(s4[0], s4[1], s4[2], s4[3]);
+            uint8_t* dst = blocked ? codes + dblk_offset(8, mbt, m, 16 * ch) : out + 16 * ch;
+            *reinterpret_cast<uint4*>(dst) = make_uint4(s4[0], s4[1], s4[2], s4[3]);
           }
         } else {
           // int4 codes: 8 consecutive codes per 32-bit word, code k0+4j+i at bits 8i+4j
           uint8_t* out = codes + (size_t)m * (K / 2);
+          const int mbt = (M + 15) >> 4;
           constexpr int OB = E / 2;  // output bytes per thread
           if constexpr (OB >= 16) {
 #pragma unroll
@@ -258,7 +262,8 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
 #pragma unroll
               for (int i = 0; i < 4; ++i)
                 w[i] = (s4[2 * i] & 0x0F0F0F0Fu) | ((s4[2 * i + 1] & 0x0F0F0F0Fu) << 4);
-              *reinterpret_cast<uint4*>(out + 16 * ch) = make_uint4(w[0], w[1], w[2], w[3]);
+              uint8_t* dst = blocked ? codes + dblk_offset(4, mbt, m, 32 * ch) : out + 16 * ch;
+              *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
             }
           } else {
             static_assert(OB == 8, "E >= 16");
@@ -266,7 +271,8 @@ __global__ __launch_bounds__(prep_wg(LOGK, LOGE)) void prep_kernel(
             const uint32_t* s4 = reinterpret_cast<const uint32_t*>(bytes + padb(16 * ch));
             uint32_t w0 = (s4[0] & 0x0F0F0F0Fu) | ((s4[1] & 0x0F0F0F0Fu) << 4);
             uint32_t w1 = (s4[2] & 0x0F0F0F0Fu) | ((s4[3] & 0x0F0F0F0Fu) << 4);
-            *reinterpret_cast<uint2*>(out + 8 * ch) = make_uint2(w0, w1);
+            uint8_t* dst = blocked ? codes + dblk_offset(4, mbt, m, 16 * ch) : out + 8 * ch;
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
           }
         }
       }
@@ -299,12 +305,13 @@ static hipError_t launch_prep_t(const PrepArgs& a) {
   if (grid == 0) return hipSuccess;   // (M == 0: no matmul follows either)
 #define HBL_PREP(BITS, BF, MODE, ROT)                                                           \
   hipLaunchKernelGGL((prep_kernel<LOGK, LOGE, P2, BITS, BF, MODE, ROT>), dim3(grid), dim3(C::WG), 0, \
-                     a.stream, a.x, a.gain, a.M, a.codes, a.dscale, a.xt, a.zero, a.zero ? a.nzero : 0)
+                     a.stream, a.x, a.gain, a.M, a.codes, a.dscale, a.xt, a.zero, a.zero ? a.nzero : 0, \
+                     a.blocked ? 1 : 0)
 #define HBL_PREP_R(BITS, BF, MODE) \
   if (a.rotate) HBL_PREP(BITS, BF, MODE, true); else HBL_PREP(BITS, BF, MODE, false)
 #define HBL_PREP_G(BITS, MODE)                                                                            \
   hipLaunchKernelGGL((prep_kernel<LOGK, LOGE, P2, BITS, false, MODE, false, false>), dim3(grid), dim3(C::WG), 0, \
-                     a.stream, a.x, nullptr, a.M, a.codes, a.dscale, nullptr, a.zero, a.zero ? a.nzero : 0)
+                     a.stream, a.x, nullptr, a.M, a.codes, a.dscale, nullptr, a.zero, a.zero ? a.nzero : 0, 0)
   if (a.as_given) {
     if (a.x_bf16 || a.rotate || (a.mode != 0 && a.mode != 2)) return hipErrorInvalidValue;
     if (a.mode == 2) HBL_PREP_G(4, 2); else if (a.bits == 8) HBL_PREP_G(8, 0); else HBL_PREP_G(4, 0);

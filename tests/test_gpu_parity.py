@@ -595,6 +595,26 @@ def test_token_permutation_equivariance():
     assert torch.equal(yp, y[perm])
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,K,N", [(5, 512, 48), (16, 2048, 272), (17, 16384, 4096), (31, 4096, 64),
+                                   (33, 16384, 4096), (64, 8192, 512), (40, 32768, 272)])
+def test_forward_decode_codes_layout_matches_stages(bits, M, K, N):
+    """From 5 to 64 tokens the forward keeps its codes in the decode-blocked
+    layout (each fragment load one contiguous KiB); the stage calls keep them
+    row-major.  Same codes, exact integer sums, same dequant: the forward
+    equals quantize_act + matmul_dequant bit for bit."""
+    w = synthetic.Workload("t", M, K, N, bits, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, 7 * M + K + bits)
+    x, xb, wl = synthetic.make_inputs(w)
+    xd = x_to_dev(x, xb)
+    wp, a = hbl.quantize_weights(dev(wl))
+    y = hbl.forward(xd, wp, a, bits)
+    codes, d = hbl.quantize_act(xd, bits)
+    ys = hbl.matmul_dequant(codes, bits, d, wp, a, K)
+    assert torch.equal(y, ys)
+    ynone = hbl.forward_noalloc(xd, wp, a, bits)
+    assert torch.equal(ynone, ys)
+
+
 def test_forward_writes_the_given_output_dtype():
     """A caller-given output of another dtype than x: the call writes that
     dtype (fp32 x into a bf16 output equals the bf16 output asked for by

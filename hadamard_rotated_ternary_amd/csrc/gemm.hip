@@ -618,8 +618,16 @@ constexpr int kDecodeMaxSplit = 4;   // split-K ways the in-kernel reduction han
 // 16 channels: 64 tokens took 18.0 us unsplit against 13.5 us split), at the
 // price of the cross-workgroup reduction.  Measured at K = 16384, N = 4096:
 // 17 / 32 tokens 8.2 / 10.8 us unsplit against ~12.5 us split.
-static DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
-  DecodePlan p = M <= 16 ? DecodePlan{1, 1, 1, 8} : M <= 32 ? DecodePlan{1, 1, 2, 8} : DecodePlan{4, 4, 4, 8};
+// Codes in the decode-blocked layout (blocked, the forward's) make the code
+// stream cheap enough that 33..64 tokens also run unsplit on 16 channels
+// per workgroup (four token groups) up to K = 16384: the 64-token matmul
+// inside the forward 13.0 us against 14.6 us split, 40 tokens 11.7 against
+// 13.3 us.
+static DecodePlan decode_plan(int64_t M, int64_t K, int64_t N, bool blocked) {
+  DecodePlan p = M <= 16                    ? DecodePlan{1, 1, 1, 8}
+                 : M <= 32                  ? DecodePlan{1, 1, 2, 8}
+                 : (blocked && K <= 16384) ? DecodePlan{1, 1, 4, 8}
+                                            : DecodePlan{4, 4, 4, 8};
   while (p.S > 1 && K / p.S < DKB) p.S /= 2;
   // split-K partials are addressed with 32-bit byte offsets
   if (p.S > 1 && (int64_t)p.S * M * N * 4 >= (int64_t(1) << 31)) p.S = 1;
@@ -1204,20 +1212,20 @@ __global__ __launch_bounds__(256) void gemm_smallk_kernel(const uint8_t* __restr
 static size_t partials_bytes(const DecodePlan& p, int64_t M, int64_t N) {
   return p.S > 1 ? (((size_t)p.S * M * N * 4 + 255) & ~(size_t)255) : 0;
 }
-int gemm_tile_counters(int64_t M, int64_t K, int64_t N) {
+int gemm_tile_counters(int64_t M, int64_t K, int64_t N, bool blocked) {
   if (M > 64 || M <= 4) return 0;
-  const DecodePlan p = decode_plan(M, K, N);
+  const DecodePlan p = decode_plan(M, K, N, blocked);
   return p.S > 1 ? (int)((N + 16 * p.cpw - 1) / (16 * p.cpw)) : 0;
 }
-size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, bool blocked) {
   if (M > 64 || M <= 0) return 0;
-  const DecodePlan p = decode_plan(M, K, N);
-  const size_t nc = (size_t)gemm_tile_counters(M, K, N);
+  const DecodePlan p = decode_plan(M, K, N, blocked);
+  const size_t nc = (size_t)gemm_tile_counters(M, K, N, blocked);
   return partials_bytes(p, M, N) + ((nc * 4 + 255) & ~(size_t)255);
 }
-uint32_t* gemm_tile_counter_ptr(void* ws, int64_t M, int64_t K, int64_t N) {
-  if (gemm_tile_counters(M, K, N) == 0 || ws == nullptr) return nullptr;
-  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + partials_bytes(decode_plan(M, K, N), M, N));
+uint32_t* gemm_tile_counter_ptr(void* ws, int64_t M, int64_t K, int64_t N, bool blocked) {
+  if (gemm_tile_counters(M, K, N, blocked) == 0 || ws == nullptr) return nullptr;
+  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + partials_bytes(decode_plan(M, K, N, blocked), M, N));
 }
 
 template <int BITS, int MB, int CPW, int NW, int OUT, bool BLK = false>
@@ -1272,10 +1280,11 @@ template <int BITS, int OUT>
 static void launch_decode_t(const GemmArgs& a) {
   // (the few-token kernel stages all codes in LDS and streams at most 16384 k)
   if (a.M <= 4 && a.K <= 16384) { launch_decode_few<BITS, OUT>(a); return; }
-  const DecodePlan p = decode_plan(a.M, a.K, a.N);
+  const DecodePlan p = decode_plan(a.M, a.K, a.N, a.codes_blocked);
   if (a.codes_blocked) {
     if (p.mb == 1) launch_decode_p<BITS, 1, 1, 8, OUT, true>(a, p.S);
     else if (p.mb == 2) launch_decode_p<BITS, 2, 1, 8, OUT, true>(a, p.S);
+    else if (p.cpw == 1) launch_decode_p<BITS, 4, 1, 8, OUT, true>(a, p.S);
     else launch_decode_p<BITS, 4, 4, 8, OUT, true>(a, p.S);
     return;
   }
@@ -1330,7 +1339,7 @@ static void launch_t(const GemmArgs& a) {
 // only stage calls bring fp6 codes).
 template <int OUT>
 static void launch_decode_fp6(const GemmArgs& a) {
-  const DecodePlan p = decode_plan(a.M, a.K, a.N);
+  const DecodePlan p = decode_plan(a.M, a.K, a.N, false);
   launch_decode_p<6, 4, 4, 8, OUT>(a, p.cpw == 4 ? p.S : 1);
 }
 

@@ -131,18 +131,18 @@ hbl_status forward(int bits, bool rotate, const void* x, hbl_dtype x_dtype, cons
   uint8_t* codes = ws;
   float* dscale = reinterpret_cast<float*>(ws + codes_bytes(bits, M, K));
   void* gws = ws + codes_bytes(bits, M, K) + scales_bytes(M);
-  const size_t gws_bytes = hbl::gemm_workspace_bytes(M, K, N);
+  const bool blocked = blocked_path(bits, M, K);
+  const size_t gws_bytes = hbl::gemm_workspace_bytes(M, K, N, blocked);
 
   // split-K decode shapes: prep clears the matmul's arrival counters, so the
   // matmul's last workgroup per tile reduces (no separate reduction launch)
   const bool fp6 = fp6_path(bits, M, K);
-  uint32_t* counts = hbl::gemm_tile_counter_ptr(gws, M, K, N);
+  uint32_t* counts = hbl::gemm_tile_counter_ptr(gws, M, K, N, blocked);
 
   hbl::PrepArgs p{};
   p.x = x; p.x_bf16 = x_dtype == HBL_BF16; p.gain = gain; p.M = (int)M; p.cus = cus; p.logk = log2_exact(K);
-  const bool blocked = blocked_path(bits, M, K);
   p.bits = bits; p.mode = fp6 ? 2 : 0; p.rotate = rotate; p.codes = codes; p.dscale = dscale; p.blocked = blocked;
-  p.xt = nullptr; p.zero = counts; p.nzero = counts ? hbl::gemm_tile_counters(M, K, N) : 0; p.stream = stream;
+  p.xt = nullptr; p.zero = counts; p.nzero = counts ? hbl::gemm_tile_counters(M, K, N, blocked) : 0; p.stream = stream;
   if (hipError_t e = hbl::launch_prep(p)) return launched(e);
 
   hbl::GemmArgs g{};
@@ -178,12 +178,13 @@ size_t hbl_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
   switch (op) {
     case HBL_OP_QUANTIZE_WEIGHTS: return align256((size_t)N * 8);
     case HBL_OP_QUANTIZE_WEIGHTS_ROTATED: return align256((size_t)N * 8) + align256((size_t)N * K * 4);
-    case HBL_OP_MATMUL: return align256(hbl::gemm_workspace_bytes(M, K, N));
+    case HBL_OP_MATMUL: return align256(hbl::gemm_workspace_bytes(M, K, N, false));
     case HBL_OP_BACKWARD: return M > 0 && log2_exact(K) > 0 ? bwd_layout(M, K, N).total : 0;
     case HBL_OP_FORWARD_INT8:
     case HBL_OP_FORWARD_INT4: {
       const int bits = op == HBL_OP_FORWARD_INT8 ? 8 : 4;
-      return codes_bytes(bits, M, K) + scales_bytes(M) + align256(hbl::gemm_workspace_bytes(M, K, N));
+      return codes_bytes(bits, M, K) + scales_bytes(M) +
+             align256(hbl::gemm_workspace_bytes(M, K, N, blocked_path(bits, M, K)));
     }
     default: return 0;
   }
@@ -305,7 +306,7 @@ static hbl_status matmul(const void* codes, int bits, const float* dscale, const
   if (!codes || !w_packed || !out) return HBL_ERR_NULL;
   if (out_kind != hbl::OUT_ACC_I32 && (!dscale || !w_alpha)) return HBL_ERR_NULL;
   const bool fp6 = bits == HBL_BITS_INT4_FP6;
-  const size_t need = align256(hbl::gemm_workspace_bytes(M, K, N));
+  const size_t need = align256(hbl::gemm_workspace_bytes(M, K, N, false));
   if (need && !workspace) return HBL_ERR_NULL;
   if (!aligned16(codes) || !aligned16(w_packed) || !aligned16(out) || (dscale && !aligned16(dscale)) ||
       (w_alpha && !aligned16(w_alpha)) || (workspace && !aligned16(workspace)))

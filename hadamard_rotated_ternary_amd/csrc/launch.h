@@ -64,12 +64,14 @@ constexpr int kFp6MinM = 64;
 // blocks per step, so format 6 needs K >= 256 (shorter rows use format 4).
 constexpr int kFp6MinK = 256;
 hipError_t launch_gemm_fp6(const GemmArgs& a);
-// Workspace bytes the matmul needs beyond the codes and scales.
-size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+// Workspace bytes the matmul needs beyond the codes and scales (blocked: the
+// codes come in the decode-blocked layout, which changes the plan for 33-64
+// tokens).
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, bool blocked);
 // Split-K arrival counters inside that workspace (count 0 / nullptr when the
 // shape needs none); they must be zero when the matmul starts.
-int gemm_tile_counters(int64_t M, int64_t K, int64_t N);
-uint32_t* gemm_tile_counter_ptr(void* ws, int64_t M, int64_t K, int64_t N);
+int gemm_tile_counters(int64_t M, int64_t K, int64_t N, bool blocked);
+uint32_t* gemm_tile_counter_ptr(void* ws, int64_t M, int64_t K, int64_t N, bool blocked);
 
 // Single-launch forward for 1..4 tokens with K = 8192 or 16384 (decode):
 // transform, quantiser and matmul in one kernel.

@@ -50,10 +50,16 @@ def test_workspace_sizes(L):
     assert ws4 < ws8
     assert L.hbl_workspace_bytes(0, 0, 16384, 4096) >= 4096 * 8
     assert L.hbl_workspace_bytes(1, 64, 16384, 4096) > 0      # split-K scratch of the small-M path
-    # 17..64 tokens: int32 partials [S][M][N] (256-aligned), then one arrival
-    # counter per 64-channel tile (256-aligned); S = 4, halved while K / S < 256
+    # stage matmul, 33..64 tokens: int32 partials [S][M][N] (256-aligned), then
+    # one arrival counter per 64-channel tile (256-aligned); S = 4, halved
+    # while K / S < 256
     assert L.hbl_workspace_bytes(1, 64, 16384, 4096) == 4 * 64 * 4096 * 4 + 256
     assert L.hbl_workspace_bytes(1, 40, 512, 96) == 2 * 40 * 96 * 4 + 256
+    # the forward's 33..64 tokens read decode-blocked codes (rows padded to 16)
+    # and run unsplit up to K = 16384: codes + scales only; split at K = 32768
+    assert L.hbl_workspace_bytes(4, 64, 16384, 4096) == 64 * 16384 // 2 + 256
+    assert L.hbl_workspace_bytes(8, 40, 8192, 4096) == 48 * 8192 + 256
+    assert L.hbl_workspace_bytes(4, 40, 32768, 4096) == 48 * 32768 // 2 + 256 + 4 * 40 * 4096 * 4 + 256
     assert L.hbl_workspace_bytes(1, 16, 16384, 4096) == 0      # up to 16 tokens: no split
     assert L.hbl_workspace_bytes(1, 1, 16384, 4096) == 0      # one token: no split
     assert L.hbl_workspace_bytes(1, 8192, 16384, 4096) == 0

@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip the INT8 and decode side measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall-clock budget of the CPU baseline")
+    ap.add_argument("--extra", choices=["layers", "decode", "attention", "backward"], default=None,
+                    help="run only this group of side measurements (for profiling one kernel family)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -388,134 +390,141 @@ def tiny_extra(torch, hbl, synthetic):
 def extras(torch, hbl, synthetic, args):
     out = {}
     steps = max(10, args.steps // 2)
-    # every other configuration of the layer, end to end
-    for name in ("wo_1p3b_int4", "wdown_3b_int4", "wo_7b_int8", "wo_7b_int4"):
-        out[name] = layer_config_extra(torch, hbl, synthetic, name, steps)
-    out["wdown_7b_int4_on_int8_mfma"] = int4_on_int8_extra(torch, hbl, synthetic, steps)
-    out["tiny_int8"] = tiny_extra(torch, hbl, synthetic)
-    # INT8 activations on the same 7B Wdown shape
-    w8 = synthetic.WORKLOADS["wdown_7b_int8"]
-    x, xb, wl = synthetic.make_inputs(w8)
-    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
-    wp, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
-    r = time_layer(torch, hbl, xd, wp, a, w8.M, w8.K, w8.N, 8, max(10, args.steps // 2), 5)
-    ops = 2.0 * w8.M * w8.N * w8.K
-    out["wdown_7b_int8"] = {"tokens_per_s": w8.M / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
-                            "prep_ms": r["prep_ms"], "gemm_ms": r["gemm_ms"],
-                            "gemm_tops": ops / (r["gemm_ms"] / 1e3) / 1e12,
-                            "gemm_mfma_frac": ops / (r["gemm_ms"] / 1e3) / 1e12 / PEAK_INT8_TOPS}
-    del xd, wp
-    # BitLinear without the rotation on a 7B-scale FFN input projection
-    wu = synthetic.WORKLOADS["up_7b_bitlinear_int4"]
-    x, xb, wl = synthetic.make_inputs(wu)
-    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
-    wp, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
-    r = time_layer(torch, hbl, xd, wp, a, wu.M, wu.K, wu.N, 4, max(10, args.steps // 2), 5, rotate=False)
-    ops = 2.0 * wu.M * wu.N * wu.K
-    out[wu.name] = {"tokens_per_s": wu.M / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
-                    "prep_ms": r["prep_ms"], "gemm_ms": r["gemm_ms"], "M": wu.M, "K": wu.K, "N": wu.N,
-                    "gemm_tflops": ops / (r["gemm_ms"] / 1e3) / 1e12,
-                    "gemm_frac_fp6": ops / (r["gemm_ms"] / 1e3) / 1e12 / PEAK_FP6_TFLOPS}
-    del xd, wp
-    # decode shapes: weights rotated over enough copies to defeat the 256 MB
-    # Infinity Cache; calls replayed from a captured graph so the timing is
-    # not bound by host launch overhead.
-    base = synthetic.WORKLOADS["decode_7b_m64"]
-    x, xb, wl = synthetic.make_inputs(base)
-    wp0, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
-    R = 40
-    wps = [wp0.clone() for _ in range(R)]
-    xfull = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
-    for M in (1, 16, 64):
-        xd = xfull[:M].contiguous()
-        codes, d = hbl.quantize_act(xd, 4)
-        ws = torch.empty(max(hbl.workspace_bytes(hbl.OP_MATMUL, M, base.K, base.N), 16), dtype=torch.uint8, device="cuda")
-        wsf = torch.empty(hbl.workspace_bytes(hbl.OP_FORWARD_INT4, M, base.K, base.N), dtype=torch.uint8, device="cuda")
-        y = torch.empty((M, base.N), dtype=torch.bfloat16, device="cuda")
-        y_eager = hbl.matmul_dequant(codes, 4, d, wps[0], a, base.K, workspace=ws)
-        f_eager = hbl.forward(xd, wps[0], a, 4, workspace=wsf)
-        res = {}
-        codes2, d2 = torch.empty_like(codes), torch.empty_like(d)
-        for kind in ("gemm", "forward", "prep"):
-            def body(i):
-                if kind == "gemm":
-                    hbl.matmul_dequant(codes, 4, d, wps[i % R], a, base.K, workspace=ws, out=y)
-                elif kind == "forward":
-                    hbl.forward(xd, wps[i % R], a, 4, workspace=wsf, out=y)
-                else:
-                    hbl.quantize_act(xd, 4, out=(codes2, d2))
-            s_ = torch.cuda.Stream()
-            s_.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s_):
-                for i in range(3):
-                    body(i)
-            torch.cuda.current_stream().wait_stream(s_)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(R):
-                    body(i)
-            reps = 10
-            g.replay()
-            torch.cuda.synchronize()
-            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            f0.record()
-            for _ in range(reps):
-                g.replay()
-            f1.record()
-            torch.cuda.synchronize()
-            res[kind] = 1e3 * f0.elapsed_time(f1) / (reps * R)
-            # the last captured call used wps[R-1], a copy of wps[0]: same result as eager
-            if kind != "prep":
-                ref = y_eager if kind == "gemm" else f_eager
-                assert torch.equal(y, ref), f"graph replay differs from eager ({kind}, M={M})"
-        gbytes = base.N * base.K / 4 + M * base.K / 2 + M * base.N * 2 + M * 4
-        # inside the forward, 5..64 tokens, the matmul reads its codes in the
-        # decode-blocked layout (the stage call above reads row-major codes):
-        # its time is the forward's less a prep stage call of the same tokens
-        # (one token: the forward is a single fused kernel, no prep stage)
-        out[f"decode_7b_m{M}"] = {"gemm_us": res["gemm"], "gemm_gbps": gbytes / (res["gemm"] / 1e6) / 1e9,
-                                  "gemm_hbm_frac": gbytes / (res["gemm"] / 1e6) / 1e9 / PEAK_HBM_GBS,
-                                  "forward_us": res["forward"], "tokens_per_s": M / (res["forward"] / 1e6),
-                                  "timing": f"graph replay of {R} back-to-back calls over {R} weight copies"}
-        if M >= 5:
-            fg = res["forward"] - res["prep"]
-            out[f"decode_7b_m{M}"].update({"prep_us": res["prep"], "forward_gemm_us": fg,
-                                           "forward_gemm_hbm_frac": gbytes / (fg / 1e6) / 1e9 / PEAK_HBM_GBS})
-    # a plain read of one 16 MiB weight copy per call (a torch row-wise
-    # max-reduction over it: 4096 rows of 4 KiB; the value is not used) in the
-    # same graph-replay harness over the same 40 copies
-    red = torch.empty((base.N,), dtype=torch.int64, device="cuda")
 
-    def read_body(i):
-        torch.amax(wps[i % R].view(torch.int64), dim=1, out=red)
-    s_ = torch.cuda.Stream()
-    s_.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s_):
-        for i in range(3):
-            read_body(i)
-    torch.cuda.current_stream().wait_stream(s_)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(R):
-            read_body(i)
-    g.replay()
-    torch.cuda.synchronize()
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record()
-    for _ in range(10):
+    def want(group):
+        return args.extra in (None, group)
+    if want("layers"):
+        # every other configuration of the layer, end to end
+        for name in ("wo_1p3b_int4", "wdown_3b_int4", "wo_7b_int8", "wo_7b_int4"):
+            out[name] = layer_config_extra(torch, hbl, synthetic, name, steps)
+        out["wdown_7b_int4_on_int8_mfma"] = int4_on_int8_extra(torch, hbl, synthetic, steps)
+        out["tiny_int8"] = tiny_extra(torch, hbl, synthetic)
+        # INT8 activations on the same 7B Wdown shape
+        w8 = synthetic.WORKLOADS["wdown_7b_int8"]
+        x, xb, wl = synthetic.make_inputs(w8)
+        xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+        wp, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
+        r = time_layer(torch, hbl, xd, wp, a, w8.M, w8.K, w8.N, 8, max(10, args.steps // 2), 5)
+        ops = 2.0 * w8.M * w8.N * w8.K
+        out["wdown_7b_int8"] = {"tokens_per_s": w8.M / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
+                                "prep_ms": r["prep_ms"], "gemm_ms": r["gemm_ms"],
+                                "gemm_tops": ops / (r["gemm_ms"] / 1e3) / 1e12,
+                                "gemm_mfma_frac": ops / (r["gemm_ms"] / 1e3) / 1e12 / PEAK_INT8_TOPS}
+        del xd, wp
+        # BitLinear without the rotation on a 7B-scale FFN input projection
+        wu = synthetic.WORKLOADS["up_7b_bitlinear_int4"]
+        x, xb, wl = synthetic.make_inputs(wu)
+        xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+        wp, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
+        r = time_layer(torch, hbl, xd, wp, a, wu.M, wu.K, wu.N, 4, max(10, args.steps // 2), 5, rotate=False)
+        ops = 2.0 * wu.M * wu.N * wu.K
+        out[wu.name] = {"tokens_per_s": wu.M / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
+                        "prep_ms": r["prep_ms"], "gemm_ms": r["gemm_ms"], "M": wu.M, "K": wu.K, "N": wu.N,
+                        "gemm_tflops": ops / (r["gemm_ms"] / 1e3) / 1e12,
+                        "gemm_frac_fp6": ops / (r["gemm_ms"] / 1e3) / 1e12 / PEAK_FP6_TFLOPS}
+        del xd, wp
+    if want("decode"):
+        # decode shapes: weights rotated over enough copies to defeat the 256 MB
+        # Infinity Cache; calls replayed from a captured graph so the timing is
+        # not bound by host launch overhead.
+        base = synthetic.WORKLOADS["decode_7b_m64"]
+        x, xb, wl = synthetic.make_inputs(base)
+        wp0, a = hbl.quantize_weights(torch.from_numpy(wl).cuda())
+        R = 40
+        wps = [wp0.clone() for _ in range(R)]
+        xfull = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+        for M in (1, 16, 64):
+            xd = xfull[:M].contiguous()
+            codes, d = hbl.quantize_act(xd, 4)
+            ws = torch.empty(max(hbl.workspace_bytes(hbl.OP_MATMUL, M, base.K, base.N), 16), dtype=torch.uint8, device="cuda")
+            wsf = torch.empty(hbl.workspace_bytes(hbl.OP_FORWARD_INT4, M, base.K, base.N), dtype=torch.uint8, device="cuda")
+            y = torch.empty((M, base.N), dtype=torch.bfloat16, device="cuda")
+            y_eager = hbl.matmul_dequant(codes, 4, d, wps[0], a, base.K, workspace=ws)
+            f_eager = hbl.forward(xd, wps[0], a, 4, workspace=wsf)
+            res = {}
+            codes2, d2 = torch.empty_like(codes), torch.empty_like(d)
+            for kind in ("gemm", "forward", "prep"):
+                def body(i):
+                    if kind == "gemm":
+                        hbl.matmul_dequant(codes, 4, d, wps[i % R], a, base.K, workspace=ws, out=y)
+                    elif kind == "forward":
+                        hbl.forward(xd, wps[i % R], a, 4, workspace=wsf, out=y)
+                    else:
+                        hbl.quantize_act(xd, 4, out=(codes2, d2))
+                s_ = torch.cuda.Stream()
+                s_.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s_):
+                    for i in range(3):
+                        body(i)
+                torch.cuda.current_stream().wait_stream(s_)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(R):
+                        body(i)
+                reps = 10
+                g.replay()
+                torch.cuda.synchronize()
+                f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                f0.record()
+                for _ in range(reps):
+                    g.replay()
+                f1.record()
+                torch.cuda.synchronize()
+                res[kind] = 1e3 * f0.elapsed_time(f1) / (reps * R)
+                # the last captured call used wps[R-1], a copy of wps[0]: same result as eager
+                if kind != "prep":
+                    ref = y_eager if kind == "gemm" else f_eager
+                    assert torch.equal(y, ref), f"graph replay differs from eager ({kind}, M={M})"
+            gbytes = base.N * base.K / 4 + M * base.K / 2 + M * base.N * 2 + M * 4
+            # inside the forward, 5..64 tokens, the matmul reads its codes in the
+            # decode-blocked layout (the stage call above reads row-major codes):
+            # its time is the forward's less a prep stage call of the same tokens
+            # (one token: the forward is a single fused kernel, no prep stage)
+            out[f"decode_7b_m{M}"] = {"gemm_us": res["gemm"], "gemm_gbps": gbytes / (res["gemm"] / 1e6) / 1e9,
+                                      "gemm_hbm_frac": gbytes / (res["gemm"] / 1e6) / 1e9 / PEAK_HBM_GBS,
+                                      "forward_us": res["forward"], "tokens_per_s": M / (res["forward"] / 1e6),
+                                      "timing": f"graph replay of {R} back-to-back calls over {R} weight copies"}
+            if M >= 5:
+                fg = res["forward"] - res["prep"]
+                out[f"decode_7b_m{M}"].update({"prep_us": res["prep"], "forward_gemm_us": fg,
+                                               "forward_gemm_hbm_frac": gbytes / (fg / 1e6) / 1e9 / PEAK_HBM_GBS})
+        # a plain read of one 16 MiB weight copy per call (a torch row-wise
+        # max-reduction over it: 4096 rows of 4 KiB; the value is not used) in the
+        # same graph-replay harness over the same 40 copies
+        red = torch.empty((base.N,), dtype=torch.int64, device="cuda")
+
+        def read_body(i):
+            torch.amax(wps[i % R].view(torch.int64), dim=1, out=red)
+        s_ = torch.cuda.Stream()
+        s_.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_):
+            for i in range(3):
+                read_body(i)
+        torch.cuda.current_stream().wait_stream(s_)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                read_body(i)
         g.replay()
-    f1.record()
-    torch.cuda.synchronize()
-    read_us = 1e3 * f0.elapsed_time(f1) / (10 * R)
-    wbytes = base.N * base.K / 4
-    out["plain_read_16mib"] = {"us": read_us, "gbps": wbytes / (read_us / 1e6) / 1e9,
-                               "hbm_frac": wbytes / (read_us / 1e6) / 1e9 / PEAK_HBM_GBS,
-                               "timing": f"graph replay of {R} torch row-wise max-reductions, one {R}-way rotated "
-                                         "weight copy each (a library read of the decode matmul's weight stream)"}
-    for M in (1, 16, 64):
-        out[f"decode_7b_m{M}"]["gemm_over_plain_read"] = out[f"decode_7b_m{M}"]["gemm_us"] / read_us
-    out["decode_attn_7b_kv3"] = attention_extra(torch, hbl, synthetic, args)
-    out["backward_wdown_7b_int4"] = backward_extra(torch, hbl, synthetic, args)
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for _ in range(10):
+            g.replay()
+        f1.record()
+        torch.cuda.synchronize()
+        read_us = 1e3 * f0.elapsed_time(f1) / (10 * R)
+        wbytes = base.N * base.K / 4
+        out["plain_read_16mib"] = {"us": read_us, "gbps": wbytes / (read_us / 1e6) / 1e9,
+                                   "hbm_frac": wbytes / (read_us / 1e6) / 1e9 / PEAK_HBM_GBS,
+                                   "timing": f"graph replay of {R} torch row-wise max-reductions, one {R}-way rotated "
+                                             "weight copy each (a library read of the decode matmul's weight stream)"}
+        for M in (1, 16, 64):
+            out[f"decode_7b_m{M}"]["gemm_over_plain_read"] = out[f"decode_7b_m{M}"]["gemm_us"] / read_us
+    if want("attention"):
+        out["decode_attn_7b_kv3"] = attention_extra(torch, hbl, synthetic, args)
+    if want("backward"):
+        out["backward_wdown_7b_int4"] = backward_extra(torch, hbl, synthetic, args)
     return out
 
 
@@ -546,10 +555,31 @@ def backward_extra(torch, hbl, synthetic, args):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     flops = 2 * 2.0 * w.M * w.N * w.K            # two products of 2MNK each
+    # context, not part of the path: the input-gradient product dy . W_t
+    # through the library GEMM (torch.mm, hipBLASLt) on the same operands
+    wt = wbt.t().contiguous()                     # [N][K] bf16
+    lib = {}
+    for name, fn in (("bf16_out", lambda: torch.mm(dy, wt)),
+                     ("fp32_out", lambda: torch.mm(dy, wt, out_dtype=torch.float32))):
+        try:
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            lib[name] = e0.elapsed_time(e1) / n
+        except (TypeError, RuntimeError):
+            lib[name] = None
+    del wt
     return {"M": w.M, "K": w.K, "N": w.N, "ms_per_step": ms, "tokens_per_s": w.M / (ms / 1e3),
             "matmul_tflops_if_all_time": flops / (ms / 1e3) / 1e12,
+            "library_dxh_product_ms": lib,
             "timing": "events around back-to-back hbl_backward calls (both products, transform, norm, gain and "
-                      "weight gradients); per-kernel split in the rocprofv3 trace"}
+                      "weight gradients); per-kernel split in the rocprofv3 trace; library_dxh_product_ms: "
+                      "torch.mm of the same dy and ternary weights, for comparison with one product's kernel time"}
 
 
 def attention_extra(torch, hbl, synthetic, args):

@@ -20,8 +20,8 @@
 //  * prefill on the fp6 x fp4 instruction (INT4 codes in format 6, more than
 //    64 tokens): described with gemm_fp6_kernel below.
 //  * decode (M <= 64): weight streaming.  Every wave owns 16 output channels
-//    (64 per workgroup above 32 tokens) and a share of the 256-k blocks of its
-//    K range; its packed weights are loaded with 16-byte loads straight into
+//    (64 per workgroup above 32 tokens when the codes are row-major) and a
+//    share of the 256-k blocks of its K range; its packed weights are loaded with 16-byte loads straight into
 //    registers (each weight byte is read from HBM once), and
 //    v_mfma_i32_16x16x64_i8 runs with the channels on the MFMA's M side and 16
 //    tokens on its N side per token group.  When K is split, the partials of
@@ -1335,7 +1335,7 @@ static void launch_t(const GemmArgs& a) {
 }
 
 // fp6 codes with at most 64 tokens: the split decode matmul (64 channels per
-// workgroup; K split as the plan says above 32 tokens, unsplit below, where
+// workgroup; K split as the row-major plan says above 32 tokens, unsplit below, where
 // only stage calls bring fp6 codes).
 template <int OUT>
 static void launch_decode_fp6(const GemmArgs& a) {

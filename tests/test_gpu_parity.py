@@ -466,16 +466,17 @@ def test_single_launch_decode(bits, M, K, N, xdt, gain):
 
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("M,K,N", [(17, 4096, 272), (33, 16384, 4096), (64, 16384, 4096), (64, 1024, 48),
-                                   (40, 512, 96)])
+                                   (40, 512, 96), (33, 32768, 272), (64, 32768, 4096)])
 def test_split_k_decode_reduction_in_kernel(bits, M, K, N):
-    """33..64 tokens: the forward's matmul splits K and the last workgroup of
-    each channel tile sums the partials; the stage calls sum them in a
-    separate reduction kernel (17..32 tokens run unsplit: the 17-token case
-    checks that path the same way).  Same codes, exact integer sums: equal bit for
-    bit, with a workspace that starts full of 0xFF (the first kernel clears
-    the arrival counters) and over repeated calls on it whose inputs
-    alternate in sign, so partial sums left over from the call before would
-    show."""
+    """33..64 tokens at K = 32768: the forward's matmul splits K and the last
+    workgroup of each channel tile sums the partials; the stage calls (row-
+    major codes) split at every K and sum in a separate reduction kernel.  Up
+    to K = 16384 the forward runs unsplit on its decode-blocked codes, and
+    17..32 tokens run unsplit everywhere: those cases check the same way.
+    Same codes, exact integer sums: equal bit for bit, with a workspace that
+    starts full of 0xFF (the first kernel clears the arrival counters) and
+    over repeated calls on it whose inputs alternate in sign, so partial
+    sums left over from the call before would show."""
     w = synthetic.Workload("t", M, K, N, bits, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, 9 * M + K + N)
     x, xb, wl = synthetic.make_inputs(w)
     wp, a = hbl.quantize_weights(dev(wl))
@@ -493,14 +494,15 @@ def test_split_k_decode_reduction_in_kernel(bits, M, K, N):
         assert torch.equal(y.view(torch.int16), y_refs[i % 2].view(torch.int16)), i
 
 
-@pytest.mark.parametrize("M", [1, 24, 40, 64])
-def test_forward_graph_replays(M):
+@pytest.mark.parametrize("M,K", [(1, 16384), (24, 16384), (40, 16384), (64, 16384), (48, 32768)])
+def test_forward_graph_replays(M, K):
     """The forward captured once in a HIP graph and replayed with new inputs
     written into the captured buffers between replays (eager work and a
     synchronisation in between): every replay equals the eager forward on the
-    same input.  Covers the one-kernel decode (M = 1) and the split-K decode
-    whose arrival counters the prep kernel clears inside the graph."""
-    K, N, bits = 16384, 4096, 4
+    same input.  Covers the one-kernel decode (M = 1), the unsplit decode on
+    decode-blocked codes, and the split-K decode (K = 32768) whose arrival
+    counters the prep kernel clears inside the graph."""
+    N, bits = 4096, 4
     w = synthetic.Workload("t", M, K, N, bits, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, 13 * M + 5)
     x, xb, wl = synthetic.make_inputs(w)
     wp, a = hbl.quantize_weights(dev(wl))

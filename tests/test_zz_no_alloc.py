@@ -31,14 +31,17 @@ def layer_inputs(M, K, N, bits, seed):
 
 
 # (bits, first call (M, K, N), second call, smaller): the fp6 prefill then a
-# split-K decode; split-K decode then a smaller split-K decode (partials and
-# counters left by the first); INT8 prefill then the one-kernel decode; the
-# largest INT8 problem that fits the scratch, then a split-K decode.
+# decode on decode-blocked codes; two such decodes; INT8 prefill then the
+# one-kernel decode; the largest INT8 problem that fits the scratch, then a
+# blocked decode; a split-K decode (K = 32768) then a smaller one (partials
+# and arrival counters left by the first).
 CASES = [
     (4, (1000, 16384, 512), (40, 16384, 4096)),
     (4, (64, 16384, 4096), (33, 4096, 272)),
     (8, (300, 2048, 272), (1, 16384, 4096)),
     (8, (1900, 16384, 272), (64, 8192, 528)),
+    (4, (64, 32768, 4096), (33, 32768, 272)),
+    (8, (48, 32768, 528), (40, 32768, 272)),
 ]
 
 

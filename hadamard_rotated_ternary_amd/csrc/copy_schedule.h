@@ -93,6 +93,27 @@ struct Fp6Small : Fp6 {
   static constexpr int wait_prologue() { return 3 * A_COPIES + B_COPIES; }
 };
 
+// gemm_fp6_kernel with 256x192 tiles (four waves of 128x96): an A stage is
+// still 6 copies per wave, a B pair 3 (192 columns of 64 bytes), and the
+// second MFMA step has 12 matrix instructions: even stages take the A copies
+// after MFMAs 1, 3, ..., 11; odd stages the B copies after MFMAs 0-2 and the
+// A copies after 3-8.  Buffers, slots, stage choice and prologue as Fp6.
+struct Fp6Wide : Fp6 {
+  static constexpr int A_COPIES = 6, B_COPIES = 3;
+  static constexpr int MFMAS = 12;
+  static constexpr Copy after(int i, bool odd) {
+    if (odd) {
+      if (i < B_COPIES) return {2, i};
+      if (i < B_COPIES + A_COPIES) return {1, i - B_COPIES};
+      return {0, 0};
+    }
+    if ((i & 1) && (i >> 1) < A_COPIES) return {1, i >> 1};
+    return {0, 0};
+  }
+  static constexpr int wait(bool odd) { return odd ? 2 * A_COPIES : 2 * A_COPIES + B_COPIES; }
+  static constexpr int wait_prologue() { return 3 * A_COPIES + B_COPIES; }
+};
+
 // Issue log of one wave's copy instructions.
 struct Log {
   static constexpr int CAP = 4096;

@@ -303,20 +303,27 @@ constexpr int F6_BPROW = 2 * F6_BK / 4;            // 64 bytes of packed weights
 constexpr int F6_B_PAIR = PBN * F6_BPROW;          // 16 KiB
 constexpr int F6_B_BASE = F6_NBUF * F6_A_STAGE;    // B slots after the A ring
 constexpr int F6_LDS = F6_B_BASE + 2 * F6_B_PAIR;  // 128 KiB
-// The same pipeline on T x T tiles (T = 256 above, or 128: four waves of
-// 64 x 64, for problems with fewer 256 x 256 tiles than compute units).
-template <int T>
+// The same pipeline on T x TN tiles: T = TN = 256 above; T = TN = 128 (four
+// waves of 64 x 64) for problems with fewer 256 x 256 tiles than compute
+// units; T = 256, TN = 192 (four waves of 128 x 96) where N is cut in 192s
+// more evenly than in 256s -- N = 3072 at M = 4096 is 256 such tiles, one
+// per compute unit, against 192 tiles of 256 x 256 (a quarter of the chip
+// idle) or 768 of 128 x 128 (one and a half rounds of two per CU).
+template <int T, int TN = T>
 struct F6Geo {
-  static constexpr int RB = T / 64;                  // 32-row (and 32-column) blocks per wave
+  static constexpr int RBM = T / 64;                 // 32-row blocks per wave
+  static constexpr int RBN = TN / 64;                // 32-column blocks per wave
   static constexpr int A_STAGE = T * F6_AROW;        // bytes of one A stage
-  static constexpr int B_PAIR = T * F6_BPROW;        // bytes of one B stage pair
+  static constexpr int B_PAIR = TN * F6_BPROW;       // bytes of one B stage pair
   static constexpr int B_BASE = F6_NBUF * A_STAGE;
   static constexpr int LDS = B_BASE + 2 * B_PAIR;
   static constexpr int A_LOADS = A_STAGE / 1024 / 4, B_LOADS = B_PAIR / 1024 / 4;
-  static constexpr int READS = RB + 3 * RB;          // LDS reads per stage: B blocks, then A units
+  static constexpr int READS = RBN + 3 * RBM;        // LDS reads per stage: B blocks, then A units
 };
 static_assert(F6Geo<256>::LDS == F6_LDS && F6Geo<256>::A_STAGE == F6_A_STAGE && F6Geo<256>::B_PAIR == F6_B_PAIR,
               "256-tile geometry");
+static_assert(F6Geo<256, 192>::LDS == 120 * 1024 && F6Geo<256, 192>::B_LOADS == 3 && F6Geo<256, 192>::READS == 15,
+              "256 x 192 geometry");
 
 // gfx950 LDS: 64 banks of 4 bytes; a 16-byte read serves 16 consecutive
 // lanes per cycle, so 16 consecutive rows reading the same logical unit must
@@ -335,19 +342,21 @@ HBL_DEV void lds_copy16s(const void* gbase, uint32_t voff, uint32_t lds_base) {
 }
 
 // US: stages per loop trip (4; 2 when K = 256), so that LDS buffer numbers are
-// compile-time constants.  T: tile size (256, or 128 with two workgroups per CU).
-template <int OUT, int US, int T = 256>
+// compile-time constants.  T x TN: tile rows x columns (256 x 256 or 256 x 192,
+// one workgroup per CU; 128 x 128 with two).
+template <int OUT, int US, int T = 256, int TN = T>
 __global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ dscale,
     const float* __restrict__ walpha, void* __restrict__ Y, int M, int N, int K, int tiles_m, int tiles_n) {
-  using G = F6Geo<T>;
-  constexpr int RB = G::RB;                          // 32 x 32 blocks per wave: RB x RB
-  constexpr int WT = T / 2;                          // wave tile
+  using G = F6Geo<T, TN>;
+  constexpr int RBM = G::RBM, RBN = G::RBN;          // 32 x 32 blocks per wave: RBM x RBN
+  constexpr int WT = T / 2, WTN = TN / 2;            // wave tile
+  static_assert((T == 256 && (TN == 256 || TN == 192)) || (T == 128 && TN == 128), "shipped tile shapes");
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
-  constexpr int A_LOADS = G::A_LOADS, B_LOADS = G::B_LOADS;   // 6 and 4 (T = 256), 3 and 2 (T = 128)
-  using S6 = std::conditional_t<T == 256, sched::Fp6, sched::Fp6Small>;
+  constexpr int A_LOADS = G::A_LOADS, B_LOADS = G::B_LOADS;   // 6 and 4 (256 x 256), 6 and 3 (256 x 192), 3 and 2
+  using S6 = std::conditional_t<T == 256, std::conditional_t<TN == 256, sched::Fp6, sched::Fp6Wide>, sched::Fp6Small>;
   static_assert(S6::NBUF == F6_NBUF && S6::WAVES == 4 && S6::A_COPIES == A_LOADS && S6::B_COPIES == B_LOADS &&
-                    S6::MFMAS == (T == 256 ? 16 : 8),
+                    S6::MFMAS == (T == 256 ? RBM * RBN : 8),
                 "schedule model and kernel geometry agree");
   static_assert(sched::fp6_ok<S6>(2) && sched::fp6_ok<S6>(4) && sched::fp6_ok<S6>(8) && sched::fp6_ok<S6>(20) &&
                     sched::fp6_ok<S6>(256),
@@ -361,7 +370,7 @@ __global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
   const int gm = min(tiles_m - first_m, GM);
   const int in_g = logical % per_group;
   const int m0 = (first_m + in_g % gm) * T;
-  const int n0 = (in_g / gm) * T;
+  const int n0 = (in_g / gm) * TN;
   __shared__ __attribute__((aligned(16))) float srow[T];   // epilogue row scales (row_scale_copy)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -388,7 +397,7 @@ __global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
   }
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
-    const int P = (j * 4 + wave) * 64 + lane, col = P >> 2, u = (P & 3) ^ f6_bswz(col);
+    const int P = (j * 4 + wave) * 64 + lane, col = P >> 2, u = (P & 3) ^ f6_bswz(col);   // col < TN
     const int nr = min(n0 + col, N - 1) - n0;       // tiled: 16-row blocks of 4K bytes, 64-byte row segments
     b_off[j] = (uint32_t)(nr >> 4) * (uint32_t)K * 4u + (uint32_t)(nr & 15) * 64u + 16u * u;
   }
@@ -401,31 +410,31 @@ __global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
     lds_copy16s(b_tile + (size_t)p * 1024, b_off[j], lds0 + G::B_BASE + sl * G::B_PAIR + (j * 4 + wave_s) * 1024);
   };
 
-  v16f acc[RB][RB];
+  v16f acc[RBM][RBN];
 #pragma unroll
-  for (int i = 0; i < RB; ++i)
+  for (int i = 0; i < RBM; ++i)
 #pragma unroll
-    for (int j = 0; j < RB; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < RBN; ++j) acc[i][j] = v16f{};
 
   // Register fragments of one stage: per lane 48 A bytes (32-k groups 2g and
   // 2g+1 of four 32-row blocks), kept as one 12-dword vector per block so the
   // two 6-dword MFMA operands (8-dword vectors, the last two unused) are
   // sub-ranges of it, and 16 packed B bytes
-  // (the same groups of four 32-column blocks).  Read r of a stage: r < 4 the
-  // B block r, else A block (r-4)/3, unit (r-4)%3.
+  // (the same groups of the 32-column blocks).  Read r of a stage: r < RBN
+  // the B block r, else A block (r-RBN)/3, unit (r-RBN)%3.
   struct Frag {
-    v16i a[RB];
-    v4i b[RB];
+    v16i a[RBM];
+    v4i b[RBN];
   };
   // read r of stage kt (A buffer kt % 4, B slot (kt / 2) % 2, half kt % 2)
   auto read1 = [&](Frag& f, int r, int kt) __attribute__((always_inline)) {
     const uint8_t* sa = smem + (kt & (F6_NBUF - 1)) * G::A_STAGE;
-    if (r < RB) {
-      const int n = wn * WT + r * 32 + l32;
+    if (r < RBN) {
+      const int n = wn * WTN + r * 32 + l32;
       const uint8_t* sb = smem + G::B_BASE + ((kt >> 1) & 1) * G::B_PAIR;
       f.b[r] = *reinterpret_cast<const v4i*>(sb + n * F6_BPROW + 16 * ((2 * (kt & 1) + g) ^ f6_bswz(n)));
     } else {
-      const int rb = (r - RB) / 3, t = (r - RB) % 3;
+      const int rb = (r - RBN) / 3, t = (r - RBN) % 3;
       const int row = wm * WT + rb * 32 + l32;
       int pu = 3 * g + t + f6_arot(row);
       if (pu >= 6) pu -= 6;
@@ -483,12 +492,12 @@ __global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
   auto stage = [&](int kt, int u, const Frag& cur, Frag& nxt, v8i* bf0, v8i* bf1) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < RBM; ++rb) {
       const v8i af = aop(cur, 0, rb);
 #pragma unroll
-      for (int cb = 0; cb < RB; ++cb) {
+      for (int cb = 0; cb < RBN; ++cb) {
         mfma(af, bf0[cb], acc[rb][cb]);
-        if (cb == 1) bf1[rb] = bexp1(cur, 1, rb);
+        if (cb == 1 && rb < RBN) bf1[rb] = bexp1(cur, 1, rb);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -497,21 +506,30 @@ __global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
     const int akt = S6::a_stage(kt, KT);
     const int bp = S6::b_pair(kt, KT);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < RBM; ++rb) {
       const v8i af = aop(cur, 1, rb);
 #pragma unroll
-      for (int cb = 0; cb < RB; ++cb) {
-        const int i = rb * RB + cb;
+      for (int cb = 0; cb < RBN; ++cb) {
+        const int i = rb * RBN + cb;
         mfma(af, bf1[cb], acc[rb][cb]);
         if constexpr (T == 256) {
+          // MF = RBM * RBN MFMAs (16, or 12 with 192 columns) and READS LDS
+          // reads (16, or 15): read i after MFMA i, and the reads past MF
+          // (the last A block's units) after the last MFMAs
+          constexpr int MF = RBM * RBN, XR = G::READS - MF;
+          static_assert(XR >= 0 && XR <= MF, "reads per stage");
           read1(nxt, i, u + 1);
+          if (i >= MF - XR) read1(nxt, i + XR, u + 1);
           // odd stage: B pair into the slot this pair of stages used, then A;
           // even stage: the A copies of stage kt+4 after MFMAs 1, 3, ..., 11
           // (u is kt modulo a multiple of 4, or kt itself when K = 256)
           const sched::Copy cp = S6::after(i, u & 1);
           if (cp.kind == 2) dmaB(cp.j, bp, S6::b_slot(u));
           else if (cp.kind == 1) dmaA(cp.j, akt, S6::a_buf(u));
-          if (i >= 8 && !(i & 1)) bf0[(i - 8) >> 1] = bexp1(nxt, 0, (i - 8) >> 1);
+          // the next stage's B operands, expanded after every other one of
+          // the last 2 * RBN MFMAs (their reads were the first RBN)
+          constexpr int E0 = MF - 2 * RBN;
+          if (i >= E0 && !((i - E0) & 1)) bf0[(i - E0) >> 1] = bexp1(nxt, 0, (i - E0) >> 1);
         } else {
           // four MFMAs: two reads and two copy slots after each; the next
           // stage's B expansion after the last two (its B reads came first)
@@ -549,9 +567,9 @@ __global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 #pragma unroll
   for (int r = 0; r < G::READS; ++r) read1(f0, r, 0);
-  v8i bf0[RB], bf1[RB];
+  v8i bf0[RBN], bf1[RBN];
 #pragma unroll
-  for (int cb = 0; cb < RB; ++cb) bf0[cb] = bexp1(f0, 0, cb);
+  for (int cb = 0; cb < RBN; ++cb) bf0[cb] = bexp1(f0, 0, cb);
   for (int kt = 0; kt < KT; kt += US) {
 #pragma unroll
     for (int u = 0; u < US; u += 2) {
@@ -568,14 +586,14 @@ __global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
   const float aw = OUT == OUT_ACC_I32 ? 0.f : fmaxf(walpha[0], kEpsQ);
   if constexpr (OUT == OUT_BF16) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");   // every wave is done with the ring
-    static_assert(4 * 64 * (RB * 64 + 32) <= G::LDS, "staging fits the ring");
-    store_bf16_staged<RB, RB / 2>(smem + wave * (64 * (RB * 64 + 32)), static_cast<uint16_t*>(Y), srow + wm * WT, aw,
-                                  M, N, m0 + wm * WT, n0 + wn * WT, lane,
+    static_assert(4 * 64 * (RBN * 64 + 32) <= G::LDS, "staging fits the ring");
+    store_bf16_staged<RBN, RBM / 2>(smem + wave * (64 * (RBN * 64 + 32)), static_cast<uint16_t*>(Y), srow + wm * WT,
+                                    aw, M, N, m0 + wm * WT, n0 + wn * WTN, lane,
                                   [&](int rb, int cb, int r) { return acc[rb][cb][r]; });
   } else {
     __syncthreads();
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < RBM; ++rb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rl = wm * WT + rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -583,8 +601,8 @@ __global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
         if (m >= M) continue;
         const float t = OUT == OUT_ACC_I32 ? 0.f : srow[rl] * aw;
 #pragma unroll
-        for (int cb = 0; cb < RB; ++cb) {
-          const int n = n0 + wn * WT + cb * 32 + l32;
+        for (int cb = 0; cb < RBN; ++cb) {
+          const int n = n0 + wn * WTN + cb * 32 + l32;
           if (n < N) store_out<OUT>(Y, (size_t)m * N + n, (int)acc[rb][cb][r], t);
         }
       }
@@ -1344,16 +1362,42 @@ static void launch_decode_fp6(const GemmArgs& a) {
 }
 
 constexpr int kFp6SmallTileBelow = 256;
+constexpr int kCUs = 256;   // compute units of the part: one 256-row tile each per round
 
-template <int OUT, int T>
+template <int OUT, int T, int TN = T>
 static void launch_fp6_t(const GemmArgs& a) {
-  const int tm = (a.M + T - 1) / T, tn = (a.N + T - 1) / T;
+  const int tm = (a.M + T - 1) / T, tn = (a.N + TN - 1) / TN;
   if (a.K == 256)
-    hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 2, T>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack, a.dscale,
-                       a.walpha, a.out, a.M, a.N, a.K, tm, tn);
+    hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 2, T, TN>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,
+                       a.dscale, a.walpha, a.out, a.M, a.N, a.K, tm, tn);
   else
-    hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 4, T>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack, a.dscale,
-                       a.walpha, a.out, a.M, a.N, a.K, tm, tn);
+    hipLaunchKernelGGL((gemm_fp6_kernel<OUT, 4, T, TN>), dim3(tm * tn), dim3(256), 0, a.stream, a.codes, a.wpack,
+                       a.dscale, a.walpha, a.out, a.M, a.N, a.K, tm, tn);
+}
+
+// Tile shape of the fp6 x fp4 matmul.  256 x 192 when it gives the busiest
+// compute unit less work than 256 x 256 -- rounds of 256 resident tiles times
+// the tile's work, a 256 x 192 tile counted at 0.78 of a square one (three
+// quarters of the products with a little less operand reuse) -- and fills at
+// least three quarters of its last round (N = 3072: 256 tiles at M = 4096,
+// 512 at M = 8192, against 192 and 384 square ones).  Otherwise 256 x 256,
+// or 128 x 128 when there are fewer 256 x 256 tiles than compute units.
+enum F6Tile { kTile256, kTile256x192, kTile128 };
+static F6Tile fp6_tile(int64_t M, int64_t N) {
+  const int64_t tm = (M + 255) / 256;
+  const int64_t t256 = tm * ((N + 255) / 256), t192 = tm * ((N + 191) / 192);
+  const int64_t r256 = (t256 + kCUs - 1) / kCUs, r192 = (t192 + kCUs - 1) / kCUs;
+  if (r192 * 78 < r256 * 100 && 4 * t192 >= 3 * kCUs * r192) return kTile256x192;
+  return t256 < kFp6SmallTileBelow ? kTile128 : kTile256;
+}
+
+template <int OUT>
+static void launch_fp6_o(const GemmArgs& a) {
+  switch (fp6_tile(a.M, a.N)) {
+    case kTile256x192: launch_fp6_t<OUT, 256, 192>(a); break;
+    case kTile128: launch_fp6_t<OUT, 128>(a); break;
+    default: launch_fp6_t<OUT, 256>(a); break;
+  }
 }
 
 hipError_t launch_gemm_fp6(const GemmArgs& a) {
@@ -1366,13 +1410,10 @@ hipError_t launch_gemm_fp6(const GemmArgs& a) {
     }
     return hipGetLastError();
   }
-  // 256 x 256 tiles unless they would leave compute units idle (fewer tiles
-  // than the 256 CUs of the part): then 128 x 128 tiles, four times as many
-  const bool small = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256) < kFp6SmallTileBelow;
   switch (a.out_kind) {
-    case OUT_ACC_I32: small ? launch_fp6_t<OUT_ACC_I32, 128>(a) : launch_fp6_t<OUT_ACC_I32, 256>(a); break;
-    case OUT_F32: small ? launch_fp6_t<OUT_F32, 128>(a) : launch_fp6_t<OUT_F32, 256>(a); break;
-    default: small ? launch_fp6_t<OUT_BF16, 128>(a) : launch_fp6_t<OUT_BF16, 256>(a); break;
+    case OUT_ACC_I32: launch_fp6_o<OUT_ACC_I32>(a); break;
+    case OUT_F32: launch_fp6_o<OUT_F32>(a); break;
+    default: launch_fp6_o<OUT_BF16>(a); break;
   }
   return hipGetLastError();
 }

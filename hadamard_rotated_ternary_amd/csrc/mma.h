@@ -108,7 +108,8 @@ HBL_DEV void row_scale_copy(const float* __restrict__ dscale, int m0, int M, flo
   if (wave < ROWS / 64) lds_copy4(dscale + min(m0 + 64 * wave + lane, M - 1), srow + 64 * wave);
 }
 
-// bf16 output of a wave's (64*HALVES) x (32*CB) accumulator block through
+// bf16 output of a wave's (64*HALVES) x (32*CB) accumulator block (CB = 2,
+// 3 or 4) through
 // LDS: the block is rounded into the wave's own LDS rows, 64 rows at a time, then
 // written with 16-byte stores as whole row segments (instead of 2-byte
 // stores scattered over 64 rows).  getv(rb, cb, r) returns the unscaled
@@ -123,7 +124,8 @@ HBL_DEV void store_bf16_staged(uint8_t* stage, uint16_t* Y, const float* srow, f
                                int ncol0, int lane, GetV getv) {
   constexpr int ER = CB * 64 + 32;             // staged row bytes
   constexpr int LPR = CB * 4;                  // lanes per row on the way out (16 bytes each)
-  constexpr int RPI = 64 / LPR;                // rows per store instruction
+  constexpr int RPI = 64 / LPR;                // rows per store instruction (lanes past RPI * LPR idle)
+  constexpr int NI = (64 + RPI - 1) / RPI;     // store instructions per 64 rows
   const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int hf = 0; hf < HALVES; ++hf) {
@@ -141,8 +143,9 @@ HBL_DEV void store_bf16_staged(uint8_t* stage, uint16_t* Y, const float* srow, f
     }
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
 #pragma unroll
-    for (int i = 0; i < 64 / RPI; ++i) {
+    for (int i = 0; i < NI; ++i) {
       const int rl = RPI * i + lane / LPR, c16 = lane % LPR;
+      if (64 % LPR != 0 && (lane >= RPI * LPR || rl >= 64)) continue;
       const int m = mrow0 + 64 * hf + rl, n = ncol0 + 8 * c16;
       const uint4 v = *reinterpret_cast<const uint4*>(stage + rl * ER + 16 * c16);
       if (m < M && n < N) *reinterpret_cast<uint4*>(Y + (size_t)m * N + n) = v;

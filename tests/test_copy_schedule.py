@@ -8,7 +8,7 @@ schedules with a planted mistake -- more copies than a stage has (the race
 of an earlier fp6 schedule: two extra copies landed in the buffer being
 read), a wait that leaves a needed copy in flight, a copy into the buffer
 being read, a ring too short for its lead, the 256-tile counts applied to
-the 128-tile schedule -- fail to compile.
+the 128-tile or the 256 x 192 schedule -- fail to compile.
 """
 import os
 import shutil
@@ -36,6 +36,9 @@ def test_shipped_schedules_pass():
         // the 128x128 tile of the same kernel
         static_assert(fp6_ok<Fp6Small>(2) && fp6_ok<Fp6Small>(6) && fp6_ok<Fp6Small>(16)
                       && fp6_ok<Fp6Small>(128), "");
+        // the 256x192 tile
+        static_assert(fp6_ok<Fp6Wide>(2) && fp6_ok<Fp6Wide>(4) && fp6_ok<Fp6Wide>(16)
+                      && fp6_ok<Fp6Wide>(128), "");
         // the int8 instruction kernel: 10 copies per stage (INT8), 6 (INT4)
         static_assert(ring_ok<Ring3>(1, 10) && ring_ok<Ring3>(2, 10) && ring_ok<Ring3>(64, 10), "");
         static_assert(ring_ok<Ring3>(5, 6) && ring_ok<Ring3>(64, 6), "");
@@ -98,6 +101,27 @@ def test_broken_fp6_schedules_fail(name, body):
         struct Bad : Fp6Small { static constexpr int wait_prologue() { return Fp6::wait_prologue(); } };"""),
 ])
 def test_broken_small_tile_schedules_fail(name, body):
+    assert not compiles(body + '\nstatic_assert(fp6_ok<Bad>(16), "");'), name
+
+
+@pytest.mark.parametrize("name,body", [
+    ("a fourth B copy per pair (the 256-column count)", """
+        struct Bad : Fp6Wide {
+          static constexpr Copy after(int i, bool odd) {
+            if (odd && i == 9) return {2, 3};
+            return Fp6Wide::after(i, odd);
+          }
+        };"""),
+    ("the 256-column B count with the 192-column slots", """
+        struct Bad : Fp6Wide { static constexpr int B_COPIES = 4; };"""),
+    ("wait counts of the square tile", """
+        struct Bad : Fp6Wide { static constexpr int wait(bool odd) { return Fp6::wait(odd); } };"""),
+    ("last A copy of even stages past the twelve MFMAs", """
+        struct Bad : Fp6Wide {
+          static constexpr int MFMAS = 11;
+        };"""),
+])
+def test_broken_wide_tile_schedules_fail(name, body):
     assert not compiles(body + '\nstatic_assert(fp6_ok<Bad>(16), "");'), name
 
 

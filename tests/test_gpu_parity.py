@@ -272,6 +272,23 @@ def test_matmul_bit_exact(bits, M, K, N):
     np.testing.assert_array_equal(acc, acc_or)
 
 
+@pytest.mark.parametrize("M,K,N", [(4059, 512, 3056), (4096, 256, 3072), (8192, 1024, 3072)])
+def test_fp6_wide_tile_bit_exact(M, K, N):
+    """Format 6 codes on the 256 x 192 tile of the fp6 x fp4 matmul (chosen
+    for these N): int32 accumulators equal the oracle's on sampled rows --
+    the first and last tile rows (ragged at M = 4059), every column (ragged
+    last tile at N = 3056) -- with extreme codes in the first row."""
+    rng = np.random.default_rng(M + 3 * K + N)
+    q = rng.integers(-8, 8, (M, K)).astype(np.int8)
+    q[0, :] = -8
+    q[M - 1, :] = 7
+    wt = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    wt[N - 1, :] = -1
+    acc = host(hbl.gemm_ternary(dev(pack_codes(q, 6)), 6, dev(pack_ternary(wt)), K))
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(M - 300, M), synthetic.sample_rows(M, 32)]))
+    np.testing.assert_array_equal(acc[rows], oracle.gemm_ternary(np.ascontiguousarray(q[rows]), wt))
+
+
 # ------------------------------------------------------------------ whole layer
 
 def oracle_weights_dev(wt, alpha):
@@ -550,14 +567,17 @@ def test_fp6_matmul_repeatable_with_fresh_buffers():
 
 
 @pytest.mark.parametrize("M,K,N", [(65, 256, 16), (257, 1024, 272), (300, 2048, 512), (513, 16384, 256),
-                                   (1000, 4096, 4096), (1023, 2048, 1040), (4096, 1024, 4096), (8192, 16384, 4096)])
+                                   (1000, 4096, 4096), (1023, 2048, 1040), (4096, 1024, 4096), (8192, 16384, 4096),
+                                   (4059, 1024, 3056), (4000, 256, 3072), (4096, 8192, 3072), (8192, 2048, 3072)])
 def test_int4_prefill_fp6_path_equals_int8_instruction_path(M, K, N):
     """The fused INT4 forward for more than 64 tokens runs its matmul on the
     fp6 x fp4 instruction; the stage calls run the same codes through the
     int8 instruction (bit-exact against the oracle above).  Same codes, exact
     integer accumulators and the same dequantisation: equal bit for bit.
     Shapes with fewer than 256 tiles of 256 x 256 take 128 x 128 tiles (ragged
-    edges included); 4096 x 4096 and the 7B shape take 256 x 256."""
+    edges included); 4096 x 4096 and the 7B shape take 256 x 256; N = 3072
+    (and 3056, ragged in both M and N; K = 256, two stages per loop trip)
+    takes 256 x 192."""
     w = synthetic.Workload("t", M, K, N, 4, "bf16", "laplace", 0.05, max(1, K // 200), 100.0, M + 3 * K + N)
     x, xb, wl = synthetic.make_inputs(w)
     wp, a = hbl.quantize_weights(dev(wl))

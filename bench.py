@@ -433,6 +433,28 @@ def extras(torch, hbl, synthetic, args):
         R = 40
         wps = [wp0.clone() for _ in range(R)]
         xfull = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+
+        def graph_time(body):
+            s_ = torch.cuda.Stream()
+            s_.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s_):
+                for i in range(3):
+                    body(i)
+            torch.cuda.current_stream().wait_stream(s_)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(R):
+                    body(i)
+            g.replay()
+            torch.cuda.synchronize()
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            f0.record()
+            for _ in range(10):
+                g.replay()
+            f1.record()
+            torch.cuda.synchronize()
+            return 1e3 * f0.elapsed_time(f1) / (10 * R)
+
         for M in (1, 16, 64):
             xd = xfull[:M].contiguous()
             codes, d = hbl.quantize_act(xd, 4)
@@ -488,39 +510,37 @@ def extras(torch, hbl, synthetic, args):
                 fg = res["forward"] - res["prep"]
                 out[f"decode_7b_m{M}"].update({"prep_us": res["prep"], "forward_gemm_us": fg,
                                                "forward_gemm_hbm_frac": gbytes / (fg / 1e6) / 1e9 / PEAK_HBM_GBS})
-        # a plain read of one 16 MiB weight copy per call (a torch row-wise
-        # max-reduction over it: 4096 rows of 4 KiB; the value is not used) in the
-        # same graph-replay harness over the same 40 copies
+                # every workgroup of the matmul reads all M tokens' codes
+                # (M K / 2 bytes) from L2: the same bytes read by 256
+                # workgroups, nothing else, in the same harness
+                bdig = torch.empty((256,), dtype=torch.int32, device="cuda")
+                cf = graph_time(lambda i: hbl.broadcast_read(codes, 256, bdig))
+                out[f"decode_7b_m{M}"].update({"code_broadcast_read_us": cf,
+                                               "code_broadcast_bytes_per_wg": codes.numel() * codes.element_size()})
+        # a plain read of one 16 MiB weight copy per call in the same
+        # graph-replay harness over the same 40 copies: the hand-written
+        # streaming read (libhbl_calib.so: 64 KiB per workgroup, 1 KiB per wave
+        # instruction, every load issued up front), and a torch row-wise
+        # max-reduction (4096 rows of 4 KiB) as a library reference
         red = torch.empty((base.N,), dtype=torch.int64, device="cuda")
+        dig = torch.empty((base.N * base.K // 4 // 65536,), dtype=torch.int32, device="cuda")
 
-        def read_body(i):
-            torch.amax(wps[i % R].view(torch.int64), dim=1, out=red)
-        s_ = torch.cuda.Stream()
-        s_.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s_):
-            for i in range(3):
-                read_body(i)
-        torch.cuda.current_stream().wait_stream(s_)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(R):
-                read_body(i)
-        g.replay()
-        torch.cuda.synchronize()
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f0.record()
-        for _ in range(10):
-            g.replay()
-        f1.record()
-        torch.cuda.synchronize()
-        read_us = 1e3 * f0.elapsed_time(f1) / (10 * R)
+        read_us = graph_time(lambda i: hbl.stream_read(wps[i % R], dig))
+        lib_us = graph_time(lambda i: torch.amax(wps[i % R].view(torch.int64), dim=1, out=red))
         wbytes = base.N * base.K / 4
         out["plain_read_16mib"] = {"us": read_us, "gbps": wbytes / (read_us / 1e6) / 1e9,
                                    "hbm_frac": wbytes / (read_us / 1e6) / 1e9 / PEAK_HBM_GBS,
-                                   "timing": f"graph replay of {R} torch row-wise max-reductions, one {R}-way rotated "
-                                             "weight copy each (a library read of the decode matmul's weight stream)"}
+                                   "library_read_us": lib_us,
+                                   "timing": f"graph replay of {R} streaming reads (hbl_calib_stream_read), one "
+                                             f"{R}-way rotated weight copy each; library_read_us: torch row-wise "
+                                             "max-reductions of the same copies"}
         for M in (1, 16, 64):
-            out[f"decode_7b_m{M}"]["gemm_over_plain_read"] = out[f"decode_7b_m{M}"]["gemm_us"] / read_us
+            e = out[f"decode_7b_m{M}"]
+            e["gemm_over_plain_read"] = e["gemm_us"] / read_us
+            # the matmul's floor: the weight stream (plain read) or the code
+            # stream through L2 (broadcast read), whichever is longer
+            e["gemm_floor_us"] = max(read_us, e.get("code_broadcast_read_us", 0.0))
+            e["forward_gemm_over_floor"] = e.get("forward_gemm_us", e["gemm_us"]) / e["gemm_floor_us"]
     if want("attention"):
         out["decode_attn_7b_kv3"] = attention_extra(torch, hbl, synthetic, args)
     if want("backward"):

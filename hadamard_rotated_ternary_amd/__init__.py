@@ -84,6 +84,52 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+CALIB_PATH = os.path.join(_HERE, "libhbl_calib.so")
+CALIB_HEADER = os.path.join(_HERE, "..", "include", "hbl_calib.h")
+_calib = None
+
+
+def calib_lib() -> ctypes.CDLL:
+    """Load libhbl_calib.so, the streaming-read measurement helper
+    (include/hbl_calib.h); raises if it has not been built."""
+    global _calib
+    if _calib is None:
+        if not os.path.exists(CALIB_PATH):
+            raise RuntimeError(f"{CALIB_PATH} is missing: build it with hadamard_rotated_ternary_amd/build.py")
+        L = ctypes.CDLL(CALIB_PATH)
+        L.hbl_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+        L.hbl_calib_stream_read.restype = ctypes.c_int
+        L.hbl_calib_broadcast_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        L.hbl_calib_broadcast_read.restype = ctypes.c_int
+        _calib = L
+    return _calib
+
+
+def stream_read(src: torch.Tensor, digest: torch.Tensor = None) -> torch.Tensor:
+    """Plain streaming read of src's bytes; returns the per-64-KiB XOR digests
+    (uint32 viewed as int32)."""
+    nbytes = src.numel() * src.element_size()
+    if digest is None:
+        digest = torch.empty(((nbytes + 65535) // 65536,), dtype=torch.int32, device=src.device)
+    rc = calib_lib().hbl_calib_stream_read(_ptr(src), nbytes, _ptr(digest), _stream())
+    if rc != 0:
+        raise HBLError("hbl_calib_stream_read", rc)
+    return digest
+
+
+def broadcast_read(src: torch.Tensor, workgroups: int, digest: torch.Tensor = None) -> torch.Tensor:
+    """Every one of `workgroups` workgroups reads all of src's bytes; returns
+    one XOR digest per workgroup (uint32 viewed as int32)."""
+    nbytes = src.numel() * src.element_size()
+    if digest is None:
+        digest = torch.empty((workgroups,), dtype=torch.int32, device=src.device)
+    rc = calib_lib().hbl_calib_broadcast_read(_ptr(src), nbytes, workgroups, _ptr(digest), _stream())
+    if rc != 0:
+        raise HBLError("hbl_calib_broadcast_read", rc)
+    return digest
+
+
 def _call(name, *args):
     rc = getattr(lib(), name)(*args)
     if rc != 0:

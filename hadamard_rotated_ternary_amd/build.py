@@ -69,7 +69,27 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed linking libhbl.so")
     os.replace(tmp, LIB)
+    build_calib(verbose)
     return LIB
+
+
+CALIB_LIB = os.path.join(HERE, "libhbl_calib.so")
+
+
+def build_calib(verbose: bool = False) -> str:
+    """libhbl_calib.so: the plain streaming read the benchmark times beside
+    the decode matmul (include/hbl_calib.h); kept out of libhbl.so."""
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    tmp = CALIB_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, *inc, os.path.join(CSRC, "calib.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on calib.hip")
+    os.replace(tmp, CALIB_LIB)
+    return CALIB_LIB
 
 
 if __name__ == "__main__":

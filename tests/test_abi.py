@@ -271,3 +271,32 @@ def test_attention_entry_points_validate_without_device():
     # partial records: B * Hq * ceil(Tmax / 512 tokens) of (d + 4) floats, rounded up to 256 bytes
     assert L.hbl_attention_workspace_bytes(2, 8, 128, 1000) == -(-(2 * 8 * 2 * 132 * 4) // 256) * 256
     assert L.hbl_attention_workspace_bytes(1, 1, 64, 1) == 0     # one chunk: the output is written directly
+
+
+def test_calib_library_exports_and_validates():
+    """libhbl_calib.so (the benchmark's streaming read, include/hbl_calib.h)
+    exports what its header declares and rejects bad arguments before any
+    launch."""
+    import re
+    if not os.path.exists(hbl.CALIB_PATH):
+        from hadamard_rotated_ternary_amd import build
+        build.build_calib()
+    with open(hbl.CALIB_HEADER) as f:
+        declared = set(re.findall(r"^\s*int\s+(hbl_\w+)\s*\(", f.read(), re.M))
+    assert declared == {"hbl_calib_stream_read", "hbl_calib_broadcast_read"}
+    out = subprocess.run(["nm", "-D", "--defined-only", hbl.CALIB_PATH], capture_output=True, text=True).stdout
+    assert declared <= {line.split()[-1] for line in out.splitlines() if " T " in line}
+    C = hbl.calib_lib()
+    f = C.hbl_calib_stream_read
+    assert f(None, 1024, A2, S) == NULL
+    assert f(A, 1024, None, S) == NULL
+    assert f(A, 0, A2, S) == SHAPE
+    assert f(A, 1000, A2, S) == SHAPE
+    assert f(BAD, 1024, A2, S) == ALIGN
+    b = C.hbl_calib_broadcast_read
+    assert b(None, 1024, 256, A2, S) == NULL
+    assert b(A, 1024, 256, None, S) == NULL
+    assert b(A, 1000, 256, A2, S) == SHAPE
+    assert b(A, 1024, 0, A2, S) == SHAPE
+    assert b(A, 1024, 65537, A2, S) == SHAPE
+    assert b(BAD, 1024, 256, A2, S) == ALIGN

@@ -511,7 +511,7 @@ def test_split_k_decode_reduction_in_kernel(bits, M, K, N):
         assert torch.equal(y.view(torch.int16), y_refs[i % 2].view(torch.int16)), i
 
 
-@pytest.mark.parametrize("M,K", [(1, 16384), (24, 16384), (40, 16384), (64, 16384), (48, 32768)])
+@pytest.mark.parametrize("M,K", [(1, 16384), (16, 16384), (24, 16384), (40, 16384), (64, 16384), (48, 32768)])
 def test_forward_graph_replays(M, K):
     """The forward captured once in a HIP graph and replayed with new inputs
     written into the captured buffers between replays (eager work and a
@@ -619,7 +619,8 @@ def test_token_permutation_equivariance():
 
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("M,K,N", [(5, 512, 48), (16, 2048, 272), (17, 16384, 4096), (31, 4096, 64),
-                                   (33, 16384, 4096), (64, 8192, 512), (40, 32768, 272)])
+                                   (33, 16384, 4096), (64, 8192, 512), (40, 32768, 272),
+                                   (9, 16384, 4096), (16, 16384, 4096), (13, 1024, 80), (16, 32768, 272)])
 def test_forward_decode_codes_layout_matches_stages(bits, M, K, N):
     """From 5 to 64 tokens the forward keeps its codes in the decode-blocked
     layout (each fragment load one contiguous KiB); the stage calls keep them

@@ -614,17 +614,19 @@ __global__ __launch_bounds__(256, T == 256 ? 1 : 2) void gemm_fp6_kernel(
 // Decode (M <= 64): weight streaming.
 //
 // A workgroup of NW waves owns 16*CPW output channels and one of S equal K
-// ranges.  The range is cut into 256-k blocks dealt round-robin to the waves.
-// Each wave issues every load it will need up front -- per block, its packed
-// weights (16 bytes per lane per 16 channels) and then that block's
-// activation codes -- so the whole weight stream is in flight at once and,
-// because loads retire in issue order, block i can start as soon as its own
-// two loads have landed.  Every weight byte is read from HBM once.
+// ranges.  The range is cut into 256-k blocks dealt round-robin to the waves;
+// each block's packed weights (16 bytes per lane per 16 channels) and
+// activation codes are loaded straight into registers, and every weight byte
+// is read from HBM once.  With one channel group (CPW == 1) a wave keeps a
+// ring of a few blocks requested ahead (decode_plan and the kernel below say
+// how many); with four groups it requests two blocks at a time.
 // v_mfma_i32_16x16x64_i8 runs with channels on the MFMA's M side and up to 16
-// tokens on its N side.  The waves' int32 partials meet in LDS through integer
-// atomics (exact, order free).  With S > 1 a second small kernel sums the S
-// partials in order and dequantises; integer sums are exact, so the result is
-// the same for every S.
+// tokens on its N side.  The waves' int32 partials meet in LDS: per-wave
+// slices summed in a fixed order (CPW == 1) or integer atomics into one tile
+// (CPW == 4); both exact.  With S > 1 the S partials of a channel tile are
+// summed by the last workgroup of the tile to finish (when the launch passes
+// arrival counters: the forward) or by decode_reduce_kernel (stage calls);
+// integer sums are exact, so the result is the same for every S.
 constexpr int DKB = 256;
 
 struct DecodePlan { int cpw, S, mb, nw; };

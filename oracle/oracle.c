@@ -27,6 +27,9 @@
  *     quantised per head by absmax to unsigned integers (3-bit KV cache), and
  *     one decode step of attention over that cache.
  *
+ * Parity unpinned by the pages: the INT4 multiplier sqrt(7) (see Q4 below);
+ * every function is otherwise pinned by the tests in test_oracle_pins.py.
+ *
  * Precision: every floating-point step is done in double; values are rounded
  * only where the method itself produces a stored low-precision quantity
  * (the per-tensor weight scale, the integer codes) -- see each function.
@@ -49,7 +52,10 @@
 static const double EPS_NORM = 1e-6;
 static const double EPS_Q = 1e-5;
 static const double Q8 = 127.0;      /* INT8 absmax: max |x| maps to code 127 */
-/* INT4 absmean multiplier: sqrt(7) (reading; not printed on the pages). */
+/* INT4 absmean multiplier: sqrt(7) (reading; not printed on the pages, so
+ * this constant is parity unpinned by the pages: the tests pin every
+ * consequence of it -- hand-worked codes, Gaussian code-edge frequencies --
+ * but no page fixes the value itself). */
 #define Q4 (sqrt(7.0))
 
 int oracle_version(void) { return 1; }

@@ -8,6 +8,7 @@ device raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import re
 
@@ -136,12 +137,15 @@ def _call(name, *args):
         raise HBLError(name, rc)
 
 
+# Pointers and the stream go to ctypes as plain integers (argtypes c_void_p
+# converts them); building c_void_p objects per argument cost more host time
+# per call than the launches of the smallest layer.
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _dtype_code(dt):
@@ -157,7 +161,10 @@ def _dev(t, name):
         raise ValueError(f"{name} must be a contiguous device tensor")
 
 
+@functools.lru_cache(maxsize=4096)
 def workspace_bytes(op: int, M: int, K: int, N: int) -> int:
+    # a pure function of its arguments: cached, so repeated calls of one
+    # shape pay no ctypes round trip for it
     return int(lib().hbl_workspace_bytes(op, M, K, N))
 
 

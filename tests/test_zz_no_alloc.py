@@ -34,8 +34,10 @@ def layer_inputs(M, K, N, bits, seed):
 # decode on decode-blocked codes; two such decodes; INT8 prefill then the
 # one-kernel decode; the largest INT8 problem that fits the scratch, then a
 # blocked decode; a split-K decode (K = 32768) then a smaller one (partials
-# and arrival counters left by the first).
+# and arrival counters left by the first); the 3B down projection (256 x 192
+# tiles of the fp6 matmul) then a prefill on 128 x 128 tiles.
 CASES = [
+    (4, (4096, 8192, 3072), (300, 1024, 272)),
     (4, (1000, 16384, 512), (40, 16384, 4096)),
     (4, (64, 16384, 4096), (33, 4096, 272)),
     (8, (300, 2048, 272), (1, 16384, 4096)),

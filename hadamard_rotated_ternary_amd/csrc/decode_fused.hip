@@ -197,6 +197,131 @@ __global__ __launch_bounds__(64 * FD_NW) void decode_fused_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Short rows (K = 64, 128, 256) and up to 64 tokens: the whole layer in one
+// launch.  Every workgroup (4 waves, 64 output channels) first computes the
+// codes of all M tokens itself -- one wave per token, K / 64 values per lane,
+// the butterflies of the lane's own index bits in registers and those of the
+// six lane bits by lane exchanges -- with the same arithmetic as the prep
+// kernel (unnormalised transform of x * g, 1/r and 1/sqrt(K) folded into the
+// quantiser multiplier, rounding by the 1.5 * 2^23 adder, INT4 clamped to
+// [-8, 7]); codes go to LDS as int8 (an INT4 code is its own int8 value, so
+// both widths take the INT8 matmul: weights expanded to 64 w, sums shifted
+// back by 6).  Then each wave multiplies 16 channels by the M tokens on
+// v_mfma_i32_16x16x64_i8 (channels on the M side, as in the short-row
+// matmul) and stores the dequantised outputs.  At these sizes the work is
+// a few microseconds of launch and latency; one launch instead of two halves
+// that.
+constexpr int SF_MAXM = 64;
+template <int LOGK, int BITS, bool XBF16, int OUT, bool ROT>
+__global__ __launch_bounds__(256) void forward_short_kernel(const void* __restrict__ x, const float* __restrict__ gain,
+                                                            const uint8_t* __restrict__ W,
+                                                            const float* __restrict__ walpha, void* __restrict__ Y,
+                                                            int M, int N) {
+  constexpr int K = 1 << LOGK, E = K / 64, LOGE = LOGK - 6;
+  static_assert(LOGK >= 6 && LOGK <= 8, "short rows only");
+  __shared__ __attribute__((aligned(16))) int8_t codes[SF_MAXM][K];
+  __shared__ float dtok[SF_MAXM];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // ---- codes of every token, one wave per token (the loop is wave-uniform)
+  for (int t = wave; t < M; t += 4) {
+    float v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const size_t i = (size_t)t * K + lane * E + e;
+      v[e] = XBF16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(x)[i] << 16)
+                   : static_cast<const float*>(x)[i];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
+    if (gain != nullptr) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[e] *= gain[lane * E + e];
+    }
+    if constexpr (ROT) {
+      // index k = E * lane + e: the low LOGE bits are the register's, the
+      // next six the lane's
+#pragma unroll
+      for (int bb = 0; bb < LOGE; ++bb)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (!(e & (1 << bb))) {
+            const float p = v[e], q = v[e | (1 << bb)];
+            v[e] = p + q;
+            v[e | (1 << bb)] = p - q;
+          }
+#pragma unroll
+      for (int bb = 0; bb < 6; ++bb) {
+        const bool upper = (lane >> bb) & 1;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float other = __shfl_xor(v[e], 1 << bb, 64);
+          v[e] = upper ? other - v[e] : v[e] + other;
+        }
+      }
+    }
+    float st = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) st = BITS == 8 ? fmaxf(st, fabsf(v[e])) : st + fabsf(v[e]);
+    ss = lane_reduce<64, false>(ss);
+    st = lane_reduce<64, BITS == 8>(st);
+    const float r = sqrtf(ss * (1.0f / K) + kEpsNorm);
+    const float cc = ROT ? 1.0f / (r * sqrtf((float)K)) : 1.0f / r;
+    st = BITS == 8 ? st * cc : (st * (1.0f / K)) * cc;
+    const float Q = BITS == 8 ? kQ8 : kQ4;
+    const float G = fmaxf(st, kEpsQ);
+    const float cs = cc * (Q / G);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float q = __builtin_fmaf(v[e], cs, kRoundMagic);
+      if constexpr (BITS == 4) q = fminf(fmaxf(q, kRoundMagic - 8.0f), kRoundMagic + 7.0f);
+      codes[t][lane * E + e] = (int8_t)(__float_as_uint(q) & 0xFFu);
+    }
+    if (lane == 0) dtok[t] = G / Q;
+  }
+  __syncthreads();
+
+  // ---- 16 channels x up to 64 tokens per wave
+  const int ch0 = blockIdx.x * 64 + 16 * wave;
+  if (ch0 >= N) return;                          // whole wave past the last channel (N % 16 == 0)
+  const int c = lane & 15, g = lane >> 4;
+  constexpr int STEPS = K / 64;
+  const uint32_t* wrow = reinterpret_cast<const uint32_t*>(W + (size_t)(ch0 + c) * (K / 4));
+  const float aw = fmaxf(walpha[0], kEpsQ);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    if (16 * mb >= M) break;                     // wave-uniform
+    const int tt = min(16 * mb + c, M - 1);      // tokens past M repeat the last; never stored
+    v4i acc = v4i{};
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) {
+      const uint4 a4 = *reinterpret_cast<const uint4*>(&codes[tt][64 * j + 16 * g]);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wstep(wrow[4 * j + g]), as_v4i(a4), acc, 0, 0, 0);
+    }
+    const int t = 16 * mb + c;
+    // lane l / register r hold channel 4*(l/16)+r, token l%16
+    if (t < M) store_out4<OUT>(Y, (size_t)t * N + ch0 + 4 * g, unscale4<8>(acc), dtok[t] * aw);
+  }
+}
+
+template <int LOGK, bool ROT>
+static hipError_t launch_short_k(const FusedDecodeArgs& a) {
+#define HBL_SF(BITS, BF, OUT)                                                                                   \
+  hipLaunchKernelGGL((forward_short_kernel<LOGK, BITS, BF, OUT, ROT>), dim3((a.N + 63) / 64), dim3(256), 0,    \
+                     a.stream, a.x, a.gain, a.wpack, a.walpha, a.out, a.M, a.N);                               \
+  return hipGetLastError()
+  if (a.bits == 8) {
+    if (a.x_bf16) { if (a.out_kind == OUT_BF16) { HBL_SF(8, true, OUT_BF16); } HBL_SF(8, true, OUT_F32); }
+    if (a.out_kind == OUT_BF16) { HBL_SF(8, false, OUT_BF16); }
+    HBL_SF(8, false, OUT_F32);
+  }
+  if (a.x_bf16) { if (a.out_kind == OUT_BF16) { HBL_SF(4, true, OUT_BF16); } HBL_SF(4, true, OUT_F32); }
+  if (a.out_kind == OUT_BF16) { HBL_SF(4, false, OUT_BF16); }
+  HBL_SF(4, false, OUT_F32);
+#undef HBL_SF
+}
+
 template <int LOGK, int LOGE, int P2, int BITS, bool XBF16, int OUT, bool ROT>
 static hipError_t launch_fd_t(const FusedDecodeArgs& a) {
   using C = PrepCfg<LOGK, LOGE, P2>;
@@ -233,6 +358,8 @@ static hipError_t launch_fd_k(const FusedDecodeArgs& a) {
 }
 
 bool decode_fused_supported(int M, int logk, bool rotate) {
+  // short rows: up to 64 tokens (forward_short_kernel)
+  if (logk <= 8) return M >= 1 && M <= SF_MAXM && logk >= 6;
   // without the transform the per-token work on each CU is smaller: one
   // kernel wins while M * K <= 49152 (at K = 16384, 6.5 / 8.0 / 10.0 / 11.7 us
   // for 1-4 tokens against 9.6 / 9.8 / 10.2 / 10.7 us for prep + matmul)
@@ -242,6 +369,9 @@ bool decode_fused_supported(int M, int logk, bool rotate) {
 
 hipError_t launch_decode_fused(const FusedDecodeArgs& a) {
   if (!decode_fused_supported(a.M, a.logk, a.rotate)) return hipErrorInvalidValue;
+  if (a.logk == 6) return a.rotate ? launch_short_k<6, true>(a) : launch_short_k<6, false>(a);
+  if (a.logk == 7) return a.rotate ? launch_short_k<7, true>(a) : launch_short_k<7, false>(a);
+  if (a.logk == 8) return a.rotate ? launch_short_k<8, true>(a) : launch_short_k<8, false>(a);
   // T = 512 threads per token: E = K / 512 values per thread
   if (a.logk == 14) return a.rotate ? launch_fd_k<14, 5, 8, true>(a) : launch_fd_k<14, 5, 8, false>(a);
   return a.rotate ? launch_fd_k<13, 4, 6, true>(a) : launch_fd_k<13, 4, 6, false>(a);

@@ -349,6 +349,32 @@ def test_layer_small(bits, M, K, N):
     np.testing.assert_allclose(host(d), ref["d"], rtol=1e-5)
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,K,N,xdt,gain", [(1, 64, 16, "bf16", False), (8, 256, 256, "f32", True),
+                                            (33, 128, 272, "bf16", True), (64, 256, 4096, "bf16", False),
+                                            (17, 64, 80, "f32", False), (64, 128, 48, "f32", True)])
+def test_short_rows_one_launch(bits, M, K, N, xdt, gain):
+    """K = 64, 128, 256 with up to 64 tokens: the whole layer is one kernel
+    (every workgroup computes all tokens' codes, then its channels' outputs).
+    Against the oracle at the layer bar, with and without the transform, and
+    equal bit for bit to the no-alloc entry (same kernel)."""
+    w = synthetic.Workload("t", M, K, N, bits, xdt, "laplace", 0.05, max(1, K // 64), 100.0, 3 * M + K + N + bits)
+    g = synthetic.make_gain(K, M) if gain else None
+    yh, y_ref, ref, xd, wp, a, rows = run_layer(w, gain=g)
+    check_layer(yh, y_ref, ref)
+    gd = None if g is None else dev(g)
+    x, xb, wl = synthetic.make_inputs(w)
+    wt, alpha = oracle.quantize_weights(wl)
+    yu = hbl.forward(xd, wp, a, bits, gain=gd, rotate=False, out_dtype=torch.float32)
+    refu = oracle.forward(x, wt, alpha, bits, g=g, rotate=False)
+    refu["alpha"] = alpha
+    check_layer(host(yu), refu["y"], refu)
+    y = hbl.forward(xd, wp, a, bits, gain=gd)
+    yn = hbl.forward_noalloc(xd, wp, a, bits, gain=gd)
+    assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32),
+                       yn.view(torch.int16) if yn.dtype == torch.bfloat16 else yn.view(torch.int32))
+
+
 def test_layer_with_gain_fp32_out():
     w = synthetic.WORKLOADS["tiny_int8"]
     g = synthetic.make_gain(w.K, 3)

@@ -144,7 +144,10 @@ hbl_status hbl_quantize_weights(const float *w, int64_t N, int64_t K,
  *   w_packed  uint8 [N][K/4] from hbl_quantize_weights;  w_alpha fp32 [1]
  *   y         [M][N] output, dtype y_dtype (fp32 or bf16; bf16 rounds to nearest even)
  *   workspace at least hbl_workspace_bytes(HBL_OP_FORWARD_INT8, M, K, N) bytes;
- *             holds the activation codes and scales between the two kernels,
+ *             holds the activation codes and scales between the two kernels
+ *             (unused where the whole layer is one kernel: 1..4 tokens at
+ *             K = 8192 / 16384 while M * K <= 16384, and up to 64 tokens at
+ *             K <= 256; the size asked for is the same),
  *             and for 33..64 tokens with K = 32768 the split-K partial sums
  *             plus one arrival counter per 64-channel tile, which the first
  *             kernel of each call clears (the workspace needs no
